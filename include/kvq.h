@@ -1,0 +1,232 @@
+/*
+ * kvq.h -- C ABI of the quantised KV-cache library (MI355X / gfx950).
+ *
+ * Two computations make up the hot path:
+ *   (a) quantize-append: new keys/values of every sequence are encoded into a
+ *       packed cache (KIVI-style asymmetric b-bit codes with a full-precision
+ *       residual window, a symmetric per-head-per-token variant, or FP8 E4M3
+ *       with a per-head scale);
+ *   (b) decode attention: q.K^T, softmax and P.V computed straight from the
+ *       packed cache, split over the token axis and merged on the GPU.
+ *
+ * Sources the operations follow (web pages on KV-cache quantisation):
+ *   [QC]   "Quantising the Cache." (llm.curionode.com, efficient-inference /
+ *          kv-quantisation): Workshop; "Twice the users for nearly nothing";
+ *          Terms (per-token, per-channel).
+ *   [QKV]  "Quantizing the KV cache" (learning.iampt.xyz/quantization/kv-cache):
+ *          "The other big memory user" (KV-bytes equation); "How the KV cache is
+ *          quantized" (FP8 KV cache); "Keys and values are shaped differently";
+ *          going deeper: "Per-channel and per-token grouping" (Q_b, s) and
+ *          "Why values per token" (o = sum_t p_t V_t).
+ *   [KIVI] "KIVI: A Tuning-Free Asymmetric 2bit Quantization for KV Cache"
+ *          (crackai.dev/papers/kivi): "How It Works" (per-channel keys,
+ *          per-token values, residual length of recent tokens kept unquantised).
+ *   [KVQ]  "KVQuant: Towards 10 Million Context Length LLM Inference with KV
+ *          Cache Quantization" (research.elamur.ai): Summary (keys quantised
+ *          before the rotary embedding).
+ *
+ * Conventions shared by every entry point
+ *   - All device buffers are owned by the caller. The library allocates and
+ *     frees nothing and keeps no global mutable state.
+ *   - Device pointers must be 16-byte aligned.
+ *   - Calls are asynchronous: they validate their arguments on the host, then
+ *     enqueue kernels on `stream` (a hipStream_t; NULL = the default stream)
+ *     and return. Inputs must stay live until the stream has passed them.
+ *   - Validation happens before anything is enqueued. On any error nothing is
+ *     launched and the negative status is returned.
+ *   - KVQ_ERR_DEVICE is returned when a kernel launch reports an error.
+ *   - Keys, values and queries must be finite; non-finite input is outside the
+ *     contract and not checked.
+ *   - Calls on distinct streams are independent; concurrent calls that touch
+ *     the same cache slab or workspace race (the caller's responsibility).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_ABI_VERSION 1
+
+/* ---- status codes ------------------------------------------------------ */
+#define KVQ_OK               0
+#define KVQ_ERR_NULL        -1  /* a required pointer is NULL                */
+#define KVQ_ERR_INVALID     -2  /* a value is out of range / inconsistent    */
+#define KVQ_ERR_UNSUPPORTED -3  /* valid but not built (e.g. head_dim 96)    */
+#define KVQ_ERR_CAPACITY    -4  /* past_tokens + new_tokens > max_tokens     */
+#define KVQ_ERR_WORKSPACE   -5  /* workspace_bytes too small                 */
+#define KVQ_ERR_DEVICE      -6  /* the HIP runtime reported a launch error   */
+
+/* ---- schemes ------------------------------------------------------------ */
+/* KVQ_KIVI: asymmetric round-to-nearest, keys per channel over groups of
+ *   `group` consecutive tokens, values per token (one scale and offset per
+ *   token per KV head); the newest `residual` tokens stay in the input dtype.
+ *   [QKV] going deeper: "Per-channel and per-token grouping"; [KIVI] How It
+ *   Works. bits in {2,4,8}.
+ * KVQ_SYM_TOKEN: symmetric round-to-nearest of each head's key and value at
+ *   every token, one scale per (token, KV head) for K and one for V; every
+ *   token is encoded on arrival. [QC] Workshop. bits in {2,4,8}.
+ * KVQ_FP8_E4M3: each element divided by a static per-(layer, KV head) fp32
+ *   scale and rounded to OCP FP8 E4M3FN (nearest, ties to even mantissa,
+ *   saturating at +-448). [QKV] "How the KV cache is quantized", FP8 KV cache.
+ *   bits must be 8. */
+#define KVQ_KIVI       0
+#define KVQ_SYM_TOKEN  1
+#define KVQ_FP8_E4M3   2
+
+/* ---- dtypes (K/V input + residual ring, and the query) ------------------ */
+#define KVQ_F32   0
+#define KVQ_BF16  1
+
+/* ---- kvq_cache_bytes kinds --------------------------------------------- */
+#define KVQ_BYTES_FORMULA    0  /* batch * 2*layers*kv_heads*head_dim*tokens*bits/8 */
+#define KVQ_BYTES_CACHE      1  /* exact bytes of the layout below              */
+#define KVQ_BYTES_WORKSPACE  2  /* decode workspace for a call over `tokens`    */
+
+/* Shape and encoding of one cache. All fields by value; struct_size must be
+ * sizeof(kvq_config) (ABI guard). [QKV] "The other big memory user": the cache
+ * is layers x KV heads x head size x tokens x bits; several query heads share
+ * one KV head (grouped-query attention). */
+typedef struct kvq_config {
+  uint32_t struct_size;  /* = sizeof(kvq_config)                            */
+  int32_t  scheme;       /* KVQ_KIVI / KVQ_SYM_TOKEN / KVQ_FP8_E4M3         */
+  int32_t  bits;         /* 2, 4 or 8 (8 for FP8)                           */
+  int32_t  layers;       /* >= 1                                            */
+  int32_t  q_heads;      /* multiple of kv_heads; q_heads/kv_heads in 1..16 */
+  int32_t  kv_heads;     /* >= 1                                            */
+  int32_t  head_dim;     /* 32, 64, 128 or 256                              */
+  int32_t  batch;        /* sequences; all share one length in this ABI     */
+  int64_t  max_tokens;   /* capacity per sequence                           */
+  int32_t  group;        /* tokens per page / key group; must be 32         */
+  int32_t  residual;     /* KIVI: R >= 0 newest tokens kept unquantised;
+                            must be 0 for SYM_TOKEN and FP8                 */
+  int32_t  in_dtype;     /* dtype of k_new/v_new and of the residual ring   */
+  int32_t  q_dtype;      /* dtype of the decode query                       */
+  double   rope_theta;   /* > 0: keys are cached before the rotary embedding
+                            and decode rotates dequantised keys (position t)
+                            and the query (position tokens-1) [KVQ] Summary;
+                            0: no rotation                                  */
+  float    sm_scale;     /* softmax scale; 0 selects 1/sqrt(head_dim)       */
+  int32_t  num_splits;   /* decode token splits per (seq, KV head);
+                            0 = automatic, else an upper bound              */
+} kvq_config;
+
+/* ==== Cache layout, version 1 =============================================
+ * The cache is one byte buffer. It holds, in this order, one slab per
+ * (layer, sequence, KV head):   slab_index = (layer*batch + seq)*kv_heads + h.
+ * A slab is `P` pages followed (KIVI only) by the residual ring. Every page
+ * holds `group` = 32 consecutive tokens of one (layer, seq, KV head); page p
+ * covers tokens [32p, 32p+32).
+ *
+ * Packing: b-bit field i of a packed run occupies bits [i*b, (i+1)*b) of the
+ * run read as a little-endian bit stream (LSB of byte 0 first).
+ * "K rows": the page's 32 tokens one after another, each token's d channel
+ *           codes contiguous (field index = channel).
+ * "V cols": the page's d channels one after another, each channel's 32 token
+ *           codes contiguous (field index = token).
+ * d = head_dim, b = bits. All sizes below are multiples of 16 bytes and every
+ * page size is a multiple of 256 bytes.
+ *
+ * KIVI page (8*d*b + 8*d + 256 bytes), P = floor(max(0, max_tokens-R)/32):
+ *   Kc  K rows, unsigned codes     32*d*b/8 bytes
+ *   Ks  fp32 scale per channel     4*d
+ *   Kz  fp32 offset (group min)    4*d
+ *   Vc  V cols, unsigned codes     32*d*b/8
+ *   Vs  fp32 scale per token       128
+ *   Vz  fp32 offset per token      128
+ *   Ring after the P pages: (R+32) K rows then (R+32) V rows, each d values of
+ *   in_dtype; token t lives in slot t mod (R+32) while it is unquantised.
+ * SYM_TOKEN page (8*d*b + 256 bytes), P = ceil(max_tokens/32):
+ *   Kc  K rows, b-bit two's-complement codes   32*d*b/8
+ *   Ks  fp32 scale per token                   128
+ *   Vc  V cols, b-bit two's-complement codes   32*d*b/8
+ *   Vs  fp32 scale per token                   128
+ * FP8_E4M3 page (64*d bytes), P = ceil(max_tokens/32):
+ *   Kc  K rows, one E4M3FN byte per value      32*d
+ *   Vc  V cols, one E4M3FN byte per value      32*d
+ *
+ * Which tokens are quantised (KIVI), for a cache holding T tokens:
+ *   q(T) = 32*floor(max(0, T-R)/32) tokens live in pages [0, q(T)/32); the
+ *   other n_r = T - q(T) tokens live in the ring. So the newest R tokens are
+ *   always in full precision, and whenever R+32 tokens are unquantised the
+ *   oldest 32 are encoded as one group. [QKV] "Keys and values are shaped
+ *   differently" (window of recent tokens quantised as a group once it fills)
+ *   and going deeper (the newest R tokens kept in full precision); [KIVI] How
+ *   It Works (residual length).
+ * Encoding of one KIVI group (fp32 arithmetic, IEEE division, ties-to-even
+ * rounding, no fused multiply-add), L = 2^b - 1, per key channel over the 32
+ * tokens of the page and per value token over its d channels:
+ *   mn = min x (+0 replaces -0), mx = max x, s = (mx - mn) / L,
+ *   code = s == 0 ? 0 : clamp(rint((x - mn) / s), 0, L),  stored offset = mn;
+ *   dequantised value = code*s + mn.  [QKV] going deeper, Q_b and s.
+ * SYM_TOKEN, per (token, KV head), K and V separately, Q = 2^(b-1) - 1:
+ *   s = max|x| / Q, code = s == 0 ? 0 : clamp(rint(x / s), -Q, Q);
+ *   dequantised value = code*s.  [QC] Workshop.
+ * FP8_E4M3: code = E4M3FN(x / scale[h]) (round to nearest, ties to even
+ *   mantissa, |y| >= 448 -> +-448, sign kept); dequantised = value*scale[h].
+ * ========================================================================== */
+
+/* Bytes for `tokens` tokens per sequence. Host-only; never touches a device.
+ *   KVQ_BYTES_FORMULA:   batch * 2*layers*kv_heads*head_dim*tokens*bits/8, the
+ *                        KV-bytes equation of [QKV] "The other big memory
+ *                        user" with scales ignored (as in [QC] Workshop).
+ *   KVQ_BYTES_CACHE:     exact size of the layout above for capacity `tokens`
+ *                        (all layers, all sequences).
+ *   KVQ_BYTES_WORKSPACE: decode workspace needed by a call over `tokens`
+ *                        cached tokens (monotone in `tokens`).
+ * Returns the byte count (>= 0) or a negative status. */
+int64_t kvq_cache_bytes(const kvq_config* cfg, int64_t tokens, int32_t kind);
+
+/* Quantize-append: append `new_tokens` tokens to every sequence of `layer`.
+ *   cache        device, >= kvq_cache_bytes(cfg, max_tokens, KVQ_BYTES_CACHE)
+ *   past_tokens  tokens already held per sequence (all sequences equal)
+ *   k_new, v_new device [batch][new_tokens][kv_heads][head_dim], in_dtype
+ *   k_scale,
+ *   v_scale      FP8 only: device fp32 [kv_heads], this layer's per-head
+ *                scales (must be > 0); NULL for the other schemes
+ * Requires past_tokens + new_tokens <= max_tokens (else KVQ_ERR_CAPACITY).
+ * new_tokens == 0 is a no-op. Appending in any chunking (one call of T tokens
+ * or T calls of one token) leaves identical bytes in every defined field.
+ * Steps [QKV] going deeper; [KIVI] How It Works; [QC] Workshop; [QKV] FP8. */
+int32_t kvq_quantize_append(const kvq_config* cfg, void* cache, int32_t layer,
+                            int64_t past_tokens, int64_t new_tokens,
+                            const void* k_new, const void* v_new,
+                            const float* k_scale, const float* v_scale,
+                            void* stream);
+
+/* Decode attention over the `tokens` cached tokens of `layer`:
+ *   out[b][h][:] = sum_t p_t * V^[t],  p = softmax_t(sm_scale * q[b][h].K^[t])
+ * where K^, V^ are the dequantised cache and query head h reads KV head
+ * floor(h / (q_heads/kv_heads)).  [QKV] going deeper, "Why values per token".
+ * With rope_theta > 0 the dequantised key at position t and the query (at
+ * position tokens-1) are rotated by the rotary embedding: channel pairs
+ * (2i, 2i+1) turned by angle pos * theta^(-2i/head_dim).  [KVQ] Summary.
+ *   q          device [batch][q_heads][head_dim], q_dtype
+ *   k_scale,
+ *   v_scale    FP8 only: as for append; NULL otherwise
+ *   out        device fp32 [batch][q_heads][head_dim]
+ *   workspace  device, >= kvq_cache_bytes(cfg, tokens, KVQ_BYTES_WORKSPACE);
+ *              must be zero-filled before its first use; every call leaves
+ *              it zero-filled again
+ * Requires 1 <= tokens <= max_tokens and that the cache holds `tokens` tokens.
+ */
+int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache,
+                             int32_t layer, int64_t tokens, const void* q,
+                             const float* k_scale, const float* v_scale,
+                             float* out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* kvq_status_string(int32_t status);
+
+/* KVQ_ABI_VERSION of the built library. */
+int32_t kvq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

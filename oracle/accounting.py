@@ -1,0 +1,86 @@
+"""Oracle: memory accounting of the KV cache (test infrastructure only).
+
+* ``kv_bytes_formula`` -- "Quantizing the KV cache", section "The other big
+  memory user": KV bytes = 2 x layers x KV heads x head size x tokens x bytes
+  per value, the 2 counting keys and values.
+* ``concurrency`` -- "Quantising the Cache.", Workshop and "Twice the users for
+  nearly nothing": how many 8192-token conversations fit beside Llama 3 8B's
+  16.1 GB of BF16 weights on an 80 GB GPU used to 90%, cache scales ignored.
+* ``layout_cache_bytes`` -- the byte size of the documented cache layout
+  (pages of 32 tokens per (layer, sequence, KV head), plus the residual ring
+  for the KIVI scheme), computed here from that description alone.
+"""
+
+from fractions import Fraction
+
+KIVI, SYM_TOKEN, FP8_E4M3 = 0, 1, 2
+PAGE = 32
+
+
+def kv_bytes_formula(layers, kv_heads, head_dim, tokens, bits, batch=1):
+    """2 * layers * kv_heads * head_dim * tokens * bits/8 (times sequences).
+
+    Exact integer arithmetic (bits/8 kept as a fraction, so 4-bit works)."""
+    b = Fraction(2 * layers * kv_heads * head_dim * tokens * batch) * Fraction(bits, 8)
+    assert b.denominator == 1, "bytes must be whole"
+    return int(b)
+
+
+def concurrency(bits, gpu_bytes=80e9, use=0.9, weight_bytes=16.1e9,
+                context=8192, layers=32, kv_heads=8, head_dim=128):
+    """Conversations of `context` tokens that fit in the memory left beside
+    the weights: floor((use*gpu - weights) / (context * bytes per token)).
+    Llama 3 8B shape (32 layers, 8 KV heads of 128), scales ignored."""
+    per_token = kv_bytes_formula(layers, kv_heads, head_dim, 1, bits)
+    free = use * gpu_bytes - weight_bytes
+    return int(free // (context * per_token))
+
+
+def flush_plan(tokens, residual, group=PAGE):
+    """Split of a T-token KIVI cache into quantised and full-precision parts.
+
+    The newest `residual` tokens always stay in full precision; whenever the
+    unquantised tokens reach residual+group, the oldest `group` of them are
+    encoded together ("Quantizing the KV cache": the window is quantised as a
+    group once it fills, and the newest R tokens are kept in full precision;
+    KIVI How It Works: the most recent tokens kept unquantised).
+    Returns (q, n_r): q tokens in quantised groups, n_r = T - q unquantised."""
+    q = group * (max(0, tokens - residual) // group)
+    return q, tokens - q
+
+
+def page_bytes(scheme, head_dim, bits):
+    """Bytes of one 32-token page of the documented layout."""
+    d, b = head_dim, bits
+    if scheme == KIVI:
+        # K codes + K scale/offset per channel + V codes + V scale/offset per token
+        return PAGE * d * b // 8 + 4 * d + 4 * d + PAGE * d * b // 8 + 4 * PAGE + 4 * PAGE
+    if scheme == SYM_TOKEN:
+        return PAGE * d * b // 8 + 4 * PAGE + PAGE * d * b // 8 + 4 * PAGE
+    if scheme == FP8_E4M3:
+        return PAGE * d + PAGE * d
+    raise ValueError(scheme)
+
+
+def pages_per_slab(scheme, capacity, residual):
+    if scheme == KIVI:
+        return max(0, capacity - residual) // PAGE
+    return -(-capacity // PAGE)
+
+
+def ring_bytes(scheme, head_dim, residual, in_itemsize):
+    if scheme != KIVI:
+        return 0
+    return 2 * (residual + PAGE) * head_dim * in_itemsize
+
+
+def slab_bytes(scheme, head_dim, bits, capacity, residual, in_itemsize):
+    return (pages_per_slab(scheme, capacity, residual) * page_bytes(scheme, head_dim, bits)
+            + ring_bytes(scheme, head_dim, residual, in_itemsize))
+
+
+def layout_cache_bytes(scheme, layers, batch, kv_heads, head_dim, bits, capacity,
+                       residual, in_itemsize):
+    """Whole cache: one slab per (layer, sequence, KV head)."""
+    return layers * batch * kv_heads * slab_bytes(scheme, head_dim, bits, capacity,
+                                                  residual, in_itemsize)

@@ -1,0 +1,185 @@
+"""Oracle: a whole quantised KV cache, appended to and attended over
+(test infrastructure only).
+
+The oracle keeps every appended token exactly (its float32 value and the raw
+bits of its input dtype) and derives the cache from that history each time it
+is asked, which makes the result independent of how the appends were
+chunked by construction:
+
+* KIVI: with T tokens held, tokens [0, q(T)) are encoded in 32-token groups
+  (keys per channel, values per token) and the newest T - q(T) sit in the
+  residual ring unquantised, slot t mod (R + 32) ("Quantizing the KV cache":
+  the newest R tokens stay in full precision, a full window is quantised as a
+  group; KIVI How It Works: recent tokens kept in 16-bit).
+* SYM_TOKEN / FP8_E4M3: every token is encoded as it arrives ("Quantising the
+  Cache.", Workshop: rounded before it enters the cache).
+
+Decode attention (``decode``) dequantises in float64, applies the rotary
+embedding to keys at their positions and to the query at position T-1 when
+rope_theta > 0 (KVQuant Summary: keys cached before RoPE), and takes the
+float64 softmax-weighted sum of value rows ("Quantizing the KV cache", "Why
+values per token").
+"""
+
+import numpy as np
+
+from . import accounting, attention, codec, layout, rope
+
+KIVI, SYM_TOKEN, FP8_E4M3 = accounting.KIVI, accounting.SYM_TOKEN, accounting.FP8_E4M3
+PAGE = 32
+
+
+def bf16_bits_to_f32(raw):
+    """bfloat16 bit patterns (uint16) to their exact float32 values."""
+    raw = np.asarray(raw, np.uint16)
+    return (raw.astype(np.uint32) << 16).view(np.float32)
+
+
+class OracleCache:
+    """in_dtype is "f32" (inputs float32) or "bf16" (inputs uint16 bit patterns)."""
+
+    def __init__(self, scheme, bits, layers, batch, kv_heads, head_dim, capacity,
+                 residual=0, in_dtype="bf16"):
+        if scheme != KIVI:
+            assert residual == 0
+        self.scheme, self.bits, self.layers, self.batch = scheme, bits, layers, batch
+        self.kv_heads, self.d, self.capacity = kv_heads, head_dim, capacity
+        self.residual, self.in_dtype = residual, in_dtype
+        self.itemsize = 2 if in_dtype == "bf16" else 4
+        self.raw_k = [None] * layers      # [B, T, Hkv, d] raw input (uint16 or float32)
+        self.raw_v = [None] * layers
+        self.k_scale = [None] * layers    # FP8: float32 [Hkv] per layer
+        self.v_scale = [None] * layers
+
+    # ---- appends ----------------------------------------------------------
+    def tokens(self, layer):
+        return 0 if self.raw_k[layer] is None else self.raw_k[layer].shape[1]
+
+    def append(self, layer, k_new, v_new, k_scale=None, v_scale=None):
+        k_new, v_new = np.asarray(k_new), np.asarray(v_new)
+        assert k_new.shape == v_new.shape and k_new.shape[0] == self.batch
+        assert self.tokens(layer) + k_new.shape[1] <= self.capacity
+        if self.scheme == FP8_E4M3:
+            ks = np.asarray(k_scale, np.float32)
+            vs = np.asarray(v_scale, np.float32)
+            if self.k_scale[layer] is not None:   # static per-head scales
+                assert np.array_equal(ks, self.k_scale[layer])
+                assert np.array_equal(vs, self.v_scale[layer])
+            self.k_scale[layer], self.v_scale[layer] = ks, vs
+        if self.raw_k[layer] is None:
+            self.raw_k[layer], self.raw_v[layer] = k_new.copy(), v_new.copy()
+        else:
+            self.raw_k[layer] = np.concatenate([self.raw_k[layer], k_new], axis=1)
+            self.raw_v[layer] = np.concatenate([self.raw_v[layer], v_new], axis=1)
+
+    def values(self, layer):
+        """Exact float32 values of all held tokens, [B, T, Hkv, d] each."""
+        if self.in_dtype == "bf16":
+            return bf16_bits_to_f32(self.raw_k[layer]), bf16_bits_to_f32(self.raw_v[layer])
+        return (np.asarray(self.raw_k[layer], np.float32),
+                np.asarray(self.raw_v[layer], np.float32))
+
+    # ---- byte image -------------------------------------------------------
+    def slab_size(self):
+        return accounting.slab_bytes(self.scheme, self.d, self.bits, self.capacity,
+                                     self.residual, self.itemsize)
+
+    def page_size(self):
+        return accounting.page_bytes(self.scheme, self.d, self.bits)
+
+    def slab_image(self, layer, b, h):
+        """(bytes, mask) of one slab for the tokens held now."""
+        size = self.slab_size()
+        buf = np.zeros(size, np.uint8)
+        mask = np.zeros(size, np.uint8)
+        T = self.tokens(layer)
+        if T == 0:
+            return buf, mask
+        K, V = self.values(layer)
+        K, V = K[b, :, h, :], V[b, :, h, :]
+        ps = self.page_size()
+        if self.scheme == KIVI:
+            q, _ = accounting.flush_plan(T, self.residual)
+            for p in range(q // PAGE):
+                pb, pm = layout.kivi_page(K[p * PAGE:(p + 1) * PAGE], V[p * PAGE:(p + 1) * PAGE],
+                                          self.bits)
+                buf[p * ps:(p + 1) * ps], mask[p * ps:(p + 1) * ps] = pb, pm
+            n_pages = accounting.pages_per_slab(KIVI, self.capacity, self.residual)
+            ring0 = n_pages * ps
+            slots = self.residual + PAGE
+            row = self.d * self.itemsize
+            rk = np.ascontiguousarray(self.raw_k[layer][b, :, h, :]).view(np.uint8).reshape(T, row)
+            rv = np.ascontiguousarray(self.raw_v[layer][b, :, h, :]).view(np.uint8).reshape(T, row)
+            for t in range(q, T):
+                s = t % slots
+                ko = ring0 + s * row
+                vo = ring0 + (slots + s) * row
+                buf[ko:ko + row], mask[ko:ko + row] = rk[t], 0xFF
+                buf[vo:vo + row], mask[vo:vo + row] = rv[t], 0xFF
+        else:
+            for p in range(-(-T // PAGE)):
+                n = min(PAGE, T - p * PAGE)
+                k32 = np.zeros((PAGE, self.d), np.float32)
+                v32 = np.zeros((PAGE, self.d), np.float32)
+                k32[:n], v32[:n] = K[p * PAGE:p * PAGE + n], V[p * PAGE:p * PAGE + n]
+                if self.scheme == SYM_TOKEN:
+                    pb, pm = layout.sym_page(k32, v32, self.bits, n)
+                else:
+                    pb, pm = layout.fp8_page(k32, v32, self.k_scale[layer][h],
+                                             self.v_scale[layer][h], n)
+                buf[p * ps:(p + 1) * ps], mask[p * ps:(p + 1) * ps] = pb, pm
+        return buf, mask
+
+    def cache_image(self):
+        """(bytes, mask) of the whole cache, slabs ordered (layer, seq, KV head)."""
+        bufs, masks = [], []
+        for layer in range(self.layers):
+            for b in range(self.batch):
+                for h in range(self.kv_heads):
+                    bb, mm = self.slab_image(layer, b, h)
+                    bufs.append(bb)
+                    masks.append(mm)
+        return np.concatenate(bufs), np.concatenate(masks)
+
+    # ---- dequantised cache and attention -----------------------------------
+    def dequantized(self, layer):
+        """K^, V^ as float64 [B, Hkv, T, d] (no rotary embedding)."""
+        K, V = self.values(layer)
+        B, T, H, d = K.shape
+        K = np.transpose(K, (0, 2, 1, 3))        # [B, H, T, d]
+        V = np.transpose(V, (0, 2, 1, 3))
+        kh = np.empty((B, H, T, d))
+        vh = np.empty((B, H, T, d))
+        if self.scheme == KIVI:
+            q, _ = accounting.flush_plan(T, self.residual)
+            for p in range(q // PAGE):
+                sl = slice(p * PAGE, (p + 1) * PAGE)
+                kc, ks, kz = codec.kivi_quantize(K[:, :, sl], self.bits, axis=2)
+                vc, vs, vz = codec.kivi_quantize(V[:, :, sl], self.bits, axis=3)
+                kh[:, :, sl] = codec.kivi_dequantize(kc, ks, kz, axis=2)
+                vh[:, :, sl] = codec.kivi_dequantize(vc, vs, vz, axis=3)
+            kh[:, :, q:] = K[:, :, q:]
+            vh[:, :, q:] = V[:, :, q:]
+        elif self.scheme == SYM_TOKEN:
+            kc, ks = codec.sym_quantize(K, self.bits, axis=3)
+            vc, vs = codec.sym_quantize(V, self.bits, axis=3)
+            kh[:] = codec.sym_dequantize(kc, ks, axis=3)
+            vh[:] = codec.sym_dequantize(vc, vs, axis=3)
+        else:
+            ksc = self.k_scale[layer][None, :, None, None]
+            vsc = self.v_scale[layer][None, :, None, None]
+            kh[:] = codec.fp8_dequantize(codec.fp8_quantize(K, ksc), ksc)
+            vh[:] = codec.fp8_dequantize(codec.fp8_quantize(V, vsc), vsc)
+        return kh, vh
+
+    def decode(self, layer, q, sm_scale=None, rope_theta=0.0):
+        """Attention of q [B, Hq, d] (float values) over all held tokens."""
+        kh, vh = self.dequantized(layer)
+        q = np.asarray(q, np.float64)
+        T = kh.shape[2]
+        if sm_scale is None or sm_scale == 0:
+            sm_scale = 1.0 / np.sqrt(self.d)
+        if rope_theta > 0:
+            kh = rope.rotate(kh, np.arange(T), rope_theta)
+            q = rope.rotate(q, np.full(q.shape[:-1], T - 1), rope_theta)
+        return attention.decode(q, kh, vh, sm_scale)

@@ -1,0 +1,100 @@
+"""Oracle: byte image of the documented cache layout (test infrastructure only).
+
+The layout itself is this library's own choice (the pages fix no byte
+format): one slab per (layer, sequence, KV head), each slab a run of 32-token
+pages followed, for the KIVI scheme, by the residual ring. Packed b-bit field
+i of a run occupies bits [i*b, (i+1)*b), least significant bit of byte 0
+first. "K rows" = the page's tokens in order, each token's channels
+contiguous; "V cols" = the page's channels in order, each channel's 32 tokens
+contiguous.
+
+Every builder returns (bytes, mask): mask has a 1 bit wherever the layout
+defines the byte's bit for the tokens the cache holds; bits outside the mask
+(unfilled tokens of a partial page, free ring slots) are not specified.
+
+What goes into a page is the encoding of ``codec`` applied exactly as the
+pages state it: KIVI keys per channel over the page's 32 tokens and values per
+token ("Quantizing the KV cache", going deeper; KIVI How It Works); symmetric
+per (token, head) for K and V ("Quantising the Cache.", Workshop); FP8 E4M3
+with one scale per KV head ("Quantizing the KV cache", FP8 KV cache).
+"""
+
+import numpy as np
+
+from . import codec
+
+PAGE = 32
+
+
+def pack_fields(codes, bits):
+    """Concatenate b-bit fields, field 0 in the lowest bits of byte 0."""
+    codes = np.asarray(codes).astype(np.int64).reshape(-1) & ((1 << bits) - 1)
+    bit_stream = ((codes[:, None] >> np.arange(bits)) & 1).astype(np.uint8).reshape(-1)
+    assert bit_stream.size % 8 == 0
+    return np.packbits(bit_stream, bitorder="little")
+
+
+def unpack_fields(buf, bits, n):
+    bit_stream = np.unpackbits(np.asarray(buf, np.uint8), bitorder="little")[: n * bits]
+    return (bit_stream.reshape(n, bits).astype(np.int64) << np.arange(bits)).sum(axis=1)
+
+
+def _f32_bytes(x):
+    return np.ascontiguousarray(np.asarray(x, np.float32)).view(np.uint8).reshape(-1)
+
+
+def _full(n):
+    return np.full(n, 0xFF, np.uint8)
+
+
+def kivi_page(k32, v32, bits):
+    """One full KIVI page from 32 tokens of keys and values (float32 [32, d])."""
+    kc, ks, kz = codec.kivi_quantize(k32, bits, axis=0)   # per channel over the tokens
+    vc, vs, vz = codec.kivi_quantize(v32, bits, axis=1)   # per token over the channels
+    parts = [pack_fields(kc, bits),            # K rows: kc[t, c], channel fastest
+             _f32_bytes(ks), _f32_bytes(kz),
+             pack_fields(vc.T, bits),          # V cols: vc[t, c] stored channel-major
+             _f32_bytes(vs), _f32_bytes(vz)]
+    buf = np.concatenate(parts)
+    return buf, _full(buf.size)
+
+
+def _valid_fields_mask(n_valid, per_row, bits):
+    """Mask for `per_row`-field runs whose first n_valid fields are defined."""
+    ones = np.where(np.arange(per_row) < n_valid, (1 << bits) - 1, 0)
+    return pack_fields(ones, bits)
+
+
+def sym_page(k32, v32, bits, n_valid):
+    """Symmetric page; tokens >= n_valid of k32/v32 are ignored (undefined)."""
+    d = k32.shape[1]
+    kc, ks = codec.sym_quantize(k32, bits, axis=1)        # one scale per token (K)
+    vc, vs = codec.sym_quantize(v32, bits, axis=1)        # one scale per token (V)
+    valid = np.arange(PAGE) < n_valid
+    kc = np.where(valid[:, None], kc, 0)
+    vc = np.where(valid[:, None], vc, 0)
+    ks = np.where(valid, ks, np.float32(0))
+    vs = np.where(valid, vs, np.float32(0))
+    buf = np.concatenate([pack_fields(kc, bits), _f32_bytes(ks),
+                          pack_fields(vc.T, bits), _f32_bytes(vs)])
+    row = d * bits // 8
+    mask = np.concatenate([
+        np.repeat(np.where(valid, 0xFF, 0).astype(np.uint8), row),
+        np.repeat(np.where(valid, 0xFF, 0).astype(np.uint8), 4),
+        np.tile(_valid_fields_mask(n_valid, PAGE, bits), d),
+        np.repeat(np.where(valid, 0xFF, 0).astype(np.uint8), 4)])
+    return buf, mask
+
+
+def fp8_page(k32, v32, k_scale, v_scale, n_valid):
+    """FP8 page with the KV head's scalar scales; tokens >= n_valid undefined."""
+    d = k32.shape[1]
+    kc = codec.fp8_quantize(k32, k_scale)
+    vc = codec.fp8_quantize(v32, v_scale)
+    valid = np.arange(PAGE) < n_valid
+    kc = np.where(valid[:, None], kc, 0).astype(np.uint8)
+    vc = np.where(valid[:, None], vc, 0).astype(np.uint8)
+    buf = np.concatenate([kc.reshape(-1), vc.T.reshape(-1)])
+    mask = np.concatenate([np.repeat(np.where(valid, 0xFF, 0).astype(np.uint8), d),
+                           np.tile(np.where(valid, 0xFF, 0).astype(np.uint8), d)])
+    return buf, mask

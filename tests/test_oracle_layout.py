@@ -1,0 +1,163 @@
+"""Pins of oracle.layout and oracle.cache: bit packing by hand, page contents
+decoded back, the flush rule, and chunking independence."""
+
+import numpy as np
+import pytest
+
+from oracle import accounting as acc
+from oracle import codec, layout
+from oracle.cache import OracleCache, bf16_bits_to_f32
+
+F32 = np.float32
+
+
+def test_pack_fields_by_hand():
+    # 2-bit fields 1,2,3,0 -> 0b00_11_10_01
+    assert layout.pack_fields([1, 2, 3, 0], 2).tolist() == [0b00111001]
+    # 4-bit fields 0xA, 0x5, 0xF, 0x1 -> bytes 0x5A, 0x1F
+    assert layout.pack_fields([0xA, 0x5, 0xF, 0x1], 4).tolist() == [0x5A, 0x1F]
+    assert layout.pack_fields([7, 200], 8).tolist() == [7, 200]
+    # two's complement 4-bit: -1 -> 0xF, -7 -> 0x9
+    assert layout.pack_fields([-1, -7], 4).tolist() == [0x9F]
+    rng = np.random.default_rng(0)
+    for b in (2, 4, 8):
+        c = rng.integers(0, 2 ** b, 256)
+        assert np.array_equal(layout.unpack_fields(layout.pack_fields(c, b), b, 256), c)
+
+
+def test_bf16_bits():
+    assert bf16_bits_to_f32(np.array([0x3F80, 0xC000, 0x0000, 0x8000], np.uint16)).tolist() == \
+        [1.0, -2.0, 0.0, -0.0]
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_kivi_page_roundtrip(bits):
+    rng = np.random.default_rng(bits)
+    d = 64
+    k = rng.standard_normal((32, d)).astype(F32)
+    v = rng.standard_normal((32, d)).astype(F32)
+    buf, mask = layout.kivi_page(k, v, bits)
+    assert buf.size == acc.page_bytes(acc.KIVI, d, bits) and np.all(mask == 0xFF)
+    nb = 32 * d * bits // 8
+    kc = layout.unpack_fields(buf[:nb], bits, 32 * d).reshape(32, d)
+    ks = buf[nb:nb + 4 * d].view(F32)
+    kz = buf[nb + 4 * d:nb + 8 * d].view(F32)
+    o = nb + 8 * d
+    vcols = layout.unpack_fields(buf[o:o + nb], bits, 32 * d).reshape(d, 32)
+    vs = buf[o + nb:o + nb + 128].view(F32)
+    vz = buf[o + nb + 128:o + nb + 256].view(F32)
+    # keys: one scale per channel; values: one per token
+    assert np.array_equal(kz, k.min(axis=0)) and np.array_equal(vz, v.min(axis=1))
+    kh = kc * ks.astype(np.float64) + kz
+    vh = vcols.T * vs.astype(np.float64)[:, None] + vz[:, None]
+    assert np.all(np.abs(kh - k) <= ks / 2 * (1 + 1e-5))
+    assert np.all(np.abs(vh - v) <= vs[:, None] / 2 * (1 + 1e-5))
+    # an element in token 3, channel 5 sits at field 3*d+5 (K) and 5*32+3 (V)
+    c, s, z = codec.kivi_quantize(k, bits, axis=0)
+    assert kc[3, 5] == c[3, 5]
+    c, s, z = codec.kivi_quantize(v, bits, axis=1)
+    assert vcols[5, 3] == c[3, 5]
+
+
+def test_sym_and_fp8_partial_page_masks():
+    rng = np.random.default_rng(1)
+    k = rng.standard_normal((32, 32)).astype(F32)
+    v = rng.standard_normal((32, 32)).astype(F32)
+    buf, mask = layout.sym_page(k, v, 4, 5)
+    assert buf.size == mask.size == acc.page_bytes(acc.SYM_TOKEN, 32, 4)
+    row = 32 * 4 // 8
+    assert np.all(mask[:5 * row] == 0xFF) and np.all(mask[5 * row:32 * row] == 0)
+    kc = layout.unpack_fields(buf[:5 * row], 4, 5 * 32)
+    kc = np.where(kc > 7, kc - 16, kc).reshape(5, 32)
+    c, s = codec.sym_quantize(k[:5], 4, axis=1)
+    assert np.array_equal(kc, c)
+    # V cols: first 5 of each channel's 32 four-bit fields defined -> 0xFF,0xFF,0x0F,0...
+    vmask = mask[32 * row + 128: 32 * row + 128 + 16]
+    assert vmask.tolist() == [0xFF, 0xFF, 0x0F] + [0] * 13
+    buf, mask = layout.fp8_page(k, v, F32(0.5), F32(2.0), 31)
+    assert buf.size == 2048 and mask.sum() == 0xFF * 31 * 32 * 2
+    assert mask[32 * 31 + 1] == 0 and mask[32 * 30 + 1] == 0xFF
+    assert buf[32 * 30 + 1] == codec.fp8_quantize(k[30, 1], F32(0.5))
+    assert buf[1024 + 7 * 32 + 30] == codec.fp8_quantize(v[30, 7], F32(2.0))
+
+
+def _bf16(rng, *shape):
+    return (rng.standard_normal(shape).astype(F32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_kivi_cache_ring_and_pages():
+    rng = np.random.default_rng(2)
+    B, H, d, R, T = 2, 2, 32, 8, 77
+    c = OracleCache(acc.KIVI, 2, 1, B, H, d, capacity=96, residual=R, in_dtype="bf16")
+    k, v = _bf16(rng, B, T, H, d), _bf16(rng, B, T, H, d)
+    c.append(0, k, v)
+    q, n_r = acc.flush_plan(T, R)
+    assert (q, n_r) == (64, 13)
+    buf, mask = c.slab_image(0, 1, 1)
+    ps = acc.page_bytes(acc.KIVI, d, 2)
+    n_pages = acc.pages_per_slab(acc.KIVI, 96, R)
+    assert n_pages == 2 and np.all(mask[:2 * ps] == 0xFF)
+    ring0 = n_pages * ps
+    row = d * 2
+    for t in range(q, T):
+        s = t % (R + 32)
+        assert buf[ring0 + s * row: ring0 + (s + 1) * row].view(np.uint16).tolist() == \
+            k[1, t, 1].tolist()
+        vo = ring0 + (R + 32 + s) * row
+        assert buf[vo:vo + row].view(np.uint16).tolist() == v[1, t, 1].tolist()
+    assert mask[ring0:].sum() == 0xFF * 2 * n_r * row
+    # page 1 holds tokens 32..63
+    pb, _ = layout.kivi_page(bf16_bits_to_f32(k[1, 32:64, 1]), bf16_bits_to_f32(v[1, 32:64, 1]), 2)
+    assert np.array_equal(buf[ps:2 * ps], pb)
+
+
+def test_cache_chunking_independent():
+    rng = np.random.default_rng(3)
+    B, H, d = 1, 2, 32
+    k, v = _bf16(rng, B, 100, H, d), _bf16(rng, B, 100, H, d)
+    one = OracleCache(acc.KIVI, 4, 1, B, H, d, 128, residual=16)
+    one.append(0, k, v)
+    many = OracleCache(acc.KIVI, 4, 1, B, H, d, 128, residual=16)
+    for a, b in [(0, 1), (1, 33), (33, 34), (34, 90), (90, 100)]:
+        many.append(0, k[:, a:b], v[:, a:b])
+    b1, m1 = one.cache_image()
+    b2, m2 = many.cache_image()
+    assert np.array_equal(m1, m2) and np.array_equal(b1 & m1, b2 & m2)
+
+
+def test_cache_dequant_matches_pages():
+    """dequantized() (used for attention) agrees with decoding the byte image."""
+    rng = np.random.default_rng(4)
+    B, H, d = 1, 1, 32
+    k, v = _bf16(rng, B, 70, H, d), _bf16(rng, B, 70, H, d)
+    c = OracleCache(acc.KIVI, 2, 1, B, H, d, 80, residual=4)
+    c.append(0, k, v)
+    kh, vh = c.dequantized(0)
+    buf, _ = c.slab_image(0, 0, 0)
+    ps = acc.page_bytes(acc.KIVI, d, 2)
+    nb = 32 * d * 2 // 8
+    for p in range(2):
+        pg = buf[p * ps:(p + 1) * ps]
+        kc = layout.unpack_fields(pg[:nb], 2, 32 * d).reshape(32, d)
+        ks, kz = pg[nb:nb + 4 * d].view(F32), pg[nb + 4 * d:nb + 8 * d].view(F32)
+        assert np.array_equal(kh[0, 0, p * 32:(p + 1) * 32], kc * ks.astype(np.float64) + kz)
+    assert np.array_equal(kh[0, 0, 64:], bf16_bits_to_f32(k[0, 64:, 0]))   # ring exact
+    assert np.array_equal(vh[0, 0, 64:], bf16_bits_to_f32(v[0, 64:, 0]))
+
+
+def test_cache_decode_small():
+    rng = np.random.default_rng(5)
+    B, H, Hq, d = 2, 2, 4, 32
+    c = OracleCache(acc.SYM_TOKEN, 8, 1, B, H, d, 64, in_dtype="f32")
+    k = rng.standard_normal((B, 40, H, d)).astype(F32)
+    v = rng.standard_normal((B, 40, H, d)).astype(F32)
+    c.append(0, k, v)
+    q = rng.standard_normal((B, Hq, d))
+    out = c.decode(0, q)
+    kh, vh = c.dequantized(0)
+    # 8-bit symmetric is close to the unquantised attention
+    from oracle import attention
+    ref = attention.decode(q, np.transpose(k, (0, 2, 1, 3)), np.transpose(v, (0, 2, 1, 3)),
+                           1 / np.sqrt(d))
+    assert np.max(np.abs(out - ref)) < 0.02
+    assert np.allclose(out[1, 2], attention.attend(q[1, 2], kh[1, 1], vh[1, 1], 1 / np.sqrt(d)))
