@@ -52,6 +52,13 @@ extern "C" {
 
 #define KVQ_ABI_VERSION 1
 
+/* Exported entry points (the library is built with hidden visibility). */
+#if defined(__GNUC__)
+#define KVQ_API __attribute__((visibility("default")))
+#else
+#define KVQ_API
+#endif
+
 /* ---- status codes ------------------------------------------------------ */
 #define KVQ_OK               0
 #define KVQ_ERR_NULL        -1  /* a required pointer is NULL                */
@@ -96,11 +103,11 @@ typedef struct kvq_config {
   int32_t  scheme;       /* KVQ_KIVI / KVQ_SYM_TOKEN / KVQ_FP8_E4M3         */
   int32_t  bits;         /* 2, 4 or 8 (8 for FP8)                           */
   int32_t  layers;       /* >= 1                                            */
-  int32_t  q_heads;      /* multiple of kv_heads; q_heads/kv_heads in 1..16 */
-  int32_t  kv_heads;     /* >= 1                                            */
+  int32_t  q_heads;      /* kv_heads * {1, 2, 4, 8}                        */
+  int32_t  kv_heads;     /* 1..65535                                        */
   int32_t  head_dim;     /* 32, 64, 128 or 256                              */
-  int32_t  batch;        /* sequences; all share one length in this ABI     */
-  int64_t  max_tokens;   /* capacity per sequence                           */
+  int32_t  batch;        /* 1..65535 sequences, all of one length           */
+  int64_t  max_tokens;   /* capacity per sequence, < 2^36                   */
   int32_t  group;        /* tokens per page / key group; must be 32         */
   int32_t  residual;     /* KIVI: R >= 0 newest tokens kept unquantised;
                             must be 0 for SYM_TOKEN and FP8                 */
@@ -179,7 +186,7 @@ typedef struct kvq_config {
  *   KVQ_BYTES_WORKSPACE: decode workspace needed by a call over `tokens`
  *                        cached tokens (monotone in `tokens`).
  * Returns the byte count (>= 0) or a negative status. */
-int64_t kvq_cache_bytes(const kvq_config* cfg, int64_t tokens, int32_t kind);
+KVQ_API int64_t kvq_cache_bytes(const kvq_config* cfg, int64_t tokens, int32_t kind);
 
 /* Quantize-append: append `new_tokens` tokens to every sequence of `layer`.
  *   cache        device, >= kvq_cache_bytes(cfg, max_tokens, KVQ_BYTES_CACHE)
@@ -192,7 +199,7 @@ int64_t kvq_cache_bytes(const kvq_config* cfg, int64_t tokens, int32_t kind);
  * new_tokens == 0 is a no-op. Appending in any chunking (one call of T tokens
  * or T calls of one token) leaves identical bytes in every defined field.
  * Steps [QKV] going deeper; [KIVI] How It Works; [QC] Workshop; [QKV] FP8. */
-int32_t kvq_quantize_append(const kvq_config* cfg, void* cache, int32_t layer,
+KVQ_API int32_t kvq_quantize_append(const kvq_config* cfg, void* cache, int32_t layer,
                             int64_t past_tokens, int64_t new_tokens,
                             const void* k_new, const void* v_new,
                             const float* k_scale, const float* v_scale,
@@ -214,17 +221,17 @@ int32_t kvq_quantize_append(const kvq_config* cfg, void* cache, int32_t layer,
  *              it zero-filled again
  * Requires 1 <= tokens <= max_tokens and that the cache holds `tokens` tokens.
  */
-int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache,
+KVQ_API int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache,
                              int32_t layer, int64_t tokens, const void* q,
                              const float* k_scale, const float* v_scale,
                              float* out, void* workspace,
                              size_t workspace_bytes, void* stream);
 
 /* Static description of a status code (never NULL). */
-const char* kvq_status_string(int32_t status);
+KVQ_API const char* kvq_status_string(int32_t status);
 
 /* KVQ_ABI_VERSION of the built library. */
-int32_t kvq_abi_version(void);
+KVQ_API int32_t kvq_abi_version(void);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,363 @@
+// Quantize-append kernels.
+//
+// KIVI ("Quantizing the KV cache", going deeper: Q_b and s; "Keys and values
+// are shaped differently"; KIVI How It Works): when the unquantised window
+// holds R+32 tokens, its oldest 32 are encoded as one page -- keys per channel
+// over the 32 tokens, values per token over the head's channels -- and the
+// newest tokens are copied bit-exactly into the residual ring. A page being
+// encoded may draw tokens from the ring (appended by earlier calls) and from
+// this call's input, so the flush runs before the ring is overwritten: two
+// launches in stream order.
+//
+// SYM_TOKEN ("Quantising the Cache.", Workshop) and FP8_E4M3 ("Quantizing the
+// KV cache", FP8 KV cache with per-head scales): every new token is encoded on
+// arrival into the page that holds it; value codes are channel-major inside a
+// page, so a partially filled page is updated with read-modify-write of the
+// words that carry the new tokens' fields (each word owned by one thread).
+//
+// All encoding arithmetic is fp32 with IEEE division and rintf (ties to
+// even); the library is compiled with -ffp-contract=off so no FMA is formed.
+#include <hip/hip_runtime.h>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kThreads = 256;
+
+struct AppendParams {
+  uint8_t* layer_base;
+  const uint8_t* k_new;
+  const uint8_t* v_new;
+  const float* k_scale;
+  const float* v_scale;
+  int64_t slab_bytes, page_bytes, ring_base;  // ring_base = P * page_bytes
+  int64_t past, n;
+  int64_t first_page;                         // first page written by this launch
+  int64_t ring_slots;
+  int32_t kv_heads;
+  int32_t off_kc, off_ks, off_kz, off_vc, off_vs, off_vz;
+};
+
+// Loads one token row of D elements (bf16 or f32 bytes) into an LDS row.
+template <int D, int IB>
+__device__ __forceinline__ void stage_row_chunk(const uint8_t* src, float* dst, int chunk) {
+  if constexpr (IB == 2) {
+    const uint4 v = *reinterpret_cast<const uint4*>(src + chunk * 16);
+    float f[8];
+    unpack_bf16x8(v, f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[chunk * 8 + i] = f[i];
+  } else {
+    const float4 v = *reinterpret_cast<const float4*>(src + chunk * 16);
+    dst[chunk * 4 + 0] = v.x;
+    dst[chunk * 4 + 1] = v.y;
+    dst[chunk * 4 + 2] = v.z;
+    dst[chunk * 4 + 3] = v.w;
+  }
+}
+
+// ---- KIVI: encode one 32-token page per block --------------------------------
+// grid = (pages to flush, kv_heads, batch)
+template <int D, int BITS, int IB>
+__global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
+  constexpr int LD = D + 1;                   // padded LDS row (no bank conflicts on columns)
+  constexpr float kLevels = float((1 << BITS) - 1);
+  constexpr int FPW = 32 / BITS;              // fields per 32-bit word
+  constexpr int CHUNKS = D * IB / 16;         // 16-byte chunks per row
+  __shared__ float ks_tile[kPage * LD];
+  __shared__ float vs_tile[kPage * LD];
+  __shared__ float k_mn[D], k_s[D], v_mn[kPage], v_s[kPage];
+
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t page = p.first_page + blockIdx.x;
+  uint8_t* slab = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes;
+  uint8_t* pg = slab + page * p.page_bytes;
+  const int64_t row_bytes = static_cast<int64_t>(D) * IB;
+
+  // 1. stage the page's 32 key and value rows (ring for tokens < past, else input)
+  for (int i = tid; i < 2 * kPage * CHUNKS; i += kThreads) {
+    const int which = i / (kPage * CHUNKS);   // 0 = K, 1 = V
+    const int r = (i / CHUNKS) % kPage;
+    const int c = i % CHUNKS;
+    const int64_t t = page * kPage + r;
+    const uint8_t* src;
+    if (t < p.past) {
+      const int64_t slot = t % p.ring_slots;
+      src = slab + p.ring_base + (which * p.ring_slots + slot) * row_bytes;
+    } else {
+      const int64_t j = t - p.past;
+      const uint8_t* base = which ? p.v_new : p.k_new;
+      src = base + ((static_cast<int64_t>(b) * p.n + j) * p.kv_heads + h) * row_bytes;
+    }
+    stage_row_chunk<D, IB>(src, (which ? vs_tile : ks_tile) + r * LD, c);
+  }
+  __syncthreads();
+
+  // 2. statistics: per key channel over the tokens, per value token over channels
+  for (int i = tid; i < D + kPage; i += kThreads) {
+    if (i < D) {
+      float mn = ks_tile[i], mx = ks_tile[i];
+      for (int r = 1; r < kPage; ++r) {
+        const float x = ks_tile[r * LD + i];
+        mn = fminf(mn, x);
+        mx = fmaxf(mx, x);
+      }
+      mn = mn + 0.0f;                          // -0 -> +0
+      const float s = (mx - mn) / kLevels;
+      k_mn[i] = mn;
+      k_s[i] = s;
+      reinterpret_cast<float*>(pg + p.off_ks)[i] = s;
+      reinterpret_cast<float*>(pg + p.off_kz)[i] = mn;
+    } else {
+      const int r = i - D;
+      float mn = vs_tile[r * LD], mx = mn;
+      for (int c = 1; c < D; ++c) {
+        const float x = vs_tile[r * LD + c];
+        mn = fminf(mn, x);
+        mx = fmaxf(mx, x);
+      }
+      mn = mn + 0.0f;
+      const float s = (mx - mn) / kLevels;
+      v_mn[r] = mn;
+      v_s[r] = s;
+      reinterpret_cast<float*>(pg + p.off_vs)[r] = s;
+      reinterpret_cast<float*>(pg + p.off_vz)[r] = mn;
+    }
+  }
+  __syncthreads();
+
+  // 3. codes. K rows: field f = token*D + channel. V cols: field f = channel*32 + token.
+  constexpr int WORDS = kPage * D * BITS / 32;
+  uint32_t* kc = reinterpret_cast<uint32_t*>(pg + p.off_kc);
+  uint32_t* vc = reinterpret_cast<uint32_t*>(pg + p.off_vc);
+  for (int w = tid; w < WORDS; w += kThreads) {
+    const int f0 = w * FPW;
+    const int t = f0 / D, c0 = f0 % D;
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < FPW; ++j) {
+      const int c = c0 + j;
+      word |= quant_asym(ks_tile[t * LD + c], k_mn[c], k_s[c], kLevels) << (j * BITS);
+    }
+    kc[w] = word;
+  }
+  for (int w = tid; w < WORDS; w += kThreads) {
+    const int f0 = w * FPW;
+    const int c = f0 / kPage, t0 = f0 % kPage;
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < FPW; ++j) {
+      const int t = t0 + j;
+      word |= quant_asym(vs_tile[t * LD + c], v_mn[t], v_s[t], kLevels) << (j * BITS);
+    }
+    vc[w] = word;
+  }
+}
+
+// ---- KIVI: copy tokens [t0, past+n) of the input into their ring slots --------
+// grid = (tokens, kv_heads, batch), one 16-byte chunk per thread
+template <int D, int IB>
+__global__ __launch_bounds__(64) void ring_write_kernel(AppendParams p, int64_t t0) {
+  constexpr int CHUNKS = D * IB / 16;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t t = t0 + blockIdx.x;
+  const int64_t j = t - p.past;
+  const int64_t row_bytes = static_cast<int64_t>(D) * IB;
+  uint8_t* slab = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes;
+  const int64_t slot = t % p.ring_slots;
+  const int64_t in_off = ((static_cast<int64_t>(b) * p.n + j) * p.kv_heads + h) * row_bytes;
+  for (int i = threadIdx.x; i < 2 * CHUNKS; i += 64) {
+    const int which = i / CHUNKS, c = i % CHUNKS;
+    const uint8_t* src = (which ? p.v_new : p.k_new) + in_off + c * 16;
+    uint8_t* dst = slab + p.ring_base + (which * p.ring_slots + slot) * row_bytes + c * 16;
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+  }
+}
+
+// ---- SYM_TOKEN / FP8_E4M3: encode the new tokens of one page per block ------
+// grid = (pages touched, kv_heads, batch)
+template <int SCHEME, int D, int BITS, int IB>
+__global__ __launch_bounds__(kThreads) void token_append_kernel(AppendParams p) {
+  constexpr int LD = D + 1;
+  constexpr int FPW = 32 / BITS;
+  constexpr int CHUNKS = D * IB / 16;
+  constexpr uint32_t kMask = (1u << BITS) - 1u;  // BITS < 32
+  constexpr float kQmax = float((1 << (BITS - 1)) - 1);
+  __shared__ float ktile[kPage * LD];
+  __shared__ float vtile[kPage * LD];
+  __shared__ float k_sc[kPage], v_sc[kPage];
+
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t page = p.first_page + blockIdx.x;
+  const int64_t end = p.past + p.n;
+  const int lo = static_cast<int>((p.past > page * kPage ? p.past : page * kPage) - page * kPage);
+  const int hi = static_cast<int>((end < page * kPage + kPage ? end : page * kPage + kPage) -
+                                  page * kPage);
+  uint8_t* slab = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes;
+  uint8_t* pg = slab + page * p.page_bytes;
+  const int64_t row_bytes = static_cast<int64_t>(D) * IB;
+
+  for (int i = tid; i < 2 * (hi - lo) * CHUNKS; i += kThreads) {
+    const int which = i / ((hi - lo) * CHUNKS);
+    const int r = lo + (i / CHUNKS) % (hi - lo);
+    const int c = i % CHUNKS;
+    const int64_t j = page * kPage + r - p.past;
+    const uint8_t* src = (which ? p.v_new : p.k_new) +
+                         ((static_cast<int64_t>(b) * p.n + j) * p.kv_heads + h) * row_bytes;
+    stage_row_chunk<D, IB>(src, (which ? vtile : ktile) + r * LD, c);
+  }
+  __syncthreads();
+
+  if constexpr (SCHEME == KVQ_SYM_TOKEN) {
+    // one scale per (token, head) for K and for V: s = max|x| / Q
+    for (int i = tid; i < 2 * kPage; i += kThreads) {
+      const int which = i / kPage, r = i % kPage;
+      if (r < lo || r >= hi) continue;
+      const float* row = (which ? vtile : ktile) + r * LD;
+      float a = fabsf(row[0]);
+      for (int c = 1; c < D; ++c) a = fmaxf(a, fabsf(row[c]));
+      const float s = a / kQmax;
+      (which ? v_sc : k_sc)[r] = s;
+      reinterpret_cast<float*>(pg + (which ? p.off_vs : p.off_ks))[r] = s;
+    }
+  } else {
+    if (tid < kPage) {
+      k_sc[tid] = p.k_scale[h];
+      v_sc[tid] = p.v_scale[h];
+    }
+  }
+  __syncthreads();
+
+  auto encode = [&](float x, float s) -> uint32_t {
+    if constexpr (SCHEME == KVQ_SYM_TOKEN) {
+      return quant_sym(x, s, kQmax, kMask);
+    } else {
+      return e4m3_encode(x / s);
+    }
+  };
+
+  // K rows of the new tokens: whole words
+  constexpr int ROW_WORDS = D * BITS / 32;
+  uint32_t* kc = reinterpret_cast<uint32_t*>(pg + p.off_kc);
+  for (int i = tid; i < (hi - lo) * ROW_WORDS; i += kThreads) {
+    const int r = lo + i / ROW_WORDS;
+    const int c0 = (i % ROW_WORDS) * FPW;
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < FPW; ++j) word |= encode(ktile[r * LD + c0 + j], k_sc[r]) << (j * BITS);
+    kc[r * ROW_WORDS + i % ROW_WORDS] = word;
+  }
+  // V cols: per channel, the words that hold fields of tokens [lo, hi)
+  constexpr int COL_WORDS = kPage * BITS / 32;
+  const int w_lo = lo / FPW, w_hi = (hi - 1) / FPW + 1;
+  uint32_t* vc = reinterpret_cast<uint32_t*>(pg + p.off_vc);
+  for (int i = tid; i < D * (w_hi - w_lo); i += kThreads) {
+    const int c = i / (w_hi - w_lo);
+    const int w = w_lo + i % (w_hi - w_lo);
+    uint32_t word = 0, mask = 0;
+#pragma unroll
+    for (int j = 0; j < FPW; ++j) {
+      const int t = w * FPW + j;
+      if (t >= lo && t < hi) {
+        word |= encode(vtile[t * LD + c], v_sc[t]) << (j * BITS);
+        mask |= kMask << (j * BITS);
+      }
+    }
+    uint32_t* dst = vc + c * COL_WORDS + w;
+    *dst = mask == 0xffffffffu ? word : ((*dst & ~mask) | word);
+  }
+}
+
+// ---- dispatch ---------------------------------------------------------------
+
+template <int D, int BITS, int IB>
+hipError_t run_kivi(const AppendArgs& a, const AppendParams& base, hipStream_t st) {
+  const Geometry& g = a.g;
+  const int64_t end = a.past + a.n;
+  const int64_t q_old = kivi_quantised(a.past, g.residual);
+  const int64_t q_new = kivi_quantised(end, g.residual);
+  AppendParams p = base;
+  if (q_new > q_old) {
+    p.first_page = q_old / kPage;
+    dim3 grid(static_cast<unsigned>((q_new - q_old) / kPage), g.kv_heads, g.batch);
+    hipLaunchKernelGGL((kivi_flush_kernel<D, BITS, IB>), grid, dim3(kThreads), 0, st, p);
+  }
+  const int64_t t0 = q_new > a.past ? q_new : a.past;
+  if (end > t0) {
+    dim3 grid(static_cast<unsigned>(end - t0), g.kv_heads, g.batch);
+    hipLaunchKernelGGL((ring_write_kernel<D, IB>), grid, dim3(64), 0, st, p, t0);
+  }
+  return hipGetLastError();
+}
+
+template <int SCHEME, int D, int BITS, int IB>
+hipError_t run_token(const AppendArgs& a, const AppendParams& base, hipStream_t st) {
+  const Geometry& g = a.g;
+  AppendParams p = base;
+  p.first_page = a.past / kPage;
+  const int64_t last = (a.past + a.n - 1) / kPage;
+  dim3 grid(static_cast<unsigned>(last - p.first_page + 1), g.kv_heads, g.batch);
+  hipLaunchKernelGGL((token_append_kernel<SCHEME, D, BITS, IB>), grid, dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+template <int D, int IB>
+hipError_t dispatch_bits(const AppendArgs& a, const AppendParams& p, hipStream_t st) {
+  const Geometry& g = a.g;
+  if (g.scheme == KVQ_FP8_E4M3) return run_token<KVQ_FP8_E4M3, D, 8, IB>(a, p, st);
+  if (g.scheme == KVQ_SYM_TOKEN) {
+    switch (g.bits) {
+      case 2: return run_token<KVQ_SYM_TOKEN, D, 2, IB>(a, p, st);
+      case 4: return run_token<KVQ_SYM_TOKEN, D, 4, IB>(a, p, st);
+      default: return run_token<KVQ_SYM_TOKEN, D, 8, IB>(a, p, st);
+    }
+  }
+  switch (g.bits) {
+    case 2: return run_kivi<D, 2, IB>(a, p, st);
+    case 4: return run_kivi<D, 4, IB>(a, p, st);
+    default: return run_kivi<D, 8, IB>(a, p, st);
+  }
+}
+
+template <int D>
+hipError_t dispatch_dtype(const AppendArgs& a, const AppendParams& p, hipStream_t st) {
+  return a.g.in_bytes == 2 ? dispatch_bits<D, 2>(a, p, st) : dispatch_bits<D, 4>(a, p, st);
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
+  const Geometry& g = a.g;
+  AppendParams p{};
+  p.layer_base = a.layer_base;
+  p.k_new = static_cast<const uint8_t*>(a.k_new);
+  p.v_new = static_cast<const uint8_t*>(a.v_new);
+  p.k_scale = a.k_scale;
+  p.v_scale = a.v_scale;
+  p.slab_bytes = g.slab_bytes;
+  p.page_bytes = g.page_bytes;
+  p.ring_base = g.pages_per_slab * g.page_bytes;
+  p.past = a.past;
+  p.n = a.n;
+  p.ring_slots = g.ring_slots > 0 ? g.ring_slots : 1;
+  p.kv_heads = g.kv_heads;
+  p.off_kc = g.off_kc;
+  p.off_ks = g.off_ks;
+  p.off_kz = g.off_kz;
+  p.off_vc = g.off_vc;
+  p.off_vs = g.off_vs;
+  p.off_vz = g.off_vz;
+  switch (g.d) {
+    case 32: return dispatch_dtype<32>(a, p, st);
+    case 64: return dispatch_dtype<64>(a, p, st);
+    case 128: return dispatch_dtype<128>(a, p, st);
+    default: return dispatch_dtype<256>(a, p, st);
+  }
+}
+
+}  // namespace kvq

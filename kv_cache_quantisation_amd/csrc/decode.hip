@@ -1,0 +1,478 @@
+// Decode attention straight from the packed cache.
+//
+// out[b][h] = sum_t p_t V^_t with p = softmax(sm_scale q[b][h] . K^_t) over all
+// cached tokens ("Quantizing the KV cache", going deeper: "Why values per
+// token"); K^, V^ are the dequantised cache; query head h reads KV head
+// h / (q_heads/kv_heads) (grouped-query attention, same page). With a rotary
+// base the dequantised key at position t and the query at position T-1 are
+// rotated (KVQuant Summary: keys cached before RoPE).
+//
+// Work split: for each (sequence, KV head) the pages (32 tokens each) and, for
+// KIVI, the residual-ring chunks (32 tokens each) form a list of work items.
+// The list is cut into `splits` contiguous ranges, one block of 4 waves per
+// range; waves take items round-robin. Each wave keeps an online softmax
+// (running max m, running sum l, unnormalised output o) for the GQA group of
+// query heads; the waves are combined in LDS and the block writes one partial
+// (m, l, o). A second kernel merges the partials of a (sequence, query head):
+// M = max m_s, out = sum 2^(m_s-M) o_s / sum 2^(m_s-M) l_s. Scores are kept in
+// the log2 domain (the query is pre-scaled by sm_scale*log2(e)).
+//
+// Folding the scales out of the inner loops:
+//   KIVI keys:   q.k^ = sum_c (q_c s_c) code_tc + sum_c q_c z_c  (per page)
+//   KIVI values: sum_t p_t (code_tc s_t + z_t) = sum_t (p_t s_t) code_tc + sum_t p_t z_t
+//   SYM:         q.k^ = s_t sum_c q_c code_tc;   values: p_t s_t
+//   FP8:         the per-head key scale goes into q, the value scale into out.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct DecodeParams {
+  const uint8_t* layer_base;
+  const uint8_t* q;
+  const float* k_scale;
+  const float* v_scale;
+  float* out;
+  float* partials;
+  int64_t slab_bytes, page_bytes, ring_base, ring_slots;
+  int64_t T, q_tokens;  // cached tokens; tokens held in pages
+  int32_t n_pages, items, splits;
+  int32_t kv_heads, q_heads;
+  int32_t off_kc, off_ks, off_kz, off_vc, off_vs, off_vz;
+  int32_t q_bf16, in_bf16;
+  float qscale;         // sm_scale * log2(e)
+  double rope_theta;    // 0 = off
+};
+
+template <int BITS>
+__device__ __forceinline__ float ucode(uint32_t w, int j) {
+  return static_cast<float>((w >> (j * BITS)) & ((1u << BITS) - 1u));
+}
+
+template <int BITS>
+__device__ __forceinline__ float scode(uint32_t w, int j) {
+  const int32_t v = static_cast<int32_t>(w << (32 - (j + 1) * BITS)) >> (32 - BITS);
+  return static_cast<float>(v);
+}
+
+// Value of the j-th field of word w under the scheme's code type.
+template <int SCHEME, int BITS>
+__device__ __forceinline__ float code_value(uint32_t w, int j) {
+  if constexpr (SCHEME == KVQ_KIVI) return ucode<BITS>(w, j);
+  else if constexpr (SCHEME == KVQ_SYM_TOKEN) return scode<BITS>(w, j);
+  else return e4m3_decode((w >> (8 * j)) & 0xFFu);
+}
+
+__device__ __forceinline__ float load_elem(const uint8_t* base, int64_t idx, int bf16) {
+  if (bf16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
+  return reinterpret_cast<const float*>(base)[idx];
+}
+
+// Rotates (x0, x1) by 2*pi*frac(pos * w2pi).
+__device__ __forceinline__ void rope_pair(float& x0, float& x1, int64_t pos, double w2pi) {
+  const double turns = static_cast<double>(pos) * w2pi;
+  const float f = static_cast<float>(turns - floor(turns));
+  float s, c;
+  sincospif(2.0f * f, &s, &c);
+  const float y0 = x0 * c - x1 * s;
+  const float y1 = x0 * s + x1 * c;
+  x0 = y0;
+  x1 = y1;
+}
+
+template <int SCHEME, int BITS, int D, int HG>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
+  constexpr int CPL = D >= 64 ? D / 64 : 1;  // channels per lane in the P.V phase
+  constexpr int LPC = D / CPL;                // lanes per token subset (64 or 32)
+  constexpr int TSUB = 64 / LPC;              // token subsets (1, or 2 when D == 32)
+  constexpr int TPS = kPage / TSUB;           // tokens per subset
+  constexpr int HALF = D / 2;                 // channels per lane in the score phase
+  constexpr int FPW = 32 / BITS;              // fields per 32-bit word
+  constexpr int QROWS = HG > 2 ? HG : 2;
+  constexpr int WQ = kWaves * QROWS * D;
+  constexpr int RED = kWaves * HG * (D + 2);
+  constexpr int SCRATCH = WQ > RED ? WQ : RED;
+
+  __shared__ float qs[HG][D];
+  __shared__ float scratch[SCRATCH];          // per-wave folded query / scales; later the combine
+  __shared__ float wp[kWaves][HG][kPage];
+  __shared__ double w2pi[D / 2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int tok = lane & 31, hf = lane >> 5;
+  const int cs = lane % LPC, ts = lane / LPC;
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const bool rope = p.rope_theta > 0.0;
+  const uint8_t* slab = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes;
+  float* wq = scratch + wave * QROWS * D;
+
+  // ---- stage the GQA group's query: rotate at T-1, scale ----------------------
+  if (rope) {
+    for (int i = tid; i < D / 2; i += kThreads)
+      w2pi[i] = pow(p.rope_theta, -2.0 * i / D) * 0.15915494309189535;  // omega / (2 pi)
+    __syncthreads();
+  }
+  {
+    const float ks_h = SCHEME == KVQ_FP8_E4M3 ? p.k_scale[h] : 1.0f;
+    const float mult = p.qscale * ks_h;
+    for (int i = tid; i < HG * D / 2; i += kThreads) {
+      const int g = i / (D / 2), pr = i % (D / 2);
+      const int64_t base = (static_cast<int64_t>(b) * p.q_heads + h * HG + g) * D + 2 * pr;
+      float x0 = load_elem(p.q, base, p.q_bf16);
+      float x1 = load_elem(p.q, base + 1, p.q_bf16);
+      if (rope) {
+        const double ang = static_cast<double>(p.T - 1) * (w2pi[pr] * 6.283185307179586);
+        const double sn = sin(ang), cn = cos(ang);
+        const double y0 = x0 * cn - x1 * sn, y1 = x0 * sn + x1 * cn;
+        x0 = static_cast<float>(y0);
+        x1 = static_cast<float>(y1);
+      }
+      qs[g][2 * pr] = x0 * mult;
+      qs[g][2 * pr + 1] = x1 * mult;
+    }
+  }
+  __syncthreads();
+
+  // ---- item range of this split -------------------------------------------
+  const int i0 = static_cast<int>(static_cast<int64_t>(split) * p.items / p.splits);
+  const int i1 = static_cast<int>(static_cast<int64_t>(split + 1) * p.items / p.splits);
+  const int rounds = (i1 - i0 + kWaves - 1) / kWaves;
+
+  float m[HG], l_l[HG], z_l[HG], o[HG][CPL];
+#pragma unroll
+  for (int g = 0; g < HG; ++g) {
+    m[g] = -INFINITY;
+    l_l[g] = 0.f;
+    z_l[g] = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) o[g][c] = 0.f;
+  }
+
+  for (int r = 0; r < rounds; ++r) {
+    const int item = i0 + r * kWaves + wave;
+    const bool active = item < i1;
+    const bool is_page = item < p.n_pages;
+    const uint8_t* pg = slab + static_cast<int64_t>(item) * p.page_bytes;
+    const int64_t t_first = is_page ? static_cast<int64_t>(item) * kPage
+                                    : p.q_tokens + static_cast<int64_t>(item - p.n_pages) * kPage;
+    const int n_valid = static_cast<int>(p.T - t_first < kPage ? p.T - t_first : kPage);
+
+    __syncthreads();
+    // ---- prologue: per-page key scales ----------------------------------------
+    float bias[HG];
+#pragma unroll
+    for (int g = 0; g < HG; ++g) bias[g] = 0.f;
+    if (active && is_page && SCHEME == KVQ_KIVI) {
+      const float* ksp = reinterpret_cast<const float*>(pg + p.off_ks);
+      const float* kzp = reinterpret_cast<const float*>(pg + p.off_kz);
+      for (int c = lane; c < D; c += 64) {
+        const float s = ksp[c], z = kzp[c];
+        if (rope) {
+          wq[c] = s;
+          wq[D + c] = z;
+        } else {
+#pragma unroll
+          for (int g = 0; g < HG; ++g) {
+            const float qv = qs[g][c];
+            wq[g * D + c] = qv * s;
+            bias[g] = fmaf(qv, z, bias[g]);
+          }
+        }
+      }
+      if (!rope) {
+#pragma unroll
+        for (int g = 0; g < HG; ++g) bias[g] = wave_sum(bias[g]);
+      }
+    }
+    __syncthreads();
+
+    // ---- scores: lane = (token, channel half) ----------------------------------
+    float score[HG];
+    if (active) {
+      float acc[HG];
+#pragma unroll
+      for (int g = 0; g < HG; ++g) acc[g] = 0.f;
+      const bool valid = tok < n_valid;
+      if (is_page) {
+        // KIVI keys without rotation use the per-page folded query
+        const float* qsrc = (SCHEME == KVQ_KIVI && !rope) ? wq : &qs[0][0];
+        constexpr int NWORD = D * BITS / 64;   // words per half row
+        const uint32_t* kw = reinterpret_cast<const uint32_t*>(pg + p.off_kc) +
+                             tok * (D * BITS / 32) + hf * NWORD;
+        float kst = 1.0f;
+        if constexpr (SCHEME == KVQ_SYM_TOKEN)
+          kst = reinterpret_cast<const float*>(pg + p.off_ks)[tok];
+#pragma unroll
+        for (int wi = 0; wi < NWORD; ++wi) {
+          const uint32_t w = kw[wi];
+          const int c0 = hf * HALF + wi * FPW;
+          float kv[FPW];
+#pragma unroll
+          for (int j = 0; j < FPW; ++j) kv[j] = code_value<SCHEME, BITS>(w, j);
+          if (rope) {
+            if constexpr (SCHEME == KVQ_KIVI) {
+#pragma unroll
+              for (int j = 0; j < FPW; ++j) kv[j] = kv[j] * wq[c0 + j] + wq[D + c0 + j];
+            }
+#pragma unroll
+            for (int j = 0; j < FPW; j += 2)
+              rope_pair(kv[j], kv[j + 1], t_first + tok, w2pi[(c0 + j) / 2]);
+          }
+#pragma unroll
+          for (int j = 0; j < FPW; ++j) {
+#pragma unroll
+            for (int g = 0; g < HG; ++g)
+              acc[g] = fmaf(qsrc[g * D + c0 + j], kv[j], acc[g]);
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < HG; ++g) acc[g] *= kst;
+      } else {
+        // residual ring: exact input-dtype rows
+        const int64_t t = t_first + tok;
+        if (valid) {
+          const int64_t slot = t % p.ring_slots;
+          const uint8_t* row = slab + p.ring_base + slot * D * (p.in_bf16 ? 2 : 4);
+          for (int c = hf * HALF; c < hf * HALF + HALF; c += 2) {
+            float x0 = load_elem(row, c, p.in_bf16);
+            float x1 = load_elem(row, c + 1, p.in_bf16);
+            if (rope) rope_pair(x0, x1, t, w2pi[c / 2]);
+#pragma unroll
+            for (int g = 0; g < HG; ++g) acc[g] = fmaf(qs[g][c + 1], x1, fmaf(qs[g][c], x0, acc[g]));
+          }
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < HG; ++g) {
+        acc[g] += __shfl_xor(acc[g], 32, 64);
+        score[g] = valid ? acc[g] + bias[g] : -INFINITY;
+      }
+
+      // ---- online softmax --------------------------------------------------
+      float vsc = 1.0f, vz = 0.0f;
+      if (is_page && valid) {
+        if constexpr (SCHEME == KVQ_KIVI) {
+          vsc = reinterpret_cast<const float*>(pg + p.off_vs)[tok];
+          vz = reinterpret_cast<const float*>(pg + p.off_vz)[tok];
+        } else if constexpr (SCHEME == KVQ_SYM_TOKEN) {
+          vsc = reinterpret_cast<const float*>(pg + p.off_vs)[tok];
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < HG; ++g) {
+        const float mn = fmaxf(m[g], half_max(score[g]));
+        const float alpha = exp2f(m[g] - mn);
+        const float pe = exp2f(score[g] - mn);
+        m[g] = mn;
+        l_l[g] = l_l[g] * alpha + (hf == 0 ? pe : 0.f);
+        z_l[g] = z_l[g] * alpha + (hf == 0 ? pe * vz : 0.f);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) o[g][c] *= alpha;
+        if (hf == 0) wp[wave][g][tok] = valid ? pe * vsc : 0.f;
+      }
+    }
+    __syncthreads();
+
+    // ---- P.V: lane = (channel set, token subset) --------------------------------
+    if (active) {
+      if (is_page) {
+        constexpr int COLW = kPage * BITS / 32;   // words per channel column
+        constexpr int SUBW = TPS * BITS / 32;     // words per token subset
+#pragma unroll
+        for (int ci = 0; ci < CPL; ++ci) {
+          const int c = cs * CPL + ci;
+          const uint32_t* vw = reinterpret_cast<const uint32_t*>(pg + p.off_vc) + c * COLW +
+                               ts * SUBW;
+#pragma unroll
+          for (int wi = 0; wi < SUBW; ++wi) {
+            const uint32_t w = vw[wi];
+#pragma unroll
+            for (int j = 0; j < FPW; ++j) {
+              const float cv = code_value<SCHEME, BITS>(w, j);
+              const int t = ts * TPS + wi * FPW + j;
+#pragma unroll
+              for (int g = 0; g < HG; ++g) o[g][ci] = fmaf(wp[wave][g][t], cv, o[g][ci]);
+            }
+          }
+        }
+      } else {
+        const int ib = p.in_bf16 ? 2 : 4;
+        for (int j = 0; j < TPS; ++j) {
+          const int tl = ts * TPS + j;
+          if (tl >= n_valid) break;
+          const int64_t slot = (t_first + tl) % p.ring_slots;
+          const uint8_t* row = slab + p.ring_base + (p.ring_slots + slot) * D * ib;
+#pragma unroll
+          for (int ci = 0; ci < CPL; ++ci) {
+            const float x = load_elem(row, cs * CPL + ci, p.in_bf16);
+#pragma unroll
+            for (int g = 0; g < HG; ++g) o[g][ci] = fmaf(wp[wave][g][tl], x, o[g][ci]);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- combine the waves ----------------------------------------------------
+  __syncthreads();
+  float* red = scratch;  // [wave][g][D + 2]: m, l, o[D]
+#pragma unroll
+  for (int g = 0; g < HG; ++g) {
+    const float lw = wave_sum(l_l[g]);
+    const float zw = wave_sum(z_l[g]);
+    float* rw = red + (wave * HG + g) * (D + 2);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      float v = o[g][c];
+      if constexpr (TSUB == 2) v += __shfl_xor(v, 32, 64);
+      if (ts == 0) rw[2 + cs * CPL + c] = v + zw;
+    }
+    if (lane == 0) {
+      rw[0] = m[g];
+      rw[1] = lw;
+    }
+  }
+  __syncthreads();
+  const float vsc_h = SCHEME == KVQ_FP8_E4M3 ? p.v_scale[h] : 1.0f;
+  for (int i = tid; i < HG * D; i += kThreads) {
+    const int g = i / D, c = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red[(w * HG + g) * (D + 2)]);
+    float so = 0.f, sl = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float* rw = red + (w * HG + g) * (D + 2);
+      const float e = exp2f(rw[0] - M);  // empty wave: 2^-inf = 0
+      so = fmaf(e, rw[2 + c], so);
+      sl = fmaf(e, rw[1], sl);
+    }
+    so *= vsc_h;
+    const int hq = h * HG + g;
+    if (p.splits == 1) {
+      p.out[(static_cast<int64_t>(b) * p.q_heads + hq) * D + c] = so / sl;
+    } else {
+      float* part = p.partials +
+                    ((static_cast<int64_t>(b) * p.q_heads + hq) * p.splits + split) * (D + 2);
+      part[2 + c] = so;
+      if (c == 0) {
+        part[0] = M;
+        part[1] = sl;
+      }
+    }
+  }
+}
+
+// Merges the split partials of one (sequence, query head): grid = batch*q_heads.
+template <int D>
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
+  const int bh = blockIdx.x;
+  const float* part = p.partials + static_cast<int64_t>(bh) * p.splits * (D + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < p.splits; ++s) M = fmaxf(M, part[s * (D + 2)]);
+  float L = 0.f;
+  for (int s = 0; s < p.splits; ++s) L = fmaf(exp2f(part[s * (D + 2)] - M), part[s * (D + 2) + 1], L);
+  for (int c = threadIdx.x; c < D; c += 64) {
+    float acc = 0.f;
+    for (int s = 0; s < p.splits; ++s)
+      acc = fmaf(exp2f(part[s * (D + 2)] - M), part[s * (D + 2) + 2 + c], acc);
+    p.out[static_cast<int64_t>(bh) * D + c] = acc / L;
+  }
+}
+
+template <int SCHEME, int BITS, int D, int HG>
+hipError_t launch(const DecodeParams& p, int batch, hipStream_t st) {
+  dim3 grid(p.splits, p.kv_heads, batch);
+  hipLaunchKernelGGL((decode_split_kernel<SCHEME, BITS, D, HG>), grid, dim3(kThreads), 0, st, p);
+  if (p.splits > 1) {
+    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(batch * p.q_heads), dim3(64), 0, st, p);
+  }
+  return hipGetLastError();
+}
+
+template <int SCHEME, int BITS, int D>
+hipError_t by_hg(const DecodeParams& p, int hg, int batch, hipStream_t st) {
+  switch (hg) {
+    case 1: return launch<SCHEME, BITS, D, 1>(p, batch, st);
+    case 2: return launch<SCHEME, BITS, D, 2>(p, batch, st);
+    case 4: return launch<SCHEME, BITS, D, 4>(p, batch, st);
+    default: return launch<SCHEME, BITS, D, 8>(p, batch, st);
+  }
+}
+
+template <int SCHEME, int BITS>
+hipError_t by_d(const DecodeParams& p, int d, int hg, int batch, hipStream_t st) {
+  switch (d) {
+    case 32: return by_hg<SCHEME, BITS, 32>(p, hg, batch, st);
+    case 64: return by_hg<SCHEME, BITS, 64>(p, hg, batch, st);
+    case 128: return by_hg<SCHEME, BITS, 128>(p, hg, batch, st);
+    default: return by_hg<SCHEME, BITS, 256>(p, hg, batch, st);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
+  const Geometry& g = a.g;
+  DecodeParams p{};
+  p.layer_base = a.layer_base;
+  p.q = static_cast<const uint8_t*>(a.q);
+  p.k_scale = a.k_scale;
+  p.v_scale = a.v_scale;
+  p.out = a.out;
+  p.partials = reinterpret_cast<float*>(a.workspace + workspace_partials_offset(g));
+  p.slab_bytes = g.slab_bytes;
+  p.page_bytes = g.page_bytes;
+  p.ring_base = g.pages_per_slab * g.page_bytes;
+  p.ring_slots = g.ring_slots > 0 ? g.ring_slots : 1;
+  p.T = a.tokens;
+  if (g.scheme == KVQ_KIVI) {
+    p.q_tokens = kivi_quantised(a.tokens, g.residual);
+    p.n_pages = static_cast<int32_t>(p.q_tokens / kPage);
+  } else {
+    p.q_tokens = a.tokens;
+    p.n_pages = static_cast<int32_t>((a.tokens + kPage - 1) / kPage);
+  }
+  p.items = a.items;
+  p.splits = a.splits;
+  p.kv_heads = g.kv_heads;
+  p.q_heads = g.q_heads;
+  p.off_kc = g.off_kc;
+  p.off_ks = g.off_ks;
+  p.off_kz = g.off_kz;
+  p.off_vc = g.off_vc;
+  p.off_vs = g.off_vs;
+  p.off_vz = g.off_vz;
+  p.q_bf16 = a.q_dtype == KVQ_BF16;
+  p.in_bf16 = g.in_bytes == 2;
+  p.qscale = a.sm_scale * kLog2e;
+  p.rope_theta = a.rope_theta;
+  switch (g.scheme) {
+    case KVQ_KIVI:
+      switch (g.bits) {
+        case 2: return by_d<KVQ_KIVI, 2>(p, g.d, g.hg, g.batch, st);
+        case 4: return by_d<KVQ_KIVI, 4>(p, g.d, g.hg, g.batch, st);
+        default: return by_d<KVQ_KIVI, 8>(p, g.d, g.hg, g.batch, st);
+      }
+    case KVQ_SYM_TOKEN:
+      switch (g.bits) {
+        case 2: return by_d<KVQ_SYM_TOKEN, 2>(p, g.d, g.hg, g.batch, st);
+        case 4: return by_d<KVQ_SYM_TOKEN, 4>(p, g.d, g.hg, g.batch, st);
+        default: return by_d<KVQ_SYM_TOKEN, 8>(p, g.d, g.hg, g.batch, st);
+      }
+    default:
+      return by_d<KVQ_FP8_E4M3, 8>(p, g.d, g.hg, g.batch, st);
+  }
+}
+
+}  // namespace kvq

@@ -1,0 +1,289 @@
+// Host side of the C ABI: argument validation, cache geometry, byte counts
+// and kernel dispatch. Nothing here touches a device before validation has
+// passed, so every error path can be exercised without a GPU.
+#include <cmath>
+#include <cstdint>
+#include <limits>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+bool is_pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+
+// Multiplies non-negative int64 values, returning -1 on overflow.
+int64_t mul_ck(int64_t a, int64_t b) {
+  if (a < 0 || b < 0) return -1;
+  if (a != 0 && b > std::numeric_limits<int64_t>::max() / a) return -1;
+  return a * b;
+}
+
+int32_t validate_config(const kvq_config* cfg) {
+  if (!cfg) return KVQ_ERR_NULL;
+  if (cfg->struct_size != sizeof(kvq_config)) return KVQ_ERR_INVALID;
+  const kvq_config& c = *cfg;
+  if (c.scheme != KVQ_KIVI && c.scheme != KVQ_SYM_TOKEN && c.scheme != KVQ_FP8_E4M3)
+    return KVQ_ERR_INVALID;
+  if (c.scheme == KVQ_FP8_E4M3) {
+    if (c.bits != 8) return KVQ_ERR_INVALID;
+  } else if (c.bits != 2 && c.bits != 4 && c.bits != 8) {
+    return (c.bits >= 1 && c.bits <= 8) ? KVQ_ERR_UNSUPPORTED : KVQ_ERR_INVALID;
+  }
+  if (c.layers < 1 || c.q_heads < 1 || c.kv_heads < 1 || c.batch < 1 || c.max_tokens < 0)
+    return KVQ_ERR_INVALID;
+  if (c.q_heads % c.kv_heads != 0) return KVQ_ERR_INVALID;
+  // grid limits: (splits, kv_heads, batch); page counts fit in int32
+  if (c.kv_heads > 65535 || c.batch > 65535 || c.max_tokens >= (int64_t(1) << 36))
+    return KVQ_ERR_UNSUPPORTED;
+  if (!is_pow2_in(c.q_heads / c.kv_heads, 1, 8)) return KVQ_ERR_UNSUPPORTED;
+  if (c.head_dim < 1) return KVQ_ERR_INVALID;
+  if (!is_pow2_in(c.head_dim, 32, 256)) return KVQ_ERR_UNSUPPORTED;
+  if (c.group < 1) return KVQ_ERR_INVALID;
+  if (c.group != kPage) return KVQ_ERR_UNSUPPORTED;
+  if (c.residual < 0) return KVQ_ERR_INVALID;
+  if (c.scheme != KVQ_KIVI && c.residual != 0) return KVQ_ERR_INVALID;
+  if (c.in_dtype != KVQ_F32 && c.in_dtype != KVQ_BF16) return KVQ_ERR_INVALID;
+  if (c.q_dtype != KVQ_F32 && c.q_dtype != KVQ_BF16) return KVQ_ERR_INVALID;
+  if (!std::isfinite(c.rope_theta) || c.rope_theta < 0) return KVQ_ERR_INVALID;
+  if (!std::isfinite(c.sm_scale)) return KVQ_ERR_INVALID;
+  if (c.num_splits < 0) return KVQ_ERR_INVALID;
+  return KVQ_OK;
+}
+
+int64_t slab_bytes_for(const Geometry& g, int64_t capacity) {
+  const int64_t pages = g.scheme == KVQ_KIVI
+                            ? (capacity > g.residual ? (capacity - g.residual) / kPage : 0)
+                            : (capacity + kPage - 1) / kPage;
+  const int64_t p = mul_ck(pages, g.page_bytes);
+  if (p < 0) return -1;
+  return p + g.ring_bytes;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+int32_t make_geometry(const kvq_config& c, Geometry* g) {
+  const int32_t st = validate_config(&c);
+  if (st != KVQ_OK) return st;
+  Geometry x{};
+  x.scheme = c.scheme;
+  x.bits = c.bits;
+  x.d = c.head_dim;
+  x.hg = c.q_heads / c.kv_heads;
+  x.kv_heads = c.kv_heads;
+  x.q_heads = c.q_heads;
+  x.batch = c.batch;
+  x.layers = c.layers;
+  x.residual = c.residual;
+  x.in_bytes = c.in_dtype == KVQ_BF16 ? 2 : 4;
+  x.capacity = c.max_tokens;
+  const int32_t d = c.head_dim, b = c.bits;
+  const int32_t codes = kPage * d * b / 8;  // one packed K-rows or V-cols run
+  switch (c.scheme) {
+    case KVQ_KIVI:
+      x.off_kc = 0;
+      x.off_ks = codes;
+      x.off_kz = codes + 4 * d;
+      x.off_vc = codes + 8 * d;
+      x.off_vs = 2 * codes + 8 * d;
+      x.off_vz = 2 * codes + 8 * d + 4 * kPage;
+      x.page_bytes = 2 * codes + 8 * d + 8 * kPage;
+      x.ring_slots = c.residual + kPage;
+      break;
+    case KVQ_SYM_TOKEN:
+      x.off_kc = 0;
+      x.off_ks = codes;
+      x.off_vc = codes + 4 * kPage;
+      x.off_vs = 2 * codes + 4 * kPage;
+      x.off_kz = x.off_vz = -1;
+      x.page_bytes = 2 * codes + 8 * kPage;
+      x.ring_slots = 0;
+      break;
+    default:  // FP8
+      x.off_kc = 0;
+      x.off_vc = kPage * d;
+      x.off_ks = x.off_kz = x.off_vs = x.off_vz = -1;
+      x.page_bytes = 2 * kPage * d;
+      x.ring_slots = 0;
+      break;
+  }
+  x.ring_bytes = 2 * x.ring_slots * d * x.in_bytes;
+  x.pages_per_slab = x.scheme == KVQ_KIVI
+                         ? (c.max_tokens > c.residual ? (c.max_tokens - c.residual) / kPage : 0)
+                         : (c.max_tokens + kPage - 1) / kPage;
+  x.slab_bytes = slab_bytes_for(x, c.max_tokens);
+  if (x.slab_bytes < 0) return KVQ_ERR_INVALID;
+  const int64_t slabs = mul_ck(mul_ck(c.layers, c.batch), c.kv_heads);
+  if (mul_ck(slabs, x.slab_bytes) < 0) return KVQ_ERR_INVALID;
+  *g = x;
+  return KVQ_OK;
+}
+
+int32_t decode_items(const Geometry& g, int64_t tokens) {
+  if (g.scheme == KVQ_KIVI) {
+    const int64_t q = kivi_quantised(tokens, g.residual);
+    const int64_t nr = tokens - q;
+    return static_cast<int32_t>(q / kPage + (nr + kPage - 1) / kPage);
+  }
+  return static_cast<int32_t>((tokens + kPage - 1) / kPage);
+}
+
+int32_t decode_splits(const Geometry& g, int64_t tokens, int32_t requested) {
+  const int64_t items = decode_items(g, tokens);
+  if (items <= 0) return 1;
+  int64_t s;
+  if (requested > 0) {
+    s = requested;
+  } else {
+    // Aim at ~1024 blocks on 256 CUs while keeping >= 8 work items per block.
+    const int64_t units = static_cast<int64_t>(g.batch) * g.kv_heads;
+    s = (1024 + units - 1) / units;
+    const int64_t cap = (items + 7) / 8;
+    if (s > cap) s = cap;
+  }
+  if (s > items) s = items;
+  if (s < 1) s = 1;
+  return static_cast<int32_t>(s);
+}
+
+int64_t workspace_partials_offset(const Geometry& g) {
+  const int64_t counters = static_cast<int64_t>(g.batch) * g.kv_heads * 4;
+  return (counters + 255) / 256 * 256;
+}
+
+int64_t workspace_bytes(const Geometry& g, int64_t tokens, int32_t requested) {
+  const int64_t s = decode_splits(g, tokens, requested);
+  const int64_t per = static_cast<int64_t>(g.d + 2) * 4;
+  int64_t p = mul_ck(mul_ck(mul_ck(g.batch, g.q_heads), s), per);
+  if (p < 0) return -1;
+  return workspace_partials_offset(g) + p;
+}
+
+}  // namespace kvq
+
+using kvq::Geometry;
+
+extern "C" {
+
+int32_t kvq_abi_version(void) { return KVQ_ABI_VERSION; }
+
+const char* kvq_status_string(int32_t s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_NULL: return "a required pointer is NULL";
+    case KVQ_ERR_INVALID: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVQ_ERR_CAPACITY: return "cache capacity exceeded";
+    case KVQ_ERR_WORKSPACE: return "workspace too small";
+    case KVQ_ERR_DEVICE: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int64_t kvq_cache_bytes(const kvq_config* cfg, int64_t tokens, int32_t kind) {
+  if (!cfg) return KVQ_ERR_NULL;
+  Geometry g;
+  const int32_t st = kvq::make_geometry(*cfg, &g);
+  if (st != KVQ_OK) return st;
+  if (tokens < 0) return KVQ_ERR_INVALID;
+  if (tokens >= (int64_t(1) << 36)) return KVQ_ERR_UNSUPPORTED;
+  switch (kind) {
+    case KVQ_BYTES_FORMULA: {
+      // batch * 2 * layers * kv_heads * head_dim * tokens * bits / 8
+      int64_t v = kvq::mul_ck(2, cfg->batch);
+      v = kvq::mul_ck(v, cfg->layers);
+      v = kvq::mul_ck(v, cfg->kv_heads);
+      v = kvq::mul_ck(v, cfg->head_dim);
+      v = kvq::mul_ck(v, tokens);
+      v = kvq::mul_ck(v, cfg->bits);
+      return v < 0 ? KVQ_ERR_INVALID : v / 8;
+    }
+    case KVQ_BYTES_CACHE: {
+      const int64_t slab = kvq::slab_bytes_for(g, tokens);
+      int64_t v = kvq::mul_ck(kvq::mul_ck(kvq::mul_ck(cfg->layers, cfg->batch), cfg->kv_heads),
+                              slab);
+      return (slab < 0 || v < 0) ? KVQ_ERR_INVALID : v;
+    }
+    case KVQ_BYTES_WORKSPACE: {
+      const int64_t v = kvq::workspace_bytes(g, tokens, cfg->num_splits);
+      return v < 0 ? KVQ_ERR_INVALID : v;
+    }
+    default:
+      return KVQ_ERR_INVALID;
+  }
+}
+
+int32_t kvq_quantize_append(const kvq_config* cfg, void* cache, int32_t layer,
+                            int64_t past_tokens, int64_t new_tokens, const void* k_new,
+                            const void* v_new, const float* k_scale, const float* v_scale,
+                            void* stream) {
+  if (!cfg) return KVQ_ERR_NULL;
+  Geometry g;
+  const int32_t st = kvq::make_geometry(*cfg, &g);
+  if (st != KVQ_OK) return st;
+  if (!cache) return KVQ_ERR_NULL;
+  if (layer < 0 || layer >= cfg->layers) return KVQ_ERR_INVALID;
+  if (past_tokens < 0 || new_tokens < 0) return KVQ_ERR_INVALID;
+  if (past_tokens > cfg->max_tokens || new_tokens > cfg->max_tokens - past_tokens)
+    return KVQ_ERR_CAPACITY;
+  if (new_tokens == 0) return KVQ_OK;
+  if (!k_new || !v_new) return KVQ_ERR_NULL;
+  if (cfg->scheme == KVQ_FP8_E4M3 && (!k_scale || !v_scale)) return KVQ_ERR_NULL;
+  if (!kvq::aligned16(cache) || !kvq::aligned16(k_new) || !kvq::aligned16(v_new))
+    return KVQ_ERR_INVALID;
+  kvq::AppendArgs a{};
+  a.g = g;
+  a.layer_base = static_cast<uint8_t*>(cache) +
+                 static_cast<int64_t>(layer) * cfg->batch * cfg->kv_heads * g.slab_bytes;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.past = past_tokens;
+  a.n = new_tokens;
+  const hipError_t e = kvq::launch_append(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
+}
+
+int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache, int32_t layer,
+                             int64_t tokens, const void* q, const float* k_scale,
+                             const float* v_scale, float* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!cfg) return KVQ_ERR_NULL;
+  Geometry g;
+  const int32_t st = kvq::make_geometry(*cfg, &g);
+  if (st != KVQ_OK) return st;
+  if (!cache || !q || !out || !workspace) return KVQ_ERR_NULL;
+  if (cfg->scheme == KVQ_FP8_E4M3 && (!k_scale || !v_scale)) return KVQ_ERR_NULL;
+  if (layer < 0 || layer >= cfg->layers) return KVQ_ERR_INVALID;
+  if (tokens < 1) return KVQ_ERR_INVALID;
+  if (tokens > cfg->max_tokens) return KVQ_ERR_CAPACITY;
+  if (!kvq::aligned16(cache) || !kvq::aligned16(q) || !kvq::aligned16(out) ||
+      !kvq::aligned16(workspace))
+    return KVQ_ERR_INVALID;
+  const int64_t need = kvq::workspace_bytes(g, tokens, cfg->num_splits);
+  if (need < 0) return KVQ_ERR_INVALID;
+  if (workspace_bytes < static_cast<size_t>(need)) return KVQ_ERR_WORKSPACE;
+  kvq::DecodeArgs a{};
+  a.g = g;
+  a.layer_base = static_cast<const uint8_t*>(cache) +
+                 static_cast<int64_t>(layer) * cfg->batch * cfg->kv_heads * g.slab_bytes;
+  a.tokens = tokens;
+  a.q = q;
+  a.q_dtype = cfg->q_dtype;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.out = out;
+  a.workspace = static_cast<uint8_t*>(workspace);
+  a.sm_scale = cfg->sm_scale != 0.0f ? cfg->sm_scale
+                                     : static_cast<float>(1.0 / std::sqrt((double)cfg->head_dim));
+  a.rope_theta = cfg->rope_theta;
+  a.items = kvq::decode_items(g, tokens);
+  a.splits = kvq::decode_splits(g, tokens, cfg->num_splits);
+  const hipError_t e = kvq::launch_decode(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Internal geometry of the cache layout and kernel launch interfaces.
+// Layout v1 is specified in include/kvq.h; this is the library's own
+// computation of its offsets.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+constexpr int kPage = 32;  // tokens per page == KIVI key group
+
+// Everything a kernel needs to address one layer of the cache.
+struct Geometry {
+  int32_t scheme, bits, d, hg, kv_heads, q_heads, batch, layers, residual;
+  int32_t in_bytes;         // bytes per K/V input element (and ring element)
+  int64_t capacity;         // max_tokens
+  int64_t page_bytes;       // bytes of one 32-token page
+  int64_t pages_per_slab;   // P
+  int64_t ring_slots;       // R + 32 (KIVI), else 0
+  int64_t ring_bytes;       // 2 * ring_slots * d * in_bytes
+  int64_t slab_bytes;       // P * page_bytes + ring_bytes
+  // byte offsets inside a page
+  int32_t off_kc, off_ks, off_kz, off_vc, off_vs, off_vz;
+};
+
+// Fills g from a validated config. Returns KVQ_OK or a negative status.
+int32_t make_geometry(const kvq_config& cfg, Geometry* g);
+
+// Number of quantised tokens of a KIVI cache holding T tokens.
+__host__ __device__ inline int64_t kivi_quantised(int64_t T, int32_t R) {
+  const int64_t over = T - R;
+  return over > 0 ? (over / kPage) * kPage : 0;
+}
+
+// ---- launch interfaces (implemented in append.hip / decode.hip) ----------
+
+struct AppendArgs {
+  Geometry g;
+  uint8_t* layer_base;      // cache + layer * batch * kv_heads * slab_bytes
+  const void* k_new;        // [B][n][Hkv][d] in_dtype
+  const void* v_new;
+  const float* k_scale;     // FP8 only
+  const float* v_scale;
+  int64_t past, n;          // tokens before the call, tokens appended
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+  Geometry g;
+  const uint8_t* layer_base;
+  int64_t tokens;
+  const void* q;            // [B][Hq][d] q_dtype
+  int32_t q_dtype;
+  const float* k_scale;     // FP8 only
+  const float* v_scale;
+  float* out;               // [B][Hq][d]
+  uint8_t* workspace;
+  float sm_scale;           // resolved (never 0)
+  double rope_theta;        // 0 = off
+  int32_t splits;           // token splits per (seq, KV head), >= 1
+  int32_t items;            // work items (pages + ring chunks) per (seq, KV head)
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Decode split plan, shared by kvq_cache_bytes(WORKSPACE) and the launcher.
+int32_t decode_items(const Geometry& g, int64_t tokens);
+int32_t decode_splits(const Geometry& g, int64_t tokens, int32_t requested);
+int64_t workspace_bytes(const Geometry& g, int64_t tokens, int32_t requested);
+// Offset of the split partials inside the workspace (after the counters).
+int64_t workspace_partials_offset(const Geometry& g);
+
+}  // namespace kvq

@@ -1,0 +1,160 @@
+"""ctypes binding of libkvq.so -- argument marshalling only.
+
+Each function has the name of the C entry point it calls and forwards plain
+pointers and sizes; torch is used for device memory and the current HIP stream
+(``torch.cuda.current_stream().cuda_stream`` is PyTorch-ROCm's name for the
+hipStream_t). Every computation happens in the library's HIP kernels. There is
+no fallback: if libkvq.so is missing or fails to load, every call raises.
+"""
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkvq.so")
+
+KVQ_OK, KVQ_ERR_NULL, KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED = 0, -1, -2, -3
+KVQ_ERR_CAPACITY, KVQ_ERR_WORKSPACE, KVQ_ERR_DEVICE = -4, -5, -6
+KVQ_KIVI, KVQ_SYM_TOKEN, KVQ_FP8_E4M3 = 0, 1, 2
+KVQ_F32, KVQ_BF16 = 0, 1
+KVQ_BYTES_FORMULA, KVQ_BYTES_CACHE, KVQ_BYTES_WORKSPACE = 0, 1, 2
+
+SYMBOLS = ("kvq_cache_bytes", "kvq_quantize_append", "kvq_decode_attention",
+           "kvq_status_string", "kvq_abi_version")
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+
+
+class kvq_config(ctypes.Structure):
+    """Mirror of the C struct kvq_config (include/kvq.h)."""
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("scheme", ctypes.c_int32),
+        ("bits", ctypes.c_int32),
+        ("layers", ctypes.c_int32),
+        ("q_heads", ctypes.c_int32),
+        ("kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("max_tokens", ctypes.c_int64),
+        ("group", ctypes.c_int32),
+        ("residual", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32),
+        ("q_dtype", ctypes.c_int32),
+        ("rope_theta", ctypes.c_double),
+        ("sm_scale", ctypes.c_float),
+        ("num_splits", ctypes.c_int32),
+    ]
+
+
+def make_config(scheme, bits, layers, q_heads, kv_heads, head_dim, batch, max_tokens,
+                residual=0, in_dtype=KVQ_BF16, q_dtype=KVQ_BF16, rope_theta=0.0,
+                sm_scale=0.0, num_splits=0, group=32):
+    c = kvq_config()
+    c.struct_size = ctypes.sizeof(kvq_config)
+    c.scheme, c.bits, c.layers = scheme, bits, layers
+    c.q_heads, c.kv_heads, c.head_dim = q_heads, kv_heads, head_dim
+    c.batch, c.max_tokens, c.group, c.residual = batch, max_tokens, group, residual
+    c.in_dtype, c.q_dtype = in_dtype, q_dtype
+    c.rope_theta, c.sm_scale, c.num_splits = rope_theta, sm_scale, num_splits
+    return c
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m "
+                               "kv_cache_quantisation_amd.build` (no fallback path exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        cfgp = ctypes.POINTER(kvq_config)
+        L.kvq_cache_bytes.argtypes = [cfgp, I64, I32]
+        L.kvq_cache_bytes.restype = I64
+        L.kvq_quantize_append.argtypes = [cfgp, P, I32, I64, I64, P, P, P, P, P]
+        L.kvq_quantize_append.restype = I32
+        L.kvq_decode_attention.argtypes = [cfgp, P, I32, I64, P, P, P, P, P, ctypes.c_size_t, P]
+        L.kvq_decode_attention.restype = I32
+        L.kvq_status_string.argtypes = [I32]
+        L.kvq_status_string.restype = ctypes.c_char_p
+        L.kvq_abi_version.argtypes = []
+        L.kvq_abi_version.restype = I32
+        _lib = L
+    return _lib
+
+
+def _ptr(x):
+    """Device address of a tensor, or an int address, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def status_string(status):
+    return lib().kvq_status_string(status).decode()
+
+
+def kvq_abi_version():
+    return lib().kvq_abi_version()
+
+
+def kvq_cache_bytes(cfg, tokens, kind):
+    """Byte count for `tokens` tokens per sequence (raises on a negative status)."""
+    v = lib().kvq_cache_bytes(ctypes.byref(cfg), tokens, kind)
+    if v < 0:
+        raise KvqError(v, "kvq_cache_bytes")
+    return v
+
+
+def kvq_quantize_append(cfg, cache, layer, past_tokens, new_tokens, k_new, v_new,
+                        k_scale=None, v_scale=None, stream=None, check=True):
+    st = lib().kvq_quantize_append(ctypes.byref(cfg), _ptr(cache), layer, past_tokens,
+                                   new_tokens, _ptr(k_new), _ptr(v_new), _ptr(k_scale),
+                                   _ptr(v_scale), _stream(stream))
+    if check and st != KVQ_OK:
+        raise KvqError(st, "kvq_quantize_append")
+    return st
+
+
+def kvq_decode_attention(cfg, cache, layer, tokens, q, out, workspace, workspace_bytes=None,
+                         k_scale=None, v_scale=None, stream=None, check=True):
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = lib().kvq_decode_attention(ctypes.byref(cfg), _ptr(cache), layer, tokens, _ptr(q),
+                                    _ptr(k_scale), _ptr(v_scale), _ptr(out), _ptr(workspace),
+                                    workspace_bytes, _stream(stream))
+    if check and st != KVQ_OK:
+        raise KvqError(st, "kvq_decode_attention")
+    return st
+
+
+# ---- allocation helpers (torch memory only) ----------------------------------
+
+def alloc_cache(cfg, device="cuda", zero=True):
+    import torch
+    n = kvq_cache_bytes(cfg, cfg.max_tokens, KVQ_BYTES_CACHE)
+    return (torch.zeros if zero else torch.empty)(n, dtype=torch.uint8, device=device)
+
+
+def alloc_workspace(cfg, tokens=None, device="cuda"):
+    """Zero-filled decode workspace for calls over up to `tokens` tokens."""
+    import torch
+    n = kvq_cache_bytes(cfg, cfg.max_tokens if tokens is None else tokens, KVQ_BYTES_WORKSPACE)
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)

@@ -23,3 +23,11 @@ def golden():
         with open(os.path.join(GOLDEN, name)) as f:
             return json.load(f)
     return load
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Names each GPU case on stderr (flushed) before it touches the device."""
+    if request.node.get_closest_marker("gpu") is not None:
+        print(f"\n[gpu case] {request.node.nodeid}", file=sys.stderr, flush=True)
+    yield

@@ -1,0 +1,172 @@
+"""The C ABI on the host: the library loads, exports what include/kvq.h
+declares, sizes agree with the oracle's independent layout arithmetic, and every
+validation error is returned before any device work (no GPU needed)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import kv_cache_quantisation_amd as kvq
+from oracle import accounting as acc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    return sorted(set(re.findall(r"KVQ_API\s+[\w\s\*]+?\b(kvq_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kvq.lib()
+    declared = header_functions()
+    assert set(declared) == set(kvq.kvq.SYMBOLS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", kvq.kvq.LIB_PATH],
+                         capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (kvq_\w+)$", out, re.M))
+    assert exported == set(declared)     # nothing internal leaks out
+
+
+def test_abi_version_and_strings():
+    assert kvq.kvq_abi_version() == 1
+    assert kvq.status_string(0) == "ok"
+    for st in (-1, -2, -3, -4, -5, -6):
+        assert kvq.status_string(st) != "unknown status"
+
+
+def cfg(**kw):
+    base = dict(scheme=kvq.KVQ_KIVI, bits=2, layers=2, q_heads=32, kv_heads=8, head_dim=128,
+                batch=3, max_tokens=4096, residual=128)
+    base.update(kw)
+    return kvq.make_config(**base)
+
+
+def test_struct_layout():
+    assert ctypes.sizeof(kvq.kvq_config) == 72
+    assert kvq.kvq_config.max_tokens.offset == 32 and kvq.kvq_config.rope_theta.offset == 56
+    c = cfg()
+    assert kvq.kvq_cache_bytes(c, 10, kvq.KVQ_BYTES_FORMULA) > 0
+    c.struct_size = 64
+    assert kvq.lib().kvq_cache_bytes(ctypes.byref(c), 10, 0) == kvq.KVQ_ERR_INVALID
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_formula_matches_oracle(bits):
+    for scheme in (kvq.KVQ_KIVI, kvq.KVQ_SYM_TOKEN):
+        c = cfg(scheme=scheme, bits=bits, residual=128 if scheme == kvq.KVQ_KIVI else 0)
+        for T in (0, 1, 4096, 131072):
+            assert kvq.kvq_cache_bytes(c, T, kvq.KVQ_BYTES_FORMULA) == \
+                acc.kv_bytes_formula(2, 8, 128, T, bits, batch=3)
+    # the page's Llama 3 8B figure through the library: 128 KiB per token at 16 bits
+    # is twice the 8-bit formula value
+    c = cfg(scheme=kvq.KVQ_FP8_E4M3, bits=8, residual=0, layers=32, batch=1)
+    assert 2 * kvq.kvq_cache_bytes(c, 1, kvq.KVQ_BYTES_FORMULA) == 131072
+
+
+@pytest.mark.parametrize("scheme,bits,d,R,dtype", [
+    (kvq.KVQ_KIVI, 2, 128, 128, kvq.KVQ_BF16), (kvq.KVQ_KIVI, 4, 64, 0, kvq.KVQ_F32),
+    (kvq.KVQ_KIVI, 8, 256, 37, kvq.KVQ_BF16), (kvq.KVQ_KIVI, 2, 32, 5, kvq.KVQ_F32),
+    (kvq.KVQ_SYM_TOKEN, 4, 32, 0, kvq.KVQ_F32), (kvq.KVQ_SYM_TOKEN, 2, 128, 0, kvq.KVQ_BF16),
+    (kvq.KVQ_FP8_E4M3, 8, 128, 0, kvq.KVQ_BF16)])
+def test_cache_bytes_match_oracle_layout(scheme, bits, d, R, dtype):
+    c = cfg(scheme=scheme, bits=bits, head_dim=d, residual=R, in_dtype=dtype, q_heads=8)
+    item = 2 if dtype == kvq.KVQ_BF16 else 4
+    for T in (0, 1, 31, 32, 33, 160, 161, 4096, 10000):
+        assert kvq.kvq_cache_bytes(c, T, kvq.KVQ_BYTES_CACHE) == \
+            acc.layout_cache_bytes(scheme, 2, 3, 8, d, bits, T, R, item), T
+
+
+def test_config_sizes_of_the_workloads():
+    # KIVI 2-bit at 4096 tokens: 124 pages of 104 B/token-head + a 160-row bf16 ring
+    c = cfg(batch=16, layers=1)
+    assert kvq.kvq_cache_bytes(c, 4096, kvq.KVQ_BYTES_CACHE) == 16 * 8 * (124 * 3328 + 81920)
+
+
+def test_workspace_monotone():
+    c = cfg()
+    prev = 0
+    for T in list(range(1, 400)) + [4096, 100000, 1 << 20]:
+        w = kvq.kvq_cache_bytes(c, T, kvq.KVQ_BYTES_WORKSPACE)
+        assert w >= prev
+        prev = w
+    c.num_splits = 3
+    assert kvq.kvq_cache_bytes(c, 4096, kvq.KVQ_BYTES_WORKSPACE) >= 3 * 32 * 3 * 130 * 4
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("scheme", 7, kvq.KVQ_ERR_INVALID), ("bits", 3, kvq.KVQ_ERR_UNSUPPORTED),
+    ("bits", 0, kvq.KVQ_ERR_INVALID), ("bits", 16, kvq.KVQ_ERR_INVALID),
+    ("layers", 0, kvq.KVQ_ERR_INVALID), ("q_heads", 12, kvq.KVQ_ERR_INVALID),
+    ("q_heads", 8 * 16, kvq.KVQ_ERR_UNSUPPORTED), ("q_heads", 8 * 3, kvq.KVQ_ERR_UNSUPPORTED),
+    ("head_dim", 96, kvq.KVQ_ERR_UNSUPPORTED), ("head_dim", 0, kvq.KVQ_ERR_INVALID),
+    ("group", 64, kvq.KVQ_ERR_UNSUPPORTED), ("group", 0, kvq.KVQ_ERR_INVALID),
+    ("residual", -1, kvq.KVQ_ERR_INVALID), ("in_dtype", 5, kvq.KVQ_ERR_INVALID),
+    ("q_dtype", -1, kvq.KVQ_ERR_INVALID), ("rope_theta", -1.0, kvq.KVQ_ERR_INVALID),
+    ("rope_theta", float("nan"), kvq.KVQ_ERR_INVALID), ("sm_scale", float("inf"), kvq.KVQ_ERR_INVALID),
+    ("num_splits", -2, kvq.KVQ_ERR_INVALID), ("batch", 0, kvq.KVQ_ERR_INVALID),
+    ("batch", 70000, kvq.KVQ_ERR_UNSUPPORTED), ("max_tokens", -5, kvq.KVQ_ERR_INVALID),
+    ("max_tokens", 1 << 40, kvq.KVQ_ERR_UNSUPPORTED)])
+def test_config_validation(field, value, status):
+    c = cfg()
+    setattr(c, field, value)
+    L = kvq.lib()
+    assert L.kvq_cache_bytes(ctypes.byref(c), 8, 1) == status
+    # the same status comes back from both device entry points, before any launch
+    fake = 1 << 20
+    assert L.kvq_quantize_append(ctypes.byref(c), fake, 0, 0, 4, fake, fake, None, None, None) \
+        == status
+    assert L.kvq_decode_attention(ctypes.byref(c), fake, 0, 8, fake, None, None, fake, fake,
+                                  1 << 30, None) == status
+
+
+def test_scheme_specific_validation():
+    L = kvq.lib()
+    c = cfg(scheme=kvq.KVQ_SYM_TOKEN, bits=4, residual=3)
+    assert L.kvq_cache_bytes(ctypes.byref(c), 8, 1) == kvq.KVQ_ERR_INVALID
+    c = cfg(scheme=kvq.KVQ_FP8_E4M3, bits=4, residual=0)
+    assert L.kvq_cache_bytes(ctypes.byref(c), 8, 1) == kvq.KVQ_ERR_INVALID
+    c = cfg(scheme=kvq.KVQ_FP8_E4M3, bits=8, residual=0)
+    fake = 1 << 20
+    # FP8 needs its per-head scales
+    assert L.kvq_quantize_append(ctypes.byref(c), fake, 0, 0, 4, fake, fake, None, None, None) \
+        == kvq.KVQ_ERR_NULL
+    assert L.kvq_decode_attention(ctypes.byref(c), fake, 0, 8, fake, fake, None, fake, fake,
+                                  1 << 30, None) == kvq.KVQ_ERR_NULL
+    assert L.kvq_cache_bytes(ctypes.byref(c), 8, 9) == kvq.KVQ_ERR_INVALID
+    assert L.kvq_cache_bytes(ctypes.byref(c), -1, 1) == kvq.KVQ_ERR_INVALID
+    assert L.kvq_cache_bytes(None, 8, 1) == kvq.KVQ_ERR_NULL
+
+
+def test_call_validation():
+    L = kvq.lib()
+    c = cfg()
+    p = ctypes.byref(c)
+    f = 1 << 20
+    big = 1 << 30
+    ap = L.kvq_quantize_append
+    assert ap(None, f, 0, 0, 4, f, f, None, None, None) == kvq.KVQ_ERR_NULL
+    assert ap(p, None, 0, 0, 4, f, f, None, None, None) == kvq.KVQ_ERR_NULL
+    assert ap(p, f, 2, 0, 4, f, f, None, None, None) == kvq.KVQ_ERR_INVALID      # layer
+    assert ap(p, f, -1, 0, 4, f, f, None, None, None) == kvq.KVQ_ERR_INVALID
+    assert ap(p, f, 0, -1, 4, f, f, None, None, None) == kvq.KVQ_ERR_INVALID
+    assert ap(p, f, 0, 4000, 97, f, f, None, None, None) == kvq.KVQ_ERR_CAPACITY
+    assert ap(p, f, 0, 4097, 0, f, f, None, None, None) == kvq.KVQ_ERR_CAPACITY
+    assert ap(p, f, 0, 4000, 0, None, None, None, None, None) == kvq.KVQ_OK       # no-op
+    assert ap(p, f, 0, 0, 4, None, f, None, None, None) == kvq.KVQ_ERR_NULL
+    assert ap(p, f + 4, 0, 0, 4, f, f, None, None, None) == kvq.KVQ_ERR_INVALID  # alignment
+    assert ap(p, f, 0, 0, 4, f + 2, f, None, None, None) == kvq.KVQ_ERR_INVALID
+    de = L.kvq_decode_attention
+    assert de(p, f, 0, 0, f, None, None, f, f, big, None) == kvq.KVQ_ERR_INVALID   # tokens
+    assert de(p, f, 0, 4097, f, None, None, f, f, big, None) == kvq.KVQ_ERR_CAPACITY
+    assert de(p, f, 0, 8, None, None, None, f, f, big, None) == kvq.KVQ_ERR_NULL
+    assert de(p, f, 0, 8, f, None, None, None, f, big, None) == kvq.KVQ_ERR_NULL
+    assert de(p, f, 0, 8, f, None, None, f, None, big, None) == kvq.KVQ_ERR_NULL
+    assert de(p, f, 0, 8, f, None, None, f + 8, f, big, None) == kvq.KVQ_ERR_INVALID
+    need = kvq.kvq_cache_bytes(c, 4096, kvq.KVQ_BYTES_WORKSPACE)
+    assert de(p, f, 0, 4096, f, None, None, f, f, need - 1, None) == kvq.KVQ_ERR_WORKSPACE
+    assert de(p, f, 3, 8, f, None, None, f, f, big, None) == kvq.KVQ_ERR_INVALID    # layer
