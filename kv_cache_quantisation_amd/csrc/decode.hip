@@ -373,20 +373,22 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   }
 }
 
-// Merges the split partials of one (sequence, query head): grid = batch*q_heads.
+// Merges the split partials of one (sequence, query head): grid = rows.
+// M = max m_s; out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
 template <int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64) void decode_merge_kernel(const float* partials, float* out,
+                                                          int splits) {
   const int bh = blockIdx.x;
-  const float* part = p.partials + static_cast<int64_t>(bh) * p.splits * (D + 2);
+  const float* part = partials + static_cast<int64_t>(bh) * splits * (D + 2);
   float M = -INFINITY;
-  for (int s = 0; s < p.splits; ++s) M = fmaxf(M, part[s * (D + 2)]);
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, part[s * (D + 2)]);
   float L = 0.f;
-  for (int s = 0; s < p.splits; ++s) L = fmaf(exp2f(part[s * (D + 2)] - M), part[s * (D + 2) + 1], L);
+  for (int s = 0; s < splits; ++s) L = fmaf(exp2f(part[s * (D + 2)] - M), part[s * (D + 2) + 1], L);
   for (int c = threadIdx.x; c < D; c += 64) {
     float acc = 0.f;
-    for (int s = 0; s < p.splits; ++s)
+    for (int s = 0; s < splits; ++s)
       acc = fmaf(exp2f(part[s * (D + 2)] - M), part[s * (D + 2) + 2 + c], acc);
-    p.out[static_cast<int64_t>(bh) * D + c] = acc / L;
+    out[static_cast<int64_t>(bh) * D + c] = acc / L;
   }
 }
 
@@ -395,7 +397,9 @@ hipError_t launch(const DecodeParams& p, int batch, hipStream_t st) {
   dim3 grid(p.splits, p.kv_heads, batch);
   hipLaunchKernelGGL((decode_split_kernel<SCHEME, BITS, D, HG>), grid, dim3(kThreads), 0, st, p);
   if (p.splits > 1) {
-    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(batch * p.q_heads), dim3(64), 0, st, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_merge(p.partials, p.out, batch * p.q_heads, p.splits, D, st);
   }
   return hipGetLastError();
 }
@@ -422,8 +426,20 @@ hipError_t by_d(const DecodeParams& p, int d, int hg, int batch, hipStream_t st)
 
 }  // namespace
 
+hipError_t launch_merge(float* partials, float* out, int rows, int splits, int d,
+                        hipStream_t st) {
+  switch (d) {
+    case 32: hipLaunchKernelGGL((decode_merge_kernel<32>), dim3(rows), dim3(64), 0, st, partials, out, splits); break;
+    case 64: hipLaunchKernelGGL((decode_merge_kernel<64>), dim3(rows), dim3(64), 0, st, partials, out, splits); break;
+    case 128: hipLaunchKernelGGL((decode_merge_kernel<128>), dim3(rows), dim3(64), 0, st, partials, out, splits); break;
+    default: hipLaunchKernelGGL((decode_merge_kernel<256>), dim3(rows), dim3(64), 0, st, partials, out, splits); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   const Geometry& g = a.g;
+  if (mfma_path(g)) return launch_kivi_mfma(a, st);
   DecodeParams p{};
   p.layer_base = a.layer_base;
   p.q = static_cast<const uint8_t*>(a.q);

@@ -78,6 +78,7 @@ int32_t make_geometry(const kvq_config& c, Geometry* g) {
   x.layers = c.layers;
   x.residual = c.residual;
   x.in_bytes = c.in_dtype == KVQ_BF16 ? 2 : 4;
+  x.rope = c.rope_theta;
   x.capacity = c.max_tokens;
   const int32_t d = c.head_dim, b = c.bits;
   const int32_t codes = kPage * d * b / 8;  // one packed K-rows or V-cols run
@@ -154,7 +155,13 @@ int64_t workspace_partials_offset(const Geometry& g) {
 }
 
 int64_t workspace_bytes(const Geometry& g, int64_t tokens, int32_t requested) {
-  const int64_t s = decode_splits(g, tokens, requested);
+  int64_t s;
+  if (mfma_path(g)) {
+    const MfmaPlan pl = mfma_plan(g, tokens, requested);
+    s = static_cast<int64_t>(pl.page_splits) + pl.ring_splits_max;
+  } else {
+    s = decode_splits(g, tokens, requested);
+  }
   const int64_t per = static_cast<int64_t>(g.d + 2) * 4;
   int64_t p = mul_ck(mul_ck(mul_ck(g.batch, g.q_heads), s), per);
   if (p < 0) return -1;
@@ -282,6 +289,7 @@ int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache, int32_t l
   a.rope_theta = cfg->rope_theta;
   a.items = kvq::decode_items(g, tokens);
   a.splits = kvq::decode_splits(g, tokens, cfg->num_splits);
+  a.requested_splits = cfg->num_splits;
   const hipError_t e = kvq::launch_decode(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
 }

@@ -16,6 +16,7 @@ constexpr int kPage = 32;  // tokens per page == KIVI key group
 struct Geometry {
   int32_t scheme, bits, d, hg, kv_heads, q_heads, batch, layers, residual;
   int32_t in_bytes;         // bytes per K/V input element (and ring element)
+  double rope;              // rotary base (0 = none)
   int64_t capacity;         // max_tokens
   int64_t page_bytes;       // bytes of one 32-token page
   int64_t pages_per_slab;   // P
@@ -62,8 +63,21 @@ struct DecodeArgs {
   double rope_theta;        // 0 = off
   int32_t splits;           // token splits per (seq, KV head), >= 1
   int32_t items;            // work items (pages + ring chunks) per (seq, KV head)
+  int32_t requested_splits; // cfg.num_splits
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Matrix-core path: KIVI 2/4-bit pages, head_dim >= 64, no rotary embedding.
+// Blocks [0, page_splits) take page ranges; ring_splits more take ring chunks.
+struct MfmaPlan {
+  int32_t pages, chunks, page_splits, ring_splits, ring_splits_max;
+};
+bool mfma_path(const Geometry& g);
+MfmaPlan mfma_plan(const Geometry& g, int64_t tokens, int32_t requested);
+hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t stream);
+// Merges `splits` partials (m, l, o[d]) per row into out (rows = batch*q_heads).
+hipError_t launch_merge(float* partials, float* out, int rows, int splits, int d,
+                        hipStream_t stream);
 
 // Decode split plan, shared by kvq_cache_bytes(WORKSPACE) and the launcher.
 int32_t decode_items(const Geometry& g, int64_t tokens);

@@ -132,6 +132,48 @@ def test_decode_parity(scheme, bits, d, hg, dtype, R, T, rope, splits):
     assert err <= H.ATOL, err
 
 
+MFMA_CASES = [
+    # KIVI 2/4-bit pages on the matrix cores: every GQA width, head_dim 64/128/256
+    (bits, d, hg, R, T, dtype)
+    for bits in (2, 4)
+    for (d, hg, R, T, dtype) in [(128, 1, 128, 300, torch.bfloat16), (128, 2, 0, 256, torch.float32),
+                                 (128, 8, 128, 900, torch.bfloat16), (64, 4, 32, 500, torch.bfloat16),
+                                 (256, 8, 64, 333, torch.bfloat16), (256, 1, 0, 96, torch.float32),
+                                 (64, 8, 0, 64, torch.float32), (128, 4, 0, 32, torch.bfloat16)]
+]
+
+
+@pytest.mark.parametrize("bits,d,hg,R,T,dtype", MFMA_CASES)
+def test_decode_mfma_pages(bits, d, hg, R, T, dtype):
+    w = small(synth.KIVI, bits, d, dtype, R, hg=hg, T=T)
+    cfg, cache, oc, *_ = run_append(w, [T], capacity=T + 40)
+    q = synth.query(w, device=DEV)
+    out = H.decode(cfg, cache, 0, T, q)
+    err = H.max_err(out, oc.decode(0, H.values(q)))
+    assert err <= H.ATOL, err
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_decode_mfma_dynamic_range(bits):
+    """Keys and values over many orders of magnitude: per-channel scales from
+    1e-4 to 1e3, so q * s spans far more than fp16's 11 bits and the hi/lo
+    split carries the accuracy; peaked attention through large queries."""
+    w = small(synth.KIVI, bits, 128, torch.float32, 32, hg=4, T=600)
+    k, v = synth.keys_values(w, device=DEV)
+    ch = torch.logspace(-4, 3, 128, device=DEV)
+    k = (k * ch.view(1, 1, 1, 128)).contiguous()
+    v = (v * torch.logspace(-2, 2, 600, device=DEV).view(1, 600, 1, 1)).contiguous()
+    cfg = H.config(w, 640)
+    cache = kvq.alloc_cache(cfg)
+    oc = H.oracle_cache(w, 640)
+    H.append_chunks(cfg, cache, k, v, [600], oc=oc)
+    q = (synth.query(w, device=DEV) * 3.0).contiguous()
+    out = H.decode(cfg, cache, 0, 600, q)
+    want = oc.decode(0, H.values(q))
+    scale = max(1.0, float(np.max(np.abs(want))))
+    assert H.max_err(out, want) <= H.ATOL * scale
+
+
 def test_decode_split_invariance_and_determinism():
     w = small(synth.KIVI, 2, 128, torch.bfloat16, 128, hg=4, T=1500)
     cfg, cache, oc, *_ = run_append(w, [w.tokens], capacity=1600)
