@@ -25,7 +25,7 @@ SOURCES = ["kvq_api.cpp", "append.hip", "decode.hip", "decode_mfma.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-fvisibility=hidden", "-Wall", "-Wno-unused-function", "-I", INCLUDE,
+    "-fvisibility=hidden", "-Wall", "-Wno-unused-function", "-Wno-pass-failed", "-I", INCLUDE,
 ]
 
 

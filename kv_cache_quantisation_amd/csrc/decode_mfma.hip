@@ -17,8 +17,8 @@
 //           A = P' [16 rows x 32 tokens] (rows 0..HG-1 hi, HG..2HG-1 lo),
 //           B = value codes [32 tokens x 16 channels].
 //
-// The unquantised residual tokens (bf16) take the same path 16 tokens at a
-// time: A = key rows as stored, B = q split into three bf16 parts (hi, mid,
+// The unquantised residual tokens (bf16) take the same path 8 tokens at a
+// time (one half of a 16-row tile): A = key rows as stored, B = q split into three bf16 parts (hi, mid,
 // lo columns); P (split hi/lo in bf16) times the value rows, gathered per
 // channel from LDS. They update the same softmax state and accumulators.
 //
@@ -34,8 +34,8 @@
 // the order {0,2,1,3,4,6,5,7} within each 8, and q' is laid out to match.
 //
 // Memory: each wave streams its pages HBM -> LDS with global_load_lds_dwordx4
-// (16 bytes per lane, a whole page in 4-11 instructions), one or two pages
-// ahead of the one it computes, so fetches overlap arithmetic without holding
+// (16 bytes per lane, a whole page in 4-11 instructions), one page ahead of
+// the one it computes, so fetches overlap arithmetic without holding
 // registers; `s_waitcnt vmcnt` retires them in issue order.
 //
 // Online softmax per head in the log2 domain (q pre-scaled by sm_scale*log2 e);
@@ -69,7 +69,7 @@ struct MfmaParams {
   int* counters;                  // one per (sequence, KV head), zero between calls
   int64_t slab_bytes, page_bytes, ring_base, ring_slots;
   int64_t T, q_tokens;            // cached tokens; tokens held in pages
-  int32_t n_pages, n_halves;      // quantised pages; residual tokens in 16-token steps
+  int32_t n_pages, n_steps;       // quantised pages; residual tokens in 8-token steps
   int32_t splits;                 // blocks per (sequence, KV head)
   int32_t kv_heads, q_heads;
   int32_t q_bf16;
@@ -86,9 +86,9 @@ struct PageGeom {
   static constexpr int OFF_VZ = OFF_VS + 128;
   static constexpr int BYTES = OFF_VZ + 128;
   static constexpr int DMA = (BYTES + 1023) / 1024;  // 16-byte-per-lane copies per page
-  static constexpr int NBUF = BYTES <= 4096 ? 3 : 2;  // page buffers per wave
-  static constexpr int RING = 2 * 16 * D * 2;         // 16 key + 16 value bf16 rows
-  static constexpr int WAVE_LDS = NBUF * BYTES > RING ? NBUF * BYTES : RING;
+  static constexpr int NBUF = 2;                       // page buffers per wave
+  static constexpr int RING = 2 * 8 * D * 2;          // 8 key + 8 value bf16 rows
+  static constexpr int WAVE_LDS = NBUF * BYTES + RING;
 };
 
 // ---- wave-level helpers ------------------------------------------------------
@@ -107,6 +107,29 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   // vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14; expcnt, lgkmcnt: no wait
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Waits until at most n (0..15; larger values wait for 15) vector-memory
+// operations of this wave are outstanding.
+__device__ __forceinline__ void wait_vm_upto(int n) {
+  switch (n) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<1>(); break;
+    case 2: wait_vm<2>(); break;
+    case 3: wait_vm<3>(); break;
+    case 4: wait_vm<4>(); break;
+    case 5: wait_vm<5>(); break;
+    case 6: wait_vm<6>(); break;
+    case 7: wait_vm<7>(); break;
+    case 8: wait_vm<8>(); break;
+    case 9: wait_vm<9>(); break;
+    case 10: wait_vm<10>(); break;
+    case 11: wait_vm<11>(); break;
+    case 12: wait_vm<12>(); break;
+    case 13: wait_vm<13>(); break;
+    case 14: wait_vm<14>(); break;
+    default: wait_vm<15>(); break;
+  }
 }
 
 // Waits for this wave's LDS operations.
@@ -185,10 +208,11 @@ __device__ __forceinline__ float row_shl(float v) {  // lane l gets lane l+SHIFT
                                                                0x100 + SHIFT, 0xF, 0xF, false));
 }
 
+// Lane l gets v of lane l-SHIFT of its row; lanes with no such source keep `keep`.
 template <int SHIFT>
-__device__ __forceinline__ uint32_t row_shr_u(uint32_t v) {  // lane l gets lane l-SHIFT of its row
-  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x110 + SHIFT,
-                                                           0xF, 0xF, false));
+__device__ __forceinline__ uint32_t shr_keep(uint32_t keep, uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(keep), static_cast<int>(v),
+                                                           0x110 + SHIFT, 0xF, 0xF, false));
 }
 
 // f32 pair -> packed f16 (hi) and packed f16 remainder (lo), hi + lo ~ x.
@@ -228,7 +252,7 @@ __device__ __forceinline__ float load_q(const uint8_t* base, int64_t idx, int bf
 }
 
 template <int BITS, int D, int HG>
-__global__ __launch_bounds__(kThreads) void kivi_mfma_kernel(MfmaParams p) {
+__global__ __launch_bounds__(kThreads, 3) void kivi_mfma_kernel(MfmaParams p) {
   static_assert(BITS == 2 || BITS == 4, "2- or 4-bit pages");
   static_assert(2 * HG <= 16, "hi and lo columns of the GQA group fit one tile");
   using PG = PageGeom<BITS, D>;
@@ -247,7 +271,8 @@ __global__ __launch_bounds__(kThreads) void kivi_mfma_kernel(MfmaParams p) {
   static_assert(KW >= 1, "at least one word per lane");
 
   __shared__ __attribute__((aligned(16))) float qs[HG][D];
-  __shared__ __attribute__((aligned(16))) uint32_t frag[kWaves][KS][64][4];  // B fragments of q'
+  // B fragments of q' for the live columns (hi, lo) of each lane group: [ks][g][2*HG]
+  __shared__ __attribute__((aligned(16))) uint32_t frag[kWaves][KS][4][2 * HG][4];
   __shared__ __attribute__((aligned(16))) uint8_t arena[ARENA];              // page buffers / reduction
   __shared__ int last_block;
 
@@ -258,20 +283,8 @@ __global__ __launch_bounds__(kThreads) void kivi_mfma_kernel(MfmaParams p) {
   const uint8_t* slab = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes;
   uint8_t* wbuf = arena + wave * PG::WAVE_LDS;
 
-  for (int i = tid; i < HG * D; i += kThreads) {
-    const int gg = i / D, c = i % D;
-    const int64_t qi = (static_cast<int64_t>(b) * p.q_heads + h * HG + gg) * D + c;
-    qs[gg][c] = load_q(p.q, qi, p.q_bf16) * p.qscale;
-  }
-  // zero B-fragment columns >= 2*HG once; they are never written again
-  for (int i = lane; i < KS * 64; i += 64) {
-    const int ks = i / 64, ln = i % 64;
-    if ((ln & 15) >= 2 * HG) {
-      frag[wave][ks][ln][0] = frag[wave][ks][ln][1] = 0u;
-      frag[wave][ks][ln][2] = frag[wave][ks][ln][3] = 0u;
-    }
-  }
-  __syncthreads();
+  // (q staging and the first memory requests are issued below, after the
+  // helpers they need are defined)
 
   // ---- per-wave online-softmax state ----------------------------------------
   // Lane (j, g), j < HG, tracks head j: running max m, and the sums of p and
@@ -315,20 +328,15 @@ __global__ __launch_bounds__(kThreads) void kivi_mfma_kernel(MfmaParams p) {
   };
 
   // ---- work of this wave --------------------------------------------------------
+  // Block `split` takes a contiguous range of pages; its waves take every
+  // kWaves-th page of that range.
+  const int unit = b * p.kv_heads + h;
+  const int waves_total = p.splits * kWaves;
   const int pg0 = static_cast<int>(static_cast<int64_t>(split) * p.n_pages / p.splits);
   const int pg1 = static_cast<int>(static_cast<int64_t>(split + 1) * p.n_pages / p.splits);
   const int n_mine = pg0 + wave < pg1 ? (pg1 - pg0 - wave + kWaves - 1) / kWaves : 0;
 
-  // fold units handled by this lane: (head, lane group, k-step) -> 8 channels
-  float qreg[REPS][8];
-#pragma unroll
-  for (int r = 0; r < REPS; ++r) {
-    const int cidx = lane + 64 * r;
-    const int fh = cidx / PER_HEAD, fg = (cidx / KS) % 4, fk = cidx % KS;
-    const int c0 = fg * CPG + 8 * fk;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qreg[r][i] = cidx < COMBOS ? qs[fh][c0 + i] : 0.f;
-  }
+  float qreg[REPS][8];   // this lane's fold units of q (set once q is staged)
 
   auto issue_page = [&](int k) {   // page k of this wave -> buffer k % NBUF
     const uint8_t* src = slab + static_cast<int64_t>(pg0 + wave + kWaves * k) * p.page_bytes;
@@ -368,8 +376,8 @@ __global__ __launch_bounds__(kThreads) void kivi_mfma_kernel(MfmaParams p) {
       split_f16(qp[4], qp[6], hi[2], lo[2]);
       split_f16(qp[5], qp[7], hi[3], lo[3]);
       if (cidx < COMBOS) {
-        *reinterpret_cast<uint4*>(frag[wave][fk][16 * fg + fh]) = uint4{hi[0], hi[1], hi[2], hi[3]};
-        *reinterpret_cast<uint4*>(frag[wave][fk][16 * fg + HG + fh]) = uint4{lo[0], lo[1], lo[2], lo[3]};
+        *reinterpret_cast<uint4*>(frag[wave][fk][fg][fh]) = uint4{hi[0], hi[1], hi[2], hi[3]};
+        *reinterpret_cast<uint4*>(frag[wave][fk][fg][HG + fh]) = uint4{lo[0], lo[1], lo[2], lo[3]};
       }
     }
     // bias of head j for this lane: the fold units of head hh are lanes
@@ -388,18 +396,23 @@ __global__ __launch_bounds__(kThreads) void kivi_mfma_kernel(MfmaParams p) {
       const float got = __shfl(v, src & 63, 64);
       if (src >= 0 && src < 64) bias_j = got;
     }
+    if (j >= HG) bias_j = 0.f;   // lo columns carry no offset
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    // columns >= 2*HG only produce score columns that are never read
     half8 bq[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) bq[ks] = *reinterpret_cast<const half8*>(frag[wave][ks][lane]);
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 f = *reinterpret_cast<const uint4*>(frag[wave][ks][g][j % (2 * HG)]);
+      bq[ks] = cat4h(f.x, f.y, f.z, f.w);
+    }
 
     // scores S^T = codes x q'^T
     float s[8];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const uint32_t* kp = reinterpret_cast<const uint32_t*>(pg + (16 * mt + j) * KROW + g * (KW * 4));
-      floatx4 c = {0.f, 0.f, 0.f, 0.f};
+      floatx4 c = {bias_j, bias_j, bias_j, bias_j};   // hi column carries q . z
       if constexpr (BITS == 2) {
 #pragma unroll
         for (int w = 0; w < KW; ++w) {
@@ -414,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void kivi_mfma_kernel(MfmaParams p) {
           c = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes4_frag(kp[w]), bq[w], c, 0, 0, 0);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s[4 * mt + r] = c[r] + row_shl<HG>(c[r]) + bias_j;
+      for (int r = 0; r < 4; ++r) s[4 * mt + r] = c[r] + row_shl<HG>(c[r]);
     }
 
     softmax_update(s, std::integral_constant<int, 8>{});
@@ -437,12 +450,11 @@ __global__ __launch_bounds__(kThreads) void kivi_mfma_kernel(MfmaParams p) {
     split_f16(pv[1], pv[3], ph[1], pl[1]);
     split_f16(pv[4], pv[6], ph[2], pl[2]);
     split_f16(pv[5], pv[7], ph[3], pl[3]);
+    // rows j < HG: hi of head j; rows j >= HG: lo of lane j-HG (rows >= 2HG
+    // only reach accumulator rows that are never read)
     uint32_t pa[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t lo_from_head = row_shr_u<HG>(pl[i]);   // lane j gets lane j-HG
-      pa[i] = j < HG ? ph[i] : (j < 2 * HG ? lo_from_head : 0u);
-    }
+    for (int i = 0; i < 4; ++i) pa[i] = shr_keep<HG>(ph[i], pl[i]);
     const half8 ap = cat4h(pa[0], pa[1], pa[2], pa[3]);
 
     // P' x value codes; channel of N-tile nt in column j is NT*j + nt
@@ -471,42 +483,48 @@ __global__ __launch_bounds__(kThreads) void kivi_mfma_kernel(MfmaParams p) {
     }
   };
 
-  // ---- residual (unquantised) tokens, 16 per step ---------------------------
-  // The steps of this (sequence, KV head) are spread over all its waves.
-  const int waves_total = p.splits * kWaves;
-  const int my_wave = split * kWaves + wave;
-#pragma unroll 1
-  for (int hs = my_wave; hs < p.n_halves; hs += waves_total) {
-    const int64_t t0 = p.q_tokens + static_cast<int64_t>(hs) * 16;
-    const int nv = static_cast<int>(p.T - t0 < 16 ? p.T - t0 : 16);
-    // 16 key rows then 16 value rows of D bf16 (2D bytes each) into LDS
-    constexpr int LPR = 2 * D / 16;           // lanes per row
-    constexpr int RPI = 64 / LPR;             // rows per copy
+  // ---- residual (unquantised) tokens, 8 per step ----------------------------
+  // Step hs covers tokens [q_tokens + 8 hs, +8); the steps of this (sequence,
+  // KV head) are spread over all its waves. Rows go HBM -> LDS slot `wring`.
+  uint8_t* wring = wbuf + PG::NBUF * PG::BYTES;
+  constexpr int LPR = 2 * D / 16;           // lanes per bf16 row
+  constexpr int RPI = 64 / LPR;             // rows per 16-byte-per-lane copy
+  constexpr int RSTEP = 8;                  // tokens per residual step
+  auto issue_step = [&](int hs) -> int {    // returns the copies issued
+    const int64_t t0 = p.q_tokens + static_cast<int64_t>(hs) * RSTEP;
+    const int nv = static_cast<int>(p.T - t0 < RSTEP ? p.T - t0 : RSTEP);
     const int row_in = lane / LPR, col_b = (lane % LPR) * 16;
+    const int slots = static_cast<int>(p.ring_slots);
+    const int slot0 = static_cast<int>(t0 % p.ring_slots);
+    int issued = 0;
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {
 #pragma unroll
-      for (int i = 0; i < 16 / RPI; ++i) {
+      for (int i = 0; i < (RSTEP + RPI - 1) / RPI; ++i) {
+        if (i * RPI >= nv) continue;          // wave-uniform: no row of this copy exists
         const int r = i * RPI + row_in;
-        const int64_t slot = (t0 + r) % p.ring_slots;
+        const int slot = slot0 + r < slots ? slot0 + r : slot0 + r - slots;
         const uint8_t* src = slab + p.ring_base + (kv * p.ring_slots + slot) * (2 * D) + col_b;
-        if (r < nv) dma16(src, lds_addr(wbuf + kv * 16 * 2 * D + i * 1024));
+        if (r < nv && r < RSTEP) dma16(src, lds_addr(wring + kv * RSTEP * 2 * D + i * 1024));
+        ++issued;
       }
     }
     // value rows of absent tokens must be finite (they meet weight 0): zero them
-    for (int i = lane; i < (16 - nv) * 2 * D / 16; i += 64)
-      *reinterpret_cast<uint4*>(wbuf + 16 * 2 * D + nv * 2 * D + i * 16) = uint4{0u, 0u, 0u, 0u};
-    wait_vm<0>();
-    wait_lds();
-    __builtin_amdgcn_wave_barrier();
-
+    for (int i = lane; i < (RSTEP - nv) * 2 * D / 16; i += 64)
+      *reinterpret_cast<uint4*>(wring + RSTEP * 2 * D + nv * 2 * D + i * 16) = uint4{0u, 0u, 0u, 0u};
+    return issued;
+  };
+  // tile rows (tokens) 8..15 of a step are masked; key rows repeat rows 0..7
+  auto process_step = [&](int hs) {
+    const int64_t t0 = p.q_tokens + static_cast<int64_t>(hs) * RSTEP;
+    const int nv = static_cast<int>(p.T - t0 < RSTEP ? p.T - t0 : RSTEP);
     // B = q^T in three bf16 parts: columns [0,HG) hi, [HG,2HG) mid, [2HG,3HG) lo
     floatx4 cres[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) cres[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(wbuf + j * 2 * D + (32 * ks + 8 * g) * 2);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(wring + (j & 7) * 2 * D + (32 * ks + 8 * g) * 2);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int col = 16 * qb + j;
@@ -514,15 +532,12 @@ __global__ __launch_bounds__(kThreads) void kivi_mfma_kernel(MfmaParams p) {
         uint32_t w4[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float x0 = 0.f, x1 = 0.f;
-          if (part < 3) {
-            const float q0 = qs[hh][32 * ks + 8 * g + 2 * i];
-            const float q1 = qs[hh][32 * ks + 8 * g + 2 * i + 1];
-            const float h0 = bf16_trunc(q0), h1 = bf16_trunc(q1);
-            const float m0 = bf16_trunc(q0 - h0), m1 = bf16_trunc(q1 - h1);
-            x0 = part == 0 ? h0 : (part == 1 ? m0 : q0 - h0 - m0);
-            x1 = part == 0 ? h1 : (part == 1 ? m1 : q1 - h1 - m1);
-          }
+          const float2 qq = *reinterpret_cast<const float2*>(&qs[hh][32 * ks + 8 * g + 2 * i]);
+          const float h0 = bf16_trunc(qq.x), h1 = bf16_trunc(qq.y);
+          const float m0 = bf16_trunc(qq.x - h0), m1 = bf16_trunc(qq.y - h1);
+          float x0 = part == 0 ? h0 : (part == 1 ? m0 : qq.x - h0 - m0);
+          float x1 = part == 0 ? h1 : (part == 1 ? m1 : qq.y - h1 - m1);
+          if (part >= 3) x0 = x1 = 0.f;      // unused columns
           w4[i] = pack_bf16(x0, x1);
         }
         const bf16x8 bq = __builtin_bit_cast(bf16x8, uint4{w4[0], w4[1], w4[2], w4[3]});
@@ -554,43 +569,104 @@ __global__ __launch_bounds__(kThreads) void kivi_mfma_kernel(MfmaParams p) {
     }
     uint32_t pa[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t lo_from_head = row_shr_u<HG>(pl[i]);
-      pa[i] = j < HG ? ph[i] : (j < 2 * HG ? lo_from_head : 0u);
-    }
+    for (int i = 0; i < 2; ++i) pa[i] = shr_keep<HG>(ph[i], pl[i]);
     const bf16x8 ap = __builtin_bit_cast(bf16x8, uint4{pa[0], pa[1], 0u, 0u});
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int c = NT * j + nt;
-      const uint16_t* vr = reinterpret_cast<const uint16_t*>(wbuf + 16 * 2 * D) + c;
-      const uint32_t v0 = vr[(4 * g + 0) * D], v1 = vr[(4 * g + 1) * D];
-      const uint32_t v2 = vr[(4 * g + 2) * D], v3 = vr[(4 * g + 3) * D];
+      const uint16_t* vr = reinterpret_cast<const uint16_t*>(wring + RSTEP * 2 * D) + c;
+      const int t4 = (4 * g) & 7;             // tokens >= 8 carry weight 0
+      const uint32_t v0 = vr[(t4 + 0) * D], v1 = vr[(t4 + 1) * D];
+      const uint32_t v2 = vr[(t4 + 2) * D], v3 = vr[(t4 + 3) * D];
       const bf16x8 bv = __builtin_bit_cast(bf16x8, uint4{v0 | (v1 << 16), v2 | (v3 << 16), 0u, 0u});
       acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, bv, acc[nt], 0, 0, 0);
     }
+  };
+
+  // ---- first requests, all in flight together: q (wave 0), this wave's first
+  // residual step, its first page ------------------------------------------------
+  // residual steps go first to the waves with the fewest pages: the last wave
+  // of every block, then the one before, ... (wave 0 may hold one page more)
+  const int my_wave = (kWaves - 1 - wave) * p.splits + split;
+  const int q_bytes = HG * D * (p.q_bf16 ? 2 : 4);
+  int after_q = 0;
+  if (wave == 0) {
+    const uint8_t* qsrc = p.q + (static_cast<int64_t>(b) * p.q_heads + h * HG) * D * (p.q_bf16 ? 2 : 4);
+    for (int off = 0; off < q_bytes; off += 1024)
+      if (off + lane * 16 < q_bytes) dma16(qsrc + off + lane * 16, lds_addr(&qs[0][0]) + off);
+  }
+  const bool has_step = my_wave < p.n_steps;
+  if (has_step) after_q += issue_step(my_wave);
+  if (n_mine > 0) {
+    issue_page(0);
+    after_q += PG::DMA;
+  }
+  if (wave == 0) wait_vm_upto(after_q);   // q has landed
+  __syncthreads();
+  {
+    // raw query (bf16 or f32) -> f32 * sm_scale * log2(e), in place
+    constexpr int PER = (HG * D + kThreads - 1) / kThreads;
+    float qv[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = tid + k * kThreads;
+      qv[k] = 0.f;
+      if (i < HG * D)
+        qv[k] = p.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(&qs[0][0])[i])
+                         : (&qs[0][0])[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = tid + k * kThreads;
+      if (i < HG * D) (&qs[0][0])[i] = qv[k] * p.qscale;
+    }
+    __syncthreads();
+  }
+  // fold units handled by this lane: (head, lane group, k-step) -> 8 channels
+#pragma unroll
+  for (int r = 0; r < REPS; ++r) {
+    const int cidx = lane + 64 * r;
+    const int fh = cidx / PER_HEAD, fg = (cidx / KS) % 4, fk = cidx % KS;
+    const int c0 = fg * CPG + 8 * fk;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qreg[r][i] = cidx < COMBOS ? qs[fh][c0 + i] : 0.f;
+  }
+  if (has_step) {
+    if (n_mine > 0) wait_vm<PG::DMA>();   // the first page may stay in flight
+    else wait_vm<0>();
+    wait_lds();
+    __builtin_amdgcn_wave_barrier();
+    process_step(my_wave);
     wait_lds();
     __builtin_amdgcn_wave_barrier();
   }
 
-  // ---- pages: DMA pipeline, NBUF-1 pages ahead -------------------------------
-  {
-    constexpr int AHEAD = PG::NBUF - 1;
-#pragma unroll
-    for (int k = 0; k < AHEAD; ++k)
-      if (k < n_mine) issue_page(k);
+  // ---- pages: DMA pipeline, one page ahead (page 0 already requested) --------
 #pragma unroll 1
-    for (int k = 0; k < n_mine; ++k) {
-      wait_lds();   // the buffer about to be refilled has been read
-      __builtin_amdgcn_wave_barrier();
-      if (k + AHEAD < n_mine) issue_page(k + AHEAD);
-      const int ahead = n_mine - 1 - k < AHEAD ? n_mine - 1 - k : AHEAD;
-      if (ahead >= 2) wait_vm<2 * PG::DMA>();
-      else if (ahead == 1) wait_vm<PG::DMA>();
-      else wait_vm<0>();
-      __builtin_amdgcn_wave_barrier();
-      process_page(wbuf + (k % PG::NBUF) * PG::BYTES);
-    }
+  for (int k = 0; k < n_mine; ++k) {
+    wait_lds();   // the buffer about to be refilled has been read
+    __builtin_amdgcn_wave_barrier();
+    const bool next = k + 1 < n_mine;
+    if (next) issue_page(k + 1);
+    if (next) wait_vm<PG::DMA>();
+    else wait_vm<0>();
+    __builtin_amdgcn_wave_barrier();
+    process_page(wbuf + (k % PG::NBUF) * PG::BYTES);
   }
+
+  // ---- any further residual steps of this wave (when steps outnumber waves) --
+#pragma unroll 1
+  for (int hs = my_wave + waves_total; hs < p.n_steps; hs += waves_total) {
+    wait_lds();
+    __builtin_amdgcn_wave_barrier();
+    issue_step(hs);
+    wait_vm<0>();
+    wait_lds();
+    __builtin_amdgcn_wave_barrier();
+    process_step(hs);
+  }
+  wait_lds();
 
   // ---- wave epilogue -----------------------------------------------------------
   float lsum[HG], zsum[HG], mh[HG];
@@ -685,28 +761,68 @@ __global__ __launch_bounds__(kThreads) void kivi_mfma_kernel(MfmaParams p) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // this block's stores done
   __syncthreads();
   if (tid == 0) {
-    const int done = __hip_atomic_fetch_add(&p.counters[b * p.kv_heads + h], 1, __ATOMIC_RELAXED,
+    const int done = __hip_atomic_fetch_add(&p.counters[unit], 1, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
     last_block = done == p.splits - 1;
   }
   __syncthreads();
   if (!last_block) return;
-  for (int i = tid; i < HG * D; i += kThreads) {
-    const int hh = i / D, c = i % D;
-    const float* part = part_bh + static_cast<int64_t>(hh) * p.splits * (D + 2);
-    float M = -INFINITY;
-    for (int sp = 0; sp < p.splits; ++sp) M = fmaxf(M, load_coherent(part + sp * (D + 2)));
-    float so = 0.f, sl = 0.f;
-    for (int sp = 0; sp < p.splits; ++sp) {
-      const float* ps = part + sp * (D + 2);
-      const float e = fast_exp2(load_coherent(ps) - M);
-      sl = fmaf(e, load_coherent(ps + 1), sl);
-      so = fmaf(e, load_coherent(ps + 2 + c), so);
+  // each thread merges up to two output elements at a time, with the loads of
+  // a batch of 8 splits for both issued before any use
+  constexpr int PER = (HG * D + kThreads - 1) / kThreads;
+  constexpr int CH = PER < 2 ? PER : 2;
+  for (int e0 = 0; e0 < PER; e0 += CH) {
+    float M[CH], so[CH], sl[CH];
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      M[e] = -INFINITY;
+      so[e] = 0.f;
+      sl[e] = 0.f;
     }
-    p.out[(static_cast<int64_t>(b) * p.q_heads + h * HG + hh) * D + c] = so / sl;
+    for (int s0 = 0; s0 < p.splits; s0 += 8) {
+      float mv[CH][8], lv[CH][8], ov[CH][8];
+#pragma unroll
+      for (int e = 0; e < CH; ++e) {
+        const int i = tid + (e0 + e) * kThreads;
+        const int hh = (i < HG * D ? i : 0) / D, c = i % D;
+        const float* part = part_bh + static_cast<int64_t>(hh) * p.splits * (D + 2);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float* ps = part + (s0 + k < p.splits ? s0 + k : s0) * (D + 2);
+          mv[e][k] = load_coherent(ps);
+          lv[e][k] = load_coherent(ps + 1);
+          ov[e][k] = load_coherent(ps + 2 + c);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < CH; ++e) {
+        float bm = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) bm = s0 + k < p.splits ? fmaxf(bm, mv[e][k]) : bm;
+        const float Mn = fmaxf(M[e], bm);
+        const float a = fast_exp2(M[e] - Mn);
+        so[e] *= a;
+        sl[e] *= a;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float w8 = s0 + k < p.splits ? fast_exp2(mv[e][k] - Mn) : 0.f;
+          sl[e] = fmaf(w8, lv[e][k], sl[e]);
+          so[e] = fmaf(w8, ov[e][k], so[e]);
+        }
+        M[e] = Mn;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      const int i = tid + (e0 + e) * kThreads;
+      if (i < HG * D) {
+        const int hh = i / D, c = i % D;
+        p.out[(static_cast<int64_t>(b) * p.q_heads + h * HG + hh) * D + c] = so[e] / sl[e];
+      }
+    }
   }
   if (tid == 0)
-    __hip_atomic_store(&p.counters[b * p.kv_heads + h], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int BITS, int D>
@@ -741,14 +857,14 @@ MfmaPlan mfma_plan(const Geometry& g, int64_t tokens, int32_t requested) {
   MfmaPlan pl{};
   const int64_t q = kivi_quantised(tokens, g.residual);
   pl.pages = static_cast<int32_t>(q / kPage);
-  pl.chunks = static_cast<int32_t>((tokens - q + 15) / 16);   // residual 16-token steps
+  pl.chunks = static_cast<int32_t>((tokens - q + 7) / 8);     // residual 8-token steps
   int64_t s;
   if (requested > 0) {
     s = requested;
   } else {
-    // about one resident round of blocks (two per CU on 256 CUs), >= 8 pages each
+    // about one resident round of blocks (three per CU on 256 CUs), >= 8 pages each
     const int64_t units = static_cast<int64_t>(g.batch) * g.kv_heads;
-    s = (512 + units - 1) / units;
+    s = (768 + units - 1) / units;
     const int64_t cap = (pl.pages + 7) / 8;
     if (s > cap) s = cap;
   }
@@ -775,7 +891,7 @@ hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t st) {
   p.T = a.tokens;
   p.q_tokens = static_cast<int64_t>(pl.pages) * kPage;
   p.n_pages = pl.pages;
-  p.n_halves = pl.chunks;
+  p.n_steps = pl.chunks;
   p.splits = pl.page_splits;
   p.kv_heads = g.kv_heads;
   p.q_heads = g.q_heads;
