@@ -15,8 +15,17 @@ query and writes the output; append reads the new K/V rows and writes the ring
 (and, on flush steps, reads 32 ring rows and writes the page).
 
 Also reported: quantize-append tokens/s for the 4096-token prefill of each
-layer, the decode kernel against the HBM roofline (per-launch HIP events on
-the launch stream), and the CPU oracle on a bounded sample.
+layer, the decode kernel against the HBM roofline, and the CPU oracle on a
+bounded sample.
+
+Roofline: the decode kernel's algorithmic bytes per launch (the bytes a decode
+call must move: packed codes, scales and offsets of every page, the residual
+rows, the query and the output) divided by its average launch duration. That
+duration is measured with HIP events recorded on the launch stream around a
+burst of back-to-back decode launches over the 32 layers (so no host launch
+latency is counted), after the timed steps. `--copy-calibration` runs only a
+plain device-to-device copy of 256 MiB, whose hardware FETCH_SIZE/WRITE_SIZE
+counters calibrate the decode kernel's counter readings into HBM bytes.
 """
 
 import argparse
@@ -34,6 +43,39 @@ import kv_cache_quantisation_amd as kvq  # noqa: E402
 import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
+
+# Hardware byte counters of the decode kernel (rocprofv3 --pmc, FETCH_SIZE and
+# WRITE_SIZE in separate runs of this script with its default settings; median
+# KiB per dispatch over the roofline burst at context 4119), with the scale that
+# turns each counter into bytes: a plain 256 MiB device copy
+# (`--copy-calibration`) reads FETCH_SIZE = 131084 KiB for 262144 KiB read and
+# WRITE_SIZE = 262144 KiB for 262144 KiB written. The readings hold only for the
+# kernel sources they were taken with (SHA-256 over DECODE_SOURCES); after any
+# change to those, `traffic` is reported as null until they are taken again.
+COUNTERS = {
+    "kivi2": {"context": 4119, "fetch_kib": 31916.28125, "write_kib": 2156.0,
+              "fetch_scale": 262144 / 131084, "write_scale": 1.0,
+              "sources_sha256": "c1f5591625d21dcc1df4388f3b42f7e360877c2f855ece76939f743b5bc5f5d9"},
+}
+DECODE_SOURCES = ["decode_mfma.hip", "kvq_device.h", "kvq_internal.h"]
+
+
+def decode_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "kv_cache_quantisation_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counter_traffic(w, context):
+    """HBM bytes per decode launch from the stored counter readings, or None."""
+    c = COUNTERS.get(w.name)
+    if (not c or c["fetch_kib"] is None or c["context"] != context
+            or c["sources_sha256"] != decode_sources_sha256()):
+        return None
+    return round((c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024)
 METRIC = "decode-attn effective HBM GB/s (% of MI355X peak) + quantize-append tokens/s"
 
 
@@ -123,27 +165,31 @@ def gpu_bench(args, w):
                       for i in range(W, W + K))
     gbs = total_bytes / (total_ms * 1e-3) / 1e9
 
-    # decode kernel alone: per-launch event pairs on the launch stream
+    # decode kernel alone: HIP events on the launch stream around bursts of
+    # back-to-back launches (every layer once per burst)
     T_end = T0 + W + K
-    n_rep = 3
-    evs = []
+    n_rep = 4
+    for layer in range(L):   # warm the launch path at this context length
+        kvq.kvq_decode_attention(cfg, cache, layer, T_end, qs[layer], outs[layer], ws, stream=stream)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
     for _ in range(n_rep):
         for layer in range(L):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
             kvq.kvq_decode_attention(cfg, cache, layer, T_end, qs[layer], outs[layer], ws,
                                      stream=stream)
-            b.record(stream)
-            evs.append((a, b))
+    b.record(stream)
     torch.cuda.synchronize()
-    launch_us = [a.elapsed_time(b) * 1e3 for a, b in evs]
-    avg_us = sum(launch_us) / len(launch_us)
+    avg_us = a.elapsed_time(b) * 1e3 / (n_rep * L)
     per_launch = decode_bytes(w, T_end)
     achieved = per_launch / (avg_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "kvq decode (split + merge)", "avg_launch_us": round(avg_us, 2),
-                "bytes_per_launch": per_launch}
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": counter_traffic(w, T_end),
+                "kernel": f"kivi_mfma_kernel<{w.bits},{w.head_dim},{w.q_heads // w.kv_heads}> "
+                          "(decode, merge fused)",
+                "avg_launch_us": round(avg_us, 3), "bytes_per_launch": per_launch,
+                "context": T_end}
     return {
         "ms_per_step": total_ms / K, "gbs": gbs, "append_tps": append_tps,
         "prefill_ms_per_layer": prefill_ms, "prefill_gbs": prefill_bytes / (prefill_ms * 1e-3) / 1e9,
@@ -151,37 +197,59 @@ def gpu_bench(args, w):
     }
 
 
-def cpu_baseline(w, budget_s=12.0, max_units=256):
-    """The oracle (as it stands) on a bounded sample: decode attention of whole
-    (sequence, KV head) units of one layer at the workload's context, each unit
-    quantised, dequantised and attended by the oracle on the host."""
+def cpu_baseline(w, layers, budget_s=12.0):
+    """The oracle (as it stands) on a bounded sample of the workload: decode
+    attention of whole (sequence, KV head) units at the workload's context,
+    layer after layer, each unit quantised, dequantised and attended by the
+    oracle on one host thread, until about budget_s seconds of oracle work."""
     import numpy as np
     from oracle.cache import OracleCache
     from threadpoolctl import threadpool_limits
-    k, v = synth.keys_values(w, layer=0, device="cpu")
-    q = synth.query(w, layer=0, device="cpu")
-    raw_k = k.view(torch.int16).numpy().view(np.uint16)
-    raw_v = v.view(torch.int16).numpy().view(np.uint16)
     hg = w.q_heads // w.kv_heads
     T = w.tokens
     one = synth.scaled(w, batch=1, kv_heads=1, q_heads=hg)
-    done, t0 = 0, time.perf_counter()
-    units = [(b, h) for b in range(w.batch) for h in range(w.kv_heads)]
+    done, spent = 0, 0.0
     with threadpool_limits(limits=1):
-        for b, h in units[:max_units]:
-            oc = OracleCache(w.scheme, w.bits, 1, 1, 1, w.head_dim, T, residual=w.residual)
-            oc.append(0, raw_k[b:b + 1, :, h:h + 1], raw_v[b:b + 1, :, h:h + 1])
-            qv = q[b:b + 1, h * hg:(h + 1) * hg].float().numpy()
-            oc.decode(0, qv)
-            done += 1
-            if time.perf_counter() - t0 > budget_s:
+        for layer in range(layers):
+            k, v = synth.keys_values(w, layer=layer, device="cpu")
+            q = synth.query(w, layer=layer, device="cpu")
+            raw_k = k.view(torch.int16).numpy().view(np.uint16)
+            raw_v = v.view(torch.int16).numpy().view(np.uint16)
+            for b in range(w.batch):
+                for h in range(w.kv_heads):
+                    qv = q[b:b + 1, h * hg:(h + 1) * hg].float().numpy()
+                    t0 = time.perf_counter()
+                    oc = OracleCache(w.scheme, w.bits, 1, 1, 1, w.head_dim, T, residual=w.residual)
+                    oc.append(0, raw_k[b:b + 1, :, h:h + 1], raw_v[b:b + 1, :, h:h + 1])
+                    oc.decode(0, qv)
+                    spent += time.perf_counter() - t0
+                    done += 1
+                    if spent > budget_s:
+                        break
+                if spent > budget_s:
+                    break
+            del k, v
+            if spent > budget_s:
                 break
-    dt = time.perf_counter() - t0
     byts = decode_bytes(one, T) * done
-    return {"value": round(byts / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {len(units)} (sequence, KV head) units of one layer at "
-                      f"{T} tokens: oracle quantise + fp64 dequantise + fp64 attention, "
-                      f"{dt:.1f} s on one host thread"}
+    return {"value": round(byts / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} (sequence, KV head) units at {T} tokens (layers in order, "
+                      f"{w.batch * w.kv_heads} units per layer): oracle quantise + fp64 "
+                      f"dequantise + fp64 attention, {spent:.1f} s of oracle time on one host "
+                      f"thread; value = algorithmic decode bytes of those units / that time"}
+
+
+def copy_calibration(mib=256, reps=5):
+    """A plain device copy of known size, for calibrating the byte counters."""
+    dev = torch.device("cuda", 0)
+    n = mib * (1 << 20) // 4
+    x = torch.randn(n, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        torch.mul(x, 1.0, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4,
+                      "reps": reps}), flush=True)
 
 
 def main():
@@ -192,7 +260,12 @@ def main():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--workload", default="kivi2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the hot path shards "
               "by (sequence, KV head) with no communication, so more GPUs only repeat the "
@@ -202,7 +275,7 @@ def main():
     if w.scheme != synth.KIVI:
         sys.exit("bench.py times the KIVI workloads")
     r = gpu_bench(args, w)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.layers)
     line = {
         "metric": METRIC,
         "value": round(r["gbs"], 1),
