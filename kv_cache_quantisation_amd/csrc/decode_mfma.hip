@@ -14,8 +14,11 @@
 //           after the product.
 //   values: O[h][c] += sum_t P'_ht code_tc,  P'_ht = p_ht s_t, plus
 //           sum_t p_ht z_t added to every channel at the end.
-//           A = P' [16 rows x 32 tokens] (rows 0..HG-1 hi, HG..2HG-1 lo),
-//           B = value codes [32 tokens x 16 channels].
+//           v_mfma_f32_16x16x32_bf16: A = P' [16 rows x 32 tokens] (rows
+//           0..HG-1 the bf16 nearest value, HG..2HG-1 the bf16 remainder: 16
+//           bits at any magnitude, so tiny weights keep their relative
+//           precision), B = value codes [32 tokens x 16 channels] as exact
+//           bf16 integers.
 //
 // The unquantised residual tokens (bf16) take the same path 8 tokens at a
 // time (one half of a 16-row tile): A = key rows as stored, B = q split into three bf16 parts (hi, mid,
@@ -28,10 +31,11 @@
 // and {16+4g..16+4g+3}: the lane and token set the P.V A-operand needs, so P
 // never moves between lanes. Value codes are fed in that token order (for
 // channel c, tokens 4g..4g+3 are byte g of its 2-bit column, bytes 2g, 2g+1 of
-// its 4-bit column). Codes become exact f16 integers with the scaled converts:
+// its 4-bit column). Codes become exact small integers with the scaled converts:
 // a 2-bit code in an FP4 E2M1 nibble is code/2 (scale 2), a 4-bit code in an
-// FP8 E4M3 byte is code * 2^-9 (scale 512); the converts produce channels in
-// the order {0,2,1,3,4,6,5,7} within each 8, and q' is laid out to match.
+// FP8 E4M3 byte is code * 2^-9 (scale 512), to f16 for keys and bf16 for
+// values; the converts produce channels in the order {0,2,1,3,4,6,5,7} within
+// each 8, and q' is laid out to match.
 //
 // Memory: each wave streams its pages HBM -> LDS with global_load_lds_dwordx4
 // (16 bytes per lane, a whole page in 4-11 instructions), one page ahead of
@@ -56,6 +60,7 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -223,15 +228,19 @@ __device__ __forceinline__ void split_f16(float a, float b, uint32_t& hi, uint32
   lo = bits32(r);
 }
 
+// f32 pair -> packed bf16 (hi, nearest) and packed bf16 remainder (lo); hi + lo
+// carries 16 significant bits of each value at any magnitude (no subnormal
+// floor, unlike f16), and the rounding is unbiased.
+__device__ __forceinline__ void split_bf16(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const uint32_t h = __builtin_bit_cast(uint32_t, bf16x2{static_cast<__bf16>(a), static_cast<__bf16>(b)});
+  const float ha = __uint_as_float(h << 16), hb = __uint_as_float(h & 0xFFFF0000u);
+  hi = h;
+  lo = __builtin_bit_cast(uint32_t, bf16x2{static_cast<__bf16>(a - ha), static_cast<__bf16>(b - hb)});
+}
+
 // bf16 value of x by truncation (top 16 bits); x - trunc(x) is exact in f32.
 __device__ __forceinline__ float bf16_trunc(float x) {
   return __uint_as_float(__float_as_uint(x) & 0xFFFF0000u);
-}
-// bf16 value of x rounded to nearest even; x - rne(x) is exact in f32.
-__device__ __forceinline__ float bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return __uint_as_float(u & 0xFFFF0000u);
 }
 // Packs the bf16 top halves of a (low) and b (high) into one word.
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -446,40 +455,46 @@ __global__ __launch_bounds__(kThreads, 3) void kivi_mfma_kernel(MfmaParams p) {
     }
     // P' into A fragments: token order {4g+0,4g+2,4g+1,4g+3, 16+4g+0,...}
     uint32_t ph[4], pl[4];
-    split_f16(pv[0], pv[2], ph[0], pl[0]);
-    split_f16(pv[1], pv[3], ph[1], pl[1]);
-    split_f16(pv[4], pv[6], ph[2], pl[2]);
-    split_f16(pv[5], pv[7], ph[3], pl[3]);
+    split_bf16(pv[0], pv[2], ph[0], pl[0]);
+    split_bf16(pv[1], pv[3], ph[1], pl[1]);
+    split_bf16(pv[4], pv[6], ph[2], pl[2]);
+    split_bf16(pv[5], pv[7], ph[3], pl[3]);
     // rows j < HG: hi of head j; rows j >= HG: lo of lane j-HG (rows >= 2HG
     // only reach accumulator rows that are never read)
     uint32_t pa[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) pa[i] = shr_keep<HG>(ph[i], pl[i]);
-    const half8 ap = cat4h(pa[0], pa[1], pa[2], pa[3]);
+    const bf16x8 ap = __builtin_bit_cast(bf16x8, uint4{pa[0], pa[1], pa[2], pa[3]});
 
     // P' x value codes; channel of N-tile nt in column j is NT*j + nt
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const uint8_t* col = pg + PG::OFF_VC + (NT * j + nt) * VROW;
-      half8 bv;
+      uint4 bw;
       if constexpr (BITS == 2) {
         const uint2 v2 = *reinterpret_cast<const uint2*>(col);
         // byte g of each word: tokens 4g..4g+3 and 16+4g..16+4g+3
         const uint32_t x = __builtin_amdgcn_perm(v2.y, v2.x, 0x0C0C0400u + 0x0101u * g);
         const uint32_t y0 = x & 0x3333u, y1 = (x >> 2) & 0x3333u;
-        bv = cat4h(bits32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y0, 2.0f, 0)),
-                   bits32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y1, 2.0f, 0)),
-                   bits32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y0, 2.0f, 1)),
-                   bits32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y1, 2.0f, 1)));
+        bw = uint4{bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y0, 2.0f, 0)),
+                   bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 0)),
+                   bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y0, 2.0f, 1)),
+                   bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 1))};
       } else {
         // bytes 2g,2g+1 (tokens 4g..4g+3) and 8+2g, 9+2g (tokens 16+4g..)
         const uint32_t lo = reinterpret_cast<const uint32_t*>(col)[g >> 1];
         const uint32_t hi = reinterpret_cast<const uint32_t*>(col)[2 + (g >> 1)];
         const uint32_t sh = (g & 1) * 2;
         const uint32_t sel = (0x0100u + 0x0101u * sh) | ((0x0504u + 0x0101u * sh) << 16);
-        bv = codes4_frag(__builtin_amdgcn_perm(hi, lo, sel));
+        const uint32_t w = __builtin_amdgcn_perm(hi, lo, sel);
+        const uint32_t y0 = w & 0x0F0F0F0Fu, y1 = (w >> 4) & 0x0F0F0F0Fu;
+        bw = uint4{bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y0, 512.0f, false)),
+                   bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y1, 512.0f, false)),
+                   bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y0, 512.0f, true)),
+                   bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y1, 512.0f, true))};
       }
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, bv, acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, __builtin_bit_cast(bf16x8, bw), acc[nt],
+                                                         0, 0, 0);
     }
   };
 
@@ -560,13 +575,8 @@ __global__ __launch_bounds__(kThreads, 3) void kivi_mfma_kernel(MfmaParams p) {
     for (int r = 0; r < 4; ++r) l_lane += sc[r];   // absent tokens contribute 0
     // P in bf16 hi/lo rows; k index 8g+i holds token 4g+i for i < 4, zero after
     uint32_t ph[2], pl[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const float a0 = sc[2 * i], a1 = sc[2 * i + 1];
-      const float h0 = bf16_rne(a0), h1 = bf16_rne(a1);
-      ph[i] = pack_bf16(h0, h1);
-      pl[i] = pack_bf16(a0 - h0, a1 - h1);
-    }
+    split_bf16(sc[0], sc[1], ph[0], pl[0]);
+    split_bf16(sc[2], sc[3], ph[1], pl[1]);
     uint32_t pa[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) pa[i] = shr_keep<HG>(ph[i], pl[i]);

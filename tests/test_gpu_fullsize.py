@@ -1,0 +1,114 @@
+"""Parity at the five workloads' full sizes, through the C ABI, in the launch
+configuration the benchmark uses: the whole context appended by one
+quantize-append call (plus one appended token for the FP8 workload), then one
+decode call with the automatic split plan.
+
+The oracle cannot redo a whole cache of this size quickly, so sampled
+(sequence, KV head) units are checked: sampled pages bit-exact against the
+oracle's page images, every residual-ring row bit-exact, and the decode output
+rows of the unit's query-head group within 2e-3 of the oracle's fp64
+attention over that unit's dequantised keys and values."""
+
+import numpy as np
+import pytest
+import torch
+
+import harness as H
+import kv_cache_quantisation_amd as kvq
+import synth
+from oracle import accounting, layout
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+PAGE = 32
+
+# (sequence, KV head) units checked per workload
+UNITS = {
+    "tiny": [(0, 0), (0, 1), (0, 2), (0, 3)],
+    "kivi2": [(0, 0), (7, 3), (15, 7)],
+    "fp8": [(0, 0), (37, 5), (63, 7)],
+    "int4": [(0, 0), (31, 7)],
+    "longctx": [(0, 6)],
+}
+
+
+def sampled_pages(n_pages, k=8):
+    """First and last pages and a spread in between."""
+    if n_pages <= 3 * k:
+        return list(range(n_pages))
+    mid = np.linspace(k, n_pages - k - 1, k).astype(int).tolist()
+    return sorted(set(range(k)) | set(mid) | set(range(n_pages - k, n_pages)))
+
+
+def page_image(w, kf, vf, p, T, ks=None, vs=None):
+    """Oracle (bytes, mask) of page p of one unit holding T tokens."""
+    n = min(PAGE, T - p * PAGE)
+    k32 = np.zeros((PAGE, w.head_dim), np.float32)
+    v32 = np.zeros((PAGE, w.head_dim), np.float32)
+    k32[:n], v32[:n] = kf[p * PAGE:p * PAGE + n], vf[p * PAGE:p * PAGE + n]
+    if w.scheme == synth.KIVI:
+        return layout.kivi_page(k32, v32, w.bits)
+    if w.scheme == synth.SYM_TOKEN:
+        return layout.sym_page(k32, v32, w.bits, n)
+    return layout.fp8_page(k32, v32, ks, vs, n)
+
+
+@pytest.mark.parametrize("name", list(UNITS))
+def test_fullsize_workload(name):
+    w = synth.WORKLOADS[name]
+    extra = 1 if name == "fp8" else 0
+    T = w.tokens + extra
+    print(f"[fullsize] {name}: B={w.batch} Hkv={w.kv_heads} d={w.head_dim} T={T}", flush=True)
+    cfg = H.config(w, T)
+    cache = kvq.alloc_cache(cfg, zero=False)
+    k, v = synth.keys_values(w, device=DEV)
+    ks = vs = None
+    if w.scheme == synth.FP8_E4M3:
+        ks, vs = synth.fp8_scales(k, v)
+    kvq.kvq_quantize_append(cfg, cache, 0, 0, w.tokens, k, v, ks, vs)
+    if extra:
+        k1, v1 = synth.keys_values(w, tokens=1, device=DEV, tag=1)
+        kvq.kvq_quantize_append(cfg, cache, 0, w.tokens, 1, k1, v1, ks, vs)
+        k, v = torch.cat([k, k1], dim=1), torch.cat([v, v1], dim=1)
+    q = synth.query(w, device=DEV)
+    out = H.decode(cfg, cache, 0, T, q, ks, vs)
+    torch.cuda.synchronize()
+
+    slab = cache.numel() // (w.batch * w.kv_heads)
+    assert slab * w.batch * w.kv_heads == cache.numel()
+    itemsize = 2 if w.in_dtype == torch.bfloat16 else 4
+    ps = accounting.page_bytes(w.scheme, w.head_dim, w.bits)
+    hg = w.q_heads // w.kv_heads
+    qv = H.values(q)
+    outh = out.cpu().numpy()
+    for b, h in UNITS[name]:
+        kf, vf = H.values(k[b, :, h]), H.values(v[b, :, h])
+        ksh = None if ks is None else float(ks[h])
+        vsh = None if vs is None else float(vs[h])
+        got = cache[(b * w.kv_heads + h) * slab:(b * w.kv_heads + h + 1) * slab].cpu().numpy()
+        if w.scheme == synth.KIVI:
+            qtok, _ = accounting.flush_plan(T, w.residual)
+            n_pages = qtok // PAGE
+        else:
+            qtok, n_pages = T, -(-T // PAGE)
+        for p in sampled_pages(n_pages):
+            want, mask = page_image(w, kf, vf, p, T, ksh, vsh)
+            H.compare_bytes(got[p * ps:(p + 1) * ps], want, mask, f"{name} unit {b},{h} page {p}")
+        if w.scheme == synth.KIVI:
+            # residual ring: the input rows, bit for bit, in slot t mod (R + 32)
+            ring0 = accounting.pages_per_slab(synth.KIVI, T, w.residual) * ps
+            slots, row = w.residual + PAGE, w.head_dim * itemsize
+            rk = H.host(k[b, qtok:T, h]).view(np.uint8).reshape(T - qtok, row)
+            rv = H.host(v[b, qtok:T, h]).view(np.uint8).reshape(T - qtok, row)
+            for i, t in enumerate(range(qtok, T)):
+                s = t % slots
+                assert np.array_equal(got[ring0 + s * row:ring0 + (s + 1) * row], rk[i]), (name, t)
+                vo = ring0 + (slots + s) * row
+                assert np.array_equal(got[vo:vo + row], rv[i]), (name, t)
+        kh, vh = H.oracle_dequant_head(w, kf, vf, T, ksh, vsh)
+        want = H.oracle_attend_head(w, qv[b, h * hg:(h + 1) * hg], kh, vh, T)
+        err = float(np.max(np.abs(outh[b, h * hg:(h + 1) * hg].astype(np.float64) - want)))
+        print(f"[fullsize] {name} unit ({b},{h}): {len(sampled_pages(n_pages))} pages bit-exact, "
+              f"decode max-abs error {err:.2e}", flush=True)
+        assert err <= H.ATOL, (name, b, h, err)
+    assert np.isfinite(outh).all()
