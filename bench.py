@@ -106,6 +106,87 @@ def append_bytes(w, T_old, n, in_bytes=2):
     return w.batch * w.kv_heads * (rd + wr)
 
 
+def token_bytes(w):
+    """Cache bytes per token per KV head (codes + fp32 metadata) of a
+    non-KIVI scheme."""
+    d, b = w.head_dim, w.bits
+    if w.scheme == synth.SYM_TOKEN:
+        return 2 * (d * b // 8 + 4)
+    return 2 * d   # FP8: one byte per value, per-head scales are arguments
+
+
+def any_decode_bytes(w, T):
+    """Algorithmic bytes of one decode call for any scheme."""
+    in_b = 2 if w.in_dtype == torch.bfloat16 else 4
+    q_b = 2 if w.q_dtype == torch.bfloat16 else 4
+    if w.scheme == synth.KIVI:
+        return decode_bytes(w, T, in_b, q_b)
+    hg = w.q_heads // w.kv_heads
+    return w.batch * w.kv_heads * (T * token_bytes(w) + hg * w.head_dim * (q_b + 4))
+
+
+def any_append_bytes(w, T_old, n):
+    """Algorithmic bytes of appending n tokens for any scheme."""
+    in_b = 2 if w.in_dtype == torch.bfloat16 else 4
+    if w.scheme == synth.KIVI:
+        return append_bytes(w, T_old, n, in_b)
+    return w.batch * w.kv_heads * n * (2 * w.head_dim * in_b + token_bytes(w))
+
+
+def workload_kernels(name, reps=5):
+    """Times the path's kernels on one workload at its full size: the prefill
+    quantize-append (one call for the whole context), the 1-token append, and
+    decode over the full context (back-to-back launches between HIP events)."""
+    dev = torch.device("cuda", 0)
+    w = synth.WORKLOADS[name]
+    T = w.tokens
+    dt = {torch.bfloat16: kvq.KVQ_BF16, torch.float32: kvq.KVQ_F32}
+    cfg = kvq.make_config(w.scheme, w.bits, 1, w.q_heads, w.kv_heads, w.head_dim, w.batch, T + 1,
+                          residual=w.residual, in_dtype=dt[w.in_dtype], q_dtype=dt[w.q_dtype],
+                          rope_theta=w.rope_theta)
+    cache = kvq.alloc_cache(cfg, device=dev, zero=False)
+    k, v = synth.keys_values(w, device=dev)
+    ks = vs = None
+    if w.scheme == synth.FP8_E4M3:
+        ks, vs = synth.fp8_scales(k, v)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    pre_us = timed(lambda: kvq.kvq_quantize_append(cfg, cache, 0, 0, T, k, v, ks, vs, stream=stream),
+                   reps)
+    del k, v
+    k1, v1 = synth.keys_values(w, tokens=1, device=dev, tag=1)
+    app_us = timed(lambda: kvq.kvq_quantize_append(cfg, cache, 0, T, 1, k1, v1, ks, vs,
+                                                   stream=stream), reps)
+    q = synth.query(w, device=dev)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    ws = kvq.alloc_workspace(cfg, T + 1, device=dev)
+    dec_us = timed(lambda: kvq.kvq_decode_attention(cfg, cache, 0, T + 1, q, out, ws, k_scale=ks,
+                                                    v_scale=vs,
+                                                    stream=stream), reps)
+    pre_b, app_b, dec_b = any_append_bytes(w, 0, T), any_append_bytes(w, T, 1), \
+        any_decode_bytes(w, T + 1)
+    return {
+        "workload": name, "batch": w.batch, "context": T, "bits": w.bits,
+        "prefill_us": round(pre_us, 2), "prefill_gbs": round(pre_b / pre_us / 1e3, 1),
+        "prefill_tokens_per_s": round(w.batch * T / (pre_us * 1e-6)),
+        "append1_us": round(app_us, 2), "append1_gbs": round(app_b / app_us / 1e3, 1),
+        "decode_us": round(dec_us, 2), "decode_gbs": round(dec_b / dec_us / 1e3, 1),
+        "decode_frac_of_hbm_peak": round(dec_b / dec_us / 1e3 / HBM_PEAK_GBS, 4),
+        "decode_bytes": dec_b, "prefill_bytes": pre_b,
+    }
+
+
 def gpu_bench(args, w):
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -262,9 +343,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device copy (counter calibration)")
+    ap.add_argument("--workload-kernels", nargs="*", metavar="NAME",
+                    help="only time prefill, 1-token append and decode of the named "
+                         "workloads at full size (one JSON line each)")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.workload_kernels is not None:
+        for name in args.workload_kernels or list(synth.WORKLOADS):
+            print(json.dumps(workload_kernels(name)), flush=True)
+            torch.cuda.empty_cache()
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the hot path shards "

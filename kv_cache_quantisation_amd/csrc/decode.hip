@@ -440,6 +440,7 @@ hipError_t launch_merge(float* partials, float* out, int rows, int splits, int d
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   const Geometry& g = a.g;
   if (mfma_path(g)) return launch_kivi_mfma(a, st);
+  if (fp8_mfma_path(g)) return launch_fp8_mfma(a, st);
   DecodeParams p{};
   p.layer_base = a.layer_base;
   p.q = static_cast<const uint8_t*>(a.q);

@@ -1,0 +1,428 @@
+// Decode attention over an FP8 E4M3 cache on the matrix cores (gfx950).
+//
+// softmax(sm_scale q.K^T) V over the dequantised cache ("Quantizing the KV
+// cache", going deeper; FP8 cache with a scale per KV head, "How the KV cache
+// is quantized"). The dequantised key is e * ks_h and the value e * vs_h with
+// e the E4M3 value of the stored byte, so the key scale folds into the query
+// once per call and the value scale multiplies the output once:
+//
+//   scores: S^T[t][h] = sum_c e_tc (q_hc ks_h)   v_mfma_f32_16x16x32_f16,
+//           A = E4M3 key bytes converted to f16 (exact), B = q' = q ks_h
+//           split into an f16 high part (columns 0..HG-1) and remainder
+//           (columns HG..2HG-1); B stays in registers for the whole call.
+//   values: O[h][c] = vs_h sum_t p_ht e_tc       v_mfma_f32_16x16x32_bf16,
+//           A = p in bf16 high/remainder rows, B = E4M3 value bytes converted
+//           to bf16 (exact).
+//
+// Operand layouts (wave64): lane l holds A[l%16][8(l/16)+i], B[8(l/16)+i][l%16]
+// and C[4(l/16)+r][l%16]. Key tile mt (0, 1) row rho holds token
+// 8(rho/4) + 4 mt + rho%4 of the page, so lane (j, g) = (l%16, l/16) ends up
+// with head j's scores for tokens 8g..8g+7 -- exactly the k-block of the P.V
+// A operand, and the 8 value bytes of a channel it needs are contiguous.
+//
+// Pages (32 tokens, 64*d bytes) stream HBM -> LDS with global_load_lds_dwordx4,
+// one page ahead of the one being computed. The last page of a cache may be
+// partial: its absent tokens get score -inf and their value bytes are zeroed
+// before conversion (unwritten bytes may hold E4M3 NaN patterns). Blocks of a
+// (sequence, KV head) write partial (m, l, o); the last block to finish merges
+// them and writes the output.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+#include "kvq_wave.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct Fp8Params {
+  const uint8_t* layer_base;
+  const uint8_t* q;
+  const float* k_scale;           // [kv_heads] of this layer
+  const float* v_scale;
+  float* out;
+  float* partials;
+  int* counters;                  // one per (sequence, KV head), zero between calls
+  int64_t slab_bytes, page_bytes;
+  int64_t T;
+  int32_t n_pages, last_valid;    // pages holding tokens; tokens in the last one
+  int32_t splits;
+  int32_t kv_heads, q_heads;
+  int32_t q_bf16;
+  float qscale;                   // sm_scale * log2(e)
+};
+
+template <int D>
+struct Fp8Page {
+  static constexpr int OFF_VC = 32 * D;            // V cols after the K rows
+  static constexpr int BYTES = 64 * D;
+  static constexpr int DMA = BYTES / 1024;          // 16-byte-per-lane copies
+  static constexpr int NBUF = 2;
+  static constexpr int WAVE_LDS = NBUF * BYTES;
+};
+
+// Two E4M3 bytes (low or high half of w) -> packed f16 / bf16, exact.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_f16(uint32_t w) {
+  return bits32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_bf16(uint32_t w) {
+  return bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+template <int D, int HG>
+__global__ __launch_bounds__(kThreads, 2) void fp8_mfma_kernel(Fp8Params p) {
+  static_assert(2 * HG <= 16, "high and remainder columns of the GQA group fit one tile");
+  using PG = Fp8Page<D>;
+  constexpr int KS = D / 32;             // k-steps of the key product
+  constexpr int NT = D / 16;             // channel tiles of the value product
+  constexpr int CPG = D / 4;             // key channels per lane group (contiguous bytes)
+  constexpr int RED = kWaves * HG * (D + 2) * 4;
+  constexpr int ARENA = kWaves * PG::WAVE_LDS > RED ? kWaves * PG::WAVE_LDS : RED;
+
+  __shared__ __attribute__((aligned(16))) float qs[HG][D];
+  __shared__ __attribute__((aligned(16))) uint8_t arena[ARENA];
+  __shared__ int last_block;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 15, g = lane >> 4;
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int unit = b * p.kv_heads + h;
+  const uint8_t* slab = p.layer_base + static_cast<int64_t>(unit) * p.slab_bytes;
+  uint8_t* wbuf = arena + wave * PG::WAVE_LDS;
+
+  // pages of this block, every kWaves-th one per wave
+  const int pg0 = static_cast<int>(static_cast<int64_t>(split) * p.n_pages / p.splits);
+  const int pg1 = static_cast<int>(static_cast<int64_t>(split + 1) * p.n_pages / p.splits);
+  const int n_mine = pg0 + wave < pg1 ? (pg1 - pg0 - wave + kWaves - 1) / kWaves : 0;
+
+  auto issue_page = [&](int k) {
+    const uint8_t* src = slab + static_cast<int64_t>(pg0 + wave + kWaves * k) * p.page_bytes;
+    const uint32_t dst = lds_addr(wbuf + (k % PG::NBUF) * PG::BYTES);
+#pragma unroll
+    for (int i = 0; i < PG::DMA; ++i) dma16(src + i * 1024 + lane * 16, dst + i * 1024);
+  };
+  if (n_mine > 0) issue_page(0);   // in flight while the query is staged
+
+  // ---- query group: q * sm_scale * log2(e) * ks_h ----------------------------
+  {
+    const float mult = p.qscale * p.k_scale[h];
+    const int64_t q0 = (static_cast<int64_t>(b) * p.q_heads + h * HG) * D;
+    for (int i = tid; i < HG * D; i += kThreads) {
+      const float x = p.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(p.q)[q0 + i])
+                               : reinterpret_cast<const float*>(p.q)[q0 + i];
+      (&qs[0][0])[i] = x * mult;
+    }
+  }
+  __syncthreads();
+  // B operand of the key product for this lane: column j is head j % HG's
+  // high part (j < HG), its remainder (HG <= j < 2HG) or zero.
+  half8 bq[KS];
+  {
+    const int hh = j % HG, part = j / HG;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint32_t w4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = qs[hh][g * CPG + 8 * ks + 2 * i];
+        const float c = qs[hh][g * CPG + 8 * ks + 2 * i + 1];
+        uint32_t hi, lo;
+        split_f16(a, c, hi, lo);
+        w4[i] = part == 0 ? hi : (part == 1 ? lo : 0u);
+      }
+      bq[ks] = cat4h(w4[0], w4[1], w4[2], w4[3]);
+    }
+  }
+
+  // ---- per-wave online softmax -----------------------------------------------
+  floatx4 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_lane = -INFINITY, l_lane = 0.f;
+
+  auto process_page = [&](const uint8_t* pg, int n_valid) {
+    // scores; tile mt row rho = token 8(rho/4) + 4mt + rho%4
+    float s[8];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int row = 8 * (j >> 2) + 4 * mt + (j & 3);
+      const uint8_t* kr = pg + row * D + g * CPG;
+      floatx4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint2 w = *reinterpret_cast<const uint2*>(kr + 8 * ks);
+        const half8 a = cat4h(e4m3x2_f16<false>(w.x), e4m3x2_f16<true>(w.x),
+                              e4m3x2_f16<false>(w.y), e4m3x2_f16<true>(w.y));
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[ks], c, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[4 * mt + r] = c[r] + row_shl<HG>(c[r]);
+    }
+    if (n_valid < kPage) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[i] = 8 * g + i < n_valid ? s[i] : -INFINITY;
+    }
+    // online softmax: running max per head (lanes j < HG), weights 2^(s - m)
+    float pmax = s[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) pmax = fmaxf(pmax, s[i]);
+    pmax = fmaxf(pmax, xor16(pmax));
+    pmax = fmaxf(pmax, xor32(pmax));
+    const float m_new = fmaxf(m_lane, pmax);
+    if (__builtin_amdgcn_ballot_w64((j < HG) && (m_new > m_lane)) != 0) {
+      const float alpha = fast_exp2(m_lane - m_new);
+      l_lane *= alpha;
+      m_lane = m_new;
+      float a_h[HG];
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh)
+        a_h[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), hh));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float a = a_h[r % HG];
+        if constexpr (HG == 8) a = (g & 1) ? a_h[4 + r] : a_h[r];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= a;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      s[i] = fast_exp2(s[i] - m_lane);
+      l_lane += s[i];
+    }
+    // P rows: j < HG high part of head j, HG <= j < 2HG remainder of head j-HG
+    uint32_t ph[4], pl[4], pa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) split_bf16(s[2 * i], s[2 * i + 1], ph[i], pl[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pa[i] = shr_keep<HG>(ph[i], pl[i]);
+    const bf16x8 ap = __builtin_bit_cast(bf16x8, uint4{pa[0], pa[1], pa[2], pa[3]});
+    // value bytes of tokens 8g..8g+7 of channel NT*j + nt; absent tokens -> 0
+    uint32_t m0 = 0xFFFFFFFFu, m1 = 0xFFFFFFFFu;
+    if (n_valid < kPage) {
+      const int k = min(max(n_valid - 8 * g, 0), 8);
+      m0 = k >= 4 ? 0xFFFFFFFFu : (1u << (8 * k)) - 1u;
+      m1 = k >= 8 ? 0xFFFFFFFFu : (k <= 4 ? 0u : (1u << (8 * (k - 4))) - 1u);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const uint2 w = *reinterpret_cast<const uint2*>(pg + PG::OFF_VC + (NT * j + nt) * kPage + 8 * g);
+      const uint32_t x0 = w.x & m0, x1 = w.y & m1;
+      const uint4 bw = uint4{e4m3x2_bf16<false>(x0), e4m3x2_bf16<true>(x0),
+                             e4m3x2_bf16<false>(x1), e4m3x2_bf16<true>(x1)};
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, __builtin_bit_cast(bf16x8, bw), acc[nt],
+                                                         0, 0, 0);
+    }
+  };
+
+  // ---- pages: DMA pipeline, one page ahead ----------------------------------
+#pragma unroll 1
+  for (int k = 0; k < n_mine; ++k) {
+    wait_lds();   // the buffer about to be refilled has been read
+    __builtin_amdgcn_wave_barrier();
+    const bool next = k + 1 < n_mine;
+    if (next) issue_page(k + 1);
+    if (next) wait_vm<PG::DMA>();
+    else wait_vm<0>();
+    __builtin_amdgcn_wave_barrier();
+    const int page = pg0 + wave + kWaves * k;
+    process_page(wbuf + (k % PG::NBUF) * PG::BYTES, page == p.n_pages - 1 ? p.last_valid : kPage);
+  }
+  wait_lds();
+
+  // ---- wave epilogue -----------------------------------------------------------
+  float lsum[HG], mh[HG];
+  {
+    float l_ = l_lane;
+    l_ += xor16(l_);
+    l_ += xor32(l_);
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      lsum[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_), hh));
+      mh[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_lane), hh));
+    }
+  }
+  __syncthreads();   // every wave is done with its page buffers (the arena)
+  float* red = reinterpret_cast<float*>(arena);   // [wave][HG][D + 2]: m, l, o
+  auto R = [&](int w, int hh) { return red + (w * HG + hh) * (D + 2); };
+  // acc rows 4g+r: row < HG is head row (high), HG <= row < 2HG head row-HG (remainder)
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float x = acc[nt][r];
+      if constexpr (HG == 1) {
+        x = r == 0 ? acc[nt][0] + acc[nt][1] : 0.f;
+      } else if constexpr (HG == 2) {
+        x = r < 2 ? acc[nt][r] + acc[nt][r + 2] : 0.f;
+      } else if constexpr (HG == 4) {
+        x += xor16(x);
+      } else {
+        x += xor32(x);
+      }
+      v[r] = x;
+    }
+    const int c = NT * j + nt;
+    if (4 * g < HG) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int hh = 4 * g + r;
+        if (hh < HG) R(wave, hh)[2 + c] = v[r];
+      }
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      R(wave, hh)[0] = mh[hh];
+      R(wave, hh)[1] = lsum[hh];
+    }
+  }
+  __syncthreads();
+
+  // ---- combine the waves; write the output, or this block's partial --------
+  const float vs_h = p.v_scale[h];
+  float* part_bh = p.partials + (static_cast<int64_t>(b) * p.q_heads + h * HG) * p.splits * (D + 2);
+  for (int i = tid; i < HG * D; i += kThreads) {
+    const int hh = i / D, c = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, R(w, hh)[0]);
+    float so = 0.f, sl = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float e = fast_exp2(R(w, hh)[0] - M);   // idle wave: m = -inf -> 0
+      so = fmaf(e, R(w, hh)[2 + c], so);
+      sl = fmaf(e, R(w, hh)[1], sl);
+    }
+    so *= vs_h;
+    const int hq = h * HG + hh;
+    if (p.splits == 1) {
+      p.out[(static_cast<int64_t>(b) * p.q_heads + hq) * D + c] = so / sl;
+    } else {
+      float* part = part_bh + (static_cast<int64_t>(hh) * p.splits + split) * (D + 2);
+      store_coherent(part + 2 + c, so);
+      if (c == 0) {
+        store_coherent(part, M);
+        store_coherent(part + 1, sl);
+      }
+    }
+  }
+  if (p.splits == 1) return;
+
+  // ---- the last block of this (sequence, KV head) merges every partial ------
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  if (tid == 0) {
+    const int done = __hip_atomic_fetch_add(&p.counters[unit], 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    last_block = done == p.splits - 1;
+  }
+  __syncthreads();
+  if (!last_block) return;
+  for (int i = tid; i < HG * D; i += kThreads) {
+    const int hh = i / D, c = i % D;
+    const float* part = part_bh + static_cast<int64_t>(hh) * p.splits * (D + 2);
+    float M = -INFINITY, so = 0.f, sl = 0.f;
+    for (int s0 = 0; s0 < p.splits; s0 += 8) {
+      float mv[8], lv[8], ov[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float* ps = part + (s0 + k < p.splits ? s0 + k : s0) * (D + 2);
+        mv[k] = load_coherent(ps);
+        lv[k] = load_coherent(ps + 1);
+        ov[k] = load_coherent(ps + 2 + c);
+      }
+      float bm = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) bm = s0 + k < p.splits ? fmaxf(bm, mv[k]) : bm;
+      const float Mn = fmaxf(M, bm);
+      const float a = fast_exp2(M - Mn);
+      so *= a;
+      sl *= a;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float e = s0 + k < p.splits ? fast_exp2(mv[k] - Mn) : 0.f;
+        sl = fmaf(e, lv[k], sl);
+        so = fmaf(e, ov[k], so);
+      }
+      M = Mn;
+    }
+    p.out[(static_cast<int64_t>(b) * p.q_heads + h * HG + hh) * D + c] = so / sl;
+  }
+  if (tid == 0)
+    __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int D>
+hipError_t by_hg(const Fp8Params& p, int hg, int batch, hipStream_t st) {
+  dim3 grid(p.splits, p.kv_heads, batch);
+  switch (hg) {
+    case 1: hipLaunchKernelGGL((fp8_mfma_kernel<D, 1>), grid, dim3(kThreads), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((fp8_mfma_kernel<D, 2>), grid, dim3(kThreads), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((fp8_mfma_kernel<D, 4>), grid, dim3(kThreads), 0, st, p); break;
+    default: hipLaunchKernelGGL((fp8_mfma_kernel<D, 8>), grid, dim3(kThreads), 0, st, p); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool fp8_mfma_path(const Geometry& g) {
+  return g.scheme == KVQ_FP8_E4M3 && g.rope == 0.0 && g.d >= 64;
+}
+
+int32_t fp8_mfma_splits(const Geometry& g, int64_t tokens, int32_t requested) {
+  const int64_t pages = (tokens + kPage - 1) / kPage;
+  int64_t s;
+  if (requested > 0) {
+    s = requested;
+  } else {
+    // about one resident round of blocks (two per CU on 256 CUs), >= 8 pages each
+    const int64_t units = static_cast<int64_t>(g.batch) * g.kv_heads;
+    s = (512 + units - 1) / units;
+    const int64_t cap = (pages + 7) / 8;
+    if (s > cap) s = cap;
+  }
+  if (s > pages) s = pages;
+  return static_cast<int32_t>(s < 1 ? 1 : s);
+}
+
+hipError_t launch_fp8_mfma(const DecodeArgs& a, hipStream_t st) {
+  const Geometry& g = a.g;
+  Fp8Params p{};
+  p.layer_base = a.layer_base;
+  p.q = static_cast<const uint8_t*>(a.q);
+  p.k_scale = a.k_scale;
+  p.v_scale = a.v_scale;
+  p.out = a.out;
+  p.partials = reinterpret_cast<float*>(a.workspace + workspace_partials_offset(g));
+  p.counters = reinterpret_cast<int*>(a.workspace);
+  p.slab_bytes = g.slab_bytes;
+  p.page_bytes = g.page_bytes;
+  p.T = a.tokens;
+  p.n_pages = static_cast<int32_t>((a.tokens + kPage - 1) / kPage);
+  p.last_valid = static_cast<int32_t>(a.tokens - static_cast<int64_t>(p.n_pages - 1) * kPage);
+  p.splits = fp8_mfma_splits(g, a.tokens, a.requested_splits);
+  p.kv_heads = g.kv_heads;
+  p.q_heads = g.q_heads;
+  p.q_bf16 = a.q_dtype == KVQ_BF16;
+  p.qscale = a.sm_scale * kLog2e;
+  switch (g.d) {
+    case 64: return by_hg<64>(p, g.hg, g.batch, st);
+    case 128: return by_hg<128>(p, g.hg, g.batch, st);
+    default: return by_hg<256>(p, g.hg, g.batch, st);
+  }
+}
+
+}  // namespace kvq

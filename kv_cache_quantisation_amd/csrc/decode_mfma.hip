@@ -53,14 +53,11 @@
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "kvq_wave.h"
 
 namespace kvq {
 namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -96,65 +93,6 @@ struct PageGeom {
   static constexpr int WAVE_LDS = NBUF * BYTES + RING;
 };
 
-// ---- wave-level helpers ------------------------------------------------------
-
-// HBM -> LDS copy of 16 bytes per active lane: lane l writes lds_base + 16 l.
-// lds_base must be the same in every lane of the wave.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(base), "v"(src) : "memory");
-}
-
-// Waits until at most N vector-memory operations of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  // vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14; expcnt, lgkmcnt: no wait
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Waits until at most n (0..15; larger values wait for 15) vector-memory
-// operations of this wave are outstanding.
-__device__ __forceinline__ void wait_vm_upto(int n) {
-  switch (n) {
-    case 0: wait_vm<0>(); break;
-    case 1: wait_vm<1>(); break;
-    case 2: wait_vm<2>(); break;
-    case 3: wait_vm<3>(); break;
-    case 4: wait_vm<4>(); break;
-    case 5: wait_vm<5>(); break;
-    case 6: wait_vm<6>(); break;
-    case 7: wait_vm<7>(); break;
-    case 8: wait_vm<8>(); break;
-    case 9: wait_vm<9>(); break;
-    case 10: wait_vm<10>(); break;
-    case 11: wait_vm<11>(); break;
-    case 12: wait_vm<12>(); break;
-    case 13: wait_vm<13>(); break;
-    case 14: wait_vm<14>(); break;
-    default: wait_vm<15>(); break;
-  }
-}
-
-// Waits for this wave's LDS operations.
-__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
-}
-
-// 2^x on the transcendental unit; results below 2^-126 flush to zero, which
-// only drops negligible softmax weights.
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ half8 cat4h(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  return __builtin_bit_cast(half8, uint4{a, b, c, d});
-}
-
-template <typename V2>
-__device__ __forceinline__ uint32_t bits32(V2 v) { return __builtin_bit_cast(uint32_t, v); }
-
 // 16 two-bit codes (one word) -> two 8-channel fragments, channel order
 // {0,2,1,3,4,6,5,7} within each 8.
 __device__ __forceinline__ void codes2_frags(uint32_t w, half8& f0, half8& f1) {
@@ -176,83 +114,6 @@ __device__ __forceinline__ half8 codes4_frag(uint32_t w) {
                bits32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(y1, 512.0f, false)),
                bits32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(y0, 512.0f, true)),
                bits32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(y1, 512.0f, true)));
-}
-
-// Sum over aligned groups of 8 lanes (all lanes receive it).
-__device__ __forceinline__ float sum8(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));  // row_half_mirror
-  return v;
-}
-
-// Sum over the 16 lanes of each DPP row (all lanes receive it).
-__device__ __forceinline__ float row_sum16(float v) {
-  v = sum8(v);
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));  // row_mirror
-  return v;
-}
-
-// Value of lane l ^ 32.
-__device__ __forceinline__ float xor32(float v) {
-  const int lane = threadIdx.x & 63;
-  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
-                                            false, false);
-  return __builtin_bit_cast(float, lane < 32 ? r[1] : r[0]);
-}
-
-// Value of lane l ^ 16 (within each half of the wave).
-__device__ __forceinline__ float xor16(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
-                                                               (0x10 << 10) | 0x1F));
-}
-
-template <int SHIFT>
-__device__ __forceinline__ float row_shl(float v) {  // lane l gets lane l+SHIFT of its row
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                               0x100 + SHIFT, 0xF, 0xF, false));
-}
-
-// Lane l gets v of lane l-SHIFT of its row; lanes with no such source keep `keep`.
-template <int SHIFT>
-__device__ __forceinline__ uint32_t shr_keep(uint32_t keep, uint32_t v) {
-  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(keep), static_cast<int>(v),
-                                                           0x110 + SHIFT, 0xF, 0xF, false));
-}
-
-// f32 pair -> packed f16 (hi) and packed f16 remainder (lo), hi + lo ~ x.
-__device__ __forceinline__ void split_f16(float a, float b, uint32_t& hi, uint32_t& lo) {
-  const auto h = __builtin_amdgcn_cvt_pkrtz(a, b);
-  const auto r = __builtin_amdgcn_cvt_pkrtz(a - static_cast<float>(h[0]), b - static_cast<float>(h[1]));
-  hi = bits32(h);
-  lo = bits32(r);
-}
-
-// f32 pair -> packed bf16 (hi, nearest) and packed bf16 remainder (lo); hi + lo
-// carries 16 significant bits of each value at any magnitude (no subnormal
-// floor, unlike f16), and the rounding is unbiased.
-__device__ __forceinline__ void split_bf16(float a, float b, uint32_t& hi, uint32_t& lo) {
-  const uint32_t h = __builtin_bit_cast(uint32_t, bf16x2{static_cast<__bf16>(a), static_cast<__bf16>(b)});
-  const float ha = __uint_as_float(h << 16), hb = __uint_as_float(h & 0xFFFF0000u);
-  hi = h;
-  lo = __builtin_bit_cast(uint32_t, bf16x2{static_cast<__bf16>(a - ha), static_cast<__bf16>(b - hb)});
-}
-
-// bf16 value of x by truncation (top 16 bits); x - trunc(x) is exact in f32.
-__device__ __forceinline__ float bf16_trunc(float x) {
-  return __uint_as_float(__float_as_uint(x) & 0xFFFF0000u);
-}
-// Packs the bf16 top halves of a (low) and b (high) into one word.
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
-}
-
-// Device-scope (all XCDs) relaxed store / load of a split partial.
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ float load_q(const uint8_t* base, int64_t idx, int bf16) {

@@ -159,6 +159,8 @@ int64_t workspace_bytes(const Geometry& g, int64_t tokens, int32_t requested) {
   if (mfma_path(g)) {
     const MfmaPlan pl = mfma_plan(g, tokens, requested);
     s = static_cast<int64_t>(pl.page_splits) + pl.ring_splits_max;
+  } else if (fp8_mfma_path(g)) {
+    s = fp8_mfma_splits(g, tokens, requested);
   } else {
     s = decode_splits(g, tokens, requested);
   }

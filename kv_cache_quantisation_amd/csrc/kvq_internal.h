@@ -75,6 +75,10 @@ struct MfmaPlan {
 bool mfma_path(const Geometry& g);
 MfmaPlan mfma_plan(const Geometry& g, int64_t tokens, int32_t requested);
 hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t stream);
+// Matrix-core path of FP8 E4M3 caches (head_dim >= 64, no rotary embedding).
+bool fp8_mfma_path(const Geometry& g);
+int32_t fp8_mfma_splits(const Geometry& g, int64_t tokens, int32_t requested);
+hipError_t launch_fp8_mfma(const DecodeArgs& a, hipStream_t stream);
 // Merges `splits` partials (m, l, o[d]) per row into out (rows = batch*q_heads).
 hipError_t launch_merge(float* partials, float* out, int rows, int splits, int d,
                         hipStream_t stream);

@@ -153,6 +153,46 @@ def test_decode_mfma_pages(bits, d, hg, R, T, dtype):
     assert err <= H.ATOL, err
 
 
+FP8_CASES = [
+    # FP8 pages on the matrix cores: GQA widths, head_dim 64/128/256, partial
+    # last pages (T % 32 = 0, 1, 17, 31), single-page caches, split counts
+    (d, hg, T, dtype, splits)
+    for (d, hg, T, dtype, splits) in [
+        (128, 4, 333, torch.bfloat16, 0), (128, 1, 32, torch.bfloat16, 0),
+        (128, 2, 257, torch.float32, 3), (128, 8, 95, torch.bfloat16, 1),
+        (64, 4, 1, torch.bfloat16, 0), (64, 8, 500, torch.float32, 7),
+        (256, 4, 161, torch.bfloat16, 2), (256, 1, 5, torch.float32, 0),
+        (128, 4, 1024, torch.bfloat16, 40)]
+]
+
+
+@pytest.mark.parametrize("d,hg,T,dtype,splits", FP8_CASES)
+def test_decode_fp8_mfma(d, hg, T, dtype, splits):
+    w = small(synth.FP8_E4M3, 8, d, dtype, 0, hg=hg, T=T)
+    cfg, cache, oc, k, v, ks, vs = run_append(w, [T], capacity=T + 40)
+    cfg.num_splits = splits
+    q = synth.query(w, device=DEV)
+    out = H.decode(cfg, cache, 0, T, q, ks, vs)
+    assert H.max_err(out, oc.decode(0, H.values(q))) <= H.ATOL
+
+
+def test_decode_fp8_unwritten_bytes_are_ignored():
+    """The cache beyond the last token holds 0xFF bytes (an E4M3 NaN pattern):
+    the partial last page must not let them into the scores or the output."""
+    w = small(synth.FP8_E4M3, 8, 128, torch.bfloat16, 0, hg=4, T=45)
+    cfg = H.config(w, 96)
+    cache = kvq.alloc_cache(cfg, zero=False)
+    cache.fill_(0xFF)
+    oc = H.oracle_cache(w, 96)
+    k, v = synth.keys_values(w, device=DEV)
+    ks, vs = synth.fp8_scales(k, v)
+    H.append_chunks(cfg, cache, k, v, [45], ks=ks, vs=vs, oc=oc)
+    q = synth.query(w, device=DEV)
+    out = H.decode(cfg, cache, 0, 45, q, ks, vs)
+    assert torch.isfinite(out).all()
+    assert H.max_err(out, oc.decode(0, H.values(q))) <= H.ATOL
+
+
 @pytest.mark.parametrize("bits", [2, 4])
 def test_decode_mfma_dynamic_range(bits):
     """Keys and values over many orders of magnitude: per-channel scales from
