@@ -60,23 +60,37 @@ __device__ __forceinline__ void stage_row_chunk(const uint8_t* src, float* dst, 
 }
 
 // ---- KIVI: encode one 32-token page per block --------------------------------
-// grid = (pages to flush, kv_heads, batch)
+// grid = (pages to flush, kv_heads, batch). The page's 32 key and value rows
+// are staged in LDS in the input dtype (padded rows); every thread then takes
+// part in the statistics (several threads per key channel / value token,
+// combined with lane shuffles) and in the codes (one or more packed words per
+// thread), where each quotient comes from a reciprocal with an exact fallback.
 template <int D, int BITS, int IB>
 __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
-  constexpr int LD = D + 1;                   // padded LDS row (no bank conflicts on columns)
   constexpr float kLevels = float((1 << BITS) - 1);
   constexpr int FPW = 32 / BITS;              // fields per 32-bit word
-  constexpr int CHUNKS = D * IB / 16;         // 16-byte chunks per row
-  __shared__ float ks_tile[kPage * LD];
-  __shared__ float vs_tile[kPage * LD];
-  __shared__ float k_mn[D], k_s[D], v_mn[kPage], v_s[kPage];
+  constexpr int ROW = D * IB;                 // bytes per input row
+  constexpr int PITCH = ROW + 16;             // padded LDS row
+  constexpr int CHUNKS = ROW / 16;            // 16-byte chunks per row
+  constexpr int TPC = kThreads / D > 1 ? kThreads / D : 1;   // threads per key channel
+  constexpr int RPT = kPage / TPC;            // rows per thread (key statistics)
+  constexpr int TPT = kThreads / kPage;       // threads per value token (8)
+  constexpr int CPT = D / TPT;                // channels per thread (value statistics)
+  static_assert(TPC <= 8 && (TPC & (TPC - 1)) == 0, "key statistics lane groups");
+  __shared__ __attribute__((aligned(16))) uint8_t tile[2][kPage * PITCH];   // K rows, V rows
+  __shared__ float k_mn[D], k_s[D], k_r[D], v_mn[kPage], v_s[kPage], v_r[kPage];
 
   const int tid = threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   const int64_t page = p.first_page + blockIdx.x;
   uint8_t* slab = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes;
   uint8_t* pg = slab + page * p.page_bytes;
-  const int64_t row_bytes = static_cast<int64_t>(D) * IB;
+
+  auto elem = [&](int which, int r, int c) -> float {
+    const uint8_t* row = tile[which] + r * PITCH;
+    if constexpr (IB == 2) return bf16_to_f32(reinterpret_cast<const uint16_t*>(row)[c]);
+    else return reinterpret_cast<const float*>(row)[c];
+  };
 
   // 1. stage the page's 32 key and value rows (ring for tokens < past, else input)
   for (int i = tid; i < 2 * kPage * CHUNKS; i += kThreads) {
@@ -87,43 +101,65 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
     const uint8_t* src;
     if (t < p.past) {
       const int64_t slot = t % p.ring_slots;
-      src = slab + p.ring_base + (which * p.ring_slots + slot) * row_bytes;
+      src = slab + p.ring_base + (which * p.ring_slots + slot) * ROW;
     } else {
       const int64_t j = t - p.past;
       const uint8_t* base = which ? p.v_new : p.k_new;
-      src = base + ((static_cast<int64_t>(b) * p.n + j) * p.kv_heads + h) * row_bytes;
+      src = base + ((static_cast<int64_t>(b) * p.n + j) * p.kv_heads + h) * ROW;
     }
-    stage_row_chunk<D, IB>(src, (which ? vs_tile : ks_tile) + r * LD, c);
+    *reinterpret_cast<uint4*>(tile[which] + r * PITCH + c * 16) =
+        *reinterpret_cast<const uint4*>(src + c * 16);
   }
   __syncthreads();
 
-  // 2. statistics: per key channel over the tokens, per value token over channels
-  for (int i = tid; i < D + kPage; i += kThreads) {
-    if (i < D) {
-      float mn = ks_tile[i], mx = ks_tile[i];
-      for (int r = 1; r < kPage; ++r) {
-        const float x = ks_tile[r * LD + i];
+  // 2a. key statistics per channel over the 32 tokens (TPC lanes per channel)
+  for (int c0 = 0; c0 < D; c0 += kThreads / TPC) {
+    const int c = c0 + tid / TPC, part = tid % TPC;
+    float mn = INFINITY, mx = -INFINITY;
+    if (c < D) {
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) {
+        const float x = elem(0, part * RPT + r, c);
         mn = fminf(mn, x);
         mx = fmaxf(mx, x);
       }
+    }
+#pragma unroll
+    for (int m = 1; m < TPC; m <<= 1) {
+      mn = fminf(mn, __shfl_xor(mn, m, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+    }
+    if (c < D && part == 0) {
       mn = mn + 0.0f;                          // -0 -> +0
       const float s = (mx - mn) / kLevels;
-      k_mn[i] = mn;
-      k_s[i] = s;
-      reinterpret_cast<float*>(pg + p.off_ks)[i] = s;
-      reinterpret_cast<float*>(pg + p.off_kz)[i] = mn;
-    } else {
-      const int r = i - D;
-      float mn = vs_tile[r * LD], mx = mn;
-      for (int c = 1; c < D; ++c) {
-        const float x = vs_tile[r * LD + c];
-        mn = fminf(mn, x);
-        mx = fmaxf(mx, x);
-      }
+      k_mn[c] = mn;
+      k_s[c] = s;
+      k_r[c] = __builtin_amdgcn_rcpf(s);
+      reinterpret_cast<float*>(pg + p.off_ks)[c] = s;
+      reinterpret_cast<float*>(pg + p.off_kz)[c] = mn;
+    }
+  }
+  // 2b. value statistics per token over the D channels (8 lanes per token)
+  {
+    const int r = tid / TPT, part = tid % TPT;
+    float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const float x = elem(1, r, part * CPT + i);
+      mn = fminf(mn, x);
+      mx = fmaxf(mx, x);
+    }
+#pragma unroll
+    for (int m = 1; m < TPT; m <<= 1) {
+      mn = fminf(mn, __shfl_xor(mn, m, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+    }
+    if (part == 0) {
       mn = mn + 0.0f;
       const float s = (mx - mn) / kLevels;
       v_mn[r] = mn;
       v_s[r] = s;
+      v_r[r] = __builtin_amdgcn_rcpf(s);
       reinterpret_cast<float*>(pg + p.off_vs)[r] = s;
       reinterpret_cast<float*>(pg + p.off_vz)[r] = mn;
     }
@@ -141,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
 #pragma unroll
     for (int j = 0; j < FPW; ++j) {
       const int c = c0 + j;
-      word |= quant_asym(ks_tile[t * LD + c], k_mn[c], k_s[c], kLevels) << (j * BITS);
+      word |= quant_asym_rcp(elem(0, t, c), k_mn[c], k_s[c], k_r[c], kLevels) << (j * BITS);
     }
     kc[w] = word;
   }
@@ -152,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
 #pragma unroll
     for (int j = 0; j < FPW; ++j) {
       const int t = t0 + j;
-      word |= quant_asym(vs_tile[t * LD + c], v_mn[t], v_s[t], kLevels) << (j * BITS);
+      word |= quant_asym_rcp(elem(1, t, c), v_mn[t], v_s[t], v_r[t], kLevels) << (j * BITS);
     }
     vc[w] = word;
   }

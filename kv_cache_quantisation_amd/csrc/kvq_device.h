@@ -30,6 +30,22 @@ __device__ __forceinline__ uint32_t quant_asym(float x, float mn, float s, float
   return static_cast<uint32_t>(r);
 }
 
+// The same code as quant_asym, computed with a reciprocal r ~ 1/s (v_rcp_f32,
+// 1 ulp): q = (x - mn) * r is within 2^-13 of the exactly rounded quotient for
+// quotients up to 256, so rint(q) equals rint of the IEEE quotient unless q is
+// within 2^-12 of a half-integer; those rare elements (and tiny scales, where
+// the reciprocal could flush) take the IEEE division.
+__device__ __forceinline__ uint32_t quant_asym_rcp(float x, float mn, float s, float r,
+                                                   float levels) {
+  if (s == 0.0f) return 0u;
+  const float a = x - mn;
+  float q = rintf(a * r);
+  const float t = a * r - q;
+  if (fabsf(t) > 0.5f - 0x1p-12f || !(s >= 0x1p-100f)) q = rintf(a / s);
+  q = fminf(fmaxf(q, 0.0f), levels);
+  return static_cast<uint32_t>(q);
+}
+
 // Symmetric code: clamp(rint(x / s), -Q, Q), 0 when s == 0; returned as the
 // low b bits of its two's complement.
 __device__ __forceinline__ uint32_t quant_sym(float x, float s, float qmax, uint32_t mask) {
