@@ -76,6 +76,7 @@ struct MfmaParams {
   int32_t kv_heads, q_heads;
   int32_t q_bf16;
   float qscale;
+  double rope_theta;              // > 0: keys cached before the rotary embedding
 };
 
 template <int BITS, int D>
@@ -121,9 +122,10 @@ __device__ __forceinline__ float load_q(const uint8_t* base, int64_t idx, int bf
   return reinterpret_cast<const float*>(base)[idx];
 }
 
-template <int BITS, int D, int HG>
-__global__ __launch_bounds__(kThreads, 3) void kivi_mfma_kernel(MfmaParams p) {
+template <int BITS, int D, int HG, bool ROPE>
+__global__ __launch_bounds__(kThreads, ROPE ? 2 : 3) void kivi_mfma_kernel(MfmaParams p) {
   static_assert(BITS == 2 || BITS == 4, "2- or 4-bit pages");
+  static_assert(!ROPE || (BITS == 2 && D <= 128), "rotary decode: 2-bit pages, head_dim <= 128");
   static_assert(2 * HG <= 16, "hi and lo columns of the GQA group fit one tile");
   using PG = PageGeom<BITS, D>;
   constexpr int KS = D / 32;             // k-steps of the key product
@@ -144,6 +146,10 @@ __global__ __launch_bounds__(kThreads, 3) void kivi_mfma_kernel(MfmaParams p) {
   // B fragments of q' for the live columns (hi, lo) of each lane group: [ks][g][2*HG]
   __shared__ __attribute__((aligned(16))) uint32_t frag[kWaves][KS][4][2 * HG][4];
   __shared__ __attribute__((aligned(16))) uint8_t arena[ARENA];              // page buffers / reduction
+  // rotary decode: each wave's query rotated for the page in hand (row HG is
+  // kept zero for the unused B columns), and omega_i / (2 pi) per channel pair
+  __shared__ __attribute__((aligned(16))) float qpage[ROPE ? kWaves : 1][ROPE ? HG + 1 : 1][ROPE ? D : 4];
+  __shared__ double w2pi[ROPE ? D / 2 : 1];
   __shared__ int last_block;
 
   const int tid = threadIdx.x;
@@ -207,6 +213,51 @@ __global__ __launch_bounds__(kThreads, 3) void kivi_mfma_kernel(MfmaParams p) {
   const int n_mine = pg0 + wave < pg1 ? (pg1 - pg0 - wave + kWaves - 1) / kWaves : 0;
 
   float qreg[REPS][8];   // this lane's fold units of q (set once q is staged)
+  // rotary decode: this lane's channel pairs are (D/8) g + m, m < D/8; rcos/rsin
+  // hold the rotation of tile row j (token 16 mt + j of a page) by omega_i, and
+  // qpair this lane's pair (lane) of every head's query
+  constexpr int NPL = ROPE ? D / 8 : 1;
+  float rcos[2][NPL], rsin[2][NPL], qpair[HG][2];
+
+  // qpage[wave][hh] = R(omega (T-1-t0)) q[hh]: scores of keys at t0 + j are then
+  // qpage . R(omega j) k (the rotations of query and key combine into one by
+  // the relative position)
+  auto rotate_q = [&](int64_t t0) {
+    if (lane < D / 2) {
+      const double turns = static_cast<double>(p.T - 1 - t0) * w2pi[lane];
+      float sn, cs;
+      sincospif(2.0f * static_cast<float>(turns - floor(turns)), &sn, &cs);
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) {
+        const float q0 = qpair[hh][0], q1 = qpair[hh][1];
+        *reinterpret_cast<float2*>(&qpage[wave][hh][2 * lane]) = float2{q0 * cs - q1 * sn, q0 * sn + q1 * cs};
+      }
+    }
+    wait_lds();
+    __builtin_amdgcn_wave_barrier();
+  };
+  // B values of the fp32 key product for this lane: column j is head j (or zero)
+  auto load_bq = [&](float* bqv) {
+    const float* src = &qpage[wave][j < HG ? j : HG][(D / 4) * g];
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      const float4 v = *reinterpret_cast<const float4*>(src + 4 * i);
+      bqv[4 * i] = v.x;
+      bqv[4 * i + 1] = v.y;
+      bqv[4 * i + 2] = v.z;
+      bqv[4 * i + 3] = v.w;
+    }
+  };
+  // y (this lane's D/4 channels, dequantised) -> R(omega tau) y, pair by pair
+  auto rotate_keys = [&](float* y, int mt) {
+#pragma unroll
+    for (int m = 0; m < NPL; ++m) {
+      const float x0 = y[2 * m], x1 = y[2 * m + 1];
+      const float c = rcos[mt][m], sn = rsin[mt][m];
+      y[2 * m] = x0 * c - x1 * sn;
+      y[2 * m + 1] = x0 * sn + x1 * c;
+    }
+  };
 
   auto issue_page = [&](int k) {   // page k of this wave -> buffer k % NBUF
     const uint8_t* src = slab + static_cast<int64_t>(pg0 + wave + kWaves * k) * p.page_bytes;
@@ -218,7 +269,42 @@ __global__ __launch_bounds__(kThreads, 3) void kivi_mfma_kernel(MfmaParams p) {
     }
   };
 
-  auto process_page = [&](const uint8_t* pg) {
+  auto process_page = [&](const uint8_t* pg, int64_t t0) {
+    float s[8];
+    if constexpr (ROPE) {
+      // scores of tile row j = qpage . R(omega tau) (code * s + z), tau = 16 mt + j,
+      // on v_mfma_f32_16x16x4f32 (lane group g holds channels (D/4) g ..)
+      rotate_q(t0);
+      float bqv[D / 4], sv[D / 4], zv[D / 4];
+      load_bq(bqv);
+      const float* sp = reinterpret_cast<const float*>(pg + PG::OFF_KS) + (D / 4) * g;
+      const float* zp = reinterpret_cast<const float*>(pg + PG::OFF_KZ) + (D / 4) * g;
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) {
+        const float4 a = *reinterpret_cast<const float4*>(sp + 4 * i);
+        const float4 c = *reinterpret_cast<const float4*>(zp + 4 * i);
+        sv[4 * i] = a.x; sv[4 * i + 1] = a.y; sv[4 * i + 2] = a.z; sv[4 * i + 3] = a.w;
+        zv[4 * i] = c.x; zv[4 * i + 1] = c.y; zv[4 * i + 2] = c.z; zv[4 * i + 3] = c.w;
+      }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const uint32_t* kp = reinterpret_cast<const uint32_t*>(pg + (16 * mt + j) * KROW + (D / 16) * g);
+        float y[D / 4];
+#pragma unroll
+        for (int w = 0; w < D / 64; ++w) {
+          const uint32_t word = kp[w];
+#pragma unroll
+          for (int c = 0; c < 16; ++c)
+            y[16 * w + c] = fmaf(static_cast<float>((word >> (2 * c)) & 3u), sv[16 * w + c], zv[16 * w + c]);
+        }
+        rotate_keys(y, mt);
+        floatx4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < D / 4; ++ks) c = __builtin_amdgcn_mfma_f32_16x16x4f32(y[ks], bqv[ks], c, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[4 * mt + r] = c[r];
+      }
+    } else {
     // q' = q * s per channel, split hi/lo into B fragments; bias q . z
     float bias_part[REPS];
 #pragma unroll
@@ -278,7 +364,6 @@ __global__ __launch_bounds__(kThreads, 3) void kivi_mfma_kernel(MfmaParams p) {
     }
 
     // scores S^T = codes x q'^T
-    float s[8];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const uint32_t* kp = reinterpret_cast<const uint32_t*>(pg + (16 * mt + j) * KROW + g * (KW * 4));
@@ -299,6 +384,7 @@ __global__ __launch_bounds__(kThreads, 3) void kivi_mfma_kernel(MfmaParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) s[4 * mt + r] = c[r] + row_shl<HG>(c[r]);
     }
+    }   // rotary / plain keys
 
     softmax_update(s, std::integral_constant<int, 8>{});
     const float4 vs0 = *reinterpret_cast<const float4*>(pg + PG::OFF_VS + 16 * g);
@@ -394,6 +480,25 @@ __global__ __launch_bounds__(kThreads, 3) void kivi_mfma_kernel(MfmaParams p) {
   auto process_step = [&](int hs) {
     const int64_t t0 = p.q_tokens + static_cast<int64_t>(hs) * RSTEP;
     const int nv = static_cast<int>(p.T - t0 < RSTEP ? p.T - t0 : RSTEP);
+    float sc[4];
+    if constexpr (ROPE) {
+      // key rows rotated by their position in the step, fp32 product as for pages
+      rotate_q(t0);
+      float bqv[D / 4], y[D / 4];
+      load_bq(bqv);
+      const uint16_t* kr = reinterpret_cast<const uint16_t*>(wring + (j & 7) * 2 * D) + (D / 4) * g;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) {
+        const uint4 v = *reinterpret_cast<const uint4*>(kr + 8 * i);
+        unpack_bf16x8(v, y + 8 * i);
+      }
+      rotate_keys(y, 0);
+      floatx4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < D / 4; ++ks) c = __builtin_amdgcn_mfma_f32_16x16x4f32(y[ks], bqv[ks], c, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[r] = (4 * g + r < nv) ? c[r] : -INFINITY;
+    } else {
     // B = q^T in three bf16 parts: columns [0,HG) hi, [HG,2HG) mid, [2HG,3HG) lo
     floatx4 cres[QB];
 #pragma unroll
@@ -420,7 +525,6 @@ __global__ __launch_bounds__(kThreads, 3) void kivi_mfma_kernel(MfmaParams p) {
         cres[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq, cres[qb], 0, 0, 0);
       }
     }
-    float sc[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float v;
@@ -431,6 +535,7 @@ __global__ __launch_bounds__(kThreads, 3) void kivi_mfma_kernel(MfmaParams p) {
       }
       sc[r] = (4 * g + r < nv) ? v : -INFINITY;
     }
+    }   // rotary / plain keys
     softmax_update(sc, std::integral_constant<int, 4>{});
 #pragma unroll
     for (int r = 0; r < 4; ++r) l_lane += sc[r];   // absent tokens contribute 0
@@ -472,6 +577,11 @@ __global__ __launch_bounds__(kThreads, 3) void kivi_mfma_kernel(MfmaParams p) {
     issue_page(0);
     after_q += PG::DMA;
   }
+  if constexpr (ROPE) {
+    for (int i = tid; i < D / 2; i += kThreads)
+      w2pi[i] = pow(p.rope_theta, -2.0 * i / D) * 0.15915494309189535;   // omega_i / (2 pi)
+    for (int i = lane; i < D; i += 64) qpage[wave][HG][i] = 0.f;
+  }
   if (wave == 0) wait_vm_upto(after_q);   // q has landed
   __syncthreads();
   {
@@ -493,6 +603,21 @@ __global__ __launch_bounds__(kThreads, 3) void kivi_mfma_kernel(MfmaParams p) {
       if (i < HG * D) (&qs[0][0])[i] = qv[k] * p.qscale;
     }
     __syncthreads();
+  }
+  if constexpr (ROPE) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int m = 0; m < NPL; ++m) {
+        const double turns = static_cast<double>(16 * mt + j) * w2pi[(D / 8) * g + m];
+        sincospif(2.0f * static_cast<float>(turns - floor(turns)), &rsin[mt][m], &rcos[mt][m]);
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      qpair[hh][0] = lane < D / 2 ? qs[hh][2 * lane] : 0.f;
+      qpair[hh][1] = lane < D / 2 ? qs[hh][2 * lane + 1] : 0.f;
+    }
   }
   // fold units handled by this lane: (head, lane group, k-step) -> 8 channels
 #pragma unroll
@@ -523,7 +648,8 @@ __global__ __launch_bounds__(kThreads, 3) void kivi_mfma_kernel(MfmaParams p) {
     if (next) wait_vm<PG::DMA>();
     else wait_vm<0>();
     __builtin_amdgcn_wave_barrier();
-    process_page(wbuf + (k % PG::NBUF) * PG::BYTES);
+    process_page(wbuf + (k % PG::NBUF) * PG::BYTES,
+                 static_cast<int64_t>(pg0 + wave + kWaves * k) * kPage);
   }
 
   // ---- any further residual steps of this wave (when steps outnumber waves) --
@@ -696,14 +822,14 @@ __global__ __launch_bounds__(kThreads, 3) void kivi_mfma_kernel(MfmaParams p) {
     __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int BITS, int D>
+template <int BITS, int D, bool ROPE>
 hipError_t by_hg(const MfmaParams& p, int hg, int batch, hipStream_t st) {
   dim3 grid(p.splits, p.kv_heads, batch);
   switch (hg) {
-    case 1: hipLaunchKernelGGL((kivi_mfma_kernel<BITS, D, 1>), grid, dim3(kThreads), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((kivi_mfma_kernel<BITS, D, 2>), grid, dim3(kThreads), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((kivi_mfma_kernel<BITS, D, 4>), grid, dim3(kThreads), 0, st, p); break;
-    default: hipLaunchKernelGGL((kivi_mfma_kernel<BITS, D, 8>), grid, dim3(kThreads), 0, st, p); break;
+    case 1: hipLaunchKernelGGL((kivi_mfma_kernel<BITS, D, 1, ROPE>), grid, dim3(kThreads), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((kivi_mfma_kernel<BITS, D, 2, ROPE>), grid, dim3(kThreads), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((kivi_mfma_kernel<BITS, D, 4, ROPE>), grid, dim3(kThreads), 0, st, p); break;
+    default: hipLaunchKernelGGL((kivi_mfma_kernel<BITS, D, 8, ROPE>), grid, dim3(kThreads), 0, st, p); break;
   }
   return hipGetLastError();
 }
@@ -711,17 +837,22 @@ hipError_t by_hg(const MfmaParams& p, int hg, int batch, hipStream_t st) {
 template <int BITS>
 hipError_t by_d(const MfmaParams& p, int d, int hg, int batch, hipStream_t st) {
   switch (d) {
-    case 64: return by_hg<BITS, 64>(p, hg, batch, st);
-    case 128: return by_hg<BITS, 128>(p, hg, batch, st);
-    default: return by_hg<BITS, 256>(p, hg, batch, st);
+    case 64: return by_hg<BITS, 64, false>(p, hg, batch, st);
+    case 128: return by_hg<BITS, 128, false>(p, hg, batch, st);
+    default: return by_hg<BITS, 256, false>(p, hg, batch, st);
   }
+}
+
+hipError_t by_d_rope(const MfmaParams& p, int d, int hg, int batch, hipStream_t st) {
+  return d == 64 ? by_hg<2, 64, true>(p, hg, batch, st) : by_hg<2, 128, true>(p, hg, batch, st);
 }
 
 }  // namespace
 
 bool mfma_path(const Geometry& g) {
-  return g.scheme == KVQ_KIVI && (g.bits == 2 || g.bits == 4) && g.d >= 64 && g.rope == 0.0 &&
-         g.in_bytes == 2;
+  if (g.scheme != KVQ_KIVI || g.d < 64 || g.in_bytes != 2) return false;
+  if (g.rope == 0.0) return g.bits == 2 || g.bits == 4;
+  return g.bits == 2 && g.d <= 128;   // rotary keys: 2-bit pages, head_dim 64 or 128
 }
 
 MfmaPlan mfma_plan(const Geometry& g, int64_t tokens, int32_t requested) {
@@ -733,9 +864,11 @@ MfmaPlan mfma_plan(const Geometry& g, int64_t tokens, int32_t requested) {
   if (requested > 0) {
     s = requested;
   } else {
-    // about one resident round of blocks (three per CU on 256 CUs), >= 8 pages each
+    // about one resident round of blocks (three per CU on 256 CUs, two with
+    // rotary keys), >= 8 pages each
     const int64_t units = static_cast<int64_t>(g.batch) * g.kv_heads;
-    s = (768 + units - 1) / units;
+    const int64_t target = g.rope == 0.0 ? 768 : 512;
+    s = (target + units - 1) / units;
     const int64_t cap = (pl.pages + 7) / 8;
     if (s > cap) s = cap;
   }
@@ -768,6 +901,8 @@ hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t st) {
   p.q_heads = g.q_heads;
   p.q_bf16 = a.q_dtype == KVQ_BF16;
   p.qscale = a.sm_scale * kLog2e;
+  p.rope_theta = a.rope_theta;
+  if (a.rope_theta > 0.0) return by_d_rope(p, g.d, g.hg, g.batch, st);
   return g.bits == 2 ? by_d<2>(p, g.d, g.hg, g.batch, st) : by_d<4>(p, g.d, g.hg, g.batch, st);
 }
 

@@ -153,6 +153,29 @@ def test_decode_mfma_pages(bits, d, hg, R, T, dtype):
     assert err <= H.ATOL, err
 
 
+ROPE_CASES = [
+    # KIVI 2-bit with keys cached before the rotary embedding, on the matrix
+    # cores: GQA widths, head_dim 64/128, residual windows, ring-only caches,
+    # split counts, a large base and a small one
+    (d, hg, R, T, theta, splits)
+    for (d, hg, R, T, theta, splits) in [
+        (128, 4, 128, 700, 500000.0, 0), (128, 1, 0, 321, 10000.0, 0),
+        (128, 2, 40, 1000, 500000.0, 5), (128, 8, 128, 260, 1e6, 1),
+        (64, 4, 128, 90, 10000.0, 0), (64, 8, 16, 777, 500000.0, 3),
+        (128, 4, 128, 3000, 500000.0, 64)]
+]
+
+
+@pytest.mark.parametrize("d,hg,R,T,theta,splits", ROPE_CASES)
+def test_decode_rope_mfma(d, hg, R, T, theta, splits):
+    w = small(synth.KIVI, 2, d, torch.bfloat16, R, hg=hg, T=T, rope=theta)
+    cfg, cache, oc, *_ = run_append(w, [T], capacity=T + 40)
+    cfg.num_splits = splits
+    q = synth.query(w, device=DEV)
+    out = H.decode(cfg, cache, 0, T, q)
+    assert H.max_err(out, oc.decode(0, H.values(q), rope_theta=theta)) <= H.ATOL
+
+
 FP8_CASES = [
     # FP8 pages on the matrix cores: GQA widths, head_dim 64/128/256, partial
     # last pages (T % 32 = 0, 1, 17, 31), single-page caches, split counts
