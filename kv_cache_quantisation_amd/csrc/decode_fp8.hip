@@ -108,7 +108,11 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_mfma_kernel(Fp8Params p) {
     const uint8_t* src = slab + static_cast<int64_t>(pg0 + wave + kWaves * k) * p.page_bytes;
     const uint32_t dst = lds_addr(wbuf + (k % PG::NBUF) * PG::BYTES);
 #pragma unroll
-    for (int i = 0; i < PG::DMA; ++i) dma16(src + i * 1024 + lane * 16, dst + i * 1024);
+    for (int i = 0; i < PG::DMA; ++i) {
+      const int off = i * 1024 + lane * 16;   // key rows: chunk permutation (see kswz)
+      const int from = off < PG::OFF_VC ? krow_off<D / 16>(off / D, off % D) : off;
+      dma16(src + from, dst + i * 1024);
+    }
   };
   if (n_mine > 0) issue_page(0);   // in flight while the query is staged
 
@@ -155,11 +159,10 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_mfma_kernel(Fp8Params p) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int row = 8 * (j >> 2) + 4 * mt + (j & 3);
-      const uint8_t* kr = pg + row * D + g * CPG;
       floatx4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const uint2 w = *reinterpret_cast<const uint2*>(kr + 8 * ks);
+        const uint2 w = *reinterpret_cast<const uint2*>(pg + krow_off<D / 16>(row, g * CPG + 8 * ks));
         const half8 a = cat4h(e4m3x2_f16<false>(w.x), e4m3x2_f16<true>(w.x),
                               e4m3x2_f16<false>(w.y), e4m3x2_f16<true>(w.y));
         c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[ks], c, 0, 0, 0);
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_mfma_kernel(Fp8Params p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) pa[i] = shr_keep<HG>(ph[i], pl[i]);
     const bf16x8 ap = __builtin_bit_cast(bf16x8, uint4{pa[0], pa[1], pa[2], pa[3]});
-    // value bytes of tokens 8g..8g+7 of channel NT*j + nt; absent tokens -> 0
+    // value bytes of tokens 8g..8g+7 of channel 16 nt + j; absent tokens -> 0
     uint32_t m0 = 0xFFFFFFFFu, m1 = 0xFFFFFFFFu;
     if (n_valid < kPage) {
       const int k = min(max(n_valid - 8 * g, 0), 8);
@@ -215,7 +218,7 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_mfma_kernel(Fp8Params p) {
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const uint2 w = *reinterpret_cast<const uint2*>(pg + PG::OFF_VC + (NT * j + nt) * kPage + 8 * g);
+      const uint2 w = *reinterpret_cast<const uint2*>(pg + PG::OFF_VC + (16 * nt + j) * kPage + 8 * g);
       const uint32_t x0 = w.x & m0, x1 = w.y & m1;
       const uint4 bw = uint4{e4m3x2_bf16<false>(x0), e4m3x2_bf16<true>(x0),
                              e4m3x2_bf16<false>(x1), e4m3x2_bf16<true>(x1)};
@@ -272,7 +275,7 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_mfma_kernel(Fp8Params p) {
       }
       v[r] = x;
     }
-    const int c = NT * j + nt;
+    const int c = 16 * nt + j;
     if (4 * g < HG) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {

@@ -132,6 +132,7 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : 3) void kivi_mfma_kernel(MfmaP
   constexpr int NT = D / 16;             // channel tiles of the value product
   constexpr int CPG = D / 4;             // key channels per lane group
   constexpr int KROW = D * BITS / 8;     // bytes per key token row
+  constexpr int CPR_K = KROW / 16;       // 16-byte chunks per key row
   constexpr int KW = CPG * BITS / 32;    // key-code words per lane per 16-token tile
   constexpr int VROW = 32 * BITS / 8;    // bytes per value channel column
   constexpr int COMBOS = HG * 4 * KS;    // (head, lane group, k-step) fold units
@@ -265,7 +266,9 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : 3) void kivi_mfma_kernel(MfmaP
 #pragma unroll
     for (int i = 0; i < PG::DMA; ++i) {
       const int off = i * 1024 + lane * 16;
-      if (i + 1 < PG::DMA || off < PG::BYTES) dma16(src + off, dst + i * 1024);
+      int from = off;   // key rows: chunk permutation (see kswz)
+      if (off < PG::CODES) from = krow_off<CPR_K>(off / KROW, off % KROW);
+      if (i + 1 < PG::DMA || off < PG::BYTES) dma16(src + from, dst + i * 1024);
     }
   };
 
@@ -288,11 +291,11 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : 3) void kivi_mfma_kernel(MfmaP
       }
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const uint32_t* kp = reinterpret_cast<const uint32_t*>(pg + (16 * mt + j) * KROW + (D / 16) * g);
         float y[D / 4];
 #pragma unroll
         for (int w = 0; w < D / 64; ++w) {
-          const uint32_t word = kp[w];
+          const uint32_t word =
+              *reinterpret_cast<const uint32_t*>(pg + krow_off<CPR_K>(16 * mt + j, (D / 16) * g + 4 * w));
 #pragma unroll
           for (int c = 0; c < 16; ++c)
             y[16 * w + c] = fmaf(static_cast<float>((word >> (2 * c)) & 3u), sv[16 * w + c], zv[16 * w + c]);
@@ -366,7 +369,10 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : 3) void kivi_mfma_kernel(MfmaP
     // scores S^T = codes x q'^T
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      const uint32_t* kp = reinterpret_cast<const uint32_t*>(pg + (16 * mt + j) * KROW + g * (KW * 4));
+      uint32_t kp[KW];
+#pragma unroll
+      for (int w = 0; w < KW; ++w)
+        kp[w] = *reinterpret_cast<const uint32_t*>(pg + krow_off<CPR_K>(16 * mt + j, g * (KW * 4) + 4 * w));
       floatx4 c = {bias_j, bias_j, bias_j, bias_j};   // hi column carries q . z
       if constexpr (BITS == 2) {
 #pragma unroll
@@ -413,10 +419,11 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : 3) void kivi_mfma_kernel(MfmaP
     for (int i = 0; i < 4; ++i) pa[i] = shr_keep<HG>(ph[i], pl[i]);
     const bf16x8 ap = __builtin_bit_cast(bf16x8, uint4{pa[0], pa[1], pa[2], pa[3]});
 
-    // P' x value codes; channel of N-tile nt in column j is NT*j + nt
+    // P' x value codes; channel of N-tile nt in column j is 16 nt + j (adjacent
+    // lanes read adjacent value columns: no LDS bank conflicts)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const uint8_t* col = pg + PG::OFF_VC + (NT * j + nt) * VROW;
+      const uint8_t* col = pg + PG::OFF_VC + (16 * nt + j) * VROW;
       uint4 bw;
       if constexpr (BITS == 2) {
         const uint2 v2 = *reinterpret_cast<const uint2*>(col);
@@ -549,7 +556,7 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : 3) void kivi_mfma_kernel(MfmaP
     const bf16x8 ap = __builtin_bit_cast(bf16x8, uint4{pa[0], pa[1], 0u, 0u});
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int c = NT * j + nt;
+      const int c = 16 * nt + j;
       const uint16_t* vr = reinterpret_cast<const uint16_t*>(wring + RSTEP * 2 * D) + c;
       const int t4 = (4 * g) & 7;             // tokens >= 8 carry weight 0
       const uint32_t v0 = vr[(t4 + 0) * D], v1 = vr[(t4 + 1) * D];
@@ -701,7 +708,7 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : 3) void kivi_mfma_kernel(MfmaP
       }
       v[r] = x;
     }
-    const int c = NT * j + nt;
+    const int c = 16 * nt + j;
     if (4 * g < HG) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {

@@ -147,4 +147,20 @@ __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Key rows of a page are copied HBM -> LDS with their 16-byte chunks permuted
+// inside each row: logical chunk h of row r sits at chunk h ^ kswz<CPR>(r)
+// (CPR = chunks per row, a power of two), so the rows that the 16 lanes of a
+// wave read together fall into different LDS banks.
+template <int CPR>
+__device__ __forceinline__ int kswz(int r) {
+  if constexpr (CPR >= 8) return r & 7;
+  else return (r * CPR / 8) % CPR;
+}
+
+// LDS byte offset of byte b of key row r (rows of CPR chunks, permuted as above).
+template <int CPR>
+__device__ __forceinline__ int krow_off(int r, int b) {
+  return r * (16 * CPR) + 16 * ((b >> 4) ^ kswz<CPR>(r)) + (b & 15);
+}
+
 }  // namespace kvq
