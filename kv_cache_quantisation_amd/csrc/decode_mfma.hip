@@ -144,8 +144,13 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : 3) void kivi_mfma_kernel(MfmaP
   static_assert(KW >= 1, "at least one word per lane");
 
   __shared__ __attribute__((aligned(16))) float qs[HG][D];
-  // B fragments of q' for the live columns (hi, lo) of each lane group: [ks][g][2*HG]
-  __shared__ __attribute__((aligned(16))) uint32_t frag[kWaves][KS][4][2 * HG][4];
+  // B fragments of q' for the live columns (hi, lo): [column][(4 ks + g) ^ column]
+  // in 16-byte slots; the XOR puts the 16 lanes that read one (ks, g) for
+  // different columns, and the 16 lanes that write one column, on different
+  // LDS banks (no padding: three blocks must fit a CU's LDS)
+  constexpr int FSTRIDE = 4 * KS;
+  static_assert(FSTRIDE >= 8, "column slots cover the XOR range");
+  __shared__ __attribute__((aligned(16))) uint32_t frag[kWaves][2 * HG * FSTRIDE][4];
   __shared__ __attribute__((aligned(16))) uint8_t arena[ARENA];              // page buffers / reduction
   // rotary decode: each wave's query rotated for the page in hand (row HG is
   // kept zero for the unused B columns), and omega_i / (2 pi) per channel pair
@@ -335,8 +340,10 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : 3) void kivi_mfma_kernel(MfmaP
       split_f16(qp[4], qp[6], hi[2], lo[2]);
       split_f16(qp[5], qp[7], hi[3], lo[3]);
       if (cidx < COMBOS) {
-        *reinterpret_cast<uint4*>(frag[wave][fk][fg][fh]) = uint4{hi[0], hi[1], hi[2], hi[3]};
-        *reinterpret_cast<uint4*>(frag[wave][fk][fg][HG + fh]) = uint4{lo[0], lo[1], lo[2], lo[3]};
+        *reinterpret_cast<uint4*>(frag[wave][fh * FSTRIDE + ((4 * fk + fg) ^ (fh & 7))]) =
+            uint4{hi[0], hi[1], hi[2], hi[3]};
+        *reinterpret_cast<uint4*>(frag[wave][(HG + fh) * FSTRIDE + ((4 * fk + fg) ^ ((HG + fh) & 7))]) =
+            uint4{lo[0], lo[1], lo[2], lo[3]};
       }
     }
     // bias of head j for this lane: the fold units of head hh are lanes
@@ -362,7 +369,8 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : 3) void kivi_mfma_kernel(MfmaP
     half8 bq[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const uint4 f = *reinterpret_cast<const uint4*>(frag[wave][ks][g][j % (2 * HG)]);
+      const int col = j % (2 * HG);
+      const uint4 f = *reinterpret_cast<const uint4*>(frag[wave][col * FSTRIDE + ((4 * ks + g) ^ (col & 7))]);
       bq[ks] = cat4h(f.x, f.y, f.z, f.w);
     }
 
