@@ -837,6 +837,542 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : 3) void kivi_mfma_kernel(MfmaP
     __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---- rotary keys, GQA group of 4: dense scores on v_mfma_f32_4x4x1_16b_f32 ----
+// Same result as kivi_mfma_kernel<2, D, 4, true> with the key product laid out
+// so that no MFMA column is wasted. Lane l takes token l % 32 of a page (or of
+// a residual step) and the channel half l / 32; the 16 blocks of the 4x4x1
+// instruction are (token quad, channel half) and its 4 columns the 4 heads, so
+// one instruction is one channel of 32 tokens x 4 heads for each half:
+//   A = R(omega j) (code * s + z) of the lane's token j and channel (fp32),
+//   B = qpage of the lane's head l % 4 and channel, qpage = R(omega (T-1-t0)) q.
+// The two halves are added across lanes (l, l ^ 32). Every lane then holds the
+// scores of tokens 4((l/4) % 8) + r of head l % 4, the running max of each head
+// is wave-uniform, and the weights P' are moved through LDS into the operand
+// layout of the value product (v_mfma_f32_16x16x32_bf16, as in
+// kivi_mfma_kernel).
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
+  constexpr int HG = 4, BITS = 2;
+  using PG = PageGeom<BITS, D>;
+  constexpr int NT = D / 16;             // channel tiles of the value product
+  constexpr int KROW = D * BITS / 8;     // bytes per key token row
+  constexpr int CPR_K = KROW / 16;
+  constexpr int HALF = D / 2;            // channels per lane
+  constexpr int NPL = HALF / 2;          // channel pairs per lane
+  constexpr int VROW = 32 * BITS / 8;    // bytes per value channel column
+  constexpr int RED = kWaves * HG * (D + 2) * 4;
+  constexpr int ARENA = kWaves * PG::WAVE_LDS > RED ? kWaves * PG::WAVE_LDS : RED;
+  constexpr int RSTEP = 8;
+
+  __shared__ __attribute__((aligned(16))) float qs[HG][D];
+  __shared__ __attribute__((aligned(16))) float qpage[kWaves][HG][D];
+  // weights P' of the page in hand, [hi/lo][head][32 tokens] in bf16, in the
+  // k order of the value operand
+  __shared__ __attribute__((aligned(16))) uint16_t pbuf[kWaves][2][HG][32];
+  __shared__ __attribute__((aligned(16))) uint8_t arena[ARENA];
+  __shared__ double w2pi[D / 2];
+  __shared__ int last_block;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 15, g = lane >> 4;          // 16x16 operand coordinates
+  const int hd = lane & 3;                          // head of this lane (4x4 column)
+  const int tk = lane & 31;                         // token of this lane (4x4 row)
+  const int hf = lane >> 5;                         // channel half of this lane
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int unit = b * p.kv_heads + h;
+  const uint8_t* slab = p.layer_base + static_cast<int64_t>(unit) * p.slab_bytes;
+  uint8_t* wbuf = arena + wave * PG::WAVE_LDS;
+  uint8_t* wring = wbuf + PG::NBUF * PG::BYTES;
+
+  const int pg0 = static_cast<int>(static_cast<int64_t>(split) * p.n_pages / p.splits);
+  const int pg1 = static_cast<int>(static_cast<int64_t>(split + 1) * p.n_pages / p.splits);
+  const int n_mine = pg0 + wave < pg1 ? (pg1 - pg0 - wave + kWaves - 1) / kWaves : 0;
+  const int waves_total = p.splits * kWaves;
+  const int my_wave = (kWaves - 1 - wave) * p.splits + split;
+
+  auto issue_page = [&](int k) {
+    const uint8_t* src = slab + static_cast<int64_t>(pg0 + wave + kWaves * k) * p.page_bytes;
+    const uint32_t dst = lds_addr(wbuf + (k % PG::NBUF) * PG::BYTES);
+#pragma unroll
+    for (int i = 0; i < PG::DMA; ++i) {
+      const int off = i * 1024 + lane * 16;
+      int from = off;
+      if (off < PG::CODES) from = krow_off<CPR_K>(off / KROW, off % KROW);
+      if (i + 1 < PG::DMA || off < PG::BYTES) dma16(src + from, dst + i * 1024);
+    }
+  };
+  constexpr int LPR = 2 * D / 16;
+  constexpr int RPI = 64 / LPR;
+  auto issue_step = [&](int hs) -> int {
+    const int64_t t0 = p.q_tokens + static_cast<int64_t>(hs) * RSTEP;
+    const int nv = static_cast<int>(p.T - t0 < RSTEP ? p.T - t0 : RSTEP);
+    const int row_in = lane / LPR, col_b = (lane % LPR) * 16;
+    const int slots = static_cast<int>(p.ring_slots);
+    const int slot0 = static_cast<int>(t0 % p.ring_slots);
+    int issued = 0;
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+#pragma unroll
+      for (int i = 0; i < (RSTEP + RPI - 1) / RPI; ++i) {
+        if (i * RPI >= nv) continue;
+        const int r = i * RPI + row_in;
+        const int slot = slot0 + r < slots ? slot0 + r : slot0 + r - slots;
+        const uint8_t* src = slab + p.ring_base + (kv * p.ring_slots + slot) * (2 * D) + col_b;
+        if (r < nv && r < RSTEP) dma16(src, lds_addr(wring + kv * RSTEP * 2 * D + i * 1024));
+        ++issued;
+      }
+    }
+    for (int i = lane; i < (RSTEP - nv) * 2 * D / 16; i += 64)
+      *reinterpret_cast<uint4*>(wring + RSTEP * 2 * D + nv * 2 * D + i * 16) = uint4{0u, 0u, 0u, 0u};
+    return issued;
+  };
+
+  // ---- first requests: q (wave 0), this wave's first residual step and page ----
+  const int q_bytes = HG * D * (p.q_bf16 ? 2 : 4);
+  int after_q = 0;
+  if (wave == 0) {
+    const uint8_t* qsrc = p.q + (static_cast<int64_t>(b) * p.q_heads + h * HG) * D * (p.q_bf16 ? 2 : 4);
+    for (int off = 0; off < q_bytes; off += 1024)
+      if (off + lane * 16 < q_bytes) dma16(qsrc + off + lane * 16, lds_addr(&qs[0][0]) + off);
+  }
+  const bool has_step = my_wave < p.n_steps;
+  if (has_step) after_q += issue_step(my_wave);
+  if (n_mine > 0) {
+    issue_page(0);
+    after_q += PG::DMA;
+  }
+  for (int i = tid; i < D / 2; i += kThreads)
+    w2pi[i] = pow(p.rope_theta, -2.0 * i / D) * 0.15915494309189535;   // omega_i / (2 pi)
+  if (wave == 0) wait_vm_upto(after_q);   // q has landed
+  __syncthreads();
+  {
+    constexpr int PER = (HG * D + kThreads - 1) / kThreads;
+    float qv[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = tid + k * kThreads;
+      qv[k] = 0.f;
+      if (i < HG * D)
+        qv[k] = p.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(&qs[0][0])[i])
+                         : (&qs[0][0])[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = tid + k * kThreads;
+      if (i < HG * D) (&qs[0][0])[i] = qv[k] * p.qscale;
+    }
+    __syncthreads();
+  }
+  // rotation of this lane's token (position tk in its page or step) for its pairs
+  float rcos[NPL], rsin[NPL], qpair[HG][2];
+#pragma unroll
+  for (int m = 0; m < NPL; ++m) {
+    const double turns = static_cast<double>(tk) * w2pi[hf * NPL + m];
+    sincospif(2.0f * static_cast<float>(turns - floor(turns)), &rsin[m], &rcos[m]);
+  }
+#pragma unroll
+  for (int hh = 0; hh < HG; ++hh) {
+    qpair[hh][0] = lane < D / 2 ? qs[hh][2 * lane] : 0.f;
+    qpair[hh][1] = lane < D / 2 ? qs[hh][2 * lane + 1] : 0.f;
+  }
+
+  // ---- online softmax state --------------------------------------------------
+  // mh[hh]: running max of head hh (wave-uniform). lane_l / lane_z: sums of p
+  // and p z over this lane's tokens for head hd (lanes < 32; the upper half
+  // holds copies). acc: the value product, rows 0..3 high parts of heads
+  // 0..3, rows 4..7 remainders (as in kivi_mfma_kernel).
+  floatx4 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float mh[HG];
+#pragma unroll
+  for (int hh = 0; hh < HG; ++hh) mh[hh] = -INFINITY;
+  float lane_l = 0.f, lane_z = 0.f;
+
+  // qpage[wave][hh] = R(omega (T-1-t0)) q[hh]
+  auto rotate_q = [&](int64_t t0) {
+    if (lane < D / 2) {
+      const double turns = static_cast<double>(p.T - 1 - t0) * w2pi[lane];
+      float sn, cs;
+      sincospif(2.0f * static_cast<float>(turns - floor(turns)), &sn, &cs);
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) {
+        const float q0 = qpair[hh][0], q1 = qpair[hh][1];
+        *reinterpret_cast<float2*>(&qpage[wave][hh][2 * lane]) =
+            float2{fmaf(q0, cs, -(q1 * sn)), fmaf(q0, sn, q1 * cs)};
+      }
+    }
+    wait_lds();
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  // y: this lane's HALF channels of its token (dequantised); rotates them by
+  // the token's position, then the key product against qpage; returns the 4
+  // scores of tokens 4((l/4)%8) + r for head hd (both halves added)
+  auto scores = [&](float* y) -> floatx4 {
+#pragma unroll
+    for (int m = 0; m < NPL; ++m) {
+      const float x0 = y[2 * m], x1 = y[2 * m + 1];
+      y[2 * m] = fmaf(x0, rcos[m], -(x1 * rsin[m]));
+      y[2 * m + 1] = fmaf(x0, rsin[m], x1 * rcos[m]);
+    }
+    const float* qb = &qpage[wave][hd][hf * HALF];
+    floatx4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0;
+#pragma unroll
+    for (int i = 0; i < HALF / 4; ++i) {
+      const float4 bq = *reinterpret_cast<const float4*>(qb + 4 * i);
+      c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(y[4 * i], bq.x, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(y[4 * i + 1], bq.y, c1, 0, 0, 0);
+      c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(y[4 * i + 2], bq.z, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(y[4 * i + 3], bq.w, c1, 0, 0, 0);
+    }
+    floatx4 s;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = c0[r] + c1[r];
+      s[r] = v + xor32(v);
+    }
+    return s;
+  };
+
+  // folds 4 scores per lane (tokens 4((l/4)%8) + r, head hd; -inf = absent)
+  // into the softmax state; returns the weights 2^(s - m)
+  auto softmax = [&](floatx4 s) -> floatx4 {
+    float pm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    // max over the 8 token quads of this half: lanes l ^ 4, l ^ 8, l ^ 16
+    pm = fmaxf(pm, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, pm), (0x04 << 10) | 0x1F)));
+    pm = fmaxf(pm, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, pm), (0x08 << 10) | 0x1F)));
+    pm = fmaxf(pm, xor16(pm));
+    float mine = mh[0];
+#pragma unroll
+    for (int hh = 1; hh < HG; ++hh) mine = hd == hh ? mh[hh] : mine;
+    const float m_new = fmaxf(mine, pm);
+    float a_h[HG];
+    bool grow = false;
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      const float mn = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_new), hh));
+      grow |= mn > mh[hh];
+      a_h[hh] = mn;
+    }
+    if (grow) {   // wave-uniform
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) {
+        const float a = fast_exp2(mh[hh] - a_h[hh]);
+        mh[hh] = a_h[hh];
+        a_h[hh] = a;
+      }
+      float a_mine = a_h[0];
+#pragma unroll
+      for (int hh = 1; hh < HG; ++hh) a_mine = hd == hh ? a_h[hh] : a_mine;
+      lane_l *= a_mine;
+      lane_z *= a_mine;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= a_h[r];   // rows 4g + r: head r
+      }
+    }
+    float mcur = mh[0];
+#pragma unroll
+    for (int hh = 1; hh < HG; ++hh) mcur = hd == hh ? mh[hh] : mcur;
+    floatx4 w;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) w[r] = fast_exp2(s[r] - mcur);
+    return w;
+  };
+
+  // P' (4 per lane, lanes < 32) -> LDS in the value operand's k order -> A
+  // operand: rows 0..3 high part of head j, rows 4..7 remainder of head j-4
+  auto weights_to_a = [&](floatx4 pw, bool permuted) -> bf16x8 {
+    if (lane < 32) {
+      uint32_t ph[2], pl[2];
+      if (permuted) {   // element order {0,2,1,3} of each token quad (the fp4 converts' order)
+        split_bf16(pw[0], pw[2], ph[0], pl[0]);
+        split_bf16(pw[1], pw[3], ph[1], pl[1]);
+      } else {
+        split_bf16(pw[0], pw[1], ph[0], pl[0]);
+        split_bf16(pw[2], pw[3], ph[1], pl[1]);
+      }
+      const int t0 = 4 * ((lane >> 2) & 7);
+      *reinterpret_cast<uint2*>(&pbuf[wave][0][hd][t0]) = uint2{ph[0], ph[1]};
+      *reinterpret_cast<uint2*>(&pbuf[wave][1][hd][t0]) = uint2{pl[0], pl[1]};
+    }
+    wait_lds();
+    __builtin_amdgcn_wave_barrier();
+    uint4 v = uint4{0u, 0u, 0u, 0u};
+    if (j < 8) v = *reinterpret_cast<const uint4*>(&pbuf[wave][j >> 2][j & 3][8 * g]);
+    return __builtin_bit_cast(bf16x8, v);
+  };
+
+  auto process_page = [&](const uint8_t* pg, int64_t t0) {
+    rotate_q(t0);
+    // this lane's token row, its channel half: D/8 bytes of 2-bit codes
+    float y[HALF];
+    {
+      const float* sp = reinterpret_cast<const float*>(pg + PG::OFF_KS) + hf * HALF;
+      const float* zp = reinterpret_cast<const float*>(pg + PG::OFF_KZ) + hf * HALF;
+#pragma unroll
+      for (int w = 0; w < HALF / 16; ++w) {
+        const uint32_t word = *reinterpret_cast<const uint32_t*>(pg + krow_off<CPR_K>(tk, hf * (D / 8) + 4 * w));
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 sv = *reinterpret_cast<const float4*>(sp + 16 * w + 4 * q4);
+          const float4 zv = *reinterpret_cast<const float4*>(zp + 16 * w + 4 * q4);
+          const uint32_t byte = (word >> (8 * q4)) & 0xFFu;
+          y[16 * w + 4 * q4 + 0] = fmaf(static_cast<float>(byte & 3u), sv.x, zv.x);
+          y[16 * w + 4 * q4 + 1] = fmaf(static_cast<float>((byte >> 2) & 3u), sv.y, zv.y);
+          y[16 * w + 4 * q4 + 2] = fmaf(static_cast<float>((byte >> 4) & 3u), sv.z, zv.z);
+          y[16 * w + 4 * q4 + 3] = fmaf(static_cast<float>(byte >> 6), sv.w, zv.w);
+        }
+      }
+    }
+    const floatx4 w = softmax(scores(y));
+    // P' = p * s_t; sums of p and p * z_t (lanes < 32 own the tokens)
+    const int t0q = 4 * ((lane >> 2) & 7);
+    const float4 vs = *reinterpret_cast<const float4*>(pg + PG::OFF_VS + 4 * t0q);
+    const float4 vz = *reinterpret_cast<const float4*>(pg + PG::OFF_VZ + 4 * t0q);
+    if (lane < 32) {
+      lane_l += (w[0] + w[1]) + (w[2] + w[3]);
+      lane_z = fmaf(w[0], vz.x, fmaf(w[1], vz.y, fmaf(w[2], vz.z, fmaf(w[3], vz.w, lane_z))));
+    }
+    const floatx4 pv = {w[0] * vs.x, w[1] * vs.y, w[2] * vs.z, w[3] * vs.w};
+    const bf16x8 ap = weights_to_a(pv, true);
+    // value codes of tokens {8g..8g+7} of channel 16 nt + j (bytes 2g, 2g+1)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const uint32_t x = *reinterpret_cast<const uint16_t*>(pg + PG::OFF_VC + (16 * nt + j) * VROW + 2 * g);
+      const uint32_t y0 = x & 0x3333u, y1 = (x >> 2) & 0x3333u;
+      const uint4 bw = uint4{bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y0, 2.0f, 0)),
+                             bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 0)),
+                             bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y0, 2.0f, 1)),
+                             bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 1))};
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, __builtin_bit_cast(bf16x8, bw), acc[nt], 0, 0, 0);
+    }
+  };
+
+  // residual step: tokens 0..7 of the step are lanes with tk < 8
+  auto process_step = [&](int hs) {
+    const int64_t t0 = p.q_tokens + static_cast<int64_t>(hs) * RSTEP;
+    const int nv = static_cast<int>(p.T - t0 < RSTEP ? p.T - t0 : RSTEP);
+    rotate_q(t0);
+    float y[HALF];
+    const uint16_t* kr = reinterpret_cast<const uint16_t*>(wring + (tk & 7) * 2 * D) + hf * HALF;
+#pragma unroll
+    for (int i = 0; i < HALF / 8; ++i) {
+      const uint4 v = *reinterpret_cast<const uint4*>(kr + 8 * i);
+      unpack_bf16x8(v, y + 8 * i);
+    }
+    floatx4 s = scores(y);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] = 4 * ((lane >> 2) & 7) + r < nv ? s[r] : -INFINITY;
+    const floatx4 w = softmax(s);
+    if (lane < 32) lane_l += (w[0] + w[1]) + (w[2] + w[3]);   // absent tokens: 0
+    const bf16x8 ap = weights_to_a(w, false);
+    // value rows: tokens 8g..8g+7 exist for g = 0 only (absent rows are zero)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      uint4 bw = uint4{0u, 0u, 0u, 0u};
+      if (g == 0) {
+        const uint16_t* vr = reinterpret_cast<const uint16_t*>(wring + RSTEP * 2 * D) + 16 * nt + j;
+        bw = uint4{uint32_t(vr[0]) | (uint32_t(vr[D]) << 16), uint32_t(vr[2 * D]) | (uint32_t(vr[3 * D]) << 16),
+                   uint32_t(vr[4 * D]) | (uint32_t(vr[5 * D]) << 16), uint32_t(vr[6 * D]) | (uint32_t(vr[7 * D]) << 16)};
+      }
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, __builtin_bit_cast(bf16x8, bw), acc[nt], 0, 0, 0);
+    }
+  };
+
+  // ---- residual steps first (all of this wave's), then the pages ---------------
+  for (int hs = my_wave; hs < p.n_steps; hs += waves_total) {
+    if (hs != my_wave) {
+      wait_lds();
+      __builtin_amdgcn_wave_barrier();
+      issue_step(hs);
+      wait_vm<0>();
+    } else if (n_mine > 0) {
+      wait_vm<PG::DMA>();   // the first page may stay in flight
+    } else {
+      wait_vm<0>();
+    }
+    wait_lds();
+    __builtin_amdgcn_wave_barrier();
+    process_step(hs);
+  }
+#pragma unroll 1
+  for (int k = 0; k < n_mine; ++k) {
+    wait_lds();
+    __builtin_amdgcn_wave_barrier();
+    const bool next = k + 1 < n_mine;
+    if (next) issue_page(k + 1);
+    if (next) wait_vm<PG::DMA>();
+    else wait_vm<0>();
+    __builtin_amdgcn_wave_barrier();
+    process_page(wbuf + (k % PG::NBUF) * PG::BYTES, static_cast<int64_t>(pg0 + wave + kWaves * k) * kPage);
+  }
+  wait_lds();
+
+  // ---- wave epilogue: per-head sums (lanes < 32 with head hd) ----------------
+  float lsum[HG], zsum[HG];
+  {
+    float l_ = lane < 32 ? lane_l : 0.f, z_ = lane < 32 ? lane_z : 0.f;
+    // sum over the 8 token quads: lanes l ^ 4, l ^ 8, l ^ 16, then l ^ 32
+    l_ += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, l_), (0x04 << 10) | 0x1F));
+    z_ += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, z_), (0x04 << 10) | 0x1F));
+    l_ += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, l_), (0x08 << 10) | 0x1F));
+    z_ += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, z_), (0x08 << 10) | 0x1F));
+    l_ += xor16(l_);
+    z_ += xor16(z_);
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      lsum[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_), hh));
+      zsum[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, z_), hh));
+    }
+  }
+  __syncthreads();   // every wave is done with its page buffers (the arena)
+  float* red = reinterpret_cast<float*>(arena);   // [wave][HG][D + 2]: m, l, o
+  auto R = [&](int w, int hh) { return red + (w * HG + hh) * (D + 2); };
+  // acc rows 4g+r: row < HG is head row (hi), HG <= row < 2HG is head row-HG (lo)
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float x = acc[nt][r];
+      if constexpr (HG == 1) {
+        x = r == 0 ? acc[nt][0] + acc[nt][1] : 0.f;
+      } else if constexpr (HG == 2) {
+        x = r < 2 ? acc[nt][r] + acc[nt][r + 2] : 0.f;
+      } else if constexpr (HG == 4) {
+        x += xor16(x);          // rows 0-3 (g=0) + rows 4-7 (g=1)
+      } else {
+        x += xor32(x);          // rows 0-7 (g=0,1) + rows 8-15 (g=2,3)
+      }
+      v[r] = x;
+    }
+    const int c = 16 * nt + j;
+    if (4 * g < HG) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int hh = 4 * g + r;
+        float zz = 0.f;   // sum_t p z_t of head hh goes to every channel
+#pragma unroll
+        for (int k = 0; k < HG; ++k) zz = hh == k ? zsum[k] : zz;
+        if (hh < HG) R(wave, hh)[2 + c] = v[r] + zz;
+      }
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      R(wave, hh)[0] = mh[hh];
+      R(wave, hh)[1] = lsum[hh];
+    }
+  }
+  __syncthreads();
+
+  // ---- combine the waves; write the output, or this block's partial --------
+  float* part_bh = p.partials + (static_cast<int64_t>(b) * p.q_heads + h * HG) * p.splits * (D + 2);
+  for (int i = tid; i < HG * D; i += kThreads) {
+    const int hh = i / D, c = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, R(w, hh)[0]);
+    float so = 0.f, sl = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float e = fast_exp2(R(w, hh)[0] - M);   // idle wave: m = -inf -> 0
+      so = fmaf(e, R(w, hh)[2 + c], so);
+      sl = fmaf(e, R(w, hh)[1], sl);
+    }
+    const int hq = h * HG + hh;
+    if (p.splits == 1) {
+      p.out[(static_cast<int64_t>(b) * p.q_heads + hq) * D + c] = so / sl;
+    } else {
+      float* part = part_bh + (static_cast<int64_t>(hh) * p.splits + split) * (D + 2);
+      store_coherent(part + 2 + c, so);
+      if (c == 0) {
+        store_coherent(part, M);
+        store_coherent(part + 1, sl);
+      }
+    }
+  }
+  if (p.splits == 1) return;
+
+  // ---- the last block of this (sequence, KV head) merges every partial ------
+  // M = max_s m_s; out = sum_s 2^(m_s-M) o_s / sum_s 2^(m_s-M) l_s. Partials
+  // are written and read at device scope (through to the coherence point, not
+  // the per-XCD L2); the counter lives in the workspace and is returned to
+  // zero for the next call.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // this block's stores done
+  __syncthreads();
+  if (tid == 0) {
+    const int done = __hip_atomic_fetch_add(&p.counters[unit], 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    last_block = done == p.splits - 1;
+  }
+  __syncthreads();
+  if (!last_block) return;
+  // each thread merges up to two output elements at a time, with the loads of
+  // a batch of 8 splits for both issued before any use
+  constexpr int PER = (HG * D + kThreads - 1) / kThreads;
+  constexpr int CH = PER < 2 ? PER : 2;
+  for (int e0 = 0; e0 < PER; e0 += CH) {
+    float M[CH], so[CH], sl[CH];
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      M[e] = -INFINITY;
+      so[e] = 0.f;
+      sl[e] = 0.f;
+    }
+    for (int s0 = 0; s0 < p.splits; s0 += 8) {
+      float mv[CH][8], lv[CH][8], ov[CH][8];
+#pragma unroll
+      for (int e = 0; e < CH; ++e) {
+        const int i = tid + (e0 + e) * kThreads;
+        const int hh = (i < HG * D ? i : 0) / D, c = i % D;
+        const float* part = part_bh + static_cast<int64_t>(hh) * p.splits * (D + 2);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float* ps = part + (s0 + k < p.splits ? s0 + k : s0) * (D + 2);
+          mv[e][k] = load_coherent(ps);
+          lv[e][k] = load_coherent(ps + 1);
+          ov[e][k] = load_coherent(ps + 2 + c);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < CH; ++e) {
+        float bm = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) bm = s0 + k < p.splits ? fmaxf(bm, mv[e][k]) : bm;
+        const float Mn = fmaxf(M[e], bm);
+        const float a = fast_exp2(M[e] - Mn);
+        so[e] *= a;
+        sl[e] *= a;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float w8 = s0 + k < p.splits ? fast_exp2(mv[e][k] - Mn) : 0.f;
+          sl[e] = fmaf(w8, lv[e][k], sl[e]);
+          so[e] = fmaf(w8, ov[e][k], so[e]);
+        }
+        M[e] = Mn;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      const int i = tid + (e0 + e) * kThreads;
+      if (i < HG * D) {
+        const int hh = i / D, c = i % D;
+        p.out[(static_cast<int64_t>(b) * p.q_heads + h * HG + hh) * D + c] = so[e] / sl[e];
+      }
+    }
+  }
+  if (tid == 0)
+    __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+
 template <int BITS, int D, bool ROPE>
 hipError_t by_hg(const MfmaParams& p, int hg, int batch, hipStream_t st) {
   dim3 grid(p.splits, p.kv_heads, batch);
@@ -859,6 +1395,12 @@ hipError_t by_d(const MfmaParams& p, int d, int hg, int batch, hipStream_t st) {
 }
 
 hipError_t by_d_rope(const MfmaParams& p, int d, int hg, int batch, hipStream_t st) {
+  if (hg == 4) {   // dense-score kernel
+    dim3 grid(p.splits, p.kv_heads, batch);
+    if (d == 64) hipLaunchKernelGGL((rope4_kernel<64>), grid, dim3(kThreads), 0, st, p);
+    else hipLaunchKernelGGL((rope4_kernel<128>), grid, dim3(kThreads), 0, st, p);
+    return hipGetLastError();
+  }
   return d == 64 ? by_hg<2, 64, true>(p, hg, batch, st) : by_hg<2, 128, true>(p, hg, batch, st);
 }
 
