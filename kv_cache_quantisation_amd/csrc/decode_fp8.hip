@@ -324,7 +324,9 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_mfma_kernel(Fp8Params p) {
   if (p.splits == 1) return;
 
   // ---- the last block of this (sequence, KV head) merges every partial ------
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  // every wave's partial stores (device scope, written through) have completed
+  // before the block's arrival is counted: the block that counts last reads them
+  wait_vm<0>();
   __syncthreads();
   if (tid == 0) {
     const int done = __hip_atomic_fetch_add(&p.counters[unit], 1, __ATOMIC_RELAXED,

@@ -770,7 +770,9 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : 3) void kivi_mfma_kernel(MfmaP
   // are written and read at device scope (through to the coherence point, not
   // the per-XCD L2); the counter lives in the workspace and is returned to
   // zero for the next call.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // this block's stores done
+  // every wave's partial stores (device scope, written through) have completed
+  // before the block's arrival is counted: the block that counts last reads them
+  wait_vm<0>();
   __syncthreads();
   if (tid == 0) {
     const int done = __hip_atomic_fetch_add(&p.counters[unit], 1, __ATOMIC_RELAXED,
@@ -1305,7 +1307,9 @@ __global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
   // are written and read at device scope (through to the coherence point, not
   // the per-XCD L2); the counter lives in the workspace and is returned to
   // zero for the next call.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // this block's stores done
+  // every wave's partial stores (device scope, written through) have completed
+  // before the block's arrival is counted: the block that counts last reads them
+  wait_vm<0>();
   __syncthreads();
   if (tid == 0) {
     const int done = __hip_atomic_fetch_add(&p.counters[unit], 1, __ATOMIC_RELAXED,
