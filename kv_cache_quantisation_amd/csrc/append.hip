@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
       const float s = (mx - mn) / kLevels;
       k_mn[c] = mn;
       k_s[c] = s;
-      k_r[c] = __builtin_amdgcn_rcpf(s);
+      k_r[c] = quant_rcp_prep(s);
       reinterpret_cast<float*>(pg + p.off_ks)[c] = s;
       reinterpret_cast<float*>(pg + p.off_kz)[c] = mn;
     }
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
       const float s = (mx - mn) / kLevels;
       v_mn[r] = mn;
       v_s[r] = s;
-      v_r[r] = __builtin_amdgcn_rcpf(s);
+      v_r[r] = quant_rcp_prep(s);
       reinterpret_cast<float*>(pg + p.off_vs)[r] = s;
       reinterpret_cast<float*>(pg + p.off_vz)[r] = mn;
     }

@@ -30,20 +30,23 @@ __device__ __forceinline__ uint32_t quant_asym(float x, float mn, float s, float
   return static_cast<uint32_t>(r);
 }
 
-// The same code as quant_asym, computed with a reciprocal r ~ 1/s (v_rcp_f32,
-// 1 ulp): q = (x - mn) * r is within 2^-13 of the exactly rounded quotient for
-// quotients up to 256, so rint(q) equals rint of the IEEE quotient unless q is
-// within 2^-12 of a half-integer; those rare elements (and tiny scales, where
-// the reciprocal could flush) take the IEEE division.
+// The same code as quant_asym, computed with a prepared reciprocal r of s
+// (quant_rcp_prep): q = (x - mn) * r is within 2^-13 of the exactly rounded
+// quotient for quotients up to 256 (v_rcp_f32 is within 1 ulp), so rint(q)
+// equals rint of the IEEE quotient unless q is within 2^-12 of a
+// half-integer; those rare elements take the IEEE division. r = 0 for s = 0
+// gives code 0; r = NaN (s too small for the reciprocal) sends every element
+// to the division.
+__device__ __forceinline__ float quant_rcp_prep(float s) {
+  return s == 0.0f ? 0.0f : (s >= 0x1p-100f ? __builtin_amdgcn_rcpf(s) : __builtin_nanf(""));
+}
 __device__ __forceinline__ uint32_t quant_asym_rcp(float x, float mn, float s, float r,
                                                    float levels) {
-  if (s == 0.0f) return 0u;
   const float a = x - mn;
-  float q = rintf(a * r);
-  const float t = a * r - q;
-  if (fabsf(t) > 0.5f - 0x1p-12f || !(s >= 0x1p-100f)) q = rintf(a / s);
-  q = fminf(fmaxf(q, 0.0f), levels);
-  return static_cast<uint32_t>(q);
+  const float ar = a * r;
+  float q = rintf(ar);
+  if (!(fabsf(ar - q) <= 0.5f - 0x1p-12f)) q = rintf(a / s);
+  return static_cast<uint32_t>(__builtin_amdgcn_fmed3f(q, 0.0f, levels));
 }
 
 // Symmetric code: clamp(rint(x / s), -Q, Q), 0 when s == 0; returned as the
