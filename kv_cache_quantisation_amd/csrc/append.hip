@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
   constexpr int CPT = D / TPT;                // channels per thread (value statistics)
   static_assert(TPC <= 8 && (TPC & (TPC - 1)) == 0, "key statistics lane groups");
   __shared__ __attribute__((aligned(16))) uint8_t tile[2][kPage * PITCH];   // K rows, V rows
-  __shared__ float k_mn[D], k_s[D], k_r[D], v_mn[kPage], v_s[kPage], v_r[kPage];
+  __shared__ __attribute__((aligned(16))) float k_mn[D], k_s[D], k_r[D], v_mn[kPage], v_s[kPage], v_r[kPage];
 
   const int tid = threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -167,29 +167,57 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
   __syncthreads();
 
   // 3. codes. K rows: field f = token*D + channel. V cols: field f = channel*32 + token.
+  //    Statistics and key elements of a word are read as vectors.
   constexpr int WORDS = kPage * D * BITS / 32;
   uint32_t* kc = reinterpret_cast<uint32_t*>(pg + p.off_kc);
   uint32_t* vc = reinterpret_cast<uint32_t*>(pg + p.off_vc);
+  auto load4 = [](const float* src, float* dst) {   // FPW floats, 16-byte aligned
+#pragma unroll
+    for (int i = 0; i < FPW / 4; ++i) {
+      const float4 v = reinterpret_cast<const float4*>(src)[i];
+      dst[4 * i] = v.x;
+      dst[4 * i + 1] = v.y;
+      dst[4 * i + 2] = v.z;
+      dst[4 * i + 3] = v.w;
+    }
+  };
   for (int w = tid; w < WORDS; w += kThreads) {
     const int f0 = w * FPW;
     const int t = f0 / D, c0 = f0 % D;
+    float x[FPW], mn[FPW], rc[FPW];
+    const uint8_t* row = tile[0] + t * PITCH + c0 * IB;
+    if constexpr (IB == 2) {
+      if constexpr (FPW >= 8) {
+#pragma unroll
+        for (int i = 0; i < FPW / 8; ++i) unpack_bf16x8(reinterpret_cast<const uint4*>(row)[i], x + 8 * i);
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(row);
+        x[0] = __uint_as_float(v.x << 16);
+        x[1] = __uint_as_float(v.x & 0xffff0000u);
+        x[2] = __uint_as_float(v.y << 16);
+        x[3] = __uint_as_float(v.y & 0xffff0000u);
+      }
+    } else {
+      load4(reinterpret_cast<const float*>(row), x);
+    }
+    load4(k_mn + c0, mn);
+    load4(k_r + c0, rc);
     uint32_t word = 0;
 #pragma unroll
-    for (int j = 0; j < FPW; ++j) {
-      const int c = c0 + j;
-      word |= quant_asym_rcp(elem(0, t, c), k_mn[c], k_s[c], k_r[c], kLevels) << (j * BITS);
-    }
+    for (int j = 0; j < FPW; ++j)
+      word |= quant_asym_rcp(x[j], mn[j], k_s + c0 + j, rc[j], kLevels) << (j * BITS);
     kc[w] = word;
   }
   for (int w = tid; w < WORDS; w += kThreads) {
     const int f0 = w * FPW;
     const int c = f0 / kPage, t0 = f0 % kPage;
+    float mn[FPW], rc[FPW];
+    load4(v_mn + t0, mn);
+    load4(v_r + t0, rc);
     uint32_t word = 0;
 #pragma unroll
-    for (int j = 0; j < FPW; ++j) {
-      const int t = t0 + j;
-      word |= quant_asym_rcp(elem(1, t, c), v_mn[t], v_s[t], v_r[t], kLevels) << (j * BITS);
-    }
+    for (int j = 0; j < FPW; ++j)
+      word |= quant_asym_rcp(elem(1, t0 + j, c), mn[j], v_s + t0 + j, rc[j], kLevels) << (j * BITS);
     vc[w] = word;
   }
 }

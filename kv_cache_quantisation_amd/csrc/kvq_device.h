@@ -40,12 +40,13 @@ __device__ __forceinline__ uint32_t quant_asym(float x, float mn, float s, float
 __device__ __forceinline__ float quant_rcp_prep(float s) {
   return s == 0.0f ? 0.0f : (s >= 0x1p-100f ? __builtin_amdgcn_rcpf(s) : __builtin_nanf(""));
 }
-__device__ __forceinline__ uint32_t quant_asym_rcp(float x, float mn, float s, float r,
+// (s is read only on the division path.)
+__device__ __forceinline__ uint32_t quant_asym_rcp(float x, float mn, const float* s, float r,
                                                    float levels) {
   const float a = x - mn;
   const float ar = a * r;
   float q = rintf(ar);
-  if (!(fabsf(ar - q) <= 0.5f - 0x1p-12f)) q = rintf(a / s);
+  if (!(fabsf(ar - q) <= 0.5f - 0x1p-12f)) q = rintf(a / *s);
   return static_cast<uint32_t>(__builtin_amdgcn_fmed3f(q, 0.0f, levels));
 }
 
