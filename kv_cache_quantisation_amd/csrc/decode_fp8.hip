@@ -92,7 +92,8 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_mfma_kernel(Fp8Params p) {
   __shared__ int last_block;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform in the wave
   const int j = lane & 15, g = lane >> 4;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int unit = b * p.kv_heads + h;

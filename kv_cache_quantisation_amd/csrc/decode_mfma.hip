@@ -122,6 +122,165 @@ __device__ __forceinline__ float load_q(const uint8_t* base, int64_t idx, int bf
   return reinterpret_cast<const float*>(base)[idx];
 }
 
+// ---- end of every decode kernel of this file -------------------------------
+// Combines the block's waves (their running max mh, sums of p and p z per head,
+// and value accumulators acc: rows 4g + r, high parts of the heads then their
+// remainders), writes the output rows (one split) or the block's partial, and
+// in the last block of a (sequence, KV head) to finish merges every partial.
+template <int D, int HG>
+__device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* acc, const float* mh,
+                                            const float* lsum, const float* zsum, uint8_t* arena,
+                                            int& last_block, int b, int h, int split) {
+  constexpr int NT = D / 16;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform in the wave
+  const int j = lane & 15, g = lane >> 4;
+  const int unit = b * p.kv_heads + h;
+  __syncthreads();   // every wave is done with its page buffers (the arena)
+  float* red = reinterpret_cast<float*>(arena);   // [wave][HG][D + 2]: m, l, o
+  auto R = [&](int w, int hh) { return red + (w * HG + hh) * (D + 2); };
+  // acc rows 4g+r: row < HG is head row (hi), HG <= row < 2HG is head row-HG (lo)
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float x = acc[nt][r];
+      if constexpr (HG == 1) {
+        x = r == 0 ? acc[nt][0] + acc[nt][1] : 0.f;
+      } else if constexpr (HG == 2) {
+        x = r < 2 ? acc[nt][r] + acc[nt][r + 2] : 0.f;
+      } else if constexpr (HG == 4) {
+        x += xor16(x);          // rows 0-3 (g=0) + rows 4-7 (g=1)
+      } else {
+        x += xor32(x);          // rows 0-7 (g=0,1) + rows 8-15 (g=2,3)
+      }
+      v[r] = x;
+    }
+    const int c = 16 * nt + j;
+    if (4 * g < HG) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int hh = 4 * g + r;
+        float zz = 0.f;   // sum_t p z_t of head hh goes to every channel
+#pragma unroll
+        for (int k = 0; k < HG; ++k) zz = hh == k ? zsum[k] : zz;
+        if (hh < HG) R(wave, hh)[2 + c] = v[r] + zz;
+      }
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      R(wave, hh)[0] = mh[hh];
+      R(wave, hh)[1] = lsum[hh];
+    }
+  }
+  __syncthreads();
+
+  // ---- combine the waves; write the output, or this block's partial --------
+  float* part_bh = p.partials + (static_cast<int64_t>(b) * p.q_heads + h * HG) * p.splits * (D + 2);
+  for (int i = tid; i < HG * D; i += kThreads) {
+    const int hh = i / D, c = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, R(w, hh)[0]);
+    float so = 0.f, sl = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float e = fast_exp2(R(w, hh)[0] - M);   // idle wave: m = -inf -> 0
+      so = fmaf(e, R(w, hh)[2 + c], so);
+      sl = fmaf(e, R(w, hh)[1], sl);
+    }
+    const int hq = h * HG + hh;
+    if (p.splits == 1) {
+      p.out[(static_cast<int64_t>(b) * p.q_heads + hq) * D + c] = so / sl;
+    } else {
+      float* part = part_bh + (static_cast<int64_t>(hh) * p.splits + split) * (D + 2);
+      store_coherent(part + 2 + c, so);
+      if (c == 0) {
+        store_coherent(part, M);
+        store_coherent(part + 1, sl);
+      }
+    }
+  }
+  if (p.splits == 1) return;
+
+  // ---- the last block of this (sequence, KV head) merges every partial ------
+  // M = max_s m_s; out = sum_s 2^(m_s-M) o_s / sum_s 2^(m_s-M) l_s. Partials
+  // are written and read at device scope (through to the coherence point, not
+  // the per-XCD L2); the counter lives in the workspace and is returned to
+  // zero for the next call.
+  // every wave's partial stores (device scope, written through) have completed
+  // before the block's arrival is counted: the block that counts last reads them
+  wait_vm<0>();
+  __syncthreads();
+  if (tid == 0) {
+    const int done = __hip_atomic_fetch_add(&p.counters[unit], 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    last_block = done == p.splits - 1;
+  }
+  __syncthreads();
+  if (!last_block) return;
+  // each thread merges up to two output elements at a time, with the loads of
+  // a batch of 8 splits for both issued before any use
+  constexpr int PER = (HG * D + kThreads - 1) / kThreads;
+  constexpr int CH = PER < 2 ? PER : 2;
+  for (int e0 = 0; e0 < PER; e0 += CH) {
+    float M[CH], so[CH], sl[CH];
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      M[e] = -INFINITY;
+      so[e] = 0.f;
+      sl[e] = 0.f;
+    }
+    for (int s0 = 0; s0 < p.splits; s0 += 8) {
+      float mv[CH][8], lv[CH][8], ov[CH][8];
+#pragma unroll
+      for (int e = 0; e < CH; ++e) {
+        const int i = tid + (e0 + e) * kThreads;
+        const int hh = (i < HG * D ? i : 0) / D, c = i % D;
+        const float* part = part_bh + static_cast<int64_t>(hh) * p.splits * (D + 2);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float* ps = part + (s0 + k < p.splits ? s0 + k : s0) * (D + 2);
+          mv[e][k] = load_coherent(ps);
+          lv[e][k] = load_coherent(ps + 1);
+          ov[e][k] = load_coherent(ps + 2 + c);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < CH; ++e) {
+        float bm = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) bm = s0 + k < p.splits ? fmaxf(bm, mv[e][k]) : bm;
+        const float Mn = fmaxf(M[e], bm);
+        const float a = fast_exp2(M[e] - Mn);
+        so[e] *= a;
+        sl[e] *= a;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float w8 = s0 + k < p.splits ? fast_exp2(mv[e][k] - Mn) : 0.f;
+          sl[e] = fmaf(w8, lv[e][k], sl[e]);
+          so[e] = fmaf(w8, ov[e][k], so[e]);
+        }
+        M[e] = Mn;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      const int i = tid + (e0 + e) * kThreads;
+      if (i < HG * D) {
+        const int hh = i / D, c = i % D;
+        p.out[(static_cast<int64_t>(b) * p.q_heads + h * HG + hh) * D + c] = so[e] / sl[e];
+      }
+    }
+  }
+  if (tid == 0)
+    __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int BITS, int D, int HG, bool ROPE>
 __global__ __launch_bounds__(kThreads, ROPE ? 2 : 3) void kivi_mfma_kernel(MfmaParams p) {
   static_assert(BITS == 2 || BITS == 4, "2- or 4-bit pages");
@@ -159,7 +318,8 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : 3) void kivi_mfma_kernel(MfmaP
   __shared__ int last_block;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform in the wave
   const int j = lane & 15, g = lane >> 4;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const uint8_t* slab = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes;
@@ -212,7 +372,6 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : 3) void kivi_mfma_kernel(MfmaP
   // ---- work of this wave --------------------------------------------------------
   // Block `split` takes a contiguous range of pages; its waves take every
   // kWaves-th page of that range.
-  const int unit = b * p.kv_heads + h;
   const int waves_total = p.splits * kWaves;
   const int pg0 = static_cast<int>(static_cast<int64_t>(split) * p.n_pages / p.splits);
   const int pg1 = static_cast<int>(static_cast<int64_t>(split + 1) * p.n_pages / p.splits);
@@ -695,148 +854,7 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : 3) void kivi_mfma_kernel(MfmaP
       mh[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_lane), hh));
     }
   }
-  __syncthreads();   // every wave is done with its page buffers (the arena)
-  float* red = reinterpret_cast<float*>(arena);   // [wave][HG][D + 2]: m, l, o
-  auto R = [&](int w, int hh) { return red + (w * HG + hh) * (D + 2); };
-  // acc rows 4g+r: row < HG is head row (hi), HG <= row < 2HG is head row-HG (lo)
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    float v[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float x = acc[nt][r];
-      if constexpr (HG == 1) {
-        x = r == 0 ? acc[nt][0] + acc[nt][1] : 0.f;
-      } else if constexpr (HG == 2) {
-        x = r < 2 ? acc[nt][r] + acc[nt][r + 2] : 0.f;
-      } else if constexpr (HG == 4) {
-        x += xor16(x);          // rows 0-3 (g=0) + rows 4-7 (g=1)
-      } else {
-        x += xor32(x);          // rows 0-7 (g=0,1) + rows 8-15 (g=2,3)
-      }
-      v[r] = x;
-    }
-    const int c = 16 * nt + j;
-    if (4 * g < HG) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int hh = 4 * g + r;
-        float zz = 0.f;   // sum_t p z_t of head hh goes to every channel
-#pragma unroll
-        for (int k = 0; k < HG; ++k) zz = hh == k ? zsum[k] : zz;
-        if (hh < HG) R(wave, hh)[2 + c] = v[r] + zz;
-      }
-    }
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-      R(wave, hh)[0] = mh[hh];
-      R(wave, hh)[1] = lsum[hh];
-    }
-  }
-  __syncthreads();
-
-  // ---- combine the waves; write the output, or this block's partial --------
-  float* part_bh = p.partials + (static_cast<int64_t>(b) * p.q_heads + h * HG) * p.splits * (D + 2);
-  for (int i = tid; i < HG * D; i += kThreads) {
-    const int hh = i / D, c = i % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, R(w, hh)[0]);
-    float so = 0.f, sl = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float e = fast_exp2(R(w, hh)[0] - M);   // idle wave: m = -inf -> 0
-      so = fmaf(e, R(w, hh)[2 + c], so);
-      sl = fmaf(e, R(w, hh)[1], sl);
-    }
-    const int hq = h * HG + hh;
-    if (p.splits == 1) {
-      p.out[(static_cast<int64_t>(b) * p.q_heads + hq) * D + c] = so / sl;
-    } else {
-      float* part = part_bh + (static_cast<int64_t>(hh) * p.splits + split) * (D + 2);
-      store_coherent(part + 2 + c, so);
-      if (c == 0) {
-        store_coherent(part, M);
-        store_coherent(part + 1, sl);
-      }
-    }
-  }
-  if (p.splits == 1) return;
-
-  // ---- the last block of this (sequence, KV head) merges every partial ------
-  // M = max_s m_s; out = sum_s 2^(m_s-M) o_s / sum_s 2^(m_s-M) l_s. Partials
-  // are written and read at device scope (through to the coherence point, not
-  // the per-XCD L2); the counter lives in the workspace and is returned to
-  // zero for the next call.
-  // every wave's partial stores (device scope, written through) have completed
-  // before the block's arrival is counted: the block that counts last reads them
-  wait_vm<0>();
-  __syncthreads();
-  if (tid == 0) {
-    const int done = __hip_atomic_fetch_add(&p.counters[unit], 1, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-    last_block = done == p.splits - 1;
-  }
-  __syncthreads();
-  if (!last_block) return;
-  // each thread merges up to two output elements at a time, with the loads of
-  // a batch of 8 splits for both issued before any use
-  constexpr int PER = (HG * D + kThreads - 1) / kThreads;
-  constexpr int CH = PER < 2 ? PER : 2;
-  for (int e0 = 0; e0 < PER; e0 += CH) {
-    float M[CH], so[CH], sl[CH];
-#pragma unroll
-    for (int e = 0; e < CH; ++e) {
-      M[e] = -INFINITY;
-      so[e] = 0.f;
-      sl[e] = 0.f;
-    }
-    for (int s0 = 0; s0 < p.splits; s0 += 8) {
-      float mv[CH][8], lv[CH][8], ov[CH][8];
-#pragma unroll
-      for (int e = 0; e < CH; ++e) {
-        const int i = tid + (e0 + e) * kThreads;
-        const int hh = (i < HG * D ? i : 0) / D, c = i % D;
-        const float* part = part_bh + static_cast<int64_t>(hh) * p.splits * (D + 2);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float* ps = part + (s0 + k < p.splits ? s0 + k : s0) * (D + 2);
-          mv[e][k] = load_coherent(ps);
-          lv[e][k] = load_coherent(ps + 1);
-          ov[e][k] = load_coherent(ps + 2 + c);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < CH; ++e) {
-        float bm = -INFINITY;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) bm = s0 + k < p.splits ? fmaxf(bm, mv[e][k]) : bm;
-        const float Mn = fmaxf(M[e], bm);
-        const float a = fast_exp2(M[e] - Mn);
-        so[e] *= a;
-        sl[e] *= a;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float w8 = s0 + k < p.splits ? fast_exp2(mv[e][k] - Mn) : 0.f;
-          sl[e] = fmaf(w8, lv[e][k], sl[e]);
-          so[e] = fmaf(w8, ov[e][k], so[e]);
-        }
-        M[e] = Mn;
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < CH; ++e) {
-      const int i = tid + (e0 + e) * kThreads;
-      if (i < HG * D) {
-        const int hh = i / D, c = i % D;
-        p.out[(static_cast<int64_t>(b) * p.q_heads + h * HG + hh) * D + c] = so[e] / sl[e];
-      }
-    }
-  }
-  if (tid == 0)
-    __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  finish_unit<D, HG>(p, acc, mh, lsum, zsum, arena, last_block, b, h, split);
 }
 
 // ---- rotary keys, GQA group of 4: dense scores on v_mfma_f32_4x4x1_16b_f32 ----
@@ -876,7 +894,8 @@ __global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
   __shared__ int last_block;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform in the wave
   const int j = lane & 15, g = lane >> 4;          // 16x16 operand coordinates
   const int hd = lane & 3;                          // head of this lane (4x4 column)
   const int tk = lane & 31;                         // token of this lane (4x4 row)
@@ -1232,148 +1251,7 @@ __global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
       zsum[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, z_), hh));
     }
   }
-  __syncthreads();   // every wave is done with its page buffers (the arena)
-  float* red = reinterpret_cast<float*>(arena);   // [wave][HG][D + 2]: m, l, o
-  auto R = [&](int w, int hh) { return red + (w * HG + hh) * (D + 2); };
-  // acc rows 4g+r: row < HG is head row (hi), HG <= row < 2HG is head row-HG (lo)
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    float v[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float x = acc[nt][r];
-      if constexpr (HG == 1) {
-        x = r == 0 ? acc[nt][0] + acc[nt][1] : 0.f;
-      } else if constexpr (HG == 2) {
-        x = r < 2 ? acc[nt][r] + acc[nt][r + 2] : 0.f;
-      } else if constexpr (HG == 4) {
-        x += xor16(x);          // rows 0-3 (g=0) + rows 4-7 (g=1)
-      } else {
-        x += xor32(x);          // rows 0-7 (g=0,1) + rows 8-15 (g=2,3)
-      }
-      v[r] = x;
-    }
-    const int c = 16 * nt + j;
-    if (4 * g < HG) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int hh = 4 * g + r;
-        float zz = 0.f;   // sum_t p z_t of head hh goes to every channel
-#pragma unroll
-        for (int k = 0; k < HG; ++k) zz = hh == k ? zsum[k] : zz;
-        if (hh < HG) R(wave, hh)[2 + c] = v[r] + zz;
-      }
-    }
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-      R(wave, hh)[0] = mh[hh];
-      R(wave, hh)[1] = lsum[hh];
-    }
-  }
-  __syncthreads();
-
-  // ---- combine the waves; write the output, or this block's partial --------
-  float* part_bh = p.partials + (static_cast<int64_t>(b) * p.q_heads + h * HG) * p.splits * (D + 2);
-  for (int i = tid; i < HG * D; i += kThreads) {
-    const int hh = i / D, c = i % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, R(w, hh)[0]);
-    float so = 0.f, sl = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float e = fast_exp2(R(w, hh)[0] - M);   // idle wave: m = -inf -> 0
-      so = fmaf(e, R(w, hh)[2 + c], so);
-      sl = fmaf(e, R(w, hh)[1], sl);
-    }
-    const int hq = h * HG + hh;
-    if (p.splits == 1) {
-      p.out[(static_cast<int64_t>(b) * p.q_heads + hq) * D + c] = so / sl;
-    } else {
-      float* part = part_bh + (static_cast<int64_t>(hh) * p.splits + split) * (D + 2);
-      store_coherent(part + 2 + c, so);
-      if (c == 0) {
-        store_coherent(part, M);
-        store_coherent(part + 1, sl);
-      }
-    }
-  }
-  if (p.splits == 1) return;
-
-  // ---- the last block of this (sequence, KV head) merges every partial ------
-  // M = max_s m_s; out = sum_s 2^(m_s-M) o_s / sum_s 2^(m_s-M) l_s. Partials
-  // are written and read at device scope (through to the coherence point, not
-  // the per-XCD L2); the counter lives in the workspace and is returned to
-  // zero for the next call.
-  // every wave's partial stores (device scope, written through) have completed
-  // before the block's arrival is counted: the block that counts last reads them
-  wait_vm<0>();
-  __syncthreads();
-  if (tid == 0) {
-    const int done = __hip_atomic_fetch_add(&p.counters[unit], 1, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-    last_block = done == p.splits - 1;
-  }
-  __syncthreads();
-  if (!last_block) return;
-  // each thread merges up to two output elements at a time, with the loads of
-  // a batch of 8 splits for both issued before any use
-  constexpr int PER = (HG * D + kThreads - 1) / kThreads;
-  constexpr int CH = PER < 2 ? PER : 2;
-  for (int e0 = 0; e0 < PER; e0 += CH) {
-    float M[CH], so[CH], sl[CH];
-#pragma unroll
-    for (int e = 0; e < CH; ++e) {
-      M[e] = -INFINITY;
-      so[e] = 0.f;
-      sl[e] = 0.f;
-    }
-    for (int s0 = 0; s0 < p.splits; s0 += 8) {
-      float mv[CH][8], lv[CH][8], ov[CH][8];
-#pragma unroll
-      for (int e = 0; e < CH; ++e) {
-        const int i = tid + (e0 + e) * kThreads;
-        const int hh = (i < HG * D ? i : 0) / D, c = i % D;
-        const float* part = part_bh + static_cast<int64_t>(hh) * p.splits * (D + 2);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float* ps = part + (s0 + k < p.splits ? s0 + k : s0) * (D + 2);
-          mv[e][k] = load_coherent(ps);
-          lv[e][k] = load_coherent(ps + 1);
-          ov[e][k] = load_coherent(ps + 2 + c);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < CH; ++e) {
-        float bm = -INFINITY;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) bm = s0 + k < p.splits ? fmaxf(bm, mv[e][k]) : bm;
-        const float Mn = fmaxf(M[e], bm);
-        const float a = fast_exp2(M[e] - Mn);
-        so[e] *= a;
-        sl[e] *= a;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float w8 = s0 + k < p.splits ? fast_exp2(mv[e][k] - Mn) : 0.f;
-          sl[e] = fmaf(w8, lv[e][k], sl[e]);
-          so[e] = fmaf(w8, ov[e][k], so[e]);
-        }
-        M[e] = Mn;
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < CH; ++e) {
-      const int i = tid + (e0 + e) * kThreads;
-      if (i < HG * D) {
-        const int hh = i / D, c = i % D;
-        p.out[(static_cast<int64_t>(b) * p.q_heads + h * HG + hh) * D + c] = so[e] / sl[e];
-      }
-    }
-  }
-  if (tid == 0)
-    __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  finish_unit<D, HG>(p, acc, mh, lsum, zsum, arena, last_block, b, h, split);
 }
 
 
