@@ -1012,7 +1012,25 @@ __global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
   for (int hh = 0; hh < HG; ++hh) mh[hh] = -INFINITY;
   float lane_l = 0.f, lane_z = 0.f;
 
-  // qpage[wave][hh] = R(omega (T-1-t0)) q[hh]
+  // qpage[wave][hh] = R(omega (T-1-t0)) q[hh]; lane < D/2 keeps its pair of
+  // every head in qrot. rotate_q sets it from the angle; advance_q moves it to
+  // the wave's next page (kWaves pages = kWaves * 32 tokens on) by the fixed
+  // rotation R(-omega kWaves 32) of this lane's pair (dcs, dsn).
+  float qrot[HG][2];
+  float dcs = 1.f, dsn = 0.f;
+  if (lane < D / 2) {
+    const double turns = static_cast<double>(kWaves * kPage) * w2pi[lane];
+    sincospif(2.0f * static_cast<float>(turns - floor(turns)), &dsn, &dcs);
+  }
+  auto write_qpage = [&]() {
+    if (lane < D / 2) {
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh)
+        *reinterpret_cast<float2*>(&qpage[wave][hh][2 * lane]) = float2{qrot[hh][0], qrot[hh][1]};
+    }
+    wait_lds();
+    __builtin_amdgcn_wave_barrier();
+  };
   auto rotate_q = [&](int64_t t0) {
     if (lane < D / 2) {
       const double turns = static_cast<double>(p.T - 1 - t0) * w2pi[lane];
@@ -1021,12 +1039,22 @@ __global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
 #pragma unroll
       for (int hh = 0; hh < HG; ++hh) {
         const float q0 = qpair[hh][0], q1 = qpair[hh][1];
-        *reinterpret_cast<float2*>(&qpage[wave][hh][2 * lane]) =
-            float2{fmaf(q0, cs, -(q1 * sn)), fmaf(q0, sn, q1 * cs)};
+        qrot[hh][0] = fmaf(q0, cs, -(q1 * sn));
+        qrot[hh][1] = fmaf(q0, sn, q1 * cs);
       }
     }
-    wait_lds();
-    __builtin_amdgcn_wave_barrier();
+    write_qpage();
+  };
+  auto advance_q = [&]() {
+    if (lane < D / 2) {
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) {
+        const float x = qrot[hh][0], y = qrot[hh][1];
+        qrot[hh][0] = fmaf(x, dcs, y * dsn);
+        qrot[hh][1] = fmaf(y, dcs, -(x * dsn));
+      }
+    }
+    write_qpage();
   };
 
   // y: this lane's HALF channels of its token (dequantised); rotates them by
@@ -1128,8 +1156,12 @@ __global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
     return __builtin_bit_cast(bf16x8, v);
   };
 
-  auto process_page = [&](const uint8_t* pg, int64_t t0) {
-    rotate_q(t0);
+  // page k of this wave starts at token t0; its qpage is set exactly every 16th
+  // page and advanced by one fixed rotation in between (the fp32 drift over 15
+  // steps stays near the rounding of one rotation)
+  auto process_page = [&](const uint8_t* pg, int64_t t0, int k) {
+    if ((k & 15) == 0) rotate_q(t0);
+    else advance_q();
     // this lane's token row, its channel half: D/8 bytes of 2-bit codes
     float y[HALF];
     {
@@ -1138,15 +1170,19 @@ __global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
 #pragma unroll
       for (int w = 0; w < HALF / 16; ++w) {
         const uint32_t word = *reinterpret_cast<const uint32_t*>(pg + krow_off<CPR_K>(tk, hf * (D / 8) + 4 * w));
+        // nibble n of ev / od: the code of channel 2n / 2n + 1 of the word, so
+        // byte q4 of ev holds channels 4 q4 and 4 q4 + 2, of od 4 q4 + 1 and 4 q4 + 3
+        const uint32_t ev = word & 0x33333333u, od = (word >> 2) & 0x33333333u;
+        const float2 ce[4] = {codes2_f32<0>(ev), codes2_f32<1>(ev), codes2_f32<2>(ev), codes2_f32<3>(ev)};
+        const float2 co[4] = {codes2_f32<0>(od), codes2_f32<1>(od), codes2_f32<2>(od), codes2_f32<3>(od)};
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const float4 sv = *reinterpret_cast<const float4*>(sp + 16 * w + 4 * q4);
           const float4 zv = *reinterpret_cast<const float4*>(zp + 16 * w + 4 * q4);
-          const uint32_t byte = (word >> (8 * q4)) & 0xFFu;
-          y[16 * w + 4 * q4 + 0] = fmaf(static_cast<float>(byte & 3u), sv.x, zv.x);
-          y[16 * w + 4 * q4 + 1] = fmaf(static_cast<float>((byte >> 2) & 3u), sv.y, zv.y);
-          y[16 * w + 4 * q4 + 2] = fmaf(static_cast<float>((byte >> 4) & 3u), sv.z, zv.z);
-          y[16 * w + 4 * q4 + 3] = fmaf(static_cast<float>(byte >> 6), sv.w, zv.w);
+          y[16 * w + 4 * q4 + 0] = fmaf(ce[q4].x, sv.x, zv.x);
+          y[16 * w + 4 * q4 + 1] = fmaf(co[q4].x, sv.y, zv.y);
+          y[16 * w + 4 * q4 + 2] = fmaf(ce[q4].y, sv.z, zv.z);
+          y[16 * w + 4 * q4 + 3] = fmaf(co[q4].y, sv.w, zv.w);
         }
       }
     }
@@ -1230,7 +1266,7 @@ __global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
     if (next) wait_vm<PG::DMA>();
     else wait_vm<0>();
     __builtin_amdgcn_wave_barrier();
-    process_page(wbuf + (k % PG::NBUF) * PG::BYTES, static_cast<int64_t>(pg0 + wave + kWaves * k) * kPage);
+    process_page(wbuf + (k % PG::NBUF) * PG::BYTES, static_cast<int64_t>(pg0 + wave + kWaves * k) * kPage, k);
   }
   wait_lds();
 

@@ -70,6 +70,14 @@ __device__ __forceinline__ half8 cat4h(uint32_t a, uint32_t b, uint32_t c, uint3
 template <typename V2>
 __device__ __forceinline__ uint32_t bits32(V2 v) { return __builtin_bit_cast(uint32_t, v); }
 
+// Byte SEL of y holds two 2-bit codes as FP4 E2M1 nibbles (code c reads as
+// c / 2) -> the exact codes as f32 (low nibble first).
+template <int SEL>
+__device__ __forceinline__ float2 codes2_f32(uint32_t y) {
+  const auto r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(y, 2.0f, SEL);
+  return float2{r[0], r[1]};
+}
+
 // Sum over aligned groups of 8 lanes (all lanes receive it).
 __device__ __forceinline__ float sum8(float v) {
   v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
