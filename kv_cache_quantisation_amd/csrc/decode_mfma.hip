@@ -281,8 +281,19 @@ __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* 
     __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Blocks of kivi_mfma_kernel<bits, d, *, rope> resident per CU: what its LDS
+// (page buffers, fragments, query) and registers are sized for. The split
+// plan fills one round of the 256 CUs with this many blocks each. (2-bit pages
+// at d <= 128 would fit a fourth block, but eight splits per (sequence, KV
+// head) instead of six measured no faster at batch 16, context 4096.)
+constexpr int kivi_blocks_per_cu(int bits, int d, bool rope) {
+  if (rope) return 2;
+  if (d >= 256) return bits == 2 ? 2 : 1;
+  return 3;
+}
+
 template <int BITS, int D, int HG, bool ROPE>
-__global__ __launch_bounds__(kThreads, ROPE ? 2 : 3) void kivi_mfma_kernel(MfmaParams p) {
+__global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(BITS, D, ROPE)) void kivi_mfma_kernel(MfmaParams p) {
   static_assert(BITS == 2 || BITS == 4, "2- or 4-bit pages");
   static_assert(!ROPE || (BITS == 2 && D <= 128), "rotary decode: 2-bit pages, head_dim <= 128");
   static_assert(2 * HG <= 16, "hi and lo columns of the GQA group fit one tile");
@@ -298,19 +309,26 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : 3) void kivi_mfma_kernel(MfmaP
   constexpr int REPS = (COMBOS + 63) / 64;
   constexpr int PER_HEAD = 4 * KS;       // fold units (lanes) per head
   constexpr int QB = (3 * HG + 15) / 16; // bf16 B-operand sets for the residual keys
-  constexpr int RED = kWaves * HG * (D + 2) * 4;
-  constexpr int ARENA = kWaves * PG::WAVE_LDS > RED ? kWaves * PG::WAVE_LDS : RED;
   static_assert(KW >= 1, "at least one word per lane");
-
-  __shared__ __attribute__((aligned(16))) float qs[HG][D];
   // B fragments of q' for the live columns (hi, lo): [column][(4 ks + g) ^ column]
   // in 16-byte slots; the XOR puts the 16 lanes that read one (ks, g) for
   // different columns, and the 16 lanes that write one column, on different
-  // LDS banks (no padding: three blocks must fit a CU's LDS)
+  // LDS banks (no padding)
   constexpr int FSTRIDE = 4 * KS;
   static_assert(FSTRIDE >= 8, "column slots cover the XOR range");
-  __shared__ __attribute__((aligned(16))) uint32_t frag[kWaves][2 * HG * FSTRIDE][4];
-  __shared__ __attribute__((aligned(16))) uint8_t arena[ARENA];              // page buffers / reduction
+  constexpr int FRAG = 2 * HG * FSTRIDE * 16;
+  // Per-wave LDS: [page buffer 0][page buffer 1][q' fragments]. A residual
+  // step's 8 key + 8 value rows borrow page buffer 1 and the fragments: the
+  // wave's first step is taken before its first page is computed (buffer 1 is
+  // first filled for page 1, the fragments first written for page 0), any
+  // further step after its last page.
+  constexpr int WAVE_LDS = PG::NBUF * PG::BYTES + FRAG > PG::BYTES + PG::RING
+                               ? PG::NBUF * PG::BYTES + FRAG : PG::BYTES + PG::RING;
+  constexpr int RED = kWaves * HG * (D + 2) * 4;
+  constexpr int ARENA = kWaves * WAVE_LDS > RED ? kWaves * WAVE_LDS : RED;
+
+  __shared__ __attribute__((aligned(16))) float qs[HG][D];
+  __shared__ __attribute__((aligned(16))) uint8_t arena[ARENA];              // per-wave areas / reduction
   // rotary decode: each wave's query rotated for the page in hand (row HG is
   // kept zero for the unused B columns), and omega_i / (2 pi) per channel pair
   __shared__ __attribute__((aligned(16))) float qpage[ROPE ? kWaves : 1][ROPE ? HG + 1 : 1][ROPE ? D : 4];
@@ -323,7 +341,8 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : 3) void kivi_mfma_kernel(MfmaP
   const int j = lane & 15, g = lane >> 4;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const uint8_t* slab = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes;
-  uint8_t* wbuf = arena + wave * PG::WAVE_LDS;
+  uint8_t* wbuf = arena + wave * WAVE_LDS;
+  uint32_t (*frag)[4] = reinterpret_cast<uint32_t (*)[4]>(wbuf + PG::NBUF * PG::BYTES);
 
   // (q staging and the first memory requests are issued below, after the
   // helpers they need are defined)
@@ -499,9 +518,9 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : 3) void kivi_mfma_kernel(MfmaP
       split_f16(qp[4], qp[6], hi[2], lo[2]);
       split_f16(qp[5], qp[7], hi[3], lo[3]);
       if (cidx < COMBOS) {
-        *reinterpret_cast<uint4*>(frag[wave][fh * FSTRIDE + ((4 * fk + fg) ^ (fh & 7))]) =
+        *reinterpret_cast<uint4*>(frag[fh * FSTRIDE + ((4 * fk + fg) ^ (fh & 7))]) =
             uint4{hi[0], hi[1], hi[2], hi[3]};
-        *reinterpret_cast<uint4*>(frag[wave][(HG + fh) * FSTRIDE + ((4 * fk + fg) ^ ((HG + fh) & 7))]) =
+        *reinterpret_cast<uint4*>(frag[(HG + fh) * FSTRIDE + ((4 * fk + fg) ^ ((HG + fh) & 7))]) =
             uint4{lo[0], lo[1], lo[2], lo[3]};
       }
     }
@@ -529,7 +548,7 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : 3) void kivi_mfma_kernel(MfmaP
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int col = j % (2 * HG);
-      const uint4 f = *reinterpret_cast<const uint4*>(frag[wave][col * FSTRIDE + ((4 * ks + g) ^ (col & 7))]);
+      const uint4 f = *reinterpret_cast<const uint4*>(frag[col * FSTRIDE + ((4 * ks + g) ^ (col & 7))]);
       bq[ks] = cat4h(f.x, f.y, f.z, f.w);
     }
 
@@ -622,7 +641,7 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : 3) void kivi_mfma_kernel(MfmaP
   // ---- residual (unquantised) tokens, 8 per step ----------------------------
   // Step hs covers tokens [q_tokens + 8 hs, +8); the steps of this (sequence,
   // KV head) are spread over all its waves. Rows go HBM -> LDS slot `wring`.
-  uint8_t* wring = wbuf + PG::NBUF * PG::BYTES;
+  uint8_t* wring = wbuf + PG::BYTES;
   constexpr int LPR = 2 * D / 16;           // lanes per bf16 row
   constexpr int RPI = 64 / LPR;             // rows per 16-byte-per-lane copy
   constexpr int RSTEP = 8;                  // tokens per residual step
@@ -1339,10 +1358,10 @@ MfmaPlan mfma_plan(const Geometry& g, int64_t tokens, int32_t requested) {
   if (requested > 0) {
     s = requested;
   } else {
-    // about one resident round of blocks (three per CU on 256 CUs, two with
-    // rotary keys), >= 8 pages each
+    // about one resident round of blocks (256 CUs), >= 8 pages each
     const int64_t units = static_cast<int64_t>(g.batch) * g.kv_heads;
-    const int64_t target = g.rope == 0.0 ? 768 : 512;
+    const bool rope = g.rope != 0.0;
+    const int64_t target = 256 * (rope ? 2 : kivi_blocks_per_cu(g.bits, g.d, false));
     s = (target + units - 1) / units;
     const int64_t cap = (pl.pages + 7) / 8;
     if (s > cap) s = cap;
