@@ -904,7 +904,10 @@ __global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
   constexpr int RSTEP = 8;
 
   __shared__ __attribute__((aligned(16))) float qs[HG][D];
-  __shared__ __attribute__((aligned(16))) float qpage[kWaves][HG][D];
+  // qpage rows (head, channel half) padded by 16 bytes: the 8 rows that the
+  // lanes of a wave read together start in different LDS banks
+  constexpr int QROW = HALF + 4;
+  __shared__ __attribute__((aligned(16))) float qpage[kWaves][HG * 2][QROW];
   // weights P' of the page in hand, [hi/lo][head][32 tokens] in bf16, in the
   // k order of the value operand
   __shared__ __attribute__((aligned(16))) uint16_t pbuf[kWaves][2][HG][32];
@@ -1045,7 +1048,8 @@ __global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
     if (lane < D / 2) {
 #pragma unroll
       for (int hh = 0; hh < HG; ++hh)
-        *reinterpret_cast<float2*>(&qpage[wave][hh][2 * lane]) = float2{qrot[hh][0], qrot[hh][1]};
+        *reinterpret_cast<float2*>(&qpage[wave][2 * hh + (2 * lane) / HALF][(2 * lane) % HALF]) =
+            float2{qrot[hh][0], qrot[hh][1]};
     }
     wait_lds();
     __builtin_amdgcn_wave_barrier();
@@ -1086,20 +1090,20 @@ __global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
       y[2 * m] = fmaf(x0, rcos[m], -(x1 * rsin[m]));
       y[2 * m + 1] = fmaf(x0, rsin[m], x1 * rcos[m]);
     }
-    const float* qb = &qpage[wave][hd][hf * HALF];
-    floatx4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0;
+    const float* qb = &qpage[wave][2 * hd + hf][0];
+    floatx4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0, c2 = c0, c3 = c0;   // four independent chains
 #pragma unroll
     for (int i = 0; i < HALF / 4; ++i) {
       const float4 bq = *reinterpret_cast<const float4*>(qb + 4 * i);
       c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(y[4 * i], bq.x, c0, 0, 0, 0);
       c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(y[4 * i + 1], bq.y, c1, 0, 0, 0);
-      c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(y[4 * i + 2], bq.z, c0, 0, 0, 0);
-      c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(y[4 * i + 3], bq.w, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_4x4x1f32(y[4 * i + 2], bq.z, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_4x4x1f32(y[4 * i + 3], bq.w, c3, 0, 0, 0);
     }
     floatx4 s;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float v = c0[r] + c1[r];
+      const float v = (c0[r] + c1[r]) + (c2[r] + c3[r]);
       s[r] = v + xor32(v);
     }
     return s;
