@@ -61,6 +61,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kRopeWaves = 4;      // waves per block of rope4_kernel
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct MfmaParams {
@@ -127,11 +128,12 @@ __device__ __forceinline__ float load_q(const uint8_t* base, int64_t idx, int bf
 // and value accumulators acc: rows 4g + r, high parts of the heads then their
 // remainders), writes the output rows (one split) or the block's partial, and
 // in the last block of a (sequence, KV head) to finish merges every partial.
-template <int D, int HG>
+template <int D, int HG, int NW = kWaves>
 __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* acc, const float* mh,
                                             const float* lsum, const float* zsum, uint8_t* arena,
                                             int& last_block, int b, int h, int split) {
   constexpr int NT = D / 16;
+  constexpr int NTH = NW * 64;             // threads of the block
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform in the wave
@@ -181,14 +183,14 @@ __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* 
 
   // ---- combine the waves; write the output, or this block's partial --------
   float* part_bh = p.partials + (static_cast<int64_t>(b) * p.q_heads + h * HG) * p.splits * (D + 2);
-  for (int i = tid; i < HG * D; i += kThreads) {
+  for (int i = tid; i < HG * D; i += NTH) {
     const int hh = i / D, c = i % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, R(w, hh)[0]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, R(w, hh)[0]);
     float so = 0.f, sl = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float e = fast_exp2(R(w, hh)[0] - M);   // idle wave: m = -inf -> 0
       so = fmaf(e, R(w, hh)[2 + c], so);
       sl = fmaf(e, R(w, hh)[1], sl);
@@ -225,7 +227,7 @@ __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* 
   if (!last_block) return;
   // each thread merges up to two output elements at a time, with the loads of
   // a batch of 8 splits for both issued before any use
-  constexpr int PER = (HG * D + kThreads - 1) / kThreads;
+  constexpr int PER = (HG * D + NTH - 1) / NTH;
   constexpr int CH = PER < 2 ? PER : 2;
   for (int e0 = 0; e0 < PER; e0 += CH) {
     float M[CH], so[CH], sl[CH];
@@ -239,7 +241,7 @@ __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* 
       float mv[CH][8], lv[CH][8], ov[CH][8];
 #pragma unroll
       for (int e = 0; e < CH; ++e) {
-        const int i = tid + (e0 + e) * kThreads;
+        const int i = tid + (e0 + e) * NTH;
         const int hh = (i < HG * D ? i : 0) / D, c = i % D;
         const float* part = part_bh + static_cast<int64_t>(hh) * p.splits * (D + 2);
 #pragma unroll
@@ -270,7 +272,7 @@ __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* 
     }
 #pragma unroll
     for (int e = 0; e < CH; ++e) {
-      const int i = tid + (e0 + e) * kThreads;
+      const int i = tid + (e0 + e) * NTH;
       if (i < HG * D) {
         const int hh = i / D, c = i % D;
         p.out[(static_cast<int64_t>(b) * p.q_heads + h * HG + hh) * D + c] = so[e] / sl[e];
@@ -889,31 +891,53 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(BITS, D, ROPE)) void k
 // is wave-uniform, and the weights P' are moved through LDS into the operand
 // layout of the value product (v_mfma_f32_16x16x32_bf16, as in
 // kivi_mfma_kernel).
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
+// The rotation of token position j by omega_i is a block-wide LDS table
+// (every wave uses the same token-to-lane map), so it costs no registers; the
+// key product runs in two chunks of a quarter of the channels to keep fewer
+// dequantised keys live. With 4 waves per block, LDS (53 760 B at d = 128)
+// and registers fit three blocks per CU.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
   constexpr int HG = 4, BITS = 2;
+  constexpr int NTH = NW * 64;           // threads of the block
   using PG = PageGeom<BITS, D>;
   constexpr int NT = D / 16;             // channel tiles of the value product
   constexpr int KROW = D * BITS / 8;     // bytes per key token row
   constexpr int CPR_K = KROW / 16;
   constexpr int HALF = D / 2;            // channels per lane
   constexpr int NPL = HALF / 2;          // channel pairs per lane
+  constexpr int CH = HALF / 2;           // channels per chunk of the key product
   constexpr int VROW = 32 * BITS / 8;    // bytes per value channel column
-  constexpr int RED = kWaves * HG * (D + 2) * 4;
-  constexpr int ARENA = kWaves * PG::WAVE_LDS > RED ? kWaves * PG::WAVE_LDS : RED;
   constexpr int RSTEP = 8;
+  static_assert(CH % 16 == 0, "whole code words per chunk");
+  // Per-wave LDS: two page buffers. A residual step (8 key + 8 value rows)
+  // borrows them: a wave takes all its steps before it requests its first page.
+  constexpr int WAVE_LDS = 2 * PG::BYTES;
+  static_assert(WAVE_LDS >= PG::RING, "a residual step fits the page buffers");
+  constexpr int RED = NW * HG * (D + 2) * 4;
+  constexpr int ARENA = NW * WAVE_LDS > RED + 16 ? NW * WAVE_LDS : RED + 16;
 
-  __shared__ __attribute__((aligned(16))) float qs[HG][D];
   // qpage rows (head, channel half) padded by 16 bytes: the 8 rows that the
   // lanes of a wave read together start in different LDS banks
   constexpr int QROW = HALF + 4;
-  __shared__ __attribute__((aligned(16))) float qpage[kWaves][HG * 2][QROW];
+  __shared__ __attribute__((aligned(16))) float qpage[NW][HG * 2][QROW];
   // weights P' of the page in hand, [hi/lo][head][32 tokens] in bf16, in the
   // k order of the value operand
-  __shared__ __attribute__((aligned(16))) uint16_t pbuf[kWaves][2][HG][32];
+  __shared__ __attribute__((aligned(16))) uint16_t pbuf[NW][2][HG][32];
   __shared__ __attribute__((aligned(16))) uint8_t arena[ARENA];
-  __shared__ double w2pi[D / 2];
-  __shared__ int last_block;
+  // rotation table: entry (half, m2, token) = {cos, sin} of omega_i * token for
+  // the pairs i = half * NPL + 2 m2 and the next one; consecutive tokens are
+  // consecutive 16-byte entries (the 32 lanes of a half read 512 bytes)
+  __shared__ __attribute__((aligned(16))) float4 rtab[2 * (NPL / 2) * 32];
+  // set-up data in LDS that is idle at that time: the scaled query in the
+  // rotation table (read into registers before the table is built), omega_i /
+  // (2 pi) in wave 0's weight buffer (each lane keeps its own in a register);
+  // the last-block flag of the merge lives in the arena, which is free then
+  static_assert(HG * D * 4 <= static_cast<int>(sizeof(rtab)), "query fits the table");
+  static_assert(D / 2 * 8 <= static_cast<int>(sizeof(pbuf)), "omega fits the weight buffers");
+  float (*qs)[D] = reinterpret_cast<float (*)[D]>(&rtab[0]);
+  double* w2pi = reinterpret_cast<double*>(&pbuf[0][0][0][0]);
+  int& last_block = *reinterpret_cast<int*>(arena + ARENA - 16);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -925,18 +949,18 @@ __global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int unit = b * p.kv_heads + h;
   const uint8_t* slab = p.layer_base + static_cast<int64_t>(unit) * p.slab_bytes;
-  uint8_t* wbuf = arena + wave * PG::WAVE_LDS;
-  uint8_t* wring = wbuf + PG::NBUF * PG::BYTES;
+  uint8_t* wbuf = arena + wave * WAVE_LDS;
+  uint8_t* wring = wbuf;
 
   const int pg0 = static_cast<int>(static_cast<int64_t>(split) * p.n_pages / p.splits);
   const int pg1 = static_cast<int>(static_cast<int64_t>(split + 1) * p.n_pages / p.splits);
-  const int n_mine = pg0 + wave < pg1 ? (pg1 - pg0 - wave + kWaves - 1) / kWaves : 0;
-  const int waves_total = p.splits * kWaves;
-  const int my_wave = (kWaves - 1 - wave) * p.splits + split;
+  const int n_mine = pg0 + wave < pg1 ? (pg1 - pg0 - wave + NW - 1) / NW : 0;
+  const int waves_total = p.splits * NW;
+  const int my_wave = (NW - 1 - wave) * p.splits + split;
 
   auto issue_page = [&](int k) {
-    const uint8_t* src = slab + static_cast<int64_t>(pg0 + wave + kWaves * k) * p.page_bytes;
-    const uint32_t dst = lds_addr(wbuf + (k % PG::NBUF) * PG::BYTES);
+    const uint8_t* src = slab + static_cast<int64_t>(pg0 + wave + NW * k) * p.page_bytes;
+    const uint32_t dst = lds_addr(wbuf + (k % 2) * PG::BYTES);
 #pragma unroll
     for (int i = 0; i < PG::DMA; ++i) {
       const int off = i * 1024 + lane * 16;
@@ -971,7 +995,7 @@ __global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
     return issued;
   };
 
-  // ---- first requests: q (wave 0), this wave's first residual step and page ----
+  // ---- first requests: q (wave 0), this wave's first residual step or page ----
   const int q_bytes = HG * D * (p.q_bf16 ? 2 : 4);
   int after_q = 0;
   if (wave == 0) {
@@ -980,21 +1004,22 @@ __global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
       if (off + lane * 16 < q_bytes) dma16(qsrc + off + lane * 16, lds_addr(&qs[0][0]) + off);
   }
   const bool has_step = my_wave < p.n_steps;
-  if (has_step) after_q += issue_step(my_wave);
-  if (n_mine > 0) {
+  if (has_step) {
+    after_q += issue_step(my_wave);
+  } else if (n_mine > 0) {
     issue_page(0);
     after_q += PG::DMA;
   }
-  for (int i = tid; i < D / 2; i += kThreads)
+  for (int i = tid; i < D / 2; i += NTH)
     w2pi[i] = pow(p.rope_theta, -2.0 * i / D) * 0.15915494309189535;   // omega_i / (2 pi)
   if (wave == 0) wait_vm_upto(after_q);   // q has landed
   __syncthreads();
   {
-    constexpr int PER = (HG * D + kThreads - 1) / kThreads;
+    constexpr int PER = (HG * D + NTH - 1) / NTH;
     float qv[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int i = tid + k * kThreads;
+      const int i = tid + k * NTH;
       qv[k] = 0.f;
       if (i < HG * D)
         qv[k] = p.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(&qs[0][0])[i])
@@ -1003,23 +1028,31 @@ __global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int i = tid + k * kThreads;
+      const int i = tid + k * NTH;
       if (i < HG * D) (&qs[0][0])[i] = qv[k] * p.qscale;
     }
-    __syncthreads();
   }
-  // rotation of this lane's token (position tk in its page or step) for its pairs
-  float rcos[NPL], rsin[NPL], qpair[HG][2];
-#pragma unroll
-  for (int m = 0; m < NPL; ++m) {
-    const double turns = static_cast<double>(tk) * w2pi[hf * NPL + m];
-    sincospif(2.0f * static_cast<float>(turns - floor(turns)), &rsin[m], &rcos[m]);
-  }
+  __syncthreads();
+  float qpair[HG][2];
 #pragma unroll
   for (int hh = 0; hh < HG; ++hh) {
     qpair[hh][0] = lane < D / 2 ? qs[hh][2 * lane] : 0.f;
     qpair[hh][1] = lane < D / 2 ? qs[hh][2 * lane + 1] : 0.f;
   }
+  const double w2pi_l = lane < D / 2 ? w2pi[lane] : 0.0;
+  __syncthreads();   // the query is in registers: the table may overwrite it
+  // rotation table (w2pi is ready since the first barrier)
+  for (int e = tid; e < 2 * (NPL / 2) * 32; e += NTH) {
+    const int t = e % 32, hm = e / 32;                 // hm = half * (NPL / 2) + m2
+    const int i0 = (hm / (NPL / 2)) * NPL + 2 * (hm % (NPL / 2));
+    float4 v;
+    double turns = static_cast<double>(t) * w2pi[i0];
+    sincospif(2.0f * static_cast<float>(turns - floor(turns)), &v.y, &v.x);
+    turns = static_cast<double>(t) * w2pi[i0 + 1];
+    sincospif(2.0f * static_cast<float>(turns - floor(turns)), &v.w, &v.z);
+    rtab[e] = v;
+  }
+  __syncthreads();   // table ready; omega read by all (wave 0's weight buffer is free)
 
   // ---- online softmax state --------------------------------------------------
   // mh[hh]: running max of head hh (wave-uniform). lane_l / lane_z: sums of p
@@ -1036,12 +1069,12 @@ __global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
 
   // qpage[wave][hh] = R(omega (T-1-t0)) q[hh]; lane < D/2 keeps its pair of
   // every head in qrot. rotate_q sets it from the angle; advance_q moves it to
-  // the wave's next page (kWaves pages = kWaves * 32 tokens on) by the fixed
-  // rotation R(-omega kWaves 32) of this lane's pair (dcs, dsn).
+  // the wave's next page (NW pages = NW * 32 tokens on) by the fixed rotation
+  // R(-omega NW 32) of this lane's pair (dcs, dsn).
   float qrot[HG][2];
   float dcs = 1.f, dsn = 0.f;
   if (lane < D / 2) {
-    const double turns = static_cast<double>(kWaves * kPage) * w2pi[lane];
+    const double turns = static_cast<double>(NW * kPage) * w2pi_l;
     sincospif(2.0f * static_cast<float>(turns - floor(turns)), &dsn, &dcs);
   }
   auto write_qpage = [&]() {
@@ -1056,7 +1089,7 @@ __global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
   };
   auto rotate_q = [&](int64_t t0) {
     if (lane < D / 2) {
-      const double turns = static_cast<double>(p.T - 1 - t0) * w2pi[lane];
+      const double turns = static_cast<double>(p.T - 1 - t0) * w2pi_l;
       float sn, cs;
       sincospif(2.0f * static_cast<float>(turns - floor(turns)), &sn, &cs);
 #pragma unroll
@@ -1080,35 +1113,40 @@ __global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
     write_qpage();
   };
 
-  // y: this lane's HALF channels of its token (dequantised); rotates them by
-  // the token's position, then the key product against qpage; returns the 4
-  // scores of tokens 4((l/4)%8) + r for head hd (both halves added)
-  auto scores = [&](float* y) -> floatx4 {
+  // y: channels [part * CH, part * CH + CH) of this lane's half of its token
+  // (dequantised); rotates them by the token's position (table), then adds
+  // their key product against qpage into the four chains c
+  const float* qrow = &qpage[wave][2 * hd + hf][0];
+  auto rotate_mfma = [&](float* y, int part, floatx4* c) {
 #pragma unroll
-    for (int m = 0; m < NPL; ++m) {
-      const float x0 = y[2 * m], x1 = y[2 * m + 1];
-      y[2 * m] = fmaf(x0, rcos[m], -(x1 * rsin[m]));
-      y[2 * m + 1] = fmaf(x0, rsin[m], x1 * rcos[m]);
+    for (int m2 = 0; m2 < CH / 4; ++m2) {
+      const float4 r = rtab[(hf * (NPL / 2) + part * (CH / 4) + m2) * 32 + tk];
+      const float x0 = y[4 * m2], x1 = y[4 * m2 + 1], x2 = y[4 * m2 + 2], x3 = y[4 * m2 + 3];
+      y[4 * m2] = fmaf(x0, r.x, -(x1 * r.y));
+      y[4 * m2 + 1] = fmaf(x0, r.y, x1 * r.x);
+      y[4 * m2 + 2] = fmaf(x2, r.z, -(x3 * r.w));
+      y[4 * m2 + 3] = fmaf(x2, r.w, x3 * r.z);
     }
-    const float* qb = &qpage[wave][2 * hd + hf][0];
-    floatx4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0, c2 = c0, c3 = c0;   // four independent chains
+    const float* qb = qrow + part * CH;
 #pragma unroll
-    for (int i = 0; i < HALF / 4; ++i) {
+    for (int i = 0; i < CH / 4; ++i) {
       const float4 bq = *reinterpret_cast<const float4*>(qb + 4 * i);
-      c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(y[4 * i], bq.x, c0, 0, 0, 0);
-      c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(y[4 * i + 1], bq.y, c1, 0, 0, 0);
-      c2 = __builtin_amdgcn_mfma_f32_4x4x1f32(y[4 * i + 2], bq.z, c2, 0, 0, 0);
-      c3 = __builtin_amdgcn_mfma_f32_4x4x1f32(y[4 * i + 3], bq.w, c3, 0, 0, 0);
+      c[0] = __builtin_amdgcn_mfma_f32_4x4x1f32(y[4 * i], bq.x, c[0], 0, 0, 0);
+      c[1] = __builtin_amdgcn_mfma_f32_4x4x1f32(y[4 * i + 1], bq.y, c[1], 0, 0, 0);
+      c[2] = __builtin_amdgcn_mfma_f32_4x4x1f32(y[4 * i + 2], bq.z, c[2], 0, 0, 0);
+      c[3] = __builtin_amdgcn_mfma_f32_4x4x1f32(y[4 * i + 3], bq.w, c[3], 0, 0, 0);
     }
+  };
+  // the 4 scores of tokens 4((l/4)%8) + r for head hd (both halves added)
+  auto finish_scores = [&](const floatx4* c) -> floatx4 {
     floatx4 s;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float v = (c0[r] + c1[r]) + (c2[r] + c3[r]);
+      const float v = (c[0][r] + c[1][r]) + (c[2][r] + c[3][r]);
       s[r] = v + xor32(v);
     }
     return s;
   };
-
   // folds 4 scores per lane (tokens 4((l/4)%8) + r, head hd; -inf = absent)
   // into the softmax state; returns the weights 2^(s - m)
   auto softmax = [&](floatx4 s) -> floatx4 {
@@ -1185,14 +1223,19 @@ __global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
   auto process_page = [&](const uint8_t* pg, int64_t t0, int k) {
     if ((k & 15) == 0) rotate_q(t0);
     else advance_q();
-    // this lane's token row, its channel half: D/8 bytes of 2-bit codes
-    float y[HALF];
-    {
-      const float* sp = reinterpret_cast<const float*>(pg + PG::OFF_KS) + hf * HALF;
-      const float* zp = reinterpret_cast<const float*>(pg + PG::OFF_KZ) + hf * HALF;
+    floatx4 c[4];
 #pragma unroll
-      for (int w = 0; w < HALF / 16; ++w) {
-        const uint32_t word = *reinterpret_cast<const uint32_t*>(pg + krow_off<CPR_K>(tk, hf * (D / 8) + 4 * w));
+    for (int i = 0; i < 4; ++i) c[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const float* sp = reinterpret_cast<const float*>(pg + PG::OFF_KS) + hf * HALF;
+    const float* zp = reinterpret_cast<const float*>(pg + PG::OFF_KZ) + hf * HALF;
+#pragma unroll
+    for (int part = 0; part < 2; ++part) {
+      // this lane's token row, channels [part * CH, +CH) of its half: CH / 16 words
+      float y[CH];
+#pragma unroll
+      for (int w = 0; w < CH / 16; ++w) {
+        const int cw = part * CH + 16 * w;   // first channel of the word within the half
+        const uint32_t word = *reinterpret_cast<const uint32_t*>(pg + krow_off<CPR_K>(tk, hf * (D / 8) + cw / 4));
         // nibble n of ev / od: the code of channel 2n / 2n + 1 of the word, so
         // byte q4 of ev holds channels 4 q4 and 4 q4 + 2, of od 4 q4 + 1 and 4 q4 + 3
         const uint32_t ev = word & 0x33333333u, od = (word >> 2) & 0x33333333u;
@@ -1200,16 +1243,17 @@ __global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
         const float2 co[4] = {codes2_f32<0>(od), codes2_f32<1>(od), codes2_f32<2>(od), codes2_f32<3>(od)};
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 sv = *reinterpret_cast<const float4*>(sp + 16 * w + 4 * q4);
-          const float4 zv = *reinterpret_cast<const float4*>(zp + 16 * w + 4 * q4);
+          const float4 sv = *reinterpret_cast<const float4*>(sp + cw + 4 * q4);
+          const float4 zv = *reinterpret_cast<const float4*>(zp + cw + 4 * q4);
           y[16 * w + 4 * q4 + 0] = fmaf(ce[q4].x, sv.x, zv.x);
           y[16 * w + 4 * q4 + 1] = fmaf(co[q4].x, sv.y, zv.y);
           y[16 * w + 4 * q4 + 2] = fmaf(ce[q4].y, sv.z, zv.z);
           y[16 * w + 4 * q4 + 3] = fmaf(co[q4].y, sv.w, zv.w);
         }
       }
+      rotate_mfma(y, part, c);
     }
-    const floatx4 w = softmax(scores(y));
+    const floatx4 w = softmax(finish_scores(c));
     // P' = p * s_t; sums of p and p * z_t (lanes < 32 own the tokens)
     const int t0q = 4 * ((lane >> 2) & 7);
     const float4 vs = *reinterpret_cast<const float4*>(pg + PG::OFF_VS + 4 * t0q);
@@ -1238,14 +1282,21 @@ __global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
     const int64_t t0 = p.q_tokens + static_cast<int64_t>(hs) * RSTEP;
     const int nv = static_cast<int>(p.T - t0 < RSTEP ? p.T - t0 : RSTEP);
     rotate_q(t0);
-    float y[HALF];
+    floatx4 c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = floatx4{0.f, 0.f, 0.f, 0.f};
     const uint16_t* kr = reinterpret_cast<const uint16_t*>(wring + (tk & 7) * 2 * D) + hf * HALF;
 #pragma unroll
-    for (int i = 0; i < HALF / 8; ++i) {
-      const uint4 v = *reinterpret_cast<const uint4*>(kr + 8 * i);
-      unpack_bf16x8(v, y + 8 * i);
+    for (int part = 0; part < 2; ++part) {
+      float y[CH];
+#pragma unroll
+      for (int i = 0; i < CH / 8; ++i) {
+        const uint4 v = *reinterpret_cast<const uint4*>(kr + part * CH + 8 * i);
+        unpack_bf16x8(v, y + 8 * i);
+      }
+      rotate_mfma(y, part, c);
     }
-    floatx4 s = scores(y);
+    floatx4 s = finish_scores(c);
 #pragma unroll
     for (int r = 0; r < 4; ++r) s[r] = 4 * ((lane >> 2) & 7) + r < nv ? s[r] : -INFINITY;
     const floatx4 w = softmax(s);
@@ -1264,21 +1315,23 @@ __global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
     }
   };
 
-  // ---- residual steps first (all of this wave's), then the pages ---------------
+  // ---- residual steps first (all of this wave's, in the page buffers), then
+  // the pages; a wave with steps requests its first page after them ------------
   for (int hs = my_wave; hs < p.n_steps; hs += waves_total) {
     if (hs != my_wave) {
       wait_lds();
       __builtin_amdgcn_wave_barrier();
       issue_step(hs);
-      wait_vm<0>();
-    } else if (n_mine > 0) {
-      wait_vm<PG::DMA>();   // the first page may stay in flight
-    } else {
-      wait_vm<0>();
     }
+    wait_vm<0>();
     wait_lds();
     __builtin_amdgcn_wave_barrier();
     process_step(hs);
+  }
+  if (has_step && n_mine > 0) {
+    wait_lds();   // the step rows have been read
+    __builtin_amdgcn_wave_barrier();
+    issue_page(0);
   }
 #pragma unroll 1
   for (int k = 0; k < n_mine; ++k) {
@@ -1289,7 +1342,7 @@ __global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
     if (next) wait_vm<PG::DMA>();
     else wait_vm<0>();
     __builtin_amdgcn_wave_barrier();
-    process_page(wbuf + (k % PG::NBUF) * PG::BYTES, static_cast<int64_t>(pg0 + wave + kWaves * k) * kPage, k);
+    process_page(wbuf + (k % 2) * PG::BYTES, static_cast<int64_t>(pg0 + wave + NW * k) * kPage, k);
   }
   wait_lds();
 
@@ -1310,7 +1363,7 @@ __global__ __launch_bounds__(kThreads, 2) void rope4_kernel(MfmaParams p) {
       zsum[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, z_), hh));
     }
   }
-  finish_unit<D, HG>(p, acc, mh, lsum, zsum, arena, last_block, b, h, split);
+  finish_unit<D, HG, NW>(p, acc, mh, lsum, zsum, arena, last_block, b, h, split);
 }
 
 
@@ -1338,8 +1391,8 @@ hipError_t by_d(const MfmaParams& p, int d, int hg, int batch, hipStream_t st) {
 hipError_t by_d_rope(const MfmaParams& p, int d, int hg, int batch, hipStream_t st) {
   if (hg == 4) {   // dense-score kernel
     dim3 grid(p.splits, p.kv_heads, batch);
-    if (d == 64) hipLaunchKernelGGL((rope4_kernel<64>), grid, dim3(kThreads), 0, st, p);
-    else hipLaunchKernelGGL((rope4_kernel<128>), grid, dim3(kThreads), 0, st, p);
+    if (d == 64) hipLaunchKernelGGL((rope4_kernel<64, kRopeWaves>), grid, dim3(64 * kRopeWaves), 0, st, p);
+    else hipLaunchKernelGGL((rope4_kernel<128, kRopeWaves>), grid, dim3(64 * kRopeWaves), 0, st, p);
     return hipGetLastError();
   }
   return d == 64 ? by_hg<2, 64, true>(p, hg, batch, st) : by_hg<2, 128, true>(p, hg, batch, st);
@@ -1365,7 +1418,8 @@ MfmaPlan mfma_plan(const Geometry& g, int64_t tokens, int32_t requested) {
     // about one resident round of blocks (256 CUs), >= 8 pages each
     const int64_t units = static_cast<int64_t>(g.batch) * g.kv_heads;
     const bool rope = g.rope != 0.0;
-    const int64_t target = 256 * (rope ? 2 : kivi_blocks_per_cu(g.bits, g.d, false));
+    // rotary keys at GQA 4 run rope4_kernel (three blocks per CU)
+    const int64_t target = 256 * (rope && g.hg == 4 ? 3 : kivi_blocks_per_cu(g.bits, g.d, rope));
     s = (target + units - 1) / units;
     const int64_t cap = (pl.pages + 7) / 8;
     if (s > cap) s = cap;
