@@ -41,21 +41,19 @@ struct AppendParams {
   int32_t off_kc, off_ks, off_kz, off_vc, off_vs, off_vz;
 };
 
-// Loads one token row of D elements (bf16 or f32 bytes) into an LDS row.
-template <int D, int IB>
-__device__ __forceinline__ void stage_row_chunk(const uint8_t* src, float* dst, int chunk) {
+// Widens one 16-byte chunk of a token row (bf16 or f32) into an fp32 LDS row.
+template <int IB>
+__device__ __forceinline__ void stage_chunk(const uint4& v, float* dst, int chunk) {
   if constexpr (IB == 2) {
-    const uint4 v = *reinterpret_cast<const uint4*>(src + chunk * 16);
     float f[8];
     unpack_bf16x8(v, f);
 #pragma unroll
     for (int i = 0; i < 8; ++i) dst[chunk * 8 + i] = f[i];
   } else {
-    const float4 v = *reinterpret_cast<const float4*>(src + chunk * 16);
-    dst[chunk * 4 + 0] = v.x;
-    dst[chunk * 4 + 1] = v.y;
-    dst[chunk * 4 + 2] = v.z;
-    dst[chunk * 4 + 3] = v.w;
+    dst[chunk * 4 + 0] = __uint_as_float(v.x);
+    dst[chunk * 4 + 1] = __uint_as_float(v.y);
+    dst[chunk * 4 + 2] = __uint_as_float(v.z);
+    dst[chunk * 4 + 3] = __uint_as_float(v.w);
   }
 }
 
@@ -92,23 +90,37 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
     else return reinterpret_cast<const float*>(row)[c];
   };
 
-  // 1. stage the page's 32 key and value rows (ring for tokens < past, else input)
-  for (int i = tid; i < 2 * kPage * CHUNKS; i += kThreads) {
-    const int which = i / (kPage * CHUNKS);   // 0 = K, 1 = V
-    const int r = (i / CHUNKS) % kPage;
-    const int c = i % CHUNKS;
-    const int64_t t = page * kPage + r;
-    const uint8_t* src;
-    if (t < p.past) {
-      const int64_t slot = t % p.ring_slots;
-      src = slab + p.ring_base + (which * p.ring_slots + slot) * ROW;
-    } else {
-      const int64_t j = t - p.past;
-      const uint8_t* base = which ? p.v_new : p.k_new;
-      src = base + ((static_cast<int64_t>(b) * p.n + j) * p.kv_heads + h) * ROW;
+  // 1. stage the page's 32 key and value rows (ring for tokens < past, else
+  //    input): every load of the thread is issued before the first LDS write
+  //    (no branch between them: each row's source is a select)
+  constexpr int NCH = 2 * kPage * CHUNKS;
+  static_assert(NCH % kThreads == 0, "whole chunks per thread");
+  constexpr int SPT = NCH / kThreads;          // 16-byte chunks per thread
+  const int64_t t_page = page * kPage;
+  const int slots = static_cast<int>(p.ring_slots);
+  const int s0 = static_cast<int>(t_page % p.ring_slots);
+  {
+    uint4 chunk[SPT];
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+      const int i = tid + k * kThreads;
+      const int which = i / (kPage * CHUNKS);   // 0 = K, 1 = V
+      const int r = (i / CHUNKS) % kPage;
+      const int64_t t = t_page + r;
+      const int slot = s0 + r >= slots ? s0 + r - slots : s0 + r;
+      const uint8_t* ring = slab + p.ring_base + (static_cast<int64_t>(which) * p.ring_slots + slot) * ROW;
+      const int64_t j = t >= p.past ? t - p.past : 0;
+      const uint8_t* in = (which ? p.v_new : p.k_new) +
+                          ((static_cast<int64_t>(b) * p.n + j) * p.kv_heads + h) * ROW;
+      chunk[k] = *reinterpret_cast<const uint4*>((t < p.past ? ring : in) + (i % CHUNKS) * 16);
     }
-    *reinterpret_cast<uint4*>(tile[which] + r * PITCH + c * 16) =
-        *reinterpret_cast<const uint4*>(src + c * 16);
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+      const int i = tid + k * kThreads;
+      const int which = i / (kPage * CHUNKS);
+      const int r = (i / CHUNKS) % kPage;
+      *reinterpret_cast<uint4*>(tile[which] + r * PITCH + (i % CHUNKS) * 16) = chunk[k];
+    }
   }
   __syncthreads();
 
@@ -266,14 +278,30 @@ __global__ __launch_bounds__(kThreads) void token_append_kernel(AppendParams p) 
   uint8_t* pg = slab + page * p.page_bytes;
   const int64_t row_bytes = static_cast<int64_t>(D) * IB;
 
-  for (int i = tid; i < 2 * (hi - lo) * CHUNKS; i += kThreads) {
+  // every load of the thread is issued before the first LDS write (threads
+  // past the last chunk load chunk 0 again and do not store it)
+  constexpr int SPT = (2 * kPage * CHUNKS + kThreads - 1) / kThreads;   // chunks per thread, at most
+  uint4 chunk[SPT];
+  const int nch = 2 * (hi - lo) * CHUNKS;
+#pragma unroll
+  for (int k = 0; k < SPT; ++k) {
+    const int i = tid + k * kThreads < nch ? tid + k * kThreads : 0;
     const int which = i / ((hi - lo) * CHUNKS);
     const int r = lo + (i / CHUNKS) % (hi - lo);
-    const int c = i % CHUNKS;
     const int64_t j = page * kPage + r - p.past;
     const uint8_t* src = (which ? p.v_new : p.k_new) +
                          ((static_cast<int64_t>(b) * p.n + j) * p.kv_heads + h) * row_bytes;
-    stage_row_chunk<D, IB>(src, (which ? vtile : ktile) + r * LD, c);
+    chunk[k] = *reinterpret_cast<const uint4*>(src + (i % CHUNKS) * 16);
+  }
+#pragma unroll
+  for (int k = 0; k < SPT; ++k) {
+    const int i = tid + k * kThreads;
+    if (i < nch) {
+      const int which = i / ((hi - lo) * CHUNKS);
+      const int r = lo + (i / CHUNKS) % (hi - lo);
+      const int c = i % CHUNKS;
+      stage_chunk<IB>(chunk[k], (which ? vtile : ktile) + r * LD, c);
+    }
   }
   __syncthreads();
 
