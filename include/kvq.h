@@ -80,10 +80,15 @@ extern "C" {
  * KVQ_FP8_E4M3: each element divided by a static per-(layer, KV head) fp32
  *   scale and rounded to OCP FP8 E4M3FN (nearest, ties to even mantissa,
  *   saturating at +-448). [QKV] "How the KV cache is quantized", FP8 KV cache.
- *   bits must be 8. */
+ *   bits must be 8.
+ * KVQ_BF16_CACHE: no quantisation, every value stored as bfloat16 (the
+ *   16-bit cache the pages compare the quantised ones against, [QKV] "The
+ *   other big memory user"); the baseline for measuring what 2/4/8-bit codes
+ *   save. bits must be 16. */
 #define KVQ_KIVI       0
 #define KVQ_SYM_TOKEN  1
 #define KVQ_FP8_E4M3   2
+#define KVQ_BF16_CACHE 3
 
 /* ---- dtypes (K/V input + residual ring, and the query) ------------------ */
 #define KVQ_F32   0
@@ -100,8 +105,9 @@ extern "C" {
  * one KV head (grouped-query attention). */
 typedef struct kvq_config {
   uint32_t struct_size;  /* = sizeof(kvq_config)                            */
-  int32_t  scheme;       /* KVQ_KIVI / KVQ_SYM_TOKEN / KVQ_FP8_E4M3         */
-  int32_t  bits;         /* 2, 4 or 8 (8 for FP8)                           */
+  int32_t  scheme;       /* KVQ_KIVI / KVQ_SYM_TOKEN / KVQ_FP8_E4M3 /
+                            KVQ_BF16_CACHE                                  */
+  int32_t  bits;         /* 2, 4 or 8 (8 for FP8, 16 for BF16_CACHE)        */
   int32_t  layers;       /* >= 1                                            */
   int32_t  q_heads;      /* kv_heads * {1, 2, 4, 8}                        */
   int32_t  kv_heads;     /* 1..65535                                        */
@@ -110,7 +116,7 @@ typedef struct kvq_config {
   int64_t  max_tokens;   /* capacity per sequence, < 2^36                   */
   int32_t  group;        /* tokens per page / key group; must be 32         */
   int32_t  residual;     /* KIVI: R >= 0 newest tokens kept unquantised;
-                            must be 0 for SYM_TOKEN and FP8                 */
+                            must be 0 for the other schemes                 */
   int32_t  in_dtype;     /* dtype of k_new/v_new and of the residual ring   */
   int32_t  q_dtype;      /* dtype of the decode query                       */
   double   rope_theta;   /* > 0: keys are cached before the rotary embedding
@@ -155,6 +161,9 @@ typedef struct kvq_config {
  * FP8_E4M3 page (64*d bytes), P = ceil(max_tokens/32):
  *   Kc  K rows, one E4M3FN byte per value      32*d
  *   Vc  V cols, one E4M3FN byte per value      32*d
+ * BF16_CACHE page (128*d bytes), P = ceil(max_tokens/32):
+ *   Kc  K rows, bfloat16 per value (16-bit fields)   64*d
+ *   Vc  V cols, bfloat16 per value                   64*d
  *
  * Which tokens are quantised (KIVI), for a cache holding T tokens:
  *   q(T) = 32*floor(max(0, T-R)/32) tokens live in pages [0, q(T)/32); the
@@ -175,6 +184,8 @@ typedef struct kvq_config {
  *   dequantised value = code*s.  [QC] Workshop.
  * FP8_E4M3: code = E4M3FN(x / scale[h]) (round to nearest, ties to even
  *   mantissa, |y| >= 448 -> +-448, sign kept); dequantised = value*scale[h].
+ * BF16_CACHE: bf16 input is stored bit for bit; fp32 input is rounded to
+ *   bfloat16 (nearest, ties to even); the stored value is used as is.
  * ========================================================================== */
 
 /* Bytes for `tokens` tokens per sequence. Host-only; never touches a device.

@@ -69,7 +69,8 @@ template <int SCHEME, int BITS>
 __device__ __forceinline__ float code_value(uint32_t w, int j) {
   if constexpr (SCHEME == KVQ_KIVI) return ucode<BITS>(w, j);
   else if constexpr (SCHEME == KVQ_SYM_TOKEN) return scode<BITS>(w, j);
-  else return e4m3_decode((w >> (8 * j)) & 0xFFu);
+  else if constexpr (SCHEME == KVQ_FP8_E4M3) return e4m3_decode((w >> (8 * j)) & 0xFFu);
+  else return __uint_as_float(j ? (w & 0xFFFF0000u) : (w << 16));   // bf16 field j
 }
 
 __device__ __forceinline__ float load_elem(const uint8_t* base, int64_t idx, int bf16) {
@@ -487,6 +488,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
         case 4: return by_d<KVQ_SYM_TOKEN, 4>(p, g.d, g.hg, g.batch, st);
         default: return by_d<KVQ_SYM_TOKEN, 8>(p, g.d, g.hg, g.batch, st);
       }
+    case KVQ_BF16_CACHE:
+      return by_d<KVQ_BF16_CACHE, 16>(p, g.d, g.hg, g.batch, st);
     default:
       return by_d<KVQ_FP8_E4M3, 8>(p, g.d, g.hg, g.batch, st);
   }

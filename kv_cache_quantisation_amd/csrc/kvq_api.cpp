@@ -23,10 +23,13 @@ int32_t validate_config(const kvq_config* cfg) {
   if (!cfg) return KVQ_ERR_NULL;
   if (cfg->struct_size != sizeof(kvq_config)) return KVQ_ERR_INVALID;
   const kvq_config& c = *cfg;
-  if (c.scheme != KVQ_KIVI && c.scheme != KVQ_SYM_TOKEN && c.scheme != KVQ_FP8_E4M3)
+  if (c.scheme != KVQ_KIVI && c.scheme != KVQ_SYM_TOKEN && c.scheme != KVQ_FP8_E4M3 &&
+      c.scheme != KVQ_BF16_CACHE)
     return KVQ_ERR_INVALID;
   if (c.scheme == KVQ_FP8_E4M3) {
     if (c.bits != 8) return KVQ_ERR_INVALID;
+  } else if (c.scheme == KVQ_BF16_CACHE) {
+    if (c.bits != 16) return KVQ_ERR_INVALID;
   } else if (c.bits != 2 && c.bits != 4 && c.bits != 8) {
     return (c.bits >= 1 && c.bits <= 8) ? KVQ_ERR_UNSUPPORTED : KVQ_ERR_INVALID;
   }
@@ -102,11 +105,11 @@ int32_t make_geometry(const kvq_config& c, Geometry* g) {
       x.page_bytes = 2 * codes + 8 * kPage;
       x.ring_slots = 0;
       break;
-    default:  // FP8
+    default:  // FP8 (b = 8) and BF16_CACHE (b = 16): K rows, then V cols
       x.off_kc = 0;
-      x.off_vc = kPage * d;
+      x.off_vc = codes;
       x.off_ks = x.off_kz = x.off_vs = x.off_vz = -1;
-      x.page_bytes = 2 * kPage * d;
+      x.page_bytes = 2 * codes;
       x.ring_slots = 0;
       break;
   }

@@ -78,6 +78,12 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
   return sign | mag;
 }
 
+// fp32 -> bfloat16 bits, nearest with ties to even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
 // OCP E4M3FN byte -> fp32 (finite codes).
 __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   const uint32_t e = (c >> 3) & 0xFu;

@@ -13,7 +13,7 @@
 
 from fractions import Fraction
 
-KIVI, SYM_TOKEN, FP8_E4M3 = 0, 1, 2
+KIVI, SYM_TOKEN, FP8_E4M3, BF16_CACHE = 0, 1, 2, 3
 PAGE = 32
 
 
@@ -59,6 +59,8 @@ def page_bytes(scheme, head_dim, bits):
         return PAGE * d * b // 8 + 4 * PAGE + PAGE * d * b // 8 + 4 * PAGE
     if scheme == FP8_E4M3:
         return PAGE * d + PAGE * d
+    if scheme == BF16_CACHE:
+        return PAGE * d * 2 + PAGE * d * 2      # 16-bit K rows + V cols
     raise ValueError(scheme)
 
 

@@ -13,6 +13,8 @@ chunked by construction:
   group; KIVI How It Works: recent tokens kept in 16-bit).
 * SYM_TOKEN / FP8_E4M3: every token is encoded as it arrives ("Quantising the
   Cache.", Workshop: rounded before it enters the cache).
+* BF16_CACHE: every token is stored as bfloat16 as it arrives (the 16-bit
+  baseline of "Quantizing the KV cache", "The other big memory user").
 
 Decode attention (``decode``) dequantises in float64, applies the rotary
 embedding to keys at their positions and to the query at position T-1 when
@@ -25,7 +27,8 @@ import numpy as np
 
 from . import accounting, attention, codec, layout, rope
 
-KIVI, SYM_TOKEN, FP8_E4M3 = accounting.KIVI, accounting.SYM_TOKEN, accounting.FP8_E4M3
+KIVI, SYM_TOKEN, FP8_E4M3, BF16_CACHE = (accounting.KIVI, accounting.SYM_TOKEN,
+                                         accounting.FP8_E4M3, accounting.BF16_CACHE)
 PAGE = 32
 
 
@@ -124,6 +127,8 @@ class OracleCache:
                 k32[:n], v32[:n] = K[p * PAGE:p * PAGE + n], V[p * PAGE:p * PAGE + n]
                 if self.scheme == SYM_TOKEN:
                     pb, pm = layout.sym_page(k32, v32, self.bits, n)
+                elif self.scheme == BF16_CACHE:
+                    pb, pm = layout.bf16_page(k32, v32, n)
                 else:
                     pb, pm = layout.fp8_page(k32, v32, self.k_scale[layer][h],
                                              self.v_scale[layer][h], n)
@@ -160,6 +165,9 @@ class OracleCache:
                 vh[:, :, sl] = codec.kivi_dequantize(vc, vs, vz, axis=3)
             kh[:, :, q:] = K[:, :, q:]
             vh[:, :, q:] = V[:, :, q:]
+        elif self.scheme == BF16_CACHE:
+            kh[:] = codec.bf16_decode(codec.bf16_encode(K))
+            vh[:] = codec.bf16_decode(codec.bf16_encode(V))
         elif self.scheme == SYM_TOKEN:
             kc, ks = codec.sym_quantize(K, self.bits, axis=3)
             vc, vs = codec.sym_quantize(V, self.bits, axis=3)

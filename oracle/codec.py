@@ -20,6 +20,11 @@ the formulas are written, with true division and ties-to-even rounding
   E4M3FN format (exponent bias 7, no infinities, S.1111.111 is NaN, largest
   finite 448); a value goes to the nearest finite E4M3 number, ties to the
   even code, so anything beyond 448 saturates to 448; the sign is kept.
+* ``bf16_encode`` / ``bf16_decode`` -- the unquantised 16-bit cache that the
+  pages measure the others against ("Quantizing the KV cache", "The other big
+  memory user": two bytes per value). Reading: bfloat16 (the top 16 bits of a
+  float32), float32 input rounded to the nearest bfloat16, ties to the even
+  pattern.
 """
 
 import numpy as np
@@ -133,3 +138,25 @@ def fp8_quantize(x, scale):
 
 def fp8_dequantize(codes, scale):
     return e4m3_decode(codes) * np.asarray(scale, np.float64)
+
+
+# ---- bfloat16 ---------------------------------------------------------------
+
+def bf16_encode(x):
+    """bfloat16 patterns (uint16) nearest to the finite float32 values `x`.
+
+    The two bfloat16 neighbours of a float32 are its top 16 bits (toward zero)
+    and that pattern plus one (away from zero); the dropped low 16 bits say
+    how far x is past the first: below half a unit keep it, above take the
+    next, exactly half take whichever pattern is even."""
+    bits = np.asarray(x, dtype=F32).view(np.uint32).astype(np.uint64)
+    keep = bits >> 16
+    dropped = bits & 0xFFFF
+    up = (dropped > 0x8000) | ((dropped == 0x8000) & ((keep & 1) == 1))
+    return (keep + up).astype(np.uint16)
+
+
+def bf16_decode(codes):
+    """Exact float64 values of bfloat16 patterns."""
+    raw = np.asarray(codes, np.uint16).astype(np.uint32) << 16
+    return raw.view(np.float32).astype(np.float64)

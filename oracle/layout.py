@@ -86,6 +86,21 @@ def sym_page(k32, v32, bits, n_valid):
     return buf, mask
 
 
+def bf16_page(k32, v32, n_valid):
+    """Unquantised page: bfloat16 K rows and V cols (2 bytes per value, least
+    significant byte first); tokens >= n_valid undefined."""
+    d = k32.shape[1]
+    valid = np.arange(PAGE) < n_valid
+    kc = np.where(valid[:, None], codec.bf16_encode(k32), 0).astype(np.uint16)
+    vc = np.where(valid[:, None], codec.bf16_encode(v32), 0).astype(np.uint16)
+    buf = np.concatenate([kc.astype("<u2").view(np.uint8).reshape(-1),
+                          np.ascontiguousarray(vc.T).astype("<u2").view(np.uint8).reshape(-1)])
+    tok = np.where(valid, 0xFF, 0).astype(np.uint8)
+    mask = np.concatenate([np.repeat(tok, 2 * d),            # K rows: a token's 2d bytes
+                           np.tile(np.repeat(tok, 2), d)])   # V cols: 2 bytes per token, per channel
+    return buf, mask
+
+
 def fp8_page(k32, v32, k_scale, v_scale, n_valid):
     """FP8 page with the KV head's scalar scales; tokens >= n_valid undefined."""
     d = k32.shape[1]

@@ -20,7 +20,7 @@ from dataclasses import dataclass, replace
 
 import torch
 
-KIVI, SYM_TOKEN, FP8_E4M3 = 0, 1, 2
+KIVI, SYM_TOKEN, FP8_E4M3, BF16_CACHE = 0, 1, 2, 3
 
 
 @dataclass(frozen=True)

@@ -103,6 +103,8 @@ def oracle_dequant_head(w, kf, vf, T, ks=None, vs=None):
             c, s, z = codec.kivi_quantize(vg, w.bits, axis=2)
             vh[:q] = codec.kivi_dequantize(c, s, z, axis=2).reshape(q, d)
         return kh, vh
+    if w.scheme == synth.BF16_CACHE:
+        return codec.bf16_decode(codec.bf16_encode(kf[:T])), codec.bf16_decode(codec.bf16_encode(vf[:T]))
     if w.scheme == synth.SYM_TOKEN:
         c, s = codec.sym_quantize(kf[:T], w.bits, axis=1)
         kh = codec.sym_dequantize(c, s, axis=1)

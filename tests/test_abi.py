@@ -66,13 +66,18 @@ def test_formula_matches_oracle(bits):
     # is twice the 8-bit formula value
     c = cfg(scheme=kvq.KVQ_FP8_E4M3, bits=8, residual=0, layers=32, batch=1)
     assert 2 * kvq.kvq_cache_bytes(c, 1, kvq.KVQ_BYTES_FORMULA) == 131072
+    # and directly for the unquantised bfloat16 cache
+    c = cfg(scheme=kvq.KVQ_BF16_CACHE, bits=16, residual=0, layers=32, batch=1)
+    assert kvq.kvq_cache_bytes(c, 1, kvq.KVQ_BYTES_FORMULA) == 131072 == \
+        acc.kv_bytes_formula(32, 8, 128, 1, 16)
 
 
 @pytest.mark.parametrize("scheme,bits,d,R,dtype", [
     (kvq.KVQ_KIVI, 2, 128, 128, kvq.KVQ_BF16), (kvq.KVQ_KIVI, 4, 64, 0, kvq.KVQ_F32),
     (kvq.KVQ_KIVI, 8, 256, 37, kvq.KVQ_BF16), (kvq.KVQ_KIVI, 2, 32, 5, kvq.KVQ_F32),
     (kvq.KVQ_SYM_TOKEN, 4, 32, 0, kvq.KVQ_F32), (kvq.KVQ_SYM_TOKEN, 2, 128, 0, kvq.KVQ_BF16),
-    (kvq.KVQ_FP8_E4M3, 8, 128, 0, kvq.KVQ_BF16)])
+    (kvq.KVQ_FP8_E4M3, 8, 128, 0, kvq.KVQ_BF16), (kvq.KVQ_BF16_CACHE, 16, 128, 0, kvq.KVQ_BF16),
+    (kvq.KVQ_BF16_CACHE, 16, 32, 0, kvq.KVQ_F32)])
 def test_cache_bytes_match_oracle_layout(scheme, bits, d, R, dtype):
     c = cfg(scheme=scheme, bits=bits, head_dim=d, residual=R, in_dtype=dtype, q_heads=8)
     item = 2 if dtype == kvq.KVQ_BF16 else 4
@@ -130,6 +135,11 @@ def test_scheme_specific_validation():
     assert L.kvq_cache_bytes(ctypes.byref(c), 8, 1) == kvq.KVQ_ERR_INVALID
     c = cfg(scheme=kvq.KVQ_FP8_E4M3, bits=4, residual=0)
     assert L.kvq_cache_bytes(ctypes.byref(c), 8, 1) == kvq.KVQ_ERR_INVALID
+    for bits, R in ((8, 0), (2, 0), (16, 4)):      # bfloat16 cache: bits 16, no residual
+        c = cfg(scheme=kvq.KVQ_BF16_CACHE, bits=bits, residual=R)
+        assert L.kvq_cache_bytes(ctypes.byref(c), 8, 1) == kvq.KVQ_ERR_INVALID
+    c = cfg(scheme=kvq.KVQ_BF16_CACHE, bits=16, residual=0)
+    assert L.kvq_cache_bytes(ctypes.byref(c), 64, 1) == 2 * 3 * 8 * 2 * 128 * 32 * 4
     c = cfg(scheme=kvq.KVQ_FP8_E4M3, bits=8, residual=0)
     fake = 1 << 20
     # FP8 needs its per-head scales

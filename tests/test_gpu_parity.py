@@ -81,6 +81,18 @@ def test_append_fp8_bytes(d, shrink, chunking):
     H.compare_bytes(cache.cpu().numpy(), want, mask, f"fp8 d{d} x{shrink} {chunking}")
 
 
+@pytest.mark.parametrize("chunking", ["one", "steps", "mixed"])
+@pytest.mark.parametrize("d,dtype", [(128, torch.bfloat16), (64, torch.float32),
+                                     (32, torch.float32), (256, torch.bfloat16)])
+def test_append_bf16_cache_bytes(d, dtype, chunking):
+    """Unquantised baseline: bf16 input stored bit for bit, fp32 input rounded
+    to nearest-even bfloat16."""
+    w = small(synth.BF16_CACHE, 16, d, dtype, T=269)
+    cfg, cache, oc, *_ = run_append(w, CHUNKINGS[chunking](w.tokens), capacity=300)
+    want, mask = oc.cache_image()
+    H.compare_bytes(cache.cpu().numpy(), want, mask, f"bf16 cache d{d} {chunking}")
+
+
 def test_append_special_values():
     """Constant groups (s = 0), signed zeros and exact ties."""
     w = small(synth.KIVI, 2, 32, torch.float32, R=0, T=96)
@@ -117,6 +129,10 @@ DECODE_CASES = [
     (synth.FP8_E4M3, 8, 128, 4, torch.bfloat16, 0, 333, 0.0, 0),
     (synth.FP8_E4M3, 8, 32, 1, torch.float32, 0, 65, 0.0, 2),
     (synth.FP8_E4M3, 8, 128, 4, torch.bfloat16, 0, 300, 500000.0, 0),
+    (synth.BF16_CACHE, 16, 128, 4, torch.bfloat16, 0, 333, 0.0, 0),
+    (synth.BF16_CACHE, 16, 32, 1, torch.float32, 0, 65, 0.0, 2),
+    (synth.BF16_CACHE, 16, 64, 8, torch.bfloat16, 0, 1, 0.0, 0),
+    (synth.BF16_CACHE, 16, 256, 2, torch.bfloat16, 0, 200, 500000.0, 3),
 ]
 
 

@@ -184,3 +184,41 @@ def test_fp8_quantize_uses_scale():
     x = np.array([2.0, -4.0, 896.0, 1000.0], F32)
     c = codec.fp8_quantize(x, F32(2.0))
     assert codec.fp8_dequantize(c, 2.0).tolist() == [2.0, -4.0, 896.0, 896.0]
+
+
+# ---- bfloat16 (the unquantised 16-bit baseline) ------------------------------
+
+def test_bf16_matches_torch():
+    """torch's float32 -> bfloat16 conversion rounds to nearest, ties to even."""
+    rng = np.random.default_rng(8)
+    bits = rng.integers(0, 0x7F800000, 20000, dtype=np.uint32)       # finite positives
+    bits = np.concatenate([bits, bits | 0x80000000,
+                           (bits & 0xFFFF0000) | 0x8000,              # exact ties
+                           (bits & 0xFFFF0000) | 0x7FFF, (bits & 0xFFFF0000) | 0x8001])
+    x = bits.view(F32)
+    x = x[np.abs(x) < np.float32(3.0e38)]          # stay clear of rounding up to infinity
+    ours = codec.bf16_encode(x)
+    theirs = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, theirs)
+
+
+def test_bf16_nearest_by_brute_force():
+    """For each input, no other bfloat16 pattern near it is closer, and ties
+    pick the even pattern (fp64 distances, small inputs)."""
+    rng = np.random.default_rng(9)
+    x = np.concatenate([rng.standard_normal(300), [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -0.0,
+                                                   2.0 ** -130, 65504.0]]).astype(F32)
+    codes = codec.bf16_encode(x).astype(np.int64)
+    for xi, c in zip(x, codes):
+        best = codec.bf16_decode(np.uint16(c))
+        for cand in (c - 2, c - 1, c + 1, c + 2):
+            if 0 <= cand <= 0xFFFF and (cand & 0x7F80) != 0x7F80 and (cand >> 15) == (c >> 15):
+                dc, db = abs(codec.bf16_decode(np.uint16(cand)) - float(xi)), abs(best - float(xi))
+                assert dc > db or (dc == db and c % 2 == 0), (xi, c, cand)
+
+
+def test_bf16_inputs_are_kept():
+    raw = np.array([0x3F80, 0xC049, 0x0001, 0x8000, 0x7F7F], np.uint16)
+    x = (raw.astype(np.uint32) << 16).view(F32)
+    assert np.array_equal(codec.bf16_encode(x), raw)
+    assert codec.bf16_decode(raw).tolist() == x.astype(np.float64).tolist()

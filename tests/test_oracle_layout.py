@@ -161,3 +161,20 @@ def test_cache_decode_small():
                            1 / np.sqrt(d))
     assert np.max(np.abs(out - ref)) < 0.02
     assert np.allclose(out[1, 2], attention.attend(q[1, 2], kh[1, 1], vh[1, 1], 1 / np.sqrt(d)))
+
+
+def test_bf16_page_layout():
+    """K rows then V cols, two bytes per value (low byte first); a partial page
+    defines only its tokens."""
+    rng = np.random.default_rng(3)
+    k = rng.standard_normal((32, 64)).astype(F32)
+    v = rng.standard_normal((32, 64)).astype(F32)
+    buf, mask = layout.bf16_page(k, v, 5)
+    assert buf.size == mask.size == acc.page_bytes(acc.BF16_CACHE, 64, 16) == 8192
+    kc = buf[:4096].view("<u2").reshape(32, 64)
+    vc = buf[4096:].view("<u2").reshape(64, 32)
+    assert np.array_equal(kc[:5], codec.bf16_encode(k[:5]))
+    assert np.array_equal(vc[:, :5], codec.bf16_encode(v[:5]).T)
+    assert np.all(mask[:5 * 128] == 0xFF) and np.all(mask[5 * 128:4096] == 0)
+    vm = mask[4096:].reshape(64, 64)
+    assert np.all(vm[:, :10] == 0xFF) and np.all(vm[:, 10:] == 0)
