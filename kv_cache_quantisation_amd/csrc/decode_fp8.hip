@@ -26,7 +26,17 @@
 // before conversion (unwritten bytes may hold E4M3 NaN patterns). Blocks of a
 // (sequence, KV head) write partial (m, l, o); the last block to finish merges
 // them and writes the output.
+//
+// The unquantised bfloat16 cache (the baseline the pages compare against)
+// runs through the same kernel: its key rows are already bf16 and feed the
+// key product directly (v_mfma_f32_16x16x32_bf16, q split into bf16 high and
+// remainder), and only the key rows (64*d bytes per page) are staged in LDS;
+// each lane loads the 16 value bytes it needs (8 tokens of one channel) from
+// HBM straight into registers, one page ahead, so a page costs no more LDS
+// than an FP8 page.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include <cmath>
 
@@ -58,11 +68,13 @@ struct Fp8Params {
   float qscale;                   // sm_scale * log2(e)
 };
 
-template <int D>
-struct Fp8Page {
-  static constexpr int OFF_VC = 32 * D;            // V cols after the K rows
-  static constexpr int BYTES = 64 * D;
-  static constexpr int DMA = BYTES / 1024;          // 16-byte-per-lane copies
+template <bool BF16, int D>
+struct PagedGeom {
+  static constexpr int EB = BF16 ? 2 : 1;            // bytes per cached value
+  static constexpr int KROW = D * EB;                // bytes per key token row
+  static constexpr int OFF_VC = 32 * KROW;           // V cols after the K rows
+  static constexpr int BYTES = BF16 ? OFF_VC : 2 * OFF_VC;   // staged in LDS per page
+  static constexpr int DMA = BYTES / 1024;           // 16-byte-per-lane copies
   static constexpr int NBUF = 2;
   static constexpr int WAVE_LDS = NBUF * BYTES;
 };
@@ -77,10 +89,10 @@ __device__ __forceinline__ uint32_t e4m3x2_bf16(uint32_t w) {
   return bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
-template <int D, int HG>
-__global__ __launch_bounds__(kThreads, 2) void fp8_mfma_kernel(Fp8Params p) {
+template <bool BF16, int D, int HG>
+__global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   static_assert(2 * HG <= 16, "high and remainder columns of the GQA group fit one tile");
-  using PG = Fp8Page<D>;
+  using PG = PagedGeom<BF16, D>;
   constexpr int KS = D / 32;             // k-steps of the key product
   constexpr int NT = D / 16;             // channel tiles of the value product
   constexpr int CPG = D / 4;             // key channels per lane group (contiguous bytes)
@@ -111,15 +123,27 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_mfma_kernel(Fp8Params p) {
 #pragma unroll
     for (int i = 0; i < PG::DMA; ++i) {
       const int off = i * 1024 + lane * 16;   // key rows: chunk permutation (see kswz)
-      const int from = off < PG::OFF_VC ? krow_off<D / 16>(off / D, off % D) : off;
+      const int from = off < PG::OFF_VC ? krow_off<PG::KROW / 16>(off / PG::KROW, off % PG::KROW) : off;
       dma16(src + from, dst + i * 1024);
     }
   };
-  if (n_mine > 0) issue_page(0);   // in flight while the query is staged
+  // bf16 values: lane (j, g) loads tokens 8g..8g+7 of channel 16 nt + j (16 bytes)
+  auto load_values = [&](int k, uint4* vr) {
+    const uint8_t* src = slab + static_cast<int64_t>(pg0 + wave + kWaves * k) * p.page_bytes +
+                         PG::OFF_VC + 16 * g;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      vr[nt] = *reinterpret_cast<const uint4*>(src + (16 * nt + j) * (kPage * 2));
+  };
+  uint4 va[BF16 ? NT : 1], vb[BF16 ? NT : 1];
+  if (n_mine > 0) {   // in flight while the query is staged
+    if constexpr (BF16) load_values(0, va);
+    issue_page(0);
+  }
 
   // ---- query group: q * sm_scale * log2(e) * ks_h ----------------------------
   {
-    const float mult = p.qscale * p.k_scale[h];
+    const float mult = BF16 ? p.qscale : p.qscale * p.k_scale[h];
     const int64_t q0 = (static_cast<int64_t>(b) * p.q_heads + h * HG) * D;
     for (int i = tid; i < HG * D; i += kThreads) {
       const float x = p.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(p.q)[q0 + i])
@@ -130,7 +154,9 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_mfma_kernel(Fp8Params p) {
   __syncthreads();
   // B operand of the key product for this lane: column j is head j % HG's
   // high part (j < HG), its remainder (HG <= j < 2HG) or zero.
-  half8 bq[KS];
+  // (f16 parts against the E4M3 keys, bf16 parts against bf16 keys)
+  using BQ = std::conditional_t<BF16, bf16x8, half8>;
+  BQ bq[KS];
   {
     const int hh = j % HG, part = j / HG;
 #pragma unroll
@@ -141,10 +167,11 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_mfma_kernel(Fp8Params p) {
         const float a = qs[hh][g * CPG + 8 * ks + 2 * i];
         const float c = qs[hh][g * CPG + 8 * ks + 2 * i + 1];
         uint32_t hi, lo;
-        split_f16(a, c, hi, lo);
+        if constexpr (BF16) split_bf16(a, c, hi, lo);
+        else split_f16(a, c, hi, lo);
         w4[i] = part == 0 ? hi : (part == 1 ? lo : 0u);
       }
-      bq[ks] = cat4h(w4[0], w4[1], w4[2], w4[3]);
+      bq[ks] = __builtin_bit_cast(BQ, uint4{w4[0], w4[1], w4[2], w4[3]});
     }
   }
 
@@ -154,7 +181,7 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_mfma_kernel(Fp8Params p) {
   for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_lane = -INFINITY, l_lane = 0.f;
 
-  auto process_page = [&](const uint8_t* pg, int n_valid) {
+  auto process_page = [&](const uint8_t* pg, int n_valid, const uint4* vr) {
     // scores; tile mt row rho = token 8(rho/4) + 4mt + rho%4
     float s[8];
 #pragma unroll
@@ -163,10 +190,16 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_mfma_kernel(Fp8Params p) {
       floatx4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const uint2 w = *reinterpret_cast<const uint2*>(pg + krow_off<D / 16>(row, g * CPG + 8 * ks));
-        const half8 a = cat4h(e4m3x2_f16<false>(w.x), e4m3x2_f16<true>(w.x),
-                              e4m3x2_f16<false>(w.y), e4m3x2_f16<true>(w.y));
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[ks], c, 0, 0, 0);
+        if constexpr (BF16) {
+          const uint4 w = *reinterpret_cast<const uint4*>(
+              pg + krow_off<PG::KROW / 16>(row, 2 * (g * CPG + 8 * ks)));
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), bq[ks], c, 0, 0, 0);
+        } else {
+          const uint2 w = *reinterpret_cast<const uint2*>(pg + krow_off<D / 16>(row, g * CPG + 8 * ks));
+          const half8 a = cat4h(e4m3x2_f16<false>(w.x), e4m3x2_f16<true>(w.x),
+                                e4m3x2_f16<false>(w.y), e4m3x2_f16<true>(w.y));
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[ks], c, 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) s[4 * mt + r] = c[r] + row_shl<HG>(c[r]);
@@ -210,36 +243,65 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_mfma_kernel(Fp8Params p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) pa[i] = shr_keep<HG>(ph[i], pl[i]);
     const bf16x8 ap = __builtin_bit_cast(bf16x8, uint4{pa[0], pa[1], pa[2], pa[3]});
-    // value bytes of tokens 8g..8g+7 of channel 16 nt + j; absent tokens -> 0
-    uint32_t m0 = 0xFFFFFFFFu, m1 = 0xFFFFFFFFu;
-    if (n_valid < kPage) {
-      const int k = min(max(n_valid - 8 * g, 0), 8);
-      m0 = k >= 4 ? 0xFFFFFFFFu : (1u << (8 * k)) - 1u;
-      m1 = k >= 8 ? 0xFFFFFFFFu : (k <= 4 ? 0u : (1u << (8 * (k - 4))) - 1u);
-    }
+    if constexpr (BF16) {
+      // values of tokens 8g..8g+7 of channel 16 nt + j (registers); absent
+      // tokens -> 0 (word w holds tokens 8g+2w, 8g+2w+1)
+      uint32_t mw[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+      if (n_valid < kPage) {
+        const int k = min(max(n_valid - 8 * g, 0), 8);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const uint2 w = *reinterpret_cast<const uint2*>(pg + PG::OFF_VC + (16 * nt + j) * kPage + 8 * g);
-      const uint32_t x0 = w.x & m0, x1 = w.y & m1;
-      const uint4 bw = uint4{e4m3x2_bf16<false>(x0), e4m3x2_bf16<true>(x0),
-                             e4m3x2_bf16<false>(x1), e4m3x2_bf16<true>(x1)};
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, __builtin_bit_cast(bf16x8, bw), acc[nt],
-                                                         0, 0, 0);
+        for (int w = 0; w < 4; ++w)
+          mw[w] = 2 * w + 2 <= k ? 0xFFFFFFFFu : (2 * w + 1 == k ? 0x0000FFFFu : 0u);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const uint4 bw = uint4{vr[nt].x & mw[0], vr[nt].y & mw[1], vr[nt].z & mw[2], vr[nt].w & mw[3]};
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, __builtin_bit_cast(bf16x8, bw), acc[nt],
+                                                           0, 0, 0);
+      }
+    } else {
+      (void)vr;
+      // value bytes of tokens 8g..8g+7 of channel 16 nt + j; absent tokens -> 0
+      uint32_t m0 = 0xFFFFFFFFu, m1 = 0xFFFFFFFFu;
+      if (n_valid < kPage) {
+        const int k = min(max(n_valid - 8 * g, 0), 8);
+        m0 = k >= 4 ? 0xFFFFFFFFu : (1u << (8 * k)) - 1u;
+        m1 = k >= 8 ? 0xFFFFFFFFu : (k <= 4 ? 0u : (1u << (8 * (k - 4))) - 1u);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const uint2 w = *reinterpret_cast<const uint2*>(pg + PG::OFF_VC + (16 * nt + j) * kPage + 8 * g);
+        const uint32_t x0 = w.x & m0, x1 = w.y & m1;
+        const uint4 bw = uint4{e4m3x2_bf16<false>(x0), e4m3x2_bf16<true>(x0),
+                               e4m3x2_bf16<false>(x1), e4m3x2_bf16<true>(x1)};
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, __builtin_bit_cast(bf16x8, bw), acc[nt],
+                                                           0, 0, 0);
+      }
     }
   };
 
   // ---- pages: DMA pipeline, one page ahead ----------------------------------
-#pragma unroll 1
-  for (int k = 0; k < n_mine; ++k) {
+  // (bf16: the value registers of page k+1 are requested before the key rows,
+  // so waiting for at most NT + DMA requests leaves page k's complete)
+  auto step = [&](int k, const uint4* cur, uint4* nxt) {
     wait_lds();   // the buffer about to be refilled has been read
     __builtin_amdgcn_wave_barrier();
     const bool next = k + 1 < n_mine;
-    if (next) issue_page(k + 1);
-    if (next) wait_vm<PG::DMA>();
-    else wait_vm<0>();
+    if (next) {
+      if constexpr (BF16) load_values(k + 1, nxt);
+      issue_page(k + 1);
+      wait_vm<(BF16 ? NT : 0) + PG::DMA>();
+    } else {
+      wait_vm<0>();
+    }
     __builtin_amdgcn_wave_barrier();
     const int page = pg0 + wave + kWaves * k;
-    process_page(wbuf + (k % PG::NBUF) * PG::BYTES, page == p.n_pages - 1 ? p.last_valid : kPage);
+    process_page(wbuf + (k % PG::NBUF) * PG::BYTES, page == p.n_pages - 1 ? p.last_valid : kPage, cur);
+  };
+#pragma unroll 1
+  for (int k = 0; k < n_mine; k += 2) {
+    step(k, va, vb);
+    if (k + 1 < n_mine) step(k + 1, vb, va);
   }
   wait_lds();
 
@@ -295,7 +357,7 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_mfma_kernel(Fp8Params p) {
   __syncthreads();
 
   // ---- combine the waves; write the output, or this block's partial --------
-  const float vs_h = p.v_scale[h];
+  const float vs_h = BF16 ? 1.0f : p.v_scale[h];
   float* part_bh = p.partials + (static_cast<int64_t>(b) * p.q_heads + h * HG) * p.splits * (D + 2);
   for (int i = tid; i < HG * D; i += kThreads) {
     const int hh = i / D, c = i % D;
@@ -370,22 +432,33 @@ __global__ __launch_bounds__(kThreads, 2) void fp8_mfma_kernel(Fp8Params p) {
     __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int D>
+template <bool BF16, int D>
 hipError_t by_hg(const Fp8Params& p, int hg, int batch, hipStream_t st) {
   dim3 grid(p.splits, p.kv_heads, batch);
   switch (hg) {
-    case 1: hipLaunchKernelGGL((fp8_mfma_kernel<D, 1>), grid, dim3(kThreads), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((fp8_mfma_kernel<D, 2>), grid, dim3(kThreads), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((fp8_mfma_kernel<D, 4>), grid, dim3(kThreads), 0, st, p); break;
-    default: hipLaunchKernelGGL((fp8_mfma_kernel<D, 8>), grid, dim3(kThreads), 0, st, p); break;
+    case 1: hipLaunchKernelGGL((paged_mfma_kernel<BF16, D, 1>), grid, dim3(kThreads), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((paged_mfma_kernel<BF16, D, 2>), grid, dim3(kThreads), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((paged_mfma_kernel<BF16, D, 4>), grid, dim3(kThreads), 0, st, p); break;
+    default: hipLaunchKernelGGL((paged_mfma_kernel<BF16, D, 8>), grid, dim3(kThreads), 0, st, p); break;
   }
   return hipGetLastError();
 }
 
+template <bool BF16>
+hipError_t by_d(const Fp8Params& p, int d, int hg, int batch, hipStream_t st) {
+  switch (d) {
+    case 64: return by_hg<BF16, 64>(p, hg, batch, st);
+    case 128: return by_hg<BF16, 128>(p, hg, batch, st);
+    default: return by_hg<BF16, 256>(p, hg, batch, st);
+  }
+}
+
 }  // namespace
 
+// FP8 and bf16 caches (head_dim >= 64, no rotary embedding) take the
+// matrix-core paged kernel.
 bool fp8_mfma_path(const Geometry& g) {
-  return g.scheme == KVQ_FP8_E4M3 && g.rope == 0.0 && g.d >= 64;
+  return (g.scheme == KVQ_FP8_E4M3 || g.scheme == KVQ_BF16_CACHE) && g.rope == 0.0 && g.d >= 64;
 }
 
 int32_t fp8_mfma_splits(const Geometry& g, int64_t tokens, int32_t requested) {
@@ -424,11 +497,8 @@ hipError_t launch_fp8_mfma(const DecodeArgs& a, hipStream_t st) {
   p.q_heads = g.q_heads;
   p.q_bf16 = a.q_dtype == KVQ_BF16;
   p.qscale = a.sm_scale * kLog2e;
-  switch (g.d) {
-    case 64: return by_hg<64>(p, g.hg, g.batch, st);
-    case 128: return by_hg<128>(p, g.hg, g.batch, st);
-    default: return by_hg<256>(p, g.hg, g.batch, st);
-  }
+  return g.scheme == KVQ_BF16_CACHE ? by_d<true>(p, g.d, g.hg, g.batch, st)
+                                    : by_d<false>(p, g.d, g.hg, g.batch, st);
 }
 
 }  // namespace kvq

@@ -75,7 +75,7 @@ struct MfmaPlan {
 bool mfma_path(const Geometry& g);
 MfmaPlan mfma_plan(const Geometry& g, int64_t tokens, int32_t requested);
 hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t stream);
-// Matrix-core path of FP8 E4M3 caches (head_dim >= 64, no rotary embedding).
+// Matrix-core path of FP8 E4M3 and bfloat16 caches (head_dim >= 64, no rotary embedding).
 bool fp8_mfma_path(const Geometry& g);
 int32_t fp8_mfma_splits(const Geometry& g, int64_t tokens, int32_t requested);
 hipError_t launch_fp8_mfma(const DecodeArgs& a, hipStream_t stream);
