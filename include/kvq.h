@@ -81,6 +81,9 @@ extern "C" {
  *   scale and rounded to OCP FP8 E4M3FN (nearest, ties to even mantissa,
  *   saturating at +-448). [QKV] "How the KV cache is quantized", FP8 KV cache.
  *   bits must be 8.
+ * KVQ_FP8_E5M2: as KVQ_FP8_E4M3 with the other FP8 format the page names,
+ *   OCP E5M2 (5 exponent bits, bias 15; nearest, ties to even mantissa,
+ *   saturating at +-57344, the largest finite value). bits must be 8.
  * KVQ_BF16_CACHE: no quantisation, every value stored as bfloat16 (the
  *   16-bit cache the pages compare the quantised ones against, [QKV] "The
  *   other big memory user"); the baseline for measuring what 2/4/8-bit codes
@@ -89,6 +92,7 @@ extern "C" {
 #define KVQ_SYM_TOKEN  1
 #define KVQ_FP8_E4M3   2
 #define KVQ_BF16_CACHE 3
+#define KVQ_FP8_E5M2   4
 
 /* ---- dtypes (K/V input + residual ring, and the query) ------------------ */
 #define KVQ_F32   0
@@ -106,7 +110,7 @@ extern "C" {
 typedef struct kvq_config {
   uint32_t struct_size;  /* = sizeof(kvq_config)                            */
   int32_t  scheme;       /* KVQ_KIVI / KVQ_SYM_TOKEN / KVQ_FP8_E4M3 /
-                            KVQ_BF16_CACHE                                  */
+                            KVQ_FP8_E5M2 / KVQ_BF16_CACHE                   */
   int32_t  bits;         /* 2, 4 or 8 (8 for FP8, 16 for BF16_CACHE)        */
   int32_t  layers;       /* >= 1                                            */
   int32_t  q_heads;      /* kv_heads * {1, 2, 4, 8}                        */
@@ -158,9 +162,9 @@ typedef struct kvq_config {
  *   Ks  fp32 scale per token                   128
  *   Vc  V cols, b-bit two's-complement codes   32*d*b/8
  *   Vs  fp32 scale per token                   128
- * FP8_E4M3 page (64*d bytes), P = ceil(max_tokens/32):
- *   Kc  K rows, one E4M3FN byte per value      32*d
- *   Vc  V cols, one E4M3FN byte per value      32*d
+ * FP8_E4M3 / FP8_E5M2 page (64*d bytes), P = ceil(max_tokens/32):
+ *   Kc  K rows, one FP8 byte per value         32*d
+ *   Vc  V cols, one FP8 byte per value         32*d
  * BF16_CACHE page (128*d bytes), P = ceil(max_tokens/32):
  *   Kc  K rows, bfloat16 per value (16-bit fields)   64*d
  *   Vc  V cols, bfloat16 per value                   64*d
@@ -184,6 +188,8 @@ typedef struct kvq_config {
  *   dequantised value = code*s.  [QC] Workshop.
  * FP8_E4M3: code = E4M3FN(x / scale[h]) (round to nearest, ties to even
  *   mantissa, |y| >= 448 -> +-448, sign kept); dequantised = value*scale[h].
+ * FP8_E5M2: code = E5M2(x / scale[h]) (round to nearest, ties to even
+ *   mantissa, |y| >= 57344 -> +-57344, sign kept); dequantised = value*scale[h].
  * BF16_CACHE: bf16 input is stored bit for bit; fp32 input is rounded to
  *   bfloat16 (nearest, ties to even); the stored value is used as is.
  * ========================================================================== */
@@ -204,7 +210,7 @@ KVQ_API int64_t kvq_cache_bytes(const kvq_config* cfg, int64_t tokens, int32_t k
  *   past_tokens  tokens already held per sequence (all sequences equal)
  *   k_new, v_new device [batch][new_tokens][kv_heads][head_dim], in_dtype
  *   k_scale,
- *   v_scale      FP8 only: device fp32 [kv_heads], this layer's per-head
+ *   v_scale      FP8 (either format) only: device fp32 [kv_heads], this layer's per-head
  *                scales (must be > 0); NULL for the other schemes
  * Requires past_tokens + new_tokens <= max_tokens (else KVQ_ERR_CAPACITY).
  * new_tokens == 0 is a no-op. Appending in any chunking (one call of T tokens

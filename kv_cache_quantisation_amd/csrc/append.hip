@@ -317,7 +317,7 @@ __global__ __launch_bounds__(kThreads) void token_append_kernel(AppendParams p) 
       (which ? v_sc : k_sc)[r] = s;
       reinterpret_cast<float*>(pg + (which ? p.off_vs : p.off_ks))[r] = s;
     }
-  } else if constexpr (SCHEME == KVQ_FP8_E4M3) {
+  } else if constexpr (is_fp8(SCHEME)) {
     if (tid < kPage) {
       k_sc[tid] = p.k_scale[h];
       v_sc[tid] = p.v_scale[h];
@@ -330,6 +330,8 @@ __global__ __launch_bounds__(kThreads) void token_append_kernel(AppendParams p) 
       return quant_sym(x, s, kQmax, kMask);
     } else if constexpr (SCHEME == KVQ_FP8_E4M3) {
       return e4m3_encode(x / s);
+    } else if constexpr (SCHEME == KVQ_FP8_E5M2) {
+      return e5m2_encode(x / s);
     } else {
       (void)s;
       return bf16_bits_rne(x);
@@ -405,6 +407,7 @@ template <int D, int IB>
 hipError_t dispatch_bits(const AppendArgs& a, const AppendParams& p, hipStream_t st) {
   const Geometry& g = a.g;
   if (g.scheme == KVQ_FP8_E4M3) return run_token<KVQ_FP8_E4M3, D, 8, IB>(a, p, st);
+  if (g.scheme == KVQ_FP8_E5M2) return run_token<KVQ_FP8_E5M2, D, 8, IB>(a, p, st);
   if (g.scheme == KVQ_BF16_CACHE) return run_token<KVQ_BF16_CACHE, D, 16, IB>(a, p, st);
   if (g.scheme == KVQ_SYM_TOKEN) {
     switch (g.bits) {

@@ -70,6 +70,7 @@ __device__ __forceinline__ float code_value(uint32_t w, int j) {
   if constexpr (SCHEME == KVQ_KIVI) return ucode<BITS>(w, j);
   else if constexpr (SCHEME == KVQ_SYM_TOKEN) return scode<BITS>(w, j);
   else if constexpr (SCHEME == KVQ_FP8_E4M3) return e4m3_decode((w >> (8 * j)) & 0xFFu);
+  else if constexpr (SCHEME == KVQ_FP8_E5M2) return e5m2_decode((w >> (8 * j)) & 0xFFu);
   else return __uint_as_float(j ? (w & 0xFFFF0000u) : (w << 16));   // bf16 field j
 }
 
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     __syncthreads();
   }
   {
-    const float ks_h = SCHEME == KVQ_FP8_E4M3 ? p.k_scale[h] : 1.0f;
+    const float ks_h = is_fp8(SCHEME) ? p.k_scale[h] : 1.0f;
     const float mult = p.qscale * ks_h;
     for (int i = tid; i < HG * D / 2; i += kThreads) {
       const int g = i / (D / 2), pr = i % (D / 2);
@@ -344,7 +345,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     }
   }
   __syncthreads();
-  const float vsc_h = SCHEME == KVQ_FP8_E4M3 ? p.v_scale[h] : 1.0f;
+  const float vsc_h = is_fp8(SCHEME) ? p.v_scale[h] : 1.0f;
   for (int i = tid; i < HG * D; i += kThreads) {
     const int g = i / D, c = i % D;
     float M = -INFINITY;
@@ -490,6 +491,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
       }
     case KVQ_BF16_CACHE:
       return by_d<KVQ_BF16_CACHE, 16>(p, g.d, g.hg, g.batch, st);
+    case KVQ_FP8_E5M2:
+      return by_d<KVQ_FP8_E5M2, 8>(p, g.d, g.hg, g.batch, st);
     default:
       return by_d<KVQ_FP8_E4M3, 8>(p, g.d, g.hg, g.batch, st);
   }

@@ -79,19 +79,28 @@ struct PagedGeom {
   static constexpr int WAVE_LDS = NBUF * BYTES;
 };
 
-// Two E4M3 bytes (low or high half of w) -> packed f16 / bf16, exact.
-template <bool HI>
-__device__ __forceinline__ uint32_t e4m3x2_f16(uint32_t w) {
-  return bits32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+// Two FP8 bytes (low or high half of w; E4M3, or E5M2 when E5) -> packed
+// f16 / bf16, exact (both formats lie inside the f16 and bf16 ranges).
+template <bool E5, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_f16(uint32_t w) {
+  if constexpr (E5) return bits32(__builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, HI));
+  else return bits32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
 }
-template <bool HI>
-__device__ __forceinline__ uint32_t e4m3x2_bf16(uint32_t w) {
-  return bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+template <bool E5, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
+  if constexpr (E5) return bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, HI));
+  else return bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
-template <bool BF16, int D, int HG>
+// FMT: KVQ_FP8_E4M3, KVQ_FP8_E5M2 or KVQ_BF16_CACHE. The E5M2 key scale is
+// applied to the scores after the product instead of to q: with the scales
+// that E5M2's range calls for (max |x| / 57344), q * ks would fall among the
+// f16 subnormals.
+template <int FMT, int D, int HG>
 __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   static_assert(2 * HG <= 16, "high and remainder columns of the GQA group fit one tile");
+  constexpr bool BF16 = FMT == KVQ_BF16_CACHE;
+  constexpr bool E5 = FMT == KVQ_FP8_E5M2;
   using PG = PagedGeom<BF16, D>;
   constexpr int KS = D / 32;             // k-steps of the key product
   constexpr int NT = D / 16;             // channel tiles of the value product
@@ -111,6 +120,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   const int unit = b * p.kv_heads + h;
   const uint8_t* slab = p.layer_base + static_cast<int64_t>(unit) * p.slab_bytes;
   uint8_t* wbuf = arena + wave * PG::WAVE_LDS;
+  const float ks_h = E5 ? p.k_scale[h] : 1.0f;   // applied to the scores (E5M2)
 
   // pages of this block, every kWaves-th one per wave
   const int pg0 = static_cast<int>(static_cast<int64_t>(split) * p.n_pages / p.splits);
@@ -143,7 +153,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
 
   // ---- query group: q * sm_scale * log2(e) * ks_h ----------------------------
   {
-    const float mult = BF16 ? p.qscale : p.qscale * p.k_scale[h];
+    const float mult = (BF16 || E5) ? p.qscale : p.qscale * p.k_scale[h];
     const int64_t q0 = (static_cast<int64_t>(b) * p.q_heads + h * HG) * D;
     for (int i = tid; i < HG * D; i += kThreads) {
       const float x = p.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(p.q)[q0 + i])
@@ -196,13 +206,17 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
           c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), bq[ks], c, 0, 0, 0);
         } else {
           const uint2 w = *reinterpret_cast<const uint2*>(pg + krow_off<D / 16>(row, g * CPG + 8 * ks));
-          const half8 a = cat4h(e4m3x2_f16<false>(w.x), e4m3x2_f16<true>(w.x),
-                                e4m3x2_f16<false>(w.y), e4m3x2_f16<true>(w.y));
+          const half8 a = cat4h(fp8x2_f16<E5, false>(w.x), fp8x2_f16<E5, true>(w.x),
+                                fp8x2_f16<E5, false>(w.y), fp8x2_f16<E5, true>(w.y));
           c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[ks], c, 0, 0, 0);
         }
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) s[4 * mt + r] = c[r] + row_shl<HG>(c[r]);
+    }
+    if constexpr (E5) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[i] *= ks_h;
     }
     if (n_valid < kPage) {
 #pragma unroll
@@ -272,8 +286,8 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
       for (int nt = 0; nt < NT; ++nt) {
         const uint2 w = *reinterpret_cast<const uint2*>(pg + PG::OFF_VC + (16 * nt + j) * kPage + 8 * g);
         const uint32_t x0 = w.x & m0, x1 = w.y & m1;
-        const uint4 bw = uint4{e4m3x2_bf16<false>(x0), e4m3x2_bf16<true>(x0),
-                               e4m3x2_bf16<false>(x1), e4m3x2_bf16<true>(x1)};
+        const uint4 bw = uint4{fp8x2_bf16<E5, false>(x0), fp8x2_bf16<E5, true>(x0),
+                               fp8x2_bf16<E5, false>(x1), fp8x2_bf16<E5, true>(x1)};
         acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, __builtin_bit_cast(bf16x8, bw), acc[nt],
                                                            0, 0, 0);
       }
@@ -432,33 +446,33 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
     __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <bool BF16, int D>
+template <int FMT, int D>
 hipError_t by_hg(const Fp8Params& p, int hg, int batch, hipStream_t st) {
   dim3 grid(p.splits, p.kv_heads, batch);
   switch (hg) {
-    case 1: hipLaunchKernelGGL((paged_mfma_kernel<BF16, D, 1>), grid, dim3(kThreads), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((paged_mfma_kernel<BF16, D, 2>), grid, dim3(kThreads), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((paged_mfma_kernel<BF16, D, 4>), grid, dim3(kThreads), 0, st, p); break;
-    default: hipLaunchKernelGGL((paged_mfma_kernel<BF16, D, 8>), grid, dim3(kThreads), 0, st, p); break;
+    case 1: hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 1>), grid, dim3(kThreads), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 2>), grid, dim3(kThreads), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 4>), grid, dim3(kThreads), 0, st, p); break;
+    default: hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 8>), grid, dim3(kThreads), 0, st, p); break;
   }
   return hipGetLastError();
 }
 
-template <bool BF16>
+template <int FMT>
 hipError_t by_d(const Fp8Params& p, int d, int hg, int batch, hipStream_t st) {
   switch (d) {
-    case 64: return by_hg<BF16, 64>(p, hg, batch, st);
-    case 128: return by_hg<BF16, 128>(p, hg, batch, st);
-    default: return by_hg<BF16, 256>(p, hg, batch, st);
+    case 64: return by_hg<FMT, 64>(p, hg, batch, st);
+    case 128: return by_hg<FMT, 128>(p, hg, batch, st);
+    default: return by_hg<FMT, 256>(p, hg, batch, st);
   }
 }
 
 }  // namespace
 
-// FP8 and bf16 caches (head_dim >= 64, no rotary embedding) take the
-// matrix-core paged kernel.
+// FP8 (either format) and bf16 caches (head_dim >= 64, no rotary embedding)
+// take the matrix-core paged kernel.
 bool fp8_mfma_path(const Geometry& g) {
-  return (g.scheme == KVQ_FP8_E4M3 || g.scheme == KVQ_BF16_CACHE) && g.rope == 0.0 && g.d >= 64;
+  return (is_fp8(g.scheme) || g.scheme == KVQ_BF16_CACHE) && g.rope == 0.0 && g.d >= 64;
 }
 
 int32_t fp8_mfma_splits(const Geometry& g, int64_t tokens, int32_t requested) {
@@ -497,8 +511,11 @@ hipError_t launch_fp8_mfma(const DecodeArgs& a, hipStream_t st) {
   p.q_heads = g.q_heads;
   p.q_bf16 = a.q_dtype == KVQ_BF16;
   p.qscale = a.sm_scale * kLog2e;
-  return g.scheme == KVQ_BF16_CACHE ? by_d<true>(p, g.d, g.hg, g.batch, st)
-                                    : by_d<false>(p, g.d, g.hg, g.batch, st);
+  switch (g.scheme) {
+    case KVQ_BF16_CACHE: return by_d<KVQ_BF16_CACHE>(p, g.d, g.hg, g.batch, st);
+    case KVQ_FP8_E5M2: return by_d<KVQ_FP8_E5M2>(p, g.d, g.hg, g.batch, st);
+    default: return by_d<KVQ_FP8_E4M3>(p, g.d, g.hg, g.batch, st);
+  }
 }
 
 }  // namespace kvq

@@ -24,9 +24,9 @@ int32_t validate_config(const kvq_config* cfg) {
   if (cfg->struct_size != sizeof(kvq_config)) return KVQ_ERR_INVALID;
   const kvq_config& c = *cfg;
   if (c.scheme != KVQ_KIVI && c.scheme != KVQ_SYM_TOKEN && c.scheme != KVQ_FP8_E4M3 &&
-      c.scheme != KVQ_BF16_CACHE)
+      c.scheme != KVQ_FP8_E5M2 && c.scheme != KVQ_BF16_CACHE)
     return KVQ_ERR_INVALID;
-  if (c.scheme == KVQ_FP8_E4M3) {
+  if (c.scheme == KVQ_FP8_E4M3 || c.scheme == KVQ_FP8_E5M2) {
     if (c.bits != 8) return KVQ_ERR_INVALID;
   } else if (c.scheme == KVQ_BF16_CACHE) {
     if (c.bits != 16) return KVQ_ERR_INVALID;
@@ -105,7 +105,7 @@ int32_t make_geometry(const kvq_config& c, Geometry* g) {
       x.page_bytes = 2 * codes + 8 * kPage;
       x.ring_slots = 0;
       break;
-    default:  // FP8 (b = 8) and BF16_CACHE (b = 16): K rows, then V cols
+    default:  // FP8, either format (b = 8), and BF16_CACHE (b = 16): K rows, then V cols
       x.off_kc = 0;
       x.off_vc = codes;
       x.off_ks = x.off_kz = x.off_vs = x.off_vz = -1;
@@ -242,7 +242,7 @@ int32_t kvq_quantize_append(const kvq_config* cfg, void* cache, int32_t layer,
     return KVQ_ERR_CAPACITY;
   if (new_tokens == 0) return KVQ_OK;
   if (!k_new || !v_new) return KVQ_ERR_NULL;
-  if (cfg->scheme == KVQ_FP8_E4M3 && (!k_scale || !v_scale)) return KVQ_ERR_NULL;
+  if (kvq::is_fp8(cfg->scheme) && (!k_scale || !v_scale)) return KVQ_ERR_NULL;
   if (!kvq::aligned16(cache) || !kvq::aligned16(k_new) || !kvq::aligned16(v_new))
     return KVQ_ERR_INVALID;
   kvq::AppendArgs a{};
@@ -268,7 +268,7 @@ int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache, int32_t l
   const int32_t st = kvq::make_geometry(*cfg, &g);
   if (st != KVQ_OK) return st;
   if (!cache || !q || !out || !workspace) return KVQ_ERR_NULL;
-  if (cfg->scheme == KVQ_FP8_E4M3 && (!k_scale || !v_scale)) return KVQ_ERR_NULL;
+  if (kvq::is_fp8(cfg->scheme) && (!k_scale || !v_scale)) return KVQ_ERR_NULL;
   if (layer < 0 || layer >= cfg->layers) return KVQ_ERR_INVALID;
   if (tokens < 1) return KVQ_ERR_INVALID;
   if (tokens > cfg->max_tokens) return KVQ_ERR_CAPACITY;

@@ -84,6 +84,34 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
   return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
 }
 
+// fp32 -> OCP E5M2, nearest with ties to even mantissa, saturating at 57344
+// (the largest finite value), sign kept. Normal results round the fp32
+// significand to 2 bits; below 2^-14 the grid is uniform with step 2^-16.
+__device__ __forceinline__ uint32_t e5m2_encode(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  uint32_t mag;
+  if (a >= 57344.0f) {
+    mag = 0x7Bu;
+  } else if (a < 6.103515625e-05f) {
+    mag = static_cast<uint32_t>(rintf(a * 65536.0f));   // exact scaling, 0..4
+  } else {
+    uint32_t b = __float_as_uint(a);
+    b += 0xFFFFFu + ((b >> 21) & 1u);                 // round to 2 mantissa bits, ties even
+    mag = (b >> 21) - (112u << 2);                    // exponent bias 127 -> 15
+  }
+  return sign | mag;
+}
+
+// OCP E5M2 byte -> fp32 (finite codes).
+__device__ __forceinline__ float e5m2_decode(uint32_t c) {
+  const uint32_t e = (c >> 2) & 0x1Fu;
+  const uint32_t m = c & 3u;
+  float v = e ? __uint_as_float(((e + 112u) << 23) | (m << 21))
+              : static_cast<float>(m) * 1.52587890625e-05f;
+  return (c & 0x80u) ? -v : v;
+}
+
 // OCP E4M3FN byte -> fp32 (finite codes).
 __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   const uint32_t e = (c >> 3) & 0xFu;

@@ -12,6 +12,11 @@ namespace kvq {
 
 constexpr int kPage = 32;  // tokens per page == KIVI key group
 
+// Either FP8 format: one byte per value, per-(layer, KV head) scales.
+__host__ __device__ constexpr bool is_fp8(int scheme) {
+  return scheme == KVQ_FP8_E4M3 || scheme == KVQ_FP8_E5M2;
+}
+
 // Everything a kernel needs to address one layer of the cache.
 struct Geometry {
   int32_t scheme, bits, d, hg, kv_heads, q_heads, batch, layers, residual;

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(PKG, "libkvq.so")
 
 KVQ_OK, KVQ_ERR_NULL, KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED = 0, -1, -2, -3
 KVQ_ERR_CAPACITY, KVQ_ERR_WORKSPACE, KVQ_ERR_DEVICE = -4, -5, -6
-KVQ_KIVI, KVQ_SYM_TOKEN, KVQ_FP8_E4M3, KVQ_BF16_CACHE = 0, 1, 2, 3
+KVQ_KIVI, KVQ_SYM_TOKEN, KVQ_FP8_E4M3, KVQ_BF16_CACHE, KVQ_FP8_E5M2 = 0, 1, 2, 3, 4
 KVQ_F32, KVQ_BF16 = 0, 1
 KVQ_BYTES_FORMULA, KVQ_BYTES_CACHE, KVQ_BYTES_WORKSPACE = 0, 1, 2
 

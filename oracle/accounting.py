@@ -13,7 +13,7 @@
 
 from fractions import Fraction
 
-KIVI, SYM_TOKEN, FP8_E4M3, BF16_CACHE = 0, 1, 2, 3
+KIVI, SYM_TOKEN, FP8_E4M3, BF16_CACHE, FP8_E5M2 = 0, 1, 2, 3, 4
 PAGE = 32
 
 
@@ -57,7 +57,7 @@ def page_bytes(scheme, head_dim, bits):
         return PAGE * d * b // 8 + 4 * d + 4 * d + PAGE * d * b // 8 + 4 * PAGE + 4 * PAGE
     if scheme == SYM_TOKEN:
         return PAGE * d * b // 8 + 4 * PAGE + PAGE * d * b // 8 + 4 * PAGE
-    if scheme == FP8_E4M3:
+    if scheme in (FP8_E4M3, FP8_E5M2):
         return PAGE * d + PAGE * d
     if scheme == BF16_CACHE:
         return PAGE * d * 2 + PAGE * d * 2      # 16-bit K rows + V cols

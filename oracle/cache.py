@@ -11,7 +11,7 @@ chunked by construction:
   residual ring unquantised, slot t mod (R + 32) ("Quantizing the KV cache":
   the newest R tokens stay in full precision, a full window is quantised as a
   group; KIVI How It Works: recent tokens kept in 16-bit).
-* SYM_TOKEN / FP8_E4M3: every token is encoded as it arrives ("Quantising the
+* SYM_TOKEN / FP8 (E4M3FN or E5M2): every token is encoded as it arrives ("Quantising the
   Cache.", Workshop: rounded before it enters the cache).
 * BF16_CACHE: every token is stored as bfloat16 as it arrives (the 16-bit
   baseline of "Quantizing the KV cache", "The other big memory user").
@@ -27,8 +27,9 @@ import numpy as np
 
 from . import accounting, attention, codec, layout, rope
 
-KIVI, SYM_TOKEN, FP8_E4M3, BF16_CACHE = (accounting.KIVI, accounting.SYM_TOKEN,
-                                         accounting.FP8_E4M3, accounting.BF16_CACHE)
+KIVI, SYM_TOKEN, FP8_E4M3, BF16_CACHE, FP8_E5M2 = (
+    accounting.KIVI, accounting.SYM_TOKEN, accounting.FP8_E4M3, accounting.BF16_CACHE,
+    accounting.FP8_E5M2)
 PAGE = 32
 
 
@@ -62,7 +63,7 @@ class OracleCache:
         k_new, v_new = np.asarray(k_new), np.asarray(v_new)
         assert k_new.shape == v_new.shape and k_new.shape[0] == self.batch
         assert self.tokens(layer) + k_new.shape[1] <= self.capacity
-        if self.scheme == FP8_E4M3:
+        if self.scheme in (FP8_E4M3, FP8_E5M2):
             ks = np.asarray(k_scale, np.float32)
             vs = np.asarray(v_scale, np.float32)
             if self.k_scale[layer] is not None:   # static per-head scales
@@ -81,6 +82,9 @@ class OracleCache:
             return bf16_bits_to_f32(self.raw_k[layer]), bf16_bits_to_f32(self.raw_v[layer])
         return (np.asarray(self.raw_k[layer], np.float32),
                 np.asarray(self.raw_v[layer], np.float32))
+
+    def fp8_format(self):
+        return "e5m2" if self.scheme == FP8_E5M2 else "e4m3"
 
     # ---- byte image -------------------------------------------------------
     def slab_size(self):
@@ -131,7 +135,7 @@ class OracleCache:
                     pb, pm = layout.bf16_page(k32, v32, n)
                 else:
                     pb, pm = layout.fp8_page(k32, v32, self.k_scale[layer][h],
-                                             self.v_scale[layer][h], n)
+                                             self.v_scale[layer][h], n, self.fp8_format())
                 buf[p * ps:(p + 1) * ps], mask[p * ps:(p + 1) * ps] = pb, pm
         return buf, mask
 
@@ -176,8 +180,9 @@ class OracleCache:
         else:
             ksc = self.k_scale[layer][None, :, None, None]
             vsc = self.v_scale[layer][None, :, None, None]
-            kh[:] = codec.fp8_dequantize(codec.fp8_quantize(K, ksc), ksc)
-            vh[:] = codec.fp8_dequantize(codec.fp8_quantize(V, vsc), vsc)
+            f = self.fp8_format()
+            kh[:] = codec.fp8_dequantize(codec.fp8_quantize(K, ksc, f), ksc, f)
+            vh[:] = codec.fp8_dequantize(codec.fp8_quantize(V, vsc, f), vsc, f)
         return kh, vh
 
     def decode(self, layer, q, sm_scale=None, rope_theta=0.0):

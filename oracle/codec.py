@@ -20,6 +20,11 @@ the formulas are written, with true division and ties-to-even rounding
   E4M3FN format (exponent bias 7, no infinities, S.1111.111 is NaN, largest
   finite 448); a value goes to the nearest finite E4M3 number, ties to the
   even code, so anything beyond 448 saturates to 448; the sign is kept.
+* ``e5m2_encode`` / ``e5m2_decode`` -- the other FP8 format the same section
+  names ("E4M3 or E5M2"). Reading: OCP E5M2 (exponent bias 15, S.11111.00 is
+  infinity, S.11111.xx NaN, largest finite 57344); nearest finite value, ties
+  to the even code, beyond 57344 saturated (as for E4M3: no infinities are
+  produced); the sign is kept.
 * ``bf16_encode`` / ``bf16_decode`` -- the unquantised 16-bit cache that the
   pages measure the others against ("Quantizing the KV cache", "The other big
   memory user": two bytes per value). Reading: bfloat16 (the top 16 bits of a
@@ -107,6 +112,7 @@ def e4m3_encode(y):
     d_hi = np.abs(_MAGS[hi] - a)
     d_lo = np.abs(a - _MAGS[lo])
     pick_lo = (d_lo < d_hi) | ((d_lo == d_hi) & (lo % 2 == 0))
+    pick_lo &= a <= _MAGS[-1]            # beyond the largest finite value: saturate
     mag = np.where(pick_lo, lo, hi).astype(np.uint8)
     sign = np.signbit(y).astype(np.uint8) << 7
     return (mag | sign).astype(np.uint8)
@@ -116,7 +122,7 @@ def e4m3_encode_bruteforce(y):
     """Same rule by a full scan of all 127 finite magnitudes (small inputs)."""
     out = []
     for v in np.asarray(y, dtype=F32).reshape(-1):
-        a = abs(float(v))
+        a = min(abs(float(v)), 448.0)            # saturation, then the nearest of all
         best, best_d = None, None
         for c in range(0x7F):
             d = abs(E4M3_TABLE[c] - a)
@@ -130,14 +136,71 @@ def e4m3_decode(codes):
     return E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
-def fp8_quantize(x, scale):
-    """E4M3FN(x / scale) with a float32 scale per KV head (broadcast)."""
+# ---- FP8 E5M2 ----------------------------------------------------------------
+
+def e5m2_value(code):
+    """Value of one E5M2 byte by its definition (sign, 5-bit exponent with bias
+    15, 2-bit mantissa; exponent 0 is subnormal; exponent 31 is inf / NaN)."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 2) & 0x1F
+    m = code & 0x3
+    if e == 0x1F:
+        return sign * float("inf") if m == 0 else float("nan")
+    if e == 0:
+        return sign * (m / 4.0) * 2.0 ** (1 - 15)
+    return sign * (1.0 + m / 4.0) * 2.0 ** (e - 15)
+
+
+E5M2_TABLE = np.array([e5m2_value(c) for c in range(256)], dtype=np.float64)
+# Finite non-negative magnitudes are codes 0x00..0x7B, increasing with the code.
+_MAGS5 = E5M2_TABLE[:0x7C]
+
+
+def e5m2_encode(y):
+    """Nearest finite E5M2 number to each float32 `y`, ties to the even code,
+    beyond 57344 saturated, sign bit copied from y."""
+    y = np.asarray(y, dtype=F32)
+    a = np.abs(y).astype(np.float64)
+    hi = np.clip(np.searchsorted(_MAGS5, a, side="left"), 0, len(_MAGS5) - 1)
+    lo = np.clip(hi - 1, 0, len(_MAGS5) - 1)
+    d_hi = np.abs(_MAGS5[hi] - a)
+    d_lo = np.abs(a - _MAGS5[lo])
+    pick_lo = (d_lo < d_hi) | ((d_lo == d_hi) & (lo % 2 == 0))
+    pick_lo &= a <= _MAGS5[-1]           # beyond the largest finite value: saturate
+    mag = np.where(pick_lo, lo, hi).astype(np.uint8)
+    sign = np.signbit(y).astype(np.uint8) << 7
+    return (mag | sign).astype(np.uint8)
+
+
+def e5m2_encode_bruteforce(y):
+    """Same rule by a full scan of all 124 finite magnitudes (small inputs)."""
+    out = []
+    for v in np.asarray(y, dtype=F32).reshape(-1):
+        a = min(abs(float(v)), 57344.0)          # saturation, then the nearest of all
+        best, best_d = None, None
+        for c in range(0x7C):
+            d = abs(E5M2_TABLE[c] - a)
+            if best is None or d < best_d or (d == best_d and c % 2 == 0 and best % 2 == 1):
+                best, best_d = c, d
+        out.append(best | (0x80 if np.signbit(v) else 0))
+    return np.array(out, dtype=np.uint8).reshape(np.shape(y))
+
+
+def e5m2_decode(codes):
+    return E5M2_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def fp8_quantize(x, scale, fmt="e4m3"):
+    """FP8(x / scale) with a float32 scale per KV head (broadcast), E4M3FN or E5M2."""
     x = np.asarray(x, dtype=F32)
-    return e4m3_encode(x / np.asarray(scale, dtype=F32))
+    y = x / np.asarray(scale, dtype=F32)
+    return e5m2_encode(y) if fmt == "e5m2" else e4m3_encode(y)
 
 
-def fp8_dequantize(codes, scale):
-    return e4m3_decode(codes) * np.asarray(scale, np.float64)
+def fp8_dequantize(codes, scale, fmt="e4m3"):
+    vals = e5m2_decode(codes) if fmt == "e5m2" else e4m3_decode(codes)
+    return vals * np.asarray(scale, np.float64)
 
 
 # ---- bfloat16 ---------------------------------------------------------------

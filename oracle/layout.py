@@ -101,11 +101,12 @@ def bf16_page(k32, v32, n_valid):
     return buf, mask
 
 
-def fp8_page(k32, v32, k_scale, v_scale, n_valid):
-    """FP8 page with the KV head's scalar scales; tokens >= n_valid undefined."""
+def fp8_page(k32, v32, k_scale, v_scale, n_valid, fmt="e4m3"):
+    """FP8 page (E4M3FN or E5M2) with the KV head's scalar scales; tokens >=
+    n_valid undefined."""
     d = k32.shape[1]
-    kc = codec.fp8_quantize(k32, k_scale)
-    vc = codec.fp8_quantize(v32, v_scale)
+    kc = codec.fp8_quantize(k32, k_scale, fmt)
+    vc = codec.fp8_quantize(v32, v_scale, fmt)
     valid = np.arange(PAGE) < n_valid
     kc = np.where(valid[:, None], kc, 0).astype(np.uint8)
     vc = np.where(valid[:, None], vc, 0).astype(np.uint8)

@@ -20,7 +20,7 @@ from dataclasses import dataclass, replace
 
 import torch
 
-KIVI, SYM_TOKEN, FP8_E4M3, BF16_CACHE = 0, 1, 2, 3
+KIVI, SYM_TOKEN, FP8_E4M3, BF16_CACHE, FP8_E5M2 = 0, 1, 2, 3, 4
 
 
 @dataclass(frozen=True)
@@ -130,9 +130,10 @@ def query(w, layer=0, device="cpu", tag=0):
     return q.to(w.q_dtype)
 
 
-def fp8_scales(k, v):
-    """Static per-KV-head scales: max |x| over the head's context / 448 (the
-    caller's calibration of the FP8 range), float32 [kv_heads] each."""
-    ks = k.float().abs().amax(dim=(0, 1, 3)) / 448.0
-    vs = v.float().abs().amax(dim=(0, 1, 3)) / 448.0
+def fp8_scales(k, v, fmax=448.0):
+    """Static per-KV-head scales: max |x| over the head's context / fmax, the
+    format's largest finite value (448 for E4M3, 57344 for E5M2; the caller's
+    calibration of the FP8 range), float32 [kv_heads] each."""
+    ks = k.float().abs().amax(dim=(0, 1, 3)) / fmax
+    vs = v.float().abs().amax(dim=(0, 1, 3)) / fmax
     return ks.contiguous(), vs.contiguous()

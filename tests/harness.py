@@ -110,8 +110,9 @@ def oracle_dequant_head(w, kf, vf, T, ks=None, vs=None):
         kh = codec.sym_dequantize(c, s, axis=1)
         c, s = codec.sym_quantize(vf[:T], w.bits, axis=1)
         return kh, codec.sym_dequantize(c, s, axis=1)
-    kh = codec.fp8_dequantize(codec.fp8_quantize(kf[:T], ks), ks)
-    vh = codec.fp8_dequantize(codec.fp8_quantize(vf[:T], vs), vs)
+    f = "e5m2" if w.scheme == synth.FP8_E5M2 else "e4m3"
+    kh = codec.fp8_dequantize(codec.fp8_quantize(kf[:T], ks, f), ks, f)
+    vh = codec.fp8_dequantize(codec.fp8_quantize(vf[:T], vs, f), vs, f)
     return kh, vh
 
 

@@ -77,7 +77,7 @@ def test_formula_matches_oracle(bits):
     (kvq.KVQ_KIVI, 8, 256, 37, kvq.KVQ_BF16), (kvq.KVQ_KIVI, 2, 32, 5, kvq.KVQ_F32),
     (kvq.KVQ_SYM_TOKEN, 4, 32, 0, kvq.KVQ_F32), (kvq.KVQ_SYM_TOKEN, 2, 128, 0, kvq.KVQ_BF16),
     (kvq.KVQ_FP8_E4M3, 8, 128, 0, kvq.KVQ_BF16), (kvq.KVQ_BF16_CACHE, 16, 128, 0, kvq.KVQ_BF16),
-    (kvq.KVQ_BF16_CACHE, 16, 32, 0, kvq.KVQ_F32)])
+    (kvq.KVQ_BF16_CACHE, 16, 32, 0, kvq.KVQ_F32), (kvq.KVQ_FP8_E5M2, 8, 64, 0, kvq.KVQ_BF16)])
 def test_cache_bytes_match_oracle_layout(scheme, bits, d, R, dtype):
     c = cfg(scheme=scheme, bits=bits, head_dim=d, residual=R, in_dtype=dtype, q_heads=8)
     item = 2 if dtype == kvq.KVQ_BF16 else 4
@@ -140,6 +140,15 @@ def test_scheme_specific_validation():
         assert L.kvq_cache_bytes(ctypes.byref(c), 8, 1) == kvq.KVQ_ERR_INVALID
     c = cfg(scheme=kvq.KVQ_BF16_CACHE, bits=16, residual=0)
     assert L.kvq_cache_bytes(ctypes.byref(c), 64, 1) == 2 * 3 * 8 * 2 * 128 * 32 * 4
+    for bits in (4, 16):                                 # E5M2: bits 8
+        c = cfg(scheme=kvq.KVQ_FP8_E5M2, bits=bits, residual=0)
+        assert L.kvq_cache_bytes(ctypes.byref(c), 8, 1) == kvq.KVQ_ERR_INVALID
+    c = cfg(scheme=kvq.KVQ_FP8_E5M2, bits=8, residual=0)
+    fake = 1 << 20                                       # and needs its scales
+    assert L.kvq_quantize_append(ctypes.byref(c), fake, 0, 0, 4, fake, fake, None, fake, None) \
+        == kvq.KVQ_ERR_NULL
+    assert L.kvq_decode_attention(ctypes.byref(c), fake, 0, 8, fake, None, fake, fake, fake,
+                                  1 << 30, None) == kvq.KVQ_ERR_NULL
     c = cfg(scheme=kvq.KVQ_FP8_E4M3, bits=8, residual=0)
     fake = 1 << 20
     # FP8 needs its per-head scales

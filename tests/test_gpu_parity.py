@@ -37,8 +37,9 @@ def run_append(w, chunks, capacity, scales=None):
     oc = H.oracle_cache(w, capacity)
     k, v = synth.keys_values(w, device=DEV)
     ks = vs = None
-    if w.scheme == synth.FP8_E4M3:
-        ks, vs = scales if scales is not None else synth.fp8_scales(k, v)
+    if w.scheme in (synth.FP8_E4M3, synth.FP8_E5M2):
+        fmax = 57344.0 if w.scheme == synth.FP8_E5M2 else 448.0
+        ks, vs = scales if scales is not None else synth.fp8_scales(k, v, fmax)
         ks, vs = ks.to(DEV), vs.to(DEV)
     H.append_chunks(cfg, cache, k, v, chunks, ks=ks, vs=vs, oc=oc)
     torch.cuda.synchronize()
@@ -93,6 +94,20 @@ def test_append_bf16_cache_bytes(d, dtype, chunking):
     H.compare_bytes(cache.cpu().numpy(), want, mask, f"bf16 cache d{d} {chunking}")
 
 
+@pytest.mark.parametrize("chunking", ["one", "steps", "mixed"])
+@pytest.mark.parametrize("d,shrink", [(128, 1.0), (64, 0.02), (32, 1.0), (256, 3e3)])
+def test_append_fp8_e5m2_bytes(d, shrink, chunking):
+    """E5M2 pages; shrink < 1 saturates large values at 57344, shrink > 1
+    pushes small values into the E5M2 subnormal range."""
+    w = small(synth.FP8_E5M2, 8, d, T=269)
+    k, v = synth.keys_values(w, device=DEV)
+    ks, vs = synth.fp8_scales(k, v, 57344.0)
+    cfg, cache, oc, *_ = run_append(w, CHUNKINGS[chunking](w.tokens), capacity=300,
+                                    scales=(ks * shrink, vs * shrink))
+    want, mask = oc.cache_image()
+    H.compare_bytes(cache.cpu().numpy(), want, mask, f"e5m2 d{d} x{shrink} {chunking}")
+
+
 def test_append_special_values():
     """Constant groups (s = 0), signed zeros and exact ties."""
     w = small(synth.KIVI, 2, 32, torch.float32, R=0, T=96)
@@ -129,6 +144,10 @@ DECODE_CASES = [
     (synth.FP8_E4M3, 8, 128, 4, torch.bfloat16, 0, 333, 0.0, 0),
     (synth.FP8_E4M3, 8, 32, 1, torch.float32, 0, 65, 0.0, 2),
     (synth.FP8_E4M3, 8, 128, 4, torch.bfloat16, 0, 300, 500000.0, 0),
+    (synth.FP8_E5M2, 8, 128, 4, torch.bfloat16, 0, 333, 0.0, 0),
+    (synth.FP8_E5M2, 8, 64, 2, torch.bfloat16, 0, 97, 0.0, 3),
+    (synth.FP8_E5M2, 8, 32, 1, torch.float32, 0, 65, 0.0, 2),
+    (synth.FP8_E5M2, 8, 128, 8, torch.bfloat16, 0, 200, 500000.0, 0),
     (synth.BF16_CACHE, 16, 128, 4, torch.bfloat16, 0, 333, 0.0, 0),
     (synth.BF16_CACHE, 16, 32, 1, torch.float32, 0, 65, 0.0, 2),
     (synth.BF16_CACHE, 16, 64, 8, torch.bfloat16, 0, 1, 0.0, 0),

@@ -107,6 +107,7 @@ def test_layout_sizes():
     assert acc.page_bytes(acc.FP8_E4M3, 128, 8) == 256 * 32
     assert acc.page_bytes(acc.SYM_TOKEN, 32, 4) == 40 * 32
     assert acc.page_bytes(acc.BF16_CACHE, 128, 16) == 512 * 32      # 2 x 128 x 2 bytes per token
+    assert acc.page_bytes(acc.FP8_E5M2, 128, 8) == acc.page_bytes(acc.FP8_E4M3, 128, 8)
     for s in (acc.KIVI, acc.SYM_TOKEN):
         for d in (32, 64, 128, 256):
             for b in (2, 4, 8):

@@ -176,8 +176,8 @@ def test_e4m3_relative_error():
     y = rng.uniform(2.0 ** -6, 448.0, 20000).astype(F32)
     back = codec.e4m3_decode(codec.e4m3_encode(y))
     assert np.all(np.abs(back - y) / y <= 2.0 ** -4)
-    big = np.array([449.0, 1e4, -3e38], F32)
-    assert np.array_equal(np.abs(codec.e4m3_decode(codec.e4m3_encode(big))), [448.0] * 3)
+    big = np.array([449.0, 1e4, -3e38, 1e30], F32)
+    assert np.array_equal(np.abs(codec.e4m3_decode(codec.e4m3_encode(big))), [448.0] * 4)
 
 
 def test_fp8_quantize_uses_scale():
@@ -222,3 +222,48 @@ def test_bf16_inputs_are_kept():
     x = (raw.astype(np.uint32) << 16).view(F32)
     assert np.array_equal(codec.bf16_encode(x), raw)
     assert codec.bf16_decode(raw).tolist() == x.astype(np.float64).tolist()
+
+
+# ---- FP8 E5M2 -------------------------------------------------------------------
+
+def test_e5m2_table_definition():
+    assert codec.e5m2_value(0x3C) == 1.0 and codec.e5m2_value(0xBC) == -1.0
+    assert codec.e5m2_value(0x7B) == 57344.0                 # largest finite
+    assert codec.e5m2_value(0x04) == 2.0 ** -14              # smallest normal
+    assert codec.e5m2_value(0x01) == 2.0 ** -16              # smallest subnormal
+    assert codec.e5m2_value(0x7C) == float("inf") and np.isnan(codec.e5m2_value(0x7D))
+    mags = codec.E5M2_TABLE[:0x7C]
+    assert np.all(np.diff(mags) > 0)                          # increasing with the code
+
+
+def test_e5m2_vectorised_equals_bruteforce():
+    rng = np.random.default_rng(11)
+    y = np.concatenate([rng.standard_normal(400) * 10.0 ** rng.integers(-6, 5, 400),
+                        [0.0, -0.0, 57344.0, 60000.0, 1e9, 2.0 ** -17, 3 * 2.0 ** -17,
+                         1.125, 1.375, -1.625]]).astype(F32)
+    assert np.array_equal(codec.e5m2_encode(y), codec.e5m2_encode_bruteforce(y))
+
+
+def test_e5m2_matches_torch_in_range():
+    """torch.float8_e5m2 rounds to nearest-even and overflows to infinity; it
+    agrees wherever |y| < 61440 (the midpoint above 57344)."""
+    rng = np.random.default_rng(12)
+    y = np.concatenate([rng.uniform(-61439.0, 61439.0, 20000), rng.standard_normal(20000),
+                        rng.standard_normal(5000) * 1e-5]).astype(F32)
+    ours = codec.e5m2_encode(y)
+    theirs = torch.from_numpy(y).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert np.array_equal(ours, theirs)
+
+
+def test_e5m2_saturates_and_scales():
+    big = np.array([57344.0, 61440.0, 1e30, -7e4], F32)
+    assert np.array_equal(np.abs(codec.e5m2_decode(codec.e5m2_encode(big))), [57344.0] * 4)
+    rng = np.random.default_rng(13)
+    y = rng.uniform(2.0 ** -14, 57344.0, 20000).astype(F32)
+    back = codec.e5m2_decode(codec.e5m2_encode(y))
+    assert np.all(np.abs(back - y) / y <= 2.0 ** -3)          # half of a 2-bit mantissa step
+    # 1e5 / 2 = 50000 lies between 49152 and 57344, nearer the first;
+    # 1.2e5 / 2 = 60000 is beyond the largest finite value and saturates
+    x = np.array([2.0, -4.0, 1.0e5, 1.2e5], F32)
+    c = codec.fp8_quantize(x, F32(2.0), "e5m2")
+    assert codec.fp8_dequantize(c, 2.0, "e5m2").tolist() == [2.0, -4.0, 98304.0, 114688.0]
