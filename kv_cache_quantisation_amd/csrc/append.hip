@@ -9,11 +9,13 @@
 // this call's input, so the flush runs before the ring is overwritten: two
 // launches in stream order.
 //
-// SYM_TOKEN ("Quantising the Cache.", Workshop) and FP8_E4M3 ("Quantizing the
-// KV cache", FP8 KV cache with per-head scales): every new token is encoded on
-// arrival into the page that holds it; value codes are channel-major inside a
-// page, so a partially filled page is updated with read-modify-write of the
-// words that carry the new tokens' fields (each word owned by one thread).
+// SYM_TOKEN ("Quantising the Cache.", Workshop), FP8 E4M3 / E5M2 ("Quantizing
+// the KV cache", FP8 KV cache with per-head scales) and the bfloat16 cache:
+// every new token is encoded on arrival into the page that holds it. Value
+// codes are channel-major inside a page; SYM_TOKEN codes narrower than a byte
+// update a partially filled page with read-modify-write of the words that
+// carry the new tokens' fields (each word owned by one thread), byte-aligned
+// codes are stored whole.
 //
 // All encoding arithmetic is fp32 with IEEE division and rintf (ties to
 // even); the library is compiled with -ffp-contract=off so no FMA is formed.
@@ -254,9 +256,10 @@ __global__ __launch_bounds__(64) void ring_write_kernel(AppendParams p, int64_t 
   }
 }
 
-// ---- SYM_TOKEN / FP8_E4M3: encode the new tokens of one page per block ------
-// grid = (pages touched, kv_heads, batch)
-template <int SCHEME, int D, int BITS, int IB>
+// ---- SYM_TOKEN: encode the new tokens of one page per block -------------------
+// grid = (pages touched, kv_heads, batch). Codes narrower than a byte share
+// 32-bit words across tokens, so the page's new rows are staged in LDS first.
+template <int D, int BITS, int IB>
 __global__ __launch_bounds__(kThreads) void token_append_kernel(AppendParams p) {
   constexpr int LD = D + 1;
   constexpr int FPW = 32 / BITS;
@@ -305,38 +308,20 @@ __global__ __launch_bounds__(kThreads) void token_append_kernel(AppendParams p) 
   }
   __syncthreads();
 
-  if constexpr (SCHEME == KVQ_SYM_TOKEN) {
-    // one scale per (token, head) for K and for V: s = max|x| / Q
-    for (int i = tid; i < 2 * kPage; i += kThreads) {
-      const int which = i / kPage, r = i % kPage;
-      if (r < lo || r >= hi) continue;
-      const float* row = (which ? vtile : ktile) + r * LD;
-      float a = fabsf(row[0]);
-      for (int c = 1; c < D; ++c) a = fmaxf(a, fabsf(row[c]));
-      const float s = a / kQmax;
-      (which ? v_sc : k_sc)[r] = s;
-      reinterpret_cast<float*>(pg + (which ? p.off_vs : p.off_ks))[r] = s;
-    }
-  } else if constexpr (is_fp8(SCHEME)) {
-    if (tid < kPage) {
-      k_sc[tid] = p.k_scale[h];
-      v_sc[tid] = p.v_scale[h];
-    }
+  // one scale per (token, head) for K and for V: s = max|x| / Q
+  for (int i = tid; i < 2 * kPage; i += kThreads) {
+    const int which = i / kPage, r = i % kPage;
+    if (r < lo || r >= hi) continue;
+    const float* row = (which ? vtile : ktile) + r * LD;
+    float a = fabsf(row[0]);
+    for (int c = 1; c < D; ++c) a = fmaxf(a, fabsf(row[c]));
+    const float s = a / kQmax;
+    (which ? v_sc : k_sc)[r] = s;
+    reinterpret_cast<float*>(pg + (which ? p.off_vs : p.off_ks))[r] = s;
   }
   __syncthreads();
 
-  auto encode = [&](float x, float s) -> uint32_t {
-    if constexpr (SCHEME == KVQ_SYM_TOKEN) {
-      return quant_sym(x, s, kQmax, kMask);
-    } else if constexpr (SCHEME == KVQ_FP8_E4M3) {
-      return e4m3_encode(x / s);
-    } else if constexpr (SCHEME == KVQ_FP8_E5M2) {
-      return e5m2_encode(x / s);
-    } else {
-      (void)s;
-      return bf16_bits_rne(x);
-    }
-  };
+  auto encode = [&](float x, float s) -> uint32_t { return quant_sym(x, s, kQmax, kMask); };
 
   // K rows of the new tokens: whole words
   constexpr int ROW_WORDS = D * BITS / 32;
@@ -370,6 +355,165 @@ __global__ __launch_bounds__(kThreads) void token_append_kernel(AppendParams p) 
   }
 }
 
+// ---- FP8 (either format) and bfloat16 pages: byte-aligned codes ------------
+// Every code is a whole byte (FP8) or a whole 16-bit word (bfloat16), so no
+// token shares a word with another's field and no LDS staging or
+// read-modify-write is needed: a thread takes a 4-token x 16-byte-chunk tile
+// of the K rows and another of the V rows, issues its eight loads together,
+// encodes, and stores K codes as row pieces and V codes as 4-token pieces of
+// each channel's column. Lanes of the K tile run along a row (chunk fastest),
+// lanes of the V tile along the tokens (token quad fastest), so both loads
+// and stores touch whole 128-byte lines. FP8 quotients come from
+// the scale's reciprocal, with IEEE division only where the product could
+// round to another code, and the codes from the hardware conversion (clamped
+// so it saturates). grid.x covers (pages of this launch) x (8 * CH tiles per
+// page) flat, so that neighbouring blocks write neighbouring pages of one
+// slab; grid y, z = KV head, sequence. Tokens outside [past, past + n) of a
+// page are neither read nor written.
+template <int SCHEME, int D, int IB>
+__global__ __launch_bounds__(kThreads) void byte_append_kernel(AppendParams p, int64_t pages) {
+  constexpr int CB = SCHEME == KVQ_BF16_CACHE ? 2 : 1;   // bytes per code
+  constexpr int CH = D * IB / 16;                          // 16-byte chunks per input row
+  constexpr int EPC = 16 / IB;                             // elements per chunk
+  constexpr int TPU = 8 * CH;                              // tiles per page
+  const int64_t gtask = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (gtask >= pages * TPU) return;
+  const int task = static_cast<int>(gtask % TPU);
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t page = p.first_page + gtask / TPU;
+  const int64_t end = p.past + p.n;
+  const int lo = static_cast<int>((p.past > page * kPage ? p.past : page * kPage) - page * kPage);
+  const int hi = static_cast<int>((end < page * kPage + kPage ? end : page * kPage + kPage) -
+                                  page * kPage);
+  uint8_t* pg = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes +
+                page * p.page_bytes;
+  constexpr int64_t ROW = static_cast<int64_t>(D) * IB;
+  const int64_t row_stride = static_cast<int64_t>(p.kv_heads) * ROW;
+  // input row of page token r (valid only for lo <= r < hi)
+  const int64_t row0 = (static_cast<int64_t>(b) * p.n + page * kPage - p.past) * row_stride +
+                       static_cast<int64_t>(h) * ROW;
+
+  const int kq = task / CH, kc = task % CH;   // K tile: tokens 4kq.., chunk kc
+  const int vc = task / 8, vq = task % 8;     // V tile: chunk vc, tokens 4vq..
+  uint4 kin[4], vin[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rk = 4 * kq + i, rv = 4 * vq + i;
+    kin[i] = rk >= lo && rk < hi
+                 ? *reinterpret_cast<const uint4*>(p.k_new + row0 + rk * row_stride + kc * 16)
+                 : make_uint4(0, 0, 0, 0);
+    vin[i] = rv >= lo && rv < hi
+                 ? *reinterpret_cast<const uint4*>(p.v_new + row0 + rv * row_stride + vc * 16)
+                 : make_uint4(0, 0, 0, 0);
+  }
+
+  auto widen = [](const uint4& v, float (&f)[EPC]) {
+    if constexpr (IB == 2) {
+      unpack_bf16x8(v, f);
+    } else {
+      f[0] = __uint_as_float(v.x);
+      f[1] = __uint_as_float(v.y);
+      f[2] = __uint_as_float(v.z);
+      f[3] = __uint_as_float(v.w);
+    }
+  };
+  // FP8: quotients by the per-head scale (the reciprocal with an exact
+  // fallback), then the hardware conversion, two codes per instruction
+  float ks = 1.0f, vs = 1.0f, kr = 1.0f, vr = 1.0f;
+  bool exact = false;
+  if constexpr (SCHEME != KVQ_BF16_CACHE) {
+    ks = p.k_scale[h];
+    vs = p.v_scale[h];
+    kr = 1.0f / ks;
+    vr = 1.0f / vs;
+    exact = !(recip_usable(kr) && recip_usable(vr));
+  }
+  constexpr bool E5 = SCHEME == KVQ_FP8_E5M2;
+
+  // K rows: EPC codes of one token row per store
+  uint8_t* kdst = pg + p.off_kc + kc * EPC * CB;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * kq + i;
+    if (r < lo || r >= hi) continue;
+    float f[EPC];
+    widen(kin[i], f);
+    uint32_t w[EPC * CB / 4];
+    if constexpr (CB == 1) {
+      fp8_quotients<E5>(f, ks, kr, exact);
+#pragma unroll
+      for (int e = 0; e < EPC / 4; ++e)
+        w[e] = fp8x2_encode<E5, true>(f[4 * e + 2], f[4 * e + 3],
+                                      fp8x2_encode<E5, false>(f[4 * e], f[4 * e + 1], 0));
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPC / 2; ++e)
+        w[e] = bf16_bits_rne(f[2 * e]) | (bf16_bits_rne(f[2 * e + 1]) << 16);
+    }
+    uint8_t* dst = kdst + static_cast<int64_t>(r) * D * CB;
+    if constexpr (EPC * CB == 16) {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else if constexpr (EPC * CB == 8) {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+    } else {
+      *reinterpret_cast<uint32_t*>(dst) = w[0];
+    }
+  }
+
+  // V cols: codes of tokens 4vq..4vq+3 of each of the chunk's channels
+  float fv[4][EPC];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    widen(vin[i], fv[i]);
+    if constexpr (CB == 1) fp8_quotients<E5>(fv[i], vs, vr, exact);
+  }
+  if constexpr (CB == 1) {
+    // one dword of 4 token codes per channel; 4x4 transposes across the lane
+    // quad that holds tokens 16m..16m+15 (vq = 4m + j, j = lane & 3) leave
+    // lane j with channel 4t + j's 16 codes in dw[4t..4t+3], so the quad's
+    // stores cover four whole 32-byte columns, 128 contiguous bytes
+    uint32_t dw[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e)
+      dw[e] = fp8x2_encode<E5, true>(fv[2][e], fv[3][e], fp8x2_encode<E5, false>(fv[0][e], fv[1][e], 0));
+    const int j = vq & 3, m = vq >> 2;
+#pragma unroll
+    for (int t = 0; t < EPC / 4; ++t) {
+      uint32_t blk[4] = {dw[4 * t], dw[4 * t + 1], dw[4 * t + 2], dw[4 * t + 3]};
+      quad_transpose(blk, j);
+      uint8_t* dst = pg + p.off_vc + static_cast<int64_t>(vc * EPC + 4 * t + j) * kPage + 16 * m;
+      if (16 * m >= lo && 16 * m + 16 <= hi) {
+        *reinterpret_cast<uint4*>(dst) = make_uint4(blk[0], blk[1], blk[2], blk[3]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = 16 * m + i;
+          if (r >= lo && r < hi) dst[i] = static_cast<uint8_t>(blk[i / 4] >> (8 * (i % 4)));
+        }
+      }
+    }
+  } else {
+    const bool whole = 4 * vq >= lo && 4 * vq + 4 <= hi;
+    uint8_t* vdst = pg + p.off_vc + static_cast<int64_t>(vc) * EPC * kPage * CB + 4 * vq * CB;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      const uint32_t w0 = bf16_bits_rne(fv[0][e]) | (bf16_bits_rne(fv[1][e]) << 16);
+      const uint32_t w1 = bf16_bits_rne(fv[2][e]) | (bf16_bits_rne(fv[3][e]) << 16);
+      uint8_t* dst = vdst + e * kPage * CB;
+      if (whole) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * vq + i;
+          if (r >= lo && r < hi)
+            reinterpret_cast<uint16_t*>(dst)[i] = static_cast<uint16_t>((i < 2 ? w0 : w1) >> (16 * (i & 1)));
+        }
+      }
+    }
+  }
+}
+
 // ---- dispatch ---------------------------------------------------------------
 
 template <int D, int BITS, int IB>
@@ -398,8 +542,15 @@ hipError_t run_token(const AppendArgs& a, const AppendParams& base, hipStream_t 
   AppendParams p = base;
   p.first_page = a.past / kPage;
   const int64_t last = (a.past + a.n - 1) / kPage;
-  dim3 grid(static_cast<unsigned>(last - p.first_page + 1), g.kv_heads, g.batch);
-  hipLaunchKernelGGL((token_append_kernel<SCHEME, D, BITS, IB>), grid, dim3(kThreads), 0, st, p);
+  const int64_t pages = last - p.first_page + 1;
+  if constexpr (SCHEME == KVQ_SYM_TOKEN) {
+    dim3 grid(static_cast<unsigned>(pages), g.kv_heads, g.batch);
+    hipLaunchKernelGGL((token_append_kernel<D, BITS, IB>), grid, dim3(kThreads), 0, st, p);
+  } else {
+    constexpr int64_t TPU = 8 * (D * IB / 16);
+    dim3 grid(static_cast<unsigned>((pages * TPU + kThreads - 1) / kThreads), g.kv_heads, g.batch);
+    hipLaunchKernelGGL((byte_append_kernel<SCHEME, D, IB>), grid, dim3(kThreads), 0, st, p, pages);
+  }
   return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
 // Device helpers shared by the kernels: dtype conversion, the exact
-// quantisers, FP8 E4M3FN conversion and wavefront reductions (wave64).
+// quantisers, FP8 (E4M3FN, E5M2) conversion and wavefront reductions (wave64).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -59,48 +59,100 @@ __device__ __forceinline__ uint32_t quant_sym(float x, float s, float qmax, uint
   return static_cast<uint32_t>(static_cast<int32_t>(r)) & mask;
 }
 
-// fp32 -> OCP E4M3FN, nearest with ties to even mantissa, saturating at 448,
-// sign kept. Normal results round the fp32 significand to 3 bits with integer
-// arithmetic; below 2^-6 the grid is uniform with step 2^-9.
-__device__ __forceinline__ uint32_t e4m3_encode(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-  const float a = fabsf(y);
-  uint32_t mag;
-  if (a >= 448.0f) {
-    mag = 0x7Eu;
-  } else if (a < 0.015625f) {
-    mag = static_cast<uint32_t>(rintf(a * 512.0f));  // exact scaling, 0..8
-  } else {
-    uint32_t b = __float_as_uint(a);
-    b += 0x7FFFFu + ((b >> 20) & 1u);                 // round to 3 mantissa bits, ties even
-    mag = (b >> 20) - (120u << 3);                    // exponent bias 127 -> 7
-  }
-  return sign | mag;
-}
-
 // fp32 -> bfloat16 bits, nearest with ties to even (finite inputs).
 __device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
   const uint32_t b = __float_as_uint(x);
   return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
 }
 
-// fp32 -> OCP E5M2, nearest with ties to even mantissa, saturating at 57344
-// (the largest finite value), sign kept. Normal results round the fp32
-// significand to 2 bits; below 2^-14 the grid is uniform with step 2^-16.
-__device__ __forceinline__ uint32_t e5m2_encode(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-  const float a = fabsf(y);
-  uint32_t mag;
-  if (a >= 57344.0f) {
-    mag = 0x7Bu;
-  } else if (a < 6.103515625e-05f) {
-    mag = static_cast<uint32_t>(rintf(a * 65536.0f));   // exact scaling, 0..4
-  } else {
-    uint32_t b = __float_as_uint(a);
-    b += 0xFFFFFu + ((b >> 21) & 1u);                 // round to 2 mantissa bits, ties even
-    mag = (b >> 21) - (112u << 2);                    // exponent bias 127 -> 15
+// ---- FP8 codes of x / s through a reciprocal ---------------------------------
+// With r = RN(1/s) a normal float, q = RN(x * r) differs from RN(x / s) by at
+// most 2 units in the last place of q (two roundings of relative size 2^-24
+// each, plus half a unit for RN(x / s)), so both round to the same FP8 number
+// unless q lies within a few units of a point where FP8 rounding flips: the
+// midpoint between two neighbouring FP8 numbers. In the FP8 normal range
+// those are the floats whose bits below the FP8 mantissa (20 for E4M3, 21 for
+// E5M2) equal one half; below the FP8 normal range the check takes every
+// value above a quarter of the smallest subnormal (anything smaller is a
+// signed zero either way). Flagged lanes take the IEEE division.
+template <bool E5>
+__device__ __forceinline__ bool fp8_needs_division(float q) {
+  constexpr int DROP = E5 ? 21 : 20;
+  constexpr uint32_t HALF = 1u << (DROP - 1);
+  constexpr float NORM_MIN = E5 ? 6.103515625e-05f : 0.015625f;        // 2^-14, 2^-6
+  constexpr float ZERO_MAX = E5 ? 3.814697265625e-06f : 4.8828125e-04f;  // 2^-18, 2^-11
+  const float a = fabsf(q);
+  const uint32_t low = __float_as_uint(q) & ((1u << DROP) - 1u);
+  return (low - (HALF - 4u)) <= 8u || (a < NORM_MIN && a > ZERO_MAX);
+}
+
+// True when 1/s is a normal float (the bound above needs a full-precision r).
+__device__ __forceinline__ bool recip_usable(float r) {
+  const float a = fabsf(r);
+  return a >= 1.17549435e-38f && a <= 3.40282347e38f;
+}
+
+// x[i] <- RN(x[i] / s), or a float with the same FP8 code. exact forces the
+// division for every element (a reciprocal that is not usable).
+template <bool E5, int N>
+__device__ __forceinline__ void fp8_quotients(float (&x)[N], float s, float r, bool exact) {
+  float q[N];
+  bool any = exact;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    q[i] = x[i] * r;
+    any |= fp8_needs_division<E5>(q[i]);
   }
-  return sign | mag;
+  if (any) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (exact || fp8_needs_division<E5>(q[i])) q[i] = x[i] / s;
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = q[i];
+}
+
+// Two fp32 -> two FP8 codes in the low (HI false) or high (HI true) 16 bits of
+// the result, the other half taken from old: the hardware conversion rounds to
+// nearest with ties to even; clamping to the largest finite magnitude first
+// makes it saturate (every value beyond it is nearest to it or would round
+// past it), as the FP8 cache encoding does.
+template <bool E5, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_encode(float a, float b, uint32_t old) {
+  constexpr float FMAX = E5 ? 57344.0f : 448.0f;
+  a = __builtin_amdgcn_fmed3f(a, -FMAX, FMAX);
+  b = __builtin_amdgcn_fmed3f(b, -FMAX, FMAX);
+  if constexpr (E5) {
+    return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_bf8_f32(a, b, static_cast<int>(old), HI));
+  } else {
+    return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, static_cast<int>(old), HI));
+  }
+}
+
+// Transposes a 4x4 dword matrix held one row per lane by the four lanes of a
+// quad (j = lane & 3): afterwards lane j holds column j, a[i] = old row i of
+// lane i. Two butterfly stages (partner lane j^2, then j^1) over DPP quad
+// permutations; in each stage a lane keeps the entries whose column agrees
+// with its own lane bit and swaps the others with its partner. Every lane of
+// the quad must be active.
+template <int K>
+__device__ __forceinline__ void quad_transpose_stage(uint32_t (&a)[4], int j) {
+  constexpr int kCtrl = K == 2 ? 0x4E : 0xB1;   // quad_perm [2,3,0,1] or [1,0,3,2]
+  const bool hb = (j & K) != 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (c & K) continue;
+    const uint32_t send = hb ? a[c] : a[c ^ K];
+    const uint32_t recv = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(send), kCtrl, 0xF, 0xF, false));
+    a[c] = hb ? recv : a[c];
+    a[c ^ K] = hb ? a[c ^ K] : recv;
+  }
+}
+
+__device__ __forceinline__ void quad_transpose(uint32_t (&a)[4], int j) {
+  quad_transpose_stage<2>(a, j);
+  quad_transpose_stage<1>(a, j);
 }
 
 // OCP E5M2 byte -> fp32 (finite codes).

@@ -108,6 +108,65 @@ def test_append_fp8_e5m2_bytes(d, shrink, chunking):
     H.compare_bytes(cache.cpu().numpy(), want, mask, f"e5m2 d{d} x{shrink} {chunking}")
 
 
+def fp8_grid(e5):
+    """Non-negative finite magnitudes of the FP8 format, from its definition:
+    subnormals m * 2^(1 - bias - M), normals (1 + m / 2^M) * 2^(e - bias)."""
+    M, bias, emax = (2, 15, 30) if e5 else (3, 7, 15)
+    vals = [m * 2.0 ** (1 - bias - M) for m in range(2 ** M)]
+    for e in range(1, emax + 1):
+        for m in range(2 ** M):
+            if not e5 and e == emax and m == 2 ** M - 1:
+                continue                              # E4M3FN: S.1111.111 is NaN
+            vals.append((1 + m / 2 ** M) * 2.0 ** (e - bias))
+    return np.array(vals)
+
+
+def rounding_edges(e5, scale):
+    """Float32 inputs whose quotients by `scale` sit on or a few units around
+    every FP8 number and every midpoint between neighbours, past the largest
+    finite number, around the subnormal boundaries and at signed zeros."""
+    g = fp8_grid(e5)
+    mids = (g[:-1] + g[1:]) / 2
+    top = g[-1]
+    extra = [top * 1.0001, (top + (g[-1] - g[-2]) / 2), top * 1.5, top * 2, 1e30, 3e38,
+             g[1] / 2, g[1] / 4, g[1] / 4 * 1.001, 1e-40, 1e-45]
+    centres = np.float32(np.concatenate([g, mids, extra]) * scale)
+    out = [centres]
+    for k in (1, 2, 3, 4, 5, 8):
+        up, down = centres.copy(), centres.copy()
+        for _ in range(k):
+            up = np.nextafter(up, np.float32(np.inf))
+            down = np.nextafter(down, np.float32(0))
+        out += [up, down]
+    x = np.concatenate(out)
+    return np.concatenate([x, -x, np.float32([0.0, -0.0])]).astype(np.float32)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.3, 7.1e-3])
+@pytest.mark.parametrize("scheme", [synth.FP8_E4M3, synth.FP8_E5M2])
+def test_append_fp8_rounding_edges(scheme, scale):
+    """Codes of values on and next to every FP8 rounding boundary (exact ties
+    at scale 1; quotients a few units from a midpoint at the other scales,
+    where the reciprocal product has to give way to the division) equal the
+    oracle's nearest-even, saturating codes, in K rows and in V columns."""
+    x = rounding_edges(scheme == synth.FP8_E5M2, scale)
+    d = 128
+    T = -(-x.size // d)
+    flat = np.zeros(T * d, np.float32)
+    flat[:x.size] = x
+    w = small(scheme, 8, d, torch.float32, B=1, Hkv=1, hg=1, T=T)
+    cfg = H.config(w, T)
+    cache = kvq.alloc_cache(cfg)
+    oc = H.oracle_cache(w, T)
+    k = torch.from_numpy(flat.reshape(1, T, 1, d)).to(DEV)
+    v = torch.from_numpy(np.roll(flat, 37).reshape(1, T, 1, d)).to(DEV)   # other positions
+    ks = torch.full((1,), scale, dtype=torch.float32, device=DEV)
+    H.append_chunks(cfg, cache, k, v, [5, T - 5], ks=ks, vs=ks, oc=oc)
+    torch.cuda.synchronize()
+    want, mask = oc.cache_image()
+    H.compare_bytes(cache.cpu().numpy(), want, mask, f"fp8 edges scheme {scheme} scale {scale}")
+
+
 def test_append_special_values():
     """Constant groups (s = 0), signed zeros and exact ties."""
     w = small(synth.KIVI, 2, 32, torch.float32, R=0, T=96)
