@@ -363,10 +363,10 @@ __global__ __launch_bounds__(kThreads) void token_append_kernel(AppendParams p) 
 // encodes, and stores K codes as row pieces and V codes as 4-token pieces of
 // each channel's column. Lanes of the K tile run along a row (chunk fastest),
 // lanes of the V tile along the tokens (token quad fastest), so both loads
-// and stores touch whole 128-byte lines. FP8 quotients come from
-// the scale's reciprocal, with IEEE division only where the product could
-// round to another code, and the codes from the hardware conversion (clamped
-// so it saturates). grid.x covers (pages of this launch) x (8 * CH tiles per
+// and stores touch whole 128-byte lines. FP8 quotients are the correctly
+// rounded x / s, computed from the scale's reciprocal with two FMA
+// corrections, and the codes come from the hardware conversion (clamped so
+// it saturates). grid.x covers (pages of this launch) x (8 * CH tiles per
 // page) flat, so that neighbouring blocks write neighbouring pages of one
 // slab; grid y, z = KV head, sequence. Tokens outside [past, past + n) of a
 // page are neither read nor written.
@@ -417,8 +417,9 @@ __global__ __launch_bounds__(kThreads) void byte_append_kernel(AppendParams p, i
       f[3] = __uint_as_float(v.w);
     }
   };
-  // FP8: quotients by the per-head scale (the reciprocal with an exact
-  // fallback), then the hardware conversion, two codes per instruction
+  // FP8: quotients by the per-head scale (correctly rounded from the
+  // reciprocal, the IEEE division when it is out of range), then the hardware
+  // conversion, two codes per instruction
   float ks = 1.0f, vs = 1.0f, kr = 1.0f, vr = 1.0f;
   bool exact = false;
   if constexpr (SCHEME != KVQ_BF16_CACHE) {
@@ -440,7 +441,7 @@ __global__ __launch_bounds__(kThreads) void byte_append_kernel(AppendParams p, i
     widen(kin[i], f);
     uint32_t w[EPC * CB / 4];
     if constexpr (CB == 1) {
-      fp8_quotients<E5>(f, ks, kr, exact);
+      fp8_quotients(f, ks, kr, exact);
 #pragma unroll
       for (int e = 0; e < EPC / 4; ++e)
         w[e] = fp8x2_encode<E5, true>(f[4 * e + 2], f[4 * e + 3],
@@ -465,7 +466,7 @@ __global__ __launch_bounds__(kThreads) void byte_append_kernel(AppendParams p, i
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     widen(vin[i], fv[i]);
-    if constexpr (CB == 1) fp8_quotients<E5>(fv[i], vs, vr, exact);
+    if constexpr (CB == 1) fp8_quotients(fv[i], vs, vr, exact);
   }
   if constexpr (CB == 1) {
     // one dword of 4 token codes per channel; 4x4 transposes across the lane

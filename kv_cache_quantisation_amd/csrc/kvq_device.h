@@ -65,51 +65,39 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
   return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
 }
 
-// ---- FP8 codes of x / s through a reciprocal ---------------------------------
-// With r = RN(1/s) a normal float, q = RN(x * r) differs from RN(x / s) by at
-// most 2 units in the last place of q (two roundings of relative size 2^-24
-// each, plus half a unit for RN(x / s)), so both round to the same FP8 number
-// unless q lies within a few units of a point where FP8 rounding flips: the
-// midpoint between two neighbouring FP8 numbers. In the FP8 normal range
-// those are the floats whose bits below the FP8 mantissa (20 for E4M3, 21 for
-// E5M2) equal one half; below the FP8 normal range the check takes every
-// value above a quarter of the smallest subnormal (anything smaller is a
-// signed zero either way). Flagged lanes take the IEEE division.
-template <bool E5>
-__device__ __forceinline__ bool fp8_needs_division(float q) {
-  constexpr int DROP = E5 ? 21 : 20;
-  constexpr uint32_t HALF = 1u << (DROP - 1);
-  constexpr float NORM_MIN = E5 ? 6.103515625e-05f : 0.015625f;        // 2^-14, 2^-6
-  constexpr float ZERO_MAX = E5 ? 3.814697265625e-06f : 4.8828125e-04f;  // 2^-18, 2^-11
-  const float a = fabsf(q);
-  const uint32_t low = __float_as_uint(q) & ((1u << DROP) - 1u);
-  return (low - (HALF - 4u)) <= 8u || (a < NORM_MIN && a > ZERO_MAX);
-}
-
-// True when 1/s is a normal float (the bound above needs a full-precision r).
+// ---- x / s correctly rounded from a reciprocal --------------------------------
+// With r = RN(1/s), q0 = RN(x * r) is within 2 units in the last place of x / s.
+// One correction q1 = RN(q0 + RN(x - s * q0) * r) (the residual by FMA)
+// brings it within one unit, and a second gives RN(x / s) exactly: that is
+// Markstein's theorem (radix 2, round to nearest: a reciprocal correctly
+// rounded and a quotient within one unit make one such step correctly
+// rounded). The steps need no overflow or underflow: callers use it only with
+// 2^-60 <= |r| <= 2^60, and quotients outside [2^-100, 2^100) keep q0, whose
+// FP8 code (a signed zero or the saturated maximum) is the same as that of
+// RN(x / s).
 __device__ __forceinline__ bool recip_usable(float r) {
   const float a = fabsf(r);
-  return a >= 1.17549435e-38f && a <= 3.40282347e38f;
+  return a >= 0x1p-60f && a <= 0x1p60f;
 }
 
-// x[i] <- RN(x[i] / s), or a float with the same FP8 code. exact forces the
-// division for every element (a reciprocal that is not usable).
-template <bool E5, int N>
+__device__ __forceinline__ float div_by_recip(float x, float s, float r) {
+  const float q0 = x * r;
+  float q = __builtin_fmaf(__builtin_fmaf(-q0, s, x), r, q0);
+  q = __builtin_fmaf(__builtin_fmaf(-q, s, x), r, q);
+  const float a = fabsf(q0);
+  return a >= 0x1p-100f && a < 0x1p100f ? q : q0;
+}
+
+// x[i] <- RN(x[i] / s); exact (a reciprocal out of range) takes the division.
+template <int N>
 __device__ __forceinline__ void fp8_quotients(float (&x)[N], float s, float r, bool exact) {
-  float q[N];
-  bool any = exact;
+  if (exact) {
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    q[i] = x[i] * r;
-    any |= fp8_needs_division<E5>(q[i]);
+    for (int i = 0; i < N; ++i) x[i] = x[i] / s;
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = div_by_recip(x[i], s, r);
   }
-  if (any) {
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-      if (exact || fp8_needs_division<E5>(q[i])) q[i] = x[i] / s;
-  }
-#pragma unroll
-  for (int i = 0; i < N; ++i) x[i] = q[i];
 }
 
 // Two fp32 -> two FP8 codes in the low (HI false) or high (HI true) 16 bits of
