@@ -53,9 +53,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 # kernel sources they were taken with (SHA-256 over DECODE_SOURCES); after any
 # change to those, `traffic` is reported as null until they are taken again.
 COUNTERS = {
-    "kivi2": {"context": 4119, "fetch_kib": 31908.75, "write_kib": 2156.0,
+    "kivi2": {"context": 4119, "fetch_kib": 31912.46875, "write_kib": 2156.0,
               "fetch_scale": 262144 / 131084, "write_scale": 1.0,
-              "sources_sha256": "b682e1836ff358e4ee590e879749c523a105ed6872a03efffdded22b37fa6381"},
+              "sources_sha256": "e6832348538bef1ea885958567873a169cb5b7bc312993b64b7dd94b2733949a"},
 }
 DECODE_SOURCES = ["decode_mfma.hip", "kvq_device.h", "kvq_internal.h"]
 
@@ -112,6 +112,8 @@ def token_bytes(w):
     d, b = w.head_dim, w.bits
     if w.scheme == synth.SYM_TOKEN:
         return 2 * (d * b // 8 + 4)
+    if w.scheme == synth.BF16_CACHE:
+        return 4 * d
     return 2 * d   # FP8: one byte per value, per-head scales are arguments
 
 
