@@ -83,9 +83,16 @@ def kivi_q(T, R):
     return 32 * (max(0, T - R) // 32)
 
 
+def kivi_page_bytes(w):
+    """Bytes of one KIVI page: key codes, value codes (v_bits when set), fp32
+    scale and offset per key channel and per value token."""
+    vb = w.v_bits or w.bits
+    return 32 * w.head_dim * (w.bits + vb) // 8 + 8 * w.head_dim + 256
+
+
 def decode_bytes(w, T, in_bytes=2, q_bytes=2):
     """Algorithmic bytes of one decode call over T tokens (all sequences/heads)."""
-    page = 2 * 32 * w.head_dim * w.bits // 8 + 8 * w.head_dim + 256
+    page = kivi_page_bytes(w)
     q = kivi_q(T, w.residual)
     per_unit = (q // 32) * page + (T - q) * 2 * w.head_dim * in_bytes
     hg = w.q_heads // w.kv_heads
@@ -96,7 +103,7 @@ def decode_bytes(w, T, in_bytes=2, q_bytes=2):
 def append_bytes(w, T_old, n, in_bytes=2):
     """Algorithmic bytes of appending n tokens to a T_old-token KIVI cache."""
     d, R = w.head_dim, w.residual
-    page = 2 * 32 * d * w.bits // 8 + 8 * d + 256
+    page = kivi_page_bytes(w)
     q0, q1 = kivi_q(T_old, R), kivi_q(T_old + n, R)
     row = 2 * d * in_bytes                         # one K row + one V row
     rd = n * row                                   # new tokens
@@ -176,6 +183,7 @@ def workload_kernels(name, reps=5):
     T = w.tokens
     dt = {torch.bfloat16: kvq.KVQ_BF16, torch.float32: kvq.KVQ_F32}
     cfg = kvq.make_config(w.scheme, w.bits, 1, w.q_heads, w.kv_heads, w.head_dim, w.batch, T + 1,
+                          v_bits=w.v_bits,
                           residual=w.residual, in_dtype=dt[w.in_dtype], q_dtype=dt[w.q_dtype],
                           rope_theta=w.rope_theta)
     cache = kvq.alloc_cache(cfg, device=dev, zero=False)
@@ -219,6 +227,7 @@ def workload_kernels(name, reps=5):
                 "decode_speedup_vs_bf16_cache": round(bus / dec_us, 2)}
     return {
         "workload": name, "batch": w.batch, "context": T, "bits": w.bits,
+        "v_bits": w.v_bits or w.bits,
         "prefill_us": round(pre_us, 2), "prefill_gbs": round(pre_b / pre_us / 1e3, 1),
         "prefill_tokens_per_s": round(w.batch * T / (pre_us * 1e-6)),
         "append1_us": round(app_us, 2), "append1_gbs": round(app_b / app_us / 1e3, 1),

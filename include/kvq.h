@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 1
+#define KVQ_ABI_VERSION 2
 
 /* Exported entry points (the library is built with hidden visibility). */
 #if defined(__GNUC__)
@@ -111,7 +111,8 @@ typedef struct kvq_config {
   uint32_t struct_size;  /* = sizeof(kvq_config)                            */
   int32_t  scheme;       /* KVQ_KIVI / KVQ_SYM_TOKEN / KVQ_FP8_E4M3 /
                             KVQ_FP8_E5M2 / KVQ_BF16_CACHE                   */
-  int32_t  bits;         /* 2, 4 or 8 (8 for FP8, 16 for BF16_CACHE)        */
+  int32_t  bits;         /* 2, 4 or 8 (8 for FP8, 16 for BF16_CACHE); for
+                            KIVI the bits of the key codes (see v_bits)     */
   int32_t  layers;       /* >= 1                                            */
   int32_t  q_heads;      /* kv_heads * {1, 2, 4, 8}                        */
   int32_t  kv_heads;     /* 1..65535                                        */
@@ -130,6 +131,13 @@ typedef struct kvq_config {
   float    sm_scale;     /* softmax scale; 0 selects 1/sqrt(head_dim)       */
   int32_t  num_splits;   /* decode token splits per (seq, KV head);
                             0 = automatic, else an upper bound              */
+  int32_t  v_bits;       /* KIVI: bits of the value codes, 2, 4 or 8 and at
+                            most `bits` (keys take the wider codes: a few
+                            key channels carry large values, and rounding
+                            costs keys more than values, [QKV] "How the KV
+                            cache is quantized", INT8 / INT4 blocks with
+                            separate key and value cache types); 0 = `bits`.
+                            Other schemes: 0 or equal to `bits`.          */
 } kvq_config;
 
 /* ==== Cache layout, version 1 =============================================
@@ -145,14 +153,16 @@ typedef struct kvq_config {
  *           codes contiguous (field index = channel).
  * "V cols": the page's d channels one after another, each channel's 32 token
  *           codes contiguous (field index = token).
- * d = head_dim, b = bits. All sizes below are multiples of 16 bytes and every
+ * d = head_dim, b = bits; KIVI keys take bk = bits and values bv = v_bits (or
+ * bits when v_bits is 0). All sizes below are multiples of 16 bytes and every
  * page size is a multiple of 256 bytes.
  *
- * KIVI page (8*d*b + 8*d + 256 bytes), P = floor(max(0, max_tokens-R)/32):
- *   Kc  K rows, unsigned codes     32*d*b/8 bytes
- *   Ks  fp32 scale per channel     4*d
- *   Kz  fp32 offset (group min)    4*d
- *   Vc  V cols, unsigned codes     32*d*b/8
+ * KIVI page (4*d*(bk+bv) + 8*d + 256 bytes; 8*d*b + 8*d + 256 when bk = bv
+ * = b), P = floor(max(0, max_tokens-R)/32):
+ *   Kc  K rows, unsigned bk-bit codes     32*d*bk/8 bytes
+ *   Ks  fp32 scale per channel            4*d
+ *   Kz  fp32 offset (group min)           4*d
+ *   Vc  V cols, unsigned bv-bit codes     32*d*bv/8
  *   Vs  fp32 scale per token       128
  *   Vz  fp32 offset per token      128
  *   Ring after the P pages: (R+32) K rows then (R+32) V rows, each d values of
@@ -178,8 +188,9 @@ typedef struct kvq_config {
  *   and going deeper (the newest R tokens kept in full precision); [KIVI] How
  *   It Works (residual length).
  * Encoding of one KIVI group (fp32 arithmetic, IEEE division, ties-to-even
- * rounding, no fused multiply-add), L = 2^b - 1, per key channel over the 32
- * tokens of the page and per value token over its d channels:
+ * rounding, no fused multiply-add), L = 2^bk - 1 for keys and 2^bv - 1 for
+ * values, per key channel over the 32 tokens of the page and per value token
+ * over its d channels:
  *   mn = min x (+0 replaces -0), mx = max x, s = (mx - mn) / L,
  *   code = s == 0 ? 0 : clamp(rint((x - mn) / s), 0, L),  stored offset = mn;
  *   dequantised value = code*s + mn.  [QKV] going deeper, Q_b and s.
@@ -197,7 +208,10 @@ typedef struct kvq_config {
 /* Bytes for `tokens` tokens per sequence. Host-only; never touches a device.
  *   KVQ_BYTES_FORMULA:   batch * 2*layers*kv_heads*head_dim*tokens*bits/8, the
  *                        KV-bytes equation of [QKV] "The other big memory
- *                        user" with scales ignored (as in [QC] Workshop).
+ *                        user" with scales ignored (as in [QC] Workshop);
+ *                        with KIVI value codes of v_bits, the keys' and the
+ *                        values' halves are counted at their own widths:
+ *                        batch*layers*kv_heads*head_dim*tokens*(bits+v_bits)/8.
  *   KVQ_BYTES_CACHE:     exact size of the layout above for capacity `tokens`
  *                        (all layers, all sequences).
  *   KVQ_BYTES_WORKSPACE: decode workspace needed by a call over `tokens`

@@ -65,10 +65,12 @@ __device__ __forceinline__ void stage_chunk(const uint4& v, float* dst, int chun
 // part in the statistics (several threads per key channel / value token,
 // combined with lane shuffles) and in the codes (one or more packed words per
 // thread), where each quotient comes from a reciprocal with an exact fallback.
-template <int D, int BITS, int IB>
+template <int D, int KB, int VB, int IB>
 __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
-  constexpr float kLevels = float((1 << BITS) - 1);
-  constexpr int FPW = 32 / BITS;              // fields per 32-bit word
+  constexpr float kLevelsK = float((1 << KB) - 1);   // key / value code levels
+  constexpr float kLevelsV = float((1 << VB) - 1);
+  constexpr int FPWK = 32 / KB;               // fields per 32-bit word
+  constexpr int FPWV = 32 / VB;
   constexpr int ROW = D * IB;                 // bytes per input row
   constexpr int PITCH = ROW + 16;             // padded LDS row
   constexpr int CHUNKS = ROW / 16;            // 16-byte chunks per row
@@ -145,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
     }
     if (c < D && part == 0) {
       mn = mn + 0.0f;                          // -0 -> +0
-      const float s = (mx - mn) / kLevels;
+      const float s = (mx - mn) / kLevelsK;
       k_mn[c] = mn;
       k_s[c] = s;
       k_r[c] = quant_rcp_prep(s);
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
     }
     if (part == 0) {
       mn = mn + 0.0f;
-      const float s = (mx - mn) / kLevels;
+      const float s = (mx - mn) / kLevelsV;
       v_mn[r] = mn;
       v_s[r] = s;
       v_r[r] = quant_rcp_prep(s);
@@ -182,12 +184,14 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
 
   // 3. codes. K rows: field f = token*D + channel. V cols: field f = channel*32 + token.
   //    Statistics and key elements of a word are read as vectors.
-  constexpr int WORDS = kPage * D * BITS / 32;
+  constexpr int WORDSK = kPage * D * KB / 32;
+  constexpr int WORDSV = kPage * D * VB / 32;
   uint32_t* kc = reinterpret_cast<uint32_t*>(pg + p.off_kc);
   uint32_t* vc = reinterpret_cast<uint32_t*>(pg + p.off_vc);
-  auto load4 = [](const float* src, float* dst) {   // FPW floats, 16-byte aligned
+  auto load4 = [](const float* src, auto& dst) {   // all of dst, 16-byte aligned src
+    constexpr int N = sizeof(dst) / sizeof(float);
 #pragma unroll
-    for (int i = 0; i < FPW / 4; ++i) {
+    for (int i = 0; i < N / 4; ++i) {
       const float4 v = reinterpret_cast<const float4*>(src)[i];
       dst[4 * i] = v.x;
       dst[4 * i + 1] = v.y;
@@ -195,15 +199,15 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
       dst[4 * i + 3] = v.w;
     }
   };
-  for (int w = tid; w < WORDS; w += kThreads) {
-    const int f0 = w * FPW;
+  for (int w = tid; w < WORDSK; w += kThreads) {
+    const int f0 = w * FPWK;
     const int t = f0 / D, c0 = f0 % D;
-    float x[FPW], mn[FPW], rc[FPW];
+    float x[FPWK], mn[FPWK], rc[FPWK];
     const uint8_t* row = tile[0] + t * PITCH + c0 * IB;
     if constexpr (IB == 2) {
-      if constexpr (FPW >= 8) {
+      if constexpr (FPWK >= 8) {
 #pragma unroll
-        for (int i = 0; i < FPW / 8; ++i) unpack_bf16x8(reinterpret_cast<const uint4*>(row)[i], x + 8 * i);
+        for (int i = 0; i < FPWK / 8; ++i) unpack_bf16x8(reinterpret_cast<const uint4*>(row)[i], x + 8 * i);
       } else {
         const uint2 v = *reinterpret_cast<const uint2*>(row);
         x[0] = __uint_as_float(v.x << 16);
@@ -218,20 +222,20 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
     load4(k_r + c0, rc);
     uint32_t word = 0;
 #pragma unroll
-    for (int j = 0; j < FPW; ++j)
-      word |= quant_asym_rcp(x[j], mn[j], k_s + c0 + j, rc[j], kLevels) << (j * BITS);
+    for (int j = 0; j < FPWK; ++j)
+      word |= quant_asym_rcp(x[j], mn[j], k_s + c0 + j, rc[j], kLevelsK) << (j * KB);
     kc[w] = word;
   }
-  for (int w = tid; w < WORDS; w += kThreads) {
-    const int f0 = w * FPW;
+  for (int w = tid; w < WORDSV; w += kThreads) {
+    const int f0 = w * FPWV;
     const int c = f0 / kPage, t0 = f0 % kPage;
-    float mn[FPW], rc[FPW];
+    float mn[FPWV], rc[FPWV];
     load4(v_mn + t0, mn);
     load4(v_r + t0, rc);
     uint32_t word = 0;
 #pragma unroll
-    for (int j = 0; j < FPW; ++j)
-      word |= quant_asym_rcp(elem(1, t0 + j, c), mn[j], v_s + t0 + j, rc[j], kLevels) << (j * BITS);
+    for (int j = 0; j < FPWV; ++j)
+      word |= quant_asym_rcp(elem(1, t0 + j, c), mn[j], v_s + t0 + j, rc[j], kLevelsV) << (j * VB);
     vc[w] = word;
   }
 }
@@ -517,7 +521,7 @@ __global__ __launch_bounds__(kThreads) void byte_append_kernel(AppendParams p, i
 
 // ---- dispatch ---------------------------------------------------------------
 
-template <int D, int BITS, int IB>
+template <int D, int KB, int VB, int IB>
 hipError_t run_kivi(const AppendArgs& a, const AppendParams& base, hipStream_t st) {
   const Geometry& g = a.g;
   const int64_t end = a.past + a.n;
@@ -527,7 +531,7 @@ hipError_t run_kivi(const AppendArgs& a, const AppendParams& base, hipStream_t s
   if (q_new > q_old) {
     p.first_page = q_old / kPage;
     dim3 grid(static_cast<unsigned>((q_new - q_old) / kPage), g.kv_heads, g.batch);
-    hipLaunchKernelGGL((kivi_flush_kernel<D, BITS, IB>), grid, dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((kivi_flush_kernel<D, KB, VB, IB>), grid, dim3(kThreads), 0, st, p);
   }
   const int64_t t0 = q_new > a.past ? q_new : a.past;
   if (end > t0) {
@@ -569,9 +573,11 @@ hipError_t dispatch_bits(const AppendArgs& a, const AppendParams& p, hipStream_t
     }
   }
   switch (g.bits) {
-    case 2: return run_kivi<D, 2, IB>(a, p, st);
-    case 4: return run_kivi<D, 4, IB>(a, p, st);
-    default: return run_kivi<D, 8, IB>(a, p, st);
+    case 2: return run_kivi<D, 2, 2, IB>(a, p, st);
+    case 4: return g.vbits == 2 ? run_kivi<D, 4, 2, IB>(a, p, st) : run_kivi<D, 4, 4, IB>(a, p, st);
+    default:
+      return g.vbits == 2 ? run_kivi<D, 8, 2, IB>(a, p, st)
+             : g.vbits == 4 ? run_kivi<D, 8, 4, IB>(a, p, st) : run_kivi<D, 8, 8, IB>(a, p, st);
   }
 }
 

@@ -91,14 +91,15 @@ __device__ __forceinline__ void rope_pair(float& x0, float& x1, int64_t pos, dou
   x1 = y1;
 }
 
-template <int SCHEME, int BITS, int D, int HG>
+template <int SCHEME, int BITS, int VB, int D, int HG>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
   constexpr int CPL = D >= 64 ? D / 64 : 1;  // channels per lane in the P.V phase
   constexpr int LPC = D / CPL;                // lanes per token subset (64 or 32)
   constexpr int TSUB = 64 / LPC;              // token subsets (1, or 2 when D == 32)
   constexpr int TPS = kPage / TSUB;           // tokens per subset
   constexpr int HALF = D / 2;                 // channels per lane in the score phase
-  constexpr int FPW = 32 / BITS;              // fields per 32-bit word
+  constexpr int FPW = 32 / BITS;              // key fields per 32-bit word
+  constexpr int FPWV = 32 / VB;               // value fields per 32-bit word (VB = value bits)
   constexpr int QROWS = HG > 2 ? HG : 2;
   constexpr int WQ = kWaves * QROWS * D;
   constexpr int RED = kWaves * HG * (D + 2);
@@ -288,8 +289,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     // ---- P.V: lane = (channel set, token subset) --------------------------------
     if (active) {
       if (is_page) {
-        constexpr int COLW = kPage * BITS / 32;   // words per channel column
-        constexpr int SUBW = TPS * BITS / 32;     // words per token subset
+        constexpr int COLW = kPage * VB / 32;     // words per channel column
+        constexpr int SUBW = TPS * VB / 32;       // words per token subset
 #pragma unroll
         for (int ci = 0; ci < CPL; ++ci) {
           const int c = cs * CPL + ci;
@@ -299,9 +300,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
           for (int wi = 0; wi < SUBW; ++wi) {
             const uint32_t w = vw[wi];
 #pragma unroll
-            for (int j = 0; j < FPW; ++j) {
-              const float cv = code_value<SCHEME, BITS>(w, j);
-              const int t = ts * TPS + wi * FPW + j;
+            for (int j = 0; j < FPWV; ++j) {
+              const float cv = code_value<SCHEME, VB>(w, j);
+              const int t = ts * TPS + wi * FPWV + j;
 #pragma unroll
               for (int g = 0; g < HG; ++g) o[g][ci] = fmaf(wp[wave][g][t], cv, o[g][ci]);
             }
@@ -394,10 +395,10 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* partials,
   }
 }
 
-template <int SCHEME, int BITS, int D, int HG>
+template <int SCHEME, int BITS, int VB, int D, int HG>
 hipError_t launch(const DecodeParams& p, int batch, hipStream_t st) {
   dim3 grid(p.splits, p.kv_heads, batch);
-  hipLaunchKernelGGL((decode_split_kernel<SCHEME, BITS, D, HG>), grid, dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL((decode_split_kernel<SCHEME, BITS, VB, D, HG>), grid, dim3(kThreads), 0, st, p);
   if (p.splits > 1) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -406,23 +407,24 @@ hipError_t launch(const DecodeParams& p, int batch, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int SCHEME, int BITS, int D>
+template <int SCHEME, int BITS, int VB, int D>
 hipError_t by_hg(const DecodeParams& p, int hg, int batch, hipStream_t st) {
   switch (hg) {
-    case 1: return launch<SCHEME, BITS, D, 1>(p, batch, st);
-    case 2: return launch<SCHEME, BITS, D, 2>(p, batch, st);
-    case 4: return launch<SCHEME, BITS, D, 4>(p, batch, st);
-    default: return launch<SCHEME, BITS, D, 8>(p, batch, st);
+    case 1: return launch<SCHEME, BITS, VB, D, 1>(p, batch, st);
+    case 2: return launch<SCHEME, BITS, VB, D, 2>(p, batch, st);
+    case 4: return launch<SCHEME, BITS, VB, D, 4>(p, batch, st);
+    default: return launch<SCHEME, BITS, VB, D, 8>(p, batch, st);
   }
 }
 
-template <int SCHEME, int BITS>
+// VB: bits of the value codes (KIVI may store values narrower than keys)
+template <int SCHEME, int BITS, int VB = BITS>
 hipError_t by_d(const DecodeParams& p, int d, int hg, int batch, hipStream_t st) {
   switch (d) {
-    case 32: return by_hg<SCHEME, BITS, 32>(p, hg, batch, st);
-    case 64: return by_hg<SCHEME, BITS, 64>(p, hg, batch, st);
-    case 128: return by_hg<SCHEME, BITS, 128>(p, hg, batch, st);
-    default: return by_hg<SCHEME, BITS, 256>(p, hg, batch, st);
+    case 32: return by_hg<SCHEME, BITS, VB, 32>(p, hg, batch, st);
+    case 64: return by_hg<SCHEME, BITS, VB, 64>(p, hg, batch, st);
+    case 128: return by_hg<SCHEME, BITS, VB, 128>(p, hg, batch, st);
+    default: return by_hg<SCHEME, BITS, VB, 256>(p, hg, batch, st);
   }
 }
 
@@ -480,8 +482,13 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
     case KVQ_KIVI:
       switch (g.bits) {
         case 2: return by_d<KVQ_KIVI, 2>(p, g.d, g.hg, g.batch, st);
-        case 4: return by_d<KVQ_KIVI, 4>(p, g.d, g.hg, g.batch, st);
-        default: return by_d<KVQ_KIVI, 8>(p, g.d, g.hg, g.batch, st);
+        case 4:
+          return g.vbits == 2 ? by_d<KVQ_KIVI, 4, 2>(p, g.d, g.hg, g.batch, st)
+                              : by_d<KVQ_KIVI, 4>(p, g.d, g.hg, g.batch, st);
+        default:
+          return g.vbits == 2   ? by_d<KVQ_KIVI, 8, 2>(p, g.d, g.hg, g.batch, st)
+                 : g.vbits == 4 ? by_d<KVQ_KIVI, 8, 4>(p, g.d, g.hg, g.batch, st)
+                                : by_d<KVQ_KIVI, 8>(p, g.d, g.hg, g.batch, st);
       }
     case KVQ_SYM_TOKEN:
       switch (g.bits) {

@@ -80,13 +80,15 @@ struct MfmaParams {
   double rope_theta;              // > 0: keys cached before the rotary embedding
 };
 
-template <int BITS, int D>
+// KIVI page of KB-bit key codes and VB-bit value codes
+template <int KB, int VB, int D>
 struct PageGeom {
-  static constexpr int CODES = 32 * D * BITS / 8;   // one packed K-rows or V-cols run
+  static constexpr int CODES = 32 * D * KB / 8;     // the packed K rows
+  static constexpr int VCODES = 32 * D * VB / 8;    // the packed V cols
   static constexpr int OFF_KS = CODES;
   static constexpr int OFF_KZ = OFF_KS + 4 * D;
   static constexpr int OFF_VC = OFF_KZ + 4 * D;
-  static constexpr int OFF_VS = OFF_VC + CODES;
+  static constexpr int OFF_VS = OFF_VC + VCODES;
   static constexpr int OFF_VZ = OFF_VS + 128;
   static constexpr int BYTES = OFF_VZ + 128;
   static constexpr int DMA = (BYTES + 1023) / 1024;  // 16-byte-per-lane copies per page
@@ -283,7 +285,8 @@ __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* 
     __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Blocks of kivi_mfma_kernel<bits, d, *, rope> resident per CU: what its LDS
+// Blocks of kivi_mfma_kernel<bits, *, d, *, rope> resident per CU (bits = key
+// bits; value codes are never wider than key codes): what its LDS
 // (page buffers, fragments, query) and registers are sized for. The split
 // plan fills one round of the 256 CUs with this many blocks each. (2-bit pages
 // at d <= 128 would fit a fourth block, but eight splits per (sequence, KV
@@ -294,19 +297,20 @@ constexpr int kivi_blocks_per_cu(int bits, int d, bool rope) {
   return 3;
 }
 
-template <int BITS, int D, int HG, bool ROPE>
-__global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(BITS, D, ROPE)) void kivi_mfma_kernel(MfmaParams p) {
-  static_assert(BITS == 2 || BITS == 4, "2- or 4-bit pages");
-  static_assert(!ROPE || (BITS == 2 && D <= 128), "rotary decode: 2-bit pages, head_dim <= 128");
+// KB, VB: bits of the key and of the value codes
+template <int KB, int VB, int D, int HG, bool ROPE>
+__global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(KB, D, ROPE)) void kivi_mfma_kernel(MfmaParams p) {
+  static_assert((KB == 2 || KB == 4) && (VB == 2 || VB == 4) && VB <= KB, "2- or 4-bit codes");
+  static_assert(!ROPE || (KB == 2 && D <= 128), "rotary decode: 2-bit pages, head_dim <= 128");
   static_assert(2 * HG <= 16, "hi and lo columns of the GQA group fit one tile");
-  using PG = PageGeom<BITS, D>;
+  using PG = PageGeom<KB, VB, D>;
   constexpr int KS = D / 32;             // k-steps of the key product
   constexpr int NT = D / 16;             // channel tiles of the value product
   constexpr int CPG = D / 4;             // key channels per lane group
-  constexpr int KROW = D * BITS / 8;     // bytes per key token row
+  constexpr int KROW = D * KB / 8;       // bytes per key token row
   constexpr int CPR_K = KROW / 16;       // 16-byte chunks per key row
-  constexpr int KW = CPG * BITS / 32;    // key-code words per lane per 16-token tile
-  constexpr int VROW = 32 * BITS / 8;    // bytes per value channel column
+  constexpr int KW = CPG * KB / 32;      // key-code words per lane per 16-token tile
+  constexpr int VROW = 32 * VB / 8;      // bytes per value channel column
   constexpr int COMBOS = HG * 4 * KS;    // (head, lane group, k-step) fold units
   constexpr int REPS = (COMBOS + 63) / 64;
   constexpr int PER_HEAD = 4 * KS;       // fold units (lanes) per head
@@ -562,7 +566,7 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(BITS, D, ROPE)) void k
       for (int w = 0; w < KW; ++w)
         kp[w] = *reinterpret_cast<const uint32_t*>(pg + krow_off<CPR_K>(16 * mt + j, g * (KW * 4) + 4 * w));
       floatx4 c = {bias_j, bias_j, bias_j, bias_j};   // hi column carries q . z
-      if constexpr (BITS == 2) {
+      if constexpr (KB == 2) {
 #pragma unroll
         for (int w = 0; w < KW; ++w) {
           half8 a0, a1;
@@ -613,7 +617,7 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(BITS, D, ROPE)) void k
     for (int nt = 0; nt < NT; ++nt) {
       const uint8_t* col = pg + PG::OFF_VC + (16 * nt + j) * VROW;
       uint4 bw;
-      if constexpr (BITS == 2) {
+      if constexpr (VB == 2) {
         const uint2 v2 = *reinterpret_cast<const uint2*>(col);
         // byte g of each word: tokens 4g..4g+3 and 16+4g..16+4g+3
         const uint32_t x = __builtin_amdgcn_perm(v2.y, v2.x, 0x0C0C0400u + 0x0101u * g);
@@ -900,7 +904,7 @@ template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
   constexpr int HG = 4, BITS = 2;
   constexpr int NTH = NW * 64;           // threads of the block
-  using PG = PageGeom<BITS, D>;
+  using PG = PageGeom<BITS, BITS, D>;
   constexpr int NT = D / 16;             // channel tiles of the value product
   constexpr int KROW = D * BITS / 8;     // bytes per key token row
   constexpr int CPR_K = KROW / 16;
@@ -1367,24 +1371,24 @@ __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
 }
 
 
-template <int BITS, int D, bool ROPE>
+template <int KB, int VB, int D, bool ROPE>
 hipError_t by_hg(const MfmaParams& p, int hg, int batch, hipStream_t st) {
   dim3 grid(p.splits, p.kv_heads, batch);
   switch (hg) {
-    case 1: hipLaunchKernelGGL((kivi_mfma_kernel<BITS, D, 1, ROPE>), grid, dim3(kThreads), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((kivi_mfma_kernel<BITS, D, 2, ROPE>), grid, dim3(kThreads), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((kivi_mfma_kernel<BITS, D, 4, ROPE>), grid, dim3(kThreads), 0, st, p); break;
-    default: hipLaunchKernelGGL((kivi_mfma_kernel<BITS, D, 8, ROPE>), grid, dim3(kThreads), 0, st, p); break;
+    case 1: hipLaunchKernelGGL((kivi_mfma_kernel<KB, VB, D, 1, ROPE>), grid, dim3(kThreads), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((kivi_mfma_kernel<KB, VB, D, 2, ROPE>), grid, dim3(kThreads), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((kivi_mfma_kernel<KB, VB, D, 4, ROPE>), grid, dim3(kThreads), 0, st, p); break;
+    default: hipLaunchKernelGGL((kivi_mfma_kernel<KB, VB, D, 8, ROPE>), grid, dim3(kThreads), 0, st, p); break;
   }
   return hipGetLastError();
 }
 
-template <int BITS>
+template <int KB, int VB>
 hipError_t by_d(const MfmaParams& p, int d, int hg, int batch, hipStream_t st) {
   switch (d) {
-    case 64: return by_hg<BITS, 64, false>(p, hg, batch, st);
-    case 128: return by_hg<BITS, 128, false>(p, hg, batch, st);
-    default: return by_hg<BITS, 256, false>(p, hg, batch, st);
+    case 64: return by_hg<KB, VB, 64, false>(p, hg, batch, st);
+    case 128: return by_hg<KB, VB, 128, false>(p, hg, batch, st);
+    default: return by_hg<KB, VB, 256, false>(p, hg, batch, st);
   }
 }
 
@@ -1395,14 +1399,14 @@ hipError_t by_d_rope(const MfmaParams& p, int d, int hg, int batch, hipStream_t 
     else hipLaunchKernelGGL((rope4_kernel<128, kRopeWaves>), grid, dim3(64 * kRopeWaves), 0, st, p);
     return hipGetLastError();
   }
-  return d == 64 ? by_hg<2, 64, true>(p, hg, batch, st) : by_hg<2, 128, true>(p, hg, batch, st);
+  return d == 64 ? by_hg<2, 2, 64, true>(p, hg, batch, st) : by_hg<2, 2, 128, true>(p, hg, batch, st);
 }
 
 }  // namespace
 
 bool mfma_path(const Geometry& g) {
   if (g.scheme != KVQ_KIVI || g.d < 64 || g.in_bytes != 2) return false;
-  if (g.rope == 0.0) return g.bits == 2 || g.bits == 4;
+  if (g.rope == 0.0) return g.bits == 2 || g.bits == 4;   // value bits: 2 or 4, <= key bits
   return g.bits == 2 && g.d <= 128;   // rotary keys: 2-bit pages, head_dim 64 or 128
 }
 
@@ -1455,7 +1459,8 @@ hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t st) {
   p.qscale = a.sm_scale * kLog2e;
   p.rope_theta = a.rope_theta;
   if (a.rope_theta > 0.0) return by_d_rope(p, g.d, g.hg, g.batch, st);
-  return g.bits == 2 ? by_d<2>(p, g.d, g.hg, g.batch, st) : by_d<4>(p, g.d, g.hg, g.batch, st);
+  if (g.bits == 2) return by_d<2, 2>(p, g.d, g.hg, g.batch, st);
+  return g.vbits == 2 ? by_d<4, 2>(p, g.d, g.hg, g.batch, st) : by_d<4, 4>(p, g.d, g.hg, g.batch, st);
 }
 
 }  // namespace kvq

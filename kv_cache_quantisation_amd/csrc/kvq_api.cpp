@@ -33,6 +33,10 @@ int32_t validate_config(const kvq_config* cfg) {
   } else if (c.bits != 2 && c.bits != 4 && c.bits != 8) {
     return (c.bits >= 1 && c.bits <= 8) ? KVQ_ERR_UNSUPPORTED : KVQ_ERR_INVALID;
   }
+  if (c.v_bits != 0 && c.v_bits != c.bits) {
+    if (c.scheme != KVQ_KIVI || c.v_bits < 1 || c.v_bits > 8) return KVQ_ERR_INVALID;
+    if ((c.v_bits != 2 && c.v_bits != 4) || c.v_bits > c.bits) return KVQ_ERR_UNSUPPORTED;
+  }
   if (c.layers < 1 || c.q_heads < 1 || c.kv_heads < 1 || c.batch < 1 || c.max_tokens < 0)
     return KVQ_ERR_INVALID;
   if (c.q_heads % c.kv_heads != 0) return KVQ_ERR_INVALID;
@@ -73,6 +77,7 @@ int32_t make_geometry(const kvq_config& c, Geometry* g) {
   Geometry x{};
   x.scheme = c.scheme;
   x.bits = c.bits;
+  x.vbits = c.v_bits != 0 ? c.v_bits : c.bits;
   x.d = c.head_dim;
   x.hg = c.q_heads / c.kv_heads;
   x.kv_heads = c.kv_heads;
@@ -85,15 +90,16 @@ int32_t make_geometry(const kvq_config& c, Geometry* g) {
   x.capacity = c.max_tokens;
   const int32_t d = c.head_dim, b = c.bits;
   const int32_t codes = kPage * d * b / 8;  // one packed K-rows or V-cols run
+  const int32_t vcodes = kPage * d * x.vbits / 8;   // KIVI value codes
   switch (c.scheme) {
     case KVQ_KIVI:
       x.off_kc = 0;
       x.off_ks = codes;
       x.off_kz = codes + 4 * d;
       x.off_vc = codes + 8 * d;
-      x.off_vs = 2 * codes + 8 * d;
-      x.off_vz = 2 * codes + 8 * d + 4 * kPage;
-      x.page_bytes = 2 * codes + 8 * d + 8 * kPage;
+      x.off_vs = codes + vcodes + 8 * d;
+      x.off_vz = codes + vcodes + 8 * d + 4 * kPage;
+      x.page_bytes = codes + vcodes + 8 * d + 8 * kPage;
       x.ring_slots = c.residual + kPage;
       break;
     case KVQ_SYM_TOKEN:
@@ -203,13 +209,12 @@ int64_t kvq_cache_bytes(const kvq_config* cfg, int64_t tokens, int32_t kind) {
   if (tokens >= (int64_t(1) << 36)) return KVQ_ERR_UNSUPPORTED;
   switch (kind) {
     case KVQ_BYTES_FORMULA: {
-      // batch * 2 * layers * kv_heads * head_dim * tokens * bits / 8
-      int64_t v = kvq::mul_ck(2, cfg->batch);
-      v = kvq::mul_ck(v, cfg->layers);
+      // batch * layers * kv_heads * head_dim * tokens * (key bits + value bits) / 8
+      int64_t v = kvq::mul_ck(cfg->batch, cfg->layers);
       v = kvq::mul_ck(v, cfg->kv_heads);
       v = kvq::mul_ck(v, cfg->head_dim);
       v = kvq::mul_ck(v, tokens);
-      v = kvq::mul_ck(v, cfg->bits);
+      v = kvq::mul_ck(v, g.bits + g.vbits);
       return v < 0 ? KVQ_ERR_INVALID : v / 8;
     }
     case KVQ_BYTES_CACHE: {

@@ -20,6 +20,7 @@ __host__ __device__ constexpr bool is_fp8(int scheme) {
 // Everything a kernel needs to address one layer of the cache.
 struct Geometry {
   int32_t scheme, bits, d, hg, kv_heads, q_heads, batch, layers, residual;
+  int32_t vbits;            // bits of the value codes (KIVI; = bits otherwise)
   int32_t in_bytes;         // bytes per K/V input element (and ring element)
   double rope;              // rotary base (0 = none)
   int64_t capacity;         // max_tokens

@@ -48,12 +48,13 @@ class kvq_config(ctypes.Structure):
         ("rope_theta", ctypes.c_double),
         ("sm_scale", ctypes.c_float),
         ("num_splits", ctypes.c_int32),
+        ("v_bits", ctypes.c_int32),
     ]
 
 
 def make_config(scheme, bits, layers, q_heads, kv_heads, head_dim, batch, max_tokens,
                 residual=0, in_dtype=KVQ_BF16, q_dtype=KVQ_BF16, rope_theta=0.0,
-                sm_scale=0.0, num_splits=0, group=32):
+                sm_scale=0.0, num_splits=0, group=32, v_bits=0):
     c = kvq_config()
     c.struct_size = ctypes.sizeof(kvq_config)
     c.scheme, c.bits, c.layers = scheme, bits, layers
@@ -61,6 +62,7 @@ def make_config(scheme, bits, layers, q_heads, kv_heads, head_dim, batch, max_to
     c.batch, c.max_tokens, c.group, c.residual = batch, max_tokens, group, residual
     c.in_dtype, c.q_dtype = in_dtype, q_dtype
     c.rope_theta, c.sm_scale, c.num_splits = rope_theta, sm_scale, num_splits
+    c.v_bits = v_bits
     return c
 
 

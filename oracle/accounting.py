@@ -2,7 +2,9 @@
 
 * ``kv_bytes_formula`` -- "Quantizing the KV cache", section "The other big
   memory user": KV bytes = 2 x layers x KV heads x head size x tokens x bytes
-  per value, the 2 counting keys and values.
+  per value, the 2 counting keys and values. With keys and values stored at
+  different widths (the same page's "How the KV cache is quantized" names
+  separate key and value cache types) each half counts at its own width.
 * ``concurrency`` -- "Quantising the Cache.", Workshop and "Twice the users for
   nearly nothing": how many 8192-token conversations fit beside Llama 3 8B's
   16.1 GB of BF16 weights on an 80 GB GPU used to 90%, cache scales ignored.
@@ -17,11 +19,13 @@ KIVI, SYM_TOKEN, FP8_E4M3, BF16_CACHE, FP8_E5M2 = 0, 1, 2, 3, 4
 PAGE = 32
 
 
-def kv_bytes_formula(layers, kv_heads, head_dim, tokens, bits, batch=1):
-    """2 * layers * kv_heads * head_dim * tokens * bits/8 (times sequences).
+def kv_bytes_formula(layers, kv_heads, head_dim, tokens, bits, batch=1, v_bits=None):
+    """2 * layers * kv_heads * head_dim * tokens * bits/8 (times sequences);
+    with v_bits, layers * kv_heads * head_dim * tokens * (bits + v_bits)/8.
 
     Exact integer arithmetic (bits/8 kept as a fraction, so 4-bit works)."""
-    b = Fraction(2 * layers * kv_heads * head_dim * tokens * batch) * Fraction(bits, 8)
+    vb = bits if v_bits is None else v_bits
+    b = Fraction(layers * kv_heads * head_dim * tokens * batch) * Fraction(bits + vb, 8)
     assert b.denominator == 1, "bytes must be whole"
     return int(b)
 
@@ -49,12 +53,14 @@ def flush_plan(tokens, residual, group=PAGE):
     return q, tokens - q
 
 
-def page_bytes(scheme, head_dim, bits):
-    """Bytes of one 32-token page of the documented layout."""
+def page_bytes(scheme, head_dim, bits, v_bits=None):
+    """Bytes of one 32-token page of the documented layout (KIVI value codes
+    of v_bits when given, else of bits)."""
     d, b = head_dim, bits
+    vb = bits if v_bits is None else v_bits
     if scheme == KIVI:
         # K codes + K scale/offset per channel + V codes + V scale/offset per token
-        return PAGE * d * b // 8 + 4 * d + 4 * d + PAGE * d * b // 8 + 4 * PAGE + 4 * PAGE
+        return PAGE * d * b // 8 + 4 * d + 4 * d + PAGE * d * vb // 8 + 4 * PAGE + 4 * PAGE
     if scheme == SYM_TOKEN:
         return PAGE * d * b // 8 + 4 * PAGE + PAGE * d * b // 8 + 4 * PAGE
     if scheme in (FP8_E4M3, FP8_E5M2):
@@ -76,13 +82,13 @@ def ring_bytes(scheme, head_dim, residual, in_itemsize):
     return 2 * (residual + PAGE) * head_dim * in_itemsize
 
 
-def slab_bytes(scheme, head_dim, bits, capacity, residual, in_itemsize):
-    return (pages_per_slab(scheme, capacity, residual) * page_bytes(scheme, head_dim, bits)
+def slab_bytes(scheme, head_dim, bits, capacity, residual, in_itemsize, v_bits=None):
+    return (pages_per_slab(scheme, capacity, residual) * page_bytes(scheme, head_dim, bits, v_bits)
             + ring_bytes(scheme, head_dim, residual, in_itemsize))
 
 
 def layout_cache_bytes(scheme, layers, batch, kv_heads, head_dim, bits, capacity,
-                       residual, in_itemsize):
+                       residual, in_itemsize, v_bits=None):
     """Whole cache: one slab per (layer, sequence, KV head)."""
     return layers * batch * kv_heads * slab_bytes(scheme, head_dim, bits, capacity,
-                                                  residual, in_itemsize)
+                                                  residual, in_itemsize, v_bits)

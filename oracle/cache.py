@@ -43,10 +43,11 @@ class OracleCache:
     """in_dtype is "f32" (inputs float32) or "bf16" (inputs uint16 bit patterns)."""
 
     def __init__(self, scheme, bits, layers, batch, kv_heads, head_dim, capacity,
-                 residual=0, in_dtype="bf16"):
+                 residual=0, in_dtype="bf16", v_bits=None):
         if scheme != KIVI:
-            assert residual == 0
+            assert residual == 0 and v_bits in (None, bits)
         self.scheme, self.bits, self.layers, self.batch = scheme, bits, layers, batch
+        self.v_bits = bits if v_bits is None else v_bits   # KIVI value codes
         self.kv_heads, self.d, self.capacity = kv_heads, head_dim, capacity
         self.residual, self.in_dtype = residual, in_dtype
         self.itemsize = 2 if in_dtype == "bf16" else 4
@@ -89,10 +90,10 @@ class OracleCache:
     # ---- byte image -------------------------------------------------------
     def slab_size(self):
         return accounting.slab_bytes(self.scheme, self.d, self.bits, self.capacity,
-                                     self.residual, self.itemsize)
+                                     self.residual, self.itemsize, self.v_bits)
 
     def page_size(self):
-        return accounting.page_bytes(self.scheme, self.d, self.bits)
+        return accounting.page_bytes(self.scheme, self.d, self.bits, self.v_bits)
 
     def slab_image(self, layer, b, h):
         """(bytes, mask) of one slab for the tokens held now."""
@@ -109,7 +110,7 @@ class OracleCache:
             q, _ = accounting.flush_plan(T, self.residual)
             for p in range(q // PAGE):
                 pb, pm = layout.kivi_page(K[p * PAGE:(p + 1) * PAGE], V[p * PAGE:(p + 1) * PAGE],
-                                          self.bits)
+                                          self.bits, self.v_bits)
                 buf[p * ps:(p + 1) * ps], mask[p * ps:(p + 1) * ps] = pb, pm
             n_pages = accounting.pages_per_slab(KIVI, self.capacity, self.residual)
             ring0 = n_pages * ps
@@ -164,7 +165,7 @@ class OracleCache:
             for p in range(q // PAGE):
                 sl = slice(p * PAGE, (p + 1) * PAGE)
                 kc, ks, kz = codec.kivi_quantize(K[:, :, sl], self.bits, axis=2)
-                vc, vs, vz = codec.kivi_quantize(V[:, :, sl], self.bits, axis=3)
+                vc, vs, vz = codec.kivi_quantize(V[:, :, sl], self.v_bits, axis=3)
                 kh[:, :, sl] = codec.kivi_dequantize(kc, ks, kz, axis=2)
                 vh[:, :, sl] = codec.kivi_dequantize(vc, vs, vz, axis=3)
             kh[:, :, q:] = K[:, :, q:]

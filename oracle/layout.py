@@ -47,13 +47,15 @@ def _full(n):
     return np.full(n, 0xFF, np.uint8)
 
 
-def kivi_page(k32, v32, bits):
-    """One full KIVI page from 32 tokens of keys and values (float32 [32, d])."""
+def kivi_page(k32, v32, bits, v_bits=None):
+    """One full KIVI page from 32 tokens of keys and values (float32 [32, d]);
+    value codes of v_bits when given, else of bits."""
+    vb = bits if v_bits is None else v_bits
     kc, ks, kz = codec.kivi_quantize(k32, bits, axis=0)   # per channel over the tokens
-    vc, vs, vz = codec.kivi_quantize(v32, bits, axis=1)   # per token over the channels
+    vc, vs, vz = codec.kivi_quantize(v32, vb, axis=1)     # per token over the channels
     parts = [pack_fields(kc, bits),            # K rows: kc[t, c], channel fastest
              _f32_bytes(ks), _f32_bytes(kz),
-             pack_fields(vc.T, bits),          # V cols: vc[t, c] stored channel-major
+             pack_fields(vc.T, vb),            # V cols: vc[t, c] stored channel-major
              _f32_bytes(vs), _f32_bytes(vz)]
     buf = np.concatenate(parts)
     return buf, _full(buf.size)

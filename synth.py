@@ -43,6 +43,7 @@ class Workload:
     v_outlier_factor: float = 1.0
     rope_theta: float = 0.0
     layers: int = 1
+    v_bits: int = 0          # KIVI value-code bits; 0 = the key bits
 
 
 WORKLOADS = {
@@ -61,6 +62,11 @@ WORKLOADS = {
     "int4": Workload("int4", 3, KIVI, 4, 32, 32, 8, 128, 32768, residual=128,
                      k_outlier_channels=4, k_outlier_factor=20.0,
                      v_outlier_frac=0.01, v_outlier_factor=10.0),
+    # KIVI with 4-bit keys and 2-bit values at the kivi2 shape (keys kept wider:
+    # their outlier channels make rounding cost them more than values)
+    "kivi_k4v2": Workload("kivi_k4v2", 5, KIVI, 4, 16, 32, 8, 128, 4096, residual=128,
+                          k_outlier_channels=4, k_outlier_factor=20.0,
+                          v_outlier_frac=0.01, v_outlier_factor=10.0, v_bits=2),
     # long context 2-bit, batch 1, 1,048,576 tokens, keys pre-RoPE (theta 500000)
     "longctx": Workload("longctx", 4, KIVI, 2, 1, 32, 8, 128, 1 << 20, residual=128,
                         k_outlier_channels=4, k_outlier_factor=20.0,

@@ -38,13 +38,14 @@ def config(w, capacity=None, num_splits=0, layers=None):
     return kvq.make_config(w.scheme, w.bits, layers or w.layers, w.q_heads, w.kv_heads,
                            w.head_dim, w.batch, capacity or w.tokens, residual=w.residual,
                            in_dtype=DT[w.in_dtype], q_dtype=DT[w.q_dtype],
-                           rope_theta=w.rope_theta, num_splits=num_splits)
+                           rope_theta=w.rope_theta, num_splits=num_splits, v_bits=w.v_bits)
 
 
 def oracle_cache(w, capacity=None, layers=None):
     return OracleCache(w.scheme, w.bits, layers or w.layers, w.batch, w.kv_heads, w.head_dim,
                        capacity or w.tokens, residual=w.residual,
-                       in_dtype="bf16" if w.in_dtype == torch.bfloat16 else "f32")
+                       in_dtype="bf16" if w.in_dtype == torch.bfloat16 else "f32",
+                       v_bits=w.v_bits or None)
 
 
 def append_chunks(cfg, cache, k, v, chunks, layer=0, ks=None, vs=None, oc=None):
@@ -100,7 +101,7 @@ def oracle_dequant_head(w, kf, vf, T, ks=None, vs=None):
             vg = vf[:q].reshape(q // 32, 32, d)
             c, s, z = codec.kivi_quantize(kg, w.bits, axis=1)
             kh[:q] = codec.kivi_dequantize(c, s, z, axis=1).reshape(q, d)
-            c, s, z = codec.kivi_quantize(vg, w.bits, axis=2)
+            c, s, z = codec.kivi_quantize(vg, w.v_bits or w.bits, axis=2)
             vh[:q] = codec.kivi_dequantize(c, s, z, axis=2).reshape(q, d)
         return kh, vh
     if w.scheme == synth.BF16_CACHE:

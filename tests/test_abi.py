@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert kvq.kvq_abi_version() == 1
+    assert kvq.kvq_abi_version() == 2
     assert kvq.status_string(0) == "ok"
     for st in (-1, -2, -3, -4, -5, -6):
         assert kvq.status_string(st) != "unknown status"
@@ -47,8 +47,9 @@ def cfg(**kw):
 
 
 def test_struct_layout():
-    assert ctypes.sizeof(kvq.kvq_config) == 72
+    assert ctypes.sizeof(kvq.kvq_config) == 80
     assert kvq.kvq_config.max_tokens.offset == 32 and kvq.kvq_config.rope_theta.offset == 56
+    assert kvq.kvq_config.v_bits.offset == 72
     c = cfg()
     assert kvq.kvq_cache_bytes(c, 10, kvq.KVQ_BYTES_FORMULA) > 0
     c.struct_size = 64
@@ -84,6 +85,42 @@ def test_cache_bytes_match_oracle_layout(scheme, bits, d, R, dtype):
     for T in (0, 1, 31, 32, 33, 160, 161, 4096, 10000):
         assert kvq.kvq_cache_bytes(c, T, kvq.KVQ_BYTES_CACHE) == \
             acc.layout_cache_bytes(scheme, 2, 3, 8, d, bits, T, R, item), T
+
+
+@pytest.mark.parametrize("bits,v_bits,d,R,dtype", [
+    (4, 2, 128, 128, kvq.KVQ_BF16), (8, 4, 64, 0, kvq.KVQ_F32), (8, 2, 256, 37, kvq.KVQ_BF16),
+    (4, 2, 32, 5, kvq.KVQ_F32), (4, 4, 128, 16, kvq.KVQ_BF16)])
+def test_kivi_value_bits_sizes(bits, v_bits, d, R, dtype):
+    """KIVI with value codes narrower than key codes: exact layout size and
+    the KV-bytes equation with each half at its own width, as the oracle has
+    them; v_bits equal to bits is the same cache as v_bits 0."""
+    c = cfg(bits=bits, v_bits=v_bits, head_dim=d, residual=R, in_dtype=dtype, q_heads=8)
+    item = 2 if dtype == kvq.KVQ_BF16 else 4
+    for T in (0, 1, 31, 33, 161, 4096, 10000):
+        assert kvq.kvq_cache_bytes(c, T, kvq.KVQ_BYTES_CACHE) == \
+            acc.layout_cache_bytes(kvq.KVQ_KIVI, 2, 3, 8, d, bits, T, R, item, v_bits), T
+        assert kvq.kvq_cache_bytes(c, T, kvq.KVQ_BYTES_FORMULA) == \
+            acc.kv_bytes_formula(2, 8, d, T, bits, batch=3, v_bits=v_bits)
+    if v_bits == bits:
+        c0 = cfg(bits=bits, head_dim=d, residual=R, in_dtype=dtype, q_heads=8)
+        assert kvq.kvq_cache_bytes(c0, 999, kvq.KVQ_BYTES_CACHE) == \
+            kvq.kvq_cache_bytes(c, 999, kvq.KVQ_BYTES_CACHE)
+
+
+def test_value_bits_validation():
+    L = kvq.lib()
+    def st(**kw):
+        c = cfg(**kw)
+        return L.kvq_cache_bytes(ctypes.byref(c), 64, kvq.KVQ_BYTES_CACHE)
+    assert st(bits=4, v_bits=2) > 0 and st(bits=8, v_bits=4) > 0 and st(bits=8, v_bits=2) > 0
+    assert st(bits=2, v_bits=4) == kvq.KVQ_ERR_UNSUPPORTED     # values wider than keys
+    assert st(bits=4, v_bits=8) == kvq.KVQ_ERR_UNSUPPORTED
+    assert st(bits=8, v_bits=3) == kvq.KVQ_ERR_UNSUPPORTED     # 3-bit codes not built
+    assert st(bits=4, v_bits=9) == kvq.KVQ_ERR_INVALID
+    assert st(bits=4, v_bits=-2) == kvq.KVQ_ERR_INVALID
+    assert st(scheme=kvq.KVQ_SYM_TOKEN, bits=4, v_bits=2, residual=0) == kvq.KVQ_ERR_INVALID
+    assert st(scheme=kvq.KVQ_SYM_TOKEN, bits=4, v_bits=4, residual=0) > 0
+    assert st(scheme=kvq.KVQ_FP8_E4M3, bits=8, v_bits=4, residual=0) == kvq.KVQ_ERR_INVALID
 
 
 def test_config_sizes_of_the_workloads():

@@ -28,6 +28,7 @@ UNITS = {
     "kivi2": [(0, 0), (7, 3), (15, 7)],
     "fp8": [(0, 0), (37, 5), (63, 7)],
     "int4": [(0, 0), (31, 7)],
+    "kivi_k4v2": [(0, 0), (9, 4)],
     "longctx": [(0, 6)],
 }
 
@@ -47,7 +48,7 @@ def page_image(w, kf, vf, p, T, ks=None, vs=None):
     v32 = np.zeros((PAGE, w.head_dim), np.float32)
     k32[:n], v32[:n] = kf[p * PAGE:p * PAGE + n], vf[p * PAGE:p * PAGE + n]
     if w.scheme == synth.KIVI:
-        return layout.kivi_page(k32, v32, w.bits)
+        return layout.kivi_page(k32, v32, w.bits, w.v_bits or None)
     if w.scheme == synth.SYM_TOKEN:
         return layout.sym_page(k32, v32, w.bits, n)
     return layout.fp8_page(k32, v32, ks, vs, n)
@@ -77,7 +78,7 @@ def test_fullsize_workload(name):
     slab = cache.numel() // (w.batch * w.kv_heads)
     assert slab * w.batch * w.kv_heads == cache.numel()
     itemsize = 2 if w.in_dtype == torch.bfloat16 else 4
-    ps = accounting.page_bytes(w.scheme, w.head_dim, w.bits)
+    ps = accounting.page_bytes(w.scheme, w.head_dim, w.bits, w.v_bits or None)
     hg = w.q_heads // w.kv_heads
     qv = H.values(q)
     outh = out.cpu().numpy()

@@ -24,11 +24,12 @@ CHUNKINGS = {
 
 
 def small(scheme, bits, d, dtype=torch.bfloat16, R=0, B=2, Hkv=2, hg=2, T=300, rope=0.0,
-          v_frac=0.01):
+          v_frac=0.01, v_bits=0):
     return synth.Workload(f"s{scheme}b{bits}d{d}", 90 + scheme * 10 + bits, scheme, bits, B,
                           Hkv * hg, Hkv, d, T, residual=R, in_dtype=dtype, q_dtype=dtype,
                           k_outlier_channels=min(4, d // 16), k_outlier_factor=20.0,
-                          v_outlier_frac=v_frac, v_outlier_factor=10.0, rope_theta=rope)
+                          v_outlier_frac=v_frac, v_outlier_factor=10.0, rope_theta=rope,
+                          v_bits=v_bits)
 
 
 def run_append(w, chunks, capacity, scales=None):
@@ -56,6 +57,43 @@ def test_append_kivi_bytes(bits, d, dtype, R, chunking):
     cfg, cache, oc, *_ = run_append(w, CHUNKINGS[chunking](w.tokens), capacity=320)
     want, mask = oc.cache_image()
     H.compare_bytes(cache.cpu().numpy(), want, mask, f"kivi b{bits} d{d} R{R} {chunking}")
+
+
+@pytest.mark.parametrize("chunking", list(CHUNKINGS))
+@pytest.mark.parametrize("bits,v_bits,d,dtype,R", [
+    (4, 2, 128, torch.bfloat16, 128), (8, 4, 64, torch.float32, 0), (8, 2, 256, torch.bfloat16, 37),
+    (4, 2, 32, torch.bfloat16, 1), (8, 4, 128, torch.bfloat16, 5)])
+def test_append_kivi_value_bits_bytes(bits, v_bits, d, dtype, R, chunking):
+    """KIVI pages with value codes narrower than key codes, bit-exact."""
+    w = small(synth.KIVI, bits, d, dtype, R, v_bits=v_bits)
+    cfg, cache, oc, *_ = run_append(w, CHUNKINGS[chunking](w.tokens), capacity=320)
+    want, mask = oc.cache_image()
+    H.compare_bytes(cache.cpu().numpy(), want, mask, f"kivi k{bits}v{v_bits} d{d} R{R} {chunking}")
+
+
+VALUE_BITS_DECODE = [
+    # bits, v_bits, d, hg, dtype, R, T, rope, splits
+    (4, 2, 128, 4, torch.bfloat16, 128, 700, 0.0, 0),      # matrix cores
+    (4, 2, 64, 2, torch.bfloat16, 20, 300, 0.0, 3),
+    (4, 2, 256, 8, torch.bfloat16, 40, 300, 0.0, 2),
+    (4, 2, 128, 1, torch.bfloat16, 0, 161, 0.0, 1),
+    (8, 4, 128, 4, torch.bfloat16, 16, 333, 0.0, 0),       # generic kernel
+    (8, 2, 64, 2, torch.float32, 0, 257, 0.0, 5),
+    (4, 2, 128, 4, torch.bfloat16, 128, 700, 500000.0, 0),  # rotary keys, generic
+    (4, 2, 32, 1, torch.float32, 3, 98, 0.0, 0),
+]
+
+
+@pytest.mark.parametrize("bits,v_bits,d,hg,dtype,R,T,rope,splits", VALUE_BITS_DECODE)
+def test_decode_kivi_value_bits(bits, v_bits, d, hg, dtype, R, T, rope, splits):
+    w = small(synth.KIVI, bits, d, dtype, R, hg=hg, T=T, rope=rope, v_bits=v_bits)
+    cfg, cache, oc, k, v, ks, vs = run_append(w, [T], capacity=T + 40)
+    cfg.num_splits = splits
+    q = synth.query(w, device=DEV)
+    out = H.decode(cfg, cache, 0, T, q, ks, vs)
+    want = oc.decode(0, H.values(q), rope_theta=rope)
+    err = H.max_err(out, want)
+    assert err <= H.ATOL, err
 
 
 @pytest.mark.parametrize("chunking", ["one", "steps", "mixed"])

@@ -116,3 +116,26 @@ def test_layout_sizes():
     assert acc.slab_bytes(acc.KIVI, 128, 2, 4096, 128, 2) == 124 * 3328 + 2 * 160 * 128 * 2
     assert acc.pages_per_slab(acc.SYM_TOKEN, 513, 0) == 17
     assert acc.layout_cache_bytes(acc.FP8_E4M3, 2, 3, 4, 128, 8, 64, 0, 2) == 2 * 3 * 4 * 2 * 8192
+
+
+def test_value_bits_accounting(golden):
+    """Keys and values at their own widths ("Quantizing the KV cache", How the
+    KV cache is quantized: separate key and value cache types): each half of
+    the KV-bytes equation at its own width. Llama 3 8B's 128 KiB per token at
+    16 bits gives 24 KiB with 4-bit keys and 2-bit values (6/32 of it), half
+    way between the 4-bit and the 2-bit cache."""
+    g = golden("pages_memory.json")["llama3_8b"]
+    sh = g["shape"]
+    per16 = g["bytes_per_token_16bit"]
+    mixed = acc.kv_bytes_formula(sh["layers"], sh["kv_heads"], sh["head_dim"], 1, 4, v_bits=2)
+    assert mixed * 32 == per16 * 6 == 24 * 1024 * 32
+    assert 2 * mixed == acc.kv_bytes_formula(32, 8, 128, 1, 4) + acc.kv_bytes_formula(32, 8, 128, 1, 2)
+    assert acc.kv_bytes_formula(32, 8, 128, 77, 8, v_bits=8) == acc.kv_bytes_formula(32, 8, 128, 77, 8)
+    # a KIVI page with 4-bit keys and 2-bit values: 2048 B of key codes, 1024 B
+    # of value codes, 1024 B of key scale/offset, 256 B of value scale/offset
+    assert acc.page_bytes(acc.KIVI, 128, 4, 2) == 2048 + 1024 + 1024 + 256
+    for d in (32, 64, 128, 256):
+        for kb, vb in ((4, 2), (8, 2), (8, 4)):
+            p = acc.page_bytes(acc.KIVI, d, kb, vb)
+            assert p % 256 == 0
+            assert 2 * p == acc.page_bytes(acc.KIVI, d, kb) + acc.page_bytes(acc.KIVI, d, vb)

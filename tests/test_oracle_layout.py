@@ -178,3 +178,37 @@ def test_bf16_page_layout():
     assert np.all(mask[:5 * 128] == 0xFF) and np.all(mask[5 * 128:4096] == 0)
     vm = mask[4096:].reshape(64, 64)
     assert np.all(vm[:, :10] == 0xFF) and np.all(vm[:, 10:] == 0)
+
+
+def test_kivi_page_value_bits():
+    """A page with value codes narrower than key codes is the key half of the
+    key-width page followed by the value half of the value-width page (keys and
+    values are grouped and rounded independently), and the whole-cache oracle
+    dequantises values at their own width."""
+    rng = np.random.default_rng(11)
+    d = 64
+    k = rng.standard_normal((32, d)).astype(F32)
+    v = rng.standard_normal((32, d)).astype(F32)
+    for kb, vb in ((4, 2), (8, 2), (8, 4)):
+        mixed, mask = layout.kivi_page(k, v, kb, vb)
+        wide, _ = layout.kivi_page(k, v, kb)
+        narrow, _ = layout.kivi_page(k, v, vb)
+        kpart = 32 * d * kb // 8 + 8 * d
+        vpart = 32 * d * vb // 8 + 256
+        assert mixed.size == kpart + vpart == acc.page_bytes(acc.KIVI, d, kb, vb)
+        assert np.array_equal(mixed[:kpart], wide[:kpart])
+        assert np.array_equal(mixed[kpart:], narrow[narrow.size - vpart:])
+        assert np.all(mask == 0xFF)
+    B, H = 1, 2
+    kk, vv = _bf16(rng, B, 90, H, d), _bf16(rng, B, 90, H, d)
+    c42 = OracleCache(acc.KIVI, 4, 1, B, H, d, 96, residual=8, v_bits=2)
+    c44 = OracleCache(acc.KIVI, 4, 1, B, H, d, 96, residual=8)
+    c22 = OracleCache(acc.KIVI, 2, 1, B, H, d, 96, residual=8)
+    for c in (c42, c44, c22):
+        c.append(0, kk, vv)
+    k42, v42 = c42.dequantized(0)
+    assert np.array_equal(k42, c44.dequantized(0)[0])
+    assert np.array_equal(v42, c22.dequantized(0)[1])
+    # at d 64: 2 pages of 1024 B key codes + 512 B key scales/offsets + 512 B value
+    # codes + 256 B value scales/offsets, then the ring of 40 bf16 K and V rows
+    assert c42.slab_size() == 2 * (1024 + 512 + 512 + 256) + 2 * 40 * d * 2
