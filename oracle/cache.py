@@ -7,7 +7,9 @@ is asked, which makes the result independent of how the appends were
 chunked by construction:
 
 * KIVI: with T tokens held, tokens [0, q(T)) are encoded in 32-token groups
-  (keys per channel, values per token) and the newest T - q(T) sit in the
+  (keys per channel at `bits`, values per token at `v_bits`, which may be
+  narrower: "Quantizing the KV cache", How the KV cache is quantized, names
+  separate key and value cache types) and the newest T - q(T) sit in the
   residual ring unquantised, slot t mod (R + 32) ("Quantizing the KV cache":
   the newest R tokens stay in full precision, a full window is quantised as a
   group; KIVI How It Works: recent tokens kept in 16-bit).
