@@ -26,12 +26,14 @@
 // channel from LDS. They update the same softmax state and accumulators.
 //
 // Operand layouts (wave64): lane l holds A[l%16][8(l/16)+i], B[8(l/16)+i][l%16]
-// (i = 0..7) and C[4(l/16)+r][l%16] (r = 0..3). Computing S^T (tokens as rows)
-// leaves lane (j, g) = (l%16, l/16) with head j's scores for tokens {4g..4g+3}
-// and {16+4g..16+4g+3}: the lane and token set the P.V A-operand needs, so P
-// never moves between lanes. Value codes are fed in that token order (for
-// channel c, tokens 4g..4g+3 are byte g of its 2-bit column, bytes 2g, 2g+1 of
-// its 4-bit column). Codes become exact small integers with the scaled converts:
+// (i = 0..7) and C[4(l/16)+r][l%16] (r = 0..3). Computing S^T (tokens as rows,
+// row r of key tile mt holding token 8(r/4) + 4mt + r%4) leaves lane (j, g) =
+// (l%16, l/16) with head j's scores for tokens 8g..8g+7: the lane and token set
+// the P.V A-operand needs, so P never moves between lanes, and for channel c
+// those tokens are the 16 bits at byte 2g of its 2-bit column (32 bits at byte
+// 4g of its 4-bit column; the rotary variant keeps token 16mt + r in row r and
+// picks bytes g and 4+g of a 2-bit column). Codes become exact small integers
+// with the scaled converts:
 // a 2-bit code in an FP4 E2M1 nibble is code/2 (scale 2), a 4-bit code in an
 // FP8 E4M3 byte is code * 2^-9 (scale 512), to f16 for keys and bf16 for
 // values; the converts produce channels in the order {0,2,1,3,4,6,5,7} within
@@ -63,6 +65,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRopeWaves = 4;      // waves per block of rope4_kernel
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kMaxSlack = 8.0f;  // log2 units a score may exceed the running max by
 
 struct MfmaParams {
   const uint8_t* layer_base;
@@ -119,6 +122,20 @@ __device__ __forceinline__ half8 codes4_frag(uint32_t w) {
                bits32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(y0, 512.0f, true)),
                bits32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(y1, 512.0f, true)));
 }
+
+// Page token held by row r of the 16-row key tile mt. The C layout of the key
+// product gives lane group g rows 4g..4g+3 of each tile, so with this map lane
+// group g ends with the scores of tokens 8g..8g+7: the contiguous run of a
+// value column that the P.V operand of the same lanes needs.
+// The rotary variant keeps token 16mt + r in row r (its residual steps rotate
+// tile row j by j with the same per-lane table), so lane group g holds tokens
+// 4g..4g+3 and 16+4g..16+4g+3.
+template <bool ROPE>
+__device__ __forceinline__ int tile_tok(int mt, int r) {
+  return ROPE ? 16 * mt + r : 8 * (r >> 2) + 4 * mt + (r & 3);
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float load_q(const uint8_t* base, int64_t idx, int bf16) {
   if (bf16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
@@ -315,6 +332,9 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(KB, D, ROPE)) void kiv
   constexpr int REPS = (COMBOS + 63) / 64;
   constexpr int PER_HEAD = 4 * KS;       // fold units (lanes) per head
   constexpr int QB = (3 * HG + 15) / 16; // bf16 B-operand sets for the residual keys
+  // the residual-key B operand is built once per wave and kept in registers
+  // when it is small (QB * KS words of 16 bytes), else rebuilt for every step
+  constexpr bool QPRE = !ROPE && QB * KS <= 4;
   static_assert(KW >= 1, "at least one word per lane");
   // B fragments of q' for the live columns (hi, lo): [column][(4 ks + g) ^ column]
   // in 16-byte slots; the XOR puts the 16 lanes that read one (ks, g) for
@@ -371,8 +391,11 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(KB, D, ROPE)) void kiv
     for (int i = 1; i < NS; ++i) pmax = fmaxf(pmax, s[i]);
     pmax = fmaxf(pmax, xor16(pmax));
     pmax = fmaxf(pmax, xor32(pmax));
+    // the reference max moves only when a score exceeds it by more than
+    // kMaxSlack (weights stay below 2^kMaxSlack; any reference gives the same
+    // softmax), so the accumulators are rarely rescaled
     const float m_new = fmaxf(m_lane, pmax);
-    const bool grows = (j < HG) && (m_new > m_lane);
+    const bool grows = (j < HG) && (pmax > m_lane + kMaxSlack);
     if (__builtin_amdgcn_ballot_w64(grows) != 0) {   // wave-uniform
       const float alpha = fast_exp2(m_lane - m_new);
       l_lane *= alpha;
@@ -484,7 +507,7 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(KB, D, ROPE)) void kiv
 #pragma unroll
         for (int w = 0; w < D / 64; ++w) {
           const uint32_t word =
-              *reinterpret_cast<const uint32_t*>(pg + krow_off<CPR_K>(16 * mt + j, (D / 16) * g + 4 * w));
+              *reinterpret_cast<const uint32_t*>(pg + krow_off<CPR_K>(tile_tok<ROPE>(mt, j), (D / 16) * g + 4 * w));
 #pragma unroll
           for (int c = 0; c < 16; ++c)
             y[16 * w + c] = fmaf(static_cast<float>((word >> (2 * c)) & 3u), sv[16 * w + c], zv[16 * w + c]);
@@ -564,7 +587,7 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(KB, D, ROPE)) void kiv
       uint32_t kp[KW];
 #pragma unroll
       for (int w = 0; w < KW; ++w)
-        kp[w] = *reinterpret_cast<const uint32_t*>(pg + krow_off<CPR_K>(16 * mt + j, g * (KW * 4) + 4 * w));
+        kp[w] = *reinterpret_cast<const uint32_t*>(pg + krow_off<CPR_K>(tile_tok<ROPE>(mt, j), g * (KW * 4) + 4 * w));
       floatx4 c = {bias_j, bias_j, bias_j, bias_j};   // hi column carries q . z
       if constexpr (KB == 2) {
 #pragma unroll
@@ -585,10 +608,12 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(KB, D, ROPE)) void kiv
     }   // rotary / plain keys
 
     softmax_update(s, std::integral_constant<int, 8>{});
-    const float4 vs0 = *reinterpret_cast<const float4*>(pg + PG::OFF_VS + 16 * g);
-    const float4 vs1 = *reinterpret_cast<const float4*>(pg + PG::OFF_VS + 64 + 16 * g);
-    const float4 vz0 = *reinterpret_cast<const float4*>(pg + PG::OFF_VZ + 16 * g);
-    const float4 vz1 = *reinterpret_cast<const float4*>(pg + PG::OFF_VZ + 64 + 16 * g);
+    // per-token value scale and offset of this lane's tokens tile_tok(mt, 4g + r)
+    constexpr int VT0 = ROPE ? 16 : 32, VT1 = ROPE ? 64 : 16;
+    const float4 vs0 = *reinterpret_cast<const float4*>(pg + PG::OFF_VS + VT0 * g);
+    const float4 vs1 = *reinterpret_cast<const float4*>(pg + PG::OFF_VS + VT1 + VT0 * g);
+    const float4 vz0 = *reinterpret_cast<const float4*>(pg + PG::OFF_VZ + VT0 * g);
+    const float4 vz1 = *reinterpret_cast<const float4*>(pg + PG::OFF_VZ + VT1 + VT0 * g);
     const float vsv[8] = {vs0.x, vs0.y, vs0.z, vs0.w, vs1.x, vs1.y, vs1.z, vs1.w};
     const float vzv[8] = {vz0.x, vz0.y, vz0.z, vz0.w, vz1.x, vz1.y, vz1.z, vz1.w};
     float pv[8];
@@ -598,7 +623,7 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(KB, D, ROPE)) void kiv
       z_lane = fmaf(s[i], vzv[i], z_lane);
       pv[i] = s[i] * vsv[i];
     }
-    // P' into A fragments: token order {4g+0,4g+2,4g+1,4g+3, 16+4g+0,...}
+    // P' into A fragments: the lane's tokens in the order {0,2,1,3,4,6,5,7}
     uint32_t ph[4], pl[4];
     split_bf16(pv[0], pv[2], ph[0], pl[0]);
     split_bf16(pv[1], pv[3], ph[1], pl[1]);
@@ -612,35 +637,54 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(KB, D, ROPE)) void kiv
     const bf16x8 ap = __builtin_bit_cast(bf16x8, uint4{pa[0], pa[1], pa[2], pa[3]});
 
     // P' x value codes; channel of N-tile nt in column j is 16 nt + j (adjacent
-    // lanes read adjacent value columns: no LDS bank conflicts)
+    // lanes read adjacent value columns: no LDS bank conflicts). Lane group g
+    // needs tokens 8g..8g+7 of a column: 16 bits of a 2-bit column, 32 of a
+    // 4-bit one; the converts give them in the order {0,2,1,3,4,6,5,7} of P'.
+    if constexpr (ROPE) {   // 2-bit values, tokens 4g..4g+3 and 16+4g..16+4g+3
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const uint8_t* col = pg + PG::OFF_VC + (16 * nt + j) * VROW;
-      uint4 bw;
-      if constexpr (VB == 2) {
-        const uint2 v2 = *reinterpret_cast<const uint2*>(col);
-        // byte g of each word: tokens 4g..4g+3 and 16+4g..16+4g+3
+      for (int nt = 0; nt < NT; ++nt) {
+        const uint2 v2 = *reinterpret_cast<const uint2*>(pg + PG::OFF_VC + (16 * nt + j) * VROW);
+        // byte g of each word
         const uint32_t x = __builtin_amdgcn_perm(v2.y, v2.x, 0x0C0C0400u + 0x0101u * g);
         const uint32_t y0 = x & 0x3333u, y1 = (x >> 2) & 0x3333u;
-        bw = uint4{bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y0, 2.0f, 0)),
-                   bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 0)),
-                   bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y0, 2.0f, 1)),
-                   bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 1))};
-      } else {
-        // bytes 2g,2g+1 (tokens 4g..4g+3) and 8+2g, 9+2g (tokens 16+4g..)
-        const uint32_t lo = reinterpret_cast<const uint32_t*>(col)[g >> 1];
-        const uint32_t hi = reinterpret_cast<const uint32_t*>(col)[2 + (g >> 1)];
-        const uint32_t sh = (g & 1) * 2;
-        const uint32_t sel = (0x0100u + 0x0101u * sh) | ((0x0504u + 0x0101u * sh) << 16);
-        const uint32_t w = __builtin_amdgcn_perm(hi, lo, sel);
-        const uint32_t y0 = w & 0x0F0F0F0Fu, y1 = (w >> 4) & 0x0F0F0F0Fu;
-        bw = uint4{bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y0, 512.0f, false)),
-                   bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y1, 512.0f, false)),
-                   bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y0, 512.0f, true)),
-                   bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y1, 512.0f, true))};
+        const uint4 bw{bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y0, 2.0f, 0)),
+                       bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 0)),
+                       bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y0, 2.0f, 1)),
+                       bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 1))};
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, __builtin_bit_cast(bf16x8, bw), acc[nt], 0, 0, 0);
       }
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, __builtin_bit_cast(bf16x8, bw), acc[nt],
-                                                         0, 0, 0);
+    } else if constexpr (VB == 2) {
+#pragma unroll
+      for (int nt = 0; nt < NT; nt += 2) {   // two channel tiles per code word
+        const uint8_t* col = pg + PG::OFF_VC + (16 * nt + j) * VROW + 2 * g;
+        u16x2 xv;
+        xv.x = *reinterpret_cast<const uint16_t*>(col);
+        xv.y = *reinterpret_cast<const uint16_t*>(col + 16 * VROW);
+        const uint32_t x = __builtin_bit_cast(uint32_t, xv);
+        const uint32_t y0 = x & 0x33333333u, y1 = (x >> 2) & 0x33333333u;
+        const uint4 b0{bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y0, 2.0f, 0)),
+                       bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 0)),
+                       bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y0, 2.0f, 1)),
+                       bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 1))};
+        const uint4 b1{bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y0, 2.0f, 2)),
+                       bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 2)),
+                       bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y0, 2.0f, 3)),
+                       bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 3))};
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, __builtin_bit_cast(bf16x8, b0), acc[nt], 0, 0, 0);
+        acc[nt + 1] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, __builtin_bit_cast(bf16x8, b1), acc[nt + 1], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(pg + PG::OFF_VC + (16 * nt + j) * VROW + 4 * g);
+        const uint32_t y0 = w & 0x0F0F0F0Fu, y1 = (w >> 4) & 0x0F0F0F0Fu;
+        const uint4 bw{bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y0, 512.0f, false)),
+                       bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y1, 512.0f, false)),
+                       bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y0, 512.0f, true)),
+                       bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y1, 512.0f, true))};
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, __builtin_bit_cast(bf16x8, bw), acc[nt], 0, 0, 0);
+      }
     }
   };
 
@@ -675,6 +719,25 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(KB, D, ROPE)) void kiv
       *reinterpret_cast<uint4*>(wring + RSTEP * 2 * D + nv * 2 * D + i * 16) = uint4{0u, 0u, 0u, 0u};
     return issued;
   };
+  uint4 qstep[QPRE ? QB : 1][QPRE ? KS : 1];
+  // B operand of the residual key product: q^T in three bf16 parts, columns
+  // [0,HG) hi, [HG,2HG) mid, [2HG,3HG) lo, the rest zero (from the scaled q in qs)
+  auto qstep_operand = [&](int qb, int ks) -> uint4 {
+    const int col = 16 * qb + j;
+    const int part = col / HG, hh = col % HG;
+    uint32_t w4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float2 qq = *reinterpret_cast<const float2*>(&qs[hh][32 * ks + 8 * g + 2 * i]);
+      const float h0 = bf16_trunc(qq.x), h1 = bf16_trunc(qq.y);
+      const float m0 = bf16_trunc(qq.x - h0), m1 = bf16_trunc(qq.y - h1);
+      float x0 = part == 0 ? h0 : (part == 1 ? m0 : qq.x - h0 - m0);
+      float x1 = part == 0 ? h1 : (part == 1 ? m1 : qq.y - h1 - m1);
+      if (part >= 3) x0 = x1 = 0.f;      // unused columns
+      w4[i] = pack_bf16(x0, x1);
+    }
+    return uint4{w4[0], w4[1], w4[2], w4[3]};
+  };
   // tile rows (tokens) 8..15 of a step are masked; key rows repeat rows 0..7
   auto process_step = [&](int hs) {
     const int64_t t0 = p.q_tokens + static_cast<int64_t>(hs) * RSTEP;
@@ -698,7 +761,6 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(KB, D, ROPE)) void kiv
 #pragma unroll
       for (int r = 0; r < 4; ++r) sc[r] = (4 * g + r < nv) ? c[r] : -INFINITY;
     } else {
-    // B = q^T in three bf16 parts: columns [0,HG) hi, [HG,2HG) mid, [2HG,3HG) lo
     floatx4 cres[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) cres[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -707,21 +769,10 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(KB, D, ROPE)) void kiv
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(wring + (j & 7) * 2 * D + (32 * ks + 8 * g) * 2);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const int col = 16 * qb + j;
-        const int part = col / HG, hh = col % HG;
-        uint32_t w4[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float2 qq = *reinterpret_cast<const float2*>(&qs[hh][32 * ks + 8 * g + 2 * i]);
-          const float h0 = bf16_trunc(qq.x), h1 = bf16_trunc(qq.y);
-          const float m0 = bf16_trunc(qq.x - h0), m1 = bf16_trunc(qq.y - h1);
-          float x0 = part == 0 ? h0 : (part == 1 ? m0 : qq.x - h0 - m0);
-          float x1 = part == 0 ? h1 : (part == 1 ? m1 : qq.y - h1 - m1);
-          if (part >= 3) x0 = x1 = 0.f;      // unused columns
-          w4[i] = pack_bf16(x0, x1);
-        }
-        const bf16x8 bq = __builtin_bit_cast(bf16x8, uint4{w4[0], w4[1], w4[2], w4[3]});
-        cres[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq, cres[qb], 0, 0, 0);
+        uint4 w;
+        if constexpr (QPRE) w = qstep[QPRE ? qb : 0][QPRE ? ks : 0];
+        else w = qstep_operand(qb, ks);
+        cres[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, w), cres[qb], 0, 0, 0);
       }
     }
 #pragma unroll
@@ -808,7 +859,7 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(KB, D, ROPE)) void kiv
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int m = 0; m < NPL; ++m) {
-        const double turns = static_cast<double>(16 * mt + j) * w2pi[(D / 8) * g + m];
+        const double turns = static_cast<double>(tile_tok<ROPE>(mt, j)) * w2pi[(D / 8) * g + m];
         sincospif(2.0f * static_cast<float>(turns - floor(turns)), &rsin[mt][m], &rcos[mt][m]);
       }
     }
@@ -817,6 +868,12 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(KB, D, ROPE)) void kiv
       qpair[hh][0] = lane < D / 2 ? qs[hh][2 * lane] : 0.f;
       qpair[hh][1] = lane < D / 2 ? qs[hh][2 * lane + 1] : 0.f;
     }
+  }
+  if constexpr (QPRE) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qstep[qb][ks] = qstep_operand(qb, ks);
   }
   // fold units handled by this lane: (head, lane group, k-step) -> 8 channels
 #pragma unroll
@@ -840,6 +897,15 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(KB, D, ROPE)) void kiv
   // ---- pages: DMA pipeline, one page ahead (page 0 already requested) --------
 #pragma unroll 1
   for (int k = 0; k < n_mine; ++k) {
+    // waves with more pages left issue first: the waves of a SIMD (from
+    // different blocks) then finish their pages together instead of the
+    // oldest first, leaving the last one alone on the SIMD
+    {
+      const int rem = n_mine - k;
+      if (rem >= 4) __builtin_amdgcn_s_setprio(2);
+      else if (rem >= 2) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
     wait_lds();   // the buffer about to be refilled has been read
     __builtin_amdgcn_wave_barrier();
     const bool next = k + 1 < n_mine;
@@ -864,6 +930,7 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(KB, D, ROPE)) void kiv
   }
   wait_lds();
 
+  __builtin_amdgcn_s_setprio(3);   // the epilogue and merge end the block's critical path
   // ---- wave epilogue -----------------------------------------------------------
   float lsum[HG], zsum[HG], mh[HG];
   {
@@ -1423,7 +1490,12 @@ MfmaPlan mfma_plan(const Geometry& g, int64_t tokens, int32_t requested) {
     const int64_t units = static_cast<int64_t>(g.batch) * g.kv_heads;
     const bool rope = g.rope != 0.0;
     // rotary keys at GQA 4 run rope4_kernel (three blocks per CU)
-    const int64_t target = 256 * (rope && g.hg == 4 ? 3 : kivi_blocks_per_cu(g.bits, g.d, rope));
+    // (2-bit pages without rotation: two blocks per CU measured faster than
+    // three at batch 16, context 4096 -- less fixed work per wave)
+    const int64_t per_cu = rope && g.hg == 4 ? 3
+                         : (g.bits == 2 && !rope && g.d <= 128) ? 2
+                         : kivi_blocks_per_cu(g.bits, g.d, rope);
+    const int64_t target = 256 * per_cu;
     s = (target + units - 1) / units;
     const int64_t cap = (pl.pages + 7) / 8;
     if (s > cap) s = cap;

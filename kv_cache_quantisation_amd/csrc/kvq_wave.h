@@ -123,7 +123,13 @@ __device__ __forceinline__ uint32_t shr_keep(uint32_t keep, uint32_t v) {
 // f32 pair -> packed f16 (hi) and packed f16 remainder (lo), hi + lo ~ x.
 __device__ __forceinline__ void split_f16(float a, float b, uint32_t& hi, uint32_t& lo) {
   const auto h = __builtin_amdgcn_cvt_pkrtz(a, b);
-  const auto r = __builtin_amdgcn_cvt_pkrtz(a - static_cast<float>(h[0]), b - static_cast<float>(h[1]));
+  // a - hi as one mixed-precision fma per value, reading hi's f16 halves in
+  // place (exact: hi is a truncation of a)
+  const uint32_t hw = bits32(h);
+  float ra, rb;
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(ra) : "v"(hw), "v"(a));
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(rb) : "v"(hw), "v"(b));
+  const auto r = __builtin_amdgcn_cvt_pkrtz(ra, rb);
   hi = bits32(h);
   lo = bits32(r);
 }
@@ -132,7 +138,9 @@ __device__ __forceinline__ void split_f16(float a, float b, uint32_t& hi, uint32
 // carries 16 significant bits of each value at any magnitude (no subnormal
 // floor, unlike f16), and the rounding is unbiased.
 __device__ __forceinline__ void split_bf16(float a, float b, uint32_t& hi, uint32_t& lo) {
-  const uint32_t h = __builtin_bit_cast(uint32_t, bf16x2{static_cast<__bf16>(a), static_cast<__bf16>(b)});
+  // one conversion of the pair (left to itself the compiler converts a twice)
+  uint32_t h;
+  asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(h) : "v"(a), "v"(b));
   const float ha = __uint_as_float(h << 16), hb = __uint_as_float(h & 0xFFFF0000u);
   hi = h;
   lo = __builtin_bit_cast(uint32_t, bf16x2{static_cast<__bf16>(a - ha), static_cast<__bf16>(b - hb)});
