@@ -62,7 +62,6 @@ namespace {
 
 
 constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kRopeWaves = 4;      // waves per block of rope4_kernel
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMaxSlack = 8.0f;  // log2 units a score may exceed the running max by
@@ -314,13 +313,26 @@ constexpr int kivi_blocks_per_cu(int bits, int d, bool rope) {
   return 3;
 }
 
+// Waves per block of kivi_mfma_kernel<kb, vb, d, hg, rope>: eight for 2-bit
+// pages at d <= 128 and GQA groups up to 4 (run as one block per CU: half the
+// blocks, and half the partials to merge, of four-wave blocks; 19.8 vs 20.5 us
+// at batch 16, context 4096), four otherwise. Eight-wave blocks still fit two
+// per CU (71.7 KB of LDS, <= 128 VGPRs), which kivi_blocks_per_cu(2, d, false)
+// = 3 would only tighten, so their launch bound asks for two.
+constexpr int kivi_waves(int kb, int vb, int d, int hg, bool rope) {
+  return (kb == 2 && vb == 2 && d <= 128 && hg <= 4 && !rope) ? 8 : 4;
+}
+
 // KB, VB: bits of the key and of the value codes
 template <int KB, int VB, int D, int HG, bool ROPE>
-__global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(KB, D, ROPE)) void kivi_mfma_kernel(MfmaParams p) {
+__global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
+                             kivi_waves(KB, VB, D, HG, ROPE) == 8 ? 2 : kivi_blocks_per_cu(KB, D, ROPE)) void kivi_mfma_kernel(MfmaParams p) {
   static_assert((KB == 2 || KB == 4) && (VB == 2 || VB == 4) && VB <= KB, "2- or 4-bit codes");
   static_assert(!ROPE || (KB == 2 && D <= 128), "rotary decode: 2-bit pages, head_dim <= 128");
   static_assert(2 * HG <= 16, "hi and lo columns of the GQA group fit one tile");
   using PG = PageGeom<KB, VB, D>;
+  constexpr int NW = kivi_waves(KB, VB, D, HG, ROPE);   // waves per block
+  constexpr int NTH = 64 * NW;
   constexpr int KS = D / 32;             // k-steps of the key product
   constexpr int NT = D / 16;             // channel tiles of the value product
   constexpr int CPG = D / 4;             // key channels per lane group
@@ -350,14 +362,14 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(KB, D, ROPE)) void kiv
   // further step after its last page.
   constexpr int WAVE_LDS = PG::NBUF * PG::BYTES + FRAG > PG::BYTES + PG::RING
                                ? PG::NBUF * PG::BYTES + FRAG : PG::BYTES + PG::RING;
-  constexpr int RED = kWaves * HG * (D + 2) * 4;
-  constexpr int ARENA = kWaves * WAVE_LDS > RED ? kWaves * WAVE_LDS : RED;
+  constexpr int RED = NW * HG * (D + 2) * 4;
+  constexpr int ARENA = NW * WAVE_LDS > RED ? NW * WAVE_LDS : RED;
 
   __shared__ __attribute__((aligned(16))) float qs[HG][D];
   __shared__ __attribute__((aligned(16))) uint8_t arena[ARENA];              // per-wave areas / reduction
   // rotary decode: each wave's query rotated for the page in hand (row HG is
   // kept zero for the unused B columns), and omega_i / (2 pi) per channel pair
-  __shared__ __attribute__((aligned(16))) float qpage[ROPE ? kWaves : 1][ROPE ? HG + 1 : 1][ROPE ? D : 4];
+  __shared__ __attribute__((aligned(16))) float qpage[ROPE ? NW : 1][ROPE ? HG + 1 : 1][ROPE ? D : 4];
   __shared__ double w2pi[ROPE ? D / 2 : 1];
   __shared__ int last_block;
 
@@ -419,11 +431,11 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(KB, D, ROPE)) void kiv
 
   // ---- work of this wave --------------------------------------------------------
   // Block `split` takes a contiguous range of pages; its waves take every
-  // kWaves-th page of that range.
-  const int waves_total = p.splits * kWaves;
+  // NW-th page of that range.
+  const int waves_total = p.splits * NW;
   const int pg0 = static_cast<int>(static_cast<int64_t>(split) * p.n_pages / p.splits);
   const int pg1 = static_cast<int>(static_cast<int64_t>(split + 1) * p.n_pages / p.splits);
-  const int n_mine = pg0 + wave < pg1 ? (pg1 - pg0 - wave + kWaves - 1) / kWaves : 0;
+  const int n_mine = pg0 + wave < pg1 ? (pg1 - pg0 - wave + NW - 1) / NW : 0;
 
   float qreg[REPS][8];   // this lane's fold units of q (set once q is staged)
   // rotary decode: this lane's channel pairs are (D/8) g + m, m < D/8; rcos/rsin
@@ -473,7 +485,7 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(KB, D, ROPE)) void kiv
   };
 
   auto issue_page = [&](int k) {   // page k of this wave -> buffer k % NBUF
-    const uint8_t* src = slab + static_cast<int64_t>(pg0 + wave + kWaves * k) * p.page_bytes;
+    const uint8_t* src = slab + static_cast<int64_t>(pg0 + wave + NW * k) * p.page_bytes;
     const uint32_t dst = lds_addr(wbuf + (k % PG::NBUF) * PG::BYTES);
 #pragma unroll
     for (int i = 0; i < PG::DMA; ++i) {
@@ -813,7 +825,7 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(KB, D, ROPE)) void kiv
   // residual step, its first page ------------------------------------------------
   // residual steps go first to the waves with the fewest pages: the last wave
   // of every block, then the one before, ... (wave 0 may hold one page more)
-  const int my_wave = (kWaves - 1 - wave) * p.splits + split;
+  const int my_wave = (NW - 1 - wave) * p.splits + split;
   const int q_bytes = HG * D * (p.q_bf16 ? 2 : 4);
   int after_q = 0;
   if (wave == 0) {
@@ -828,7 +840,7 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(KB, D, ROPE)) void kiv
     after_q += PG::DMA;
   }
   if constexpr (ROPE) {
-    for (int i = tid; i < D / 2; i += kThreads)
+    for (int i = tid; i < D / 2; i += NTH)
       w2pi[i] = pow(p.rope_theta, -2.0 * i / D) * 0.15915494309189535;   // omega_i / (2 pi)
     for (int i = lane; i < D; i += 64) qpage[wave][HG][i] = 0.f;
   }
@@ -836,11 +848,11 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(KB, D, ROPE)) void kiv
   __syncthreads();
   {
     // raw query (bf16 or f32) -> f32 * sm_scale * log2(e), in place
-    constexpr int PER = (HG * D + kThreads - 1) / kThreads;
+    constexpr int PER = (HG * D + NTH - 1) / NTH;
     float qv[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int i = tid + k * kThreads;
+      const int i = tid + k * NTH;
       qv[k] = 0.f;
       if (i < HG * D)
         qv[k] = p.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(&qs[0][0])[i])
@@ -849,7 +861,7 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(KB, D, ROPE)) void kiv
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int i = tid + k * kThreads;
+      const int i = tid + k * NTH;
       if (i < HG * D) (&qs[0][0])[i] = qv[k] * p.qscale;
     }
     __syncthreads();
@@ -914,7 +926,7 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(KB, D, ROPE)) void kiv
     else wait_vm<0>();
     __builtin_amdgcn_wave_barrier();
     process_page(wbuf + (k % PG::NBUF) * PG::BYTES,
-                 static_cast<int64_t>(pg0 + wave + kWaves * k) * kPage);
+                 static_cast<int64_t>(pg0 + wave + NW * k) * kPage);
   }
 
   // ---- any further residual steps of this wave (when steps outnumber waves) --
@@ -946,7 +958,7 @@ __global__ __launch_bounds__(kThreads, kivi_blocks_per_cu(KB, D, ROPE)) void kiv
       mh[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_lane), hh));
     }
   }
-  finish_unit<D, HG>(p, acc, mh, lsum, zsum, arena, last_block, b, h, split);
+  finish_unit<D, HG, NW>(p, acc, mh, lsum, zsum, arena, last_block, b, h, split);
 }
 
 // ---- rotary keys, GQA group of 4: dense scores on v_mfma_f32_4x4x1_16b_f32 ----
@@ -1442,10 +1454,10 @@ template <int KB, int VB, int D, bool ROPE>
 hipError_t by_hg(const MfmaParams& p, int hg, int batch, hipStream_t st) {
   dim3 grid(p.splits, p.kv_heads, batch);
   switch (hg) {
-    case 1: hipLaunchKernelGGL((kivi_mfma_kernel<KB, VB, D, 1, ROPE>), grid, dim3(kThreads), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((kivi_mfma_kernel<KB, VB, D, 2, ROPE>), grid, dim3(kThreads), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((kivi_mfma_kernel<KB, VB, D, 4, ROPE>), grid, dim3(kThreads), 0, st, p); break;
-    default: hipLaunchKernelGGL((kivi_mfma_kernel<KB, VB, D, 8, ROPE>), grid, dim3(kThreads), 0, st, p); break;
+    case 1: hipLaunchKernelGGL((kivi_mfma_kernel<KB, VB, D, 1, ROPE>), grid, dim3(64 * kivi_waves(KB, VB, D, 1, ROPE)), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((kivi_mfma_kernel<KB, VB, D, 2, ROPE>), grid, dim3(64 * kivi_waves(KB, VB, D, 2, ROPE)), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((kivi_mfma_kernel<KB, VB, D, 4, ROPE>), grid, dim3(64 * kivi_waves(KB, VB, D, 4, ROPE)), 0, st, p); break;
+    default: hipLaunchKernelGGL((kivi_mfma_kernel<KB, VB, D, 8, ROPE>), grid, dim3(64 * kivi_waves(KB, VB, D, 8, ROPE)), 0, st, p); break;
   }
   return hipGetLastError();
 }
@@ -1490,10 +1502,9 @@ MfmaPlan mfma_plan(const Geometry& g, int64_t tokens, int32_t requested) {
     const int64_t units = static_cast<int64_t>(g.batch) * g.kv_heads;
     const bool rope = g.rope != 0.0;
     // rotary keys at GQA 4 run rope4_kernel (three blocks per CU)
-    // (2-bit pages without rotation: two blocks per CU measured faster than
-    // three at batch 16, context 4096 -- less fixed work per wave)
+    // (2-bit pages without rotation run eight-wave blocks, one per CU)
     const int64_t per_cu = rope && g.hg == 4 ? 3
-                         : (g.bits == 2 && !rope && g.d <= 128) ? 2
+                         : kivi_waves(g.bits, g.vbits, g.d, g.hg, rope) == 8 ? 1
                          : kivi_blocks_per_cu(g.bits, g.d, rope);
     const int64_t target = 256 * per_cu;
     s = (target + units - 1) / units;
