@@ -53,11 +53,11 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 # kernel sources they were taken with (SHA-256 over DECODE_SOURCES); after any
 # change to those, `traffic` is reported as null until they are taken again.
 COUNTERS = {
-    "kivi2": {"context": 4119, "fetch_kib": 31912.46875, "write_kib": 2156.0,
+    "kivi2": {"context": 4119, "fetch_kib": 31146.875, "write_kib": 892.0,
               "fetch_scale": 262144 / 131084, "write_scale": 1.0,
-              "sources_sha256": "e6832348538bef1ea885958567873a169cb5b7bc312993b64b7dd94b2733949a"},
+              "sources_sha256": "51c2f4eb3e67c7bd3ce31b74830f40af63d35e7c8b58f93e74f8e35a4b757a8e"},
 }
-DECODE_SOURCES = ["decode_mfma.hip", "kvq_device.h", "kvq_internal.h"]
+DECODE_SOURCES = ["decode_mfma.hip", "kvq_device.h", "kvq_internal.h", "kvq_wave.h"]
 
 
 def decode_sources_sha256():
@@ -318,8 +318,8 @@ def gpu_bench(args, w):
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": counter_traffic(w, T_end),
-                "kernel": f"kivi_mfma_kernel<{w.bits},{w.head_dim},{w.q_heads // w.kv_heads}> "
-                          "(decode, merge fused)",
+                "kernel": f"kivi_mfma_kernel<{w.bits},{w.v_bits or w.bits},{w.head_dim},"
+                          f"{w.q_heads // w.kv_heads}> (decode, merge fused)",
                 "avg_launch_us": round(avg_us, 3), "bytes_per_launch": per_launch,
                 "context": T_end}
     return {

@@ -301,12 +301,10 @@ __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* 
     __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Blocks of kivi_mfma_kernel<bits, *, d, *, rope> resident per CU (bits = key
-// bits; value codes are never wider than key codes): what its LDS
-// (page buffers, fragments, query) and registers are sized for. The split
-// plan fills one round of the 256 CUs with this many blocks each. (2-bit pages
-// at d <= 128 would fit a fourth block, but eight splits per (sequence, KV
-// head) instead of six measured no faster at batch 16, context 4096.)
+// Blocks of the four-wave kivi_mfma_kernel<bits, *, d, *, rope> resident per
+// CU (bits = key bits; value codes are never wider than key codes): what its
+// LDS (page buffers, fragments, query) and registers are sized for. The split
+// plan fills one round of the 256 CUs with this many blocks each.
 constexpr int kivi_blocks_per_cu(int bits, int d, bool rope) {
   if (rope) return 2;
   if (d >= 256) return bits == 2 ? 2 : 1;
