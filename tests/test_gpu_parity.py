@@ -433,3 +433,35 @@ def test_multi_layer_addressing():
     for layer in (0, 2):
         out = H.decode(cfg, cache, layer, 200, q)
         assert H.max_err(out, oc.decode(layer, H.values(q))) <= H.ATOL
+
+
+SCORE_RAMPS = [
+    # bits, d, hg, R, T, ramp: keys scaled by 1 + ramp * t / T, so the running
+    # maximum of the scores grows page after page, by less than and by more than
+    # the kernels' rescaling slack (8 in log2 units)
+    (2, 128, 4, 128, 1400, 3.0), (2, 128, 4, 128, 1400, 12.0), (2, 64, 1, 0, 700, 25.0),
+    (4, 128, 4, 128, 1400, 12.0), (4, 128, 8, 32, 900, 6.0), (2, 128, 2, 128, 900, -0.9),
+]
+
+
+@pytest.mark.parametrize("bits,d,hg,R,T,ramp", SCORE_RAMPS)
+def test_decode_growing_scores(bits, d, hg, R, T, ramp):
+    """Decode where later tokens score ever higher (or, for a negative ramp,
+    lower): the online softmax must rescale correctly however far the maximum
+    moves between pages."""
+    w = small(synth.KIVI, bits, d, torch.bfloat16, R, hg=hg, T=T)
+    cfg = H.config(w, T + 40)
+    cache = kvq.alloc_cache(cfg)
+    oc = H.oracle_cache(w, T + 40)
+    k, v = synth.keys_values(w, device=DEV)
+    q = synth.query(w, device=DEV)
+    # keys along the first query head's direction, growing with t
+    t = torch.arange(T, device=DEV, dtype=torch.float32)
+    scale = (1.0 + ramp * t / T).view(1, T, 1, 1)
+    qdir = q.float()[:, ::hg].unsqueeze(1)                      # [B, 1, Hkv, d]
+    k = (k.float() * 0.3 + 2.0 * qdir * scale).to(torch.bfloat16)
+    H.append_chunks(cfg, cache, k, v, [T], oc=oc)
+    torch.cuda.synchronize()
+    out = H.decode(cfg, cache, 0, T, q)
+    err = H.max_err(out, oc.decode(0, H.values(q)))
+    assert err <= H.ATOL, err
