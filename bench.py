@@ -55,7 +55,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 COUNTERS = {
     "kivi2": {"context": 4119, "fetch_kib": 31146.875, "write_kib": 892.0,
               "fetch_scale": 262144 / 131084, "write_scale": 1.0,
-              "sources_sha256": "51c2f4eb3e67c7bd3ce31b74830f40af63d35e7c8b58f93e74f8e35a4b757a8e"},
+              "sources_sha256": "8c3dbdff8b04cdedeca504d21825275e264b279b9df363e4daf790b8855d3241"},
 }
 DECODE_SOURCES = ["decode_mfma.hip", "kvq_device.h", "kvq_internal.h", "kvq_wave.h"]
 
