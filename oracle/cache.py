@@ -22,7 +22,9 @@ Decode attention (``decode``) dequantises in float64, applies the rotary
 embedding to keys at their positions and to the query at position T-1 when
 rope_theta > 0 (KVQuant Summary: keys cached before RoPE), and takes the
 float64 softmax-weighted sum of value rows ("Quantizing the KV cache", "Why
-values per token").
+values per token"). A ragged batch (per-sequence token counts, the serving
+case of the KIVI page's Key points, where KIVI pairs with PagedAttention)
+attends each sequence to its own first T_b tokens, query at T_b - 1.
 """
 
 import numpy as np
@@ -188,14 +190,27 @@ class OracleCache:
             vh[:] = codec.fp8_dequantize(codec.fp8_quantize(V, vsc, f), vsc, f)
         return kh, vh
 
-    def decode(self, layer, q, sm_scale=None, rope_theta=0.0):
-        """Attention of q [B, Hq, d] (float values) over all held tokens."""
+    def decode(self, layer, q, sm_scale=None, rope_theta=0.0, seq_tokens=None):
+        """Attention of q [B, Hq, d] (float values) over the held tokens.
+
+        seq_tokens (optional, one count per sequence, 1 <= T_b <= T): a ragged
+        batch, where sequence b attends to its first T_b tokens only and its
+        query sits at position T_b - 1. The cache itself stays as held (for
+        KIVI its page/ring split follows T, the fill level), so the tokens a
+        sequence reads are exactly those rows of the dequantised cache."""
         kh, vh = self.dequantized(layer)
         q = np.asarray(q, np.float64)
-        T = kh.shape[2]
+        B, T = kh.shape[0], kh.shape[2]
         if sm_scale is None or sm_scale == 0:
             sm_scale = 1.0 / np.sqrt(self.d)
-        if rope_theta > 0:
-            kh = rope.rotate(kh, np.arange(T), rope_theta)
-            q = rope.rotate(q, np.full(q.shape[:-1], T - 1), rope_theta)
-        return attention.decode(q, kh, vh, sm_scale)
+        lens = [T] * B if seq_tokens is None else [int(x) for x in seq_tokens]
+        out = np.zeros(q.shape)
+        for b in range(B):
+            Tb = lens[b]
+            assert 1 <= Tb <= T, (b, Tb, T)
+            kb, vb, qb = kh[b:b + 1, :, :Tb], vh[b:b + 1, :, :Tb], q[b:b + 1]
+            if rope_theta > 0:
+                kb = rope.rotate(kb, np.arange(Tb), rope_theta)
+                qb = rope.rotate(qb, np.full(qb.shape[:-1], Tb - 1), rope_theta)
+            out[b] = attention.decode(qb, kb, vb, sm_scale)[0]
+        return out

@@ -1,0 +1,97 @@
+"""Pins of the oracle's ragged-batch decode (per-sequence token counts).
+
+A sequence of a ragged batch attends to its own first T_b tokens with its query
+at position T_b - 1. The pins tie that to things fixed independently of the
+ragged code path: the uniform decode (all T_b = T), a cache that only ever held
+the first T_b tokens (for schemes whose encoding of a token never depends on
+later tokens), and brute-force attention over the dequantised rows.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import accounting as acc
+from oracle import attention, rope
+from oracle.cache import OracleCache
+
+B, H, HQ, D = 3, 2, 4, 16
+
+
+def filled(scheme, bits, T, residual=0, seed=0, rope_theta=0.0):
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((B, T, H, D)).astype(np.float32)
+    v = rng.standard_normal((B, T, H, D)).astype(np.float32)
+    c = OracleCache(scheme, bits, 1, B, H, D, T, residual=residual, in_dtype="f32")
+    ks = vs = None
+    if scheme in (acc.FP8_E4M3, acc.FP8_E5M2):
+        ks = (np.abs(k).max(axis=(0, 1, 3)) / 448.0).astype(np.float32)
+        vs = (np.abs(v).max(axis=(0, 1, 3)) / 448.0).astype(np.float32)
+    c.append(0, k, v, ks, vs)
+    q = rng.standard_normal((B, HQ, D)).astype(np.float32)
+    return c, k, v, ks, vs, q
+
+
+@pytest.mark.parametrize("scheme,bits,R", [(acc.KIVI, 2, 16), (acc.SYM_TOKEN, 4, 0),
+                                           (acc.FP8_E4M3, 8, 0), (acc.BF16_CACHE, 16, 0)])
+def test_full_lengths_equal_uniform_decode(scheme, bits, R):
+    c, *_, q = filled(scheme, bits, 90, residual=R)
+    for theta in (0.0, 10000.0):
+        want = c.decode(0, q, rope_theta=theta)
+        got = c.decode(0, q, rope_theta=theta, seq_tokens=[90] * B)
+        assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("scheme,bits", [(acc.SYM_TOKEN, 4), (acc.SYM_TOKEN, 2), (acc.FP8_E4M3, 8),
+                                         (acc.FP8_E5M2, 8), (acc.BF16_CACHE, 16)])
+@pytest.mark.parametrize("theta", [0.0, 500000.0])
+def test_prefix_equals_shorter_cache(scheme, bits, theta):
+    """Per-token schemes encode a token independently of later ones, so
+    sequence b of a ragged batch decodes exactly as a cache that only ever
+    held its first T_b tokens (same query, position T_b - 1)."""
+    T = 77
+    c, k, v, ks, vs, q = filled(scheme, bits, T, seed=3)
+    lens = [1, 40, 77]
+    got = c.decode(0, q, rope_theta=theta, seq_tokens=lens)
+    for b, Tb in enumerate(lens):
+        short = OracleCache(scheme, bits, 1, B, H, D, Tb, in_dtype="f32")
+        short.append(0, k[:, :Tb], v[:, :Tb], ks, vs)
+        want = short.decode(0, q, rope_theta=theta)
+        assert np.array_equal(got[b], want[b]), (b, Tb)
+
+
+def test_kivi_prefix_is_bruteforce_over_dequantised_rows():
+    """KIVI: the flush plan follows the fill level T, so a shorter sequence
+    reads pages and ring rows of the full cache; the result is brute-force
+    attention over those dequantised rows (tokens in a partial page, tokens in
+    the ring, and the first token alone)."""
+    T, R = 100, 8                       # q(T) = 64: two pages, 36 ring tokens
+    c, *_, q = filled(acc.KIVI, 2, T, residual=R, seed=5)
+    kh, vh = c.dequantized(0)
+    lens = [1, 47, 83]                  # inside page 0, inside page 1, in the ring
+    sm = 1.0 / np.sqrt(D)
+    for theta in (0.0, 10000.0):
+        got = c.decode(0, q, rope_theta=theta, seq_tokens=lens)
+        for b, Tb in enumerate(lens):
+            for h in range(HQ):
+                g = attention.gqa_kv_head(h, HQ, H)
+                kk = kh[b, g, :Tb]
+                qq = q[b, h].astype(np.float64)
+                if theta > 0:
+                    kk = rope.rotate(kk, np.arange(Tb), theta)
+                    qq = rope.rotate(qq, np.array(Tb - 1), theta)
+                want = attention.attend_bruteforce(qq, kk, vh[b, g, :Tb], sm)
+                np.testing.assert_allclose(got[b, h], want, rtol=0, atol=1e-12)
+
+
+def test_kivi_short_sequence_reads_quantised_rows():
+    """A sequence shorter than q(T) reads dequantised (not exact) rows: its
+    result differs from a cache that held only its tokens in full precision
+    (the ring of a short cache), which a plausible slip -- truncating before
+    quantising -- would produce."""
+    T, R = 100, 8
+    c, k, v, ks, vs, q = filled(acc.KIVI, 2, T, residual=R, seed=7)
+    Tb = 40
+    got = c.decode(0, q, seq_tokens=[Tb] * B)
+    short = OracleCache(acc.KIVI, 2, 1, B, H, D, Tb, residual=64, in_dtype="f32")   # all in the ring
+    short.append(0, k[:, :Tb], v[:, :Tb])
+    assert np.max(np.abs(got - short.decode(0, q))) > 1e-3
