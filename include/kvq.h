@@ -258,6 +258,26 @@ KVQ_API int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache,
                              float* out, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* Decode attention over a ragged batch: sequence b attends to its first
+ * seq_tokens[b] cached tokens only, its query at position seq_tokens[b] - 1
+ * (for the rotary embedding), and everything else is as kvq_decode_attention
+ * over `tokens` (the fill level of the cache, which for KIVI fixes the split of
+ * every sequence's tokens between quantised pages and the ring; a sequence
+ * shorter than that reads the dequantised rows of the pages). Serving batches
+ * hold requests of different lengths: [KIVI] Key points (KIVI pairs with
+ * PagedAttention for production serving).
+ *   seq_tokens  device int64 [batch] (8-byte aligned), read by the kernels; each value is
+ *               clamped to [1, tokens] on the device (the host cannot check it)
+ *   workspace   as for kvq_decode_attention over `tokens` (same size)
+ * Other arguments, requirements and errors as kvq_decode_attention;
+ * seq_tokens == NULL is KVQ_ERR_NULL. */
+KVQ_API int32_t kvq_decode_attention_ragged(const kvq_config* cfg, const void* cache,
+                                    int32_t layer, int64_t tokens,
+                                    const int64_t* seq_tokens, const void* q,
+                                    const float* k_scale, const float* v_scale,
+                                    float* out, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 KVQ_API const char* kvq_status_string(int32_t status);
 

@@ -45,6 +45,7 @@ struct DecodeParams {
   float* partials;
   int64_t slab_bytes, page_bytes, ring_base, ring_slots;
   int64_t T, q_tokens;  // cached tokens; tokens held in pages
+  const int64_t* seq_tokens;   // ragged batch: per-sequence token counts (device), or null
   int32_t n_pages, items, splits;
   int32_t kv_heads, q_heads;
   int32_t off_kc, off_ks, off_kz, off_vc, off_vs, off_vz;
@@ -118,6 +119,18 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   const bool rope = p.rope_theta > 0.0;
   const uint8_t* slab = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes;
   float* wq = scratch + wave * QROWS * D;
+  // tokens this sequence attends to (ragged batch) and its pages and items:
+  // shorter than the quantised part, it reads only the pages it reaches
+  const int64_t Tb = seq_len(p.seq_tokens, b, p.T);
+  int32_t n_pages = p.n_pages, items = p.items;
+  if (p.seq_tokens) {
+    if (Tb <= p.q_tokens) {
+      n_pages = static_cast<int32_t>((Tb + kPage - 1) / kPage);
+      items = n_pages;
+    } else {
+      items = n_pages + static_cast<int32_t>((Tb - p.q_tokens + kPage - 1) / kPage);
+    }
+  }
 
   // ---- stage the GQA group's query: rotate at T-1, scale ----------------------
   if (rope) {
@@ -134,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
       float x0 = load_elem(p.q, base, p.q_bf16);
       float x1 = load_elem(p.q, base + 1, p.q_bf16);
       if (rope) {
-        const double ang = static_cast<double>(p.T - 1) * (w2pi[pr] * 6.283185307179586);
+        const double ang = static_cast<double>(Tb - 1) * (w2pi[pr] * 6.283185307179586);
         const double sn = sin(ang), cn = cos(ang);
         const double y0 = x0 * cn - x1 * sn, y1 = x0 * sn + x1 * cn;
         x0 = static_cast<float>(y0);
@@ -147,8 +160,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   __syncthreads();
 
   // ---- item range of this split -------------------------------------------
-  const int i0 = static_cast<int>(static_cast<int64_t>(split) * p.items / p.splits);
-  const int i1 = static_cast<int>(static_cast<int64_t>(split + 1) * p.items / p.splits);
+  const int i0 = static_cast<int>(static_cast<int64_t>(split) * items / p.splits);
+  const int i1 = static_cast<int>(static_cast<int64_t>(split + 1) * items / p.splits);
   const int rounds = (i1 - i0 + kWaves - 1) / kWaves;
 
   float m[HG], l_l[HG], z_l[HG], o[HG][CPL];
@@ -164,11 +177,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   for (int r = 0; r < rounds; ++r) {
     const int item = i0 + r * kWaves + wave;
     const bool active = item < i1;
-    const bool is_page = item < p.n_pages;
+    const bool is_page = item < n_pages;
     const uint8_t* pg = slab + static_cast<int64_t>(item) * p.page_bytes;
     const int64_t t_first = is_page ? static_cast<int64_t>(item) * kPage
-                                    : p.q_tokens + static_cast<int64_t>(item - p.n_pages) * kPage;
-    const int n_valid = static_cast<int>(p.T - t_first < kPage ? p.T - t_first : kPage);
+                                    : p.q_tokens + static_cast<int64_t>(item - n_pages) * kPage;
+    const int n_valid = static_cast<int>(Tb - t_first < kPage ? Tb - t_first : kPage);
 
     __syncthreads();
     // ---- prologue: per-page key scales ----------------------------------------
@@ -356,7 +369,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float* rw = red + (w * HG + g) * (D + 2);
-      const float e = exp2f(rw[0] - M);  // empty wave: 2^-inf = 0
+      const float e = exp2_rel(rw[0], M);  // empty wave (or split): 0
       so = fmaf(e, rw[2 + c], so);
       sl = fmaf(e, rw[1], sl);
     }
@@ -386,11 +399,11 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* partials,
   float M = -INFINITY;
   for (int s = 0; s < splits; ++s) M = fmaxf(M, part[s * (D + 2)]);
   float L = 0.f;
-  for (int s = 0; s < splits; ++s) L = fmaf(exp2f(part[s * (D + 2)] - M), part[s * (D + 2) + 1], L);
+  for (int s = 0; s < splits; ++s) L = fmaf(exp2_rel(part[s * (D + 2)], M), part[s * (D + 2) + 1], L);
   for (int c = threadIdx.x; c < D; c += 64) {
     float acc = 0.f;
     for (int s = 0; s < splits; ++s)
-      acc = fmaf(exp2f(part[s * (D + 2)] - M), part[s * (D + 2) + 2 + c], acc);
+      acc = fmaf(exp2_rel(part[s * (D + 2)], M), part[s * (D + 2) + 2 + c], acc);
     out[static_cast<int64_t>(bh) * D + c] = acc / L;
   }
 }
@@ -457,6 +470,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   p.ring_base = g.pages_per_slab * g.page_bytes;
   p.ring_slots = g.ring_slots > 0 ? g.ring_slots : 1;
   p.T = a.tokens;
+  p.seq_tokens = a.seq_tokens;
   if (g.scheme == KVQ_KIVI) {
     p.q_tokens = kivi_quantised(a.tokens, g.residual);
     p.n_pages = static_cast<int32_t>(p.q_tokens / kPage);

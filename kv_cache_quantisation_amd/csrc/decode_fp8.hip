@@ -61,6 +61,7 @@ struct Fp8Params {
   int* counters;                  // one per (sequence, KV head), zero between calls
   int64_t slab_bytes, page_bytes;
   int64_t T;
+  const int64_t* seq_tokens;      // ragged batch: per-sequence token counts (device), or null
   int32_t n_pages, last_valid;    // pages holding tokens; tokens in the last one
   int32_t splits;
   int32_t kv_heads, q_heads;
@@ -123,8 +124,15 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   const float ks_h = E5 ? p.k_scale[h] : 1.0f;   // applied to the scores (E5M2)
 
   // pages of this block, every kWaves-th one per wave
-  const int pg0 = static_cast<int>(static_cast<int64_t>(split) * p.n_pages / p.splits);
-  const int pg1 = static_cast<int>(static_cast<int64_t>(split + 1) * p.n_pages / p.splits);
+  // pages this sequence attends to (ragged batch: its own token count)
+  int32_t n_pages = p.n_pages, last_valid = p.last_valid;
+  if (p.seq_tokens) {
+    const int64_t Tb = seq_len(p.seq_tokens, b, p.T);
+    n_pages = static_cast<int32_t>((Tb + kPage - 1) / kPage);
+    last_valid = static_cast<int32_t>(Tb - static_cast<int64_t>(n_pages - 1) * kPage);
+  }
+  const int pg0 = static_cast<int>(static_cast<int64_t>(split) * n_pages / p.splits);
+  const int pg1 = static_cast<int>(static_cast<int64_t>(split + 1) * n_pages / p.splits);
   const int n_mine = pg0 + wave < pg1 ? (pg1 - pg0 - wave + kWaves - 1) / kWaves : 0;
 
   auto issue_page = [&](int k) {
@@ -310,7 +318,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
     }
     __builtin_amdgcn_wave_barrier();
     const int page = pg0 + wave + kWaves * k;
-    process_page(wbuf + (k % PG::NBUF) * PG::BYTES, page == p.n_pages - 1 ? p.last_valid : kPage, cur);
+    process_page(wbuf + (k % PG::NBUF) * PG::BYTES, page == n_pages - 1 ? last_valid : kPage, cur);
   };
 #pragma unroll 1
   for (int k = 0; k < n_mine; k += 2) {
@@ -381,7 +389,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
     float so = 0.f, sl = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float e = fast_exp2(R(w, hh)[0] - M);   // idle wave: m = -inf -> 0
+      const float e = exp2_rel(R(w, hh)[0], M);   // idle wave (or block): 0
       so = fmaf(e, R(w, hh)[2 + c], so);
       sl = fmaf(e, R(w, hh)[1], sl);
     }
@@ -429,12 +437,12 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) bm = s0 + k < p.splits ? fmaxf(bm, mv[k]) : bm;
       const float Mn = fmaxf(M, bm);
-      const float a = fast_exp2(M - Mn);
+      const float a = exp2_rel(M, Mn);
       so *= a;
       sl *= a;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float e = s0 + k < p.splits ? fast_exp2(mv[k] - Mn) : 0.f;
+        const float e = s0 + k < p.splits ? exp2_rel(mv[k], Mn) : 0.f;
         sl = fmaf(e, lv[k], sl);
         so = fmaf(e, ov[k], so);
       }
@@ -504,6 +512,7 @@ hipError_t launch_fp8_mfma(const DecodeArgs& a, hipStream_t st) {
   p.slab_bytes = g.slab_bytes;
   p.page_bytes = g.page_bytes;
   p.T = a.tokens;
+  p.seq_tokens = a.seq_tokens;
   p.n_pages = static_cast<int32_t>((a.tokens + kPage - 1) / kPage);
   p.last_valid = static_cast<int32_t>(a.tokens - static_cast<int64_t>(p.n_pages - 1) * kPage);
   p.splits = fp8_mfma_splits(g, a.tokens, a.requested_splits);

@@ -74,6 +74,7 @@ struct MfmaParams {
   int* counters;                  // one per (sequence, KV head), zero between calls
   int64_t slab_bytes, page_bytes, ring_base, ring_slots;
   int64_t T, q_tokens;            // cached tokens; tokens held in pages
+  const int64_t* seq_tokens;      // ragged batch: per-sequence token counts (device), or null
   int32_t n_pages, n_steps;       // quantised pages; residual tokens in 8-token steps
   int32_t splits;                 // blocks per (sequence, KV head)
   int32_t kv_heads, q_heads;
@@ -209,7 +210,7 @@ __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* 
     float so = 0.f, sl = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float e = fast_exp2(R(w, hh)[0] - M);   // idle wave: m = -inf -> 0
+      const float e = exp2_rel(R(w, hh)[0], M);   // idle wave (or block): 0
       so = fmaf(e, R(w, hh)[2 + c], so);
       sl = fmaf(e, R(w, hh)[1], sl);
     }
@@ -276,12 +277,12 @@ __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* 
 #pragma unroll
         for (int k = 0; k < 8; ++k) bm = s0 + k < p.splits ? fmaxf(bm, mv[e][k]) : bm;
         const float Mn = fmaxf(M[e], bm);
-        const float a = fast_exp2(M[e] - Mn);
+        const float a = exp2_rel(M[e], Mn);
         so[e] *= a;
         sl[e] *= a;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const float w8 = s0 + k < p.splits ? fast_exp2(mv[e][k] - Mn) : 0.f;
+          const float w8 = s0 + k < p.splits ? exp2_rel(mv[e][k], Mn) : 0.f;
           sl[e] = fmaf(w8, lv[e][k], sl[e]);
           so[e] = fmaf(w8, ov[e][k], so[e]);
         }
@@ -377,6 +378,19 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   const int j = lane & 15, g = lane >> 4;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const uint8_t* slab = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes;
+  // tokens this sequence attends to (ragged batch) and its pages and
+  // residual steps: shorter than the quantised part, it reads only the pages
+  // it reaches, the last perhaps in part
+  const int64_t Tb = seq_len(p.seq_tokens, b, p.T);
+  int32_t n_pages = p.n_pages, n_steps = p.n_steps;
+  if (p.seq_tokens) {
+    if (Tb <= p.q_tokens) {
+      n_pages = static_cast<int32_t>((Tb + kPage - 1) / kPage);
+      n_steps = 0;
+    } else {
+      n_steps = static_cast<int32_t>((Tb - p.q_tokens + 7) / 8);
+    }
+  }
   uint8_t* wbuf = arena + wave * WAVE_LDS;
   uint32_t (*frag)[4] = reinterpret_cast<uint32_t (*)[4]>(wbuf + PG::NBUF * PG::BYTES);
 
@@ -431,8 +445,8 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   // Block `split` takes a contiguous range of pages; its waves take every
   // NW-th page of that range.
   const int waves_total = p.splits * NW;
-  const int pg0 = static_cast<int>(static_cast<int64_t>(split) * p.n_pages / p.splits);
-  const int pg1 = static_cast<int>(static_cast<int64_t>(split + 1) * p.n_pages / p.splits);
+  const int pg0 = static_cast<int>(static_cast<int64_t>(split) * n_pages / p.splits);
+  const int pg1 = static_cast<int>(static_cast<int64_t>(split + 1) * n_pages / p.splits);
   const int n_mine = pg0 + wave < pg1 ? (pg1 - pg0 - wave + NW - 1) / NW : 0;
 
   float qreg[REPS][8];   // this lane's fold units of q (set once q is staged)
@@ -447,7 +461,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   // the relative position)
   auto rotate_q = [&](int64_t t0) {
     if (lane < D / 2) {
-      const double turns = static_cast<double>(p.T - 1 - t0) * w2pi[lane];
+      const double turns = static_cast<double>(Tb - 1 - t0) * w2pi[lane];
       float sn, cs;
       sincospif(2.0f * static_cast<float>(turns - floor(turns)), &sn, &cs);
 #pragma unroll
@@ -617,6 +631,13 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
     }
     }   // rotary / plain keys
 
+    if (t0 + kPage > Tb) {   // ragged batch: the sequence ends inside this page
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (t0 + tile_tok<ROPE>(mt, 4 * g + r) >= Tb) s[4 * mt + r] = -INFINITY;
+    }
     softmax_update(s, std::integral_constant<int, 8>{});
     // per-token value scale and offset of this lane's tokens tile_tok(mt, 4g + r)
     constexpr int VT0 = ROPE ? 16 : 32, VT1 = ROPE ? 64 : 16;
@@ -707,7 +728,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   constexpr int RSTEP = 8;                  // tokens per residual step
   auto issue_step = [&](int hs) -> int {    // returns the copies issued
     const int64_t t0 = p.q_tokens + static_cast<int64_t>(hs) * RSTEP;
-    const int nv = static_cast<int>(p.T - t0 < RSTEP ? p.T - t0 : RSTEP);
+    const int nv = static_cast<int>(Tb - t0 < RSTEP ? Tb - t0 : RSTEP);
     const int row_in = lane / LPR, col_b = (lane % LPR) * 16;
     const int slots = static_cast<int>(p.ring_slots);
     const int slot0 = static_cast<int>(t0 % p.ring_slots);
@@ -751,7 +772,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   // tile rows (tokens) 8..15 of a step are masked; key rows repeat rows 0..7
   auto process_step = [&](int hs) {
     const int64_t t0 = p.q_tokens + static_cast<int64_t>(hs) * RSTEP;
-    const int nv = static_cast<int>(p.T - t0 < RSTEP ? p.T - t0 : RSTEP);
+    const int nv = static_cast<int>(Tb - t0 < RSTEP ? Tb - t0 : RSTEP);
     float sc[4];
     if constexpr (ROPE) {
       // key rows rotated by their position in the step, fp32 product as for pages
@@ -831,7 +852,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
     for (int off = 0; off < q_bytes; off += 1024)
       if (off + lane * 16 < q_bytes) dma16(qsrc + off + lane * 16, lds_addr(&qs[0][0]) + off);
   }
-  const bool has_step = my_wave < p.n_steps;
+  const bool has_step = my_wave < n_steps;
   if (has_step) after_q += issue_step(my_wave);
   if (n_mine > 0) {
     issue_page(0);
@@ -929,7 +950,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
 
   // ---- any further residual steps of this wave (when steps outnumber waves) --
 #pragma unroll 1
-  for (int hs = my_wave + waves_total; hs < p.n_steps; hs += waves_total) {
+  for (int hs = my_wave + waves_total; hs < n_steps; hs += waves_total) {
     wait_lds();
     __builtin_amdgcn_wave_barrier();
     issue_step(hs);
@@ -1032,9 +1053,20 @@ __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
   const uint8_t* slab = p.layer_base + static_cast<int64_t>(unit) * p.slab_bytes;
   uint8_t* wbuf = arena + wave * WAVE_LDS;
   uint8_t* wring = wbuf;
+  // tokens this sequence attends to (ragged batch), its pages and steps
+  const int64_t Tb = seq_len(p.seq_tokens, b, p.T);
+  int32_t n_pages = p.n_pages, n_steps = p.n_steps;
+  if (p.seq_tokens) {
+    if (Tb <= p.q_tokens) {
+      n_pages = static_cast<int32_t>((Tb + kPage - 1) / kPage);
+      n_steps = 0;
+    } else {
+      n_steps = static_cast<int32_t>((Tb - p.q_tokens + 7) / 8);
+    }
+  }
 
-  const int pg0 = static_cast<int>(static_cast<int64_t>(split) * p.n_pages / p.splits);
-  const int pg1 = static_cast<int>(static_cast<int64_t>(split + 1) * p.n_pages / p.splits);
+  const int pg0 = static_cast<int>(static_cast<int64_t>(split) * n_pages / p.splits);
+  const int pg1 = static_cast<int>(static_cast<int64_t>(split + 1) * n_pages / p.splits);
   const int n_mine = pg0 + wave < pg1 ? (pg1 - pg0 - wave + NW - 1) / NW : 0;
   const int waves_total = p.splits * NW;
   const int my_wave = (NW - 1 - wave) * p.splits + split;
@@ -1054,7 +1086,7 @@ __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
   constexpr int RPI = 64 / LPR;
   auto issue_step = [&](int hs) -> int {
     const int64_t t0 = p.q_tokens + static_cast<int64_t>(hs) * RSTEP;
-    const int nv = static_cast<int>(p.T - t0 < RSTEP ? p.T - t0 : RSTEP);
+    const int nv = static_cast<int>(Tb - t0 < RSTEP ? Tb - t0 : RSTEP);
     const int row_in = lane / LPR, col_b = (lane % LPR) * 16;
     const int slots = static_cast<int>(p.ring_slots);
     const int slot0 = static_cast<int>(t0 % p.ring_slots);
@@ -1084,7 +1116,7 @@ __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
     for (int off = 0; off < q_bytes; off += 1024)
       if (off + lane * 16 < q_bytes) dma16(qsrc + off + lane * 16, lds_addr(&qs[0][0]) + off);
   }
-  const bool has_step = my_wave < p.n_steps;
+  const bool has_step = my_wave < n_steps;
   if (has_step) {
     after_q += issue_step(my_wave);
   } else if (n_mine > 0) {
@@ -1170,7 +1202,7 @@ __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
   };
   auto rotate_q = [&](int64_t t0) {
     if (lane < D / 2) {
-      const double turns = static_cast<double>(p.T - 1 - t0) * w2pi_l;
+      const double turns = static_cast<double>(Tb - 1 - t0) * w2pi_l;
       float sn, cs;
       sincospif(2.0f * static_cast<float>(turns - floor(turns)), &sn, &cs);
 #pragma unroll
@@ -1334,7 +1366,12 @@ __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
       }
       rotate_mfma(y, part, c);
     }
-    const floatx4 w = softmax(finish_scores(c));
+    floatx4 sc = finish_scores(c);
+    if (t0 + kPage > Tb) {   // ragged batch: the sequence ends inside this page
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[r] = t0 + 4 * ((lane >> 2) & 7) + r < Tb ? sc[r] : -INFINITY;
+    }
+    const floatx4 w = softmax(sc);
     // P' = p * s_t; sums of p and p * z_t (lanes < 32 own the tokens)
     const int t0q = 4 * ((lane >> 2) & 7);
     const float4 vs = *reinterpret_cast<const float4*>(pg + PG::OFF_VS + 4 * t0q);
@@ -1361,7 +1398,7 @@ __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
   // residual step: tokens 0..7 of the step are lanes with tk < 8
   auto process_step = [&](int hs) {
     const int64_t t0 = p.q_tokens + static_cast<int64_t>(hs) * RSTEP;
-    const int nv = static_cast<int>(p.T - t0 < RSTEP ? p.T - t0 : RSTEP);
+    const int nv = static_cast<int>(Tb - t0 < RSTEP ? Tb - t0 : RSTEP);
     rotate_q(t0);
     floatx4 c[4];
 #pragma unroll
@@ -1398,7 +1435,7 @@ __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
 
   // ---- residual steps first (all of this wave's, in the page buffers), then
   // the pages; a wave with steps requests its first page after them ------------
-  for (int hs = my_wave; hs < p.n_steps; hs += waves_total) {
+  for (int hs = my_wave; hs < n_steps; hs += waves_total) {
     if (hs != my_wave) {
       wait_lds();
       __builtin_amdgcn_wave_barrier();
@@ -1534,6 +1571,7 @@ hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t st) {
   p.ring_base = g.pages_per_slab * g.page_bytes;
   p.ring_slots = g.ring_slots;
   p.T = a.tokens;
+  p.seq_tokens = a.seq_tokens;
   p.q_tokens = static_cast<int64_t>(pl.pages) * kPage;
   p.n_pages = pl.pages;
   p.n_steps = pl.chunks;

@@ -264,10 +264,11 @@ int32_t kvq_quantize_append(const kvq_config* cfg, void* cache, int32_t layer,
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
 }
 
-int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache, int32_t layer,
-                             int64_t tokens, const void* q, const float* k_scale,
-                             const float* v_scale, float* out, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+namespace {
+int32_t decode_call(const kvq_config* cfg, const void* cache, int32_t layer, int64_t tokens,
+                    const int64_t* seq_tokens, const void* q, const float* k_scale,
+                    const float* v_scale, float* out, void* workspace, size_t workspace_bytes,
+                    void* stream) {
   if (!cfg) return KVQ_ERR_NULL;
   Geometry g;
   const int32_t st = kvq::make_geometry(*cfg, &g);
@@ -288,6 +289,7 @@ int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache, int32_t l
   a.layer_base = static_cast<const uint8_t*>(cache) +
                  static_cast<int64_t>(layer) * cfg->batch * cfg->kv_heads * g.slab_bytes;
   a.tokens = tokens;
+  a.seq_tokens = seq_tokens;
   a.q = q;
   a.q_dtype = cfg->q_dtype;
   a.k_scale = k_scale;
@@ -302,6 +304,26 @@ int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache, int32_t l
   a.requested_splits = cfg->num_splits;
   const hipError_t e = kvq::launch_decode(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
+}
+}  // namespace
+
+int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache, int32_t layer,
+                             int64_t tokens, const void* q, const float* k_scale,
+                             const float* v_scale, float* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return decode_call(cfg, cache, layer, tokens, nullptr, q, k_scale, v_scale, out, workspace,
+                     workspace_bytes, stream);
+}
+
+int32_t kvq_decode_attention_ragged(const kvq_config* cfg, const void* cache, int32_t layer,
+                                    int64_t tokens, const int64_t* seq_tokens, const void* q,
+                                    const float* k_scale, const float* v_scale, float* out,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!seq_tokens) return KVQ_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(seq_tokens) & 7u) != 0)
+    return KVQ_ERR_INVALID;
+  return decode_call(cfg, cache, layer, tokens, seq_tokens, q, k_scale, v_scale, out, workspace,
+                     workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -50,6 +50,14 @@ __device__ __forceinline__ uint32_t quant_asym_rcp(float x, float mn, const floa
   return static_cast<uint32_t>(__builtin_amdgcn_fmed3f(q, 0.0f, levels));
 }
 
+// Weight 2^(m - M) of a partial softmax state with running max m against the
+// reference max M; 0 when M is -inf, i.e. when no token was seen at all (a
+// wave, a block or a split without tokens, which a ragged batch can leave),
+// where 2^(-inf - -inf) would be NaN.
+__device__ __forceinline__ float exp2_rel(float m, float M) {
+  return M == -INFINITY ? 0.0f : exp2f(m - M);
+}
+
 // Symmetric code: clamp(rint(x / s), -Q, Q), 0 when s == 0; returned as the
 // low b bits of its two's complement.
 __device__ __forceinline__ uint32_t quant_sym(float x, float s, float qmax, uint32_t mask) {

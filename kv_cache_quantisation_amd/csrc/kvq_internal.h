@@ -36,6 +36,13 @@ struct Geometry {
 // Fills g from a validated config. Returns KVQ_OK or a negative status.
 int32_t make_geometry(const kvq_config& cfg, Geometry* g);
 
+// Tokens sequence b attends to: seq[b] clamped to [1, T], or T without seq.
+__device__ inline int64_t seq_len(const int64_t* seq, int b, int64_t T) {
+  if (!seq) return T;
+  const int64_t t = seq[b];
+  return t < 1 ? 1 : (t > T ? T : t);
+}
+
 // Number of quantised tokens of a KIVI cache holding T tokens.
 __host__ __device__ inline int64_t kivi_quantised(int64_t T, int32_t R) {
   const int64_t over = T - R;
@@ -59,6 +66,7 @@ struct DecodeArgs {
   Geometry g;
   const uint8_t* layer_base;
   int64_t tokens;
+  const int64_t* seq_tokens;  // device [B] per-sequence token counts, or null (all = tokens)
   const void* q;            // [B][Hq][d] q_dtype
   int32_t q_dtype;
   const float* k_scale;     // FP8 only

@@ -20,7 +20,7 @@ KVQ_F32, KVQ_BF16 = 0, 1
 KVQ_BYTES_FORMULA, KVQ_BYTES_CACHE, KVQ_BYTES_WORKSPACE = 0, 1, 2
 
 SYMBOLS = ("kvq_cache_bytes", "kvq_quantize_append", "kvq_decode_attention",
-           "kvq_status_string", "kvq_abi_version")
+           "kvq_decode_attention_ragged", "kvq_status_string", "kvq_abi_version")
 
 
 class KvqError(RuntimeError):
@@ -85,6 +85,9 @@ def lib():
         L.kvq_quantize_append.restype = I32
         L.kvq_decode_attention.argtypes = [cfgp, P, I32, I64, P, P, P, P, P, ctypes.c_size_t, P]
         L.kvq_decode_attention.restype = I32
+        L.kvq_decode_attention_ragged.argtypes = [cfgp, P, I32, I64, P, P, P, P, P, P,
+                                                  ctypes.c_size_t, P]
+        L.kvq_decode_attention_ragged.restype = I32
         L.kvq_status_string.argtypes = [I32]
         L.kvq_status_string.restype = ctypes.c_char_p
         L.kvq_abi_version.argtypes = []
@@ -144,6 +147,21 @@ def kvq_decode_attention(cfg, cache, layer, tokens, q, out, workspace, workspace
                                     workspace_bytes, _stream(stream))
     if check and st != KVQ_OK:
         raise KvqError(st, "kvq_decode_attention")
+    return st
+
+
+def kvq_decode_attention_ragged(cfg, cache, layer, tokens, seq_tokens, q, out, workspace,
+                                workspace_bytes=None, k_scale=None, v_scale=None, stream=None,
+                                check=True):
+    """seq_tokens: device int64 tensor [batch] of per-sequence token counts."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = lib().kvq_decode_attention_ragged(ctypes.byref(cfg), _ptr(cache), layer, tokens,
+                                           _ptr(seq_tokens), _ptr(q), _ptr(k_scale),
+                                           _ptr(v_scale), _ptr(out), _ptr(workspace),
+                                           workspace_bytes, _stream(stream))
+    if check and st != KVQ_OK:
+        raise KvqError(st, "kvq_decode_attention_ragged")
     return st
 
 

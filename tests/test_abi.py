@@ -226,3 +226,23 @@ def test_call_validation():
     need = kvq.kvq_cache_bytes(c, 4096, kvq.KVQ_BYTES_WORKSPACE)
     assert de(p, f, 0, 4096, f, None, None, f, f, need - 1, None) == kvq.KVQ_ERR_WORKSPACE
     assert de(p, f, 3, 8, f, None, None, f, f, big, None) == kvq.KVQ_ERR_INVALID    # layer
+
+
+def test_ragged_call_validation():
+    """The ragged decode validates as kvq_decode_attention does, and needs its
+    per-sequence counts (a device array: present and 8-byte aligned)."""
+    L = kvq.lib()
+    c = cfg()
+    p = ctypes.byref(c)
+    f = 1 << 20
+    big = 1 << 30
+    rd = L.kvq_decode_attention_ragged
+    assert rd(p, f, 0, 8, None, f, None, None, f, f, big, None) == kvq.KVQ_ERR_NULL
+    assert rd(p, f, 0, 8, f + 4, f, None, None, f, f, big, None) == kvq.KVQ_ERR_INVALID
+    assert rd(None, f, 0, 8, f, f, None, None, f, f, big, None) == kvq.KVQ_ERR_NULL
+    assert rd(p, f, 0, 0, f, f, None, None, f, f, big, None) == kvq.KVQ_ERR_INVALID
+    assert rd(p, f, 0, 4097, f, f, None, None, f, f, big, None) == kvq.KVQ_ERR_CAPACITY
+    assert rd(p, f, 0, 8, f, None, None, None, f, f, big, None) == kvq.KVQ_ERR_NULL
+    assert rd(p, f, 3, 8, f, f, None, None, f, f, big, None) == kvq.KVQ_ERR_INVALID
+    need = kvq.kvq_cache_bytes(c, 4096, kvq.KVQ_BYTES_WORKSPACE)
+    assert rd(p, f, 0, 4096, f, f, None, None, f, f, need - 1, None) == kvq.KVQ_ERR_WORKSPACE
