@@ -53,9 +53,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 # kernel sources they were taken with (SHA-256 over DECODE_SOURCES); after any
 # change to those, `traffic` is reported as null until they are taken again.
 COUNTERS = {
-    "kivi2": {"context": 4119, "fetch_kib": 31146.875, "write_kib": 892.0,
+    "kivi2": {"context": 4119, "fetch_kib": 31150.53125, "write_kib": 892.0,
               "fetch_scale": 262144 / 131084, "write_scale": 1.0,
-              "sources_sha256": "8c3dbdff8b04cdedeca504d21825275e264b279b9df363e4daf790b8855d3241"},
+              "sources_sha256": "5b30301bcd1214bbffb540339181d114dac00c45f48cdb11a6a8f59f324c535b"},
 }
 DECODE_SOURCES = ["decode_mfma.hip", "kvq_device.h", "kvq_internal.h", "kvq_wave.h"]
 
@@ -98,6 +98,24 @@ def decode_bytes(w, T, in_bytes=2, q_bytes=2):
     hg = w.q_heads // w.kv_heads
     per_unit += hg * w.head_dim * (q_bytes + 4)
     return w.batch * w.kv_heads * per_unit
+
+
+def ragged_decode_bytes(w, T, lens, in_bytes=2, q_bytes=2):
+    """Algorithmic bytes of a ragged decode over a T-token KIVI cache where
+    sequence b attends to its first lens[b] tokens: the pages it reaches (a
+    partial last page is read whole: its scales and offsets cover the group),
+    its ring rows below lens[b], the query and the output."""
+    page = kivi_page_bytes(w)
+    q = kivi_q(T, w.residual)
+    hg = w.q_heads // w.kv_heads
+    total = 0
+    for Tb in lens:
+        if Tb <= q:
+            per_unit = -(-Tb // 32) * page
+        else:
+            per_unit = (q // 32) * page + (Tb - q) * 2 * w.head_dim * in_bytes
+        total += w.kv_heads * (per_unit + hg * w.head_dim * (q_bytes + 4))
+    return total
 
 
 def append_bytes(w, T_old, n, in_bytes=2):
@@ -313,6 +331,29 @@ def gpu_bench(args, w):
     torch.cuda.synchronize()
     avg_us = a.elapsed_time(b) * 1e3 / (n_rep * L)
     graph = graph_replay(cfg, cache, ws, qs, outs, news, L, T_end, n_rep)
+
+    # ragged batch over the same caches: sequence b attends to its first
+    # lens[b] tokens, lens uniform in [T/2, T] (seeded)
+    gen = torch.Generator().manual_seed(0)
+    lens = torch.randint(T_end // 2, T_end + 1, (w.batch,), generator=gen).tolist()
+    seq = torch.tensor(lens, dtype=torch.int64, device=dev)
+    for layer in range(L):
+        kvq.kvq_decode_attention_ragged(cfg, cache, layer, T_end, seq, qs[layer], outs[layer], ws,
+                                        stream=stream)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(n_rep):
+        for layer in range(L):
+            kvq.kvq_decode_attention_ragged(cfg, cache, layer, T_end, seq, qs[layer], outs[layer],
+                                            ws, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ragged_us = a.elapsed_time(b) * 1e3 / (n_rep * L)
+    ragged_b = ragged_decode_bytes(w, T_end, lens)
+    ragged = {"avg_launch_us": round(ragged_us, 3), "bytes_per_launch": ragged_b,
+              "gbs": round(ragged_b / (ragged_us * 1e-6) / 1e9, 1),
+              "lengths": f"per sequence uniform in [{T_end // 2}, {T_end}] (seed 0); "
+                         f"mean {sum(lens) / len(lens):.0f}"}
     per_launch = decode_bytes(w, T_end)
     achieved = per_launch / (avg_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -326,6 +367,7 @@ def gpu_bench(args, w):
         "ms_per_step": total_ms / K, "gbs": gbs, "append_tps": append_tps,
         "prefill_ms_per_layer": prefill_ms, "prefill_gbs": prefill_bytes / (prefill_ms * 1e-3) / 1e9,
         "roofline": roofline, "cache_bytes": int(cache.numel()), "graph": graph,
+        "ragged": ragged,
     }
 
 
@@ -513,6 +555,7 @@ def main():
         "append_prefill_gbs": round(r["prefill_gbs"], 1),
         "roofline": r["roofline"],
         "graph_replay": r["graph"],
+        "ragged_decode": r["ragged"],
         "bf16_cache_baseline": {
             "decode_us": round(base_us, 3), "context": r["roofline"]["context"],
             "speedup_of_quantised_decode": round(base_us / r["roofline"]["avg_launch_us"], 2),
