@@ -214,3 +214,51 @@ class OracleCache:
                 qb = rope.rotate(qb, np.full(qb.shape[:-1], Tb - 1), rope_theta)
             out[b] = attention.decode(qb, kb, vb, sm_scale)[0]
         return out
+
+
+class RaggedCache:
+    """A batch whose sequences hold different numbers of tokens (a ragged
+    batch: the serving case of the KIVI page's Key points, where KIVI pairs
+    with PagedAttention): one single-sequence OracleCache per sequence, each
+    with its own fill level T_b -- and so, for KIVI, its own split of tokens
+    between quantised pages [0, q(T_b)) and the ring [q(T_b), T_b). The byte
+    image is the slabs of the per-sequence caches in (layer, sequence, KV head)
+    order; decode attends each sequence to its own T_b tokens, its query at
+    T_b - 1 (test infrastructure only)."""
+
+    def __init__(self, scheme, bits, layers, batch, kv_heads, head_dim, capacity, residual=0,
+                 in_dtype="bf16", v_bits=None):
+        self.layers, self.batch, self.kv_heads = layers, batch, kv_heads
+        self.seqs = [OracleCache(scheme, bits, layers, 1, kv_heads, head_dim, capacity,
+                                 residual=residual, in_dtype=in_dtype, v_bits=v_bits)
+                     for _ in range(batch)]
+
+    def tokens(self, layer):
+        return [c.tokens(layer) for c in self.seqs]
+
+    def append(self, layer, b, k_new, v_new, k_scale=None, v_scale=None):
+        """Appends k_new, v_new [n, Hkv, d] (raw input values) to sequence b;
+        n = 0 leaves it unchanged."""
+        k_new, v_new = np.asarray(k_new), np.asarray(v_new)
+        if k_new.shape[0] == 0:
+            return
+        self.seqs[b].append(layer, k_new[None], v_new[None], k_scale, v_scale)
+
+    def cache_image(self):
+        """(bytes, mask) of the whole cache, slabs ordered (layer, seq, KV head)."""
+        bufs, masks = [], []
+        for layer in range(self.layers):
+            for b in range(self.batch):
+                for h in range(self.kv_heads):
+                    bb, mm = self.seqs[b].slab_image(layer, 0, h)
+                    bufs.append(bb)
+                    masks.append(mm)
+        return np.concatenate(bufs), np.concatenate(masks)
+
+    def decode(self, layer, q, sm_scale=None, rope_theta=0.0):
+        """q [B, Hq, d]: sequence b over its own T_b tokens."""
+        q = np.asarray(q, np.float64)
+        out = np.zeros(q.shape)
+        for b in range(self.batch):
+            out[b] = self.seqs[b].decode(layer, q[b:b + 1], sm_scale, rope_theta)[0]
+        return out

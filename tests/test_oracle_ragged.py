@@ -95,3 +95,83 @@ def test_kivi_short_sequence_reads_quantised_rows():
     short = OracleCache(acc.KIVI, 2, 1, B, H, D, Tb, residual=64, in_dtype="f32")   # all in the ring
     short.append(0, k[:, :Tb], v[:, :Tb])
     assert np.max(np.abs(got - short.decode(0, q))) > 1e-3
+
+
+# ---- a ragged batch built by per-sequence appends (own fill levels) ----------
+
+from oracle.cache import RaggedCache  # noqa: E402
+
+
+def _history(scheme, T, seed):
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((B, T, H, D)).astype(np.float32)
+    v = rng.standard_normal((B, T, H, D)).astype(np.float32)
+    ks = vs = None
+    if scheme in (acc.FP8_E4M3, acc.FP8_E5M2):
+        ks = (np.abs(k).max(axis=(0, 1, 3)) / 448.0).astype(np.float32)
+        vs = (np.abs(v).max(axis=(0, 1, 3)) / 448.0).astype(np.float32)
+    return k, v, ks, vs
+
+
+@pytest.mark.parametrize("scheme,bits,R", [(acc.KIVI, 2, 16), (acc.KIVI, 4, 0), (acc.SYM_TOKEN, 4, 0),
+                                           (acc.FP8_E4M3, 8, 0), (acc.BF16_CACHE, 16, 0)])
+def test_ragged_equal_appends_equal_batch_cache(scheme, bits, R):
+    """Every sequence appending the same chunks gives the batch cache's bytes,
+    mask and decode, bit for bit."""
+    T = 130
+    k, v, ks, vs = _history(scheme, T, 11)
+    batch = OracleCache(scheme, bits, 1, B, H, D, 160, residual=R, in_dtype="f32")
+    rag = RaggedCache(scheme, bits, 1, B, H, D, 160, residual=R, in_dtype="f32")
+    t = 0
+    for n in (50, 1, 0, 79):
+        if n:
+            batch.append(0, k[:, t:t + n], v[:, t:t + n], ks, vs)
+        for b in range(B):
+            rag.append(0, b, k[b, t:t + n], v[b, t:t + n], ks, vs)
+        t += n
+    bb, bm = batch.cache_image()
+    rb, rm = rag.cache_image()
+    assert np.array_equal(bb, rb) and np.array_equal(bm, rm)
+    q = np.random.default_rng(2).standard_normal((B, HQ, D)).astype(np.float32)
+    for theta in (0.0, 10000.0):
+        assert np.array_equal(rag.decode(0, q, rope_theta=theta), batch.decode(0, q, rope_theta=theta))
+
+
+@pytest.mark.parametrize("scheme,bits", [(acc.SYM_TOKEN, 2), (acc.FP8_E5M2, 8), (acc.BF16_CACHE, 16)])
+def test_ragged_fill_equals_masked_prefix_for_per_token_schemes(scheme, bits):
+    """Per-token schemes: sequences filled to different lengths decode as the
+    prefixes of a cache filled to the longest (two independent
+    constructions: per-sequence caches vs one batch cache read in part)."""
+    T = 90
+    k, v, ks, vs = _history(scheme, T, 13)
+    lens = [5, 90, 33]
+    full = OracleCache(scheme, bits, 1, B, H, D, T, in_dtype="f32")
+    full.append(0, k, v, ks, vs)
+    rag = RaggedCache(scheme, bits, 1, B, H, D, T, in_dtype="f32")
+    for b, Tb in enumerate(lens):
+        rag.append(0, b, k[b, :Tb], v[b, :Tb], ks, vs)
+    assert rag.tokens(0) == lens
+    q = np.random.default_rng(4).standard_normal((B, HQ, D)).astype(np.float32)
+    for theta in (0.0, 500000.0):
+        assert np.array_equal(rag.decode(0, q, rope_theta=theta),
+                              full.decode(0, q, rope_theta=theta, seq_tokens=lens))
+
+
+def test_ragged_kivi_split_follows_each_fill_level():
+    """KIVI: a sequence filled to T_b keeps its newest T_b - q(T_b) tokens
+    exact in the ring, unlike the prefix of a longer cache (whose rows below
+    q(T) are quantised), so the two constructions differ there."""
+    T, R = 100, 8
+    k, v, ks, vs = _history(acc.KIVI, T, 17)
+    lens = [40, 100, 70]
+    rag = RaggedCache(acc.KIVI, 2, 1, B, H, D, T, residual=R, in_dtype="f32")
+    for b, Tb in enumerate(lens):
+        rag.append(0, b, k[b, :Tb], v[b, :Tb])
+    kh, vh = rag.seqs[0].dequantized(0)     # 40 tokens: q(40) = 32, 8 exact ring rows
+    assert np.array_equal(kh[0, :, 32:40], np.transpose(k[0, 32:40], (1, 0, 2)).astype(np.float64))
+    full = OracleCache(acc.KIVI, 2, 1, B, H, D, T, residual=R, in_dtype="f32")
+    full.append(0, k, v)
+    q = np.random.default_rng(6).standard_normal((B, HQ, D)).astype(np.float32)
+    got, pre = rag.decode(0, q), full.decode(0, q, seq_tokens=lens)
+    assert np.array_equal(got[1], pre[1])                 # full length: same cache
+    assert np.max(np.abs(got[0] - pre[0])) > 1e-4          # 40 of 100: different rows
