@@ -236,6 +236,30 @@ KVQ_API int32_t kvq_quantize_append(const kvq_config* cfg, void* cache, int32_t 
                             const float* k_scale, const float* v_scale,
                             void* stream);
 
+/* Quantize-append for a ragged batch: sequence b appends seq_new[b] tokens
+ * (rows 0 .. seq_new[b]-1 of its slice of k_new / v_new) after the
+ * seq_past[b] tokens it holds, each sequence keeping its own fill level (and,
+ * for KIVI, its own split between quantised pages and the ring). Serving
+ * batches hold requests of different lengths: [KIVI] Key points (KIVI pairs
+ * with PagedAttention for production serving).
+ *   seq_past,
+ *   seq_new   device int64 [batch] (8-byte aligned), read by the kernels; the
+ *             host cannot check them, so each sequence's counts are clamped on
+ *             the device to 0 <= past <= max_tokens and
+ *             0 <= new <= min(new_max, max_tokens - past)
+ *   new_max   rows per sequence in k_new / v_new (>= every seq_new[b]);
+ *             new_max == 0 is a no-op; new_max > max_tokens is KVQ_ERR_CAPACITY
+ *   k_new,
+ *   v_new     device [batch][new_max][kv_heads][head_dim], in_dtype
+ * Other arguments and errors as kvq_quantize_append. A call with every
+ * seq_past[b] = past and seq_new[b] = new_max writes the same bytes as
+ * kvq_quantize_append(past, new_max). */
+KVQ_API int32_t kvq_quantize_append_ragged(const kvq_config* cfg, void* cache, int32_t layer,
+                                   const int64_t* seq_past, const int64_t* seq_new,
+                                   int64_t new_max, const void* k_new, const void* v_new,
+                                   const float* k_scale, const float* v_scale,
+                                   void* stream);
+
 /* Decode attention over the `tokens` cached tokens of `layer`:
  *   out[b][h][:] = sum_t p_t * V^[t],  p = softmax_t(sm_scale * q[b][h].K^[t])
  * where K^, V^ are the dequantised cache and query head h reads KV head
@@ -258,19 +282,22 @@ KVQ_API int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache,
                              float* out, void* workspace,
                              size_t workspace_bytes, void* stream);
 
-/* Decode attention over a ragged batch: sequence b attends to its first
- * seq_tokens[b] cached tokens only, its query at position seq_tokens[b] - 1
- * (for the rotary embedding), and everything else is as kvq_decode_attention
- * over `tokens` (the fill level of the cache, which for KIVI fixes the split of
- * every sequence's tokens between quantised pages and the ring; a sequence
- * shorter than that reads the dequantised rows of the pages). Serving batches
- * hold requests of different lengths: [KIVI] Key points (KIVI pairs with
- * PagedAttention for production serving).
- *   seq_tokens  device int64 [batch] (8-byte aligned), read by the kernels; each value is
- *               clamped to [1, tokens] on the device (the host cannot check it)
+/* Decode attention over a ragged batch: sequence b holds seq_tokens[b]
+ * tokens (its own fill level, as appended by kvq_quantize_append_ragged; for
+ * KIVI its quantised pages are [0, q(seq_tokens[b])) and the rest sits in its
+ * ring) and attends to all of them, its query at position seq_tokens[b] - 1
+ * (for the rotary embedding). Everything else is as kvq_decode_attention.
+ * Serving batches hold requests of different lengths: [KIVI] Key points
+ * (KIVI pairs with PagedAttention for production serving).
+ *   tokens      bound on every seq_tokens[b] (<= max_tokens); the split plan
+ *               and the workspace size follow it
+ *   seq_tokens  device int64 [batch] (8-byte aligned), read by the kernels;
+ *               each value is clamped to [1, tokens] on the device (the host
+ *               cannot check it)
  *   workspace   as for kvq_decode_attention over `tokens` (same size)
  * Other arguments, requirements and errors as kvq_decode_attention;
- * seq_tokens == NULL is KVQ_ERR_NULL. */
+ * seq_tokens == NULL is KVQ_ERR_NULL. With every seq_tokens[b] = tokens the
+ * result is kvq_decode_attention's, bit for bit. */
 KVQ_API int32_t kvq_decode_attention_ragged(const kvq_config* cfg, const void* cache,
                                     int32_t layer, int64_t tokens,
                                     const int64_t* seq_tokens, const void* q,

@@ -36,12 +36,30 @@ struct AppendParams {
   const float* k_scale;
   const float* v_scale;
   int64_t slab_bytes, page_bytes, ring_base;  // ring_base = P * page_bytes
-  int64_t past, n;
-  int64_t first_page;                         // first page written by this launch
+  int64_t past, n;                            // tokens held before the call, appended
+  int64_t stride;                             // input rows per sequence (n, or the ragged bound)
+  const int64_t* seq_past;                    // ragged batch: per-sequence past and new
+  const int64_t* seq_new;                     //   counts (device), or null
+  int64_t capacity;                           // max_tokens
+  int32_t residual;                           // R (KIVI)
   int64_t ring_slots;
   int32_t kv_heads;
   int32_t off_kc, off_ks, off_kz, off_vc, off_vs, off_vz;
 };
+
+// Tokens sequence b held before the call and tokens it appends: the uniform
+// counts, or its own counts of a ragged batch, clamped so that every write
+// stays in its slab (0 <= past <= capacity, 0 <= n <= min(stride, capacity - past)).
+__device__ __forceinline__ void seq_counts(const AppendParams& p, int b, int64_t& past, int64_t& n) {
+  past = p.past;
+  n = p.n;
+  if (p.seq_past) {
+    const int64_t ps = p.seq_past[b], ns = p.seq_new[b];
+    past = ps < 0 ? 0 : (ps > p.capacity ? p.capacity : ps);
+    const int64_t room = p.capacity - past < p.stride ? p.capacity - past : p.stride;
+    n = ns < 0 ? 0 : (ns > room ? room : ns);
+  }
+}
 
 // Widens one 16-byte chunk of a token row (bf16 or f32) into an fp32 LDS row.
 template <int IB>
@@ -84,7 +102,11 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
 
   const int tid = threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
-  const int64_t page = p.first_page + blockIdx.x;
+  int64_t past, n;
+  seq_counts(p, b, past, n);
+  // pages this sequence flushes: [q(past), q(past + n)) / 32
+  const int64_t page = kivi_quantised(past, p.residual) / kPage + blockIdx.x;
+  if (page >= kivi_quantised(past + n, p.residual) / kPage) return;   // whole block
   uint8_t* slab = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes;
   uint8_t* pg = slab + page * p.page_bytes;
 
@@ -113,10 +135,10 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
       const int64_t t = t_page + r;
       const int slot = s0 + r >= slots ? s0 + r - slots : s0 + r;
       const uint8_t* ring = slab + p.ring_base + (static_cast<int64_t>(which) * p.ring_slots + slot) * ROW;
-      const int64_t j = t >= p.past ? t - p.past : 0;
+      const int64_t j = t >= past ? t - past : 0;
       const uint8_t* in = (which ? p.v_new : p.k_new) +
-                          ((static_cast<int64_t>(b) * p.n + j) * p.kv_heads + h) * ROW;
-      chunk[k] = *reinterpret_cast<const uint4*>((t < p.past ? ring : in) + (i % CHUNKS) * 16);
+                          ((static_cast<int64_t>(b) * p.stride + j) * p.kv_heads + h) * ROW;
+      chunk[k] = *reinterpret_cast<const uint4*>((t < past ? ring : in) + (i % CHUNKS) * 16);
     }
 #pragma unroll
     for (int k = 0; k < SPT; ++k) {
@@ -243,15 +265,20 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
 // ---- KIVI: copy tokens [t0, past+n) of the input into their ring slots --------
 // grid = (tokens, kv_heads, batch), one 16-byte chunk per thread
 template <int D, int IB>
-__global__ __launch_bounds__(64) void ring_write_kernel(AppendParams p, int64_t t0) {
+__global__ __launch_bounds__(64) void ring_write_kernel(AppendParams p) {
   constexpr int CHUNKS = D * IB / 16;
   const int h = blockIdx.y, b = blockIdx.z;
-  const int64_t t = t0 + blockIdx.x;
-  const int64_t j = t - p.past;
+  int64_t past, n;
+  seq_counts(p, b, past, n);
+  // tokens [max(q(past + n), past), past + n) stay in the ring
+  const int64_t q_new = kivi_quantised(past + n, p.residual);
+  const int64_t t = (q_new > past ? q_new : past) + blockIdx.x;
+  if (t >= past + n) return;
+  const int64_t j = t - past;
   const int64_t row_bytes = static_cast<int64_t>(D) * IB;
   uint8_t* slab = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes;
   const int64_t slot = t % p.ring_slots;
-  const int64_t in_off = ((static_cast<int64_t>(b) * p.n + j) * p.kv_heads + h) * row_bytes;
+  const int64_t in_off = ((static_cast<int64_t>(b) * p.stride + j) * p.kv_heads + h) * row_bytes;
   for (int i = threadIdx.x; i < 2 * CHUNKS; i += 64) {
     const int which = i / CHUNKS, c = i % CHUNKS;
     const uint8_t* src = (which ? p.v_new : p.k_new) + in_off + c * 16;
@@ -276,9 +303,12 @@ __global__ __launch_bounds__(kThreads) void token_append_kernel(AppendParams p) 
 
   const int tid = threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
-  const int64_t page = p.first_page + blockIdx.x;
-  const int64_t end = p.past + p.n;
-  const int lo = static_cast<int>((p.past > page * kPage ? p.past : page * kPage) - page * kPage);
+  int64_t past, n;
+  seq_counts(p, b, past, n);
+  const int64_t page = past / kPage + blockIdx.x;
+  const int64_t end = past + n;
+  if (n == 0 || page > (end - 1) / kPage) return;   // whole block
+  const int lo = static_cast<int>((past > page * kPage ? past : page * kPage) - page * kPage);
   const int hi = static_cast<int>((end < page * kPage + kPage ? end : page * kPage + kPage) -
                                   page * kPage);
   uint8_t* slab = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes;
@@ -295,9 +325,9 @@ __global__ __launch_bounds__(kThreads) void token_append_kernel(AppendParams p) 
     const int i = tid + k * kThreads < nch ? tid + k * kThreads : 0;
     const int which = i / ((hi - lo) * CHUNKS);
     const int r = lo + (i / CHUNKS) % (hi - lo);
-    const int64_t j = page * kPage + r - p.past;
+    const int64_t j = page * kPage + r - past;
     const uint8_t* src = (which ? p.v_new : p.k_new) +
-                         ((static_cast<int64_t>(b) * p.n + j) * p.kv_heads + h) * row_bytes;
+                         ((static_cast<int64_t>(b) * p.stride + j) * p.kv_heads + h) * row_bytes;
     chunk[k] = *reinterpret_cast<const uint4*>(src + (i % CHUNKS) * 16);
   }
 #pragma unroll
@@ -381,12 +411,16 @@ __global__ __launch_bounds__(kThreads) void byte_append_kernel(AppendParams p, i
   constexpr int EPC = 16 / IB;                             // elements per chunk
   constexpr int TPU = 8 * CH;                              // tiles per page
   const int64_t gtask = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (gtask >= pages * TPU) return;
-  const int task = static_cast<int>(gtask % TPU);
   const int h = blockIdx.y, b = blockIdx.z;
-  const int64_t page = p.first_page + gtask / TPU;
-  const int64_t end = p.past + p.n;
-  const int lo = static_cast<int>((p.past > page * kPage ? p.past : page * kPage) - page * kPage);
+  int64_t past, n;
+  seq_counts(p, b, past, n);
+  const int64_t end = past + n;
+  // pages this sequence touches (at most `pages`, the launch's bound)
+  const int64_t mine = n > 0 ? (end - 1) / kPage - past / kPage + 1 : 0;
+  if (gtask >= (mine < pages ? mine : pages) * TPU) return;
+  const int task = static_cast<int>(gtask % TPU);
+  const int64_t page = past / kPage + gtask / TPU;
+  const int lo = static_cast<int>((past > page * kPage ? past : page * kPage) - page * kPage);
   const int hi = static_cast<int>((end < page * kPage + kPage ? end : page * kPage + kPage) -
                                   page * kPage);
   uint8_t* pg = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes +
@@ -394,7 +428,7 @@ __global__ __launch_bounds__(kThreads) void byte_append_kernel(AppendParams p, i
   constexpr int64_t ROW = static_cast<int64_t>(D) * IB;
   const int64_t row_stride = static_cast<int64_t>(p.kv_heads) * ROW;
   // input row of page token r (valid only for lo <= r < hi)
-  const int64_t row0 = (static_cast<int64_t>(b) * p.n + page * kPage - p.past) * row_stride +
+  const int64_t row0 = (static_cast<int64_t>(b) * p.stride + page * kPage - past) * row_stride +
                        static_cast<int64_t>(h) * ROW;
 
   const int kq = task / CH, kc = task % CH;   // K tile: tokens 4kq.., chunk kc
@@ -522,32 +556,40 @@ __global__ __launch_bounds__(kThreads) void byte_append_kernel(AppendParams p, i
 // ---- dispatch ---------------------------------------------------------------
 
 template <int D, int KB, int VB, int IB>
-hipError_t run_kivi(const AppendArgs& a, const AppendParams& base, hipStream_t st) {
+hipError_t run_kivi(const AppendArgs& a, const AppendParams& p, hipStream_t st) {
   const Geometry& g = a.g;
-  const int64_t end = a.past + a.n;
-  const int64_t q_old = kivi_quantised(a.past, g.residual);
-  const int64_t q_new = kivi_quantised(end, g.residual);
-  AppendParams p = base;
-  if (q_new > q_old) {
-    p.first_page = q_old / kPage;
-    dim3 grid(static_cast<unsigned>((q_new - q_old) / kPage), g.kv_heads, g.batch);
+  int64_t flush_pages, ring_tokens;
+  if (a.seq_past) {
+    // ragged batch: bounds over every sequence (a sequence appending n tokens
+    // flushes at most ceil(n / 32) pages and keeps at most min(n, R + 31) in
+    // the ring); blocks past their own sequence's range return at once
+    flush_pages = (a.n + kPage - 1) / kPage + 1;
+    ring_tokens = a.n < g.residual + kPage ? a.n : g.residual + kPage;
+  } else {
+    const int64_t end = a.past + a.n;
+    const int64_t q_old = kivi_quantised(a.past, g.residual);
+    const int64_t q_new = kivi_quantised(end, g.residual);
+    flush_pages = (q_new - q_old) / kPage;
+    ring_tokens = end - (q_new > a.past ? q_new : a.past);
+  }
+  if (flush_pages > 0) {
+    dim3 grid(static_cast<unsigned>(flush_pages), g.kv_heads, g.batch);
     hipLaunchKernelGGL((kivi_flush_kernel<D, KB, VB, IB>), grid, dim3(kThreads), 0, st, p);
   }
-  const int64_t t0 = q_new > a.past ? q_new : a.past;
-  if (end > t0) {
-    dim3 grid(static_cast<unsigned>(end - t0), g.kv_heads, g.batch);
-    hipLaunchKernelGGL((ring_write_kernel<D, IB>), grid, dim3(64), 0, st, p, t0);
+  if (ring_tokens > 0) {
+    dim3 grid(static_cast<unsigned>(ring_tokens), g.kv_heads, g.batch);
+    hipLaunchKernelGGL((ring_write_kernel<D, IB>), grid, dim3(64), 0, st, p);
   }
   return hipGetLastError();
 }
 
 template <int SCHEME, int D, int BITS, int IB>
-hipError_t run_token(const AppendArgs& a, const AppendParams& base, hipStream_t st) {
+hipError_t run_token(const AppendArgs& a, const AppendParams& p, hipStream_t st) {
   const Geometry& g = a.g;
-  AppendParams p = base;
-  p.first_page = a.past / kPage;
-  const int64_t last = (a.past + a.n - 1) / kPage;
-  const int64_t pages = last - p.first_page + 1;
+  // pages touched: exact for a uniform batch; for a ragged one the bound over
+  // every sequence (n tokens touch at most ceil(n / 32) + 1 pages)
+  const int64_t pages = a.seq_past ? (a.n + kPage - 1) / kPage + 1
+                                   : (a.past + a.n - 1) / kPage - a.past / kPage + 1;
   if constexpr (SCHEME == KVQ_SYM_TOKEN) {
     dim3 grid(static_cast<unsigned>(pages), g.kv_heads, g.batch);
     hipLaunchKernelGGL((token_append_kernel<D, BITS, IB>), grid, dim3(kThreads), 0, st, p);
@@ -601,6 +643,11 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
   p.ring_base = g.pages_per_slab * g.page_bytes;
   p.past = a.past;
   p.n = a.n;
+  p.stride = a.n;
+  p.seq_past = a.seq_past;
+  p.seq_new = a.seq_new;
+  p.capacity = g.capacity;
+  p.residual = g.residual;
   p.ring_slots = g.ring_slots > 0 ? g.ring_slots : 1;
   p.kv_heads = g.kv_heads;
   p.off_kc = g.off_kc;

@@ -47,6 +47,7 @@ struct DecodeParams {
   int64_t T, q_tokens;  // cached tokens; tokens held in pages
   const int64_t* seq_tokens;   // ragged batch: per-sequence token counts (device), or null
   int32_t n_pages, items, splits;
+  int32_t residual;            // R (the flush plan of a ragged KIVI sequence)
   int32_t kv_heads, q_heads;
   int32_t off_kc, off_ks, off_kz, off_vc, off_vs, off_vz;
   int32_t q_bf16, in_bf16;
@@ -119,16 +120,20 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   const bool rope = p.rope_theta > 0.0;
   const uint8_t* slab = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes;
   float* wq = scratch + wave * QROWS * D;
-  // tokens this sequence attends to (ragged batch) and its pages and items:
-  // shorter than the quantised part, it reads only the pages it reaches
+  // tokens this sequence holds (a ragged batch: its own fill level, and for
+  // KIVI its own split between quantised pages and the ring) and its items
   const int64_t Tb = seq_len(p.seq_tokens, b, p.T);
+  int64_t q_tokens = p.q_tokens;
   int32_t n_pages = p.n_pages, items = p.items;
   if (p.seq_tokens) {
-    if (Tb <= p.q_tokens) {
+    if constexpr (SCHEME == KVQ_KIVI) {
+      q_tokens = kivi_quantised(Tb, p.residual);
+      n_pages = static_cast<int32_t>(q_tokens / kPage);
+      items = n_pages + static_cast<int32_t>((Tb - q_tokens + kPage - 1) / kPage);
+    } else {
+      q_tokens = Tb;
       n_pages = static_cast<int32_t>((Tb + kPage - 1) / kPage);
       items = n_pages;
-    } else {
-      items = n_pages + static_cast<int32_t>((Tb - p.q_tokens + kPage - 1) / kPage);
     }
   }
 
@@ -180,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     const bool is_page = item < n_pages;
     const uint8_t* pg = slab + static_cast<int64_t>(item) * p.page_bytes;
     const int64_t t_first = is_page ? static_cast<int64_t>(item) * kPage
-                                    : p.q_tokens + static_cast<int64_t>(item - n_pages) * kPage;
+                                    : q_tokens + static_cast<int64_t>(item - n_pages) * kPage;
     const int n_valid = static_cast<int>(Tb - t_first < kPage ? Tb - t_first : kPage);
 
     __syncthreads();
@@ -471,6 +476,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   p.ring_slots = g.ring_slots > 0 ? g.ring_slots : 1;
   p.T = a.tokens;
   p.seq_tokens = a.seq_tokens;
+  p.residual = g.residual;
   if (g.scheme == KVQ_KIVI) {
     p.q_tokens = kivi_quantised(a.tokens, g.residual);
     p.n_pages = static_cast<int32_t>(p.q_tokens / kPage);

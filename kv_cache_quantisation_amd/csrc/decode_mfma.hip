@@ -76,6 +76,7 @@ struct MfmaParams {
   int64_t T, q_tokens;            // cached tokens; tokens held in pages
   const int64_t* seq_tokens;      // ragged batch: per-sequence token counts (device), or null
   int32_t n_pages, n_steps;       // quantised pages; residual tokens in 8-token steps
+  int32_t residual;               // R (the flush plan of a ragged sequence)
   int32_t splits;                 // blocks per (sequence, KV head)
   int32_t kv_heads, q_heads;
   int32_t q_bf16;
@@ -378,18 +379,15 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   const int j = lane & 15, g = lane >> 4;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const uint8_t* slab = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes;
-  // tokens this sequence attends to (ragged batch) and its pages and
-  // residual steps: shorter than the quantised part, it reads only the pages
-  // it reaches, the last perhaps in part
+  // tokens this sequence holds (a ragged batch: its own fill level, and its
+  // own split between quantised pages and the ring)
   const int64_t Tb = seq_len(p.seq_tokens, b, p.T);
+  int64_t q_tokens = p.q_tokens;
   int32_t n_pages = p.n_pages, n_steps = p.n_steps;
   if (p.seq_tokens) {
-    if (Tb <= p.q_tokens) {
-      n_pages = static_cast<int32_t>((Tb + kPage - 1) / kPage);
-      n_steps = 0;
-    } else {
-      n_steps = static_cast<int32_t>((Tb - p.q_tokens + 7) / 8);
-    }
+    q_tokens = kivi_quantised(Tb, p.residual);
+    n_pages = static_cast<int32_t>(q_tokens / kPage);
+    n_steps = static_cast<int32_t>((Tb - q_tokens + 7) / 8);
   }
   uint8_t* wbuf = arena + wave * WAVE_LDS;
   uint32_t (*frag)[4] = reinterpret_cast<uint32_t (*)[4]>(wbuf + PG::NBUF * PG::BYTES);
@@ -631,13 +629,6 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
     }
     }   // rotary / plain keys
 
-    if (t0 + kPage > Tb) {   // ragged batch: the sequence ends inside this page
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (t0 + tile_tok<ROPE>(mt, 4 * g + r) >= Tb) s[4 * mt + r] = -INFINITY;
-    }
     softmax_update(s, std::integral_constant<int, 8>{});
     // per-token value scale and offset of this lane's tokens tile_tok(mt, 4g + r)
     constexpr int VT0 = ROPE ? 16 : 32, VT1 = ROPE ? 64 : 16;
@@ -727,7 +718,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   constexpr int RPI = 64 / LPR;             // rows per 16-byte-per-lane copy
   constexpr int RSTEP = 8;                  // tokens per residual step
   auto issue_step = [&](int hs) -> int {    // returns the copies issued
-    const int64_t t0 = p.q_tokens + static_cast<int64_t>(hs) * RSTEP;
+    const int64_t t0 = q_tokens + static_cast<int64_t>(hs) * RSTEP;
     const int nv = static_cast<int>(Tb - t0 < RSTEP ? Tb - t0 : RSTEP);
     const int row_in = lane / LPR, col_b = (lane % LPR) * 16;
     const int slots = static_cast<int>(p.ring_slots);
@@ -771,7 +762,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   };
   // tile rows (tokens) 8..15 of a step are masked; key rows repeat rows 0..7
   auto process_step = [&](int hs) {
-    const int64_t t0 = p.q_tokens + static_cast<int64_t>(hs) * RSTEP;
+    const int64_t t0 = q_tokens + static_cast<int64_t>(hs) * RSTEP;
     const int nv = static_cast<int>(Tb - t0 < RSTEP ? Tb - t0 : RSTEP);
     float sc[4];
     if constexpr (ROPE) {
@@ -1053,16 +1044,15 @@ __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
   const uint8_t* slab = p.layer_base + static_cast<int64_t>(unit) * p.slab_bytes;
   uint8_t* wbuf = arena + wave * WAVE_LDS;
   uint8_t* wring = wbuf;
-  // tokens this sequence attends to (ragged batch), its pages and steps
+  // tokens this sequence holds (a ragged batch: its own fill level, and its
+  // own split between quantised pages and the ring)
   const int64_t Tb = seq_len(p.seq_tokens, b, p.T);
+  int64_t q_tokens = p.q_tokens;
   int32_t n_pages = p.n_pages, n_steps = p.n_steps;
   if (p.seq_tokens) {
-    if (Tb <= p.q_tokens) {
-      n_pages = static_cast<int32_t>((Tb + kPage - 1) / kPage);
-      n_steps = 0;
-    } else {
-      n_steps = static_cast<int32_t>((Tb - p.q_tokens + 7) / 8);
-    }
+    q_tokens = kivi_quantised(Tb, p.residual);
+    n_pages = static_cast<int32_t>(q_tokens / kPage);
+    n_steps = static_cast<int32_t>((Tb - q_tokens + 7) / 8);
   }
 
   const int pg0 = static_cast<int>(static_cast<int64_t>(split) * n_pages / p.splits);
@@ -1085,7 +1075,7 @@ __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
   constexpr int LPR = 2 * D / 16;
   constexpr int RPI = 64 / LPR;
   auto issue_step = [&](int hs) -> int {
-    const int64_t t0 = p.q_tokens + static_cast<int64_t>(hs) * RSTEP;
+    const int64_t t0 = q_tokens + static_cast<int64_t>(hs) * RSTEP;
     const int nv = static_cast<int>(Tb - t0 < RSTEP ? Tb - t0 : RSTEP);
     const int row_in = lane / LPR, col_b = (lane % LPR) * 16;
     const int slots = static_cast<int>(p.ring_slots);
@@ -1366,12 +1356,7 @@ __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
       }
       rotate_mfma(y, part, c);
     }
-    floatx4 sc = finish_scores(c);
-    if (t0 + kPage > Tb) {   // ragged batch: the sequence ends inside this page
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sc[r] = t0 + 4 * ((lane >> 2) & 7) + r < Tb ? sc[r] : -INFINITY;
-    }
-    const floatx4 w = softmax(sc);
+    const floatx4 w = softmax(finish_scores(c));
     // P' = p * s_t; sums of p and p * z_t (lanes < 32 own the tokens)
     const int t0q = 4 * ((lane >> 2) & 7);
     const float4 vs = *reinterpret_cast<const float4*>(pg + PG::OFF_VS + 4 * t0q);
@@ -1397,7 +1382,7 @@ __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
 
   // residual step: tokens 0..7 of the step are lanes with tk < 8
   auto process_step = [&](int hs) {
-    const int64_t t0 = p.q_tokens + static_cast<int64_t>(hs) * RSTEP;
+    const int64_t t0 = q_tokens + static_cast<int64_t>(hs) * RSTEP;
     const int nv = static_cast<int>(Tb - t0 < RSTEP ? Tb - t0 : RSTEP);
     rotate_q(t0);
     floatx4 c[4];
@@ -1575,6 +1560,7 @@ hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t st) {
   p.q_tokens = static_cast<int64_t>(pl.pages) * kPage;
   p.n_pages = pl.pages;
   p.n_steps = pl.chunks;
+  p.residual = g.residual;
   p.splits = pl.page_splits;
   p.kv_heads = g.kv_heads;
   p.q_heads = g.q_heads;

@@ -264,6 +264,41 @@ int32_t kvq_quantize_append(const kvq_config* cfg, void* cache, int32_t layer,
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
 }
 
+int32_t kvq_quantize_append_ragged(const kvq_config* cfg, void* cache, int32_t layer,
+                                   const int64_t* seq_past, const int64_t* seq_new,
+                                   int64_t new_max, const void* k_new, const void* v_new,
+                                   const float* k_scale, const float* v_scale, void* stream) {
+  if (!cfg) return KVQ_ERR_NULL;
+  Geometry g;
+  const int32_t st = kvq::make_geometry(*cfg, &g);
+  if (st != KVQ_OK) return st;
+  if (!cache) return KVQ_ERR_NULL;
+  if (layer < 0 || layer >= cfg->layers) return KVQ_ERR_INVALID;
+  if (new_max < 0) return KVQ_ERR_INVALID;
+  if (new_max > cfg->max_tokens) return KVQ_ERR_CAPACITY;
+  if (new_max == 0) return KVQ_OK;
+  if (!seq_past || !seq_new || !k_new || !v_new) return KVQ_ERR_NULL;
+  if (kvq::is_fp8(cfg->scheme) && (!k_scale || !v_scale)) return KVQ_ERR_NULL;
+  if (!kvq::aligned16(cache) || !kvq::aligned16(k_new) || !kvq::aligned16(v_new) ||
+      (reinterpret_cast<uintptr_t>(seq_past) & 7u) != 0 ||
+      (reinterpret_cast<uintptr_t>(seq_new) & 7u) != 0)
+    return KVQ_ERR_INVALID;
+  kvq::AppendArgs a{};
+  a.g = g;
+  a.layer_base = static_cast<uint8_t*>(cache) +
+                 static_cast<int64_t>(layer) * cfg->batch * cfg->kv_heads * g.slab_bytes;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.past = 0;
+  a.n = new_max;
+  a.seq_past = seq_past;
+  a.seq_new = seq_new;
+  const hipError_t e = kvq::launch_append(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
+}
+
 namespace {
 int32_t decode_call(const kvq_config* cfg, const void* cache, int32_t layer, int64_t tokens,
                     const int64_t* seq_tokens, const void* q, const float* k_scale,

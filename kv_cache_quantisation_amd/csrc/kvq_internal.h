@@ -59,6 +59,8 @@ struct AppendArgs {
   const float* k_scale;     // FP8 only
   const float* v_scale;
   int64_t past, n;          // tokens before the call, tokens appended
+  const int64_t* seq_past;  // ragged batch: per-sequence past / appended counts (device),
+  const int64_t* seq_new;   //   or null; n is then the bound (input rows per sequence)
 };
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 

@@ -19,8 +19,9 @@ KVQ_KIVI, KVQ_SYM_TOKEN, KVQ_FP8_E4M3, KVQ_BF16_CACHE, KVQ_FP8_E5M2 = 0, 1, 2, 3
 KVQ_F32, KVQ_BF16 = 0, 1
 KVQ_BYTES_FORMULA, KVQ_BYTES_CACHE, KVQ_BYTES_WORKSPACE = 0, 1, 2
 
-SYMBOLS = ("kvq_cache_bytes", "kvq_quantize_append", "kvq_decode_attention",
-           "kvq_decode_attention_ragged", "kvq_status_string", "kvq_abi_version")
+SYMBOLS = ("kvq_cache_bytes", "kvq_quantize_append", "kvq_quantize_append_ragged",
+           "kvq_decode_attention", "kvq_decode_attention_ragged", "kvq_status_string",
+           "kvq_abi_version")
 
 
 class KvqError(RuntimeError):
@@ -83,6 +84,8 @@ def lib():
         L.kvq_cache_bytes.restype = I64
         L.kvq_quantize_append.argtypes = [cfgp, P, I32, I64, I64, P, P, P, P, P]
         L.kvq_quantize_append.restype = I32
+        L.kvq_quantize_append_ragged.argtypes = [cfgp, P, I32, P, P, I64, P, P, P, P, P]
+        L.kvq_quantize_append_ragged.restype = I32
         L.kvq_decode_attention.argtypes = [cfgp, P, I32, I64, P, P, P, P, P, ctypes.c_size_t, P]
         L.kvq_decode_attention.restype = I32
         L.kvq_decode_attention_ragged.argtypes = [cfgp, P, I32, I64, P, P, P, P, P, P,
@@ -135,6 +138,19 @@ def kvq_quantize_append(cfg, cache, layer, past_tokens, new_tokens, k_new, v_new
                                    _ptr(v_scale), _stream(stream))
     if check and st != KVQ_OK:
         raise KvqError(st, "kvq_quantize_append")
+    return st
+
+
+def kvq_quantize_append_ragged(cfg, cache, layer, seq_past, seq_new, k_new, v_new, k_scale=None,
+                               v_scale=None, stream=None, check=True):
+    """seq_past, seq_new: device int64 tensors [batch]; k_new, v_new
+    [batch, new_max, kv_heads, head_dim] (sequence b's first seq_new[b] rows)."""
+    st = lib().kvq_quantize_append_ragged(ctypes.byref(cfg), _ptr(cache), layer, _ptr(seq_past),
+                                          _ptr(seq_new), k_new.shape[1], _ptr(k_new),
+                                          _ptr(v_new), _ptr(k_scale), _ptr(v_scale),
+                                          _stream(stream))
+    if check and st != KVQ_OK:
+        raise KvqError(st, "kvq_quantize_append_ragged")
     return st
 
 

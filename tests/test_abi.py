@@ -246,3 +246,24 @@ def test_ragged_call_validation():
     assert rd(p, f, 3, 8, f, f, None, None, f, f, big, None) == kvq.KVQ_ERR_INVALID
     need = kvq.kvq_cache_bytes(c, 4096, kvq.KVQ_BYTES_WORKSPACE)
     assert rd(p, f, 0, 4096, f, f, None, None, f, f, need - 1, None) == kvq.KVQ_ERR_WORKSPACE
+
+
+def test_ragged_append_validation():
+    """The ragged append validates as kvq_quantize_append does, and needs its
+    per-sequence counts (device arrays: present and 8-byte aligned)."""
+    L = kvq.lib()
+    c = cfg()
+    p = ctypes.byref(c)
+    f = 1 << 20
+    ra = L.kvq_quantize_append_ragged
+    assert ra(None, f, 0, f, f, 4, f, f, None, None, None) == kvq.KVQ_ERR_NULL
+    assert ra(p, None, 0, f, f, 4, f, f, None, None, None) == kvq.KVQ_ERR_NULL
+    assert ra(p, f, 0, None, f, 4, f, f, None, None, None) == kvq.KVQ_ERR_NULL
+    assert ra(p, f, 0, f, None, 4, f, f, None, None, None) == kvq.KVQ_ERR_NULL
+    assert ra(p, f, 0, f, f, 4, None, f, None, None, None) == kvq.KVQ_ERR_NULL
+    assert ra(p, f, 2, f, f, 4, f, f, None, None, None) == kvq.KVQ_ERR_INVALID     # layer
+    assert ra(p, f, 0, f, f, -1, f, f, None, None, None) == kvq.KVQ_ERR_INVALID    # bound
+    assert ra(p, f, 0, f, f, 4097, f, f, None, None, None) == kvq.KVQ_ERR_CAPACITY
+    assert ra(p, f, 0, f + 4, f, 4, f, f, None, None, None) == kvq.KVQ_ERR_INVALID  # alignment
+    assert ra(p, f, 0, f, f, 4, f + 2, f, None, None, None) == kvq.KVQ_ERR_INVALID
+    assert ra(p, f, 0, None, None, 0, None, None, None, None, None) == kvq.KVQ_OK   # no-op
