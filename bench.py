@@ -100,20 +100,16 @@ def decode_bytes(w, T, in_bytes=2, q_bytes=2):
     return w.batch * w.kv_heads * per_unit
 
 
-def ragged_decode_bytes(w, T, lens, in_bytes=2, q_bytes=2):
-    """Algorithmic bytes of a ragged decode over a T-token KIVI cache where
-    sequence b attends to its first lens[b] tokens: the pages it reaches (a
-    partial last page is read whole: its scales and offsets cover the group),
-    its ring rows below lens[b], the query and the output."""
+def ragged_decode_bytes(w, lens, in_bytes=2, q_bytes=2):
+    """Algorithmic bytes of a ragged decode where sequence b holds lens[b]
+    tokens (its own fill level): its q(T_b) / 32 pages, its T_b - q(T_b) ring
+    rows, the query and the output."""
     page = kivi_page_bytes(w)
-    q = kivi_q(T, w.residual)
     hg = w.q_heads // w.kv_heads
     total = 0
     for Tb in lens:
-        if Tb <= q:
-            per_unit = -(-Tb // 32) * page
-        else:
-            per_unit = (q // 32) * page + (Tb - q) * 2 * w.head_dim * in_bytes
+        q = kivi_q(Tb, w.residual)
+        per_unit = (q // 32) * page + (Tb - q) * 2 * w.head_dim * in_bytes
         total += w.kv_heads * (per_unit + hg * w.head_dim * (q_bytes + 4))
     return total
 
@@ -331,25 +327,36 @@ def gpu_bench(args, w):
     torch.cuda.synchronize()
     avg_us = a.elapsed_time(b) * 1e3 / (n_rep * L)
     graph = graph_replay(cfg, cache, ws, qs, outs, news, L, T_end, n_rep)
+    cache_bytes = int(cache.numel())
 
-    # ragged batch over the same caches: sequence b attends to its first
-    # lens[b] tokens, lens uniform in [T/2, T] (seeded)
+    # ragged batch: 32 more layer caches whose sequences hold lens[b] tokens
+    # each (filled by one ragged quantize-append per layer), lens uniform in
+    # [T/2, T] (seeded); decode each sequence over its own fill level
+    del cache
+    torch.cuda.empty_cache()
     gen = torch.Generator().manual_seed(0)
     lens = torch.randint(T_end // 2, T_end + 1, (w.batch,), generator=gen).tolist()
     seq = torch.tensor(lens, dtype=torch.int64, device=dev)
+    zeros = torch.zeros(w.batch, dtype=torch.int64, device=dev)
+    rcache = kvq.alloc_cache(cfg, device=dev, zero=False)
     for layer in range(L):
-        kvq.kvq_decode_attention_ragged(cfg, cache, layer, T_end, seq, qs[layer], outs[layer], ws,
+        k, v = synth.keys_values(w, layer=layer, tokens=T_end, device=dev)
+        kvq.kvq_quantize_append_ragged(cfg, rcache, layer, zeros, seq, k, v, stream=stream)
+        del k, v
+    for layer in range(L):
+        kvq.kvq_decode_attention_ragged(cfg, rcache, layer, T_end, seq, qs[layer], outs[layer], ws,
                                         stream=stream)
     torch.cuda.synchronize()
     a.record(stream)
     for _ in range(n_rep):
         for layer in range(L):
-            kvq.kvq_decode_attention_ragged(cfg, cache, layer, T_end, seq, qs[layer], outs[layer],
+            kvq.kvq_decode_attention_ragged(cfg, rcache, layer, T_end, seq, qs[layer], outs[layer],
                                             ws, stream=stream)
     b.record(stream)
     torch.cuda.synchronize()
     ragged_us = a.elapsed_time(b) * 1e3 / (n_rep * L)
-    ragged_b = ragged_decode_bytes(w, T_end, lens)
+    ragged_b = ragged_decode_bytes(w, lens)
+    del rcache
     ragged = {"avg_launch_us": round(ragged_us, 3), "bytes_per_launch": ragged_b,
               "gbs": round(ragged_b / (ragged_us * 1e-6) / 1e9, 1),
               "lengths": f"per sequence uniform in [{T_end // 2}, {T_end}] (seed 0); "
@@ -366,7 +373,7 @@ def gpu_bench(args, w):
     return {
         "ms_per_step": total_ms / K, "gbs": gbs, "append_tps": append_tps,
         "prefill_ms_per_layer": prefill_ms, "prefill_gbs": prefill_bytes / (prefill_ms * 1e-3) / 1e9,
-        "roofline": roofline, "cache_bytes": int(cache.numel()), "graph": graph,
+        "roofline": roofline, "cache_bytes": cache_bytes, "graph": graph,
         "ragged": ragged,
     }
 

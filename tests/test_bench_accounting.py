@@ -33,14 +33,15 @@ def test_decode_bytes_hand_count():
 def test_ragged_decode_bytes():
     w = synth.WORKLOADS["kivi2"]
     T = 4119
-    assert bench.ragged_decode_bytes(w, T, [T] * w.batch) == bench.decode_bytes(w, T)
+    assert bench.ragged_decode_bytes(w, [T] * w.batch) == bench.decode_bytes(w, T)
     qrow = 4 * 128 * (2 + 4)
-    # one token: one (whole) page per unit; 40 tokens: two pages; 4000: all
-    # 124 pages and 32 ring rows
-    lens = [1, 40, 4000] + [T] * (w.batch - 3)
-    want = 8 * (3328 + qrow) + 8 * (2 * 3328 + qrow) + 8 * (124 * 3328 + 32 * 512 + qrow) \
+    # each sequence at its own fill level: 1 token (ring only), 160 tokens
+    # (q = 32: one page, 128 ring rows), 4000 tokens (q = 3872: 121 pages,
+    # 128 ring rows)
+    lens = [1, 160, 4000] + [T] * (w.batch - 3)
+    want = 8 * (512 + qrow) + 8 * (3328 + 128 * 512 + qrow) + 8 * (121 * 3328 + 128 * 512 + qrow) \
         + (w.batch - 3) * bench.decode_bytes(w, T) // w.batch
-    assert bench.ragged_decode_bytes(w, T, lens) == want
+    assert bench.ragged_decode_bytes(w, lens) == want
 
 
 @pytest.mark.parametrize("T_old,n", [(0, 4096), (4096, 1), (4127, 1), (100, 60)])
