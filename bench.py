@@ -53,9 +53,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 # kernel sources they were taken with (SHA-256 over DECODE_SOURCES); after any
 # change to those, `traffic` is reported as null until they are taken again.
 COUNTERS = {
-    "kivi2": {"context": 4119, "fetch_kib": 31150.53125, "write_kib": 892.0,
+    "kivi2": {"context": 4119, "fetch_kib": 31153.875, "write_kib": 892.0,
               "fetch_scale": 262144 / 131084, "write_scale": 1.0,
-              "sources_sha256": "5b30301bcd1214bbffb540339181d114dac00c45f48cdb11a6a8f59f324c535b"},
+              "sources_sha256": "1c70dfe25685f460bb9037f70b636dee2ae4ed11e09f03bab6643af1180c9199"},
 }
 DECODE_SOURCES = ["decode_mfma.hip", "kvq_device.h", "kvq_internal.h", "kvq_wave.h"]
 
