@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 2
+#define KVQ_ABI_VERSION 3   /* 3: ragged-batch append and decode entry points */
 
 /* Exported entry points (the library is built with hidden visibility). */
 #if defined(__GNUC__)

@@ -19,6 +19,8 @@ KVQ_KIVI, KVQ_SYM_TOKEN, KVQ_FP8_E4M3, KVQ_BF16_CACHE, KVQ_FP8_E5M2 = 0, 1, 2, 3
 KVQ_F32, KVQ_BF16 = 0, 1
 KVQ_BYTES_FORMULA, KVQ_BYTES_CACHE, KVQ_BYTES_WORKSPACE = 0, 1, 2
 
+ABI_VERSION = 3   # KVQ_ABI_VERSION of include/kvq.h that this binding mirrors
+
 SYMBOLS = ("kvq_cache_bytes", "kvq_quantize_append", "kvq_quantize_append_ragged",
            "kvq_decode_attention", "kvq_decode_attention_ragged", "kvq_status_string",
            "kvq_abi_version")
@@ -95,6 +97,9 @@ def lib():
         L.kvq_status_string.restype = ctypes.c_char_p
         L.kvq_abi_version.argtypes = []
         L.kvq_abi_version.restype = I32
+        if L.kvq_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} reports ABI {L.kvq_abi_version()}, the binding "
+                               f"expects {ABI_VERSION}: rebuild the library")
         _lib = L
     return _lib
 
