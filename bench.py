@@ -55,7 +55,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 COUNTERS = {
     "kivi2": {"context": 4119, "fetch_kib": 31153.875, "write_kib": 892.0,
               "fetch_scale": 262144 / 131084, "write_scale": 1.0,
-              "sources_sha256": "1c70dfe25685f460bb9037f70b636dee2ae4ed11e09f03bab6643af1180c9199"},
+              "sources_sha256": "9fddc5f93e9c0eb00e1ed11795ec26f0ecd367b1c5c092c79f739abdf859f882"},
 }
 DECODE_SOURCES = ["decode_mfma.hip", "kvq_device.h", "kvq_internal.h", "kvq_wave.h"]
 

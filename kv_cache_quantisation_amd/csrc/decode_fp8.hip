@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   const float ks_h = E5 ? p.k_scale[h] : 1.0f;   // applied to the scores (E5M2)
 
   // pages of this block, every kWaves-th one per wave
-  // pages this sequence attends to (ragged batch: its own token count)
+  // pages this sequence holds (a ragged batch: its own fill level)
   int32_t n_pages = p.n_pages, last_valid = p.last_valid;
   if (p.seq_tokens) {
     const int64_t Tb = seq_len(p.seq_tokens, b, p.T);

@@ -36,7 +36,8 @@ struct Geometry {
 // Fills g from a validated config. Returns KVQ_OK or a negative status.
 int32_t make_geometry(const kvq_config& cfg, Geometry* g);
 
-// Tokens sequence b attends to: seq[b] clamped to [1, T], or T without seq.
+// Tokens sequence b holds (its own fill level in a ragged batch): seq[b]
+// clamped to [1, T], or T without seq.
 __device__ inline int64_t seq_len(const int64_t* seq, int b, int64_t T) {
   if (!seq) return T;
   const int64_t t = seq[b];
