@@ -216,6 +216,22 @@ class OracleCache:
         return out
 
 
+    def decode_multi(self, layer, q, sm_scale=None, rope_theta=0.0):
+        """Several new queries per sequence (q [B, n_q, Hq, d]): the cache holds
+        T tokens whose last n_q are the queries' own tokens, and query i, at
+        position T - n_q + i, attends causally to tokens [0, T - n_q + i] --
+        the masked-prefix decode with T_b = T - n_q + i + 1 (the same cache,
+        several more queries per step: chunked prefill or speculative
+        verification over the quantised cache)."""
+        q = np.asarray(q, np.float64)
+        B, nq = q.shape[:2]
+        T = self.tokens(layer)
+        out = np.zeros(q.shape)
+        for i in range(nq):
+            out[:, i] = self.decode(layer, q[:, i], sm_scale, rope_theta,
+                                    seq_tokens=[T - nq + i + 1] * B)
+        return out
+
 class RaggedCache:
     """A batch whose sequences hold different numbers of tokens (a ragged
     batch: the serving case of the KIVI page's Key points, where KIVI pairs

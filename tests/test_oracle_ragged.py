@@ -175,3 +175,36 @@ def test_ragged_kivi_split_follows_each_fill_level():
     got, pre = rag.decode(0, q), full.decode(0, q, seq_tokens=lens)
     assert np.array_equal(got[1], pre[1])                 # full length: same cache
     assert np.max(np.abs(got[0] - pre[0])) > 1e-4          # 40 of 100: different rows
+
+
+# ---- several queries per sequence (causal) -----------------------------------
+
+@pytest.mark.parametrize("scheme,bits,R", [(acc.KIVI, 2, 16), (acc.SYM_TOKEN, 4, 0), (acc.BF16_CACHE, 16, 0)])
+def test_multi_query_last_is_uniform_decode(scheme, bits, R):
+    """The last of n_q queries sees every token: the single-query decode."""
+    c, *_, q = filled(scheme, bits, 90, residual=R, seed=21)
+    rng = np.random.default_rng(8)
+    qm = rng.standard_normal((B, 3, HQ, D)).astype(np.float32)
+    qm[:, 2] = q
+    for theta in (0.0, 10000.0):
+        got = c.decode_multi(0, qm, rope_theta=theta)
+        assert np.array_equal(got[:, 2], c.decode(0, q, rope_theta=theta))
+
+
+def test_multi_query_is_causal_bruteforce():
+    """Query i attends to tokens [0, T - n_q + i]: brute force on the
+    dequantised rows (a KIVI cache whose queries' tokens sit in the ring)."""
+    T, R, nq = 70, 8, 4
+    c, *_ = filled(acc.KIVI, 4, T, residual=R, seed=23)
+    kh, vh = c.dequantized(0)
+    qm = np.random.default_rng(9).standard_normal((B, nq, HQ, D)).astype(np.float32)
+    got = c.decode_multi(0, qm)
+    sm = 1.0 / np.sqrt(D)
+    for b in range(B):
+        for i in range(nq):
+            n = T - nq + i + 1
+            for h in range(HQ):
+                g = attention.gqa_kv_head(h, HQ, H)
+                want = attention.attend_bruteforce(qm[b, i, h].astype(np.float64), kh[b, g, :n],
+                                                   vh[b, g, :n], sm)
+                np.testing.assert_allclose(got[b, i, h], want, rtol=0, atol=1e-12)
