@@ -55,7 +55,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 COUNTERS = {
     "kivi2": {"context": 4119, "fetch_kib": 31153.875, "write_kib": 892.0,
               "fetch_scale": 262144 / 131084, "write_scale": 1.0,
-              "sources_sha256": "9fddc5f93e9c0eb00e1ed11795ec26f0ecd367b1c5c092c79f739abdf859f882"},
+              "sources_sha256": "eb9e1b0d5d3a85b70fd9dd8e7b2f47c8d507e5839f903d693539ef05ce5c72a8"},
 }
 DECODE_SOURCES = ["decode_mfma.hip", "kvq_device.h", "kvq_internal.h", "kvq_wave.h"]
 

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 3   /* 3: ragged-batch append and decode entry points */
+#define KVQ_ABI_VERSION 4   /* 3: ragged-batch entry points; 4: several queries per sequence */
 
 /* Exported entry points (the library is built with hidden visibility). */
 #if defined(__GNUC__)
@@ -117,7 +117,8 @@ typedef struct kvq_config {
   int32_t  q_heads;      /* kv_heads * {1, 2, 4, 8}                        */
   int32_t  kv_heads;     /* 1..65535                                        */
   int32_t  head_dim;     /* 32, 64, 128 or 256                              */
-  int32_t  batch;        /* 1..65535 sequences, all of one length           */
+  int32_t  batch;        /* 1..65535 sequences (of one length; of their own
+                            with the _ragged entry points)                 */
   int64_t  max_tokens;   /* capacity per sequence, < 2^36                   */
   int32_t  group;        /* tokens per page / key group; must be 32         */
   int32_t  residual;     /* KIVI: R >= 0 newest tokens kept unquantised;
@@ -272,8 +273,10 @@ KVQ_API int32_t kvq_quantize_append_ragged(const kvq_config* cfg, void* cache, i
  *   v_scale    FP8 only: as for append; NULL otherwise
  *   out        device fp32 [batch][q_heads][head_dim]
  *   workspace  device, >= kvq_cache_bytes(cfg, tokens, KVQ_BYTES_WORKSPACE);
- *              must be zero-filled before its first use; every call leaves
- *              it zero-filled again
+ *              zero-filled before its first use. It begins with one int32
+ *              arrival counter per (sequence, KV head), which every call
+ *              leaves at zero again; the split partials after them are
+ *              scratch that each call overwrites
  * Requires 1 <= tokens <= max_tokens and that the cache holds `tokens` tokens.
  */
 KVQ_API int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache,
@@ -304,6 +307,28 @@ KVQ_API int32_t kvq_decode_attention_ragged(const kvq_config* cfg, const void* c
                                     const float* k_scale, const float* v_scale,
                                     float* out, void* workspace,
                                     size_t workspace_bytes, void* stream);
+
+/* Decode attention for several new queries per sequence, causally (chunked
+ * prefill, or verifying speculated tokens, over the quantised cache): the
+ * cache holds `tokens` tokens per sequence, the last n_queries of which are
+ * the queries' own tokens, and query i (position tokens - n_queries + i)
+ * attends to tokens [0, tokens - n_queries + i]: the same softmax as
+ * kvq_decode_attention over that prefix, with the KIVI page/ring split of
+ * the whole cache ([QKV] going deeper, "Why values per token"; one query per
+ * row as kvq_decode_attention computes it).
+ *   n_queries  1 <= n_queries <= tokens (else KVQ_ERR_INVALID); 1 is exactly
+ *              kvq_decode_attention
+ *   q          device [batch][n_queries][q_heads][head_dim], q_dtype
+ *   out        device fp32 [batch][n_queries][q_heads][head_dim]
+ *   workspace  >= n_queries * kvq_cache_bytes(cfg, tokens, KVQ_BYTES_WORKSPACE),
+ *              zero-filled before first use (as for kvq_decode_attention)
+ * Other arguments, requirements and errors as kvq_decode_attention. With
+ * n_queries > 1 every scheme runs on the generic (vector-ALU) kernel. */
+KVQ_API int32_t kvq_decode_attention_multi(const kvq_config* cfg, const void* cache,
+                                   int32_t layer, int64_t tokens, int32_t n_queries,
+                                   const void* q, const float* k_scale,
+                                   const float* v_scale, float* out, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 /* Static description of a status code (never NULL). */
 KVQ_API const char* kvq_status_string(int32_t status);

@@ -48,6 +48,7 @@ struct DecodeParams {
   const int64_t* seq_tokens;   // ragged batch: per-sequence token counts (device), or null
   int32_t n_pages, items, splits;
   int32_t residual;            // R (the flush plan of a ragged KIVI sequence)
+  int32_t nq;                  // queries per sequence (rows b * nq + i; 1 = one query)
   int32_t kv_heads, q_heads;
   int32_t off_kc, off_ks, off_kz, off_vc, off_vs, off_vz;
   int32_t q_bf16, in_bf16;
@@ -116,25 +117,27 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   const int lane = tid & 63, wave = tid >> 6;
   const int tok = lane & 31, hf = lane >> 5;
   const int cs = lane % LPC, ts = lane / LPC;
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int split = blockIdx.x, h = blockIdx.y;
+  const int row = blockIdx.z;                 // query row: sequence b, query qi
+  const int b = row / p.nq, qi = row - b * p.nq;
   const bool rope = p.rope_theta > 0.0;
   const uint8_t* slab = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes;
   float* wq = scratch + wave * QROWS * D;
   // tokens this sequence holds (a ragged batch: its own fill level, and for
-  // KIVI its own split between quantised pages and the ring) and its items
-  const int64_t Tb = seq_len(p.seq_tokens, b, p.T);
+  // KIVI its own split between quantised pages and the ring)
+  const int64_t fill = seq_len(p.seq_tokens, b, p.T);
   int64_t q_tokens = p.q_tokens;
-  int32_t n_pages = p.n_pages, items = p.items;
-  if (p.seq_tokens) {
-    if constexpr (SCHEME == KVQ_KIVI) {
-      q_tokens = kivi_quantised(Tb, p.residual);
-      n_pages = static_cast<int32_t>(q_tokens / kPage);
-      items = n_pages + static_cast<int32_t>((Tb - q_tokens + kPage - 1) / kPage);
-    } else {
-      q_tokens = Tb;
-      n_pages = static_cast<int32_t>((Tb + kPage - 1) / kPage);
-      items = n_pages;
-    }
+  if (p.seq_tokens) q_tokens = SCHEME == KVQ_KIVI ? kivi_quantised(fill, p.residual) : fill;
+  // tokens this row attends to: all of them, or with several queries per
+  // sequence (the last nq tokens are theirs) query qi sees [0, fill - nq + qi]
+  const int64_t Tb = fill - (p.nq - 1 - qi);
+  int32_t n_pages, items;
+  if (SCHEME == KVQ_KIVI && Tb > q_tokens) {   // every page, then ring chunks
+    n_pages = static_cast<int32_t>(q_tokens / kPage);
+    items = n_pages + static_cast<int32_t>((Tb - q_tokens + kPage - 1) / kPage);
+  } else {                                     // the pages it reaches, the last perhaps in part
+    n_pages = static_cast<int32_t>((Tb + kPage - 1) / kPage);
+    items = n_pages;
   }
 
   // ---- stage the GQA group's query: rotate at T-1, scale ----------------------
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     const float mult = p.qscale * ks_h;
     for (int i = tid; i < HG * D / 2; i += kThreads) {
       const int g = i / (D / 2), pr = i % (D / 2);
-      const int64_t base = (static_cast<int64_t>(b) * p.q_heads + h * HG + g) * D + 2 * pr;
+      const int64_t base = (static_cast<int64_t>(row) * p.q_heads + h * HG + g) * D + 2 * pr;
       float x0 = load_elem(p.q, base, p.q_bf16);
       float x1 = load_elem(p.q, base + 1, p.q_bf16);
       if (rope) {
@@ -381,10 +384,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     so *= vsc_h;
     const int hq = h * HG + g;
     if (p.splits == 1) {
-      p.out[(static_cast<int64_t>(b) * p.q_heads + hq) * D + c] = so / sl;
+      p.out[(static_cast<int64_t>(row) * p.q_heads + hq) * D + c] = so / sl;
     } else {
       float* part = p.partials +
-                    ((static_cast<int64_t>(b) * p.q_heads + hq) * p.splits + split) * (D + 2);
+                    ((static_cast<int64_t>(row) * p.q_heads + hq) * p.splits + split) * (D + 2);
       part[2 + c] = so;
       if (c == 0) {
         part[0] = M;
@@ -415,12 +418,12 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* partials,
 
 template <int SCHEME, int BITS, int VB, int D, int HG>
 hipError_t launch(const DecodeParams& p, int batch, hipStream_t st) {
-  dim3 grid(p.splits, p.kv_heads, batch);
+  dim3 grid(p.splits, p.kv_heads, batch * p.nq);
   hipLaunchKernelGGL((decode_split_kernel<SCHEME, BITS, VB, D, HG>), grid, dim3(kThreads), 0, st, p);
   if (p.splits > 1) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_merge(p.partials, p.out, batch * p.q_heads, p.splits, D, st);
+    return launch_merge(p.partials, p.out, batch * p.nq * p.q_heads, p.splits, D, st);
   }
   return hipGetLastError();
 }
@@ -461,8 +464,9 @@ hipError_t launch_merge(float* partials, float* out, int rows, int splits, int d
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   const Geometry& g = a.g;
-  if (mfma_path(g)) return launch_kivi_mfma(a, st);
-  if (fp8_mfma_path(g)) return launch_fp8_mfma(a, st);
+  // several queries per sequence: the generic kernel, for every scheme
+  if (a.nq <= 1 && mfma_path(g)) return launch_kivi_mfma(a, st);
+  if (a.nq <= 1 && fp8_mfma_path(g)) return launch_fp8_mfma(a, st);
   DecodeParams p{};
   p.layer_base = a.layer_base;
   p.q = static_cast<const uint8_t*>(a.q);
@@ -477,6 +481,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   p.T = a.tokens;
   p.seq_tokens = a.seq_tokens;
   p.residual = g.residual;
+  p.nq = a.nq > 1 ? a.nq : 1;
   if (g.scheme == KVQ_KIVI) {
     p.q_tokens = kivi_quantised(a.tokens, g.residual);
     p.n_pages = static_cast<int32_t>(p.q_tokens / kPage);

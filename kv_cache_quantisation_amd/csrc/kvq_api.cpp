@@ -163,16 +163,19 @@ int64_t workspace_partials_offset(const Geometry& g) {
   return (counters + 255) / 256 * 256;
 }
 
-int64_t workspace_bytes(const Geometry& g, int64_t tokens, int32_t requested) {
-  int64_t s;
+// Split count of a one-query decode of this configuration (its workspace holds
+// that many partials per (sequence, query head)).
+int64_t single_splits(const Geometry& g, int64_t tokens, int32_t requested) {
   if (mfma_path(g)) {
     const MfmaPlan pl = mfma_plan(g, tokens, requested);
-    s = static_cast<int64_t>(pl.page_splits) + pl.ring_splits_max;
-  } else if (fp8_mfma_path(g)) {
-    s = fp8_mfma_splits(g, tokens, requested);
-  } else {
-    s = decode_splits(g, tokens, requested);
+    return static_cast<int64_t>(pl.page_splits) + pl.ring_splits_max;
   }
+  if (fp8_mfma_path(g)) return fp8_mfma_splits(g, tokens, requested);
+  return decode_splits(g, tokens, requested);
+}
+
+int64_t workspace_bytes(const Geometry& g, int64_t tokens, int32_t requested) {
+  const int64_t s = single_splits(g, tokens, requested);
   const int64_t per = static_cast<int64_t>(g.d + 2) * 4;
   int64_t p = mul_ck(mul_ck(mul_ck(g.batch, g.q_heads), s), per);
   if (p < 0) return -1;
@@ -301,7 +304,7 @@ int32_t kvq_quantize_append_ragged(const kvq_config* cfg, void* cache, int32_t l
 
 namespace {
 int32_t decode_call(const kvq_config* cfg, const void* cache, int32_t layer, int64_t tokens,
-                    const int64_t* seq_tokens, const void* q, const float* k_scale,
+                    const int64_t* seq_tokens, int32_t nq, const void* q, const float* k_scale,
                     const float* v_scale, float* out, void* workspace, size_t workspace_bytes,
                     void* stream) {
   if (!cfg) return KVQ_ERR_NULL;
@@ -316,15 +319,17 @@ int32_t decode_call(const kvq_config* cfg, const void* cache, int32_t layer, int
   if (!kvq::aligned16(cache) || !kvq::aligned16(q) || !kvq::aligned16(out) ||
       !kvq::aligned16(workspace))
     return KVQ_ERR_INVALID;
-  const int64_t need = kvq::workspace_bytes(g, tokens, cfg->num_splits);
-  if (need < 0) return KVQ_ERR_INVALID;
-  if (workspace_bytes < static_cast<size_t>(need)) return KVQ_ERR_WORKSPACE;
+  if (nq < 1 || nq > tokens) return KVQ_ERR_INVALID;
+  const int64_t one = kvq::workspace_bytes(g, tokens, cfg->num_splits);
+  if (one < 0) return KVQ_ERR_INVALID;
+  if (workspace_bytes / static_cast<size_t>(nq) < static_cast<size_t>(one)) return KVQ_ERR_WORKSPACE;
   kvq::DecodeArgs a{};
   a.g = g;
   a.layer_base = static_cast<const uint8_t*>(cache) +
                  static_cast<int64_t>(layer) * cfg->batch * cfg->kv_heads * g.slab_bytes;
   a.tokens = tokens;
   a.seq_tokens = seq_tokens;
+  a.nq = nq;
   a.q = q;
   a.q_dtype = cfg->q_dtype;
   a.k_scale = k_scale;
@@ -336,6 +341,9 @@ int32_t decode_call(const kvq_config* cfg, const void* cache, int32_t layer, int
   a.rope_theta = cfg->rope_theta;
   a.items = kvq::decode_items(g, tokens);
   a.splits = kvq::decode_splits(g, tokens, cfg->num_splits);
+  // several queries run on the generic kernel with the one-query split count,
+  // so that n_queries one-query workspaces hold their partials
+  if (nq > 1) a.splits = static_cast<int32_t>(kvq::single_splits(g, tokens, cfg->num_splits));
   a.requested_splits = cfg->num_splits;
   const hipError_t e = kvq::launch_decode(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
@@ -346,8 +354,16 @@ int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache, int32_t l
                              int64_t tokens, const void* q, const float* k_scale,
                              const float* v_scale, float* out, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  return decode_call(cfg, cache, layer, tokens, nullptr, q, k_scale, v_scale, out, workspace,
+  return decode_call(cfg, cache, layer, tokens, nullptr, 1, q, k_scale, v_scale, out, workspace,
                      workspace_bytes, stream);
+}
+
+int32_t kvq_decode_attention_multi(const kvq_config* cfg, const void* cache, int32_t layer,
+                                   int64_t tokens, int32_t n_queries, const void* q,
+                                   const float* k_scale, const float* v_scale, float* out,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_call(cfg, cache, layer, tokens, nullptr, n_queries, q, k_scale, v_scale, out,
+                     workspace, workspace_bytes, stream);
 }
 
 int32_t kvq_decode_attention_ragged(const kvq_config* cfg, const void* cache, int32_t layer,
@@ -357,8 +373,8 @@ int32_t kvq_decode_attention_ragged(const kvq_config* cfg, const void* cache, in
   if (!seq_tokens) return KVQ_ERR_NULL;
   if ((reinterpret_cast<uintptr_t>(seq_tokens) & 7u) != 0)
     return KVQ_ERR_INVALID;
-  return decode_call(cfg, cache, layer, tokens, seq_tokens, q, k_scale, v_scale, out, workspace,
-                     workspace_bytes, stream);
+  return decode_call(cfg, cache, layer, tokens, seq_tokens, 1, q, k_scale, v_scale, out,
+                     workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

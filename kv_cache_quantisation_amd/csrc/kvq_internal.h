@@ -70,6 +70,7 @@ struct DecodeArgs {
   const uint8_t* layer_base;
   int64_t tokens;
   const int64_t* seq_tokens;  // device [B] per-sequence token counts, or null (all = tokens)
+  int32_t nq;               // queries per sequence (0 or 1: one; > 1: causal, generic kernel)
   const void* q;            // [B][Hq][d] q_dtype
   int32_t q_dtype;
   const float* k_scale;     // FP8 only

@@ -19,11 +19,11 @@ KVQ_KIVI, KVQ_SYM_TOKEN, KVQ_FP8_E4M3, KVQ_BF16_CACHE, KVQ_FP8_E5M2 = 0, 1, 2, 3
 KVQ_F32, KVQ_BF16 = 0, 1
 KVQ_BYTES_FORMULA, KVQ_BYTES_CACHE, KVQ_BYTES_WORKSPACE = 0, 1, 2
 
-ABI_VERSION = 3   # KVQ_ABI_VERSION of include/kvq.h that this binding mirrors
+ABI_VERSION = 4   # KVQ_ABI_VERSION of include/kvq.h that this binding mirrors
 
 SYMBOLS = ("kvq_cache_bytes", "kvq_quantize_append", "kvq_quantize_append_ragged",
-           "kvq_decode_attention", "kvq_decode_attention_ragged", "kvq_status_string",
-           "kvq_abi_version")
+           "kvq_decode_attention", "kvq_decode_attention_ragged", "kvq_decode_attention_multi",
+           "kvq_status_string", "kvq_abi_version")
 
 
 class KvqError(RuntimeError):
@@ -93,6 +93,9 @@ def lib():
         L.kvq_decode_attention_ragged.argtypes = [cfgp, P, I32, I64, P, P, P, P, P, P,
                                                   ctypes.c_size_t, P]
         L.kvq_decode_attention_ragged.restype = I32
+        L.kvq_decode_attention_multi.argtypes = [cfgp, P, I32, I64, I32, P, P, P, P, P,
+                                                 ctypes.c_size_t, P]
+        L.kvq_decode_attention_multi.restype = I32
         L.kvq_status_string.argtypes = [I32]
         L.kvq_status_string.restype = ctypes.c_char_p
         L.kvq_abi_version.argtypes = []
@@ -168,6 +171,21 @@ def kvq_decode_attention(cfg, cache, layer, tokens, q, out, workspace, workspace
                                     workspace_bytes, _stream(stream))
     if check and st != KVQ_OK:
         raise KvqError(st, "kvq_decode_attention")
+    return st
+
+
+def kvq_decode_attention_multi(cfg, cache, layer, tokens, q, out, workspace, workspace_bytes=None,
+                               k_scale=None, v_scale=None, stream=None, check=True):
+    """q, out: [batch, n_queries, q_heads, head_dim]; query i attends causally to
+    tokens [0, tokens - n_queries + i]."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = lib().kvq_decode_attention_multi(ctypes.byref(cfg), _ptr(cache), layer, tokens,
+                                          q.shape[1], _ptr(q), _ptr(k_scale), _ptr(v_scale),
+                                          _ptr(out), _ptr(workspace), workspace_bytes,
+                                          _stream(stream))
+    if check and st != KVQ_OK:
+        raise KvqError(st, "kvq_decode_attention_multi")
     return st
 
 

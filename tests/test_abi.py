@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert kvq.kvq_abi_version() == 3
+    assert kvq.kvq_abi_version() == 4
     assert kvq.status_string(0) == "ok"
     for st in (-1, -2, -3, -4, -5, -6):
         assert kvq.status_string(st) != "unknown status"
@@ -267,3 +267,20 @@ def test_ragged_append_validation():
     assert ra(p, f, 0, f + 4, f, 4, f, f, None, None, None) == kvq.KVQ_ERR_INVALID  # alignment
     assert ra(p, f, 0, f, f, 4, f + 2, f, None, None, None) == kvq.KVQ_ERR_INVALID
     assert ra(p, f, 0, None, None, 0, None, None, None, None, None) == kvq.KVQ_OK   # no-op
+
+
+def test_multi_query_validation():
+    """Several queries per sequence: 1 <= n_queries <= tokens, and a workspace
+    of n_queries single-query workspaces."""
+    L = kvq.lib()
+    c = cfg()
+    p = ctypes.byref(c)
+    f = 1 << 20
+    big = 1 << 30
+    mq = L.kvq_decode_attention_multi
+    assert mq(p, f, 0, 8, 0, f, None, None, f, f, big, None) == kvq.KVQ_ERR_INVALID
+    assert mq(p, f, 0, 8, 9, f, None, None, f, f, big, None) == kvq.KVQ_ERR_INVALID
+    assert mq(p, f, 0, 8, 2, None, None, None, f, f, big, None) == kvq.KVQ_ERR_NULL
+    assert mq(p, f, 0, 0, 1, f, None, None, f, f, big, None) == kvq.KVQ_ERR_INVALID
+    need = kvq.kvq_cache_bytes(c, 4096, kvq.KVQ_BYTES_WORKSPACE)
+    assert mq(p, f, 0, 4096, 3, f, None, None, f, f, 3 * need - 1, None) == kvq.KVQ_ERR_WORKSPACE

@@ -1,0 +1,63 @@
+"""GPU parity of decode with several causal queries per sequence
+(kvq_decode_attention_multi): query i at position T - n_q + i attends to
+tokens [0, T - n_q + i] of the cache, compared with the oracle's decode_multi
+(float64) on the same seeded inputs, for every scheme, with and without
+rotary keys, queries whose tokens sit in KIVI's ring or in its pages."""
+
+import pytest
+import torch
+
+import kv_cache_quantisation_amd as kvq
+import synth
+import harness as H
+from test_gpu_parity import run_append, small
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda", 0)
+
+CASES = [
+    # scheme, bits, d, hg, dtype, R, T, rope, splits, n_q
+    (synth.KIVI, 2, 128, 4, torch.bfloat16, 128, 700, 0.0, 0, 4),
+    (synth.KIVI, 2, 128, 4, torch.bfloat16, 0, 300, 0.0, 0, 40),     # queries over pages
+    (synth.KIVI, 4, 64, 2, torch.float32, 16, 257, 10000.0, 3, 17),
+    (synth.KIVI, 2, 128, 2, torch.bfloat16, 128, 500, 500000.0, 0, 8),
+    (synth.SYM_TOKEN, 4, 32, 1, torch.float32, 0, 200, 0.0, 0, 5),
+    (synth.FP8_E4M3, 8, 128, 4, torch.bfloat16, 0, 333, 0.0, 0, 3),
+    (synth.FP8_E5M2, 8, 64, 2, torch.bfloat16, 0, 97, 500000.0, 2, 6),
+    (synth.BF16_CACHE, 16, 128, 4, torch.bfloat16, 0, 333, 0.0, 0, 33),
+]
+
+
+def queries(w, nq):
+    return torch.stack([synth.query(w, device=DEV, tag=1 + i) for i in range(nq)], dim=1).contiguous()
+
+
+@pytest.mark.parametrize("case", list(range(len(CASES))))
+def test_multi_query_decode(case):
+    scheme, bits, d, hg, dtype, R, T, rope, splits, nq = CASES[case]
+    w = small(scheme, bits, d, dtype, R, B=3, hg=hg, T=T, rope=rope)
+    cfg, cache, oc, k, v, ks, vs = run_append(w, [T], capacity=T + 40)
+    cfg.num_splits = splits
+    q = queries(w, nq)
+    out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    one = kvq.kvq_cache_bytes(cfg, T, kvq.KVQ_BYTES_WORKSPACE)
+    ws = torch.zeros(nq * one, dtype=torch.uint8, device=DEV)
+    kvq.kvq_decode_attention_multi(cfg, cache, 0, T, q, out, ws, k_scale=ks, v_scale=vs)
+    want = oc.decode_multi(0, H.values(q), rope_theta=rope)
+    err = H.max_err(out, want)
+    assert err <= H.ATOL, err
+    counters = w.batch * w.kv_heads * 4          # arrival counters: left at zero
+    assert int(ws[:counters].count_nonzero()) == 0
+
+
+def test_single_query_is_the_plain_decode():
+    scheme, bits, d, hg, dtype, R, T, rope, splits, nq = CASES[0]
+    w = small(scheme, bits, d, dtype, R, B=3, hg=hg, T=T, rope=rope)
+    cfg, cache, oc, k, v, ks, vs = run_append(w, [T], capacity=T + 40)
+    q = synth.query(w, device=DEV)
+    want = H.decode(cfg, cache, 0, T, q)
+    out = torch.empty((w.batch, 1) + tuple(q.shape[1:]), dtype=torch.float32, device=DEV)
+    ws = kvq.alloc_workspace(cfg, T, device=DEV)
+    kvq.kvq_decode_attention_multi(cfg, cache, 0, T, q.unsqueeze(1).contiguous(), out, ws)
+    assert torch.equal(out[:, 0], want)
