@@ -329,6 +329,31 @@ def gpu_bench(args, w):
     graph = graph_replay(cfg, cache, ws, qs, outs, news, L, T_end, n_rep)
     cache_bytes = int(cache.numel())
 
+    # several causal queries per sequence (4: e.g. speculated tokens being
+    # verified) over the same caches, on the generic kernel
+    nq = 4
+    qm = [torch.stack([synth.query(w, layer=l, device=dev, tag=1 + i) for i in range(nq)], dim=1)
+          .contiguous() for l in range(L)]
+    om = [torch.empty(x.shape, dtype=torch.float32, device=dev) for x in qm]
+    wsm = torch.zeros(nq * kvq.kvq_cache_bytes(cfg, T_end, kvq.KVQ_BYTES_WORKSPACE),
+                      dtype=torch.uint8, device=dev)
+    for layer in range(L):
+        kvq.kvq_decode_attention_multi(cfg, cache, layer, T_end, qm[layer], om[layer], wsm,
+                                       stream=stream)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for layer in range(L):
+        kvq.kvq_decode_attention_multi(cfg, cache, layer, T_end, qm[layer], om[layer], wsm,
+                                       stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    multi_us = a.elapsed_time(b) * 1e3 / L
+    multi_b = decode_bytes(w, T_end) + (nq - 1) * w.batch * w.q_heads * w.head_dim * (2 + 4)
+    multi = {"n_queries": nq, "avg_launch_us": round(multi_us, 3), "bytes_per_launch": multi_b,
+             "gbs": round(multi_b / (multi_us * 1e-6) / 1e9, 1),
+             "kernel": "decode_split_kernel (generic vector-ALU path) + merge"}
+    del qm, om, wsm
+
     # ragged batch: 32 more layer caches whose sequences hold lens[b] tokens
     # each (filled by one ragged quantize-append per layer), lens uniform in
     # [T/2, T] (seeded); decode each sequence over its own fill level
@@ -374,7 +399,7 @@ def gpu_bench(args, w):
         "ms_per_step": total_ms / K, "gbs": gbs, "append_tps": append_tps,
         "prefill_ms_per_layer": prefill_ms, "prefill_gbs": prefill_bytes / (prefill_ms * 1e-3) / 1e9,
         "roofline": roofline, "cache_bytes": cache_bytes, "graph": graph,
-        "ragged": ragged,
+        "ragged": ragged, "multi": multi,
     }
 
 
@@ -563,6 +588,7 @@ def main():
         "roofline": r["roofline"],
         "graph_replay": r["graph"],
         "ragged_decode": r["ragged"],
+        "multi_query_decode": r["multi"],
         "bf16_cache_baseline": {
             "decode_us": round(base_us, 3), "context": r["roofline"]["context"],
             "speedup_of_quantised_decode": round(base_us / r["roofline"]["avg_launch_us"], 2),

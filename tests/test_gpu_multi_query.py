@@ -61,3 +61,4 @@ def test_single_query_is_the_plain_decode():
     ws = kvq.alloc_workspace(cfg, T, device=DEV)
     kvq.kvq_decode_attention_multi(cfg, cache, 0, T, q.unsqueeze(1).contiguous(), out, ws)
     assert torch.equal(out[:, 0], want)
+
