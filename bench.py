@@ -330,7 +330,8 @@ def gpu_bench(args, w):
     cache_bytes = int(cache.numel())
 
     # several causal queries per sequence (4: e.g. speculated tokens being
-    # verified) over the same caches, on the generic kernel
+    # verified) over the same caches; their tokens are in the ring, so they
+    # run on the matrix-core kernel, one row of blocks per query
     nq = 4
     qm = [torch.stack([synth.query(w, layer=l, device=dev, tag=1 + i) for i in range(nq)], dim=1)
           .contiguous() for l in range(L)]
@@ -351,7 +352,7 @@ def gpu_bench(args, w):
     multi_b = decode_bytes(w, T_end) + (nq - 1) * w.batch * w.q_heads * w.head_dim * (2 + 4)
     multi = {"n_queries": nq, "avg_launch_us": round(multi_us, 3), "bytes_per_launch": multi_b,
              "gbs": round(multi_b / (multi_us * 1e-6) / 1e9, 1),
-             "kernel": "decode_split_kernel (generic vector-ALU path) + merge"}
+             "kernel": "kivi_mfma_kernel<2,2,128,4> (rows b * n_q + i, merge fused)"}
     del qm, om, wsm
 
     # ragged batch: 32 more layer caches whose sequences hold lens[b] tokens

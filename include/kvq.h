@@ -323,7 +323,10 @@ KVQ_API int32_t kvq_decode_attention_ragged(const kvq_config* cfg, const void* c
  *   workspace  >= n_queries * kvq_cache_bytes(cfg, tokens, KVQ_BYTES_WORKSPACE),
  *              zero-filled before first use (as for kvq_decode_attention)
  * Other arguments, requirements and errors as kvq_decode_attention. With
- * n_queries > 1 every scheme runs on the generic (vector-ALU) kernel. */
+ * n_queries > 1, KIVI caches of 16-bit inputs whose queries' own tokens are
+ * all in the residual ring (n_queries <= tokens - q(tokens)) run on the
+ * matrix-core kernel, one row of blocks per query; every other case runs on
+ * the generic (vector-ALU) kernel. */
 KVQ_API int32_t kvq_decode_attention_multi(const kvq_config* cfg, const void* cache,
                                    int32_t layer, int64_t tokens, int32_t n_queries,
                                    const void* q, const float* k_scale,

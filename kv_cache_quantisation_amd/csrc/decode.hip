@@ -464,8 +464,10 @@ hipError_t launch_merge(float* partials, float* out, int rows, int splits, int d
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   const Geometry& g = a.g;
-  // several queries per sequence: the generic kernel, for every scheme
+  // several queries per sequence: the matrix-core KIVI kernel when each
+  // query's own token is in the ring, else the generic kernel
   if (a.nq <= 1 && mfma_path(g)) return launch_kivi_mfma(a, st);
+  if (a.nq > 1 && !a.seq_tokens && mfma_multi_ok(g, a.tokens, a.nq)) return launch_kivi_mfma(a, st);
   if (a.nq <= 1 && fp8_mfma_path(g)) return launch_fp8_mfma(a, st);
   DecodeParams p{};
   p.layer_base = a.layer_base;

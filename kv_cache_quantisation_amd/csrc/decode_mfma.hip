@@ -77,6 +77,7 @@ struct MfmaParams {
   const int64_t* seq_tokens;      // ragged batch: per-sequence token counts (device), or null
   int32_t n_pages, n_steps;       // quantised pages; residual tokens in 8-token steps
   int32_t residual;               // R (the flush plan of a ragged sequence)
+  int32_t nq;                     // queries per sequence: rows b * nq + i (1: one query)
   int32_t splits;                 // blocks per (sequence, KV head)
   int32_t kv_heads, q_heads;
   int32_t q_bf16;
@@ -151,14 +152,15 @@ __device__ __forceinline__ float load_q(const uint8_t* base, int64_t idx, int bf
 template <int D, int HG, int NW = kWaves>
 __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* acc, const float* mh,
                                             const float* lsum, const float* zsum, uint8_t* arena,
-                                            int& last_block, int b, int h, int split) {
+                                            int& last_block, int b, int qi, int h, int split) {
   constexpr int NT = D / 16;
   constexpr int NTH = NW * 64;             // threads of the block
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform in the wave
   const int j = lane & 15, g = lane >> 4;
-  const int unit = b * p.kv_heads + h;
+  const int unit = b * p.kv_heads + h;   // one arrival counter for every query row of b
+  const int row = b * p.nq + qi;         // this block's query row (q, out, partials)
   __syncthreads();   // every wave is done with its page buffers (the arena)
   float* red = reinterpret_cast<float*>(arena);   // [wave][HG][D + 2]: m, l, o
   auto R = [&](int w, int hh) { return red + (w * HG + hh) * (D + 2); };
@@ -202,7 +204,7 @@ __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* 
   __syncthreads();
 
   // ---- combine the waves; write the output, or this block's partial --------
-  float* part_bh = p.partials + (static_cast<int64_t>(b) * p.q_heads + h * HG) * p.splits * (D + 2);
+  float* part_bh = p.partials + (static_cast<int64_t>(row) * p.q_heads + h * HG) * p.splits * (D + 2);
   for (int i = tid; i < HG * D; i += NTH) {
     const int hh = i / D, c = i % D;
     float M = -INFINITY;
@@ -217,7 +219,7 @@ __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* 
     }
     const int hq = h * HG + hh;
     if (p.splits == 1) {
-      p.out[(static_cast<int64_t>(b) * p.q_heads + hq) * D + c] = so / sl;
+      p.out[(static_cast<int64_t>(row) * p.q_heads + hq) * D + c] = so / sl;
     } else {
       float* part = part_bh + (static_cast<int64_t>(hh) * p.splits + split) * (D + 2);
       store_coherent(part + 2 + c, so);
@@ -230,6 +232,7 @@ __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* 
   if (p.splits == 1) return;
 
   // ---- the last block of this (sequence, KV head) merges every partial ------
+  // (of every query row of the sequence: nq * splits blocks arrive)
   // M = max_s m_s; out = sum_s 2^(m_s-M) o_s / sum_s 2^(m_s-M) l_s. Partials
   // are written and read at device scope (through to the coherence point, not
   // the per-XCD L2); the counter lives in the workspace and is returned to
@@ -241,7 +244,7 @@ __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* 
   if (tid == 0) {
     const int done = __hip_atomic_fetch_add(&p.counters[unit], 1, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
-    last_block = done == p.splits - 1;
+    last_block = done == p.nq * p.splits - 1;
   }
   __syncthreads();
   if (!last_block) return;
@@ -249,6 +252,8 @@ __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* 
   // a batch of 8 splits for both issued before any use
   constexpr int PER = (HG * D + NTH - 1) / NTH;
   constexpr int CH = PER < 2 ? PER : 2;
+  for (int r = b * p.nq; r < (b + 1) * p.nq; ++r) {
+  const float* part_rh = p.partials + (static_cast<int64_t>(r) * p.q_heads + h * HG) * p.splits * (D + 2);
   for (int e0 = 0; e0 < PER; e0 += CH) {
     float M[CH], so[CH], sl[CH];
 #pragma unroll
@@ -263,7 +268,7 @@ __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* 
       for (int e = 0; e < CH; ++e) {
         const int i = tid + (e0 + e) * NTH;
         const int hh = (i < HG * D ? i : 0) / D, c = i % D;
-        const float* part = part_bh + static_cast<int64_t>(hh) * p.splits * (D + 2);
+        const float* part = part_rh + static_cast<int64_t>(hh) * p.splits * (D + 2);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const float* ps = part + (s0 + k < p.splits ? s0 + k : s0) * (D + 2);
@@ -295,9 +300,10 @@ __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* 
       const int i = tid + (e0 + e) * NTH;
       if (i < HG * D) {
         const int hh = i / D, c = i % D;
-        p.out[(static_cast<int64_t>(b) * p.q_heads + h * HG + hh) * D + c] = so[e] / sl[e];
+        p.out[(static_cast<int64_t>(r) * p.q_heads + h * HG + hh) * D + c] = so[e] / sl[e];
       }
     }
+  }
   }
   if (tid == 0)
     __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -377,18 +383,23 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform in the wave
   const int j = lane & 15, g = lane >> 4;
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int split = blockIdx.x, h = blockIdx.y;
+  const int b = blockIdx.z / p.nq, qi = blockIdx.z - b * p.nq;   // sequence, its query
   const uint8_t* slab = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes;
   // tokens this sequence holds (a ragged batch: its own fill level, and its
   // own split between quantised pages and the ring)
-  const int64_t Tb = seq_len(p.seq_tokens, b, p.T);
+  const int64_t fill = seq_len(p.seq_tokens, b, p.T);
   int64_t q_tokens = p.q_tokens;
   int32_t n_pages = p.n_pages, n_steps = p.n_steps;
   if (p.seq_tokens) {
-    q_tokens = kivi_quantised(Tb, p.residual);
+    q_tokens = kivi_quantised(fill, p.residual);
     n_pages = static_cast<int32_t>(q_tokens / kPage);
-    n_steps = static_cast<int32_t>((Tb - q_tokens + 7) / 8);
   }
+  // query qi of nq sits at position fill - nq + qi and sees the tokens up to
+  // it: all pages, and the ring up to its own token (the host sends several
+  // queries here only when each of their tokens is in the ring)
+  const int64_t Tb = fill - (p.nq - 1 - qi);
+  if (p.seq_tokens || p.nq > 1) n_steps = static_cast<int32_t>((Tb - q_tokens + 7) / 8);
   uint8_t* wbuf = arena + wave * WAVE_LDS;
   uint32_t (*frag)[4] = reinterpret_cast<uint32_t (*)[4]>(wbuf + PG::NBUF * PG::BYTES);
 
@@ -839,7 +850,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   const int q_bytes = HG * D * (p.q_bf16 ? 2 : 4);
   int after_q = 0;
   if (wave == 0) {
-    const uint8_t* qsrc = p.q + (static_cast<int64_t>(b) * p.q_heads + h * HG) * D * (p.q_bf16 ? 2 : 4);
+    const uint8_t* qsrc = p.q + (static_cast<int64_t>(b * p.nq + qi) * p.q_heads + h * HG) * D * (p.q_bf16 ? 2 : 4);
     for (int off = 0; off < q_bytes; off += 1024)
       if (off + lane * 16 < q_bytes) dma16(qsrc + off + lane * 16, lds_addr(&qs[0][0]) + off);
   }
@@ -968,7 +979,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
       mh[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_lane), hh));
     }
   }
-  finish_unit<D, HG, NW>(p, acc, mh, lsum, zsum, arena, last_block, b, h, split);
+  finish_unit<D, HG, NW>(p, acc, mh, lsum, zsum, arena, last_block, b, qi, h, split);
 }
 
 // ---- rotary keys, GQA group of 4: dense scores on v_mfma_f32_4x4x1_16b_f32 ----
@@ -1039,21 +1050,24 @@ __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
   const int hd = lane & 3;                          // head of this lane (4x4 column)
   const int tk = lane & 31;                         // token of this lane (4x4 row)
   const int hf = lane >> 5;                         // channel half of this lane
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int split = blockIdx.x, h = blockIdx.y;
+  const int b = blockIdx.z / p.nq, qi = blockIdx.z - b * p.nq;   // sequence, its query
   const int unit = b * p.kv_heads + h;
   const uint8_t* slab = p.layer_base + static_cast<int64_t>(unit) * p.slab_bytes;
   uint8_t* wbuf = arena + wave * WAVE_LDS;
   uint8_t* wring = wbuf;
   // tokens this sequence holds (a ragged batch: its own fill level, and its
   // own split between quantised pages and the ring)
-  const int64_t Tb = seq_len(p.seq_tokens, b, p.T);
+  const int64_t fill = seq_len(p.seq_tokens, b, p.T);
   int64_t q_tokens = p.q_tokens;
   int32_t n_pages = p.n_pages, n_steps = p.n_steps;
   if (p.seq_tokens) {
-    q_tokens = kivi_quantised(Tb, p.residual);
+    q_tokens = kivi_quantised(fill, p.residual);
     n_pages = static_cast<int32_t>(q_tokens / kPage);
-    n_steps = static_cast<int32_t>((Tb - q_tokens + 7) / 8);
   }
+  // query qi of nq: position fill - nq + qi, in the ring (as above)
+  const int64_t Tb = fill - (p.nq - 1 - qi);
+  if (p.seq_tokens || p.nq > 1) n_steps = static_cast<int32_t>((Tb - q_tokens + 7) / 8);
 
   const int pg0 = static_cast<int>(static_cast<int64_t>(split) * n_pages / p.splits);
   const int pg1 = static_cast<int>(static_cast<int64_t>(split + 1) * n_pages / p.splits);
@@ -1102,7 +1116,7 @@ __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
   const int q_bytes = HG * D * (p.q_bf16 ? 2 : 4);
   int after_q = 0;
   if (wave == 0) {
-    const uint8_t* qsrc = p.q + (static_cast<int64_t>(b) * p.q_heads + h * HG) * D * (p.q_bf16 ? 2 : 4);
+    const uint8_t* qsrc = p.q + (static_cast<int64_t>(b * p.nq + qi) * p.q_heads + h * HG) * D * (p.q_bf16 ? 2 : 4);
     for (int off = 0; off < q_bytes; off += 1024)
       if (off + lane * 16 < q_bytes) dma16(qsrc + off + lane * 16, lds_addr(&qs[0][0]) + off);
   }
@@ -1466,7 +1480,7 @@ __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
       zsum[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, z_), hh));
     }
   }
-  finish_unit<D, HG, NW>(p, acc, mh, lsum, zsum, arena, last_block, b, h, split);
+  finish_unit<D, HG, NW>(p, acc, mh, lsum, zsum, arena, last_block, b, qi, h, split);
 }
 
 
@@ -1542,9 +1556,19 @@ MfmaPlan mfma_plan(const Geometry& g, int64_t tokens, int32_t requested) {
   return pl;
 }
 
+bool mfma_multi_ok(const Geometry& g, int64_t tokens, int32_t nq) {
+  return mfma_path(g) && nq <= tokens - kivi_quantised(tokens, g.residual);
+}
+
 hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t st) {
   const Geometry& g = a.g;
-  const MfmaPlan pl = mfma_plan(g, a.tokens, a.requested_splits);
+  const int32_t nq = a.nq > 1 ? a.nq : 1;
+  // several queries per sequence: batch * nq rows share the chip, so the
+  // split count is planned for that many rows (never more splits than the
+  // one-query plan, whose workspace nq copies of hold the partials)
+  Geometry rows = g;
+  rows.batch = g.batch * nq;
+  const MfmaPlan pl = mfma_plan(rows, a.tokens, a.requested_splits);
   MfmaParams p{};
   p.layer_base = a.layer_base;
   p.q = static_cast<const uint8_t*>(a.q);
@@ -1561,15 +1585,18 @@ hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t st) {
   p.n_pages = pl.pages;
   p.n_steps = pl.chunks;
   p.residual = g.residual;
+  p.nq = nq;
   p.splits = pl.page_splits;
   p.kv_heads = g.kv_heads;
   p.q_heads = g.q_heads;
   p.q_bf16 = a.q_dtype == KVQ_BF16;
   p.qscale = a.sm_scale * kLog2e;
   p.rope_theta = a.rope_theta;
-  if (a.rope_theta > 0.0) return by_d_rope(p, g.d, g.hg, g.batch, st);
-  if (g.bits == 2) return by_d<2, 2>(p, g.d, g.hg, g.batch, st);
-  return g.vbits == 2 ? by_d<4, 2>(p, g.d, g.hg, g.batch, st) : by_d<4, 4>(p, g.d, g.hg, g.batch, st);
+  const int grid_rows = g.batch * nq;
+  if (a.rope_theta > 0.0) return by_d_rope(p, g.d, g.hg, grid_rows, st);
+  if (g.bits == 2) return by_d<2, 2>(p, g.d, g.hg, grid_rows, st);
+  return g.vbits == 2 ? by_d<4, 2>(p, g.d, g.hg, grid_rows, st)
+                      : by_d<4, 4>(p, g.d, g.hg, grid_rows, st);
 }
 
 }  // namespace kvq

@@ -70,7 +70,7 @@ struct DecodeArgs {
   const uint8_t* layer_base;
   int64_t tokens;
   const int64_t* seq_tokens;  // device [B] per-sequence token counts, or null (all = tokens)
-  int32_t nq;               // queries per sequence (0 or 1: one; > 1: causal, generic kernel)
+  int32_t nq;               // queries per sequence (0 or 1: one; > 1: causal)
   const void* q;            // [B][Hq][d] q_dtype
   int32_t q_dtype;
   const float* k_scale;     // FP8 only
@@ -91,6 +91,9 @@ struct MfmaPlan {
   int32_t pages, chunks, page_splits, ring_splits, ring_splits_max;
 };
 bool mfma_path(const Geometry& g);
+// Several queries (nq) of a uniform batch on the KIVI matrix-core kernel:
+// mfma_path, and every query's own token is an unquantised ring token.
+bool mfma_multi_ok(const Geometry& g, int64_t tokens, int32_t nq);
 MfmaPlan mfma_plan(const Geometry& g, int64_t tokens, int32_t requested);
 hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t stream);
 // Matrix-core path of FP8 E4M3 and bfloat16 caches (head_dim >= 64, no rotary embedding).

@@ -2,7 +2,8 @@
 (kvq_decode_attention_multi): query i at position T - n_q + i attends to
 tokens [0, T - n_q + i] of the cache, compared with the oracle's decode_multi
 (float64) on the same seeded inputs, for every scheme, with and without
-rotary keys, queries whose tokens sit in KIVI's ring or in its pages."""
+rotary keys, queries whose tokens sit in KIVI's ring (the matrix-core kernel,
+when the cache's inputs are 16-bit) or in its pages (the generic kernel)."""
 
 import pytest
 import torch
@@ -26,6 +27,13 @@ CASES = [
     (synth.FP8_E4M3, 8, 128, 4, torch.bfloat16, 0, 333, 0.0, 0, 3),
     (synth.FP8_E5M2, 8, 64, 2, torch.bfloat16, 0, 97, 500000.0, 2, 6),
     (synth.BF16_CACHE, 16, 128, 4, torch.bfloat16, 0, 333, 0.0, 0, 33),
+    # KIVI 16-bit-input caches whose queries sit in the ring: matrix-core kernel
+    (synth.KIVI, 2, 128, 4, torch.bfloat16, 128, 1000, 10000.0, 0, 3),   # rotary, GQA 4
+    (synth.KIVI, 4, 128, 8, torch.bfloat16, 64, 450, 0.0, 0, 5),
+    (synth.KIVI, 2, 64, 1, torch.bfloat16, 32, 200, 0.0, 1, 6),          # one split: no merge
+    (synth.KIVI, 2, 128, 4, torch.bfloat16, 32, 100, 0.0, 0, 36),        # n_q = ring tokens
+    (synth.KIVI, 2, 128, 4, torch.bfloat16, 128, 90, 0.0, 0, 7),         # no pages yet
+    (synth.KIVI, 2, 128, 4, torch.bfloat16, 32, 100, 0.0, 0, 37),        # one more: generic
 ]
 
 
