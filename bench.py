@@ -53,9 +53,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 # kernel sources they were taken with (SHA-256 over DECODE_SOURCES); after any
 # change to those, `traffic` is reported as null until they are taken again.
 COUNTERS = {
-    "kivi2": {"context": 4119, "fetch_kib": 31153.875, "write_kib": 892.0,
+    "kivi2": {"context": 4119, "fetch_kib": 31156.8125, "write_kib": 892.0,
               "fetch_scale": 262144 / 131084, "write_scale": 1.0,
-              "sources_sha256": "eb9e1b0d5d3a85b70fd9dd8e7b2f47c8d507e5839f903d693539ef05ce5c72a8"},
+              "sources_sha256": "7082056e957c65e67db2a28599194c3c4969ca150b34f40e134e04cd76a69b9a"},
 }
 DECODE_SOURCES = ["decode_mfma.hip", "kvq_device.h", "kvq_internal.h", "kvq_wave.h"]
 
