@@ -325,8 +325,9 @@ KVQ_API int32_t kvq_decode_attention_ragged(const kvq_config* cfg, const void* c
  * Other arguments, requirements and errors as kvq_decode_attention. With
  * n_queries > 1, KIVI caches of 16-bit inputs whose queries' own tokens are
  * all in the residual ring (n_queries <= tokens - q(tokens)) run on the
- * matrix-core kernel, one row of blocks per query; every other case runs on
- * the generic (vector-ALU) kernel. */
+ * matrix-core kernel, one row of blocks per query, and so do FP8 and
+ * bfloat16 caches without in-kernel rotary embedding (head_dim >= 64); every
+ * other case runs on the generic (vector-ALU) kernel. */
 KVQ_API int32_t kvq_decode_attention_multi(const kvq_config* cfg, const void* cache,
                                    int32_t layer, int64_t tokens, int32_t n_queries,
                                    const void* q, const float* k_scale,

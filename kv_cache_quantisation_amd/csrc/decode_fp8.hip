@@ -63,6 +63,7 @@ struct Fp8Params {
   int64_t T;
   const int64_t* seq_tokens;      // ragged batch: per-sequence token counts (device), or null
   int32_t n_pages, last_valid;    // pages holding tokens; tokens in the last one
+  int32_t nq;                     // queries per sequence: rows b * nq + i (1: one query)
   int32_t splits;
   int32_t kv_heads, q_heads;
   int32_t q_bf16;
@@ -117,17 +118,21 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform in the wave
   const int j = lane & 15, g = lane >> 4;
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int unit = b * p.kv_heads + h;
+  const int split = blockIdx.x, h = blockIdx.y;
+  const int row = blockIdx.z;                      // query row b * nq + qi
+  const int b = row / p.nq, qi = row - b * p.nq;   // sequence, its query
+  const int unit = b * p.kv_heads + h;             // one arrival counter for every row of b
   const uint8_t* slab = p.layer_base + static_cast<int64_t>(unit) * p.slab_bytes;
   uint8_t* wbuf = arena + wave * PG::WAVE_LDS;
   const float ks_h = E5 ? p.k_scale[h] : 1.0f;   // applied to the scores (E5M2)
 
   // pages of this block, every kWaves-th one per wave
-  // pages this sequence holds (a ragged batch: its own fill level)
+  // pages this sequence holds (a ragged batch: its own fill level), cut at
+  // the query's own token when there are several (query qi of nq sits at
+  // position fill - nq + qi)
   int32_t n_pages = p.n_pages, last_valid = p.last_valid;
-  if (p.seq_tokens) {
-    const int64_t Tb = seq_len(p.seq_tokens, b, p.T);
+  if (p.seq_tokens || p.nq > 1) {
+    const int64_t Tb = seq_len(p.seq_tokens, b, p.T) - (p.nq - 1 - qi);
     n_pages = static_cast<int32_t>((Tb + kPage - 1) / kPage);
     last_valid = static_cast<int32_t>(Tb - static_cast<int64_t>(n_pages - 1) * kPage);
   }
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   // ---- query group: q * sm_scale * log2(e) * ks_h ----------------------------
   {
     const float mult = (BF16 || E5) ? p.qscale : p.qscale * p.k_scale[h];
-    const int64_t q0 = (static_cast<int64_t>(b) * p.q_heads + h * HG) * D;
+    const int64_t q0 = (static_cast<int64_t>(row) * p.q_heads + h * HG) * D;
     for (int i = tid; i < HG * D; i += kThreads) {
       const float x = p.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(p.q)[q0 + i])
                                : reinterpret_cast<const float*>(p.q)[q0 + i];
@@ -380,7 +385,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
 
   // ---- combine the waves; write the output, or this block's partial --------
   const float vs_h = BF16 ? 1.0f : p.v_scale[h];
-  float* part_bh = p.partials + (static_cast<int64_t>(b) * p.q_heads + h * HG) * p.splits * (D + 2);
+  float* part_bh = p.partials + (static_cast<int64_t>(row) * p.q_heads + h * HG) * p.splits * (D + 2);
   for (int i = tid; i < HG * D; i += kThreads) {
     const int hh = i / D, c = i % D;
     float M = -INFINITY;
@@ -396,7 +401,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
     so *= vs_h;
     const int hq = h * HG + hh;
     if (p.splits == 1) {
-      p.out[(static_cast<int64_t>(b) * p.q_heads + hq) * D + c] = so / sl;
+      p.out[(static_cast<int64_t>(row) * p.q_heads + hq) * D + c] = so / sl;
     } else {
       float* part = part_bh + (static_cast<int64_t>(hh) * p.splits + split) * (D + 2);
       store_coherent(part + 2 + c, so);
@@ -409,6 +414,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   if (p.splits == 1) return;
 
   // ---- the last block of this (sequence, KV head) merges every partial ------
+  // (of every query row of the sequence: nq * splits blocks arrive);
   // every wave's partial stores (device scope, written through) have completed
   // before the block's arrival is counted: the block that counts last reads them
   wait_vm<0>();
@@ -416,13 +422,14 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   if (tid == 0) {
     const int done = __hip_atomic_fetch_add(&p.counters[unit], 1, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
-    last_block = done == p.splits - 1;
+    last_block = done == p.nq * p.splits - 1;
   }
   __syncthreads();
   if (!last_block) return;
-  for (int i = tid; i < HG * D; i += kThreads) {
-    const int hh = i / D, c = i % D;
-    const float* part = part_bh + static_cast<int64_t>(hh) * p.splits * (D + 2);
+  for (int i = tid; i < p.nq * HG * D; i += kThreads) {
+    const int r = b * p.nq + i / (HG * D), hh = (i / D) % HG, c = i % D;
+    const float* part = p.partials +
+                        ((static_cast<int64_t>(r) * p.q_heads + h * HG + hh) * p.splits) * (D + 2);
     float M = -INFINITY, so = 0.f, sl = 0.f;
     for (int s0 = 0; s0 < p.splits; s0 += 8) {
       float mv[8], lv[8], ov[8];
@@ -448,7 +455,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
       }
       M = Mn;
     }
-    p.out[(static_cast<int64_t>(b) * p.q_heads + h * HG + hh) * D + c] = so / sl;
+    p.out[(static_cast<int64_t>(r) * p.q_heads + h * HG + hh) * D + c] = so / sl;
   }
   if (tid == 0)
     __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -501,6 +508,12 @@ int32_t fp8_mfma_splits(const Geometry& g, int64_t tokens, int32_t requested) {
 
 hipError_t launch_fp8_mfma(const DecodeArgs& a, hipStream_t st) {
   const Geometry& g = a.g;
+  const int32_t nq = a.nq > 1 ? a.nq : 1;
+  // several queries per sequence: batch * nq rows, and the split count
+  // planned for that many (never more than the one-query plan, whose
+  // workspace nq copies of hold the partials)
+  Geometry rows = g;
+  rows.batch = g.batch * nq;
   Fp8Params p{};
   p.layer_base = a.layer_base;
   p.q = static_cast<const uint8_t*>(a.q);
@@ -515,15 +528,16 @@ hipError_t launch_fp8_mfma(const DecodeArgs& a, hipStream_t st) {
   p.seq_tokens = a.seq_tokens;
   p.n_pages = static_cast<int32_t>((a.tokens + kPage - 1) / kPage);
   p.last_valid = static_cast<int32_t>(a.tokens - static_cast<int64_t>(p.n_pages - 1) * kPage);
-  p.splits = fp8_mfma_splits(g, a.tokens, a.requested_splits);
+  p.nq = nq;
+  p.splits = fp8_mfma_splits(rows, a.tokens, a.requested_splits);
   p.kv_heads = g.kv_heads;
   p.q_heads = g.q_heads;
   p.q_bf16 = a.q_dtype == KVQ_BF16;
   p.qscale = a.sm_scale * kLog2e;
   switch (g.scheme) {
-    case KVQ_BF16_CACHE: return by_d<KVQ_BF16_CACHE>(p, g.d, g.hg, g.batch, st);
-    case KVQ_FP8_E5M2: return by_d<KVQ_FP8_E5M2>(p, g.d, g.hg, g.batch, st);
-    default: return by_d<KVQ_FP8_E4M3>(p, g.d, g.hg, g.batch, st);
+    case KVQ_BF16_CACHE: return by_d<KVQ_BF16_CACHE>(p, g.d, g.hg, g.batch * nq, st);
+    case KVQ_FP8_E5M2: return by_d<KVQ_FP8_E5M2>(p, g.d, g.hg, g.batch * nq, st);
+    default: return by_d<KVQ_FP8_E4M3>(p, g.d, g.hg, g.batch * nq, st);
   }
 }
 

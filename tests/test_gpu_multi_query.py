@@ -3,7 +3,8 @@
 tokens [0, T - n_q + i] of the cache, compared with the oracle's decode_multi
 (float64) on the same seeded inputs, for every scheme, with and without
 rotary keys, queries whose tokens sit in KIVI's ring (the matrix-core kernel,
-when the cache's inputs are 16-bit) or in its pages (the generic kernel)."""
+when the cache's inputs are 16-bit) or in its pages (the generic kernel), and
+FP8 and bfloat16 caches (their matrix-core kernel without rotary keys)."""
 
 import pytest
 import torch
@@ -34,6 +35,9 @@ CASES = [
     (synth.KIVI, 2, 128, 4, torch.bfloat16, 32, 100, 0.0, 0, 36),        # n_q = ring tokens
     (synth.KIVI, 2, 128, 4, torch.bfloat16, 128, 90, 0.0, 0, 7),         # no pages yet
     (synth.KIVI, 2, 128, 4, torch.bfloat16, 32, 100, 0.0, 0, 37),        # one more: generic
+    # FP8 and bfloat16 caches without rotary keys: their matrix-core kernel
+    (synth.FP8_E5M2, 8, 128, 8, torch.bfloat16, 0, 301, 0.0, 3, 45),     # queries across pages
+    (synth.BF16_CACHE, 16, 64, 2, torch.bfloat16, 0, 77, 0.0, 1, 9),     # one split: no merge
 ]
 
 
