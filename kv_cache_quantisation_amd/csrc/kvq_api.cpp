@@ -341,8 +341,9 @@ int32_t decode_call(const kvq_config* cfg, const void* cache, int32_t layer, int
   a.rope_theta = cfg->rope_theta;
   a.items = kvq::decode_items(g, tokens);
   a.splits = kvq::decode_splits(g, tokens, cfg->num_splits);
-  // several queries run on the generic kernel with the one-query split count,
-  // so that n_queries one-query workspaces hold their partials
+  // several queries: the generic kernel takes the one-query split count (the
+  // matrix-core kernels plan theirs for batch * n_queries rows, never more),
+  // so that n_queries one-query workspaces hold the partials
   if (nq > 1) a.splits = static_cast<int32_t>(kvq::single_splits(g, tokens, cfg->num_splits));
   a.requested_splits = cfg->num_splits;
   const hipError_t e = kvq::launch_decode(a, static_cast<hipStream_t>(stream));
