@@ -13,9 +13,10 @@
 // range; waves take items round-robin. Each wave keeps an online softmax
 // (running max m, running sum l, unnormalised output o) for the GQA group of
 // query heads; the waves are combined in LDS and the block writes one partial
-// (m, l, o). A second kernel merges the partials of a (sequence, query head):
-// M = max m_s, out = sum 2^(m_s-M) o_s / sum 2^(m_s-M) l_s. Scores are kept in
-// the log2 domain (the query is pre-scaled by sm_scale*log2(e)).
+// (m, l, o). The last block of a (sequence, KV head) to finish (an arrival
+// counter in the workspace) merges the partials of every query row of that
+// sequence: M = max m_s, out = sum 2^(m_s-M) o_s / sum 2^(m_s-M) l_s. Scores
+// are kept in the log2 domain (the query is pre-scaled by sm_scale*log2(e)).
 //
 // Folding the scales out of the inner loops:
 //   KIVI keys:   q.k^ = sum_c (q_c s_c) code_tc + sum_c q_c z_c  (per page)
@@ -28,6 +29,7 @@
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "kvq_wave.h"
 
 namespace kvq {
 namespace {
@@ -43,6 +45,7 @@ struct DecodeParams {
   const float* v_scale;
   float* out;
   float* partials;
+  int* counters;        // one per (sequence, KV head), zero between calls
   int64_t slab_bytes, page_bytes, ring_base, ring_slots;
   int64_t T, q_tokens;  // cached tokens; tokens held in pages
   const int64_t* seq_tokens;   // ragged batch: per-sequence token counts (device), or null
@@ -388,43 +391,53 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     } else {
       float* part = p.partials +
                     ((static_cast<int64_t>(row) * p.q_heads + hq) * p.splits + split) * (D + 2);
-      part[2 + c] = so;
+      store_coherent(part + 2 + c, so);
       if (c == 0) {
-        part[0] = M;
-        part[1] = sl;
+        store_coherent(part, M);
+        store_coherent(part + 1, sl);
       }
     }
   }
-}
+  if (p.splits == 1) return;
 
-// Merges the split partials of one (sequence, query head): grid = rows.
-// M = max m_s; out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-template <int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(const float* partials, float* out,
-                                                          int splits) {
-  const int bh = blockIdx.x;
-  const float* part = partials + static_cast<int64_t>(bh) * splits * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, part[s * (D + 2)]);
-  float L = 0.f;
-  for (int s = 0; s < splits; ++s) L = fmaf(exp2_rel(part[s * (D + 2)], M), part[s * (D + 2) + 1], L);
-  for (int c = threadIdx.x; c < D; c += 64) {
-    float acc = 0.f;
-    for (int s = 0; s < splits; ++s)
-      acc = fmaf(exp2_rel(part[s * (D + 2)], M), part[s * (D + 2) + 2 + c], acc);
-    out[static_cast<int64_t>(bh) * D + c] = acc / L;
+  // ---- the last block of this (sequence, KV head) merges every partial ------
+  // (of every query row of the sequence: nq * splits blocks arrive). Partials
+  // are written and read at device scope; every wave's stores have completed
+  // before the block's arrival is counted, and the counter is returned to zero
+  // for the next call. M = max_s m_s; out = sum_s 2^(m_s-M) o_s / sum_s 2^(m_s-M) l_s.
+  __shared__ int last_block;
+  wait_vm<0>();
+  __syncthreads();
+  const int unit = b * p.kv_heads + h;   // one arrival counter for every row of b
+  if (tid == 0) {
+    const int done = __hip_atomic_fetch_add(&p.counters[unit], 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    last_block = done == p.nq * p.splits - 1;
   }
+  __syncthreads();
+  if (!last_block) return;
+  for (int i = tid; i < p.nq * HG * D; i += kThreads) {
+    const int r = b * p.nq + i / (HG * D), g = (i / D) % HG, c = i % D;
+    const float* part = p.partials +
+                        ((static_cast<int64_t>(r) * p.q_heads + h * HG + g) * p.splits) * (D + 2);
+    float M = -INFINITY;
+    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, load_coherent(part + s * (D + 2)));
+    float so = 0.f, sl = 0.f;
+    for (int s = 0; s < p.splits; ++s) {
+      const float e = exp2_rel(load_coherent(part + s * (D + 2)), M);
+      sl = fmaf(e, load_coherent(part + s * (D + 2) + 1), sl);
+      so = fmaf(e, load_coherent(part + s * (D + 2) + 2 + c), so);
+    }
+    p.out[(static_cast<int64_t>(r) * p.q_heads + h * HG + g) * D + c] = so / sl;
+  }
+  if (tid == 0)
+    __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int SCHEME, int BITS, int VB, int D, int HG>
 hipError_t launch(const DecodeParams& p, int batch, hipStream_t st) {
   dim3 grid(p.splits, p.kv_heads, batch * p.nq);
   hipLaunchKernelGGL((decode_split_kernel<SCHEME, BITS, VB, D, HG>), grid, dim3(kThreads), 0, st, p);
-  if (p.splits > 1) {
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_merge(p.partials, p.out, batch * p.nq * p.q_heads, p.splits, D, st);
-  }
   return hipGetLastError();
 }
 
@@ -451,17 +464,6 @@ hipError_t by_d(const DecodeParams& p, int d, int hg, int batch, hipStream_t st)
 
 }  // namespace
 
-hipError_t launch_merge(float* partials, float* out, int rows, int splits, int d,
-                        hipStream_t st) {
-  switch (d) {
-    case 32: hipLaunchKernelGGL((decode_merge_kernel<32>), dim3(rows), dim3(64), 0, st, partials, out, splits); break;
-    case 64: hipLaunchKernelGGL((decode_merge_kernel<64>), dim3(rows), dim3(64), 0, st, partials, out, splits); break;
-    case 128: hipLaunchKernelGGL((decode_merge_kernel<128>), dim3(rows), dim3(64), 0, st, partials, out, splits); break;
-    default: hipLaunchKernelGGL((decode_merge_kernel<256>), dim3(rows), dim3(64), 0, st, partials, out, splits); break;
-  }
-  return hipGetLastError();
-}
-
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   const Geometry& g = a.g;
   // several queries per sequence: the matrix-core KIVI kernel when each
@@ -477,6 +479,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   p.v_scale = a.v_scale;
   p.out = a.out;
   p.partials = reinterpret_cast<float*>(a.workspace + workspace_partials_offset(g));
+  p.counters = reinterpret_cast<int*>(a.workspace);
   p.slab_bytes = g.slab_bytes;
   p.page_bytes = g.page_bytes;
   p.ring_base = g.pages_per_slab * g.page_bytes;

@@ -100,9 +100,6 @@ hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t stream);
 bool fp8_mfma_path(const Geometry& g);
 int32_t fp8_mfma_splits(const Geometry& g, int64_t tokens, int32_t requested);
 hipError_t launch_fp8_mfma(const DecodeArgs& a, hipStream_t stream);
-// Merges `splits` partials (m, l, o[d]) per row into out (rows = batch*q_heads).
-hipError_t launch_merge(float* partials, float* out, int rows, int splits, int d,
-                        hipStream_t stream);
 
 // Decode split plan, shared by kvq_cache_bytes(WORKSPACE) and the launcher.
 int32_t decode_items(const Geometry& g, int64_t tokens);
