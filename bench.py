@@ -55,7 +55,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 COUNTERS = {
     "kivi2": {"context": 4119, "fetch_kib": 31156.8125, "write_kib": 892.0,
               "fetch_scale": 262144 / 131084, "write_scale": 1.0,
-              "sources_sha256": "7082056e957c65e67db2a28599194c3c4969ca150b34f40e134e04cd76a69b9a"},
+              "sources_sha256": "7b8112d3f1ff0cd93f2b4c0d6cce7e8d37740f10046d88a13bfb79e7871bf8ee"},
 }
 DECODE_SOURCES = ["decode_mfma.hip", "kvq_device.h", "kvq_internal.h", "kvq_wave.h"]
 
