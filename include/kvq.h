@@ -323,11 +323,11 @@ KVQ_API int32_t kvq_decode_attention_ragged(const kvq_config* cfg, const void* c
  *   workspace  >= n_queries * kvq_cache_bytes(cfg, tokens, KVQ_BYTES_WORKSPACE),
  *              zero-filled before first use (as for kvq_decode_attention)
  * Other arguments, requirements and errors as kvq_decode_attention. With
- * n_queries > 1, KIVI caches of 16-bit inputs whose queries' own tokens are
- * all in the residual ring (n_queries <= tokens - q(tokens)) run on the
- * matrix-core kernel, one row of blocks per query, and so do FP8 and
- * bfloat16 caches without in-kernel rotary embedding (head_dim >= 64); every
- * other case runs on the generic (vector-ALU) kernel. */
+ * n_queries > 1, KIVI caches of 16-bit inputs run on the matrix-core kernel,
+ * one row of blocks per query (a query whose token is in a quantised page
+ * sees that page masked after its token), and so do FP8 and bfloat16 caches
+ * without in-kernel rotary embedding (head_dim >= 64); every other case runs
+ * on the generic (vector-ALU) kernel. */
 KVQ_API int32_t kvq_decode_attention_multi(const kvq_config* cfg, const void* cache,
                                    int32_t layer, int64_t tokens, int32_t n_queries,
                                    const void* q, const float* k_scale,

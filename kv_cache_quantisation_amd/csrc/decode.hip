@@ -466,9 +466,8 @@ hipError_t by_d(const DecodeParams& p, int d, int hg, int batch, hipStream_t st)
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   const Geometry& g = a.g;
-  // several queries per sequence: the matrix-core KIVI kernel when each
-  // query's own token is in the ring, the FP8/bfloat16 one always, else the
-  // generic kernel
+  // several queries per sequence: the matrix-core KIVI and FP8/bfloat16
+  // kernels where they apply, else the generic kernel
   if (a.nq <= 1 && mfma_path(g)) return launch_kivi_mfma(a, st);
   if (a.nq > 1 && !a.seq_tokens && mfma_multi_ok(g, a.tokens, a.nq)) return launch_kivi_mfma(a, st);
   if (fp8_mfma_path(g) && (a.nq <= 1 || !a.seq_tokens)) return launch_fp8_mfma(a, st);

@@ -396,10 +396,14 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
     n_pages = static_cast<int32_t>(q_tokens / kPage);
   }
   // query qi of nq sits at position fill - nq + qi and sees the tokens up to
-  // it: all pages, and the ring up to its own token (the host sends several
-  // queries here only when each of their tokens is in the ring)
+  // it: the pages and the ring up to its own token, or, when its token is in
+  // a page, the pages up to that one (the rest of that page masked)
   const int64_t Tb = fill - (p.nq - 1 - qi);
   if (p.seq_tokens || p.nq > 1) n_steps = static_cast<int32_t>((Tb - q_tokens + 7) / 8);
+  if (Tb <= q_tokens) {
+    n_pages = static_cast<int32_t>((Tb + kPage - 1) / kPage);
+    n_steps = 0;
+  }
   uint8_t* wbuf = arena + wave * WAVE_LDS;
   uint32_t (*frag)[4] = reinterpret_cast<uint32_t (*)[4]>(wbuf + PG::NBUF * PG::BYTES);
 
@@ -640,6 +644,14 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
     }
     }   // rotary / plain keys
 
+    if (Tb - t0 < kPage) {   // the query's own token is in this page (wave-uniform)
+      const int nvalid = static_cast<int>(Tb - t0);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (tile_tok<ROPE>(mt, 4 * g + r) >= nvalid) s[4 * mt + r] = -INFINITY;
+    }
     softmax_update(s, std::integral_constant<int, 8>{});
     // per-token value scale and offset of this lane's tokens tile_tok(mt, 4g + r)
     constexpr int VT0 = ROPE ? 16 : 32, VT1 = ROPE ? 64 : 16;
@@ -1065,9 +1077,13 @@ __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
     q_tokens = kivi_quantised(fill, p.residual);
     n_pages = static_cast<int32_t>(q_tokens / kPage);
   }
-  // query qi of nq: position fill - nq + qi, in the ring (as above)
+  // query qi of nq: position fill - nq + qi (as above)
   const int64_t Tb = fill - (p.nq - 1 - qi);
   if (p.seq_tokens || p.nq > 1) n_steps = static_cast<int32_t>((Tb - q_tokens + 7) / 8);
+  if (Tb <= q_tokens) {
+    n_pages = static_cast<int32_t>((Tb + kPage - 1) / kPage);
+    n_steps = 0;
+  }
 
   const int pg0 = static_cast<int>(static_cast<int64_t>(split) * n_pages / p.splits);
   const int pg1 = static_cast<int>(static_cast<int64_t>(split + 1) * n_pages / p.splits);
@@ -1370,7 +1386,14 @@ __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
       }
       rotate_mfma(y, part, c);
     }
-    const floatx4 w = softmax(finish_scores(c));
+    floatx4 sc = finish_scores(c);
+    if (Tb - t0 < kPage) {   // the query's own token is in this page (wave-uniform)
+      const int nvalid = static_cast<int>(Tb - t0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (4 * ((lane >> 2) & 7) + r >= nvalid) sc[r] = -INFINITY;
+    }
+    const floatx4 w = softmax(sc);
     // P' = p * s_t; sums of p and p * z_t (lanes < 32 own the tokens)
     const int t0q = 4 * ((lane >> 2) & 7);
     const float4 vs = *reinterpret_cast<const float4*>(pg + PG::OFF_VS + 4 * t0q);
@@ -1557,7 +1580,7 @@ MfmaPlan mfma_plan(const Geometry& g, int64_t tokens, int32_t requested) {
 }
 
 bool mfma_multi_ok(const Geometry& g, int64_t tokens, int32_t nq) {
-  return mfma_path(g) && nq <= tokens - kivi_quantised(tokens, g.residual);
+  return mfma_path(g) && nq >= 1 && nq <= tokens;
 }
 
 hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t st) {

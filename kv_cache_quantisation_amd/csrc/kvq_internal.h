@@ -91,8 +91,8 @@ struct MfmaPlan {
   int32_t pages, chunks, page_splits, ring_splits, ring_splits_max;
 };
 bool mfma_path(const Geometry& g);
-// Several queries (nq) of a uniform batch on the KIVI matrix-core kernel:
-// mfma_path, and every query's own token is an unquantised ring token.
+// Several queries (nq) of a uniform batch on the KIVI matrix-core kernel
+// (mfma_path; queries whose tokens are in pages see a masked last page).
 bool mfma_multi_ok(const Geometry& g, int64_t tokens, int32_t nq);
 MfmaPlan mfma_plan(const Geometry& g, int64_t tokens, int32_t requested);
 hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t stream);

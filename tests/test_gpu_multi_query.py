@@ -2,9 +2,10 @@
 (kvq_decode_attention_multi): query i at position T - n_q + i attends to
 tokens [0, T - n_q + i] of the cache, compared with the oracle's decode_multi
 (float64) on the same seeded inputs, for every scheme, with and without
-rotary keys, queries whose tokens sit in KIVI's ring (the matrix-core kernel,
-when the cache's inputs are 16-bit) or in its pages (the generic kernel), and
-FP8 and bfloat16 caches (their matrix-core kernel without rotary keys)."""
+rotary keys, queries whose tokens sit in KIVI's ring or in its pages (the
+matrix-core kernel when the cache's inputs are 16-bit, the generic kernel for
+fp32 inputs), and FP8 and bfloat16 caches (their matrix-core kernel without
+rotary keys)."""
 
 import pytest
 import torch
@@ -34,7 +35,13 @@ CASES = [
     (synth.KIVI, 2, 64, 1, torch.bfloat16, 32, 200, 0.0, 1, 6),          # one split: no merge
     (synth.KIVI, 2, 128, 4, torch.bfloat16, 32, 100, 0.0, 0, 36),        # n_q = ring tokens
     (synth.KIVI, 2, 128, 4, torch.bfloat16, 128, 90, 0.0, 0, 7),         # no pages yet
-    (synth.KIVI, 2, 128, 4, torch.bfloat16, 32, 100, 0.0, 0, 37),        # one more: generic
+    (synth.KIVI, 2, 128, 4, torch.bfloat16, 32, 100, 0.0, 0, 37),        # one more: in a page
+    # queries whose tokens are in pages (chunks longer than the ring): each
+    # row's last page masked after its own token
+    (synth.KIVI, 2, 128, 4, torch.bfloat16, 32, 300, 10000.0, 0, 70),    # rotary, GQA 4
+    (synth.KIVI, 2, 64, 2, torch.bfloat16, 0, 150, 500000.0, 2, 40),     # rotary, GQA 2
+    (synth.KIVI, 4, 128, 4, torch.bfloat16, 32, 200, 0.0, 0, 100),
+    (synth.KIVI, 2, 128, 8, torch.bfloat16, 128, 640, 0.0, 0, 300),
     # FP8 and bfloat16 caches without rotary keys: their matrix-core kernel
     (synth.FP8_E5M2, 8, 128, 8, torch.bfloat16, 0, 301, 0.0, 3, 45),     # queries across pages
     (synth.BF16_CACHE, 16, 64, 2, torch.bfloat16, 0, 77, 0.0, 1, 9),     # one split: no merge
