@@ -53,9 +53,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 # kernel sources they were taken with (SHA-256 over DECODE_SOURCES); after any
 # change to those, `traffic` is reported as null until they are taken again.
 COUNTERS = {
-    "kivi2": {"context": 4119, "fetch_kib": 31156.8125, "write_kib": 892.0,
+    "kivi2": {"context": 4119, "fetch_kib": 31157.5, "write_kib": 892.0,
               "fetch_scale": 262144 / 131084, "write_scale": 1.0,
-              "sources_sha256": "7b8112d3f1ff0cd93f2b4c0d6cce7e8d37740f10046d88a13bfb79e7871bf8ee"},
+              "sources_sha256": "2d92ff7a6f69489e870c03fec846a6dbe5b6a876644eb61db14bcb0c88af816b"},
 }
 DECODE_SOURCES = ["decode_mfma.hip", "kvq_device.h", "kvq_internal.h", "kvq_wave.h"]
 
