@@ -42,6 +42,11 @@ CASES = [
     (synth.KIVI, 2, 64, 2, torch.bfloat16, 0, 150, 500000.0, 2, 40),     # rotary, GQA 2
     (synth.KIVI, 4, 128, 4, torch.bfloat16, 32, 200, 0.0, 0, 100),
     (synth.KIVI, 2, 128, 8, torch.bfloat16, 128, 640, 0.0, 0, 300),
+    # every token a query (the first sees token 0 alone): all in pages, all
+    # in the ring, rotary
+    (synth.KIVI, 2, 128, 4, torch.bfloat16, 0, 64, 0.0, 0, 64),
+    (synth.KIVI, 2, 128, 4, torch.bfloat16, 128, 50, 0.0, 0, 50),
+    (synth.KIVI, 2, 128, 4, torch.bfloat16, 0, 96, 10000.0, 0, 96),
     # FP8 and bfloat16 caches without rotary keys: their matrix-core kernel
     (synth.FP8_E5M2, 8, 128, 8, torch.bfloat16, 0, 301, 0.0, 3, 45),     # queries across pages
     (synth.BF16_CACHE, 16, 64, 2, torch.bfloat16, 0, 77, 0.0, 1, 9),     # one split: no merge
