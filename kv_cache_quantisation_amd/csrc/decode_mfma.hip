@@ -320,13 +320,15 @@ constexpr int kivi_blocks_per_cu(int bits, int d, bool rope) {
 }
 
 // Waves per block of kivi_mfma_kernel<kb, vb, d, hg, rope>: eight for 2-bit
-// pages at d <= 128 and GQA groups up to 4 (run as one block per CU: half the
-// blocks, and half the partials to merge, of four-wave blocks; 19.8 vs 20.5 us
-// at batch 16, context 4096), four otherwise. Eight-wave blocks still fit two
-// per CU (71.7 KB of LDS, <= 128 VGPRs), which kivi_blocks_per_cu(2, d, false)
-// = 3 would only tighten, so their launch bound asks for two.
+// value codes (2- or 4-bit keys) at d <= 128 and GQA groups up to 4 (run as
+// one block per CU: half the blocks, and half the partials to merge, of
+// four-wave blocks; 2-bit keys 19.8 vs 20.5 us, 4-bit keys 21.5-21.8 vs
+// 23.0-23.2 us at batch 16, context 4096), four otherwise. Eight-wave 2-bit
+// blocks still fit two per CU (71.7 KB of LDS, <= 128 VGPRs), which
+// kivi_blocks_per_cu(2, d, false) = 3 would only tighten, so their launch
+// bound asks for two (4-bit keys: 88 KB of LDS, one per CU).
 constexpr int kivi_waves(int kb, int vb, int d, int hg, bool rope) {
-  return (kb == 2 && vb == 2 && d <= 128 && hg <= 4 && !rope) ? 8 : 4;
+  return ((kb == 2 || kb == 4) && vb == 2 && d <= 128 && hg <= 4 && !rope) ? 8 : 4;
 }
 
 // KB, VB: bits of the key and of the value codes
