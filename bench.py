@@ -53,9 +53,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 # kernel sources they were taken with (SHA-256 over DECODE_SOURCES); after any
 # change to those, `traffic` is reported as null until they are taken again.
 COUNTERS = {
-    "kivi2": {"context": 4119, "fetch_kib": 31156.75, "write_kib": 892.0,
+    "kivi2": {"context": 4119, "fetch_kib": 31153.0, "write_kib": 892.0,
               "fetch_scale": 262144 / 131084, "write_scale": 1.0,
-              "sources_sha256": "ad19470475682d24b0b9309a93f9c245a24cacdbca7324d6311c2bd3780a1949"},
+              "sources_sha256": "e1c91bf6ae9a72cae9310259a9c3b88d1e042af8a1577615706c58696e4d665f"},
 }
 DECODE_SOURCES = ["decode_mfma.hip", "kvq_device.h", "kvq_internal.h", "kvq_wave.h"]
 

@@ -402,7 +402,8 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   // a page, the pages up to that one (the rest of that page masked)
   const int64_t Tb = fill - (p.nq - 1 - qi);
   if (p.seq_tokens || p.nq > 1) n_steps = static_cast<int32_t>((Tb - q_tokens + 7) / 8);
-  if (Tb <= q_tokens) {
+  const bool in_page = Tb <= q_tokens;   // block-uniform: mask this row's last page
+  if (in_page) {
     n_pages = static_cast<int32_t>((Tb + kPage - 1) / kPage);
     n_steps = 0;
   }
@@ -646,7 +647,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
     }
     }   // rotary / plain keys
 
-    if (Tb - t0 < kPage) {   // the query's own token is in this page (wave-uniform)
+    if (in_page && Tb - t0 < kPage) {   // the query's own token is in this page
       const int nvalid = static_cast<int>(Tb - t0);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
@@ -1082,7 +1083,8 @@ __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
   // query qi of nq: position fill - nq + qi (as above)
   const int64_t Tb = fill - (p.nq - 1 - qi);
   if (p.seq_tokens || p.nq > 1) n_steps = static_cast<int32_t>((Tb - q_tokens + 7) / 8);
-  if (Tb <= q_tokens) {
+  const bool in_page = Tb <= q_tokens;   // block-uniform: mask this row's last page
+  if (in_page) {
     n_pages = static_cast<int32_t>((Tb + kPage - 1) / kPage);
     n_steps = 0;
   }
@@ -1389,7 +1391,7 @@ __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
       rotate_mfma(y, part, c);
     }
     floatx4 sc = finish_scores(c);
-    if (Tb - t0 < kPage) {   // the query's own token is in this page (wave-uniform)
+    if (in_page && Tb - t0 < kPage) {   // the query's own token is in this page
       const int nvalid = static_cast<int>(Tb - t0);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
