@@ -20,12 +20,23 @@ bounded sample.
 
 Roofline: the decode kernel's algorithmic bytes per launch (the bytes a decode
 call must move: packed codes, scales and offsets of every page, the residual
-rows, the query and the output) divided by its average launch duration. That
-duration is measured with HIP events recorded on the launch stream around a
-burst of back-to-back decode launches over the 32 layers (so no host launch
-latency is counted), after the timed steps. `--copy-calibration` runs only a
-plain device-to-device copy of 256 MiB, whose hardware FETCH_SIZE/WRITE_SIZE
+rows, the query and the output) divided by its launch duration. After the
+timed steps every layer is filled up to a fixed context (the workload's 4096
+tokens + 64), so the roofline launch is the same whatever --steps and --warmup
+are (up to 64 together); bursts of back-to-back decode launches over the 32
+layers run for at least --roofline-ms, each burst between HIP events recorded
+on the launch stream (no host launch latency is counted), and the mean, median
+and minimum per launch are reported. `--copy-calibration` runs only a plain
+device-to-device copy of 256 MiB, whose hardware FETCH_SIZE/WRITE_SIZE
 counters calibrate the decode kernel's counter readings into HBM bytes.
+
+Per-workload rows: prefill quantize-append tokens/s, the one-token append and
+the decode of each of the five workloads at full size (tiny, kivi2, fp8, int4,
+longctx), each decode against the HBM roofline.
+
+CPU baseline: the oracle, on a pool of host processes forked before the first
+GPU call, one per host core of this process's CPU share (at most 16), each on
+its own whole (sequence, KV head) units of the workload for a bounded time.
 """
 
 import argparse
@@ -45,21 +56,19 @@ import synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 
 # Hardware byte counters of the decode kernel (rocprofv3 --pmc, FETCH_SIZE and
-# WRITE_SIZE in separate runs of this script with its default settings; median
-# KiB per dispatch over the roofline burst at context 4119), with the scale that
-# turns each counter into bytes: a plain 256 MiB device copy
+# WRITE_SIZE in separate runs of `bench.py --gpus 1 --steps 20 --warmup 5`;
+# median KiB per dispatch of the roofline launches at the fixed context), with
+# the scale that turns each counter into bytes: a plain 256 MiB device copy
 # (`--copy-calibration`) reads FETCH_SIZE = 131084 KiB for 262144 KiB read and
 # WRITE_SIZE = 262144 KiB for 262144 KiB written. The readings hold only for the
 # kernel sources they were taken with (SHA-256 over DECODE_SOURCES); after any
 # change to those, `traffic` is reported as null until they are taken again.
+ROOFLINE_EXTRA = 64            # roofline context = workload tokens + this
 COUNTERS = {
-    "kivi2": {"context": 4119, "fetch_kib": 31153.0, "write_kib": 892.0,
+    "kivi2": {"context": 4096 + ROOFLINE_EXTRA, "fetch_kib": None, "write_kib": None,
               "fetch_scale": 262144 / 131084, "write_scale": 1.0,
-              "sources_sha256": "e1c91bf6ae9a72cae9310259a9c3b88d1e042af8a1577615706c58696e4d665f"},
+              "sources_sha256": ""},
 }
-DECODE_SOURCES = ["decode_mfma.hip", "kvq_device.h", "kvq_internal.h", "kvq_wave.h"]
-
-
 def decode_sources_sha256():
     import hashlib
     h = hashlib.sha256()
@@ -278,8 +287,9 @@ def gpu_bench(args, w):
     append_tps = w.batch * T0 / (prefill_ms * 1e-3)
     prefill_bytes = append_bytes(w, 0, T0)
 
-    # per-layer inputs of the decode steps
-    news = [synth.keys_values(w, layer=layer, tokens=W + K, device=dev, tag=1) for layer in range(L)]
+    # per-layer inputs of the decode steps (and of the fill up to the roofline context)
+    n_new = max(W + K, ROOFLINE_EXTRA)
+    news = [synth.keys_values(w, layer=layer, tokens=n_new, device=dev, tag=1) for layer in range(L)]
     qs = [synth.query(w, layer=layer, device=dev) for layer in range(L)]
     outs = [torch.empty(q.shape, dtype=torch.float32, device=dev) for q in qs]
 
@@ -310,22 +320,40 @@ def gpu_bench(args, w):
                       for i in range(W, W + K))
     gbs = total_bytes / (total_ms * 1e-3) / 1e9
 
-    # decode kernel alone: HIP events on the launch stream around bursts of
-    # back-to-back launches (every layer once per burst)
-    T_end = T0 + W + K
-    n_rep = 4
+    # decode kernel alone, at a fixed context: every layer is filled up to
+    # T0 + ROOFLINE_EXTRA tokens (whatever the step counts were), then bursts
+    # of back-to-back launches over the 32 layers, each burst between HIP
+    # events on the launch stream, for at least roofline_ms
+    T_end = T0 + max(W + K, ROOFLINE_EXTRA)
+    for i in range(W + K, T_end - T0):
+        for layer in range(L):
+            kvq.kvq_quantize_append(cfg, cache, layer, T0 + i, 1, news[layer][0][i],
+                                    news[layer][1][i], stream=stream)
     for layer in range(L):   # warm the launch path at this context length
         kvq.kvq_decode_attention(cfg, cache, layer, T_end, qs[layer], outs[layer], ws, stream=stream)
     torch.cuda.synchronize()
+    burst_us = []
+    spent = 0.0
+    while spent < args.roofline_ms * 1e-3 or len(burst_us) < 8:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(32)]
+        for a, b in evs:
+            a.record(stream)
+            for layer in range(L):
+                kvq.kvq_decode_attention(cfg, cache, layer, T_end, qs[layer], outs[layer], ws,
+                                         stream=stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        for a, b in evs:
+            us = a.elapsed_time(b) * 1e3 / L
+            burst_us.append(us)
+            spent += us * L * 1e-6
+    burst_us.sort()
+    avg_us = sum(burst_us) / len(burst_us)
+    med_us = burst_us[len(burst_us) // 2]
+    min_us = burst_us[0]
+    n_rep = 4
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(n_rep):
-        for layer in range(L):
-            kvq.kvq_decode_attention(cfg, cache, layer, T_end, qs[layer], outs[layer], ws,
-                                     stream=stream)
-    b.record(stream)
-    torch.cuda.synchronize()
-    avg_us = a.elapsed_time(b) * 1e3 / (n_rep * L)
     graph = graph_replay(cfg, cache, ws, qs, outs, news, L, T_end, n_rep)
     cache_bytes = int(cache.numel())
 
@@ -394,8 +422,12 @@ def gpu_bench(args, w):
                 "traffic": counter_traffic(w, T_end),
                 "kernel": f"kivi_mfma_kernel<{w.bits},{w.v_bits or w.bits},{w.head_dim},"
                           f"{w.q_heads // w.kv_heads}> (decode, merge fused)",
-                "avg_launch_us": round(avg_us, 3), "bytes_per_launch": per_launch,
-                "context": T_end}
+                "avg_launch_us": round(avg_us, 3), "median_launch_us": round(med_us, 3),
+                "min_launch_us": round(min_us, 3),
+                "frac_at_median": round(per_launch / (med_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "launches": len(burst_us) * L,
+                "timed_ms": round(sum(burst_us) * L * 1e-3, 1),
+                "bytes_per_launch": per_launch, "context": T_end}
     return {
         "ms_per_step": total_ms / K, "gbs": gbs, "append_tps": append_tps,
         "prefill_ms_per_layer": prefill_ms, "prefill_gbs": prefill_bytes / (prefill_ms * 1e-3) / 1e9,
@@ -474,20 +506,23 @@ def copy_ceiling(gib=1, reps=10):
     return round(2 * n * 4 / us / 1e3, 1)
 
 
-def cpu_baseline(w, layers, budget_s=12.0):
-    """The oracle (as it stands) on a bounded sample of the workload: decode
-    attention of whole (sequence, KV head) units at the workload's context,
-    layer after layer, each unit quantised, dequantised and attended by the
-    oracle on one host thread, until about budget_s seconds of oracle work."""
+def _oracle_units(job):
+    """Worker of the CPU baseline (a process of the pool): the oracle on whole
+    (sequence, KV head) units of the workload, layer after layer from `first`
+    in steps of `stride`, until `budget_s` seconds of oracle time. Returns
+    (units, algorithmic decode bytes of those units, oracle seconds)."""
+    name, first, stride, layers, budget_s = job
     import numpy as np
     from oracle.cache import OracleCache
     from threadpoolctl import threadpool_limits
+    torch.set_num_threads(1)
+    w = synth.WORKLOADS[name]
     hg = w.q_heads // w.kv_heads
     T = w.tokens
     one = synth.scaled(w, batch=1, kv_heads=1, q_heads=hg)
     done, spent = 0, 0.0
     with threadpool_limits(limits=1):
-        for layer in range(layers):
+        for layer in range(first, layers, stride):
             k, v = synth.keys_values(w, layer=layer, device="cpu")
             q = synth.query(w, layer=layer, device="cpu")
             raw_k = k.view(torch.int16).numpy().view(np.uint16)
@@ -502,18 +537,129 @@ def cpu_baseline(w, layers, budget_s=12.0):
                     spent += time.perf_counter() - t0
                     done += 1
                     if spent > budget_s:
-                        break
-                if spent > budget_s:
-                    break
+                        return done, decode_bytes(one, T) * done, spent
             del k, v
-            if spent > budget_s:
-                break
-    byts = decode_bytes(one, T) * done
-    return {"value": round(byts / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} (sequence, KV head) units at {T} tokens (layers in order, "
-                      f"{w.batch * w.kv_heads} units per layer): oracle quantise + fp64 "
-                      f"dequantise + fp64 attention, {spent:.1f} s of oracle time on one host "
-                      f"thread; value = algorithmic decode bytes of those units / that time"}
+    return done, decode_bytes(one, T) * done, spent
+
+
+def host_cpu():
+    """(cores this process may run on, capped at the 16 of a one-GPU share;
+    CPU model name)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return min(n, 16), n, model
+
+
+def cpu_pool():
+    """A pool of host processes for the oracle, forked before any GPU call
+    (and before torch runs any CPU op), one per usable core."""
+    import multiprocessing as mp
+    cores, _, _ = host_cpu()
+    return mp.get_context("fork").Pool(cores), cores
+
+
+def cpu_baseline(pool, cores, w, budget_s=12.0):
+    """The oracle (as it stands: numpy, fp64 attention) on a bounded sample of
+    the workload, in parallel on `cores` host processes: each takes whole
+    (sequence, KV head) units -- quantise, dequantise and attend -- of its own
+    layers for about budget_s seconds. value = the sum of the processes'
+    rates (algorithmic decode bytes of their units / their oracle time)."""
+    # process i takes layers i, i + cores, ... (synthetic layers beyond the
+    # model's 32 are drawn the same way) until its budget is spent
+    jobs = [(w.name, i, cores, 1 << 20, budget_s) for i in range(cores)]
+    res = pool.map(_oracle_units, jobs)
+    units = sum(r[0] for r in res)
+    rate = sum(r[1] / r[2] for r in res if r[2] > 0)
+    _, avail, model = host_cpu()
+    return {"value": round(rate / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "host_cores_available": avail, "cpu_model": model,
+            "sample": f"{units} (sequence, KV head) units of {w.name} at {w.tokens} tokens, "
+                      f"{cores} processes x ~{budget_s:.0f} s of oracle time (numpy, one thread "
+                      f"each): quantise + fp64 dequantise + fp64 attention per unit; value = "
+                      f"sum over processes of algorithmic decode bytes / oracle time"}
+
+
+def config_row(name, dec_reps=20, pre_reps=3):
+    """One workload at full size on its own cache: prefill quantize-append of
+    the whole context (one call), the one-token append, and the decode over
+    context + 1 tokens, each launch timed between HIP events on the launch
+    stream (median and minimum)."""
+    dev = torch.device("cuda", 0)
+    w = synth.WORKLOADS[name]
+    T = w.tokens
+    dt = {torch.bfloat16: kvq.KVQ_BF16, torch.float32: kvq.KVQ_F32}
+    cfg = kvq.make_config(w.scheme, w.bits, 1, w.q_heads, w.kv_heads, w.head_dim, w.batch, T + 1,
+                          v_bits=w.v_bits, residual=w.residual, in_dtype=dt[w.in_dtype],
+                          q_dtype=dt[w.q_dtype], rope_theta=w.rope_theta)
+    cache = kvq.alloc_cache(cfg, device=dev, zero=False)
+    k, v = synth.keys_values(w, device=dev)
+    ks = vs = None
+    if w.scheme == synth.FP8_E4M3:
+        ks, vs = synth.fp8_scales(k, v)
+    stream = torch.cuda.current_stream()
+
+    def each(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+
+    pre = each(lambda: kvq.kvq_quantize_append(cfg, cache, 0, 0, T, k, v, ks, vs, stream=stream),
+               pre_reps)
+    del k, v
+    k1, v1 = synth.keys_values(w, tokens=1, device=dev, tag=1)
+    app = each(lambda: kvq.kvq_quantize_append(cfg, cache, 0, T, 1, k1, v1, ks, vs, stream=stream),
+               dec_reps)
+    q = synth.query(w, device=dev)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    ws = kvq.alloc_workspace(cfg, T + 1, device=dev)
+    dec = each(lambda: kvq.kvq_decode_attention(cfg, cache, 0, T + 1, q, out, ws, k_scale=ks,
+                                                v_scale=vs, stream=stream), dec_reps)
+    del cache, ws
+    torch.cuda.empty_cache()
+    med = lambda xs: xs[len(xs) // 2]   # noqa: E731
+    dec_b, pre_b = any_decode_bytes(w, T + 1), any_append_bytes(w, 0, T)
+    return {
+        "workload": name, "batch": w.batch, "context": T + 1, "bits": w.bits,
+        "kernel": decode_kernel_name(w),
+        "decode_us_median": round(med(dec), 2), "decode_us_min": round(dec[0], 2),
+        "decode_bytes": dec_b, "decode_gbs": round(dec_b / med(dec) / 1e3, 1),
+        "decode_frac_of_hbm_peak": round(dec_b / med(dec) / 1e3 / HBM_PEAK_GBS, 4),
+        "prefill_us_median": round(med(pre), 2), "prefill_bytes": pre_b,
+        "prefill_tokens_per_s": round(w.batch * T / (med(pre) * 1e-6)),
+        "prefill_frac_of_hbm_peak": round(pre_b / med(pre) / 1e3 / HBM_PEAK_GBS, 4),
+        "append1_us_median": round(med(app), 2),
+    }
+
+
+def decode_kernel_name(w):
+    """The decode kernel the library runs for workload w (for reading profiles)."""
+    hg = w.q_heads // w.kv_heads
+    if w.scheme == synth.KIVI and w.rope_theta > 0:
+        return f"rope4_kernel<{w.head_dim},4>" if hg == 4 else \
+            f"kivi_mfma_kernel<2,2,{w.head_dim},{hg},true>"
+    if w.scheme == synth.KIVI and w.bits in (2, 4) and w.in_dtype == torch.bfloat16:
+        return f"kivi_mfma_kernel<{w.bits},{w.v_bits or w.bits},{w.head_dim},{hg},false>"
+    if w.scheme == synth.FP8_E4M3 and w.head_dim >= 64:
+        return f"paged_mfma_kernel<FP8_E4M3,{w.head_dim},{hg}>"
+    return f"decode_split_kernel<scheme {w.scheme},{w.bits},{w.head_dim},{hg}>"
 
 
 def copy_calibration(mib=256, reps=5):
@@ -536,13 +682,22 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--workload", default="kivi2")
+    ap.add_argument("--roofline-ms", type=float, default=200.0,
+                    help="minimum time of the roofline decode bursts")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload rows")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device copy (counter calibration)")
     ap.add_argument("--workload-kernels", nargs="*", metavar="NAME",
                     help="only time prefill, 1-token append and decode of the named "
                          "workloads at full size (one JSON line each)")
     args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the hot path shards "
+              "by (sequence, KV head) with no communication, so more GPUs only repeat the "
+              "one-GPU kernel on their own cache slabs", file=sys.stderr)
+        sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
         return
@@ -551,17 +706,36 @@ def main():
             print(json.dumps(workload_kernels(name)), flush=True)
             torch.cuda.empty_cache()
         return
-    if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the hot path shards "
-              "by (sequence, KV head) with no communication, so more GPUs only repeat the "
-              "one-GPU kernel on their own cache slabs", file=sys.stderr)
-        sys.exit(2)
     w = synth.WORKLOADS[args.workload]
     if w.scheme != synth.KIVI:
         sys.exit("bench.py times the KIVI workloads")
+    # the oracle's process pool is forked before anything touches the GPU
+    pool, cores = (None, 0) if args.no_cpu_baseline else cpu_pool()
     r = gpu_bench(args, w)
     base_us = bf16_baseline_decode_us(w, tokens=r["roofline"]["context"])
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.layers)
+    rows = []
+    if not args.no_configs:
+        ro = r["roofline"]
+        rows.append({
+            "workload": w.name, "batch": w.batch, "context": ro["context"], "bits": w.bits,
+            "kernel": decode_kernel_name(w), "layers": args.layers,
+            "decode_us_median": ro["median_launch_us"], "decode_us_min": ro["min_launch_us"],
+            "decode_bytes": ro["bytes_per_launch"],
+            "decode_gbs": round(ro["bytes_per_launch"] / ro["median_launch_us"] / 1e3, 1),
+            "decode_frac_of_hbm_peak": ro["frac_at_median"],
+            "prefill_us_median": round(r["prefill_ms_per_layer"] * 1e3, 2),
+            "prefill_tokens_per_s": round(r["append_tps"]),
+            "prefill_frac_of_hbm_peak": round(r["prefill_gbs"] / HBM_PEAK_GBS, 4),
+            "note": "decode rotates over the 32 layer caches (2 GB, beyond the 256 MB "
+                    "Infinity Cache)"})
+        for name in ("tiny", "fp8", "int4", "longctx"):
+            rows.append(config_row(name))
+            torch.cuda.empty_cache()
+    cpu = None
+    if pool is not None:
+        cpu = cpu_baseline(pool, cores, w)
+        pool.close()
+        pool.join()
     line = {
         "metric": METRIC,
         "value": round(r["gbs"], 1),
@@ -573,7 +747,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "u2 codes; f16/bf16 mfma, f32 accumulate",
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: KIVI {w.bits}-bit cache, {args.layers} layers of "
@@ -587,6 +761,7 @@ def main():
         "append_tokens_per_s": round(r["append_tps"]),
         "append_prefill_gbs": round(r["prefill_gbs"], 1),
         "roofline": r["roofline"],
+        "workloads": rows,
         "graph_replay": r["graph"],
         "ragged_decode": r["ragged"],
         "multi_query_decode": r["multi"],

@@ -37,6 +37,19 @@
  *   - KVQ_ERR_DEVICE is returned when a kernel launch reports an error.
  *   - Keys, values and queries must be finite; non-finite input is outside the
  *     contract and not checked.
+ *   - Accuracy of decode, against softmax attention computed exactly (fp64)
+ *     over the dequantised cache: max-abs error <= 2e-3 * max(1, V*(1+S/2)/128),
+ *     where V = max |dequantised value| and S = sum_c |sm_scale*q_c| * K_c with
+ *     K_c the largest |key| of channel c. So the error is within 2e-3 whenever
+ *     V*(1+S/2) <= 128. This is a worst-case bound from the arithmetic: scores
+ *     and accumulators are fp32 (score error <= 2^-20 of the summands'
+ *     magnitude), softmax weights enter the value product as bfloat16 high
+ *     and remainder parts (2^-17 relative). Rounding errors of real inputs do
+ *     not line up, and the measured errors are far below it (1e-6 to 3e-5 on
+ *     the benchmark workloads, which lie well outside the 2e-3 range of the
+ *     bound). No operand saturates: a page whose folded query
+ *     q * s * sm_scale * log2(e) exceeds the f16 maximum (65504) is rescaled
+ *     by a power of two inside the kernel and the scaling undone on its scores.
  *   - Calls on distinct streams are independent; concurrent calls that touch
  *     the same cache slab or workspace race (the caller's responsibility).
  */
@@ -316,8 +329,19 @@ KVQ_API int32_t kvq_decode_attention_ragged(const kvq_config* cfg, const void* c
  * kvq_decode_attention over that prefix, with the KIVI page/ring split of
  * the whole cache ([QKV] going deeper, "Why values per token"; one query per
  * row as kvq_decode_attention computes it).
+ * Causality is over positions, not over the encoding: a KIVI cache is read
+ * as it stands after all `tokens` were appended. A key page's per-channel
+ * scale and offset come from all 32 of its tokens, so a query whose token
+ * sits inside a quantised page reads that page's earlier keys through
+ * statistics that include later tokens; and tokens that a one-query decode
+ * at the query's own fill level would read unquantised from the ring are
+ * read quantised once a later flush has encoded them. Row i therefore equals
+ * kvq_decode_attention over the first tokens - n_queries + i + 1 tokens
+ * exactly when both fill levels quantise the same tokens,
+ * q(tokens - n_queries + i + 1) == q(tokens), and differs slightly otherwise.
  *   n_queries  1 <= n_queries <= tokens (else KVQ_ERR_INVALID); 1 is exactly
- *              kvq_decode_attention
+ *              kvq_decode_attention; batch * n_queries <= 65535 (one row of
+ *              blocks per (sequence, query); else KVQ_ERR_UNSUPPORTED)
  *   q          device [batch][n_queries][q_heads][head_dim], q_dtype
  *   out        device fp32 [batch][n_queries][q_heads][head_dim]
  *   workspace  >= n_queries * kvq_cache_bytes(cfg, tokens, KVQ_BYTES_WORKSPACE),

@@ -180,6 +180,23 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   // (f16 parts against the E4M3 keys, bf16 parts against bf16 keys)
   using BQ = std::conditional_t<BF16, bf16x8, half8>;
   BQ bq[KS];
+  // f16 range of the key operand: a query folded with a large key scale can
+  // exceed 65504, where the f16 high part would saturate; then the wave takes
+  // q' 2^-esc into the product and multiplies its scores by 2^esc (exact)
+  int esc = 0;
+  if constexpr (!BF16) {
+    const int hh = j % HG;
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) amax = fmaxf(amax, fabsf(qs[hh][g * CPG + i]));
+    if (__builtin_amdgcn_ballot_w64(amax > 65504.f) != 0) {
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+      int ex;
+      frexpf(amax, &ex);   // amax < 2^ex
+      esc = __builtin_amdgcn_readfirstlane(ex - 15);
+    }
+  }
   {
     const int hh = j % HG, part = j / HG;
 #pragma unroll
@@ -187,8 +204,8 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
       uint32_t w4[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float a = qs[hh][g * CPG + 8 * ks + 2 * i];
-        const float c = qs[hh][g * CPG + 8 * ks + 2 * i + 1];
+        const float a = ldexpf(qs[hh][g * CPG + 8 * ks + 2 * i], -esc);
+        const float c = ldexpf(qs[hh][g * CPG + 8 * ks + 2 * i + 1], -esc);
         uint32_t hi, lo;
         if constexpr (BF16) split_bf16(a, c, hi, lo);
         else split_f16(a, c, hi, lo);
@@ -230,6 +247,10 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
     if constexpr (E5) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) s[i] *= ks_h;
+    }
+    if (esc != 0) {   // wave-uniform, rare: undo the range scaling of q'
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[i] = ldexpf(s[i], esc);
     }
     if (n_valid < kPage) {
 #pragma unroll

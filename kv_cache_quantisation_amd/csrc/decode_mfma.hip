@@ -562,10 +562,12 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
     } else {
     // q' = q * s per channel, split hi/lo into B fragments; bias q . z
     float bias_part[REPS];
+    float qp[REPS][8];
+    float amax = 0.f;
 #pragma unroll
     for (int r = 0; r < REPS; ++r) {
       const int cidx = lane + 64 * r;
-      const int fh = cidx / PER_HEAD, fg = (cidx / KS) % 4, fk = cidx % KS;
+      const int fg = (cidx / KS) % 4, fk = cidx % KS;
       const int c0 = fg * CPG + 8 * fk;
       const float4 s0 = *reinterpret_cast<const float4*>(pg + PG::OFF_KS + 4 * c0);
       const float4 s1 = *reinterpret_cast<const float4*>(pg + PG::OFF_KS + 4 * c0 + 16);
@@ -573,19 +575,42 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
       const float4 z1 = *reinterpret_cast<const float4*>(pg + PG::OFF_KZ + 4 * c0 + 16);
       const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
       const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
-      float qp[8];
       float bp = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        qp[i] = qreg[r][i] * sv[i];
+        qp[r][i] = qreg[r][i] * sv[i];
         bp = fmaf(qreg[r][i], zv[i], bp);
+        amax = fmaxf(amax, fabsf(qp[r][i]));
       }
       bias_part[r] = bp;
+    }
+    // f16 range of the key operand: beyond 65504 the f16 high part would
+    // saturate. A page whose q' exceeds it (a key channel with an enormous
+    // range) takes q' 2^-e into the product and multiplies the product part
+    // of its scores by 2^e: exact scaling by a power of two (wave-uniform).
+    const bool big = __builtin_amdgcn_ballot_w64(amax > 65504.f) != 0;
+    int esc = 0;
+    if (big) {
+      float wm = amax;
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) wm = fmaxf(wm, __shfl_xor(wm, m, 64));
+      int ex;
+      frexpf(wm, &ex);   // wm < 2^ex
+      esc = __builtin_amdgcn_readfirstlane(ex - 15);
+#pragma unroll
+      for (int r = 0; r < REPS; ++r)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qp[r][i] = ldexpf(qp[r][i], -esc);
+    }
+#pragma unroll
+    for (int r = 0; r < REPS; ++r) {
+      const int cidx = lane + 64 * r;
+      const int fh = cidx / PER_HEAD, fg = (cidx / KS) % 4, fk = cidx % KS;
       uint32_t hi[4], lo[4];   // fragment order {0,2,1,3,4,6,5,7}
-      split_f16(qp[0], qp[2], hi[0], lo[0]);
-      split_f16(qp[1], qp[3], hi[1], lo[1]);
-      split_f16(qp[4], qp[6], hi[2], lo[2]);
-      split_f16(qp[5], qp[7], hi[3], lo[3]);
+      split_f16(qp[r][0], qp[r][2], hi[0], lo[0]);
+      split_f16(qp[r][1], qp[r][3], hi[1], lo[1]);
+      split_f16(qp[r][4], qp[r][6], hi[2], lo[2]);
+      split_f16(qp[r][5], qp[r][7], hi[3], lo[3]);
       if (cidx < COMBOS) {
         *reinterpret_cast<uint4*>(frag[fh * FSTRIDE + ((4 * fk + fg) ^ (fh & 7))]) =
             uint4{hi[0], hi[1], hi[2], hi[3]};
@@ -610,6 +635,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
       if (src >= 0 && src < 64) bias_j = got;
     }
     if (j >= HG) bias_j = 0.f;   // lo columns carry no offset
+    if (big) bias_j = ldexpf(bias_j, -esc);   // scaled with the product, undone below
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     // columns >= 2*HG only produce score columns that are never read
@@ -644,6 +670,10 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) s[4 * mt + r] = c[r] + row_shl<HG>(c[r]);
+    }
+    if (big) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[i] = ldexpf(s[i], esc);
     }
     }   // rotary / plain keys
 

@@ -320,6 +320,8 @@ int32_t decode_call(const kvq_config* cfg, const void* cache, int32_t layer, int
       !kvq::aligned16(workspace))
     return KVQ_ERR_INVALID;
   if (nq < 1 || nq > tokens) return KVQ_ERR_INVALID;
+  // one row of blocks per (sequence, query): the grid's z dimension
+  if (static_cast<int64_t>(cfg->batch) * nq > 65535) return KVQ_ERR_UNSUPPORTED;
   const int64_t one = kvq::workspace_bytes(g, tokens, cfg->num_splits);
   if (one < 0) return KVQ_ERR_INVALID;
   if (workspace_bytes / static_cast<size_t>(nq) < static_cast<size_t>(one)) return KVQ_ERR_WORKSPACE;

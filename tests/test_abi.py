@@ -284,3 +284,10 @@ def test_multi_query_validation():
     assert mq(p, f, 0, 0, 1, f, None, None, f, f, big, None) == kvq.KVQ_ERR_INVALID
     need = kvq.kvq_cache_bytes(c, 4096, kvq.KVQ_BYTES_WORKSPACE)
     assert mq(p, f, 0, 4096, 3, f, None, None, f, f, 3 * need - 1, None) == kvq.KVQ_ERR_WORKSPACE
+    # one row of blocks per (sequence, query): batch * n_queries <= 65535,
+    # checked in 64-bit before any launch
+    # (a zero workspace stops the allowed case at the next check, before any launch)
+    c.batch = 4096
+    c.max_tokens = 64
+    assert mq(p, f, 0, 64, 15, f, None, None, f, f, 0, None) == kvq.KVQ_ERR_WORKSPACE
+    assert mq(p, f, 0, 64, 16, f, None, None, f, f, 0, None) == kvq.KVQ_ERR_UNSUPPORTED

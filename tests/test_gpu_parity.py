@@ -348,25 +348,126 @@ def test_decode_fp8_unwritten_bytes_are_ignored():
     assert H.max_err(out, oc.decode(0, H.values(q))) <= H.ATOL
 
 
-@pytest.mark.parametrize("bits", [2, 4])
-def test_decode_mfma_dynamic_range(bits):
+@pytest.mark.parametrize("bits,v_bits,dtype", [
+    (2, 0, torch.float32), (4, 0, torch.float32),       # generic (vector-ALU) kernel
+    (2, 0, torch.bfloat16), (4, 0, torch.bfloat16),     # matrix-core kernel
+    (4, 2, torch.bfloat16)])
+def test_decode_mfma_dynamic_range(bits, v_bits, dtype):
     """Keys and values over many orders of magnitude: per-channel scales from
     1e-4 to 1e3, so q * s spans far more than fp16's 11 bits and the hi/lo
-    split carries the accuracy; peaked attention through large queries."""
-    w = small(synth.KIVI, bits, 128, torch.float32, 32, hg=4, T=600)
+    split carries the accuracy; value rows from 1e-2 to 1e2; peaked attention
+    through large queries. The plain max-abs 2e-3 bound, at every output
+    magnitude. bf16 inputs run on the matrix-core kernel (f16 hi/lo key
+    operand, bf16 hi/lo weights), f32 inputs on the generic kernel."""
+    w = small(synth.KIVI, bits, 128, dtype, 32, hg=4, T=600, v_bits=v_bits)
     k, v = synth.keys_values(w, device=DEV)
     ch = torch.logspace(-4, 3, 128, device=DEV)
-    k = (k * ch.view(1, 1, 1, 128)).contiguous()
-    v = (v * torch.logspace(-2, 2, 600, device=DEV).view(1, 600, 1, 1)).contiguous()
+    k = (k.float() * ch.view(1, 1, 1, 128)).to(dtype).contiguous()
+    v = (v.float() * torch.logspace(-2, 2, 600, device=DEV).view(1, 600, 1, 1)).to(dtype).contiguous()
     cfg = H.config(w, 640)
     cache = kvq.alloc_cache(cfg)
     oc = H.oracle_cache(w, 640)
     H.append_chunks(cfg, cache, k, v, [600], oc=oc)
-    q = (synth.query(w, device=DEV) * 3.0).contiguous()
+    q = (synth.query(w, device=DEV).float() * 3.0).to(dtype).contiguous()
     out = H.decode(cfg, cache, 0, 600, q)
     want = oc.decode(0, H.values(q))
-    scale = max(1.0, float(np.max(np.abs(want))))
-    assert H.max_err(out, want) <= H.ATOL * scale
+    err = H.max_err(out, want)
+    print(f"[dynamic range] b{bits} v{v_bits or bits} {dtype}: max|out| "
+          f"{float(np.max(np.abs(want))):.1f}, max-abs error {err:.2e}", flush=True)
+    assert err <= H.ATOL
+
+
+def _one_page_keys(w, kvals):
+    """[B, 32, Hkv, d] keys, zero except the listed (token, channel) -> value
+    entries (the same in every sequence and KV head)."""
+    k = torch.zeros(w.batch, 32, w.kv_heads, w.head_dim, dtype=torch.float32)
+    for (t, c), x in kvals.items():
+        k[:, t, :, c] = x
+    return k.to(w.in_dtype).to(DEV).contiguous()
+
+
+@pytest.mark.parametrize("bits,v_bits", [(2, 0), (4, 0), (4, 2)])
+def test_decode_f16_range_guard_kivi(bits, v_bits):
+    """A key channel whose scaled query q * s * sm_scale * log2(e) exceeds the
+    f16 maximum (65504) on the matrix-core kernel. One page, keys built so the
+    quantisation is exact (per-channel minimum 0): channel 0 gives token X
+    code L and token Y code L-1 or so, channel 1 gives Y the top code. With the
+    true q', X wins by thousands of log2 units; had q' saturated at the f16
+    maximum, Y would win by hundreds. Values: X's row all +1, Y's all -1,
+    others 0 -- so the output is +1 exactly, and -1 if the range were lost."""
+    w = small(synth.KIVI, bits, 128, torch.bfloat16, 0, B=1, Hkv=1, hg=4, T=32, v_bits=v_bits)
+    L = float((1 << bits) - 1)
+    X, Y = 3, 17
+    # channel 0: X = L * 2^17, Y = (L - 1) * 2^17, others 0 -> s0 = 2^17, codes L, L - 1
+    # channel 1: Y = 2^20 (code L), others 0 -> s1 = fl(2^20 / L)
+    k = _one_page_keys(w, {(X, 0): L * 2.0 ** 17, (Y, 0): (L - 1) * 2.0 ** 17, (Y, 1): 2.0 ** 20})
+    v = torch.zeros(1, 32, 1, 128, dtype=torch.float32)
+    v[0, X], v[0, Y] = 1.0, -1.0
+    v = v.to(torch.bfloat16).to(DEV).contiguous()
+    # q' = q * s * qs, qs = log2(e) / sqrt(128); score(X) - score(Y) = q0' - L q1'
+    qs = float(np.log2(np.e) / np.sqrt(128.0))
+    s0, s1 = 2.0 ** 17, float(np.float32(2.0 ** 20) / np.float32(L))
+    q0 = 8.0                                  # q0' = 8 * 2^17 * qs ~ 1.34e5 > 65504
+    q1 = None
+    for cand in np.arange(4.0, 0.0, -2.0 ** -7):  # bf16-exact candidates, largest first
+        q1p = cand * s1 * qs
+        sat = 2 * 65504.0                      # hi + lo of a saturated f16 split
+        if q1p < 65504 and q0 * s0 * qs - L * q1p > 500 and sat - L * q1p < -200:
+            q1 = float(cand)
+            break
+    assert q1 is not None
+    q = torch.zeros(1, 4, 128, dtype=torch.float32)
+    q[0, :, 0], q[0, :, 1] = q0, q1
+    q = q.to(torch.bfloat16).to(DEV).contiguous()
+    cfg = H.config(w, 32)
+    cache = kvq.alloc_cache(cfg)
+    oc = H.oracle_cache(w, 32)
+    H.append_chunks(cfg, cache, k, v, [32], oc=oc)
+    want, mask = oc.cache_image()
+    H.compare_bytes(cache.cpu().numpy(), want, mask, "range-guard page")
+    out = H.decode(cfg, cache, 0, 32, q)
+    ref = oc.decode(0, H.values(q))
+    assert np.allclose(ref, 1.0, atol=1e-6)    # the construction: X takes all the weight
+    assert H.max_err(out, ref) <= H.ATOL
+
+
+def test_decode_f16_range_guard_fp8():
+    """FP8 E4M3 keys with a per-head scale so large that q * k_scale *
+    sm_scale * log2(e) exceeds the f16 maximum: token X (channel 0 at 448)
+    must win over Y (channel 0 at 320, channel 1 at 448); with q' saturated at
+    the f16 maximum Y would win. Values: X's row +1, Y's -1."""
+    w = small(synth.FP8_E4M3, 8, 128, torch.bfloat16, 0, B=1, Hkv=1, hg=4, T=32)
+    ksc = 2.0 ** 20
+    X, Y = 5, 22
+    k = _one_page_keys(w, {(X, 0): 448 * ksc, (Y, 0): 320 * ksc, (Y, 1): 448 * ksc})
+    v = torch.zeros(1, 32, 1, 128, dtype=torch.float32)
+    v[0, X], v[0, Y] = 1.0, -1.0
+    v = v.to(torch.bfloat16).to(DEV).contiguous()
+    qs = float(np.log2(np.e) / np.sqrt(128.0))
+    q0p = 1.0 * ksc * qs                       # ~1.34e5 > 65504
+    sat = 2 * 65504.0
+    q1 = None
+    for cand in np.arange(1.0, 0.0, -2.0 ** -9):
+        q1p = cand * ksc * qs
+        if q1p < 65504 and 128 * q0p - 448 * q1p > 1e4 and 128 * sat - 448 * q1p < -1e4:
+            q1 = float(cand)
+            break
+    assert q1 is not None
+    q = torch.zeros(1, 4, 128, dtype=torch.float32)
+    q[0, :, 0], q[0, :, 1] = 1.0, q1
+    q = q.to(torch.bfloat16).to(DEV).contiguous()
+    ks = torch.full((1,), ksc, dtype=torch.float32, device=DEV)
+    vs = torch.ones(1, dtype=torch.float32, device=DEV)
+    cfg = H.config(w, 32)
+    cache = kvq.alloc_cache(cfg)
+    oc = H.oracle_cache(w, 32)
+    H.append_chunks(cfg, cache, k, v, [32], ks=ks, vs=vs, oc=oc)
+    want, mask = oc.cache_image()
+    H.compare_bytes(cache.cpu().numpy(), want, mask, "fp8 range-guard page")
+    out = H.decode(cfg, cache, 0, 32, q, ks, vs)
+    ref = oc.decode(0, H.values(q))
+    assert np.allclose(ref, 1.0, atol=1e-6)
+    assert H.max_err(out, ref) <= H.ATOL
 
 
 def test_decode_split_invariance_and_determinism():

@@ -208,3 +208,32 @@ def test_multi_query_is_causal_bruteforce():
                 want = attention.attend_bruteforce(qm[b, i, h].astype(np.float64), kh[b, g, :n],
                                                    vh[b, g, :n], sm)
                 np.testing.assert_allclose(got[b, i, h], want, rtol=0, atol=1e-12)
+
+
+def test_multi_query_rows_versus_one_query_decodes_at_their_own_fill():
+    """Several queries read the KIVI cache as it stands after every token was
+    appended. Row i equals a one-query decode of a cache that only ever held
+    its first T_i = T - n_q + i + 1 tokens exactly when both fill levels
+    quantise the same tokens (q(T_i) == q(T)); where a later flush has encoded
+    tokens that the shorter cache still holds in its ring -- or encoded the
+    page that holds the query's own token, whose statistics then include later
+    tokens -- the rows differ."""
+    R, T, nq = 16, 120, 40      # q(T) = 96; fills 81..120 give q = 64 or 96
+    c, k, v, _, _, _ = filled(acc.KIVI, 2, T, residual=R, seed=11)
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((B, nq, HQ, D)).astype(np.float32)
+    got = c.decode_multi(0, q)
+    q_all, _ = acc.flush_plan(T, R)
+    same = differ = 0
+    for i in range(nq):
+        Ti = T - nq + i + 1
+        short = OracleCache(acc.KIVI, 2, 1, B, H, D, Ti, residual=R, in_dtype="f32")
+        short.append(0, k[:, :Ti], v[:, :Ti])
+        want = short.decode(0, q[:, i])
+        if acc.flush_plan(Ti, R)[0] == q_all:
+            assert np.array_equal(got[:, i], want), i
+            same += 1
+        else:
+            assert np.max(np.abs(got[:, i] - want)) > 1e-6, i
+            differ += 1
+    assert same > 0 and differ > 0
