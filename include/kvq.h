@@ -63,7 +63,8 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 4   /* 3: ragged-batch entry points; 4: several queries per sequence */
+#define KVQ_ABI_VERSION 5   /* 3: ragged-batch entry points; 4: several queries per sequence;
+                               5: decode without a caller workspace */
 
 /* Exported entry points (the library is built with hidden visibility). */
 #if defined(__GNUC__)
@@ -357,6 +358,31 @@ KVQ_API int32_t kvq_decode_attention_multi(const kvq_config* cfg, const void* ca
                                    const void* q, const float* k_scale,
                                    const float* v_scale, float* out, void* workspace,
                                    size_t workspace_bytes, void* stream);
+
+/* Size of the library's own decode scratch array, per GPU (see
+ * kvq_decode_attention_noalloc). */
+#define KVQ_NOALLOC_SCRATCH_BYTES (16 << 20)
+
+/* kvq_decode_attention without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops that
+ * forbid allocation. Same arguments (minus workspace), same kernels, same
+ * result bit for bit as kvq_decode_attention with a workspace of
+ * kvq_cache_bytes(cfg, tokens, KVQ_BYTES_WORKSPACE) bytes.
+ *   The split partials and arrival counters live in a fixed device array of
+ *   KVQ_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, held
+ *   until the process ends. A call whose workspace need exceeds it returns
+ *   KVQ_ERR_WORKSPACE (validated on the host, nothing launched). The call
+ *   allocates nothing. The first call on a device looks up the array's
+ *   address and enqueues one small kernel on `stream` that clears it; every
+ *   decode leaves its counters at zero again.
+ *   Every call on one GPU shares that GPU's array: calls that may overlap on
+ *   one GPU (different streams, or concurrent graph replays) race and give
+ *   wrong results; serialise them, or use kvq_decode_attention with a
+ *   workspace of its own per stream. */
+KVQ_API int32_t kvq_decode_attention_noalloc(const kvq_config* cfg, const void* cache,
+                                     int32_t layer, int64_t tokens, const void* q,
+                                     const float* k_scale, const float* v_scale,
+                                     float* out, void* stream);
 
 /* Static description of a status code (never NULL). */
 KVQ_API const char* kvq_status_string(int32_t status);

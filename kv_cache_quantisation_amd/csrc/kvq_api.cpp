@@ -174,7 +174,7 @@ int64_t single_splits(const Geometry& g, int64_t tokens, int32_t requested) {
   return decode_splits(g, tokens, requested);
 }
 
-int64_t workspace_bytes(const Geometry& g, int64_t tokens, int32_t requested) {
+int64_t workspace_bytes_for(const Geometry& g, int64_t tokens, int32_t requested) {
   const int64_t s = single_splits(g, tokens, requested);
   const int64_t per = static_cast<int64_t>(g.d + 2) * 4;
   int64_t p = mul_ck(mul_ck(mul_ck(g.batch, g.q_heads), s), per);
@@ -227,7 +227,7 @@ int64_t kvq_cache_bytes(const kvq_config* cfg, int64_t tokens, int32_t kind) {
       return (slab < 0 || v < 0) ? KVQ_ERR_INVALID : v;
     }
     case KVQ_BYTES_WORKSPACE: {
-      const int64_t v = kvq::workspace_bytes(g, tokens, cfg->num_splits);
+      const int64_t v = kvq::workspace_bytes_for(g, tokens, cfg->num_splits);
       return v < 0 ? KVQ_ERR_INVALID : v;
     }
     default:
@@ -302,30 +302,32 @@ int32_t kvq_quantize_append_ragged(const kvq_config* cfg, void* cache, int32_t l
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
 }
 
-namespace {
-int32_t decode_call(const kvq_config* cfg, const void* cache, int32_t layer, int64_t tokens,
-                    const int64_t* seq_tokens, int32_t nq, const void* q, const float* k_scale,
-                    const float* v_scale, float* out, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+}  // extern "C"
+
+namespace kvq {
+// Validation of a decode call and its launch arguments (no device access).
+int32_t decode_prepare(const kvq_config* cfg, const void* cache, int32_t layer, int64_t tokens,
+                       const int64_t* seq_tokens, int32_t nq, const void* q,
+                       const float* k_scale, const float* v_scale, float* out, void* workspace,
+                       size_t workspace_bytes, DecodeArgs* args) {
   if (!cfg) return KVQ_ERR_NULL;
   Geometry g;
-  const int32_t st = kvq::make_geometry(*cfg, &g);
+  const int32_t st = make_geometry(*cfg, &g);
   if (st != KVQ_OK) return st;
   if (!cache || !q || !out || !workspace) return KVQ_ERR_NULL;
-  if (kvq::is_fp8(cfg->scheme) && (!k_scale || !v_scale)) return KVQ_ERR_NULL;
+  if (is_fp8(cfg->scheme) && (!k_scale || !v_scale)) return KVQ_ERR_NULL;
   if (layer < 0 || layer >= cfg->layers) return KVQ_ERR_INVALID;
   if (tokens < 1) return KVQ_ERR_INVALID;
   if (tokens > cfg->max_tokens) return KVQ_ERR_CAPACITY;
-  if (!kvq::aligned16(cache) || !kvq::aligned16(q) || !kvq::aligned16(out) ||
-      !kvq::aligned16(workspace))
+  if (!aligned16(cache) || !aligned16(q) || !aligned16(out) || !aligned16(workspace))
     return KVQ_ERR_INVALID;
   if (nq < 1 || nq > tokens) return KVQ_ERR_INVALID;
   // one row of blocks per (sequence, query): the grid's z dimension
   if (static_cast<int64_t>(cfg->batch) * nq > 65535) return KVQ_ERR_UNSUPPORTED;
-  const int64_t one = kvq::workspace_bytes(g, tokens, cfg->num_splits);
+  const int64_t one = workspace_bytes_for(g, tokens, cfg->num_splits);
   if (one < 0) return KVQ_ERR_INVALID;
   if (workspace_bytes / static_cast<size_t>(nq) < static_cast<size_t>(one)) return KVQ_ERR_WORKSPACE;
-  kvq::DecodeArgs a{};
+  DecodeArgs a{};
   a.g = g;
   a.layer_base = static_cast<const uint8_t*>(cache) +
                  static_cast<int64_t>(layer) * cfg->batch * cfg->kv_heads * g.slab_bytes;
@@ -341,17 +343,33 @@ int32_t decode_call(const kvq_config* cfg, const void* cache, int32_t layer, int
   a.sm_scale = cfg->sm_scale != 0.0f ? cfg->sm_scale
                                      : static_cast<float>(1.0 / std::sqrt((double)cfg->head_dim));
   a.rope_theta = cfg->rope_theta;
-  a.items = kvq::decode_items(g, tokens);
-  a.splits = kvq::decode_splits(g, tokens, cfg->num_splits);
+  a.items = decode_items(g, tokens);
+  a.splits = decode_splits(g, tokens, cfg->num_splits);
   // several queries: the generic kernel takes the one-query split count (the
   // matrix-core kernels plan theirs for batch * n_queries rows, never more),
   // so that n_queries one-query workspaces hold the partials
-  if (nq > 1) a.splits = static_cast<int32_t>(kvq::single_splits(g, tokens, cfg->num_splits));
+  if (nq > 1) a.splits = static_cast<int32_t>(single_splits(g, tokens, cfg->num_splits));
   a.requested_splits = cfg->num_splits;
+  *args = a;
+  return KVQ_OK;
+}
+}  // namespace kvq
+
+namespace {
+int32_t decode_call(const kvq_config* cfg, const void* cache, int32_t layer, int64_t tokens,
+                    const int64_t* seq_tokens, int32_t nq, const void* q, const float* k_scale,
+                    const float* v_scale, float* out, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  kvq::DecodeArgs a;
+  const int32_t st = kvq::decode_prepare(cfg, cache, layer, tokens, seq_tokens, nq, q, k_scale,
+                                         v_scale, out, workspace, workspace_bytes, &a);
+  if (st != KVQ_OK) return st;
   const hipError_t e = kvq::launch_decode(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
 }
 }  // namespace
+
+extern "C" {
 
 int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache, int32_t layer,
                              int64_t tokens, const void* q, const float* k_scale,

@@ -104,7 +104,13 @@ hipError_t launch_fp8_mfma(const DecodeArgs& a, hipStream_t stream);
 // Decode split plan, shared by kvq_cache_bytes(WORKSPACE) and the launcher.
 int32_t decode_items(const Geometry& g, int64_t tokens);
 int32_t decode_splits(const Geometry& g, int64_t tokens, int32_t requested);
-int64_t workspace_bytes(const Geometry& g, int64_t tokens, int32_t requested);
+int64_t workspace_bytes_for(const Geometry& g, int64_t tokens, int32_t requested);
+// Validates a decode call (nothing touches a device) and fills its launch
+// arguments; KVQ_OK or the negative status the entry point returns.
+int32_t decode_prepare(const kvq_config* cfg, const void* cache, int32_t layer, int64_t tokens,
+                       const int64_t* seq_tokens, int32_t nq, const void* q,
+                       const float* k_scale, const float* v_scale, float* out, void* workspace,
+                       size_t workspace_bytes, DecodeArgs* args);
 // Offset of the split partials inside the workspace (after the counters).
 int64_t workspace_partials_offset(const Geometry& g);
 

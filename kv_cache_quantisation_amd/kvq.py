@@ -19,11 +19,12 @@ KVQ_KIVI, KVQ_SYM_TOKEN, KVQ_FP8_E4M3, KVQ_BF16_CACHE, KVQ_FP8_E5M2 = 0, 1, 2, 3
 KVQ_F32, KVQ_BF16 = 0, 1
 KVQ_BYTES_FORMULA, KVQ_BYTES_CACHE, KVQ_BYTES_WORKSPACE = 0, 1, 2
 
-ABI_VERSION = 4   # KVQ_ABI_VERSION of include/kvq.h that this binding mirrors
+ABI_VERSION = 5   # KVQ_ABI_VERSION of include/kvq.h that this binding mirrors
 
 SYMBOLS = ("kvq_cache_bytes", "kvq_quantize_append", "kvq_quantize_append_ragged",
            "kvq_decode_attention", "kvq_decode_attention_ragged", "kvq_decode_attention_multi",
-           "kvq_status_string", "kvq_abi_version")
+           "kvq_decode_attention_noalloc", "kvq_status_string", "kvq_abi_version")
+KVQ_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class KvqError(RuntimeError):
@@ -96,6 +97,8 @@ def lib():
         L.kvq_decode_attention_multi.argtypes = [cfgp, P, I32, I64, I32, P, P, P, P, P,
                                                  ctypes.c_size_t, P]
         L.kvq_decode_attention_multi.restype = I32
+        L.kvq_decode_attention_noalloc.argtypes = [cfgp, P, I32, I64, P, P, P, P, P]
+        L.kvq_decode_attention_noalloc.restype = I32
         L.kvq_status_string.argtypes = [I32]
         L.kvq_status_string.restype = ctypes.c_char_p
         L.kvq_abi_version.argtypes = []
@@ -171,6 +174,17 @@ def kvq_decode_attention(cfg, cache, layer, tokens, q, out, workspace, workspace
                                     workspace_bytes, _stream(stream))
     if check and st != KVQ_OK:
         raise KvqError(st, "kvq_decode_attention")
+    return st
+
+
+def kvq_decode_attention_noalloc(cfg, cache, layer, tokens, q, out, k_scale=None, v_scale=None,
+                                 stream=None, check=True):
+    """kvq_decode_attention on the library's own scratch array (no workspace)."""
+    st = lib().kvq_decode_attention_noalloc(ctypes.byref(cfg), _ptr(cache), layer, tokens, _ptr(q),
+                                            _ptr(k_scale), _ptr(v_scale), _ptr(out),
+                                            _stream(stream))
+    if check and st != KVQ_OK:
+        raise KvqError(st, "kvq_decode_attention_noalloc")
     return st
 
 

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert kvq.kvq_abi_version() == 4
+    assert kvq.kvq_abi_version() == 5
     assert kvq.status_string(0) == "ok"
     for st in (-1, -2, -3, -4, -5, -6):
         assert kvq.status_string(st) != "unknown status"
@@ -291,3 +291,26 @@ def test_multi_query_validation():
     c.max_tokens = 64
     assert mq(p, f, 0, 64, 15, f, None, None, f, f, 0, None) == kvq.KVQ_ERR_WORKSPACE
     assert mq(p, f, 0, 64, 16, f, None, None, f, f, 0, None) == kvq.KVQ_ERR_UNSUPPORTED
+
+
+def test_noalloc_validation():
+    """The decode without a workspace validates on the host before touching a
+    device: bad arguments, and a call whose workspace need exceeds the
+    library's scratch array (KVQ_ERR_WORKSPACE)."""
+    L = kvq.lib()
+    f = 1 << 20
+    c = cfg()
+    p = ctypes.byref(c)
+    na = L.kvq_decode_attention_noalloc
+    assert na(None, f, 0, 8, f, None, None, f, None) == kvq.KVQ_ERR_NULL
+    assert na(p, None, 0, 8, f, None, None, f, None) == kvq.KVQ_ERR_NULL
+    assert na(p, f, 0, 8, f, None, None, None, None) == kvq.KVQ_ERR_NULL
+    assert na(p, f, 2, 8, f, None, None, f, None) == kvq.KVQ_ERR_INVALID       # layer
+    assert na(p, f, 0, 0, f, None, None, f, None) == kvq.KVQ_ERR_INVALID       # tokens
+    assert na(p, f, 0, 4097, f, None, None, f, None) == kvq.KVQ_ERR_CAPACITY
+    assert na(p, f + 8, 0, 8, f, None, None, f, None) == kvq.KVQ_ERR_INVALID   # alignment
+    # a workspace need beyond the scratch array: many sequences, many splits
+    big = cfg(batch=4096, max_tokens=1 << 16, num_splits=64)
+    need = kvq.kvq_cache_bytes(big, 1 << 16, kvq.KVQ_BYTES_WORKSPACE)
+    assert need > kvq.KVQ_NOALLOC_SCRATCH_BYTES
+    assert na(ctypes.byref(big), f, 0, 1 << 16, f, None, None, f, None) == kvq.KVQ_ERR_WORKSPACE
