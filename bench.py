@@ -65,10 +65,13 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 # change to those, `traffic` is reported as null until they are taken again.
 ROOFLINE_EXTRA = 64            # roofline context = workload tokens + this
 COUNTERS = {
-    "kivi2": {"context": 4096 + ROOFLINE_EXTRA, "fetch_kib": None, "write_kib": None,
+    "kivi2": {"context": 4096 + ROOFLINE_EXTRA, "fetch_kib": 30826.3125, "write_kib": 892.0,
               "fetch_scale": 262144 / 131084, "write_scale": 1.0,
-              "sources_sha256": ""},
+              "sources_sha256": "ad22a81afb0fcc76276f08cc5693a6ab0de21724cc6ac1021697a49b42074993"},
 }
+DECODE_SOURCES = ["decode_mfma.hip", "kvq_device.h", "kvq_internal.h", "kvq_wave.h"]
+
+
 def decode_sources_sha256():
     import hashlib
     h = hashlib.sha256()
