@@ -53,14 +53,26 @@ def flush_plan(tokens, residual, group=PAGE):
     return q, tokens - q
 
 
-def page_bytes(scheme, head_dim, bits, v_bits=None):
+def sparse_section_bytes(head_dim):
+    """The side matrix of one KIVI page with one outlier per vector: the key
+    outlier of each channel (float32) and the value outlier of each token
+    (float32), then their indices (one byte each: token 0..31, channel
+    0..d-1), padded to a multiple of 256 bytes."""
+    raw = 4 * head_dim + 4 * PAGE + head_dim + PAGE
+    return -(-raw // 256) * 256
+
+
+def page_bytes(scheme, head_dim, bits, v_bits=None, outliers=0):
     """Bytes of one 32-token page of the documented layout (KIVI value codes
-    of v_bits when given, else of bits)."""
+    of v_bits when given, else of bits; with the sparse side matrix of one
+    outlier per vector when outliers == 1)."""
     d, b = head_dim, bits
     vb = bits if v_bits is None else v_bits
     if scheme == KIVI:
         # K codes + K scale/offset per channel + V codes + V scale/offset per token
-        return PAGE * d * b // 8 + 4 * d + 4 * d + PAGE * d * vb // 8 + 4 * PAGE + 4 * PAGE
+        base = PAGE * d * b // 8 + 4 * d + 4 * d + PAGE * d * vb // 8 + 4 * PAGE + 4 * PAGE
+        return base + (sparse_section_bytes(d) if outliers else 0)
+    assert not outliers
     if scheme == SYM_TOKEN:
         return PAGE * d * b // 8 + 4 * PAGE + PAGE * d * b // 8 + 4 * PAGE
     if scheme in (FP8_E4M3, FP8_E5M2):
@@ -82,13 +94,14 @@ def ring_bytes(scheme, head_dim, residual, in_itemsize):
     return 2 * (residual + PAGE) * head_dim * in_itemsize
 
 
-def slab_bytes(scheme, head_dim, bits, capacity, residual, in_itemsize, v_bits=None):
-    return (pages_per_slab(scheme, capacity, residual) * page_bytes(scheme, head_dim, bits, v_bits)
+def slab_bytes(scheme, head_dim, bits, capacity, residual, in_itemsize, v_bits=None, outliers=0):
+    return (pages_per_slab(scheme, capacity, residual)
+            * page_bytes(scheme, head_dim, bits, v_bits, outliers)
             + ring_bytes(scheme, head_dim, residual, in_itemsize))
 
 
 def layout_cache_bytes(scheme, layers, batch, kv_heads, head_dim, bits, capacity,
-                       residual, in_itemsize, v_bits=None):
+                       residual, in_itemsize, v_bits=None, outliers=0):
     """Whole cache: one slab per (layer, sequence, KV head)."""
     return layers * batch * kv_heads * slab_bytes(scheme, head_dim, bits, capacity,
-                                                  residual, in_itemsize, v_bits)
+                                                  residual, in_itemsize, v_bits, outliers)

@@ -47,9 +47,10 @@ class OracleCache:
     """in_dtype is "f32" (inputs float32) or "bf16" (inputs uint16 bit patterns)."""
 
     def __init__(self, scheme, bits, layers, batch, kv_heads, head_dim, capacity,
-                 residual=0, in_dtype="bf16", v_bits=None):
+                 residual=0, in_dtype="bf16", v_bits=None, outliers=0):
         if scheme != KIVI:
-            assert residual == 0 and v_bits in (None, bits)
+            assert residual == 0 and v_bits in (None, bits) and not outliers
+        self.outliers = outliers          # KIVI: dense-and-sparse with one outlier per vector
         self.scheme, self.bits, self.layers, self.batch = scheme, bits, layers, batch
         self.v_bits = bits if v_bits is None else v_bits   # KIVI value codes
         self.kv_heads, self.d, self.capacity = kv_heads, head_dim, capacity
@@ -94,10 +95,10 @@ class OracleCache:
     # ---- byte image -------------------------------------------------------
     def slab_size(self):
         return accounting.slab_bytes(self.scheme, self.d, self.bits, self.capacity,
-                                     self.residual, self.itemsize, self.v_bits)
+                                     self.residual, self.itemsize, self.v_bits, self.outliers)
 
     def page_size(self):
-        return accounting.page_bytes(self.scheme, self.d, self.bits, self.v_bits)
+        return accounting.page_bytes(self.scheme, self.d, self.bits, self.v_bits, self.outliers)
 
     def slab_image(self, layer, b, h):
         """(bytes, mask) of one slab for the tokens held now."""
@@ -114,7 +115,7 @@ class OracleCache:
             q, _ = accounting.flush_plan(T, self.residual)
             for p in range(q // PAGE):
                 pb, pm = layout.kivi_page(K[p * PAGE:(p + 1) * PAGE], V[p * PAGE:(p + 1) * PAGE],
-                                          self.bits, self.v_bits)
+                                          self.bits, self.v_bits, self.outliers)
                 buf[p * ps:(p + 1) * ps], mask[p * ps:(p + 1) * ps] = pb, pm
             n_pages = accounting.pages_per_slab(KIVI, self.capacity, self.residual)
             ring0 = n_pages * ps
@@ -168,6 +169,12 @@ class OracleCache:
             q, _ = accounting.flush_plan(T, self.residual)
             for p in range(q // PAGE):
                 sl = slice(p * PAGE, (p + 1) * PAGE)
+                if self.outliers:
+                    kh[:, :, sl] = codec.kivi_dequantize_sparse(
+                        *codec.kivi_quantize_sparse(K[:, :, sl], self.bits, axis=2), axis=2)
+                    vh[:, :, sl] = codec.kivi_dequantize_sparse(
+                        *codec.kivi_quantize_sparse(V[:, :, sl], self.v_bits, axis=3), axis=3)
+                    continue
                 kc, ks, kz = codec.kivi_quantize(K[:, :, sl], self.bits, axis=2)
                 vc, vs, vz = codec.kivi_quantize(V[:, :, sl], self.v_bits, axis=3)
                 kh[:, :, sl] = codec.kivi_dequantize(kc, ks, kz, axis=2)
@@ -243,10 +250,11 @@ class RaggedCache:
     T_b - 1 (test infrastructure only)."""
 
     def __init__(self, scheme, bits, layers, batch, kv_heads, head_dim, capacity, residual=0,
-                 in_dtype="bf16", v_bits=None):
+                 in_dtype="bf16", v_bits=None, outliers=0):
         self.layers, self.batch, self.kv_heads = layers, batch, kv_heads
         self.seqs = [OracleCache(scheme, bits, layers, 1, kv_heads, head_dim, capacity,
-                                 residual=residual, in_dtype=in_dtype, v_bits=v_bits)
+                                 residual=residual, in_dtype=in_dtype, v_bits=v_bits,
+                                 outliers=outliers)
                      for _ in range(batch)]
 
     def tokens(self, layer):

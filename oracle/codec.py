@@ -55,6 +55,52 @@ def kivi_quantize(x, bits, axis):
     return codes, np.squeeze(s, axis=axis), np.squeeze(mn, axis=axis)
 
 
+def kivi_quantize_sparse(x, bits, axis, n_out=1):
+    """Dense-and-sparse KIVI quantisation ("KVQuant: Towards 10 Million Context
+    Length ...", Summary: a small fraction of outliers moved, per vector, into
+    a separate sparse representation; "Quantizing the KV cache", going deeper:
+    KVQuant keeps a few outliers in a sparse side matrix).
+
+    Reading: each vector along `axis` (a key channel's tokens of one group, a
+    value token's channels) moves its n_out values of largest magnitude |x|
+    (equal magnitudes: the lower index first) into the side matrix, stored
+    exactly with their index; the other values are quantised by Q_b exactly as
+    ``kivi_quantize`` does, with min and max taken over those values only; the
+    moved positions hold code 0.
+
+    Returns (codes, s, z, out_val, out_idx): codes like ``kivi_quantize``; s,
+    z with `axis` removed; out_val float32 and out_idx int64 with `axis`
+    replaced by a last axis of length n_out (in the selection order)."""
+    x = np.moveaxis(np.asarray(x, dtype=F32), axis, -1)
+    n = x.shape[-1]
+    assert 0 < n_out < n
+    order = np.argsort(-np.abs(x), axis=-1, kind="stable")   # ties: lower index first
+    out_idx = order[..., :n_out]
+    out_val = np.take_along_axis(x, out_idx, axis=-1)
+    moved = np.zeros(x.shape, bool)
+    np.put_along_axis(moved, out_idx, True, axis=-1)
+    levels = F32(2 ** bits - 1)
+    mn = np.where(moved, F32(np.inf), x).min(axis=-1, keepdims=True)
+    mx = np.where(moved, F32(-np.inf), x).max(axis=-1, keepdims=True)
+    mn = mn + F32(0.0)                         # -0 -> +0
+    s = (mx - mn) / levels
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.rint((x - mn) / s)
+    r = np.where(s == 0, F32(0.0), r)
+    r = np.where(moved, F32(0.0), r)           # moved positions: code 0
+    codes = np.clip(r, F32(0.0), levels).astype(np.uint8)
+    return (np.moveaxis(codes, -1, axis), np.squeeze(s, -1), np.squeeze(mn, -1),
+            out_val, out_idx)
+
+
+def kivi_dequantize_sparse(codes, s, z, out_val, out_idx, axis):
+    """Dense dequantisation code * s + z (float64) with the side matrix's
+    values put back exactly at their positions."""
+    x = np.moveaxis(kivi_dequantize(codes, s, z, axis), axis, -1).copy()
+    np.put_along_axis(x, np.asarray(out_idx), np.asarray(out_val, np.float64), axis=-1)
+    return np.moveaxis(x, -1, axis)
+
+
 def kivi_dequantize(codes, s, z, axis):
     """code * s + z in float64, s and z broadcast back along `axis`."""
     s64 = np.expand_dims(np.asarray(s, np.float64), axis)

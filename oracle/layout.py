@@ -47,18 +47,37 @@ def _full(n):
     return np.full(n, 0xFF, np.uint8)
 
 
-def kivi_page(k32, v32, bits, v_bits=None):
+def kivi_page(k32, v32, bits, v_bits=None, outliers=0):
     """One full KIVI page from 32 tokens of keys and values (float32 [32, d]);
-    value codes of v_bits when given, else of bits."""
+    value codes of v_bits when given, else of bits. With outliers == 1 the
+    dense-and-sparse encoding (``codec.kivi_quantize_sparse``, one outlier per
+    key channel and per value token) and its side matrix after the dense
+    page: key outlier values [d] float32, value outlier values [32] float32,
+    key outlier tokens [d] uint8, value outlier channels [32] uint8, then
+    padding to a multiple of 256 bytes (unspecified)."""
     vb = bits if v_bits is None else v_bits
-    kc, ks, kz = codec.kivi_quantize(k32, bits, axis=0)   # per channel over the tokens
-    vc, vs, vz = codec.kivi_quantize(v32, vb, axis=1)     # per token over the channels
+    d = k32.shape[1]
+    if outliers:
+        kc, ks, kz, ko, ki = codec.kivi_quantize_sparse(k32, bits, axis=0)
+        vc, vs, vz, vo, vi = codec.kivi_quantize_sparse(v32, vb, axis=1)
+    else:
+        kc, ks, kz = codec.kivi_quantize(k32, bits, axis=0)   # per channel over the tokens
+        vc, vs, vz = codec.kivi_quantize(v32, vb, axis=1)     # per token over the channels
     parts = [pack_fields(kc, bits),            # K rows: kc[t, c], channel fastest
              _f32_bytes(ks), _f32_bytes(kz),
              pack_fields(vc.T, vb),            # V cols: vc[t, c] stored channel-major
              _f32_bytes(vs), _f32_bytes(vz)]
+    masks = [_full(sum(x.size for x in parts))]
+    if outliers:
+        side = [_f32_bytes(ko[:, 0]), _f32_bytes(vo[:, 0]),
+                ki[:, 0].astype(np.uint8), vi[:, 0].astype(np.uint8)]
+        raw = sum(x.size for x in side)
+        pad = -(-raw // 256) * 256 - raw
+        parts += side + [np.zeros(pad, np.uint8)]
+        masks += [_full(raw), np.zeros(pad, np.uint8)]
+        assert raw == 5 * d + 5 * PAGE
     buf = np.concatenate(parts)
-    return buf, _full(buf.size)
+    return buf, np.concatenate(masks)
 
 
 def _valid_fields_mask(n_valid, per_row, bits):
