@@ -63,8 +63,8 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 5   /* 3: ragged-batch entry points; 4: several queries per sequence;
-                               5: decode without a caller workspace */
+#define KVQ_ABI_VERSION 6   /* 3: ragged-batch entry points; 4: several queries per sequence;
+                               5: decode without a caller workspace; 6: sparse outliers */
 
 /* Exported entry points (the library is built with hidden visibility). */
 #if defined(__GNUC__)
@@ -153,6 +153,13 @@ typedef struct kvq_config {
                             cache is quantized", INT8 / INT4 blocks with
                             separate key and value cache types); 0 = `bits`.
                             Other schemes: 0 or equal to `bits`.          */
+  int32_t  outliers;     /* KIVI: 1 = dense-and-sparse pages (each key
+                            channel's 32 tokens and each value token keep
+                            their largest-magnitude value exactly in a side
+                            matrix, [KVQ] Summary: a small fraction of
+                            outliers moved, per vector, into a separate
+                            sparse representation); 0 = dense pages. Must
+                            be 0 for the other schemes.                    */
 } kvq_config;
 
 /* ==== Cache layout, version 1 =============================================
@@ -180,6 +187,12 @@ typedef struct kvq_config {
  *   Vc  V cols, unsigned bv-bit codes     32*d*bv/8
  *   Vs  fp32 scale per token       128
  *   Vz  fp32 offset per token      128
+ *   With outliers = 1 the page continues with its side matrix
+ *   (5*d + 160 bytes, padded to a multiple of 256; the padding is unspecified):
+ *   Ko  fp32 key outlier per channel, the exact input value   4*d
+ *   Vo  fp32 value outlier per token, the exact input value   128
+ *   Ki  uint8 token (0..31) of each channel's key outlier     d
+ *   Vi  uint8 channel (0..d-1) of each token's value outlier  32
  *   Ring after the P pages: (R+32) K rows then (R+32) V rows, each d values of
  *   in_dtype; token t lives in slot t mod (R+32) while it is unquantised.
  * SYM_TOKEN page (8*d*b + 256 bytes), P = ceil(max_tokens/32):
@@ -209,6 +222,12 @@ typedef struct kvq_config {
  *   mn = min x (+0 replaces -0), mx = max x, s = (mx - mn) / L,
  *   code = s == 0 ? 0 : clamp(rint((x - mn) / s), 0, L),  stored offset = mn;
  *   dequantised value = code*s + mn.  [QKV] going deeper, Q_b and s.
+ * Dense-and-sparse KIVI group (outliers = 1): the value of largest magnitude
+ *   |x| of each vector (lowest index among equal magnitudes) goes to the side
+ *   matrix with its index; mn, mx and s above are taken over the other values
+ *   of the vector, and the moved position holds code 0. Dequantised: the
+ *   side matrix's value at that position, code*s + mn elsewhere. [KVQ]
+ *   Summary (outliers per vector in a sparse representation).
  * SYM_TOKEN, per (token, KV head), K and V separately, Q = 2^(b-1) - 1:
  *   s = max|x| / Q, code = s == 0 ? 0 : clamp(rint(x / s), -Q, Q);
  *   dequantised value = code*s.  [QC] Workshop.

@@ -45,6 +45,8 @@ struct AppendParams {
   int64_t ring_slots;
   int32_t kv_heads;
   int32_t off_kc, off_ks, off_kz, off_vc, off_vs, off_vz;
+  int32_t outliers;                           // KIVI dense-and-sparse pages (0 or 1)
+  int32_t off_ko, off_vo, off_ki, off_vi;     // their side matrix
 };
 
 // Tokens sequence b held before the call and tokens it appends: the uniform
@@ -99,6 +101,9 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
   static_assert(TPC <= 8 && (TPC & (TPC - 1)) == 0, "key statistics lane groups");
   __shared__ __attribute__((aligned(16))) uint8_t tile[2][kPage * PITCH];   // K rows, V rows
   __shared__ __attribute__((aligned(16))) float k_mn[D], k_s[D], k_r[D], v_mn[kPage], v_s[kPage], v_r[kPage];
+  // dense-and-sparse pages: the token of each key channel's outlier and the
+  // channel of each value token's outlier
+  __shared__ int k_oi[D], v_oi[kPage];
 
   const int tid = threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -150,16 +155,47 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
   }
   __syncthreads();
 
-  // 2a. key statistics per channel over the 32 tokens (TPC lanes per channel)
+  // Largest magnitude over a lane group's candidates (index lo, magnitude a):
+  // the larger one, the lower index among equal magnitudes.
+  auto argmax_abs = [](float& a, int& lo, int lanes) {
+    for (int m = 1; m < lanes; m <<= 1) {
+      const float oa = __shfl_xor(a, m, 64);
+      const int ol = __shfl_xor(lo, m, 64);
+      if (oa > a || (oa == a && ol < lo)) {
+        a = oa;
+        lo = ol;
+      }
+    }
+  };
+
+  // 2a. key statistics per channel over the 32 tokens (TPC lanes per channel);
+  //     dense-and-sparse pages first move each channel's largest |x| out
   for (int c0 = 0; c0 < D; c0 += kThreads / TPC) {
     const int c = c0 + tid / TPC, part = tid % TPC;
+    int oi = -1;   // token of this channel's outlier
+    if (p.outliers) {
+      float best = -1.0f;
+      int bi = 0;
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) {
+        const float a = fabsf(elem(0, part * RPT + r, c));
+        if (a > best) {
+          best = a;
+          bi = part * RPT + r;
+        }
+      }
+      argmax_abs(best, bi, TPC);
+      oi = bi;
+    }
     float mn = INFINITY, mx = -INFINITY;
     if (c < D) {
 #pragma unroll
       for (int r = 0; r < RPT; ++r) {
         const float x = elem(0, part * RPT + r, c);
-        mn = fminf(mn, x);
-        mx = fmaxf(mx, x);
+        if (part * RPT + r != oi) {
+          mn = fminf(mn, x);
+          mx = fmaxf(mx, x);
+        }
       }
     }
 #pragma unroll
@@ -173,19 +209,41 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
       k_mn[c] = mn;
       k_s[c] = s;
       k_r[c] = quant_rcp_prep(s);
+      k_oi[c] = oi;
       reinterpret_cast<float*>(pg + p.off_ks)[c] = s;
       reinterpret_cast<float*>(pg + p.off_kz)[c] = mn;
+      if (p.outliers) {
+        reinterpret_cast<float*>(pg + p.off_ko)[c] = elem(0, oi, c);   // exact input value
+        pg[p.off_ki + c] = static_cast<uint8_t>(oi);
+      }
     }
   }
   // 2b. value statistics per token over the D channels (8 lanes per token)
   {
     const int r = tid / TPT, part = tid % TPT;
+    int oi = -1;   // channel of this token's outlier
+    if (p.outliers) {
+      float best = -1.0f;
+      int bi = 0;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const float a = fabsf(elem(1, r, part * CPT + i));
+        if (a > best) {
+          best = a;
+          bi = part * CPT + i;
+        }
+      }
+      argmax_abs(best, bi, TPT);
+      oi = bi;
+    }
     float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const float x = elem(1, r, part * CPT + i);
-      mn = fminf(mn, x);
-      mx = fmaxf(mx, x);
+      if (part * CPT + i != oi) {
+        mn = fminf(mn, x);
+        mx = fmaxf(mx, x);
+      }
     }
 #pragma unroll
     for (int m = 1; m < TPT; m <<= 1) {
@@ -198,8 +256,13 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
       v_mn[r] = mn;
       v_s[r] = s;
       v_r[r] = quant_rcp_prep(s);
+      v_oi[r] = oi;
       reinterpret_cast<float*>(pg + p.off_vs)[r] = s;
       reinterpret_cast<float*>(pg + p.off_vz)[r] = mn;
+      if (p.outliers) {
+        reinterpret_cast<float*>(pg + p.off_vo)[r] = elem(1, r, oi);   // exact input value
+        pg[p.off_vi + r] = static_cast<uint8_t>(oi);
+      }
     }
   }
   __syncthreads();
@@ -246,6 +309,11 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
 #pragma unroll
     for (int j = 0; j < FPWK; ++j)
       word |= quant_asym_rcp(x[j], mn[j], k_s + c0 + j, rc[j], kLevelsK) << (j * KB);
+    if (p.outliers) {   // the moved values' fields hold code 0
+#pragma unroll
+      for (int j = 0; j < FPWK; ++j)
+        if (k_oi[c0 + j] == t) word &= ~(((1u << KB) - 1u) << (j * KB));
+    }
     kc[w] = word;
   }
   for (int w = tid; w < WORDSV; w += kThreads) {
@@ -258,6 +326,11 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
 #pragma unroll
     for (int j = 0; j < FPWV; ++j)
       word |= quant_asym_rcp(elem(1, t0 + j, c), mn[j], v_s + t0 + j, rc[j], kLevelsV) << (j * VB);
+    if (p.outliers) {
+#pragma unroll
+      for (int j = 0; j < FPWV; ++j)
+        if (v_oi[t0 + j] == c) word &= ~(((1u << VB) - 1u) << (j * VB));
+    }
     vc[w] = word;
   }
 }
@@ -656,6 +729,11 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
   p.off_vc = g.off_vc;
   p.off_vs = g.off_vs;
   p.off_vz = g.off_vz;
+  p.outliers = g.outliers;
+  p.off_ko = g.off_ko;
+  p.off_vo = g.off_vo;
+  p.off_ki = g.off_ki;
+  p.off_vi = g.off_vi;
   switch (g.d) {
     case 32: return dispatch_dtype<32>(a, p, st);
     case 64: return dispatch_dtype<64>(a, p, st);

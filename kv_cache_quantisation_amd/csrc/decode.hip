@@ -57,6 +57,8 @@ struct DecodeParams {
   int32_t q_bf16, in_bf16;
   float qscale;         // sm_scale * log2(e)
   double rope_theta;    // 0 = off
+  int32_t outliers;     // KIVI dense-and-sparse pages: side matrix offsets below
+  int32_t off_ko, off_vo, off_ki, off_vi;
 };
 
 template <int BITS>
@@ -115,6 +117,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   __shared__ float scratch[SCRATCH];          // per-wave folded query / scales; later the combine
   __shared__ float wp[kWaves][HG][kPage];
   __shared__ double w2pi[D / 2];
+  // dense-and-sparse pages (dynamic LDS, sized only when the cache has them),
+  // per wave: oki[D] token of each key channel's outlier, okd[D] its value
+  // (rotary keys) or its difference from the channel offset, voi[32] channel
+  // of each value token's outlier, wpo[HG][32] the weight of its difference
+  // from the token offset
+  extern __shared__ float dyn_lds[];
+  constexpr int OUT_LDS = 2 * D + kPage + HG * kPage;   // words per wave
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -126,6 +135,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   const bool rope = p.rope_theta > 0.0;
   const uint8_t* slab = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes;
   float* wq = scratch + wave * QROWS * D;
+  int* oki = reinterpret_cast<int*>(dyn_lds + wave * OUT_LDS);
+  float* okd = dyn_lds + wave * OUT_LDS + D;
+  int* voi = reinterpret_cast<int*>(dyn_lds + wave * OUT_LDS + 2 * D);
+  float* wpo = dyn_lds + wave * OUT_LDS + 2 * D + kPage;   // [HG][32]
   // tokens this sequence holds (a ragged batch: its own fill level, and for
   // KIVI its own split between quantised pages and the ring)
   const int64_t fill = seq_len(p.seq_tokens, b, p.T);
@@ -204,6 +217,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
       const float* kzp = reinterpret_cast<const float*>(pg + p.off_kz);
       for (int c = lane; c < D; c += 64) {
         const float s = ksp[c], z = kzp[c];
+        if (p.outliers) {   // the channel's outlier: its token, and what it adds
+          oki[c] = pg[p.off_ki + c];
+          const float ko = reinterpret_cast<const float*>(pg + p.off_ko)[c];
+          okd[c] = rope ? ko : ko - z;
+        }
         if (rope) {
           wq[c] = s;
           wq[D + c] = z;
@@ -250,6 +268,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
             if constexpr (SCHEME == KVQ_KIVI) {
 #pragma unroll
               for (int j = 0; j < FPW; ++j) kv[j] = kv[j] * wq[c0 + j] + wq[D + c0 + j];
+              if (p.outliers) {   // the side matrix's exact value at its position
+#pragma unroll
+                for (int j = 0; j < FPW; ++j) kv[j] = oki[c0 + j] == tok ? okd[c0 + j] : kv[j];
+              }
             }
 #pragma unroll
             for (int j = 0; j < FPW; j += 2)
@@ -264,6 +286,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         }
 #pragma unroll
         for (int g = 0; g < HG; ++g) acc[g] *= kst;
+        if (SCHEME == KVQ_KIVI && p.outliers && !rope) {
+          // moved key values: code 0 gave q z; add q (outlier - z)
+          for (int c = hf * HALF; c < hf * HALF + HALF; ++c) {
+            if (oki[c] == tok) {
+#pragma unroll
+              for (int g = 0; g < HG; ++g) acc[g] = fmaf(qs[g][c], okd[c], acc[g]);
+            }
+          }
+        }
       } else {
         // residual ring: exact input-dtype rows
         const int64_t t = t_first + tok;
@@ -286,11 +317,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
       }
 
       // ---- online softmax --------------------------------------------------
-      float vsc = 1.0f, vz = 0.0f;
+      float vsc = 1.0f, vz = 0.0f, vdo = 0.0f;
       if (is_page && valid) {
         if constexpr (SCHEME == KVQ_KIVI) {
           vsc = reinterpret_cast<const float*>(pg + p.off_vs)[tok];
           vz = reinterpret_cast<const float*>(pg + p.off_vz)[tok];
+          if (p.outliers) {   // moved value: code 0 gave z; its channel gets (outlier - z)
+            vdo = reinterpret_cast<const float*>(pg + p.off_vo)[tok] - vz;
+            if (hf == 0) voi[tok] = pg[p.off_vi + tok];
+          }
         } else if constexpr (SCHEME == KVQ_SYM_TOKEN) {
           vsc = reinterpret_cast<const float*>(pg + p.off_vs)[tok];
         }
@@ -306,7 +341,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
 #pragma unroll
         for (int c = 0; c < CPL; ++c) o[g][c] *= alpha;
         if (hf == 0) wp[wave][g][tok] = valid ? pe * vsc : 0.f;
+        if (p.outliers && hf == 0) wpo[g * kPage + tok] = valid ? pe * vdo : 0.f;
       }
+      if (p.outliers && hf == 0 && !(is_page && valid)) voi[tok] = -1;
     }
     __syncthreads();
 
@@ -329,6 +366,21 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
               const int t = ts * TPS + wi * FPWV + j;
 #pragma unroll
               for (int g = 0; g < HG; ++g) o[g][ci] = fmaf(wp[wave][g][t], cv, o[g][ci]);
+            }
+          }
+        }
+        if (SCHEME == KVQ_KIVI && p.outliers) {
+          for (int j = 0; j < TPS; ++j) {
+            const int t = ts * TPS + j;
+            const int oc = voi[t] - cs * CPL;   // outlier channel relative to this lane's
+            if (oc >= 0 && oc < CPL) {
+#pragma unroll
+              for (int ci = 0; ci < CPL; ++ci) {
+                if (ci == oc) {
+#pragma unroll
+                  for (int g = 0; g < HG; ++g) o[g][ci] += wpo[g * kPage + t];
+                }
+              }
             }
           }
         }
@@ -437,7 +489,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
 template <int SCHEME, int BITS, int VB, int D, int HG>
 hipError_t launch(const DecodeParams& p, int batch, hipStream_t st) {
   dim3 grid(p.splits, p.kv_heads, batch * p.nq);
-  hipLaunchKernelGGL((decode_split_kernel<SCHEME, BITS, VB, D, HG>), grid, dim3(kThreads), 0, st, p);
+  const size_t dyn = p.outliers ? kWaves * (2 * D + kPage + HG * kPage) * sizeof(float) : 0;
+  hipLaunchKernelGGL((decode_split_kernel<SCHEME, BITS, VB, D, HG>), grid, dim3(kThreads), dyn, st, p);
   return hipGetLastError();
 }
 
@@ -508,6 +561,11 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   p.in_bf16 = g.in_bytes == 2;
   p.qscale = a.sm_scale * kLog2e;
   p.rope_theta = a.rope_theta;
+  p.outliers = g.outliers;
+  p.off_ko = g.off_ko;
+  p.off_vo = g.off_vo;
+  p.off_ki = g.off_ki;
+  p.off_vi = g.off_vi;
   switch (g.scheme) {
     case KVQ_KIVI:
       switch (g.bits) {

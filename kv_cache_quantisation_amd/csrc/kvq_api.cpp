@@ -37,6 +37,7 @@ int32_t validate_config(const kvq_config* cfg) {
     if (c.scheme != KVQ_KIVI || c.v_bits < 1 || c.v_bits > 8) return KVQ_ERR_INVALID;
     if ((c.v_bits != 2 && c.v_bits != 4) || c.v_bits > c.bits) return KVQ_ERR_UNSUPPORTED;
   }
+  if (c.outliers != 0 && (c.outliers != 1 || c.scheme != KVQ_KIVI)) return KVQ_ERR_INVALID;
   if (c.layers < 1 || c.q_heads < 1 || c.kv_heads < 1 || c.batch < 1 || c.max_tokens < 0)
     return KVQ_ERR_INVALID;
   if (c.q_heads % c.kv_heads != 0) return KVQ_ERR_INVALID;
@@ -75,6 +76,7 @@ int32_t make_geometry(const kvq_config& c, Geometry* g) {
   const int32_t st = validate_config(&c);
   if (st != KVQ_OK) return st;
   Geometry x{};
+  x.off_ko = x.off_vo = x.off_ki = x.off_vi = -1;
   x.scheme = c.scheme;
   x.bits = c.bits;
   x.vbits = c.v_bits != 0 ? c.v_bits : c.bits;
@@ -101,6 +103,14 @@ int32_t make_geometry(const kvq_config& c, Geometry* g) {
       x.off_vz = codes + vcodes + 8 * d + 4 * kPage;
       x.page_bytes = codes + vcodes + 8 * d + 8 * kPage;
       x.ring_slots = c.residual + kPage;
+      if (c.outliers) {   // side matrix after the dense page, padded to 256 bytes
+        x.outliers = 1;
+        x.off_ko = static_cast<int32_t>(x.page_bytes);
+        x.off_vo = x.off_ko + 4 * d;
+        x.off_ki = x.off_vo + 4 * kPage;
+        x.off_vi = x.off_ki + d;
+        x.page_bytes += (5 * d + 5 * kPage + 255) / 256 * 256;
+      }
       break;
     case KVQ_SYM_TOKEN:
       x.off_kc = 0;

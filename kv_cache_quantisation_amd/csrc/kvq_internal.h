@@ -31,6 +31,9 @@ struct Geometry {
   int64_t slab_bytes;       // P * page_bytes + ring_bytes
   // byte offsets inside a page
   int32_t off_kc, off_ks, off_kz, off_vc, off_vs, off_vz;
+  // dense-and-sparse KIVI pages: one outlier per vector in the side matrix
+  int32_t outliers;
+  int32_t off_ko, off_vo, off_ki, off_vi;   // -1 without outliers
 };
 
 // Fills g from a validated config. Returns KVQ_OK or a negative status.

@@ -19,7 +19,7 @@ KVQ_KIVI, KVQ_SYM_TOKEN, KVQ_FP8_E4M3, KVQ_BF16_CACHE, KVQ_FP8_E5M2 = 0, 1, 2, 3
 KVQ_F32, KVQ_BF16 = 0, 1
 KVQ_BYTES_FORMULA, KVQ_BYTES_CACHE, KVQ_BYTES_WORKSPACE = 0, 1, 2
 
-ABI_VERSION = 5   # KVQ_ABI_VERSION of include/kvq.h that this binding mirrors
+ABI_VERSION = 6   # KVQ_ABI_VERSION of include/kvq.h that this binding mirrors
 
 SYMBOLS = ("kvq_cache_bytes", "kvq_quantize_append", "kvq_quantize_append_ragged",
            "kvq_decode_attention", "kvq_decode_attention_ragged", "kvq_decode_attention_multi",
@@ -53,12 +53,13 @@ class kvq_config(ctypes.Structure):
         ("sm_scale", ctypes.c_float),
         ("num_splits", ctypes.c_int32),
         ("v_bits", ctypes.c_int32),
+        ("outliers", ctypes.c_int32),
     ]
 
 
 def make_config(scheme, bits, layers, q_heads, kv_heads, head_dim, batch, max_tokens,
                 residual=0, in_dtype=KVQ_BF16, q_dtype=KVQ_BF16, rope_theta=0.0,
-                sm_scale=0.0, num_splits=0, group=32, v_bits=0):
+                sm_scale=0.0, num_splits=0, group=32, v_bits=0, outliers=0):
     c = kvq_config()
     c.struct_size = ctypes.sizeof(kvq_config)
     c.scheme, c.bits, c.layers = scheme, bits, layers
@@ -67,6 +68,7 @@ def make_config(scheme, bits, layers, q_heads, kv_heads, head_dim, batch, max_to
     c.in_dtype, c.q_dtype = in_dtype, q_dtype
     c.rope_theta, c.sm_scale, c.num_splits = rope_theta, sm_scale, num_splits
     c.v_bits = v_bits
+    c.outliers = outliers
     return c
 
 

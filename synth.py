@@ -10,6 +10,9 @@ library and the oracle both receive the tensors it makes. Distributions:
 * values ~ N(0,1) with floor(frac * T) outlier tokens per sequence multiplied
   by a factor, shared by the sequence's KV heads (KIVI: values have sporadic
   outlier tokens);
+* optionally, isolated elements of keys and values multiplied by a factor
+  (sparse outliers inside otherwise ordinary vectors, the case KVQuant's
+  dense-and-sparse pages address);
 * queries ~ N(0,1).
 Factors are applied in float32 before rounding to bfloat16 (round to nearest
 even). Every tensor comes from its own torch generator seeded by (workload,
@@ -44,6 +47,9 @@ class Workload:
     rope_theta: float = 0.0
     layers: int = 1
     v_bits: int = 0          # KIVI value-code bits; 0 = the key bits
+    outliers: int = 0        # KIVI: 1 = dense-and-sparse pages (a config field, no data)
+    spike_frac: float = 0.0  # fraction of single key and value elements scaled by spike_factor
+    spike_factor: float = 1.0
 
 
 WORKLOADS = {
@@ -119,6 +125,11 @@ def keys_values(w, layer=0, tokens=None, device="cpu", token_offset=0, tag=0):
         f = torch.ones(w.kv_heads, w.head_dim, device=device)
         f.scatter_(1, ch, w.k_outlier_factor)
         k.mul_(f.view(1, 1, w.kv_heads, w.head_dim))
+    if w.spike_frac > 0:
+        # isolated large elements (sparse outliers), drawn independently for K and V
+        for x, tid in ((k, 4), (v, 5)):
+            u = torch.rand(shape, generator=_gen(w, layer, tid + 100 * tag, device), device=device)
+            x.mul_(torch.where(u < w.spike_frac, w.spike_factor, 1.0))
     if tag == 0 and token_offset == 0:
         pos = outlier_tokens(w, layer, T, device)
         if pos is not None:

@@ -38,14 +38,15 @@ def config(w, capacity=None, num_splits=0, layers=None):
     return kvq.make_config(w.scheme, w.bits, layers or w.layers, w.q_heads, w.kv_heads,
                            w.head_dim, w.batch, capacity or w.tokens, residual=w.residual,
                            in_dtype=DT[w.in_dtype], q_dtype=DT[w.q_dtype],
-                           rope_theta=w.rope_theta, num_splits=num_splits, v_bits=w.v_bits)
+                           rope_theta=w.rope_theta, num_splits=num_splits, v_bits=w.v_bits,
+                           outliers=w.outliers)
 
 
 def oracle_cache(w, capacity=None, layers=None):
     return OracleCache(w.scheme, w.bits, layers or w.layers, w.batch, w.kv_heads, w.head_dim,
                        capacity or w.tokens, residual=w.residual,
                        in_dtype="bf16" if w.in_dtype == torch.bfloat16 else "f32",
-                       v_bits=w.v_bits or None)
+                       v_bits=w.v_bits or None, outliers=w.outliers)
 
 
 def append_chunks(cfg, cache, k, v, chunks, layer=0, ks=None, vs=None, oc=None):

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert kvq.kvq_abi_version() == 5
+    assert kvq.kvq_abi_version() == 6
     assert kvq.status_string(0) == "ok"
     for st in (-1, -2, -3, -4, -5, -6):
         assert kvq.status_string(st) != "unknown status"
@@ -314,3 +314,26 @@ def test_noalloc_validation():
     need = kvq.kvq_cache_bytes(big, 1 << 16, kvq.KVQ_BYTES_WORKSPACE)
     assert need > kvq.KVQ_NOALLOC_SCRATCH_BYTES
     assert na(ctypes.byref(big), f, 0, 1 << 16, f, None, None, f, None) == kvq.KVQ_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("bits,v_bits,d,R,dtype", [
+    (2, 0, 128, 128, kvq.KVQ_BF16), (4, 2, 64, 0, kvq.KVQ_F32), (8, 0, 256, 37, kvq.KVQ_BF16),
+    (2, 0, 32, 5, kvq.KVQ_F32)])
+def test_sparse_outlier_sizes_and_validation(bits, v_bits, d, R, dtype):
+    """Dense-and-sparse KIVI pages: each page grows by its side matrix
+    (5 d + 160 bytes, padded to 256) exactly as the oracle's layout has it;
+    only KIVI takes outliers, and only 0 or 1."""
+    c = cfg(bits=bits, v_bits=v_bits, head_dim=d, residual=R, in_dtype=dtype, q_heads=8,
+            outliers=1)
+    item = 2 if dtype == kvq.KVQ_BF16 else 4
+    for T in (0, 1, 31, 33, 161, 4096, 10000):
+        assert kvq.kvq_cache_bytes(c, T, kvq.KVQ_BYTES_CACHE) == \
+            acc.layout_cache_bytes(kvq.KVQ_KIVI, 2, 3, 8, d, bits, T, R, item, v_bits or None,
+                                   outliers=1), T
+    L = kvq.lib()
+    def st(**kw):
+        return L.kvq_cache_bytes(ctypes.byref(cfg(**kw)), 64, kvq.KVQ_BYTES_CACHE)
+    assert st(outliers=2) == kvq.KVQ_ERR_INVALID
+    assert st(outliers=-1) == kvq.KVQ_ERR_INVALID
+    assert st(scheme=kvq.KVQ_SYM_TOKEN, bits=4, residual=0, outliers=1) == kvq.KVQ_ERR_INVALID
+    assert st(scheme=kvq.KVQ_FP8_E4M3, bits=8, residual=0, outliers=1) == kvq.KVQ_ERR_INVALID
