@@ -63,8 +63,9 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 6   /* 3: ragged-batch entry points; 4: several queries per sequence;
-                               5: decode without a caller workspace; 6: sparse outliers */
+#define KVQ_ABI_VERSION 7   /* 3: ragged-batch entry points; 4: several queries per sequence;
+                               5: decode without a caller workspace; 6: sparse outliers;
+                               7: paged caches (block tables) */
 
 /* Exported entry points (the library is built with hidden visibility). */
 #if defined(__GNUC__)
@@ -340,6 +341,59 @@ KVQ_API int32_t kvq_decode_attention_ragged(const kvq_config* cfg, const void* c
                                     const float* k_scale, const float* v_scale,
                                     float* out, void* workspace,
                                     size_t workspace_bytes, void* stream);
+
+/* ==== Paged cache (block table) ============================================
+ * KIVI reduces the bytes per token and paged allocation removes the slab
+ * fragmentation; serving needs both ([KIVI] Key points: KIVI pairs with
+ * PagedAttention). A paged cache is one byte buffer holding, in this order:
+ *   rings   one residual ring per (layer, sequence, KV head), index
+ *           (layer*batch + seq)*kv_heads + h, each 2*(R+32)*d*in_bytes bytes
+ *           as in layout v1 (KIVI only; empty for the other schemes); the
+ *           region is padded to a multiple of 256 bytes;
+ *   blocks  per layer, num_blocks physical blocks; block n of layer l holds
+ *           one page (layout v1, page_bytes) per KV head: page of head h at
+ *           blocks + ((l*num_blocks + n)*kv_heads + h)*page_bytes.
+ * block_table: device int32 [batch][max_blocks]; entry [b][p] is the block
+ * that holds page p (tokens 32p..32p+31) of sequence b in every layer. A
+ * sequence may use any blocks; two sequences must not share a block (the
+ * caller's allocator owns the table). Entries outside [0, num_blocks) are
+ * clamped into it on the device (every access stays inside the buffer; the
+ * result is then meaningless, not a fault). max_blocks must cover a full
+ * sequence: max_blocks >= floor(max(0, max_tokens - R)/32) pages for KIVI,
+ * ceil(max_tokens/32) for the other schemes (else KVQ_ERR_CAPACITY).
+ * The paged calls take per-sequence counts as the ragged ones do. With the
+ * same counts, every page holds the same bytes as in the slab layout, and
+ * decode gives the same result bit for bit.
+ * ========================================================================== */
+
+/* Bytes of a paged cache with num_blocks blocks per layer (rings included),
+ * or a negative status. Host-only. */
+KVQ_API int64_t kvq_paged_cache_bytes(const kvq_config* cfg, int64_t num_blocks);
+
+/* kvq_quantize_append_ragged into a paged cache: sequence b's page p is
+ * written in block block_table[b][p] (KIVI rings in the ring region).
+ *   block_table  device int32 [batch][max_blocks], 4-byte aligned
+ *   max_blocks   row length of the table (see above)
+ *   num_blocks   blocks per layer in `cache` (1 .. 2^31-1); `cache` holds at
+ *                least kvq_paged_cache_bytes(cfg, num_blocks) bytes
+ * Other arguments, clamping of the counts, and errors as
+ * kvq_quantize_append_ragged; a NULL table is KVQ_ERR_NULL. */
+KVQ_API int32_t kvq_quantize_append_paged(const kvq_config* cfg, void* cache, int32_t layer,
+                                  const int32_t* block_table, int32_t max_blocks,
+                                  int64_t num_blocks, const int64_t* seq_past,
+                                  const int64_t* seq_new, int64_t new_max, const void* k_new,
+                                  const void* v_new, const float* k_scale, const float* v_scale,
+                                  void* stream);
+
+/* kvq_decode_attention_ragged over a paged cache (block table as for
+ * kvq_quantize_append_paged). Workspace, arguments and errors as
+ * kvq_decode_attention_ragged. */
+KVQ_API int32_t kvq_decode_attention_paged(const kvq_config* cfg, const void* cache,
+                                   int32_t layer, const int32_t* block_table,
+                                   int32_t max_blocks, int64_t num_blocks, int64_t tokens,
+                                   const int64_t* seq_tokens, const void* q,
+                                   const float* k_scale, const float* v_scale, float* out,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Decode attention for several new queries per sequence, causally (chunked
  * prefill, or verifying speculated tokens, over the quantised cache): the

@@ -10,6 +10,7 @@ from .kvq import (  # noqa: F401
     KVQ_BF16_CACHE, KVQ_F32, KVQ_FP8_E4M3, KVQ_FP8_E5M2, KVQ_KIVI, KVQ_OK, KVQ_SYM_TOKEN, KvqError, alloc_cache,
     alloc_workspace, kvq_abi_version, kvq_cache_bytes, kvq_config, kvq_decode_attention,
     kvq_decode_attention_multi, kvq_decode_attention_noalloc, kvq_decode_attention_ragged,
-    kvq_quantize_append_ragged, KVQ_NOALLOC_SCRATCH_BYTES,
+    kvq_quantize_append_ragged, KVQ_NOALLOC_SCRATCH_BYTES, kvq_paged_cache_bytes,
+    kvq_quantize_append_paged, kvq_decode_attention_paged,
     kvq_quantize_append, lib, make_config, status_string,
 )

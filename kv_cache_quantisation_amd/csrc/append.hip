@@ -30,6 +30,7 @@ namespace {
 constexpr int kThreads = 256;
 
 struct AppendParams {
+  PageMap pm;                                 // pages and rings of the layer (slab or paged)
   uint8_t* layer_base;
   const uint8_t* k_new;
   const uint8_t* v_new;
@@ -112,8 +113,8 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
   // pages this sequence flushes: [q(past), q(past + n)) / 32
   const int64_t page = kivi_quantised(past, p.residual) / kPage + blockIdx.x;
   if (page >= kivi_quantised(past + n, p.residual) / kPage) return;   // whole block
-  uint8_t* slab = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes;
-  uint8_t* pg = slab + page * p.page_bytes;
+  uint8_t* pg = p.pm.page(b, h, page);
+  const uint8_t* ringp = p.pm.ring(b, h);
 
   auto elem = [&](int which, int r, int c) -> float {
     const uint8_t* row = tile[which] + r * PITCH;
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
       const int r = (i / CHUNKS) % kPage;
       const int64_t t = t_page + r;
       const int slot = s0 + r >= slots ? s0 + r - slots : s0 + r;
-      const uint8_t* ring = slab + p.ring_base + (static_cast<int64_t>(which) * p.ring_slots + slot) * ROW;
+      const uint8_t* ring = ringp + (static_cast<int64_t>(which) * p.ring_slots + slot) * ROW;
       const int64_t j = t >= past ? t - past : 0;
       const uint8_t* in = (which ? p.v_new : p.k_new) +
                           ((static_cast<int64_t>(b) * p.stride + j) * p.kv_heads + h) * ROW;
@@ -349,13 +350,13 @@ __global__ __launch_bounds__(64) void ring_write_kernel(AppendParams p) {
   if (t >= past + n) return;
   const int64_t j = t - past;
   const int64_t row_bytes = static_cast<int64_t>(D) * IB;
-  uint8_t* slab = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes;
+  uint8_t* ringp = p.pm.ring(b, h);
   const int64_t slot = t % p.ring_slots;
   const int64_t in_off = ((static_cast<int64_t>(b) * p.stride + j) * p.kv_heads + h) * row_bytes;
   for (int i = threadIdx.x; i < 2 * CHUNKS; i += 64) {
     const int which = i / CHUNKS, c = i % CHUNKS;
     const uint8_t* src = (which ? p.v_new : p.k_new) + in_off + c * 16;
-    uint8_t* dst = slab + p.ring_base + (which * p.ring_slots + slot) * row_bytes + c * 16;
+    uint8_t* dst = ringp + (which * p.ring_slots + slot) * row_bytes + c * 16;
     *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
   }
 }
@@ -384,8 +385,7 @@ __global__ __launch_bounds__(kThreads) void token_append_kernel(AppendParams p) 
   const int lo = static_cast<int>((past > page * kPage ? past : page * kPage) - page * kPage);
   const int hi = static_cast<int>((end < page * kPage + kPage ? end : page * kPage + kPage) -
                                   page * kPage);
-  uint8_t* slab = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes;
-  uint8_t* pg = slab + page * p.page_bytes;
+  uint8_t* pg = p.pm.page(b, h, page);
   const int64_t row_bytes = static_cast<int64_t>(D) * IB;
 
   // every load of the thread is issued before the first LDS write (threads
@@ -496,8 +496,7 @@ __global__ __launch_bounds__(kThreads) void byte_append_kernel(AppendParams p, i
   const int lo = static_cast<int>((past > page * kPage ? past : page * kPage) - page * kPage);
   const int hi = static_cast<int>((end < page * kPage + kPage ? end : page * kPage + kPage) -
                                   page * kPage);
-  uint8_t* pg = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes +
-                page * p.page_bytes;
+  uint8_t* pg = p.pm.page(b, h, page);
   constexpr int64_t ROW = static_cast<int64_t>(D) * IB;
   const int64_t row_stride = static_cast<int64_t>(p.kv_heads) * ROW;
   // input row of page token r (valid only for lo <= r < hi)
@@ -706,6 +705,7 @@ hipError_t dispatch_dtype(const AppendArgs& a, const AppendParams& p, hipStream_
 hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
   const Geometry& g = a.g;
   AppendParams p{};
+  p.pm = a.pm;
   p.layer_base = a.layer_base;
   p.k_new = static_cast<const uint8_t*>(a.k_new);
   p.v_new = static_cast<const uint8_t*>(a.v_new);

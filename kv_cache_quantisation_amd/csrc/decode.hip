@@ -39,6 +39,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct DecodeParams {
+  PageMap pm;           // pages and rings of the layer (slab or paged)
   const uint8_t* layer_base;
   const uint8_t* q;
   const float* k_scale;
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   const int row = blockIdx.z;                 // query row: sequence b, query qi
   const int b = row / p.nq, qi = row - b * p.nq;
   const bool rope = p.rope_theta > 0.0;
-  const uint8_t* slab = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes;
+  const uint8_t* ringp = p.pm.ring(b, h);
   float* wq = scratch + wave * QROWS * D;
   int* oki = reinterpret_cast<int*>(dyn_lds + wave * OUT_LDS);
   float* okd = dyn_lds + wave * OUT_LDS + D;
@@ -202,7 +203,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     const int item = i0 + r * kWaves + wave;
     const bool active = item < i1;
     const bool is_page = item < n_pages;
-    const uint8_t* pg = slab + static_cast<int64_t>(item) * p.page_bytes;
+    // (the block table is read only for pages this wave takes)
+    const uint8_t* pg = active && is_page ? p.pm.page(b, h, item) : ringp;
     const int64_t t_first = is_page ? static_cast<int64_t>(item) * kPage
                                     : q_tokens + static_cast<int64_t>(item - n_pages) * kPage;
     const int n_valid = static_cast<int>(Tb - t_first < kPage ? Tb - t_first : kPage);
@@ -300,7 +302,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         const int64_t t = t_first + tok;
         if (valid) {
           const int64_t slot = t % p.ring_slots;
-          const uint8_t* row = slab + p.ring_base + slot * D * (p.in_bf16 ? 2 : 4);
+          const uint8_t* row = ringp + slot * D * (p.in_bf16 ? 2 : 4);
           for (int c = hf * HALF; c < hf * HALF + HALF; c += 2) {
             float x0 = load_elem(row, c, p.in_bf16);
             float x1 = load_elem(row, c + 1, p.in_bf16);
@@ -390,7 +392,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
           const int tl = ts * TPS + j;
           if (tl >= n_valid) break;
           const int64_t slot = (t_first + tl) % p.ring_slots;
-          const uint8_t* row = slab + p.ring_base + (p.ring_slots + slot) * D * ib;
+          const uint8_t* row = ringp + (p.ring_slots + slot) * D * ib;
 #pragma unroll
           for (int ci = 0; ci < CPL; ++ci) {
             const float x = load_elem(row, cs * CPL + ci, p.in_bf16);
@@ -525,6 +527,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   if (a.nq > 1 && !a.seq_tokens && mfma_multi_ok(g, a.tokens, a.nq)) return launch_kivi_mfma(a, st);
   if (fp8_mfma_path(g) && (a.nq <= 1 || !a.seq_tokens)) return launch_fp8_mfma(a, st);
   DecodeParams p{};
+  p.pm = a.pm;
   p.layer_base = a.layer_base;
   p.q = static_cast<const uint8_t*>(a.q);
   p.k_scale = a.k_scale;

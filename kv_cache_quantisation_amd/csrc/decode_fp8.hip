@@ -52,6 +52,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct Fp8Params {
+  PageMap pm;                     // pages of the layer (slab or paged)
   const uint8_t* layer_base;
   const uint8_t* q;
   const float* k_scale;           // [kv_heads] of this layer
@@ -122,7 +123,6 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   const int row = blockIdx.z;                      // query row b * nq + qi
   const int b = row / p.nq, qi = row - b * p.nq;   // sequence, its query
   const int unit = b * p.kv_heads + h;             // one arrival counter for every row of b
-  const uint8_t* slab = p.layer_base + static_cast<int64_t>(unit) * p.slab_bytes;
   uint8_t* wbuf = arena + wave * PG::WAVE_LDS;
   const float ks_h = E5 ? p.k_scale[h] : 1.0f;   // applied to the scores (E5M2)
 
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   const int n_mine = pg0 + wave < pg1 ? (pg1 - pg0 - wave + kWaves - 1) / kWaves : 0;
 
   auto issue_page = [&](int k) {
-    const uint8_t* src = slab + static_cast<int64_t>(pg0 + wave + kWaves * k) * p.page_bytes;
+    const uint8_t* src = p.pm.page(b, h, pg0 + wave + kWaves * k);
     const uint32_t dst = lds_addr(wbuf + (k % PG::NBUF) * PG::BYTES);
 #pragma unroll
     for (int i = 0; i < PG::DMA; ++i) {
@@ -152,8 +152,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   };
   // bf16 values: lane (j, g) loads tokens 8g..8g+7 of channel 16 nt + j (16 bytes)
   auto load_values = [&](int k, uint4* vr) {
-    const uint8_t* src = slab + static_cast<int64_t>(pg0 + wave + kWaves * k) * p.page_bytes +
-                         PG::OFF_VC + 16 * g;
+    const uint8_t* src = p.pm.page(b, h, pg0 + wave + kWaves * k) + PG::OFF_VC + 16 * g;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
       vr[nt] = *reinterpret_cast<const uint4*>(src + (16 * nt + j) * (kPage * 2));
@@ -536,6 +535,7 @@ hipError_t launch_fp8_mfma(const DecodeArgs& a, hipStream_t st) {
   Geometry rows = g;
   rows.batch = g.batch * nq;
   Fp8Params p{};
+  p.pm = a.pm;
   p.layer_base = a.layer_base;
   p.q = static_cast<const uint8_t*>(a.q);
   p.k_scale = a.k_scale;

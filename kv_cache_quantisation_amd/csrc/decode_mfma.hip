@@ -67,6 +67,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMaxSlack = 8.0f;  // log2 units a score may exceed the running max by
 
 struct MfmaParams {
+  PageMap pm;                     // pages and rings of the layer (slab or paged)
   const uint8_t* layer_base;
   const uint8_t* q;
   float* out;
@@ -387,7 +388,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   const int j = lane & 15, g = lane >> 4;
   const int split = blockIdx.x, h = blockIdx.y;
   const int b = blockIdx.z / p.nq, qi = blockIdx.z - b * p.nq;   // sequence, its query
-  const uint8_t* slab = p.layer_base + (static_cast<int64_t>(b) * p.kv_heads + h) * p.slab_bytes;
+  const uint8_t* ringp = p.pm.ring(b, h);
   // tokens this sequence holds (a ragged batch: its own fill level, and its
   // own split between quantised pages and the ring)
   const int64_t fill = seq_len(p.seq_tokens, b, p.T);
@@ -513,7 +514,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   };
 
   auto issue_page = [&](int k) {   // page k of this wave -> buffer k % NBUF
-    const uint8_t* src = slab + static_cast<int64_t>(pg0 + wave + NW * k) * p.page_bytes;
+    const uint8_t* src = p.pm.page(b, h, pg0 + wave + NW * k);
     const uint32_t dst = lds_addr(wbuf + (k % PG::NBUF) * PG::BYTES);
 #pragma unroll
     for (int i = 0; i < PG::DMA; ++i) {
@@ -787,7 +788,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
         if (i * RPI >= nv) continue;          // wave-uniform: no row of this copy exists
         const int r = i * RPI + row_in;
         const int slot = slot0 + r < slots ? slot0 + r : slot0 + r - slots;
-        const uint8_t* src = slab + p.ring_base + (kv * p.ring_slots + slot) * (2 * D) + col_b;
+        const uint8_t* src = ringp + (kv * p.ring_slots + slot) * (2 * D) + col_b;
         if (r < nv && r < RSTEP) dma16(src, lds_addr(wring + kv * RSTEP * 2 * D + i * 1024));
         ++issued;
       }
@@ -1097,8 +1098,7 @@ __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
   const int hf = lane >> 5;                         // channel half of this lane
   const int split = blockIdx.x, h = blockIdx.y;
   const int b = blockIdx.z / p.nq, qi = blockIdx.z - b * p.nq;   // sequence, its query
-  const int unit = b * p.kv_heads + h;
-  const uint8_t* slab = p.layer_base + static_cast<int64_t>(unit) * p.slab_bytes;
+  const uint8_t* ringp = p.pm.ring(b, h);
   uint8_t* wbuf = arena + wave * WAVE_LDS;
   uint8_t* wring = wbuf;
   // tokens this sequence holds (a ragged batch: its own fill level, and its
@@ -1126,7 +1126,7 @@ __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
   const int my_wave = (NW - 1 - wave) * p.splits + split;
 
   auto issue_page = [&](int k) {
-    const uint8_t* src = slab + static_cast<int64_t>(pg0 + wave + NW * k) * p.page_bytes;
+    const uint8_t* src = p.pm.page(b, h, pg0 + wave + NW * k);
     const uint32_t dst = lds_addr(wbuf + (k % 2) * PG::BYTES);
 #pragma unroll
     for (int i = 0; i < PG::DMA; ++i) {
@@ -1152,7 +1152,7 @@ __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
         if (i * RPI >= nv) continue;
         const int r = i * RPI + row_in;
         const int slot = slot0 + r < slots ? slot0 + r : slot0 + r - slots;
-        const uint8_t* src = slab + p.ring_base + (kv * p.ring_slots + slot) * (2 * D) + col_b;
+        const uint8_t* src = ringp + (kv * p.ring_slots + slot) * (2 * D) + col_b;
         if (r < nv && r < RSTEP) dma16(src, lds_addr(wring + kv * RSTEP * 2 * D + i * 1024));
         ++issued;
       }
@@ -1628,6 +1628,7 @@ hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t st) {
   rows.batch = g.batch * nq;
   const MfmaPlan pl = mfma_plan(rows, a.tokens, a.requested_splits);
   MfmaParams p{};
+  p.pm = a.pm;
   p.layer_base = a.layer_base;
   p.q = static_cast<const uint8_t*>(a.q);
   p.out = a.out;

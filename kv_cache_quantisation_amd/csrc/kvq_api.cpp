@@ -141,6 +141,39 @@ int32_t make_geometry(const kvq_config& c, Geometry* g) {
   return KVQ_OK;
 }
 
+int64_t paged_ring_region(const Geometry& g) {
+  const int64_t r = mul_ck(mul_ck(mul_ck(g.layers, g.batch), g.kv_heads), g.ring_bytes);
+  return r < 0 ? -1 : (r + 255) / 256 * 256;
+}
+
+int64_t paged_cache_bytes(const Geometry& g, int64_t num_blocks) {
+  const int64_t rings = paged_ring_region(g);
+  const int64_t blocks = mul_ck(mul_ck(mul_ck(g.layers, num_blocks), g.kv_heads), g.page_bytes);
+  if (rings < 0 || blocks < 0 || blocks > std::numeric_limits<int64_t>::max() - rings) return -1;
+  return rings + blocks;
+}
+
+PageMap make_page_map(const Geometry& g, const uint8_t* cache, int32_t layer,
+                      const int32_t* table, int32_t max_blocks, int64_t num_blocks) {
+  PageMap m{};
+  uint8_t* c = const_cast<uint8_t*>(cache);
+  m.page_bytes = g.page_bytes;
+  m.kv_heads = g.kv_heads;
+  if (!table) {
+    m.base = c + static_cast<int64_t>(layer) * g.batch * g.kv_heads * g.slab_bytes;
+    m.unit_bytes = g.slab_bytes;
+    m.ring_off = g.pages_per_slab * g.page_bytes;
+    return m;
+  }
+  m.table = table;
+  m.max_blocks = max_blocks;
+  m.num_blocks = static_cast<int32_t>(num_blocks);
+  m.rings = c + static_cast<int64_t>(layer) * g.batch * g.kv_heads * g.ring_bytes;
+  m.base = c + paged_ring_region(g) + static_cast<int64_t>(layer) * num_blocks * g.kv_heads * g.page_bytes;
+  m.unit_bytes = g.ring_bytes;
+  return m;
+}
+
 int32_t decode_items(const Geometry& g, int64_t tokens) {
   if (g.scheme == KVQ_KIVI) {
     const int64_t q = kivi_quantised(tokens, g.residual);
@@ -265,6 +298,7 @@ int32_t kvq_quantize_append(const kvq_config* cfg, void* cache, int32_t layer,
     return KVQ_ERR_INVALID;
   kvq::AppendArgs a{};
   a.g = g;
+  a.pm = kvq::make_page_map(g, static_cast<uint8_t*>(cache), layer, nullptr, 0, 0);
   a.layer_base = static_cast<uint8_t*>(cache) +
                  static_cast<int64_t>(layer) * cfg->batch * cfg->kv_heads * g.slab_bytes;
   a.k_new = k_new;
@@ -277,10 +311,15 @@ int32_t kvq_quantize_append(const kvq_config* cfg, void* cache, int32_t layer,
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
 }
 
-int32_t kvq_quantize_append_ragged(const kvq_config* cfg, void* cache, int32_t layer,
-                                   const int64_t* seq_past, const int64_t* seq_new,
-                                   int64_t new_max, const void* k_new, const void* v_new,
-                                   const float* k_scale, const float* v_scale, void* stream) {
+}  // extern "C"
+
+namespace {
+// Ragged quantize-append into the slab layout (table null) or a paged cache.
+int32_t append_ragged(const kvq_config* cfg, void* cache, int32_t layer, const int32_t* table,
+                      int32_t max_blocks, int64_t num_blocks, const int64_t* seq_past,
+                      const int64_t* seq_new, int64_t new_max, const void* k_new,
+                      const void* v_new, const float* k_scale, const float* v_scale,
+                      void* stream) {
   if (!cfg) return KVQ_ERR_NULL;
   Geometry g;
   const int32_t st = kvq::make_geometry(*cfg, &g);
@@ -298,6 +337,7 @@ int32_t kvq_quantize_append_ragged(const kvq_config* cfg, void* cache, int32_t l
     return KVQ_ERR_INVALID;
   kvq::AppendArgs a{};
   a.g = g;
+  a.pm = kvq::make_page_map(g, static_cast<uint8_t*>(cache), layer, table, max_blocks, num_blocks);
   a.layer_base = static_cast<uint8_t*>(cache) +
                  static_cast<int64_t>(layer) * cfg->batch * cfg->kv_heads * g.slab_bytes;
   a.k_new = k_new;
@@ -312,6 +352,56 @@ int32_t kvq_quantize_append_ragged(const kvq_config* cfg, void* cache, int32_t l
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
 }
 
+// Validates a block table's arguments against the configuration.
+int32_t check_table(const kvq_config* cfg, const kvq::Geometry& g, const int32_t* table,
+                    int32_t max_blocks, int64_t num_blocks) {
+  if (!table) return KVQ_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(table) & 3u) != 0) return KVQ_ERR_INVALID;
+  if (max_blocks < 1 || num_blocks < 1) return KVQ_ERR_INVALID;
+  if (num_blocks > INT32_MAX) return KVQ_ERR_UNSUPPORTED;
+  if (max_blocks < g.pages_per_slab) return KVQ_ERR_CAPACITY;   // a full sequence's pages
+  (void)cfg;
+  return kvq::paged_cache_bytes(g, num_blocks) < 0 ? KVQ_ERR_INVALID : KVQ_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int32_t kvq_quantize_append_ragged(const kvq_config* cfg, void* cache, int32_t layer,
+                                   const int64_t* seq_past, const int64_t* seq_new,
+                                   int64_t new_max, const void* k_new, const void* v_new,
+                                   const float* k_scale, const float* v_scale, void* stream) {
+  return append_ragged(cfg, cache, layer, nullptr, 0, 0, seq_past, seq_new, new_max, k_new,
+                       v_new, k_scale, v_scale, stream);
+}
+
+int32_t kvq_quantize_append_paged(const kvq_config* cfg, void* cache, int32_t layer,
+                                  const int32_t* block_table, int32_t max_blocks,
+                                  int64_t num_blocks, const int64_t* seq_past,
+                                  const int64_t* seq_new, int64_t new_max, const void* k_new,
+                                  const void* v_new, const float* k_scale, const float* v_scale,
+                                  void* stream) {
+  if (!cfg) return KVQ_ERR_NULL;
+  kvq::Geometry g;
+  const int32_t st = kvq::make_geometry(*cfg, &g);
+  if (st != KVQ_OK) return st;
+  const int32_t tst = check_table(cfg, g, block_table, max_blocks, num_blocks);
+  if (tst != KVQ_OK) return tst;
+  return append_ragged(cfg, cache, layer, block_table, max_blocks, num_blocks, seq_past, seq_new,
+                       new_max, k_new, v_new, k_scale, v_scale, stream);
+}
+
+int64_t kvq_paged_cache_bytes(const kvq_config* cfg, int64_t num_blocks) {
+  if (!cfg) return KVQ_ERR_NULL;
+  kvq::Geometry g;
+  const int32_t st = kvq::make_geometry(*cfg, &g);
+  if (st != KVQ_OK) return st;
+  if (num_blocks < 0) return KVQ_ERR_INVALID;
+  if (num_blocks > INT32_MAX) return KVQ_ERR_UNSUPPORTED;
+  const int64_t v = kvq::paged_cache_bytes(g, num_blocks);
+  return v < 0 ? KVQ_ERR_INVALID : v;
+}
+
 }  // extern "C"
 
 namespace kvq {
@@ -319,7 +409,8 @@ namespace kvq {
 int32_t decode_prepare(const kvq_config* cfg, const void* cache, int32_t layer, int64_t tokens,
                        const int64_t* seq_tokens, int32_t nq, const void* q,
                        const float* k_scale, const float* v_scale, float* out, void* workspace,
-                       size_t workspace_bytes, DecodeArgs* args) {
+                       size_t workspace_bytes, DecodeArgs* args, const int32_t* table,
+                       int32_t max_blocks, int64_t num_blocks) {
   if (!cfg) return KVQ_ERR_NULL;
   Geometry g;
   const int32_t st = make_geometry(*cfg, &g);
@@ -339,6 +430,7 @@ int32_t decode_prepare(const kvq_config* cfg, const void* cache, int32_t layer, 
   if (workspace_bytes / static_cast<size_t>(nq) < static_cast<size_t>(one)) return KVQ_ERR_WORKSPACE;
   DecodeArgs a{};
   a.g = g;
+  a.pm = make_page_map(g, static_cast<const uint8_t*>(cache), layer, table, max_blocks, num_blocks);
   a.layer_base = static_cast<const uint8_t*>(cache) +
                  static_cast<int64_t>(layer) * cfg->batch * cfg->kv_heads * g.slab_bytes;
   a.tokens = tokens;
@@ -369,10 +461,12 @@ namespace {
 int32_t decode_call(const kvq_config* cfg, const void* cache, int32_t layer, int64_t tokens,
                     const int64_t* seq_tokens, int32_t nq, const void* q, const float* k_scale,
                     const float* v_scale, float* out, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+                    void* stream, const int32_t* table = nullptr, int32_t max_blocks = 0,
+                    int64_t num_blocks = 0) {
   kvq::DecodeArgs a;
   const int32_t st = kvq::decode_prepare(cfg, cache, layer, tokens, seq_tokens, nq, q, k_scale,
-                                         v_scale, out, workspace, workspace_bytes, &a);
+                                         v_scale, out, workspace, workspace_bytes, &a, table,
+                                         max_blocks, num_blocks);
   if (st != KVQ_OK) return st;
   const hipError_t e = kvq::launch_decode(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
@@ -395,6 +489,24 @@ int32_t kvq_decode_attention_multi(const kvq_config* cfg, const void* cache, int
                                    void* workspace, size_t workspace_bytes, void* stream) {
   return decode_call(cfg, cache, layer, tokens, nullptr, n_queries, q, k_scale, v_scale, out,
                      workspace, workspace_bytes, stream);
+}
+
+int32_t kvq_decode_attention_paged(const kvq_config* cfg, const void* cache, int32_t layer,
+                                   const int32_t* block_table, int32_t max_blocks,
+                                   int64_t num_blocks, int64_t tokens, const int64_t* seq_tokens,
+                                   const void* q, const float* k_scale, const float* v_scale,
+                                   float* out, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  if (!cfg) return KVQ_ERR_NULL;
+  kvq::Geometry g;
+  const int32_t st = kvq::make_geometry(*cfg, &g);
+  if (st != KVQ_OK) return st;
+  const int32_t tst = check_table(cfg, g, block_table, max_blocks, num_blocks);
+  if (tst != KVQ_OK) return tst;
+  if (!seq_tokens) return KVQ_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(seq_tokens) & 7u) != 0) return KVQ_ERR_INVALID;
+  return decode_call(cfg, cache, layer, tokens, seq_tokens, 1, q, k_scale, v_scale, out,
+                     workspace, workspace_bytes, stream, block_table, max_blocks, num_blocks);
 }
 
 int32_t kvq_decode_attention_ragged(const kvq_config* cfg, const void* cache, int32_t layer,

@@ -39,6 +39,46 @@ struct Geometry {
 // Fills g from a validated config. Returns KVQ_OK or a negative status.
 int32_t make_geometry(const kvq_config& cfg, Geometry* g);
 
+// Where the pages and the residual ring of (sequence b, KV head h) of one
+// layer live. Slab layout (table == null): one contiguous slab per (sequence,
+// KV head), its pages then its ring. Paged layout: a block table maps page p
+// of sequence b to a physical block of the layer's pool (each block one page
+// per KV head) and the rings sit in their own region, one per (sequence, KV
+// head); block numbers are clamped into the pool so that every access stays
+// inside the caller's buffer.
+struct PageMap {
+  uint8_t* base;            // slab layout: the layer's first slab; paged: its first block
+  uint8_t* rings;           // paged: the layer's first ring
+  const int32_t* table;     // paged: [batch][max_blocks] block numbers, else null
+  int64_t unit_bytes;       // slab layout: bytes per slab; paged: bytes per ring
+  int64_t ring_off;         // slab layout: offset of the ring inside a slab
+  int64_t page_bytes;
+  int32_t kv_heads, max_blocks, num_blocks;
+
+  __device__ __forceinline__ uint8_t* page(int b, int h, int64_t p) const {
+    if (table) {
+      int32_t id = table[static_cast<int64_t>(b) * max_blocks + p];
+      id = id < 0 ? 0 : (id >= num_blocks ? num_blocks - 1 : id);
+      return base + (static_cast<int64_t>(id) * kv_heads + h) * page_bytes;
+    }
+    return base + (static_cast<int64_t>(b) * kv_heads + h) * unit_bytes + p * page_bytes;
+  }
+  __device__ __forceinline__ uint8_t* ring(int b, int h) const {
+    if (table) return rings + (static_cast<int64_t>(b) * kv_heads + h) * unit_bytes;
+    return base + (static_cast<int64_t>(b) * kv_heads + h) * unit_bytes + ring_off;
+  }
+};
+
+// Bytes of the ring region of a paged cache (all layers), 256-aligned.
+int64_t paged_ring_region(const Geometry& g);
+// Bytes of a paged cache with num_blocks blocks per layer, or -1 on overflow.
+int64_t paged_cache_bytes(const Geometry& g, int64_t num_blocks);
+
+// Page map of `layer` of a cache buffer: the slab layout (table null) or the
+// paged one.
+PageMap make_page_map(const Geometry& g, const uint8_t* cache, int32_t layer,
+                      const int32_t* table, int32_t max_blocks, int64_t num_blocks);
+
 // Tokens sequence b holds (its own fill level in a ragged batch): seq[b]
 // clamped to [1, T], or T without seq.
 __device__ inline int64_t seq_len(const int64_t* seq, int b, int64_t T) {
@@ -57,7 +97,8 @@ __host__ __device__ inline int64_t kivi_quantised(int64_t T, int32_t R) {
 
 struct AppendArgs {
   Geometry g;
-  uint8_t* layer_base;      // cache + layer * batch * kv_heads * slab_bytes
+  PageMap pm;               // where this layer's pages and rings are
+  uint8_t* layer_base;      // cache + layer * batch * kv_heads * slab_bytes (slab layout)
   const void* k_new;        // [B][n][Hkv][d] in_dtype
   const void* v_new;
   const float* k_scale;     // FP8 only
@@ -70,6 +111,7 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 
 struct DecodeArgs {
   Geometry g;
+  PageMap pm;               // where this layer's pages and rings are
   const uint8_t* layer_base;
   int64_t tokens;
   const int64_t* seq_tokens;  // device [B] per-sequence token counts, or null (all = tokens)
@@ -113,7 +155,9 @@ int64_t workspace_bytes_for(const Geometry& g, int64_t tokens, int32_t requested
 int32_t decode_prepare(const kvq_config* cfg, const void* cache, int32_t layer, int64_t tokens,
                        const int64_t* seq_tokens, int32_t nq, const void* q,
                        const float* k_scale, const float* v_scale, float* out, void* workspace,
-                       size_t workspace_bytes, DecodeArgs* args);
+                       size_t workspace_bytes, DecodeArgs* args,
+                       const int32_t* table = nullptr, int32_t max_blocks = 0,
+                       int64_t num_blocks = 0);
 // Offset of the split partials inside the workspace (after the counters).
 int64_t workspace_partials_offset(const Geometry& g);
 

@@ -19,11 +19,12 @@ KVQ_KIVI, KVQ_SYM_TOKEN, KVQ_FP8_E4M3, KVQ_BF16_CACHE, KVQ_FP8_E5M2 = 0, 1, 2, 3
 KVQ_F32, KVQ_BF16 = 0, 1
 KVQ_BYTES_FORMULA, KVQ_BYTES_CACHE, KVQ_BYTES_WORKSPACE = 0, 1, 2
 
-ABI_VERSION = 6   # KVQ_ABI_VERSION of include/kvq.h that this binding mirrors
+ABI_VERSION = 7   # KVQ_ABI_VERSION of include/kvq.h that this binding mirrors
 
 SYMBOLS = ("kvq_cache_bytes", "kvq_quantize_append", "kvq_quantize_append_ragged",
            "kvq_decode_attention", "kvq_decode_attention_ragged", "kvq_decode_attention_multi",
-           "kvq_decode_attention_noalloc", "kvq_status_string", "kvq_abi_version")
+           "kvq_decode_attention_noalloc", "kvq_paged_cache_bytes", "kvq_quantize_append_paged",
+           "kvq_decode_attention_paged", "kvq_status_string", "kvq_abi_version")
 KVQ_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
@@ -101,6 +102,13 @@ def lib():
         L.kvq_decode_attention_multi.restype = I32
         L.kvq_decode_attention_noalloc.argtypes = [cfgp, P, I32, I64, P, P, P, P, P]
         L.kvq_decode_attention_noalloc.restype = I32
+        L.kvq_paged_cache_bytes.argtypes = [cfgp, I64]
+        L.kvq_paged_cache_bytes.restype = I64
+        L.kvq_quantize_append_paged.argtypes = [cfgp, P, I32, P, I32, I64, P, P, I64, P, P, P, P, P]
+        L.kvq_quantize_append_paged.restype = I32
+        L.kvq_decode_attention_paged.argtypes = [cfgp, P, I32, P, I32, I64, I64, P, P, P, P, P, P,
+                                                 ctypes.c_size_t, P]
+        L.kvq_decode_attention_paged.restype = I32
         L.kvq_status_string.argtypes = [I32]
         L.kvq_status_string.restype = ctypes.c_char_p
         L.kvq_abi_version.argtypes = []
@@ -217,6 +225,41 @@ def kvq_decode_attention_ragged(cfg, cache, layer, tokens, seq_tokens, q, out, w
                                            workspace_bytes, _stream(stream))
     if check and st != KVQ_OK:
         raise KvqError(st, "kvq_decode_attention_ragged")
+    return st
+
+
+def kvq_paged_cache_bytes(cfg, num_blocks):
+    v = lib().kvq_paged_cache_bytes(ctypes.byref(cfg), num_blocks)
+    if v < 0:
+        raise KvqError(v, "kvq_paged_cache_bytes")
+    return v
+
+
+def kvq_quantize_append_paged(cfg, cache, layer, block_table, num_blocks, seq_past, seq_new,
+                              k_new, v_new, k_scale=None, v_scale=None, stream=None, check=True):
+    """block_table: device int32 [batch, max_blocks]; seq_past, seq_new: device
+    int64 [batch]; k_new, v_new [batch, new_max, kv_heads, head_dim]."""
+    st = lib().kvq_quantize_append_paged(ctypes.byref(cfg), _ptr(cache), layer, _ptr(block_table),
+                                         block_table.shape[1], num_blocks, _ptr(seq_past),
+                                         _ptr(seq_new), k_new.shape[1], _ptr(k_new), _ptr(v_new),
+                                         _ptr(k_scale), _ptr(v_scale), _stream(stream))
+    if check and st != KVQ_OK:
+        raise KvqError(st, "kvq_quantize_append_paged")
+    return st
+
+
+def kvq_decode_attention_paged(cfg, cache, layer, block_table, num_blocks, tokens, seq_tokens, q,
+                               out, workspace, workspace_bytes=None, k_scale=None, v_scale=None,
+                               stream=None, check=True):
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = lib().kvq_decode_attention_paged(ctypes.byref(cfg), _ptr(cache), layer, _ptr(block_table),
+                                          block_table.shape[1], num_blocks, tokens,
+                                          _ptr(seq_tokens), _ptr(q), _ptr(k_scale), _ptr(v_scale),
+                                          _ptr(out), _ptr(workspace), workspace_bytes,
+                                          _stream(stream))
+    if check and st != KVQ_OK:
+        raise KvqError(st, "kvq_decode_attention_paged")
     return st
 
 

@@ -286,3 +286,39 @@ class RaggedCache:
         for b in range(self.batch):
             out[b] = self.seqs[b].decode(layer, q[b:b + 1], sm_scale, rope_theta)[0]
         return out
+
+
+def paged_image(cache, table, num_blocks):
+    """(bytes, mask) of a paged cache (the KIVI page's Key points: KIVI pairs
+    with PagedAttention, which places a sequence's pages in blocks of a shared
+    pool through a block table). `cache` is an OracleCache or RaggedCache and
+    `table` an int array [batch, max_blocks]: page p of sequence b (of every
+    layer) sits in block table[b][p]. Buffer: the residual rings of every
+    (layer, sequence, KV head) in that order, padded to 256 bytes, then per
+    layer num_blocks blocks of one page per KV head. Each page and ring holds
+    exactly the bytes of its slab-layout counterpart."""
+    table = np.asarray(table)
+    seqs = cache.seqs if isinstance(cache, RaggedCache) else None
+    one = seqs[0] if seqs else cache
+    layers, batch, H = one.layers, table.shape[0], one.kv_heads
+    ps = one.page_size()
+    P = accounting.pages_per_slab(one.scheme, one.capacity, one.residual)
+    rb = accounting.ring_bytes(one.scheme, one.d, one.residual, one.itemsize)
+    assert table.shape[1] >= P
+    ring_region = -(-(layers * batch * H * rb) // 256) * 256
+    size = ring_region + layers * num_blocks * H * ps
+    buf = np.zeros(size, np.uint8)
+    mask = np.zeros(size, np.uint8)
+    for layer in range(layers):
+        for b in range(batch):
+            for h in range(H):
+                sb, sm = (seqs[b].slab_image(layer, 0, h) if seqs else cache.slab_image(layer, b, h))
+                for pg in range(P):
+                    o = ring_region + ((layer * num_blocks + int(table[b, pg])) * H + h) * ps
+                    buf[o:o + ps] = sb[pg * ps:(pg + 1) * ps]
+                    mask[o:o + ps] = sm[pg * ps:(pg + 1) * ps]
+                if rb:
+                    o = ((layer * batch + b) * H + h) * rb
+                    buf[o:o + rb] = sb[P * ps:P * ps + rb]
+                    mask[o:o + rb] = sm[P * ps:P * ps + rb]
+    return buf, mask

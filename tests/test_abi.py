@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert kvq.kvq_abi_version() == 6
+    assert kvq.kvq_abi_version() == 7
     assert kvq.status_string(0) == "ok"
     for st in (-1, -2, -3, -4, -5, -6):
         assert kvq.status_string(st) != "unknown status"
@@ -337,3 +337,33 @@ def test_sparse_outlier_sizes_and_validation(bits, v_bits, d, R, dtype):
     assert st(outliers=-1) == kvq.KVQ_ERR_INVALID
     assert st(scheme=kvq.KVQ_SYM_TOKEN, bits=4, residual=0, outliers=1) == kvq.KVQ_ERR_INVALID
     assert st(scheme=kvq.KVQ_FP8_E4M3, bits=8, residual=0, outliers=1) == kvq.KVQ_ERR_INVALID
+
+
+def test_paged_sizes_and_validation():
+    """Paged caches: size = ring region (256-aligned) + blocks, as the oracle's
+    paged image has it; the table is checked on the host (null, alignment,
+    a row too short for a full sequence, block counts) before any launch."""
+    from oracle.cache import OracleCache, paged_image
+    import numpy as np
+    L = kvq.lib()
+    c = cfg(batch=2, max_tokens=200, residual=16, head_dim=32, q_heads=8, in_dtype=kvq.KVQ_F32)
+    oc = OracleCache(kvq.KVQ_KIVI, 2, 2, 2, 8, 32, 200, residual=16, in_dtype="f32")
+    P = (200 - 16) // 32
+    for nb in (2 * P, 2 * P + 5):
+        buf, _ = paged_image(oc, np.arange(2 * P).reshape(2, P), nb)
+        assert kvq.kvq_paged_cache_bytes(c, nb) == buf.size
+    p = ctypes.byref(c)
+    f = 1 << 20
+    ap = L.kvq_quantize_append_paged
+    dp = L.kvq_decode_attention_paged
+    assert ap(p, f, 0, None, P, 10, f, f, 4, f, f, None, None, None) == kvq.KVQ_ERR_NULL
+    assert ap(p, f, 0, f + 2, P, 10, f, f, 4, f, f, None, None, None) == kvq.KVQ_ERR_INVALID
+    assert ap(p, f, 0, f, P - 1, 10, f, f, 4, f, f, None, None, None) == kvq.KVQ_ERR_CAPACITY
+    assert ap(p, f, 0, f, P, 0, f, f, 4, f, f, None, None, None) == kvq.KVQ_ERR_INVALID
+    assert ap(p, f, 0, f, P, 1 << 31, f, f, 4, f, f, None, None, None) == kvq.KVQ_ERR_UNSUPPORTED
+    assert ap(p, f, 0, f, P, 10, f, f, 0, f, f, None, None, None) == kvq.KVQ_OK    # no-op
+    assert dp(p, f, 0, None, P, 10, 8, f, f, None, None, f, f, 1 << 20, None) == kvq.KVQ_ERR_NULL
+    assert dp(p, f, 0, f, P - 1, 10, 8, f, f, None, None, f, f, 1 << 20, None) == kvq.KVQ_ERR_CAPACITY
+    assert dp(p, f, 0, f, P, 10, 8, None, f, None, None, f, f, 1 << 20, None) == kvq.KVQ_ERR_NULL
+    assert dp(p, f, 0, f, P, 10, 8, f, f, None, None, f, f, 0, None) == kvq.KVQ_ERR_WORKSPACE
+    assert L.kvq_paged_cache_bytes(p, -1) == kvq.KVQ_ERR_INVALID
