@@ -39,7 +39,7 @@ def _groups(seed, n_groups, g, scale=1.0):
     return x
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_kivi_error_bound_and_extremes(bits):
     x = _groups(bits, 4000, 32)
     x[::7] *= F32(1000.0)
@@ -61,7 +61,7 @@ def test_kivi_error_bound_and_extremes(bits):
     assert np.all(z == x.min(axis=1))
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_kivi_bruteforce_nearest_level(bits):
     """Code = the nearest of the 2^b levels k*s + z, except inside a tiny band
     around exact midpoints where float32 rounding of (x-z)/s decides."""
@@ -110,7 +110,7 @@ def test_sym_worked_examples(golden):
         assert float(s) == ex["scale"], ex["name"]
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_sym_invariants(bits):
     x = _groups(20 + bits, 3000, 32)
     x[::5] *= F32(300.0)

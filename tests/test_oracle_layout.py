@@ -30,7 +30,7 @@ def test_bf16_bits():
         [1.0, -2.0, 0.0, -0.0]
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_kivi_page_roundtrip(bits):
     rng = np.random.default_rng(bits)
     d = 64
@@ -212,3 +212,23 @@ def test_kivi_page_value_bits():
     # at d 64: 2 pages of 1024 B key codes + 512 B key scales/offsets + 512 B value
     # codes + 256 B value scales/offsets, then the ring of 40 bf16 K and V rows
     assert c42.slab_size() == 2 * (1024 + 512 + 512 + 256) + 2 * 40 * d * 2
+
+
+def test_pack_3bit_worked_example(golden):
+    """3-bit fields straddle bytes; the hand-packed bytes of the fixture."""
+    ex = golden("qb_worked_examples.json")["pack_3bit"]
+    got = layout.pack_fields(np.array(ex["codes"]), 3)
+    assert got.tolist() == ex["bytes"]
+    assert layout.unpack_fields(got, 3, 8).tolist() == ex["codes"]
+
+
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
+def test_three_bit_page_sizes(d):
+    """3-bit K rows and V cols: 12 d bytes each; a KIVI page stays a multiple
+    of 256 bytes with both widths 3, and with 3 bits next to another width
+    from d = 64 on (d = 32 then gives 128 bytes over: that combination is
+    not supported)."""
+    for kb, vb in ((3, 3), (4, 3), (8, 3), (3, 2)):
+        n = acc.page_bytes(acc.KIVI, d, kb, vb)
+        assert n == 32 * d * kb // 8 + 8 * d + 32 * d * vb // 8 + 256
+        assert (n % 256 == 0) == (kb == vb or d >= 64)
