@@ -64,6 +64,20 @@ __device__ __forceinline__ void seq_counts(const AppendParams& p, int b, int64_t
   }
 }
 
+// Places a B-bit code as field i of a run of 32 fields held in B words (3-bit
+// fields straddle words): or-ed into w, its bits recorded in m.
+template <int B>
+__device__ __forceinline__ void put_field(uint32_t (&w)[B], uint32_t (&m)[B], int i, uint32_t code) {
+  constexpr uint32_t F = (1u << B) - 1u;
+  const int bit = i * B, k = bit >> 5, sh = bit & 31;
+  w[k] |= code << sh;
+  m[k] |= F << sh;
+  if (sh + B > 32) {
+    w[k + 1] |= code >> (32 - sh);
+    m[k + 1] |= F >> (32 - sh);
+  }
+}
+
 // Widens one 16-byte chunk of a token row (bf16 or f32) into an fp32 LDS row.
 template <int IB>
 __device__ __forceinline__ void stage_chunk(const uint4& v, float* dst, int chunk) {
@@ -285,6 +299,23 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
       dst[4 * i + 3] = v.w;
     }
   };
+  if constexpr (KB == 3) {
+    // 3-bit K rows: groups of 32 fields (a token's 32 channels) in 3 words
+    for (int gi = tid; gi < kPage * D / 32; gi += kThreads) {
+      const int t = gi * 32 / D, c0 = gi * 32 % D;
+      uint32_t wd[3] = {0u, 0u, 0u}, m[3] = {0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        uint32_t code = quant_asym_rcp(elem(0, t, c0 + j), k_mn[c0 + j], k_s + c0 + j,
+                                       k_r[c0 + j], kLevelsK);
+        if (p.outliers && k_oi[c0 + j] == t) code = 0u;
+        put_field<3>(wd, m, j, code);
+      }
+      kc[3 * gi] = wd[0];
+      kc[3 * gi + 1] = wd[1];
+      kc[3 * gi + 2] = wd[2];
+    }
+  } else
   for (int w = tid; w < WORDSK; w += kThreads) {
     const int f0 = w * FPWK;
     const int t = f0 / D, c0 = f0 % D;
@@ -317,6 +348,21 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
     }
     kc[w] = word;
   }
+  if constexpr (VB == 3) {
+    // 3-bit V cols: a channel's 32 tokens in 3 words
+    for (int c = tid; c < D; c += kThreads) {
+      uint32_t wd[3] = {0u, 0u, 0u}, m[3] = {0u, 0u, 0u};
+#pragma unroll
+      for (int t = 0; t < kPage; ++t) {
+        uint32_t code = quant_asym_rcp(elem(1, t, c), v_mn[t], v_s + t, v_r[t], kLevelsV);
+        if (p.outliers && v_oi[t] == c) code = 0u;
+        put_field<3>(wd, m, t, code);
+      }
+      vc[3 * c] = wd[0];
+      vc[3 * c + 1] = wd[1];
+      vc[3 * c + 2] = wd[2];
+    }
+  } else
   for (int w = tid; w < WORDSV; w += kThreads) {
     const int f0 = w * FPWV;
     const int c = f0 / kPage, t0 = f0 % kPage;
@@ -433,6 +479,32 @@ __global__ __launch_bounds__(kThreads) void token_append_kernel(AppendParams p) 
   // K rows of the new tokens: whole words
   constexpr int ROW_WORDS = D * BITS / 32;
   uint32_t* kc = reinterpret_cast<uint32_t*>(pg + p.off_kc);
+  if constexpr (BITS == 3) {
+    // 3-bit fields straddle words: K rows in groups of 32 channels (3 words,
+    // whole words of the token's row); V cols one column (32 tokens, 3
+    // words) per thread, updating only the fields of tokens [lo, hi)
+    constexpr int GPR = D / 32;
+    for (int i = tid; i < (hi - lo) * GPR; i += kThreads) {
+      const int r = lo + i / GPR, gi = i % GPR;
+      uint32_t wd[3] = {0u, 0u, 0u}, m[3] = {0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 32; ++j) put_field<3>(wd, m, j, encode(ktile[r * LD + 32 * gi + j], k_sc[r]));
+      uint32_t* dst = kc + r * ROW_WORDS + 3 * gi;
+      dst[0] = wd[0];
+      dst[1] = wd[1];
+      dst[2] = wd[2];
+    }
+    uint32_t* vc3 = reinterpret_cast<uint32_t*>(pg + p.off_vc);
+    for (int c = tid; c < D; c += kThreads) {
+      uint32_t wd[3] = {0u, 0u, 0u}, m[3] = {0u, 0u, 0u};
+#pragma unroll
+      for (int t = 0; t < kPage; ++t)
+        if (t >= lo && t < hi) put_field<3>(wd, m, t, encode(vtile[t * LD + c], v_sc[t]));
+#pragma unroll
+      for (int k = 0; k < 3; ++k) vc3[3 * c + k] = (vc3[3 * c + k] & ~m[k]) | wd[k];
+    }
+    return;
+  }
   for (int i = tid; i < (hi - lo) * ROW_WORDS; i += kThreads) {
     const int r = lo + i / ROW_WORDS;
     const int c0 = (i % ROW_WORDS) * FPW;
@@ -682,15 +754,20 @@ hipError_t dispatch_bits(const AppendArgs& a, const AppendParams& p, hipStream_t
   if (g.scheme == KVQ_SYM_TOKEN) {
     switch (g.bits) {
       case 2: return run_token<KVQ_SYM_TOKEN, D, 2, IB>(a, p, st);
+      case 3: return run_token<KVQ_SYM_TOKEN, D, 3, IB>(a, p, st);
       case 4: return run_token<KVQ_SYM_TOKEN, D, 4, IB>(a, p, st);
       default: return run_token<KVQ_SYM_TOKEN, D, 8, IB>(a, p, st);
     }
   }
   switch (g.bits) {
     case 2: return run_kivi<D, 2, 2, IB>(a, p, st);
-    case 4: return g.vbits == 2 ? run_kivi<D, 4, 2, IB>(a, p, st) : run_kivi<D, 4, 4, IB>(a, p, st);
+    case 3: return g.vbits == 2 ? run_kivi<D, 3, 2, IB>(a, p, st) : run_kivi<D, 3, 3, IB>(a, p, st);
+    case 4:
+      return g.vbits == 2 ? run_kivi<D, 4, 2, IB>(a, p, st)
+             : g.vbits == 3 ? run_kivi<D, 4, 3, IB>(a, p, st) : run_kivi<D, 4, 4, IB>(a, p, st);
     default:
-      return g.vbits == 2 ? run_kivi<D, 8, 2, IB>(a, p, st)
+      return g.vbits == 2   ? run_kivi<D, 8, 2, IB>(a, p, st)
+             : g.vbits == 3 ? run_kivi<D, 8, 3, IB>(a, p, st)
              : g.vbits == 4 ? run_kivi<D, 8, 4, IB>(a, p, st) : run_kivi<D, 8, 8, IB>(a, p, st);
   }
 }

@@ -1577,6 +1577,7 @@ hipError_t by_d_rope(const MfmaParams& p, int d, int hg, int batch, hipStream_t 
 bool mfma_path(const Geometry& g) {
   if (g.scheme != KVQ_KIVI || g.d < 64 || g.in_bytes != 2) return false;
   if (g.outliers) return false;   // dense-and-sparse pages: the generic kernel
+  if (g.vbits != 2 && g.vbits != 4) return false;          // 3-bit values: the generic kernel
   if (g.rope == 0.0) return g.bits == 2 || g.bits == 4;   // value bits: 2 or 4, <= key bits
   return g.bits == 2 && g.d <= 128;   // rotary keys: 2-bit pages, head_dim 64 or 128
 }

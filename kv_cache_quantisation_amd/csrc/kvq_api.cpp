@@ -30,12 +30,15 @@ int32_t validate_config(const kvq_config* cfg) {
     if (c.bits != 8) return KVQ_ERR_INVALID;
   } else if (c.scheme == KVQ_BF16_CACHE) {
     if (c.bits != 16) return KVQ_ERR_INVALID;
-  } else if (c.bits != 2 && c.bits != 4 && c.bits != 8) {
+  } else if (c.bits != 2 && c.bits != 3 && c.bits != 4 && c.bits != 8) {
     return (c.bits >= 1 && c.bits <= 8) ? KVQ_ERR_UNSUPPORTED : KVQ_ERR_INVALID;
   }
   if (c.v_bits != 0 && c.v_bits != c.bits) {
     if (c.scheme != KVQ_KIVI || c.v_bits < 1 || c.v_bits > 8) return KVQ_ERR_INVALID;
-    if ((c.v_bits != 2 && c.v_bits != 4) || c.v_bits > c.bits) return KVQ_ERR_UNSUPPORTED;
+    if ((c.v_bits != 2 && c.v_bits != 3 && c.v_bits != 4) || c.v_bits > c.bits)
+      return KVQ_ERR_UNSUPPORTED;
+    // 3 bits next to another width: pages stay 256-byte multiples from d = 64
+    if ((c.bits == 3 || c.v_bits == 3) && c.head_dim < 64) return KVQ_ERR_UNSUPPORTED;
   }
   if (c.outliers != 0 && (c.outliers != 1 || c.scheme != KVQ_KIVI)) return KVQ_ERR_INVALID;
   if (c.layers < 1 || c.q_heads < 1 || c.kv_heads < 1 || c.batch < 1 || c.max_tokens < 0)

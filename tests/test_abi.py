@@ -78,7 +78,9 @@ def test_formula_matches_oracle(bits):
     (kvq.KVQ_KIVI, 8, 256, 37, kvq.KVQ_BF16), (kvq.KVQ_KIVI, 2, 32, 5, kvq.KVQ_F32),
     (kvq.KVQ_SYM_TOKEN, 4, 32, 0, kvq.KVQ_F32), (kvq.KVQ_SYM_TOKEN, 2, 128, 0, kvq.KVQ_BF16),
     (kvq.KVQ_FP8_E4M3, 8, 128, 0, kvq.KVQ_BF16), (kvq.KVQ_BF16_CACHE, 16, 128, 0, kvq.KVQ_BF16),
-    (kvq.KVQ_BF16_CACHE, 16, 32, 0, kvq.KVQ_F32), (kvq.KVQ_FP8_E5M2, 8, 64, 0, kvq.KVQ_BF16)])
+    (kvq.KVQ_BF16_CACHE, 16, 32, 0, kvq.KVQ_F32), (kvq.KVQ_FP8_E5M2, 8, 64, 0, kvq.KVQ_BF16),
+    (kvq.KVQ_KIVI, 3, 128, 128, kvq.KVQ_BF16), (kvq.KVQ_KIVI, 3, 32, 7, kvq.KVQ_F32),
+    (kvq.KVQ_SYM_TOKEN, 3, 32, 0, kvq.KVQ_F32), (kvq.KVQ_SYM_TOKEN, 3, 256, 0, kvq.KVQ_BF16)])
 def test_cache_bytes_match_oracle_layout(scheme, bits, d, R, dtype):
     c = cfg(scheme=scheme, bits=bits, head_dim=d, residual=R, in_dtype=dtype, q_heads=8)
     item = 2 if dtype == kvq.KVQ_BF16 else 4
@@ -89,7 +91,8 @@ def test_cache_bytes_match_oracle_layout(scheme, bits, d, R, dtype):
 
 @pytest.mark.parametrize("bits,v_bits,d,R,dtype", [
     (4, 2, 128, 128, kvq.KVQ_BF16), (8, 4, 64, 0, kvq.KVQ_F32), (8, 2, 256, 37, kvq.KVQ_BF16),
-    (4, 2, 32, 5, kvq.KVQ_F32), (4, 4, 128, 16, kvq.KVQ_BF16)])
+    (4, 2, 32, 5, kvq.KVQ_F32), (4, 4, 128, 16, kvq.KVQ_BF16), (4, 3, 128, 16, kvq.KVQ_BF16),
+    (8, 3, 64, 0, kvq.KVQ_F32), (3, 2, 256, 37, kvq.KVQ_BF16)])
 def test_kivi_value_bits_sizes(bits, v_bits, d, R, dtype):
     """KIVI with value codes narrower than key codes: exact layout size and
     the KV-bytes equation with each half at its own width, as the oracle has
@@ -115,7 +118,11 @@ def test_value_bits_validation():
     assert st(bits=4, v_bits=2) > 0 and st(bits=8, v_bits=4) > 0 and st(bits=8, v_bits=2) > 0
     assert st(bits=2, v_bits=4) == kvq.KVQ_ERR_UNSUPPORTED     # values wider than keys
     assert st(bits=4, v_bits=8) == kvq.KVQ_ERR_UNSUPPORTED
-    assert st(bits=8, v_bits=3) == kvq.KVQ_ERR_UNSUPPORTED     # 3-bit codes not built
+    assert st(bits=8, v_bits=3) > 0 and st(bits=3, v_bits=2) > 0 and st(bits=3) > 0
+    assert st(bits=4, v_bits=3, head_dim=32) == kvq.KVQ_ERR_UNSUPPORTED   # page off 256 bytes
+    assert st(bits=3, head_dim=32) > 0
+    assert st(scheme=kvq.KVQ_SYM_TOKEN, bits=3, residual=0) > 0
+    assert st(bits=3, v_bits=4) == kvq.KVQ_ERR_UNSUPPORTED     # values wider than keys
     assert st(bits=4, v_bits=9) == kvq.KVQ_ERR_INVALID
     assert st(bits=4, v_bits=-2) == kvq.KVQ_ERR_INVALID
     assert st(scheme=kvq.KVQ_SYM_TOKEN, bits=4, v_bits=2, residual=0) == kvq.KVQ_ERR_INVALID
@@ -141,7 +148,7 @@ def test_workspace_monotone():
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("scheme", 7, kvq.KVQ_ERR_INVALID), ("bits", 3, kvq.KVQ_ERR_UNSUPPORTED),
+    ("scheme", 7, kvq.KVQ_ERR_INVALID), ("bits", 5, kvq.KVQ_ERR_UNSUPPORTED),
     ("bits", 0, kvq.KVQ_ERR_INVALID), ("bits", 16, kvq.KVQ_ERR_INVALID),
     ("layers", 0, kvq.KVQ_ERR_INVALID), ("q_heads", 12, kvq.KVQ_ERR_INVALID),
     ("q_heads", 8 * 16, kvq.KVQ_ERR_UNSUPPORTED), ("q_heads", 8 * 3, kvq.KVQ_ERR_UNSUPPORTED),
