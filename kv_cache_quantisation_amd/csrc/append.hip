@@ -30,7 +30,6 @@ namespace {
 constexpr int kThreads = 256;
 
 struct AppendParams {
-  PageMap pm;                                 // pages and rings of the layer (slab or paged)
   uint8_t* layer_base;
   const uint8_t* k_new;
   const uint8_t* v_new;
@@ -48,6 +47,7 @@ struct AppendParams {
   int32_t off_kc, off_ks, off_kz, off_vc, off_vs, off_vz;
   int32_t outliers;                           // KIVI dense-and-sparse pages (0 or 1)
   int32_t off_ko, off_vo, off_ki, off_vi;     // their side matrix
+  PageMap pm;                                 // pages and rings of the layer (slab or paged)
 };
 
 // Tokens sequence b held before the call and tokens it appends: the uniform
@@ -100,7 +100,9 @@ __device__ __forceinline__ void stage_chunk(const uint4& v, float* dst, int chun
 // part in the statistics (several threads per key channel / value token,
 // combined with lane shuffles) and in the codes (one or more packed words per
 // thread), where each quotient comes from a reciprocal with an exact fallback.
-template <int D, int KB, int VB, int IB>
+// OUT: dense-and-sparse pages (a template parameter, so that dense pages
+// compile exactly as without the feature)
+template <int D, int KB, int VB, int IB, bool OUT>
 __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
   constexpr float kLevelsK = float((1 << KB) - 1);   // key / value code levels
   constexpr float kLevelsV = float((1 << VB) - 1);
@@ -188,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
   for (int c0 = 0; c0 < D; c0 += kThreads / TPC) {
     const int c = c0 + tid / TPC, part = tid % TPC;
     int oi = -1;   // token of this channel's outlier
-    if (p.outliers) {
+    if constexpr (OUT) {
       float best = -1.0f;
       int bi = 0;
 #pragma unroll
@@ -224,10 +226,10 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
       k_mn[c] = mn;
       k_s[c] = s;
       k_r[c] = quant_rcp_prep(s);
-      k_oi[c] = oi;
+      if constexpr (OUT) k_oi[c] = oi;
       reinterpret_cast<float*>(pg + p.off_ks)[c] = s;
       reinterpret_cast<float*>(pg + p.off_kz)[c] = mn;
-      if (p.outliers) {
+      if constexpr (OUT) {
         reinterpret_cast<float*>(pg + p.off_ko)[c] = elem(0, oi, c);   // exact input value
         pg[p.off_ki + c] = static_cast<uint8_t>(oi);
       }
@@ -237,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
   {
     const int r = tid / TPT, part = tid % TPT;
     int oi = -1;   // channel of this token's outlier
-    if (p.outliers) {
+    if constexpr (OUT) {
       float best = -1.0f;
       int bi = 0;
 #pragma unroll
@@ -271,10 +273,10 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
       v_mn[r] = mn;
       v_s[r] = s;
       v_r[r] = quant_rcp_prep(s);
-      v_oi[r] = oi;
+      if constexpr (OUT) v_oi[r] = oi;
       reinterpret_cast<float*>(pg + p.off_vs)[r] = s;
       reinterpret_cast<float*>(pg + p.off_vz)[r] = mn;
-      if (p.outliers) {
+      if constexpr (OUT) {
         reinterpret_cast<float*>(pg + p.off_vo)[r] = elem(1, r, oi);   // exact input value
         pg[p.off_vi + r] = static_cast<uint8_t>(oi);
       }
@@ -308,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
       for (int j = 0; j < 32; ++j) {
         uint32_t code = quant_asym_rcp(elem(0, t, c0 + j), k_mn[c0 + j], k_s + c0 + j,
                                        k_r[c0 + j], kLevelsK);
-        if (p.outliers && k_oi[c0 + j] == t) code = 0u;
+        if (OUT && k_oi[c0 + j] == t) code = 0u;
         put_field<3>(wd, m, j, code);
       }
       kc[3 * gi] = wd[0];
@@ -341,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
 #pragma unroll
     for (int j = 0; j < FPWK; ++j)
       word |= quant_asym_rcp(x[j], mn[j], k_s + c0 + j, rc[j], kLevelsK) << (j * KB);
-    if (p.outliers) {   // the moved values' fields hold code 0
+    if constexpr (OUT) {   // the moved values' fields hold code 0
 #pragma unroll
       for (int j = 0; j < FPWK; ++j)
         if (k_oi[c0 + j] == t) word &= ~(((1u << KB) - 1u) << (j * KB));
@@ -355,7 +357,7 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
 #pragma unroll
       for (int t = 0; t < kPage; ++t) {
         uint32_t code = quant_asym_rcp(elem(1, t, c), v_mn[t], v_s + t, v_r[t], kLevelsV);
-        if (p.outliers && v_oi[t] == c) code = 0u;
+        if (OUT && v_oi[t] == c) code = 0u;
         put_field<3>(wd, m, t, code);
       }
       vc[3 * c] = wd[0];
@@ -373,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void kivi_flush_kernel(AppendParams p) {
 #pragma unroll
     for (int j = 0; j < FPWV; ++j)
       word |= quant_asym_rcp(elem(1, t0 + j, c), mn[j], v_s + t0 + j, rc[j], kLevelsV) << (j * VB);
-    if (p.outliers) {
+    if constexpr (OUT) {
 #pragma unroll
       for (int j = 0; j < FPWV; ++j)
         if (v_oi[t0 + j] == c) word &= ~(((1u << VB) - 1u) << (j * VB));
@@ -718,7 +720,10 @@ hipError_t run_kivi(const AppendArgs& a, const AppendParams& p, hipStream_t st) 
   }
   if (flush_pages > 0) {
     dim3 grid(static_cast<unsigned>(flush_pages), g.kv_heads, g.batch);
-    hipLaunchKernelGGL((kivi_flush_kernel<D, KB, VB, IB>), grid, dim3(kThreads), 0, st, p);
+    if (g.outliers)
+      hipLaunchKernelGGL((kivi_flush_kernel<D, KB, VB, IB, true>), grid, dim3(kThreads), 0, st, p);
+    else
+      hipLaunchKernelGGL((kivi_flush_kernel<D, KB, VB, IB, false>), grid, dim3(kThreads), 0, st, p);
   }
   if (ring_tokens > 0) {
     dim3 grid(static_cast<unsigned>(ring_tokens), g.kv_heads, g.batch);

@@ -52,7 +52,6 @@ constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct Fp8Params {
-  PageMap pm;                     // pages of the layer (slab or paged)
   const uint8_t* layer_base;
   const uint8_t* q;
   const float* k_scale;           // [kv_heads] of this layer
@@ -69,6 +68,7 @@ struct Fp8Params {
   int32_t kv_heads, q_heads;
   int32_t q_bf16;
   float qscale;                   // sm_scale * log2(e)
+  PageMap pm;                     // pages of the layer (slab or paged)
 };
 
 template <bool BF16, int D>
@@ -189,8 +189,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
 #pragma unroll
     for (int i = 0; i < D / 4; ++i) amax = fmaxf(amax, fabsf(qs[hh][g * CPG + i]));
     if (__builtin_amdgcn_ballot_w64(amax > 65504.f) != 0) {
-#pragma unroll
-      for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+      amax = wave_max(amax);
       int ex;
       frexpf(amax, &ex);   // amax < 2^ex
       esc = __builtin_amdgcn_readfirstlane(ex - 15);

@@ -47,7 +47,6 @@ constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct DecodeParams {
-  PageMap pm;           // pages and rings of the layer (slab or paged)
   const uint8_t* layer_base;
   const uint8_t* q;
   const float* k_scale;
@@ -68,6 +67,7 @@ struct DecodeParams {
   double rope_theta;    // 0 = off
   int32_t outliers;     // KIVI dense-and-sparse pages: side matrix offsets below
   int32_t off_ko, off_vo, off_ki, off_vi;
+  PageMap pm;           // pages and rings of the layer (slab or paged)
 };
 
 template <int BITS>

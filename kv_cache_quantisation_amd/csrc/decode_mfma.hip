@@ -67,7 +67,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMaxSlack = 8.0f;  // log2 units a score may exceed the running max by
 
 struct MfmaParams {
-  PageMap pm;                     // pages and rings of the layer (slab or paged)
   const uint8_t* layer_base;
   const uint8_t* q;
   float* out;
@@ -84,6 +83,7 @@ struct MfmaParams {
   int32_t q_bf16;
   float qscale;
   double rope_theta;              // > 0: keys cached before the rotary embedding
+  PageMap pm;                     // pages and rings of the layer (slab or paged)
 };
 
 // KIVI page of KB-bit key codes and VB-bit value codes
@@ -563,61 +563,59 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
     } else {
     // q' = q * s per channel, split hi/lo into B fragments; bias q . z
     float bias_part[REPS];
-    float qp[REPS][8];
-    float amax = 0.f;
-#pragma unroll
-    for (int r = 0; r < REPS; ++r) {
+    float amax = 0.f;   // largest |q'| of the lane (f16 range check below)
+    // (scaled by 2^-esc: 0 except on the rare pages described below)
+    auto fold = [&](int r, int esc_, bool with_bias) {
       const int cidx = lane + 64 * r;
-      const int fg = (cidx / KS) % 4, fk = cidx % KS;
+      const int fh = cidx / PER_HEAD, fg = (cidx / KS) % 4, fk = cidx % KS;
       const int c0 = fg * CPG + 8 * fk;
       const float4 s0 = *reinterpret_cast<const float4*>(pg + PG::OFF_KS + 4 * c0);
       const float4 s1 = *reinterpret_cast<const float4*>(pg + PG::OFF_KS + 4 * c0 + 16);
-      const float4 z0 = *reinterpret_cast<const float4*>(pg + PG::OFF_KZ + 4 * c0);
-      const float4 z1 = *reinterpret_cast<const float4*>(pg + PG::OFF_KZ + 4 * c0 + 16);
       const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-      const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
-      float bp = 0.f;
+      float qp[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        qp[r][i] = qreg[r][i] * sv[i];
-        bp = fmaf(qreg[r][i], zv[i], bp);
-        amax = fmaxf(amax, fabsf(qp[r][i]));
+        qp[i] = qreg[r][i] * sv[i];
+        amax = fmaxf(amax, fabsf(qp[i]));
+        if (esc_) qp[i] = ldexpf(qp[i], -esc_);
       }
-      bias_part[r] = bp;
-    }
-    // f16 range of the key operand: beyond 65504 the f16 high part would
-    // saturate. A page whose q' exceeds it (a key channel with an enormous
-    // range) takes q' 2^-e into the product and multiplies the product part
-    // of its scores by 2^e: exact scaling by a power of two (wave-uniform).
-    const bool big = __builtin_amdgcn_ballot_w64(amax > 65504.f) != 0;
-    int esc = 0;
-    if (big) {
-      float wm = amax;
+      if (with_bias) {
+        const float4 z0 = *reinterpret_cast<const float4*>(pg + PG::OFF_KZ + 4 * c0);
+        const float4 z1 = *reinterpret_cast<const float4*>(pg + PG::OFF_KZ + 4 * c0 + 16);
+        const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+        float bp = 0.f;
 #pragma unroll
-      for (int m = 1; m < 64; m <<= 1) wm = fmaxf(wm, __shfl_xor(wm, m, 64));
-      int ex;
-      frexpf(wm, &ex);   // wm < 2^ex
-      esc = __builtin_amdgcn_readfirstlane(ex - 15);
-#pragma unroll
-      for (int r = 0; r < REPS; ++r)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qp[r][i] = ldexpf(qp[r][i], -esc);
-    }
-#pragma unroll
-    for (int r = 0; r < REPS; ++r) {
-      const int cidx = lane + 64 * r;
-      const int fh = cidx / PER_HEAD, fg = (cidx / KS) % 4, fk = cidx % KS;
+        for (int i = 0; i < 8; ++i) bp = fmaf(qreg[r][i], zv[i], bp);
+        bias_part[r] = bp;
+      }
       uint32_t hi[4], lo[4];   // fragment order {0,2,1,3,4,6,5,7}
-      split_f16(qp[r][0], qp[r][2], hi[0], lo[0]);
-      split_f16(qp[r][1], qp[r][3], hi[1], lo[1]);
-      split_f16(qp[r][4], qp[r][6], hi[2], lo[2]);
-      split_f16(qp[r][5], qp[r][7], hi[3], lo[3]);
+      split_f16(qp[0], qp[2], hi[0], lo[0]);
+      split_f16(qp[1], qp[3], hi[1], lo[1]);
+      split_f16(qp[4], qp[6], hi[2], lo[2]);
+      split_f16(qp[5], qp[7], hi[3], lo[3]);
       if (cidx < COMBOS) {
         *reinterpret_cast<uint4*>(frag[fh * FSTRIDE + ((4 * fk + fg) ^ (fh & 7))]) =
             uint4{hi[0], hi[1], hi[2], hi[3]};
         *reinterpret_cast<uint4*>(frag[(HG + fh) * FSTRIDE + ((4 * fk + fg) ^ ((HG + fh) & 7))]) =
             uint4{lo[0], lo[1], lo[2], lo[3]};
       }
+    };
+#pragma unroll
+    for (int r = 0; r < REPS; ++r) fold(r, 0, true);
+    // f16 range of the key operand: beyond 65504 the f16 high part saturates.
+    // A page whose q' exceeds it (a key channel with an enormous range) folds
+    // again with q' 2^-e (e from the wave's largest |q'|), overwriting the
+    // fragments, and multiplies the product part of its scores by 2^e:
+    // exact scaling by a power of two (wave-uniform, rare).
+    const bool big = __builtin_amdgcn_ballot_w64(amax > 65504.f) != 0;
+    int esc = 0;
+    if (big) {
+      const float wm = wave_max(amax);
+      int ex;
+      frexpf(wm, &ex);   // wm < 2^ex
+      esc = __builtin_amdgcn_readfirstlane(ex - 15);
+#pragma unroll
+      for (int r = 0; r < REPS; ++r) fold(r, esc, false);
     }
     // bias of head j for this lane: the fold units of head hh are lanes
     // [PER_HEAD*hh, PER_HEAD*(hh+1)) counted across reps of 64

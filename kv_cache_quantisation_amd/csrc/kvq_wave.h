@@ -107,6 +107,17 @@ __device__ __forceinline__ float xor16(float v) {
                                                                (0x10 << 10) | 0x1F));
 }
 
+// Maximum over the wave (all lanes receive it), by DPP moves and lane swaps
+// (no LDS permutes).
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
+  v = fmaxf(v, xor16(v));
+  return fmaxf(v, xor32(v));
+}
+
 template <int SHIFT>
 __device__ __forceinline__ float row_shl(float v) {  // lane l gets lane l+SHIFT of its row
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
