@@ -4,7 +4,9 @@ A step is one decode step of a 32-layer model of Llama-3-8B layer shape
 (32 query / 8 KV heads, head_dim 128) at batch 16 over a KIVI 2-bit cache with
 a 128-token bf16 residual window: for every layer, quantize-append of the new
 token of each sequence (flushing a 32-token group whenever the window fills),
-then decode attention of one query per sequence over all cached tokens. The
+then decode attention of one query per sequence over all cached tokens -- one
+kvq_append_decode call per layer, a single launch on the steps whose token
+lands in the residual window. The
 32 layers have distinct caches (about 2 GB, far beyond the 256 MB Infinity
 Cache), so every decode reads its cache from HBM. The context starts at 4096
 tokens (the workload's size) and grows by one token per step.
@@ -302,12 +304,13 @@ def gpu_bench(args, w):
             for kl, vl in news]
 
     def step(i):
+        # every layer: append the step's token, then decode over all tokens
+        # (kvq_append_decode: one launch when the token lands in the ring, the
+        # append's kernels first on the steps that encode a page)
         T = T0 + i
         for layer in range(L):
-            kvq.kvq_quantize_append(cfg, cache, layer, T, 1, news[layer][0][i], news[layer][1][i],
-                                    stream=stream)
-            kvq.kvq_decode_attention(cfg, cache, layer, T + 1, qs[layer], outs[layer], ws,
-                                     stream=stream)
+            kvq.kvq_append_decode(cfg, cache, layer, T, news[layer][0][i], news[layer][1][i],
+                                  qs[layer], outs[layer], ws, stream=stream)
 
     for i in range(W):
         step(i)
@@ -459,9 +462,8 @@ def graph_replay(cfg, cache, ws, qs, outs, news, L, T, n_rep):
 
     def step():
         for layer in range(L):
-            kvq.kvq_quantize_append(cfg, cache, layer, T - 1, 1, news[layer][0][0],
-                                    news[layer][1][0])
-            kvq.kvq_decode_attention(cfg, cache, layer, T, qs[layer], outs[layer], ws)
+            kvq.kvq_append_decode(cfg, cache, layer, T - 1, news[layer][0][0], news[layer][1][0],
+                                  qs[layer], outs[layer], ws)
 
     res, ok = {}, True
     for name, fn in (("decode_burst", burst), ("step", step)):

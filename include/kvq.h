@@ -63,9 +63,10 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 7   /* 3: ragged-batch entry points; 4: several queries per sequence;
+#define KVQ_ABI_VERSION 8   /* 3: ragged-batch entry points; 4: several queries per sequence;
                                5: decode without a caller workspace; 6: sparse outliers;
-                               7: paged caches (block tables) */
+                               7: paged caches (block tables);
+                               8: one-token append fused with decode */
 
 /* Exported entry points (the library is built with hidden visibility). */
 #if defined(__GNUC__)
@@ -318,6 +319,26 @@ KVQ_API int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache,
                              const float* k_scale, const float* v_scale,
                              float* out, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* One decode step of every sequence: kvq_quantize_append(cfg, cache, layer,
+ * past_tokens, 1, k_new, v_new, ...) followed by kvq_decode_attention over
+ * past_tokens + 1 tokens -- the same cache bytes and the same output, bit for
+ * bit. Generation appends the token whose query attends next ([QKV] going
+ * deeper; [KIVI] How It Works: each new token enters the full-precision
+ * window). When the new token lands in the residual window of a KIVI cache
+ * that decodes on the matrix-core kernel (no page to encode on this step),
+ * both happen in one launch: the decode reads the new rows from k_new/v_new
+ * and stores them into their ring slot. Otherwise (a page flush, other
+ * schemes) the append's kernels run first.
+ *   past_tokens  tokens held before the call; past_tokens < max_tokens
+ *   k_new, v_new device [batch][1][kv_heads][head_dim], in_dtype
+ *   q, out, workspace, k_scale, v_scale: as kvq_decode_attention over
+ *                past_tokens + 1 tokens
+ * Errors: those of both calls, checked before anything is launched. */
+KVQ_API int32_t kvq_append_decode(const kvq_config* cfg, void* cache, int32_t layer,
+                          int64_t past_tokens, const void* k_new, const void* v_new,
+                          const float* k_scale, const float* v_scale, const void* q,
+                          float* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Decode attention over a ragged batch: sequence b holds seq_tokens[b]
  * tokens (its own fill level, as appended by kvq_quantize_append_ragged; for

@@ -11,6 +11,6 @@ from .kvq import (  # noqa: F401
     alloc_workspace, kvq_abi_version, kvq_cache_bytes, kvq_config, kvq_decode_attention,
     kvq_decode_attention_multi, kvq_decode_attention_noalloc, kvq_decode_attention_ragged,
     kvq_quantize_append_ragged, KVQ_NOALLOC_SCRATCH_BYTES, kvq_paged_cache_bytes,
-    kvq_quantize_append_paged, kvq_decode_attention_paged,
+    kvq_quantize_append_paged, kvq_decode_attention_paged, kvq_append_decode,
     kvq_quantize_append, lib, make_config, status_string,
 )

@@ -265,14 +265,19 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
       const float alpha = fast_exp2(m_lane - m_new);
       l_lane *= alpha;
       m_lane = m_new;
-      float a_h[HG];
-#pragma unroll
-      for (int hh = 0; hh < HG; ++hh)
-        a_h[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), hh));
+      auto alpha_of = [&](int hh) {   // head hh's factor, read from lane hh
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), hh));
+      };
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float a = a_h[r % HG];
-        if constexpr (HG == 8) a = (g & 1) ? a_h[4 + r] : a_h[r];
+        float a = alpha_of(r % HG);
+        // HG = 8: rows 4g + r are head r (g even) or head 4 + r (g odd); a
+        // choice between two values (an index into an array of the factors
+        // would be compiled into a stack load)
+        if constexpr (HG == 8) {
+          const float a_odd = alpha_of(4 + r);
+          a = (g & 1) ? a_odd : a;
+        }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= a;
       }

@@ -83,6 +83,13 @@ struct MfmaParams {
   int32_t q_bf16;
   float qscale;
   double rope_theta;              // > 0: keys cached before the rotary embedding
+  // one-token append fused into the decode (kivi_mfma_kernel): the token at
+  // position new_tok (>= 0; -1: none) is read from k_new / v_new
+  // [batch][kv_heads][D] for its residual step, and the wave that takes that
+  // step stores it into its ring slot
+  const uint8_t* k_new;
+  const uint8_t* v_new;
+  int64_t new_tok;
   PageMap pm;                     // pages and rings of the layer (slab or paged)
 };
 
@@ -442,14 +449,19 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
       l_lane *= alpha;
       z_lane *= alpha;
       m_lane = m_new;
-      float a_h[HG];
-#pragma unroll
-      for (int hh = 0; hh < HG; ++hh)
-        a_h[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), hh));
+      auto alpha_of = [&](int hh) {   // head hh's factor, read from lane hh
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), hh));
+      };
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float a = a_h[r % HG];
-        if constexpr (HG == 8) a = (g & 1) ? a_h[4 + r] : a_h[r];
+        float a = alpha_of(r % HG);
+        // HG = 8: rows 4g + r are head r (g even) or head 4 + r (g odd); a
+        // choice between two values (an index into an array of the factors
+        // would be compiled into a stack load)
+        if constexpr (HG == 8) {
+          const float a_odd = alpha_of(4 + r);
+          a = (g & 1) ? a_odd : a;
+        }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= a;
       }
@@ -772,12 +784,23 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   constexpr int LPR = 2 * D / 16;           // lanes per bf16 row
   constexpr int RPI = 64 / LPR;             // rows per 16-byte-per-lane copy
   constexpr int RSTEP = 8;                  // tokens per residual step
+  bool owns_new = false;   // this wave's step holds the token appended by this call
+  // the appended token's K and V rows as byte offsets from the ring (plain
+  // integers: a per-lane choice between two pointers read from the
+  // parameters would be compiled into an indexed stack load)
+  const int64_t new_row = (static_cast<int64_t>(b) * p.kv_heads + h) * (2 * D);
+  const int64_t new_off[2] = {
+      static_cast<int64_t>(reinterpret_cast<uintptr_t>(p.k_new) - reinterpret_cast<uintptr_t>(ringp)) + new_row,
+      static_cast<int64_t>(reinterpret_cast<uintptr_t>(p.v_new) - reinterpret_cast<uintptr_t>(ringp)) + new_row};
   auto issue_step = [&](int hs) -> int {    // returns the copies issued
     const int64_t t0 = q_tokens + static_cast<int64_t>(hs) * RSTEP;
     const int nv = static_cast<int>(Tb - t0 < RSTEP ? Tb - t0 : RSTEP);
     const int row_in = lane / LPR, col_b = (lane % LPR) * 16;
     const int slots = static_cast<int>(p.ring_slots);
     const int slot0 = static_cast<int>(t0 % p.ring_slots);
+    // the appended token's row comes from the input (its ring slot is written below)
+    const int64_t rnew = p.new_tok - t0;
+    if (rnew >= 0 && rnew < RSTEP) owns_new = true;
     int issued = 0;
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {
@@ -786,7 +809,8 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
         if (i * RPI >= nv) continue;          // wave-uniform: no row of this copy exists
         const int r = i * RPI + row_in;
         const int slot = slot0 + r < slots ? slot0 + r : slot0 + r - slots;
-        const uint8_t* src = ringp + (kv * p.ring_slots + slot) * (2 * D) + col_b;
+        const int64_t off = r == rnew ? new_off[kv] : (kv * p.ring_slots + slot) * (2 * D);
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(ringp) + off + col_b);
         if (r < nv && r < RSTEP) dma16(src, lds_addr(wring + kv * RSTEP * 2 * D + i * 1024));
         ++issued;
       }
@@ -1006,6 +1030,16 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
     process_step(hs);
   }
   wait_lds();
+  // the appended token's K and V rows into its ring slot (one wave per
+  // (sequence, KV head) takes its step); the merge's wait or the kernel's end
+  // completes the stores
+  if (owns_new && lane < 2 * (2 * D / 16)) {
+    const int kv = lane / (2 * D / 16), c16 = lane % (2 * D / 16);
+    const int64_t slot = p.new_tok % p.ring_slots;
+    const uint8_t* src = (kv ? p.v_new : p.k_new) + (static_cast<int64_t>(b) * p.kv_heads + h) * (2 * D) + 16 * c16;
+    uint8_t* dst = const_cast<uint8_t*>(ringp) + (kv * p.ring_slots + slot) * (2 * D) + 16 * c16;
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+  }
 
   __builtin_amdgcn_s_setprio(3);   // the epilogue and merge end the block's critical path
   // ---- wave epilogue -----------------------------------------------------------
@@ -1613,6 +1647,10 @@ MfmaPlan mfma_plan(const Geometry& g, int64_t tokens, int32_t requested) {
   return pl;
 }
 
+bool mfma_fused_append_ok(const Geometry& g) {
+  return mfma_path(g) && !(g.rope != 0.0 && g.hg == 4);   // not rope4_kernel
+}
+
 bool mfma_multi_ok(const Geometry& g, int64_t tokens, int32_t nq) {
   return mfma_path(g) && nq >= 1 && nq <= tokens;
 }
@@ -1650,6 +1688,12 @@ hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t st) {
   p.q_bf16 = a.q_dtype == KVQ_BF16;
   p.qscale = a.sm_scale * kLog2e;
   p.rope_theta = a.rope_theta;
+  p.new_tok = -1;
+  if (a.k_new) {   // fused one-token append (uniform batch, one query)
+    p.k_new = static_cast<const uint8_t*>(a.k_new);
+    p.v_new = static_cast<const uint8_t*>(a.v_new);
+    p.new_tok = a.tokens - 1;
+  }
   const int grid_rows = g.batch * nq;
   if (a.rope_theta > 0.0) return by_d_rope(p, g.d, g.hg, grid_rows, st);
   if (g.bits == 2) return by_d<2, 2>(p, g.d, g.hg, grid_rows, st);

@@ -486,6 +486,39 @@ int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache, int32_t l
                      workspace_bytes, stream);
 }
 
+int32_t kvq_append_decode(const kvq_config* cfg, void* cache, int32_t layer, int64_t past_tokens,
+                          const void* k_new, const void* v_new, const float* k_scale,
+                          const float* v_scale, const void* q, float* out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!cfg) return KVQ_ERR_NULL;
+  if (past_tokens < 0) return KVQ_ERR_INVALID;
+  if (past_tokens >= cfg->max_tokens) return KVQ_ERR_CAPACITY;
+  // the decode's validation (over past_tokens + 1 tokens), then the append's
+  kvq::DecodeArgs a;
+  const int32_t st = kvq::decode_prepare(cfg, cache, layer, past_tokens + 1, nullptr, 1, q, k_scale,
+                                         v_scale, out, workspace, workspace_bytes, &a);
+  if (st != KVQ_OK) return st;
+  if (!k_new || !v_new) return KVQ_ERR_NULL;
+  if (!kvq::aligned16(k_new) || !kvq::aligned16(v_new)) return KVQ_ERR_INVALID;
+  const kvq::Geometry& g = a.g;
+  const int64_t q_old = kvq::kivi_quantised(past_tokens, g.residual);
+  const int64_t q_new = kvq::kivi_quantised(past_tokens + 1, g.residual);
+  // one launch: a KIVI cache on the matrix-core kernel, the new token landing
+  // in the ring (no page to encode); else the append's kernels, then the decode
+  if (g.scheme == KVQ_KIVI && kvq::mfma_fused_append_ok(g) && q_new == q_old &&
+      past_tokens >= q_new) {
+    a.k_new = k_new;
+    a.v_new = v_new;
+    const hipError_t e = kvq::launch_decode(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
+  }
+  const int32_t ast = kvq_quantize_append(cfg, cache, layer, past_tokens, 1, k_new, v_new,
+                                          k_scale, v_scale, stream);
+  if (ast != KVQ_OK) return ast;
+  const hipError_t e = kvq::launch_decode(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
+}
+
 int32_t kvq_decode_attention_multi(const kvq_config* cfg, const void* cache, int32_t layer,
                                    int64_t tokens, int32_t n_queries, const void* q,
                                    const float* k_scale, const float* v_scale, float* out,

@@ -127,6 +127,8 @@ struct DecodeArgs {
   int32_t splits;           // token splits per (seq, KV head), >= 1
   int32_t items;            // work items (pages + ring chunks) per (seq, KV head)
   int32_t requested_splits; // cfg.num_splits
+  const void* k_new;        // fused one-token append: the token at position tokens - 1,
+  const void* v_new;        //   [batch][kv_heads][d] in_dtype (null: none)
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
@@ -141,6 +143,9 @@ bool mfma_path(const Geometry& g);
 bool mfma_multi_ok(const Geometry& g, int64_t tokens, int32_t nq);
 MfmaPlan mfma_plan(const Geometry& g, int64_t tokens, int32_t requested);
 hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t stream);
+// The matrix-core KIVI kernel takes a fused one-token append (kivi_mfma_kernel,
+// not the rotary GQA-4 kernel).
+bool mfma_fused_append_ok(const Geometry& g);
 // Matrix-core path of FP8 E4M3 and bfloat16 caches (head_dim >= 64, no rotary embedding).
 bool fp8_mfma_path(const Geometry& g);
 int32_t fp8_mfma_splits(const Geometry& g, int64_t tokens, int32_t requested);

@@ -19,12 +19,13 @@ KVQ_KIVI, KVQ_SYM_TOKEN, KVQ_FP8_E4M3, KVQ_BF16_CACHE, KVQ_FP8_E5M2 = 0, 1, 2, 3
 KVQ_F32, KVQ_BF16 = 0, 1
 KVQ_BYTES_FORMULA, KVQ_BYTES_CACHE, KVQ_BYTES_WORKSPACE = 0, 1, 2
 
-ABI_VERSION = 7   # KVQ_ABI_VERSION of include/kvq.h that this binding mirrors
+ABI_VERSION = 8   # KVQ_ABI_VERSION of include/kvq.h that this binding mirrors
 
 SYMBOLS = ("kvq_cache_bytes", "kvq_quantize_append", "kvq_quantize_append_ragged",
            "kvq_decode_attention", "kvq_decode_attention_ragged", "kvq_decode_attention_multi",
            "kvq_decode_attention_noalloc", "kvq_paged_cache_bytes", "kvq_quantize_append_paged",
-           "kvq_decode_attention_paged", "kvq_status_string", "kvq_abi_version")
+           "kvq_decode_attention_paged", "kvq_append_decode", "kvq_status_string",
+           "kvq_abi_version")
 KVQ_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
@@ -109,6 +110,8 @@ def lib():
         L.kvq_decode_attention_paged.argtypes = [cfgp, P, I32, P, I32, I64, I64, P, P, P, P, P, P,
                                                  ctypes.c_size_t, P]
         L.kvq_decode_attention_paged.restype = I32
+        L.kvq_append_decode.argtypes = [cfgp, P, I32, I64, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.kvq_append_decode.restype = I32
         L.kvq_status_string.argtypes = [I32]
         L.kvq_status_string.restype = ctypes.c_char_p
         L.kvq_abi_version.argtypes = []
@@ -195,6 +198,20 @@ def kvq_decode_attention_noalloc(cfg, cache, layer, tokens, q, out, k_scale=None
                                             _stream(stream))
     if check and st != KVQ_OK:
         raise KvqError(st, "kvq_decode_attention_noalloc")
+    return st
+
+
+def kvq_append_decode(cfg, cache, layer, past_tokens, k_new, v_new, q, out, workspace,
+                      workspace_bytes=None, k_scale=None, v_scale=None, stream=None, check=True):
+    """One step: append one token per sequence ([batch, 1, kv_heads, head_dim])
+    at past_tokens, then decode over past_tokens + 1 tokens."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = lib().kvq_append_decode(ctypes.byref(cfg), _ptr(cache), layer, past_tokens, _ptr(k_new),
+                                 _ptr(v_new), _ptr(k_scale), _ptr(v_scale), _ptr(q), _ptr(out),
+                                 _ptr(workspace), workspace_bytes, _stream(stream))
+    if check and st != KVQ_OK:
+        raise KvqError(st, "kvq_append_decode")
     return st
 
 

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert kvq.kvq_abi_version() == 7
+    assert kvq.kvq_abi_version() == 8
     assert kvq.status_string(0) == "ok"
     for st in (-1, -2, -3, -4, -5, -6):
         assert kvq.status_string(st) != "unknown status"
@@ -374,3 +374,21 @@ def test_paged_sizes_and_validation():
     assert dp(p, f, 0, f, P, 10, 8, None, f, None, None, f, f, 1 << 20, None) == kvq.KVQ_ERR_NULL
     assert dp(p, f, 0, f, P, 10, 8, f, f, None, None, f, f, 0, None) == kvq.KVQ_ERR_WORKSPACE
     assert L.kvq_paged_cache_bytes(p, -1) == kvq.KVQ_ERR_INVALID
+
+
+def test_append_decode_validation():
+    """kvq_append_decode checks both calls' arguments before launching."""
+    L = kvq.lib()
+    c = cfg()
+    p = ctypes.byref(c)
+    f = 1 << 20
+    big = 1 << 30
+    ad = L.kvq_append_decode
+    assert ad(None, f, 0, 8, f, f, None, None, f, f, f, big, None) == kvq.KVQ_ERR_NULL
+    assert ad(p, f, 0, -1, f, f, None, None, f, f, f, big, None) == kvq.KVQ_ERR_INVALID
+    assert ad(p, f, 0, 4096, f, f, None, None, f, f, f, big, None) == kvq.KVQ_ERR_CAPACITY
+    assert ad(p, f, 0, 8, None, f, None, None, f, f, f, big, None) == kvq.KVQ_ERR_NULL
+    assert ad(p, f, 0, 8, f, f + 4, None, None, f, f, f, big, None) == kvq.KVQ_ERR_INVALID
+    assert ad(p, f, 0, 8, f, f, None, None, None, f, f, big, None) == kvq.KVQ_ERR_NULL
+    assert ad(p, f, 0, 8, f, f, None, None, f, f, f, 0, None) == kvq.KVQ_ERR_WORKSPACE
+    assert ad(p, f, 5, 8, f, f, None, None, f, f, f, big, None) == kvq.KVQ_ERR_INVALID   # layer
