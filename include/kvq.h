@@ -309,9 +309,13 @@ KVQ_API int32_t kvq_quantize_append_ragged(const kvq_config* cfg, void* cache, i
  *   out        device fp32 [batch][q_heads][head_dim]
  *   workspace  device, >= kvq_cache_bytes(cfg, tokens, KVQ_BYTES_WORKSPACE);
  *              zero-filled before its first use. It begins with one int32
- *              arrival counter per (sequence, KV head), which every call
- *              leaves at zero again; the split partials after them are
- *              scratch that each call overwrites
+ *              arrival counter per (sequence, KV head), followed by the split
+ *              partials; every call leaves all of it at zero again (a partial
+ *              slot holds the complement of a float's bits, so it reads zero
+ *              until its block has written it in the call). A workspace may
+ *              be shared by calls that run one after another (any layer,
+ *              config or token count it is large enough for), never by calls
+ *              that may overlap
  * Requires 1 <= tokens <= max_tokens and that the cache holds `tokens` tokens.
  */
 KVQ_API int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache,
@@ -468,7 +472,7 @@ KVQ_API int32_t kvq_decode_attention_multi(const kvq_config* cfg, const void* ca
  *   KVQ_ERR_WORKSPACE (validated on the host, nothing launched). The call
  *   allocates nothing. The first call on a device looks up the array's
  *   address and enqueues one small kernel on `stream` that clears it; every
- *   decode leaves its counters at zero again.
+ *   decode leaves its counters and partials at zero again.
  *   Every call on one GPU shares that GPU's array: calls that may overlap on
  *   one GPU (different streams, or concurrent graph replays) race and give
  *   wrong results; serialise them, or use kvq_decode_attention with a

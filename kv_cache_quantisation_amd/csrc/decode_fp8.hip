@@ -42,6 +42,7 @@
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "kvq_merge.h"
 #include "kvq_wave.h"
 
 namespace kvq {
@@ -406,83 +407,52 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
     }
   }
   __syncthreads();
+  // several blocks per (sequence, KV head): count this block's arrival first;
+  // the round trip overlaps the combination of the waves below
+  int arrived = 0;
+  if (p.splits > 1 && tid == 0) arrived = count_arrival(&p.counters[unit]);
 
-  // ---- combine the waves; write the output, or this block's partial --------
+  // ---- combine the waves: this thread's elements i = tid + e * kThreads ----
   const float vs_h = BF16 ? 1.0f : p.v_scale[h];
-  float* part_bh = p.partials + (static_cast<int64_t>(row) * p.q_heads + h * HG) * p.splits * (D + 2);
-  for (int i = tid; i < HG * D; i += kThreads) {
-    const int hh = i / D, c = i % D;
-    float M = -INFINITY;
+  constexpr int PER = (HG * D + kThreads - 1) / kThreads;
+  float own_m[PER], own_l[PER], own_o[PER];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, R(w, hh)[0]);
-    float so = 0.f, sl = 0.f;
+  for (int e = 0; e < PER; ++e) {
+    const int i = tid + e * kThreads;
+    own_m[e] = -INFINITY;
+    own_l[e] = 0.f;
+    own_o[e] = 0.f;
+    if (i < HG * D) {
+      const int hh = i / D, c = i % D;
+      float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float e = exp2_rel(R(w, hh)[0], M);   // idle wave (or block): 0
-      so = fmaf(e, R(w, hh)[2 + c], so);
-      sl = fmaf(e, R(w, hh)[1], sl);
-    }
-    so *= vs_h;
-    const int hq = h * HG + hh;
-    if (p.splits == 1) {
-      p.out[(static_cast<int64_t>(row) * p.q_heads + hq) * D + c] = so / sl;
-    } else {
-      float* part = part_bh + (static_cast<int64_t>(hh) * p.splits + split) * (D + 2);
-      store_coherent(part + 2 + c, so);
-      if (c == 0) {
-        store_coherent(part, M);
-        store_coherent(part + 1, sl);
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, R(w, hh)[0]);
+      float so = 0.f, sl = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float ew = exp2_rel(R(w, hh)[0], M);   // idle wave (or block): 0
+        so = fmaf(ew, R(w, hh)[2 + c], so);
+        sl = fmaf(ew, R(w, hh)[1], sl);
       }
+      so *= vs_h;
+      if (p.splits == 1) p.out[(static_cast<int64_t>(row) * p.q_heads + h * HG + hh) * D + c] = so / sl;
+      own_m[e] = M;
+      own_l[e] = sl;
+      own_o[e] = so;
     }
   }
   if (p.splits == 1) return;
 
-  // ---- the last block of this (sequence, KV head) merges every partial ------
-  // (of every query row of the sequence: nq * splits blocks arrive);
-  // every wave's partial stores (device scope, written through) have completed
-  // before the block's arrival is counted: the block that counts last reads them
-  wait_vm<0>();
+  // ---- the last of the nq * splits blocks of (b, h) to arrive merges --------
+  if (tid == 0) last_block = arrived == p.nq * p.splits - 1;
   __syncthreads();
-  if (tid == 0) {
-    const int done = __hip_atomic_fetch_add(&p.counters[unit], 1, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-    last_block = done == p.nq * p.splits - 1;
+  float* part_rh = p.partials + (static_cast<int64_t>(row) * p.q_heads + h * HG) * p.splits * (D + 2);
+  if (!last_block) {
+    store_partial<D, HG, kThreads>(part_rh, p.splits, split, own_m, own_l, own_o, tid);
+    return;
   }
-  __syncthreads();
-  if (!last_block) return;
-  for (int i = tid; i < p.nq * HG * D; i += kThreads) {
-    const int r = b * p.nq + i / (HG * D), hh = (i / D) % HG, c = i % D;
-    const float* part = p.partials +
-                        ((static_cast<int64_t>(r) * p.q_heads + h * HG + hh) * p.splits) * (D + 2);
-    float M = -INFINITY, so = 0.f, sl = 0.f;
-    for (int s0 = 0; s0 < p.splits; s0 += 8) {
-      float mv[8], lv[8], ov[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float* ps = part + (s0 + k < p.splits ? s0 + k : s0) * (D + 2);
-        mv[k] = load_coherent(ps);
-        lv[k] = load_coherent(ps + 1);
-        ov[k] = load_coherent(ps + 2 + c);
-      }
-      float bm = -INFINITY;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) bm = s0 + k < p.splits ? fmaxf(bm, mv[k]) : bm;
-      const float Mn = fmaxf(M, bm);
-      const float a = exp2_rel(M, Mn);
-      so *= a;
-      sl *= a;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float e = s0 + k < p.splits ? exp2_rel(mv[k], Mn) : 0.f;
-        sl = fmaf(e, lv[k], sl);
-        so = fmaf(e, ov[k], so);
-      }
-      M = Mn;
-    }
-    p.out[(static_cast<int64_t>(r) * p.q_heads + h * HG + hh) * D + c] = so / sl;
-  }
-  if (tid == 0)
-    __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  merge_partials<D, HG, kThreads>(p.partials, p.out, &p.counters[unit], p.q_heads, p.splits, p.nq, b, h,
+                                  row, split, own_m, own_l, own_o, tid);
 }
 
 template <int FMT, int D>

@@ -37,6 +37,7 @@
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "kvq_merge.h"
 #include "kvq_wave.h"
 
 namespace kvq {
@@ -493,68 +494,53 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     }
   }
   __syncthreads();
+  // several blocks per (sequence, KV head): count this block's arrival first;
+  // the round trip overlaps the combination of the waves below
+  __shared__ int last_block;
+  const int unit = b * p.kv_heads + h;   // one arrival counter for every row of b
+  int arrived = 0;
+  if (p.splits > 1 && tid == 0) arrived = count_arrival(&p.counters[unit]);
   const float vsc_h = is_fp8(SCHEME) ? p.v_scale[h] : 1.0f;
-  for (int i = tid; i < HG * D; i += kThreads) {
-    const int g = i / D, c = i % D;
-    float M = -INFINITY;
+  constexpr int PER = (HG * D + kThreads - 1) / kThreads;
+  float own_m[PER], own_l[PER], own_o[PER];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red[(w * HG + g) * (D + 2)]);
-    float so = 0.f, sl = 0.f;
+  for (int e = 0; e < PER; ++e) {
+    const int i = tid + e * kThreads;
+    own_m[e] = -INFINITY;
+    own_l[e] = 0.f;
+    own_o[e] = 0.f;
+    if (i < HG * D) {
+      const int g = i / D, c = i % D;
+      float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float* rw = red + (w * HG + g) * (D + 2);
-      const float e = exp2_rel(rw[0], M);  // empty wave (or split): 0
-      so = fmaf(e, rw[2 + c], so);
-      sl = fmaf(e, rw[1], sl);
-    }
-    so *= vsc_h;
-    const int hq = h * HG + g;
-    if (p.splits == 1) {
-      p.out[(static_cast<int64_t>(row) * p.q_heads + hq) * D + c] = so / sl;
-    } else {
-      float* part = p.partials +
-                    ((static_cast<int64_t>(row) * p.q_heads + hq) * p.splits + split) * (D + 2);
-      store_coherent(part + 2 + c, so);
-      if (c == 0) {
-        store_coherent(part, M);
-        store_coherent(part + 1, sl);
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red[(w * HG + g) * (D + 2)]);
+      float so = 0.f, sl = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float* rw = red + (w * HG + g) * (D + 2);
+        const float ew = exp2_rel(rw[0], M);  // empty wave (or split): 0
+        so = fmaf(ew, rw[2 + c], so);
+        sl = fmaf(ew, rw[1], sl);
       }
+      so *= vsc_h;
+      if (p.splits == 1) p.out[(static_cast<int64_t>(row) * p.q_heads + h * HG + g) * D + c] = so / sl;
+      own_m[e] = M;
+      own_l[e] = sl;
+      own_o[e] = so;
     }
   }
   if (p.splits == 1) return;
 
-  // ---- the last block of this (sequence, KV head) merges every partial ------
-  // (of every query row of the sequence: nq * splits blocks arrive). Partials
-  // are written and read at device scope; every wave's stores have completed
-  // before the block's arrival is counted, and the counter is returned to zero
-  // for the next call. M = max_s m_s; out = sum_s 2^(m_s-M) o_s / sum_s 2^(m_s-M) l_s.
-  __shared__ int last_block;
-  wait_vm<0>();
+  // ---- the last of the nq * splits blocks of (b, h) to arrive merges --------
+  if (tid == 0) last_block = arrived == p.nq * p.splits - 1;
   __syncthreads();
-  const int unit = b * p.kv_heads + h;   // one arrival counter for every row of b
-  if (tid == 0) {
-    const int done = __hip_atomic_fetch_add(&p.counters[unit], 1, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-    last_block = done == p.nq * p.splits - 1;
+  float* part_rh = p.partials + (static_cast<int64_t>(row) * p.q_heads + h * HG) * p.splits * (D + 2);
+  if (!last_block) {
+    store_partial<D, HG, kThreads>(part_rh, p.splits, split, own_m, own_l, own_o, tid);
+    return;
   }
-  __syncthreads();
-  if (!last_block) return;
-  for (int i = tid; i < p.nq * HG * D; i += kThreads) {
-    const int r = b * p.nq + i / (HG * D), g = (i / D) % HG, c = i % D;
-    const float* part = p.partials +
-                        ((static_cast<int64_t>(r) * p.q_heads + h * HG + g) * p.splits) * (D + 2);
-    float M = -INFINITY;
-    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, load_coherent(part + s * (D + 2)));
-    float so = 0.f, sl = 0.f;
-    for (int s = 0; s < p.splits; ++s) {
-      const float e = exp2_rel(load_coherent(part + s * (D + 2)), M);
-      sl = fmaf(e, load_coherent(part + s * (D + 2) + 1), sl);
-      so = fmaf(e, load_coherent(part + s * (D + 2) + 2 + c), so);
-    }
-    p.out[(static_cast<int64_t>(r) * p.q_heads + h * HG + g) * D + c] = so / sl;
-  }
-  if (tid == 0)
-    __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  merge_partials<D, HG, kThreads>(p.partials, p.out, &p.counters[unit], p.q_heads, p.splits, p.nq, b, h,
+                                  row, split, own_m, own_l, own_o, tid);
 }
 
 template <int SCHEME, int BITS, int VB, int D, int HG>

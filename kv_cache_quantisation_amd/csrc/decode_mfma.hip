@@ -55,6 +55,7 @@
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "kvq_merge.h"
 #include "kvq_wave.h"
 
 namespace kvq {
@@ -210,111 +211,50 @@ __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* 
     }
   }
   __syncthreads();
+  // several blocks per (sequence, KV head): count this block's arrival first;
+  // the round trip overlaps the combination of the waves below
+  int arrived = 0;
+  if (p.splits > 1 && tid == 0) arrived = count_arrival(&p.counters[unit]);
 
-  // ---- combine the waves; write the output, or this block's partial --------
-  float* part_bh = p.partials + (static_cast<int64_t>(row) * p.q_heads + h * HG) * p.splits * (D + 2);
-  for (int i = tid; i < HG * D; i += NTH) {
-    const int hh = i / D, c = i % D;
-    float M = -INFINITY;
+  // ---- combine the waves: this thread's elements i = tid + e * NTH --------
+  constexpr int PER = (HG * D + NTH - 1) / NTH;
+  float own_m[PER], own_l[PER], own_o[PER];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, R(w, hh)[0]);
-    float so = 0.f, sl = 0.f;
+  for (int e = 0; e < PER; ++e) {
+    const int i = tid + e * NTH;
+    own_m[e] = -INFINITY;
+    own_l[e] = 0.f;
+    own_o[e] = 0.f;
+    if (i < HG * D) {
+      const int hh = i / D, c = i % D;
+      float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float e = exp2_rel(R(w, hh)[0], M);   // idle wave (or block): 0
-      so = fmaf(e, R(w, hh)[2 + c], so);
-      sl = fmaf(e, R(w, hh)[1], sl);
-    }
-    const int hq = h * HG + hh;
-    if (p.splits == 1) {
-      p.out[(static_cast<int64_t>(row) * p.q_heads + hq) * D + c] = so / sl;
-    } else {
-      float* part = part_bh + (static_cast<int64_t>(hh) * p.splits + split) * (D + 2);
-      store_coherent(part + 2 + c, so);
-      if (c == 0) {
-        store_coherent(part, M);
-        store_coherent(part + 1, sl);
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, R(w, hh)[0]);
+      float so = 0.f, sl = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float ew = exp2_rel(R(w, hh)[0], M);   // idle wave (or block): 0
+        so = fmaf(ew, R(w, hh)[2 + c], so);
+        sl = fmaf(ew, R(w, hh)[1], sl);
       }
+      if (p.splits == 1) p.out[(static_cast<int64_t>(row) * p.q_heads + h * HG + hh) * D + c] = so / sl;
+      own_m[e] = M;
+      own_l[e] = sl;
+      own_o[e] = so;
     }
   }
   if (p.splits == 1) return;
 
-  // ---- the last block of this (sequence, KV head) merges every partial ------
-  // (of every query row of the sequence: nq * splits blocks arrive)
-  // M = max_s m_s; out = sum_s 2^(m_s-M) o_s / sum_s 2^(m_s-M) l_s. Partials
-  // are written and read at device scope (through to the coherence point, not
-  // the per-XCD L2); the counter lives in the workspace and is returned to
-  // zero for the next call.
-  // every wave's partial stores (device scope, written through) have completed
-  // before the block's arrival is counted: the block that counts last reads them
-  wait_vm<0>();
+  // ---- the last of the nq * splits blocks of (b, h) to arrive merges --------
+  if (tid == 0) last_block = arrived == p.nq * p.splits - 1;
   __syncthreads();
-  if (tid == 0) {
-    const int done = __hip_atomic_fetch_add(&p.counters[unit], 1, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-    last_block = done == p.nq * p.splits - 1;
+  float* part_rh = p.partials + (static_cast<int64_t>(row) * p.q_heads + h * HG) * p.splits * (D + 2);
+  if (!last_block) {
+    store_partial<D, HG, NTH>(part_rh, p.splits, split, own_m, own_l, own_o, tid);
+    return;
   }
-  __syncthreads();
-  if (!last_block) return;
-  // each thread merges up to two output elements at a time, with the loads of
-  // a batch of 8 splits for both issued before any use
-  constexpr int PER = (HG * D + NTH - 1) / NTH;
-  constexpr int CH = PER < 2 ? PER : 2;
-  for (int r = b * p.nq; r < (b + 1) * p.nq; ++r) {
-  const float* part_rh = p.partials + (static_cast<int64_t>(r) * p.q_heads + h * HG) * p.splits * (D + 2);
-  for (int e0 = 0; e0 < PER; e0 += CH) {
-    float M[CH], so[CH], sl[CH];
-#pragma unroll
-    for (int e = 0; e < CH; ++e) {
-      M[e] = -INFINITY;
-      so[e] = 0.f;
-      sl[e] = 0.f;
-    }
-    for (int s0 = 0; s0 < p.splits; s0 += 8) {
-      float mv[CH][8], lv[CH][8], ov[CH][8];
-#pragma unroll
-      for (int e = 0; e < CH; ++e) {
-        const int i = tid + (e0 + e) * NTH;
-        const int hh = (i < HG * D ? i : 0) / D, c = i % D;
-        const float* part = part_rh + static_cast<int64_t>(hh) * p.splits * (D + 2);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float* ps = part + (s0 + k < p.splits ? s0 + k : s0) * (D + 2);
-          mv[e][k] = load_coherent(ps);
-          lv[e][k] = load_coherent(ps + 1);
-          ov[e][k] = load_coherent(ps + 2 + c);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < CH; ++e) {
-        float bm = -INFINITY;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) bm = s0 + k < p.splits ? fmaxf(bm, mv[e][k]) : bm;
-        const float Mn = fmaxf(M[e], bm);
-        const float a = exp2_rel(M[e], Mn);
-        so[e] *= a;
-        sl[e] *= a;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float w8 = s0 + k < p.splits ? exp2_rel(mv[e][k], Mn) : 0.f;
-          sl[e] = fmaf(w8, lv[e][k], sl[e]);
-          so[e] = fmaf(w8, ov[e][k], so[e]);
-        }
-        M[e] = Mn;
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < CH; ++e) {
-      const int i = tid + (e0 + e) * NTH;
-      if (i < HG * D) {
-        const int hh = i / D, c = i % D;
-        p.out[(static_cast<int64_t>(r) * p.q_heads + h * HG + hh) * D + c] = so[e] / sl[e];
-      }
-    }
-  }
-  }
-  if (tid == 0)
-    __hip_atomic_store(&p.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  merge_partials<D, HG, NTH>(p.partials, p.out, &p.counters[unit], p.q_heads, p.splits, p.nq, b, h, row,
+                             split, own_m, own_l, own_o, tid);
 }
 
 // Blocks of the four-wave kivi_mfma_kernel<bits, *, d, *, rope> resident per

@@ -71,8 +71,7 @@ def test_multi_query_decode(case):
     want = oc.decode_multi(0, H.values(q), rope_theta=rope)
     err = H.max_err(out, want)
     assert err <= H.ATOL, err
-    counters = w.batch * w.kv_heads * 4          # arrival counters: left at zero
-    assert int(ws[:counters].count_nonzero()) == 0
+    assert int(ws.count_nonzero()) == 0   # counters and partials
 
 
 def test_single_query_is_the_plain_decode():

@@ -487,6 +487,35 @@ def test_decode_split_invariance_and_determinism():
         assert float((o - outs[0]).abs().max()) < 1e-4
 
 
+def test_shared_workspace_across_kernels():
+    """One workspace serves, one call after another, the matrix-core KIVI
+    kernel, the generic kernel and the FP8 kernel at several split counts and
+    query counts: each result stays within 2e-3 of the oracle, and after every
+    call the whole workspace (arrival counters and split partials) is zero
+    again, so no call reads partials another call left behind."""
+    cases = []
+    for scheme, bits, splits in ((synth.KIVI, 2, 7), (synth.KIVI, 8, 5), (synth.FP8_E4M3, 8, 3),
+                                 (synth.KIVI, 2, 2), (synth.KIVI, 4, 0)):
+        w = small(scheme, bits, 128, torch.bfloat16, 0 if scheme == synth.FP8_E4M3 else 32, B=3, hg=4, T=700)
+        cfg, cache, oc, k, v, ks, vs = run_append(w, [w.tokens], capacity=740)
+        cfg.num_splits = splits
+        cases.append((w, cfg, cache, oc, ks, vs, splits))
+    nq = 3
+    need = max(nq * kvq.kvq_cache_bytes(c[1], c[0].tokens, kvq.KVQ_BYTES_WORKSPACE) for c in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    for rnd in range(2):
+        for w, cfg, cache, oc, ks, vs, splits in cases:
+            q = synth.query(w, device=DEV, tag=rnd)
+            out = H.decode(cfg, cache, 0, w.tokens, q, ks, vs, ws=ws)
+            assert H.max_err(out, oc.decode(0, H.values(q))) <= H.ATOL, (w.name, splits)
+            assert int(ws.count_nonzero()) == 0, (w.name, splits)
+            qm = torch.stack([synth.query(w, device=DEV, tag=10 + i) for i in range(nq)], dim=1).contiguous()
+            om = torch.empty(qm.shape, dtype=torch.float32, device=DEV)
+            kvq.kvq_decode_attention_multi(cfg, cache, 0, w.tokens, qm, om, ws, k_scale=ks, v_scale=vs)
+            assert H.max_err(om, oc.decode_multi(0, H.values(qm))) <= H.ATOL, (w.name, splits, nq)
+            assert int(ws.count_nonzero()) == 0, (w.name, splits, nq)
+
+
 def test_append_determinism_and_noop():
     w = small(synth.KIVI, 4, 128, torch.bfloat16, 128, T=500)
     cfg, c1, *_ = run_append(w, [w.tokens], capacity=512)
