@@ -256,13 +256,15 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
       for (int i = 0; i < 8; ++i) s[i] = 8 * g + i < n_valid ? s[i] : -INFINITY;
     }
     // online softmax: running max per head (lanes j < HG), weights 2^(s - m)
+    // (whether a head's max grows is decided by each lane's own maximum; the
+    // maximum over the head's four lane groups is only formed when one does)
     float pmax = s[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) pmax = fmaxf(pmax, s[i]);
-    pmax = fmaxf(pmax, xor16(pmax));
-    pmax = fmaxf(pmax, xor32(pmax));
-    const float m_new = fmaxf(m_lane, pmax);
-    if (__builtin_amdgcn_ballot_w64((j < HG) && (m_new > m_lane)) != 0) {
+    if (__builtin_amdgcn_ballot_w64((j < HG) && (pmax > m_lane)) != 0) {
+      pmax = fmaxf(pmax, xor16(pmax));
+      pmax = fmaxf(pmax, xor32(pmax));
+      const float m_new = fmaxf(m_lane, pmax);
       const float alpha = fast_exp2(m_lane - m_new);
       l_lane *= alpha;
       m_lane = m_new;

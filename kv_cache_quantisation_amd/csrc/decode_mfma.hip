@@ -377,14 +377,17 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
     float pmax = s[0];
 #pragma unroll
     for (int i = 1; i < NS; ++i) pmax = fmaxf(pmax, s[i]);
-    pmax = fmaxf(pmax, xor16(pmax));
-    pmax = fmaxf(pmax, xor32(pmax));
     // the reference max moves only when a score exceeds it by more than
     // kMaxSlack (weights stay below 2^kMaxSlack; any reference gives the same
-    // softmax), so the accumulators are rarely rescaled
-    const float m_new = fmaxf(m_lane, pmax);
+    // softmax), so the accumulators are rarely rescaled. A head's scores are
+    // spread over its four lane groups; whether any of them exceeds the slack
+    // is decided by each lane's own maximum, so the maximum over the lane
+    // groups is only formed on the rare rescaling pages.
     const bool grows = (j < HG) && (pmax > m_lane + kMaxSlack);
     if (__builtin_amdgcn_ballot_w64(grows) != 0) {   // wave-uniform
+      pmax = fmaxf(pmax, xor16(pmax));
+      pmax = fmaxf(pmax, xor32(pmax));
+      const float m_new = fmaxf(m_lane, pmax);
       const float alpha = fast_exp2(m_lane - m_new);
       l_lane *= alpha;
       z_lane *= alpha;
@@ -1290,38 +1293,44 @@ __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
   // into the softmax state; returns the weights 2^(s - m)
   auto softmax = [&](floatx4 s) -> floatx4 {
     float pm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    // max over the 8 token quads of this half: lanes l ^ 4, l ^ 8, l ^ 16
-    pm = fmaxf(pm, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, pm), (0x04 << 10) | 0x1F)));
-    pm = fmaxf(pm, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, pm), (0x08 << 10) | 0x1F)));
-    pm = fmaxf(pm, xor16(pm));
     float mine = mh[0];
 #pragma unroll
     for (int hh = 1; hh < HG; ++hh) mine = hd == hh ? mh[hh] : mine;
-    const float m_new = fmaxf(mine, pm);
-    float a_h[HG];
-    bool grow = false;
-#pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-      const float mn = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_new), hh));
-      grow |= mn > mh[hh];
-      a_h[hh] = mn;
-    }
-    if (grow) {   // wave-uniform
+    // the reference max of a head moves only when one of its scores exceeds
+    // it by more than kMaxSlack (weights stay below 2^kMaxSlack; any
+    // reference gives the same softmax); each lane's own maximum decides, the
+    // maxima over the lanes of a head are formed only then
+    if (__builtin_amdgcn_ballot_w64(pm > mine + kMaxSlack) != 0) {   // wave-uniform, rare
+      // max over the 8 token quads of this half: lanes l ^ 4, l ^ 8, l ^ 16
+      pm = fmaxf(pm, dpp<0x124>(pm));   // row_ror:4
+      pm = fmaxf(pm, dpp<0x128>(pm));   // row_ror:8
+      pm = fmaxf(pm, xor16(pm));
+      const float m_new = fmaxf(mine, pm);
+      float a_h[HG];
+      bool grow = false;
 #pragma unroll
       for (int hh = 0; hh < HG; ++hh) {
-        const float a = fast_exp2(mh[hh] - a_h[hh]);
-        mh[hh] = a_h[hh];
-        a_h[hh] = a;
+        const float mn = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_new), hh));
+        grow |= mn > mh[hh];
+        a_h[hh] = mn;
       }
-      float a_mine = a_h[0];
+      if (grow) {   // wave-uniform
 #pragma unroll
-      for (int hh = 1; hh < HG; ++hh) a_mine = hd == hh ? a_h[hh] : a_mine;
-      lane_l *= a_mine;
-      lane_z *= a_mine;
+        for (int hh = 0; hh < HG; ++hh) {
+          const float a = fast_exp2(mh[hh] - a_h[hh]);
+          mh[hh] = a_h[hh];
+          a_h[hh] = a;
+        }
+        float a_mine = a_h[0];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+        for (int hh = 1; hh < HG; ++hh) a_mine = hd == hh ? a_h[hh] : a_mine;
+        lane_l *= a_mine;
+        lane_z *= a_mine;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= a_h[r];   // rows 4g + r: head r
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= a_h[r];   // rows 4g + r: head r
+        }
       }
     }
     float mcur = mh[0];

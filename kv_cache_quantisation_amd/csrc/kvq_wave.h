@@ -79,17 +79,25 @@ __device__ __forceinline__ float2 codes2_f32(uint32_t y) {
 }
 
 // Sum over aligned groups of 8 lanes (all lanes receive it).
+// (The moves read a source lane for every lane, so an update with old value 0
+// is the plain move; written that way the compiler folds each move into the
+// add that consumes it.)
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float sum8(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);   // row_half_mirror
   return v;
 }
 
 // Sum over the 16 lanes of each DPP row (all lanes receive it).
 __device__ __forceinline__ float row_sum16(float v) {
   v = sum8(v);
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));  // row_mirror
+  v += dpp<0x140>(v);   // row_mirror
   return v;
 }
 
@@ -101,19 +109,24 @@ __device__ __forceinline__ float xor32(float v) {
   return __builtin_bit_cast(float, lane < 32 ? r[1] : r[0]);
 }
 
-// Value of lane l ^ 16 (within each half of the wave).
+// Value of lane l ^ 16 (within each half of the wave), by a swap of row
+// pairs on the vector ALU: the swap hands each even row the odd row after it
+// (second result) and each odd row the even row before it (first result). No
+// LDS instruction, so a chain of these does not wait on LDS round trips.
 __device__ __forceinline__ float xor16(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
-                                                               (0x10 << 10) | 0x1F));
+  const int lane = threadIdx.x & 63;
+  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                            false, false);
+  return __builtin_bit_cast(float, ((lane >> 4) & 1) ? r[0] : r[1]);
 }
 
 // Maximum over the wave (all lanes receive it), by DPP moves and lane swaps
 // (no LDS permutes).
 __device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  v = fmaxf(v, dpp<0x140>(v));
   v = fmaxf(v, xor16(v));
   return fmaxf(v, xor32(v));
 }
