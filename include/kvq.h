@@ -448,9 +448,12 @@ KVQ_API int32_t kvq_decode_attention_paged(const kvq_config* cfg, const void* ca
  * Other arguments, requirements and errors as kvq_decode_attention. With
  * n_queries > 1, KIVI caches of 16-bit inputs run on the matrix-core kernel,
  * one row of blocks per query (a query whose token is in a quantised page
- * sees that page masked after its token), and so do FP8 and bfloat16 caches
- * without in-kernel rotary embedding (head_dim >= 64); every other case runs
- * on the generic (vector-ALU) kernel. */
+ * sees that page masked after its token), or, at GQA 4 without rotary keys
+ * and with an even n_queries whose tokens are all in the ring, one row of
+ * blocks per two consecutive queries that share every page; FP8 and bfloat16
+ * caches without in-kernel rotary embedding (head_dim >= 64) run on their
+ * matrix-core kernel; every other case runs on the generic (vector-ALU)
+ * kernel. */
 KVQ_API int32_t kvq_decode_attention_multi(const kvq_config* cfg, const void* cache,
                                    int32_t layer, int64_t tokens, int32_t n_queries,
                                    const void* q, const float* k_scale,

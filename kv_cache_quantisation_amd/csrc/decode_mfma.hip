@@ -154,26 +154,31 @@ __device__ __forceinline__ float load_q(const uint8_t* base, int64_t idx, int bf
 }
 
 // ---- end of every decode kernel of this file -------------------------------
-// Combines the block's waves (their running max mh, sums of p and p z per head,
-// and value accumulators acc: rows 4g + r, high parts of the heads then their
-// remainders), writes the output rows (one split) or the block's partial, and
-// in the last block of a (sequence, KV head) to finish merges every partial.
-template <int D, int HG, int NW = kWaves>
+// Combines the block's waves (their running max mh, sums of p and p z per
+// (query, head) pair, and value accumulators acc: rows 4g + r, per query the
+// high parts of its heads, then their remainders), writes the output rows
+// (one split) or the block's partials, and in the last block of a (sequence,
+// KV head) to finish merges every partial. QN: queries of the block, rows
+// b * nq + qi + qq of q, out and the partials.
+template <int D, int HG, int NW = kWaves, int QN = 1>
 __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* acc, const float* mh,
                                             const float* lsum, const float* zsum, uint8_t* arena,
                                             int& last_block, int b, int qi, int h, int split) {
   constexpr int NT = D / 16;
   constexpr int NTH = NW * 64;             // threads of the block
+  constexpr int GC = HG * QN;              // (query, head) pairs
+  static_assert(QN == 1 || HG == 4, "two queries per block: GQA 4");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform in the wave
   const int j = lane & 15, g = lane >> 4;
   const int unit = b * p.kv_heads + h;   // one arrival counter for every query row of b
-  const int row = b * p.nq + qi;         // this block's query row (q, out, partials)
+  const int row = b * p.nq + qi;         // the block's (first) query row (q, out, partials)
   __syncthreads();   // every wave is done with its page buffers (the arena)
-  float* red = reinterpret_cast<float*>(arena);   // [wave][HG][D + 2]: m, l, o
-  auto R = [&](int w, int hh) { return red + (w * HG + hh) * (D + 2); };
-  // acc rows 4g+r: row < HG is head row (hi), HG <= row < 2HG is head row-HG (lo)
+  float* red = reinterpret_cast<float*>(arena);   // [wave][GC][D + 2]: m, l, o
+  auto R = [&](int w, int vh) { return red + (w * GC + vh) * (D + 2); };
+  // acc rows 4g+r: row < HG is head row (hi), HG <= row < 2HG is head row-HG
+  // (lo); with two queries rows 2HG.. repeat that for the second query
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     float v[4];
@@ -185,29 +190,29 @@ __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* 
       } else if constexpr (HG == 2) {
         x = r < 2 ? acc[nt][r] + acc[nt][r + 2] : 0.f;
       } else if constexpr (HG == 4) {
-        x += xor16(x);          // rows 0-3 (g=0) + rows 4-7 (g=1)
+        x += xor16(x);          // rows 0-3 (g=0) + rows 4-7 (g=1); with QN = 2, 8-11 + 12-15
       } else {
         x += xor32(x);          // rows 0-7 (g=0,1) + rows 8-15 (g=2,3)
       }
       v[r] = x;
     }
     const int c = 16 * nt + j;
-    if (4 * g < HG) {
+    if ((4 * g) % (2 * HG) < HG && 4 * g < 2 * GC) {   // lane groups holding the high rows
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int hh = 4 * g + r;
-        float zz = 0.f;   // sum_t p z_t of head hh goes to every channel
+        const int vh = (4 * g / (2 * HG)) * HG + (4 * g) % (2 * HG) + r;
+        float zz = 0.f;   // sum_t p z_t of pair vh goes to every channel
 #pragma unroll
-        for (int k = 0; k < HG; ++k) zz = hh == k ? zsum[k] : zz;
-        if (hh < HG) R(wave, hh)[2 + c] = v[r] + zz;
+        for (int k = 0; k < GC; ++k) zz = vh == k ? zsum[k] : zz;
+        if ((4 * g) % (2 * HG) + r < HG) R(wave, vh)[2 + c] = v[r] + zz;
       }
     }
   }
   if (lane == 0) {
 #pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-      R(wave, hh)[0] = mh[hh];
-      R(wave, hh)[1] = lsum[hh];
+    for (int vh = 0; vh < GC; ++vh) {
+      R(wave, vh)[0] = mh[vh];
+      R(wave, vh)[1] = lsum[vh];
     }
   }
   __syncthreads();
@@ -217,7 +222,8 @@ __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* 
   if (p.splits > 1 && tid == 0) arrived = count_arrival(&p.counters[unit]);
 
   // ---- combine the waves: this thread's elements i = tid + e * NTH --------
-  constexpr int PER = (HG * D + NTH - 1) / NTH;
+  // (element i: pair vh = i / D -- query vh / HG, head vh % HG -- channel i % D)
+  constexpr int PER = (GC * D + NTH - 1) / NTH;
   float own_m[PER], own_l[PER], own_o[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
@@ -225,19 +231,20 @@ __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* 
     own_m[e] = -INFINITY;
     own_l[e] = 0.f;
     own_o[e] = 0.f;
-    if (i < HG * D) {
-      const int hh = i / D, c = i % D;
+    if (i < GC * D) {
+      const int vh = i / D, c = i % D;
       float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, R(w, hh)[0]);
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, R(w, vh)[0]);
       float so = 0.f, sl = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const float ew = exp2_rel(R(w, hh)[0], M);   // idle wave (or block): 0
-        so = fmaf(ew, R(w, hh)[2 + c], so);
-        sl = fmaf(ew, R(w, hh)[1], sl);
+        const float ew = exp2_rel(R(w, vh)[0], M);   // idle wave (or block): 0
+        so = fmaf(ew, R(w, vh)[2 + c], so);
+        sl = fmaf(ew, R(w, vh)[1], sl);
       }
-      if (p.splits == 1) p.out[(static_cast<int64_t>(row) * p.q_heads + h * HG + hh) * D + c] = so / sl;
+      const int r_out = row + vh / HG, hh = vh % HG;
+      if (p.splits == 1) p.out[(static_cast<int64_t>(r_out) * p.q_heads + h * HG + hh) * D + c] = so / sl;
       own_m[e] = M;
       own_l[e] = sl;
       own_o[e] = so;
@@ -245,16 +252,41 @@ __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* 
   }
   if (p.splits == 1) return;
 
-  // ---- the last of the nq * splits blocks of (b, h) to arrive merges --------
-  if (tid == 0) last_block = arrived == p.nq * p.splits - 1;
+  // ---- the last of the (nq / QN) * splits blocks of (b, h) to arrive merges --
+  if (tid == 0) last_block = arrived == (p.nq / QN) * p.splits - 1;
   __syncthreads();
-  float* part_rh = p.partials + (static_cast<int64_t>(row) * p.q_heads + h * HG) * p.splits * (D + 2);
-  if (!last_block) {
-    store_partial<D, HG, NTH>(part_rh, p.splits, split, own_m, own_l, own_o, tid);
-    return;
+  if constexpr (QN == 1) {
+    float* part_rh = p.partials + (static_cast<int64_t>(row) * p.q_heads + h * HG) * p.splits * (D + 2);
+    if (!last_block) {
+      store_partial<D, HG, NTH>(part_rh, p.splits, split, own_m, own_l, own_o, tid);
+      return;
+    }
+    merge_partials<D, HG, NTH>(p.partials, p.out, &p.counters[unit], p.q_heads, p.splits, p.nq, b, h, row,
+                               split, own_m, own_l, own_o, tid);
+  } else {
+    // every block stores the partials of its rows (each row's [HG][splits]
+    // block of slots, element i of pair vh at row + vh / HG); the last one
+    // merges them all from memory
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int i = tid + e * NTH;
+      if (i < GC * D) {
+        const int vh = i / D, c = i % D;
+        float* part = p.partials +
+                      ((static_cast<int64_t>(row + vh / HG) * p.q_heads + h * HG + vh % HG) * p.splits + split) *
+                          (D + 2);
+        put_partial(part + 2 + c, own_o[e]);
+        if (c == 0) {
+          put_partial(part, own_m[e]);
+          put_partial(part + 1, own_l[e]);
+        }
+      }
+    }
+    if (!last_block) return;
+    // (row -1: no row's state comes from registers; every slot is read and cleared)
+    merge_partials<D, HG, NTH>(p.partials, p.out, &p.counters[unit], p.q_heads, p.splits, p.nq, b, h, -1,
+                               split, own_m, own_l, own_o, tid);
   }
-  merge_partials<D, HG, NTH>(p.partials, p.out, &p.counters[unit], p.q_heads, p.splits, p.nq, b, h, row,
-                             split, own_m, own_l, own_o, tid);
 }
 
 // Blocks of the four-wave kivi_mfma_kernel<bits, *, d, *, rope> resident per
@@ -279,13 +311,17 @@ constexpr int kivi_waves(int kb, int vb, int d, int hg, bool rope) {
   return ((kb == 2 || kb == 4) && vb == 2 && d <= 128 && hg <= 4 && !rope) ? 8 : 4;
 }
 
-// KB, VB: bits of the key and of the value codes
-template <int KB, int VB, int D, int HG, bool ROPE>
+// KB, VB: bits of the key and of the value codes. QN: queries of a sequence
+// per block (2: two consecutive queries share every page; their high and
+// remainder columns fill the 16 columns of the key product and the 16 rows
+// of the value product, which one query at GQA 4 fills half of)
+template <int KB, int VB, int D, int HG, bool ROPE, int QN = 1>
 __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
-                             kivi_waves(KB, VB, D, HG, ROPE) == 8 ? 2 : kivi_blocks_per_cu(KB, D, ROPE)) void kivi_mfma_kernel(MfmaParams p) {
+                             QN > 1 ? 1 : kivi_waves(KB, VB, D, HG, ROPE) == 8 ? 2 : kivi_blocks_per_cu(KB, D, ROPE)) void kivi_mfma_kernel(MfmaParams p) {
   static_assert((KB == 2 || KB == 4) && (VB == 2 || VB == 4) && VB <= KB, "2- or 4-bit codes");
   static_assert(!ROPE || (KB == 2 && D <= 128), "rotary decode: 2-bit pages, head_dim <= 128");
-  static_assert(2 * HG <= 16, "hi and lo columns of the GQA group fit one tile");
+  static_assert(2 * HG * QN <= 16, "hi and lo columns of the GQA group(s) fit one tile");
+  static_assert(QN == 1 || (QN == 2 && HG == 4 && !ROPE), "two queries per block: GQA 4, keys without rotation");
   using PG = PageGeom<KB, VB, D>;
   constexpr int NW = kivi_waves(KB, VB, D, HG, ROPE);   // waves per block
   constexpr int NTH = 64 * NW;
@@ -296,10 +332,12 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   constexpr int CPR_K = KROW / 16;       // 16-byte chunks per key row
   constexpr int KW = CPG * KB / 32;      // key-code words per lane per 16-token tile
   constexpr int VROW = 32 * VB / 8;      // bytes per value channel column
-  constexpr int COMBOS = HG * 4 * KS;    // (head, lane group, k-step) fold units
+  constexpr int GC = HG * QN;            // (query, head) pairs of the block
+  constexpr int COMBOS = GC * 4 * KS;    // (pair, lane group, k-step) fold units
   constexpr int REPS = (COMBOS + 63) / 64;
   constexpr int PER_HEAD = 4 * KS;       // fold units (lanes) per head
-  constexpr int QB = (3 * HG + 15) / 16; // bf16 B-operand sets for the residual keys
+  // bf16 B-operand sets for the residual keys (one per query when QN = 2)
+  constexpr int QB = QN == 1 ? (3 * HG + 15) / 16 : QN;
   // the residual-key B operand is built once per wave and kept in registers
   // when it is small (QB * KS words of 16 bytes), else rebuilt for every step
   constexpr bool QPRE = !ROPE && QB * KS <= 4;
@@ -310,7 +348,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   // LDS banks (no padding)
   constexpr int FSTRIDE = 4 * KS;
   static_assert(FSTRIDE >= 8, "column slots cover the XOR range");
-  constexpr int FRAG = 2 * HG * FSTRIDE * 16;
+  constexpr int FRAG = 2 * GC * FSTRIDE * 16;
   // Per-wave LDS: [page buffer 0][page buffer 1][q' fragments]. A residual
   // step's 8 key + 8 value rows borrow page buffer 1 and the fragments: the
   // wave's first step is taken before its first page is computed (buffer 1 is
@@ -318,10 +356,10 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   // further step after its last page.
   constexpr int WAVE_LDS = PG::NBUF * PG::BYTES + FRAG > PG::BYTES + PG::RING
                                ? PG::NBUF * PG::BYTES + FRAG : PG::BYTES + PG::RING;
-  constexpr int RED = NW * HG * (D + 2) * 4;
+  constexpr int RED = NW * GC * (D + 2) * 4;
   constexpr int ARENA = NW * WAVE_LDS > RED ? NW * WAVE_LDS : RED;
 
-  __shared__ __attribute__((aligned(16))) float qs[HG][D];
+  __shared__ __attribute__((aligned(16))) float qs[GC][D];
   __shared__ __attribute__((aligned(16))) uint8_t arena[ARENA];              // per-wave areas / reduction
   // rotary decode: each wave's query rotated for the page in hand (row HG is
   // kept zero for the unused B columns), and omega_i / (2 pi) per channel pair
@@ -334,7 +372,15 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform in the wave
   const int j = lane & 15, g = lane >> 4;
   const int split = blockIdx.x, h = blockIdx.y;
-  const int b = blockIdx.z / p.nq, qi = blockIdx.z - b * p.nq;   // sequence, its query
+  // sequence b and its (first) query qi of the block
+  const int rows_b = p.nq / QN;
+  const int b = blockIdx.z / rows_b, qi = (blockIdx.z - b * rows_b) * QN;
+  // lane column j of the key product: query j / (2HG), high part when
+  // j % (2HG) < HG (then holding the scores of pair col_vh after the key
+  // product); with one query only columns j < HG are live
+  const bool col_hi = (j % (2 * HG)) < HG;
+  const bool col_live = QN == 1 ? j < HG : col_hi;
+  const int col_vh = (j / (2 * HG)) * HG + j % HG;
   const uint8_t* ringp = p.pm.ring(b, h);
   // tokens this sequence holds (a ragged batch: its own fill level, and its
   // own split between quantised pages and the ring)
@@ -348,8 +394,11 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   // query qi of nq sits at position fill - nq + qi and sees the tokens up to
   // it: the pages and the ring up to its own token, or, when its token is in
   // a page, the pages up to that one (the rest of that page masked)
+  // (with QN = 2 the block's second query sits one token later, at TbL - 1;
+  // both tokens are in the ring then)
   const int64_t Tb = fill - (p.nq - 1 - qi);
-  if (p.seq_tokens || p.nq > 1) n_steps = static_cast<int32_t>((Tb - q_tokens + 7) / 8);
+  const int64_t TbL = Tb + QN - 1;
+  if (p.seq_tokens || p.nq > 1) n_steps = static_cast<int32_t>((TbL - q_tokens + 7) / 8);
   const bool in_page = Tb <= q_tokens;   // block-uniform: mask this row's last page
   if (in_page) {
     n_pages = static_cast<int32_t>((Tb + kPage - 1) / kPage);
@@ -383,12 +432,15 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
     // spread over its four lane groups; whether any of them exceeds the slack
     // is decided by each lane's own maximum, so the maximum over the lane
     // groups is only formed on the rare rescaling pages.
-    const bool grows = (j < HG) && (pmax > m_lane + kMaxSlack);
+    const bool grows = col_live && (pmax > m_lane + kMaxSlack);
     if (__builtin_amdgcn_ballot_w64(grows) != 0) {   // wave-uniform
       pmax = fmaxf(pmax, xor16(pmax));
       pmax = fmaxf(pmax, xor32(pmax));
       const float m_new = fmaxf(m_lane, pmax);
-      const float alpha = fast_exp2(m_lane - m_new);
+      // a column whose max stays keeps its sums (also one that has seen no
+      // token yet, -inf: with two queries per block the other query's
+      // columns may move while this one stays there)
+      const float alpha = m_new == m_lane ? 1.0f : fast_exp2(m_lane - m_new);
       l_lane *= alpha;
       z_lane *= alpha;
       m_lane = m_new;
@@ -404,6 +456,12 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
         if constexpr (HG == 8) {
           const float a_odd = alpha_of(4 + r);
           a = (g & 1) ? a_odd : a;
+        }
+        // QN = 2: rows 4g + r of lane groups 2, 3 belong to the second query,
+        // whose head r is column 2HG + r
+        if constexpr (QN == 2) {
+          const float a_q1 = alpha_of(2 * HG + r);
+          a = g >= 2 ? a_q1 : a;
         }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= a;
@@ -524,6 +582,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
       const int cidx = lane + 64 * r;
       const int fh = cidx / PER_HEAD, fg = (cidx / KS) % 4, fk = cidx % KS;
       const int c0 = fg * CPG + 8 * fk;
+      const int chi = (fh / HG) * 2 * HG + fh % HG, clo = chi + HG;   // B columns of pair fh
       const float4 s0 = *reinterpret_cast<const float4*>(pg + PG::OFF_KS + 4 * c0);
       const float4 s1 = *reinterpret_cast<const float4*>(pg + PG::OFF_KS + 4 * c0 + 16);
       const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
@@ -549,9 +608,9 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
       split_f16(qp[4], qp[6], hi[2], lo[2]);
       split_f16(qp[5], qp[7], hi[3], lo[3]);
       if (cidx < COMBOS) {
-        *reinterpret_cast<uint4*>(frag[fh * FSTRIDE + ((4 * fk + fg) ^ (fh & 7))]) =
+        *reinterpret_cast<uint4*>(frag[chi * FSTRIDE + ((4 * fk + fg) ^ (chi & 7))]) =
             uint4{hi[0], hi[1], hi[2], hi[3]};
-        *reinterpret_cast<uint4*>(frag[(HG + fh) * FSTRIDE + ((4 * fk + fg) ^ ((HG + fh) & 7))]) =
+        *reinterpret_cast<uint4*>(frag[clo * FSTRIDE + ((4 * fk + fg) ^ (clo & 7))]) =
             uint4{lo[0], lo[1], lo[2], lo[3]};
       }
     };
@@ -584,19 +643,20 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
         v = row_sum16(v);
         if constexpr (PER_HEAD == 32) v += xor16(v);
       }
-      const int src = PER_HEAD * (j < HG ? j : 0) - 64 * r;
+      const int src = PER_HEAD * (col_live ? col_vh : 0) - 64 * r;
       const float got = __shfl(v, src & 63, 64);
       if (src >= 0 && src < 64) bias_j = got;
     }
-    if (j >= HG) bias_j = 0.f;   // lo columns carry no offset
+    if (!col_live) bias_j = 0.f;   // lo columns carry no offset
     if (big) bias_j = ldexpf(bias_j, -esc);   // scaled with the product, undone below
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    // columns >= 2*HG only produce score columns that are never read
+    // (with one query, columns >= 2*HG only produce score columns that are
+    // never read)
     half8 bq[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int col = j % (2 * HG);
+      const int col = j % (2 * GC);
       const uint4 f = *reinterpret_cast<const uint4*>(frag[col * FSTRIDE + ((4 * ks + g) ^ (col & 7))]);
       bq[ks] = cat4h(f.x, f.y, f.z, f.w);
     }
@@ -663,9 +723,13 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
     split_bf16(pv[5], pv[7], ph[3], pl[3]);
     // rows j < HG: hi of head j; rows j >= HG: lo of lane j-HG (rows >= 2HG
     // only reach accumulator rows that are never read)
+    // (QN = 2: the second query's high rows 2HG.. keep their own values)
     uint32_t pa[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pa[i] = shr_keep<HG>(ph[i], pl[i]);
+    for (int i = 0; i < 4; ++i) {
+      pa[i] = shr_keep<HG>(ph[i], pl[i]);
+      if constexpr (QN == 2) pa[i] = col_hi ? ph[i] : pa[i];
+    }
     const bf16x8 ap = __builtin_bit_cast(bf16x8, uint4{pa[0], pa[1], pa[2], pa[3]});
 
     // P' x value codes; channel of N-tile nt in column j is 16 nt + j (adjacent
@@ -737,7 +801,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
       static_cast<int64_t>(reinterpret_cast<uintptr_t>(p.v_new) - reinterpret_cast<uintptr_t>(ringp)) + new_row};
   auto issue_step = [&](int hs) -> int {    // returns the copies issued
     const int64_t t0 = q_tokens + static_cast<int64_t>(hs) * RSTEP;
-    const int nv = static_cast<int>(Tb - t0 < RSTEP ? Tb - t0 : RSTEP);
+    const int nv = static_cast<int>(TbL - t0 < RSTEP ? TbL - t0 : RSTEP);   // rows up to the last query's token
     const int row_in = lane / LPR, col_b = (lane % LPR) * 16;
     const int slots = static_cast<int>(p.ring_slots);
     const int slot0 = static_cast<int>(t0 % p.ring_slots);
@@ -766,9 +830,10 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   uint4 qstep[QPRE ? QB : 1][QPRE ? KS : 1];
   // B operand of the residual key product: q^T in three bf16 parts, columns
   // [0,HG) hi, [HG,2HG) mid, [2HG,3HG) lo, the rest zero (from the scaled q in qs)
+  // (QN = 2: set qb is query qb's, the same 3HG columns)
   auto qstep_operand = [&](int qb, int ks) -> uint4 {
-    const int col = 16 * qb + j;
-    const int part = col / HG, hh = col % HG;
+    const int col = QN == 1 ? 16 * qb + j : j;
+    const int part = col / HG, hh = (QN == 1 ? 0 : qb * HG) + col % HG;
     uint32_t w4[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -785,7 +850,9 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   // tile rows (tokens) 8..15 of a step are masked; key rows repeat rows 0..7
   auto process_step = [&](int hs) {
     const int64_t t0 = q_tokens + static_cast<int64_t>(hs) * RSTEP;
-    const int nv = static_cast<int>(Tb - t0 < RSTEP ? Tb - t0 : RSTEP);
+    // tokens of the step this lane's column sees (its query's own count)
+    const int64_t Tj = Tb + (QN == 1 ? 0 : j / (2 * HG));
+    const int nv = static_cast<int>(Tj - t0 < RSTEP ? Tj - t0 : RSTEP);
     float sc[4];
     if constexpr (ROPE) {
       // key rows rotated by their position in the step, fp32 product as for pages
@@ -822,7 +889,11 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float v;
-      if constexpr (3 * HG <= 16) {
+      if constexpr (QN == 2) {   // query q's sums in lanes < HG of set q; set 1 moves to columns 2HG..
+        const float v0 = cres[0][r] + row_shl<HG>(cres[0][r]) + row_shl<2 * HG>(cres[0][r]);
+        const float v1 = cres[1][r] + row_shl<HG>(cres[1][r]) + row_shl<2 * HG>(cres[1][r]);
+        v = __uint_as_float(shr_keep<2 * HG>(__float_as_uint(v0), __float_as_uint(v1)));
+      } else if constexpr (3 * HG <= 16) {
         v = cres[0][r] + row_shl<HG>(cres[0][r]) + row_shl<2 * HG>(cres[0][r]);
       } else {   // HG = 8: hi and mid in set 0, lo in set 1
         v = cres[0][r] + row_shl<HG>(cres[0][r]) + cres[QB - 1][r];
@@ -831,6 +902,14 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
     }
     }   // rotary / plain keys
     softmax_update(sc, std::integral_constant<int, 4>{});
+    if constexpr (QN == 2) {
+      // the block's steps reach its second query's token, so a step may hold
+      // none of the first query's tokens; in a wave that has seen no token of
+      // it yet (reference max still -inf) 2^(-inf - -inf) is not 0: absent
+      // tokens get weight 0 explicitly
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[r] = 4 * g + r < nv ? sc[r] : 0.f;
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) l_lane += sc[r];   // absent tokens contribute 0
     // P in bf16 hi/lo rows; k index 8g+i holds token 4g+i for i < 4, zero after
@@ -839,7 +918,10 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
     split_bf16(sc[2], sc[3], ph[1], pl[1]);
     uint32_t pa[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) pa[i] = shr_keep<HG>(ph[i], pl[i]);
+    for (int i = 0; i < 2; ++i) {
+      pa[i] = shr_keep<HG>(ph[i], pl[i]);
+      if constexpr (QN == 2) pa[i] = col_hi ? ph[i] : pa[i];
+    }
     const bf16x8 ap = __builtin_bit_cast(bf16x8, uint4{pa[0], pa[1], 0u, 0u});
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -858,12 +940,15 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   // residual steps go first to the waves with the fewest pages: the last wave
   // of every block, then the one before, ... (wave 0 may hold one page more)
   const int my_wave = (NW - 1 - wave) * p.splits + split;
-  const int q_bytes = HG * D * (p.q_bf16 ? 2 : 4);
+  const int q_bytes = HG * D * (p.q_bf16 ? 2 : 4);   // one query's heads of this KV head
   int after_q = 0;
   if (wave == 0) {
-    const uint8_t* qsrc = p.q + (static_cast<int64_t>(b * p.nq + qi) * p.q_heads + h * HG) * D * (p.q_bf16 ? 2 : 4);
-    for (int off = 0; off < q_bytes; off += 1024)
-      if (off + lane * 16 < q_bytes) dma16(qsrc + off + lane * 16, lds_addr(&qs[0][0]) + off);
+#pragma unroll
+    for (int qq = 0; qq < QN; ++qq) {   // raw rows of the block's queries, one after the other
+      const uint8_t* qsrc = p.q + (static_cast<int64_t>(b * p.nq + qi + qq) * p.q_heads + h * HG) * D * (p.q_bf16 ? 2 : 4);
+      for (int off = 0; off < q_bytes; off += 1024)
+        if (off + lane * 16 < q_bytes) dma16(qsrc + off + lane * 16, lds_addr(&qs[0][0]) + qq * q_bytes + off);
+    }
   }
   const bool has_step = my_wave < n_steps;
   if (has_step) after_q += issue_step(my_wave);
@@ -880,13 +965,13 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   __syncthreads();
   {
     // raw query (bf16 or f32) -> f32 * sm_scale * log2(e), in place
-    constexpr int PER = (HG * D + NTH - 1) / NTH;
+    constexpr int PER = (GC * D + NTH - 1) / NTH;
     float qv[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int i = tid + k * NTH;
       qv[k] = 0.f;
-      if (i < HG * D)
+      if (i < GC * D)
         qv[k] = p.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(&qs[0][0])[i])
                          : (&qs[0][0])[i];
     }
@@ -894,7 +979,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int i = tid + k * NTH;
-      if (i < HG * D) (&qs[0][0])[i] = qv[k] * p.qscale;
+      if (i < GC * D) (&qs[0][0])[i] = qv[k] * p.qscale;
     }
     __syncthreads();
   }
@@ -986,7 +1071,8 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
 
   __builtin_amdgcn_s_setprio(3);   // the epilogue and merge end the block's critical path
   // ---- wave epilogue -----------------------------------------------------------
-  float lsum[HG], zsum[HG], mh[HG];
+  // per (query, head) pair vh: its column (vh / HG) 2HG + vh % HG
+  float lsum[GC], zsum[GC], mh[GC];
   {
     float l_ = l_lane, z_ = z_lane;
     l_ += xor16(l_);
@@ -994,13 +1080,14 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
     z_ += xor16(z_);
     z_ += xor32(z_);
 #pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-      lsum[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_), hh));
-      zsum[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, z_), hh));
-      mh[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_lane), hh));
+    for (int vh = 0; vh < GC; ++vh) {
+      const int col = (vh / HG) * 2 * HG + vh % HG;
+      lsum[vh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_), col));
+      zsum[vh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, z_), col));
+      mh[vh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_lane), col));
     }
   }
-  finish_unit<D, HG, NW>(p, acc, mh, lsum, zsum, arena, last_block, b, qi, h, split);
+  finish_unit<D, HG, NW, QN>(p, acc, mh, lsum, zsum, arena, last_block, b, qi, h, split);
 }
 
 // ---- rotary keys, GQA group of 4: dense scores on v_mfma_f32_4x4x1_16b_f32 ----
@@ -1522,24 +1609,34 @@ __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
 }
 
 
+// rows: grid rows (batch * queries / qn); qn: queries per block (2: GQA 4,
+// keys without rotation)
 template <int KB, int VB, int D, bool ROPE>
-hipError_t by_hg(const MfmaParams& p, int hg, int batch, hipStream_t st) {
-  dim3 grid(p.splits, p.kv_heads, batch);
+hipError_t by_hg(const MfmaParams& p, int hg, int rows, int qn, hipStream_t st) {
+  dim3 grid(p.splits, p.kv_heads, rows);
   switch (hg) {
     case 1: hipLaunchKernelGGL((kivi_mfma_kernel<KB, VB, D, 1, ROPE>), grid, dim3(64 * kivi_waves(KB, VB, D, 1, ROPE)), 0, st, p); break;
     case 2: hipLaunchKernelGGL((kivi_mfma_kernel<KB, VB, D, 2, ROPE>), grid, dim3(64 * kivi_waves(KB, VB, D, 2, ROPE)), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((kivi_mfma_kernel<KB, VB, D, 4, ROPE>), grid, dim3(64 * kivi_waves(KB, VB, D, 4, ROPE)), 0, st, p); break;
+    case 4:
+      if constexpr (!ROPE) {
+        if (qn == 2) {
+          hipLaunchKernelGGL((kivi_mfma_kernel<KB, VB, D, 4, ROPE, 2>), grid, dim3(64 * kivi_waves(KB, VB, D, 4, ROPE)), 0, st, p);
+          break;
+        }
+      }
+      hipLaunchKernelGGL((kivi_mfma_kernel<KB, VB, D, 4, ROPE>), grid, dim3(64 * kivi_waves(KB, VB, D, 4, ROPE)), 0, st, p);
+      break;
     default: hipLaunchKernelGGL((kivi_mfma_kernel<KB, VB, D, 8, ROPE>), grid, dim3(64 * kivi_waves(KB, VB, D, 8, ROPE)), 0, st, p); break;
   }
   return hipGetLastError();
 }
 
 template <int KB, int VB>
-hipError_t by_d(const MfmaParams& p, int d, int hg, int batch, hipStream_t st) {
+hipError_t by_d(const MfmaParams& p, int d, int hg, int rows, int qn, hipStream_t st) {
   switch (d) {
-    case 64: return by_hg<KB, VB, 64, false>(p, hg, batch, st);
-    case 128: return by_hg<KB, VB, 128, false>(p, hg, batch, st);
-    default: return by_hg<KB, VB, 256, false>(p, hg, batch, st);
+    case 64: return by_hg<KB, VB, 64, false>(p, hg, rows, qn, st);
+    case 128: return by_hg<KB, VB, 128, false>(p, hg, rows, qn, st);
+    default: return by_hg<KB, VB, 256, false>(p, hg, rows, qn, st);
   }
 }
 
@@ -1550,7 +1647,7 @@ hipError_t by_d_rope(const MfmaParams& p, int d, int hg, int batch, hipStream_t 
     else hipLaunchKernelGGL((rope4_kernel<128, kRopeWaves>), grid, dim3(64 * kRopeWaves), 0, st, p);
     return hipGetLastError();
   }
-  return d == 64 ? by_hg<2, 2, 64, true>(p, hg, batch, st) : by_hg<2, 2, 128, true>(p, hg, batch, st);
+  return d == 64 ? by_hg<2, 2, 64, true>(p, hg, batch, 1, st) : by_hg<2, 2, 128, true>(p, hg, batch, 1, st);
 }
 
 }  // namespace
@@ -1610,8 +1707,12 @@ hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t st) {
   // several queries per sequence: batch * nq rows share the chip, so the
   // split count is planned for that many rows (never more splits than the
   // one-query plan, whose workspace nq copies of hold the partials)
+  // two queries per block: GQA 4, keys without rotation, an even number of
+  // queries whose tokens are all in the ring (every page visible to both)
+  const int qn = (nq >= 2 && nq % 2 == 0 && g.hg == 4 && a.rope_theta == 0.0 &&
+                  a.tokens - nq >= kivi_quantised(a.tokens, g.residual)) ? 2 : 1;
   Geometry rows = g;
-  rows.batch = g.batch * nq;
+  rows.batch = g.batch * nq / qn;
   const MfmaPlan pl = mfma_plan(rows, a.tokens, a.requested_splits);
   MfmaParams p{};
   p.pm = a.pm;
@@ -1643,11 +1744,11 @@ hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t st) {
     p.v_new = static_cast<const uint8_t*>(a.v_new);
     p.new_tok = a.tokens - 1;
   }
-  const int grid_rows = g.batch * nq;
+  const int grid_rows = g.batch * nq / qn;
   if (a.rope_theta > 0.0) return by_d_rope(p, g.d, g.hg, grid_rows, st);
-  if (g.bits == 2) return by_d<2, 2>(p, g.d, g.hg, grid_rows, st);
-  return g.vbits == 2 ? by_d<4, 2>(p, g.d, g.hg, grid_rows, st)
-                      : by_d<4, 4>(p, g.d, g.hg, grid_rows, st);
+  if (g.bits == 2) return by_d<2, 2>(p, g.d, g.hg, grid_rows, qn, st);
+  return g.vbits == 2 ? by_d<4, 2>(p, g.d, g.hg, grid_rows, qn, st)
+                      : by_d<4, 4>(p, g.d, g.hg, grid_rows, qn, st);
 }
 
 }  // namespace kvq

@@ -79,8 +79,8 @@ __device__ __forceinline__ void store_partial(float* part_rh, int splits, int sp
 
 // The last block merges every (query row, split) of sequence b, KV head h
 // and writes the outputs out[r][h*HG + hh][c]; its own state (row `row`,
-// split `split`) comes from registers. Then it clears what it read and the
-// counter. partials: [rows][q_heads][splits][D + 2].
+// split `split`) comes from registers (row -1: none; every slot is read).
+// Then it clears what it read and the counter. partials: [rows][q_heads][splits][D + 2].
 template <int D, int HG, int NTH>
 __device__ __forceinline__ void merge_partials(float* partials, float* out, int* counter, int q_heads,
                                                int splits, int nq, int b, int h, int row, int split,

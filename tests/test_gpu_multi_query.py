@@ -36,6 +36,12 @@ CASES = [
     (synth.KIVI, 2, 128, 4, torch.bfloat16, 32, 100, 0.0, 0, 36),        # n_q = ring tokens
     (synth.KIVI, 2, 128, 4, torch.bfloat16, 128, 90, 0.0, 0, 7),         # no pages yet
     (synth.KIVI, 2, 128, 4, torch.bfloat16, 32, 100, 0.0, 0, 37),        # one more: in a page
+    # GQA 4 without rotary keys, an even n_q in the ring: two queries per
+    # block (key columns and value rows of both in one product)
+    (synth.KIVI, 4, 128, 4, torch.bfloat16, 64, 400, 0.0, 3, 6),
+    (synth.KIVI, 2, 128, 4, torch.bfloat16, 128, 900, 0.0, 1, 2),        # one split: no merge
+    (synth.KIVI, 2, 64, 4, torch.bfloat16, 64, 333, 0.0, 5, 8),
+    (synth.KIVI, 2, 128, 4, torch.bfloat16, 40, 1000, 0.0, 0, 40),       # n_q = ring tokens
     # queries whose tokens are in pages (chunks longer than the ring): each
     # row's last page masked after its own token
     (synth.KIVI, 2, 128, 4, torch.bfloat16, 32, 300, 10000.0, 0, 70),    # rotary, GQA 4

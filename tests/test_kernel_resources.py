@@ -82,10 +82,11 @@ def test_matrix_core_decodes_use_no_scratch(kernels, stem):
 # granules of 8: two eight-wave blocks per CU (4 waves per SIMD) -> 128;
 # three four-wave blocks (3 per SIMD) -> 168; one eight-wave block -> 256.
 BUDGETS = [
-    ("kivi_mfma_kernelILi2ELi2ELi128ELi4ELb0E", 128),   # KIVI 2-bit, GQA 4, d 128
-    ("kivi_mfma_kernelILi4ELi2ELi128ELi4ELb0E", 256),   # 4-bit keys, 2-bit values (88 KB LDS)
-    ("kivi_mfma_kernelILi4ELi4ELi128ELi4ELb0E", 168),   # KIVI 4-bit
-    ("rope4_kernelILi128ELi4E", 168),                   # rotary keys, GQA 4
+    ("kivi_mfma_kernelILi2ELi2ELi128ELi4ELb0ELi1E", 128),   # KIVI 2-bit, GQA 4, d 128
+    ("kivi_mfma_kernelILi4ELi2ELi128ELi4ELb0ELi1E", 256),   # 4-bit keys, 2-bit values (88 KB LDS)
+    ("kivi_mfma_kernelILi4ELi4ELi128ELi4ELb0ELi1E", 168),   # KIVI 4-bit
+    ("kivi_mfma_kernelILi2ELi2ELi128ELi4ELb0ELi2E", 256),   # 2-bit, two queries per block (one per CU)
+    ("rope4_kernelILi128ELi4E", 168),                       # rotary keys, GQA 4
 ]
 
 
