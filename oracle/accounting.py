@@ -15,7 +15,7 @@
 
 from fractions import Fraction
 
-KIVI, SYM_TOKEN, FP8_E4M3, BF16_CACHE, FP8_E5M2 = 0, 1, 2, 3, 4
+KIVI, SYM_TOKEN, FP8_E4M3, BF16_CACHE, FP8_E5M2, FP8K_SYMV = 0, 1, 2, 3, 4, 5
 PAGE = 32
 
 
@@ -79,6 +79,10 @@ def page_bytes(scheme, head_dim, bits, v_bits=None, outliers=0):
         return PAGE * d + PAGE * d
     if scheme == BF16_CACHE:
         return PAGE * d * 2 + PAGE * d * 2      # 16-bit K rows + V cols
+    if scheme == FP8K_SYMV:
+        # FP8 K rows + symmetric V codes at v_bits + one V scale per token,
+        # the scales padded to 256 bytes (pages stay 256-byte multiples)
+        return PAGE * d + PAGE * d * vb // 8 + 256
     raise ValueError(scheme)
 
 

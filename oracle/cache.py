@@ -17,6 +17,10 @@ chunked by construction:
   Cache.", Workshop: rounded before it enters the cache).
 * BF16_CACHE: every token is stored as bfloat16 as it arrives (the 16-bit
   baseline of "Quantizing the KV cache", "The other big memory user").
+* FP8K_SYMV: keys and values in different cache types ("Quantizing the KV
+  cache", How the KV cache is quantized: separate key and value cache
+  types): each token's key encoded as FP8 E4M3 with the KV head's static key
+  scale and its value symmetric per token at v_bits, as it arrives.
 
 Decode attention (``decode``) dequantises in float64, applies the rotary
 embedding to keys at their positions and to the query at position T-1 when
@@ -31,9 +35,9 @@ import numpy as np
 
 from . import accounting, attention, codec, layout, rope
 
-KIVI, SYM_TOKEN, FP8_E4M3, BF16_CACHE, FP8_E5M2 = (
+KIVI, SYM_TOKEN, FP8_E4M3, BF16_CACHE, FP8_E5M2, FP8K_SYMV = (
     accounting.KIVI, accounting.SYM_TOKEN, accounting.FP8_E4M3, accounting.BF16_CACHE,
-    accounting.FP8_E5M2)
+    accounting.FP8_E5M2, accounting.FP8K_SYMV)
 PAGE = 32
 
 
@@ -48,7 +52,9 @@ class OracleCache:
 
     def __init__(self, scheme, bits, layers, batch, kv_heads, head_dim, capacity,
                  residual=0, in_dtype="bf16", v_bits=None, outliers=0):
-        if scheme != KIVI:
+        if scheme == FP8K_SYMV:
+            assert residual == 0 and bits == 8 and v_bits in (2, 3, 4, 8) and not outliers
+        elif scheme != KIVI:
             assert residual == 0 and v_bits in (None, bits) and not outliers
         self.outliers = outliers          # KIVI: dense-and-sparse with one outlier per vector
         self.scheme, self.bits, self.layers, self.batch = scheme, bits, layers, batch
@@ -69,6 +75,11 @@ class OracleCache:
         k_new, v_new = np.asarray(k_new), np.asarray(v_new)
         assert k_new.shape == v_new.shape and k_new.shape[0] == self.batch
         assert self.tokens(layer) + k_new.shape[1] <= self.capacity
+        if self.scheme == FP8K_SYMV:   # a static key scale only
+            ks = np.asarray(k_scale, np.float32)
+            if self.k_scale[layer] is not None:
+                assert np.array_equal(ks, self.k_scale[layer])
+            self.k_scale[layer] = ks
         if self.scheme in (FP8_E4M3, FP8_E5M2):
             ks = np.asarray(k_scale, np.float32)
             vs = np.asarray(v_scale, np.float32)
@@ -139,6 +150,8 @@ class OracleCache:
                     pb, pm = layout.sym_page(k32, v32, self.bits, n)
                 elif self.scheme == BF16_CACHE:
                     pb, pm = layout.bf16_page(k32, v32, n)
+                elif self.scheme == FP8K_SYMV:
+                    pb, pm = layout.fp8k_symv_page(k32, v32, self.k_scale[layer][h], self.v_bits, n)
                 else:
                     pb, pm = layout.fp8_page(k32, v32, self.k_scale[layer][h],
                                              self.v_scale[layer][h], n, self.fp8_format())
@@ -184,6 +197,11 @@ class OracleCache:
         elif self.scheme == BF16_CACHE:
             kh[:] = codec.bf16_decode(codec.bf16_encode(K))
             vh[:] = codec.bf16_decode(codec.bf16_encode(V))
+        elif self.scheme == FP8K_SYMV:
+            ksc = self.k_scale[layer][None, :, None, None]
+            kh[:] = codec.fp8_dequantize(codec.fp8_quantize(K, ksc, "e4m3"), ksc, "e4m3")
+            vc, vs = codec.sym_quantize(V, self.v_bits, axis=3)
+            vh[:] = codec.sym_dequantize(vc, vs, axis=3)
         elif self.scheme == SYM_TOKEN:
             kc, ks = codec.sym_quantize(K, self.bits, axis=3)
             vc, vs = codec.sym_quantize(V, self.bits, axis=3)

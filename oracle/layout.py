@@ -135,3 +135,20 @@ def fp8_page(k32, v32, k_scale, v_scale, n_valid, fmt="e4m3"):
     mask = np.concatenate([np.repeat(np.where(valid, 0xFF, 0).astype(np.uint8), d),
                            np.tile(np.where(valid, 0xFF, 0).astype(np.uint8), d)])
     return buf, mask
+
+
+def fp8k_symv_page(k32, v32, k_scale, v_bits, n_valid):
+    """Keys and values in different cache types ("Quantizing the KV cache",
+    How the KV cache is quantized: separate key and value cache types): the
+    key rows of an FP8 E4M3 page with the KV head's scalar key scale, then
+    the value columns and per-token value scales of a symmetric page at
+    v_bits, then 128 bytes of padding (undefined) that keep the page a
+    multiple of 256 bytes; tokens >= n_valid undefined."""
+    d = k32.shape[1]
+    fb, fm = fp8_page(k32, v32, k_scale, np.float32(1), n_valid, "e4m3")
+    sb, sm = sym_page(k32, v32, v_bits, n_valid)
+    k_end = PAGE * d                        # FP8 key rows: one byte per value
+    v_start = PAGE * d * v_bits // 8 + 4 * PAGE   # after sym_page's key codes and scales
+    pad = np.zeros(128, np.uint8)
+    return (np.concatenate([fb[:k_end], sb[v_start:], pad]),
+            np.concatenate([fm[:k_end], sm[v_start:], pad]))

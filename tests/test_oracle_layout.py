@@ -232,3 +232,65 @@ def test_three_bit_page_sizes(d):
         n = acc.page_bytes(acc.KIVI, d, kb, vb)
         assert n == 32 * d * kb // 8 + 8 * d + 32 * d * vb // 8 + 256
         assert (n % 256 == 0) == (kb == vb or d >= 64)
+
+
+@pytest.mark.parametrize("vb", [2, 3, 4, 8])
+def test_fp8k_symv_page_halves(vb):
+    """Keys and values in different cache types: the page is the FP8 page's key
+    rows (one E4M3 byte per value, the key scale of the KV head) followed by
+    the symmetric page's value columns and value scales; each half decoded
+    here from the bytes by hand, with a partial page's undefined tokens masked."""
+    rng = np.random.default_rng(11 + vb)
+    d, n = 64, 29
+    k = rng.standard_normal((32, d)).astype(F32) * 3
+    v = rng.standard_normal((32, d)).astype(F32)
+    ks = F32(0.0125)
+    buf, mask = layout.fp8k_symv_page(k, v, ks, vb, n)
+    assert buf.size == mask.size == acc.page_bytes(acc.FP8K_SYMV, d, 8, vb) == 32 * d + 32 * d * vb // 8 + 256
+    assert buf.size % 256 == 0
+    # key rows: byte (t, c) is the E4M3 code of k[t, c] / ks for t < n, undefined after
+    kb = buf[:32 * d].reshape(32, d)
+    assert np.array_equal(kb[:n], codec.fp8_quantize(k[:n], ks, "e4m3"))
+    assert np.all(mask[:n * d] == 0xFF) and np.all(mask[n * d:32 * d] == 0)
+    # value columns: channel c's 32 fields of vb bits (two's complement), then
+    # one float32 scale per token
+    vbytes = buf[32 * d:32 * d + 32 * d * vb // 8]
+    f = layout.unpack_fields(vbytes, vb, 32 * d).reshape(d, 32).astype(np.int64)
+    f = np.where(f >= 1 << (vb - 1), f - (1 << vb), f)
+    vs = buf[32 * d + 32 * d * vb // 8:32 * d + 32 * d * vb // 8 + 128].view(F32)
+    c, s = codec.sym_quantize(v, vb, axis=1)
+    assert np.array_equal(f.T[:n], c[:n]) and np.array_equal(vs[:n], s[:n])
+    sm = mask[32 * d + 32 * d * vb // 8:]
+    assert np.all(vs[n:] == 0) and np.all(sm[:4 * n] == 0xFF) and np.all(sm[4 * n:] == 0)   # (padding: mask 0)
+    # each value is within half a step of its code's value (symmetric rounding)
+    assert np.all(np.abs(f.T[:n] * vs[:n, None].astype(np.float64) - v[:n]) <= vs[:n, None] / 2 + 1e-7)
+
+
+def test_fp8k_symv_cache_dequant_matches_bytes():
+    """dequantized() of a cache with FP8 keys and symmetric values equals the
+    byte image decoded by hand (keys: code value x key scale; values: field x
+    token scale), for tokens across several appends and a partial last page."""
+    rng = np.random.default_rng(12)
+    B, H, d, vb = 2, 2, 32, 4
+    c = OracleCache(acc.FP8K_SYMV, 8, 1, B, H, d, 96, in_dtype="f32", v_bits=vb)
+    scales = np.array([0.02, 0.05], F32)
+    k = rng.standard_normal((B, 70, H, d)).astype(F32)
+    v = rng.standard_normal((B, 70, H, d)).astype(F32)
+    for a, z in ((0, 33), (33, 34), (34, 70)):
+        c.append(0, k[:, a:z], v[:, a:z], k_scale=scales)
+    kh, vh = c.dequantized(0)
+    ps = acc.page_bytes(acc.FP8K_SYMV, d, 8, vb)
+    for b in range(B):
+        for h in range(H):
+            buf, _ = c.slab_image(0, b, h)
+            for p in range(3):
+                n = min(32, 70 - 32 * p)
+                pg = buf[p * ps:(p + 1) * ps]
+                kc = pg[:32 * d].reshape(32, d)[:n]
+                assert np.array_equal(kh[b, h, 32 * p:32 * p + n],
+                                      codec.fp8_dequantize(kc, scales[h], "e4m3"))
+                f = layout.unpack_fields(pg[32 * d:32 * d + 32 * d * vb // 8], vb, 32 * d)
+                f = f.reshape(d, 32).astype(np.int64)
+                f = np.where(f >= 8, f - 16, f).T[:n]
+                sc = pg[32 * d + 32 * d * vb // 8:32 * d + 32 * d * vb // 8 + 128].view(F32)[:n]
+                assert np.array_equal(vh[b, h, 32 * p:32 * p + n], f * sc[:, None].astype(np.float64))
