@@ -63,10 +63,11 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 8   /* 3: ragged-batch entry points; 4: several queries per sequence;
+#define KVQ_ABI_VERSION 9   /* 3: ragged-batch entry points; 4: several queries per sequence;
                                5: decode without a caller workspace; 6: sparse outliers;
                                7: paged caches (block tables);
-                               8: one-token append fused with decode */
+                               8: one-token append fused with decode;
+                               9: keys and values in different cache types */
 
 /* Exported entry points (the library is built with hidden visibility). */
 #if defined(__GNUC__)
@@ -103,12 +104,19 @@ extern "C" {
  * KVQ_BF16_CACHE: no quantisation, every value stored as bfloat16 (the
  *   16-bit cache the pages compare the quantised ones against, [QKV] "The
  *   other big memory user"); the baseline for measuring what 2/4/8-bit codes
- *   save. bits must be 16. */
+ *   save. bits must be 16.
+ * KVQ_FP8K_SYMV: keys and values in different cache types ([QKV] "How the KV
+ *   cache is quantized": separate key and value cache types): keys as in
+ *   KVQ_FP8_E4M3 (static per-(layer, KV head) key scale), values as in
+ *   KVQ_SYM_TOKEN at v_bits (one scale per (token, KV head)); every token is
+ *   encoded on arrival. bits must be 8; v_bits in {2,3,4,8} (0 means 8; 3
+ *   needs head_dim >= 64). */
 #define KVQ_KIVI       0
 #define KVQ_SYM_TOKEN  1
 #define KVQ_FP8_E4M3   2
 #define KVQ_BF16_CACHE 3
 #define KVQ_FP8_E5M2   4
+#define KVQ_FP8K_SYMV  5
 
 /* ---- dtypes (K/V input + residual ring, and the query) ------------------ */
 #define KVQ_F32   0
@@ -154,7 +162,9 @@ typedef struct kvq_config {
                             costs keys more than values, [QKV] "How the KV
                             cache is quantized", INT8 / INT4 blocks with
                             separate key and value cache types); 0 = `bits`.
-                            Other schemes: 0 or equal to `bits`.          */
+                            FP8K_SYMV: bits of the symmetric value codes,
+                            2, 3, 4 or 8 (0 = 8). Other schemes: 0 or
+                            equal to `bits`.                               */
   int32_t  outliers;     /* KIVI: 1 = dense-and-sparse pages (each key
                             channel's 32 tokens and each value token keep
                             their largest-magnitude value exactly in a side
@@ -208,6 +218,11 @@ typedef struct kvq_config {
  * BF16_CACHE page (128*d bytes), P = ceil(max_tokens/32):
  *   Kc  K rows, bfloat16 per value (16-bit fields)   64*d
  *   Vc  V cols, bfloat16 per value                   64*d
+ * FP8K_SYMV page (32*d + 4*d*bv + 256 bytes), P = ceil(max_tokens/32):
+ *   Kc  K rows, one FP8 E4M3 byte per value            32*d
+ *   Vc  V cols, bv-bit two's-complement codes          32*d*bv/8
+ *   Vs  fp32 scale per token                           128
+ *   (then 128 bytes of padding, unspecified)
  *
  * Which tokens are quantised (KIVI), for a cache holding T tokens:
  *   q(T) = 32*floor(max(0, T-R)/32) tokens live in pages [0, q(T)/32); the
@@ -261,7 +276,8 @@ KVQ_API int64_t kvq_cache_bytes(const kvq_config* cfg, int64_t tokens, int32_t k
  *   k_new, v_new device [batch][new_tokens][kv_heads][head_dim], in_dtype
  *   k_scale,
  *   v_scale      FP8 (either format) only: device fp32 [kv_heads], this layer's per-head
- *                scales (must be > 0); NULL for the other schemes
+ *                scales (must be > 0); FP8K_SYMV: k_scale only (v_scale
+ *                ignored); NULL for the other schemes
  * Requires past_tokens + new_tokens <= max_tokens (else KVQ_ERR_CAPACITY).
  * new_tokens == 0 is a no-op. Appending in any chunking (one call of T tokens
  * or T calls of one token) leaves identical bytes in every defined field.
@@ -305,7 +321,8 @@ KVQ_API int32_t kvq_quantize_append_ragged(const kvq_config* cfg, void* cache, i
  * (2i, 2i+1) turned by angle pos * theta^(-2i/head_dim).  [KVQ] Summary.
  *   q          device [batch][q_heads][head_dim], q_dtype
  *   k_scale,
- *   v_scale    FP8 only: as for append; NULL otherwise
+ *   v_scale    FP8 only: as for append (FP8K_SYMV: k_scale only, v_scale
+ *              ignored); NULL otherwise
  *   out        device fp32 [batch][q_heads][head_dim]
  *   workspace  device, >= kvq_cache_bytes(cfg, tokens, KVQ_BYTES_WORKSPACE);
  *              zero-filled before its first use. It begins with one int32

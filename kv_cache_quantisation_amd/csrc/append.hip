@@ -412,7 +412,9 @@ __global__ __launch_bounds__(64) void ring_write_kernel(AppendParams p) {
 // ---- SYM_TOKEN: encode the new tokens of one page per block -------------------
 // grid = (pages touched, kv_heads, batch). Codes narrower than a byte share
 // 32-bit words across tokens, so the page's new rows are staged in LDS first.
-template <int D, int BITS, int IB>
+// WITH_K false: the values only (keys in another cache type, written by
+// another kernel)
+template <int D, int BITS, int IB, bool WITH_K = true>
 __global__ __launch_bounds__(kThreads) void token_append_kernel(AppendParams p) {
   constexpr int LD = D + 1;
   constexpr int FPW = 32 / BITS;
@@ -438,13 +440,14 @@ __global__ __launch_bounds__(kThreads) void token_append_kernel(AppendParams p) 
 
   // every load of the thread is issued before the first LDS write (threads
   // past the last chunk load chunk 0 again and do not store it)
-  constexpr int SPT = (2 * kPage * CHUNKS + kThreads - 1) / kThreads;   // chunks per thread, at most
+  constexpr int HALVES = WITH_K ? 2 : 1;   // K and V rows, or V rows only
+  constexpr int SPT = (HALVES * kPage * CHUNKS + kThreads - 1) / kThreads;   // chunks per thread, at most
   uint4 chunk[SPT];
-  const int nch = 2 * (hi - lo) * CHUNKS;
+  const int nch = HALVES * (hi - lo) * CHUNKS;
 #pragma unroll
   for (int k = 0; k < SPT; ++k) {
     const int i = tid + k * kThreads < nch ? tid + k * kThreads : 0;
-    const int which = i / ((hi - lo) * CHUNKS);
+    const int which = WITH_K ? i / ((hi - lo) * CHUNKS) : 1;
     const int r = lo + (i / CHUNKS) % (hi - lo);
     const int64_t j = page * kPage + r - past;
     const uint8_t* src = (which ? p.v_new : p.k_new) +
@@ -455,7 +458,7 @@ __global__ __launch_bounds__(kThreads) void token_append_kernel(AppendParams p) 
   for (int k = 0; k < SPT; ++k) {
     const int i = tid + k * kThreads;
     if (i < nch) {
-      const int which = i / ((hi - lo) * CHUNKS);
+      const int which = WITH_K ? i / ((hi - lo) * CHUNKS) : 1;
       const int r = lo + (i / CHUNKS) % (hi - lo);
       const int c = i % CHUNKS;
       stage_chunk<IB>(chunk[k], (which ? vtile : ktile) + r * LD, c);
@@ -466,7 +469,7 @@ __global__ __launch_bounds__(kThreads) void token_append_kernel(AppendParams p) 
   // one scale per (token, head) for K and for V: s = max|x| / Q
   for (int i = tid; i < 2 * kPage; i += kThreads) {
     const int which = i / kPage, r = i % kPage;
-    if (r < lo || r >= hi) continue;
+    if (r < lo || r >= hi || (!WITH_K && which == 0)) continue;
     const float* row = (which ? vtile : ktile) + r * LD;
     float a = fabsf(row[0]);
     for (int c = 1; c < D; ++c) a = fmaxf(a, fabsf(row[c]));
@@ -486,7 +489,7 @@ __global__ __launch_bounds__(kThreads) void token_append_kernel(AppendParams p) 
     // whole words of the token's row); V cols one column (32 tokens, 3
     // words) per thread, updating only the fields of tokens [lo, hi)
     constexpr int GPR = D / 32;
-    for (int i = tid; i < (hi - lo) * GPR; i += kThreads) {
+    for (int i = tid; i < (WITH_K ? (hi - lo) * GPR : 0); i += kThreads) {
       const int r = lo + i / GPR, gi = i % GPR;
       uint32_t wd[3] = {0u, 0u, 0u}, m[3] = {0u, 0u, 0u};
 #pragma unroll
@@ -507,7 +510,7 @@ __global__ __launch_bounds__(kThreads) void token_append_kernel(AppendParams p) 
     }
     return;
   }
-  for (int i = tid; i < (hi - lo) * ROW_WORDS; i += kThreads) {
+  for (int i = tid; i < (WITH_K ? (hi - lo) * ROW_WORDS : 0); i += kThreads) {
     const int r = lo + i / ROW_WORDS;
     const int c0 = (i % ROW_WORDS) * FPW;
     uint32_t word = 0;
@@ -551,7 +554,9 @@ __global__ __launch_bounds__(kThreads) void token_append_kernel(AppendParams p) 
 // page) flat, so that neighbouring blocks write neighbouring pages of one
 // slab; grid y, z = KV head, sequence. Tokens outside [past, past + n) of a
 // page are neither read nor written.
-template <int SCHEME, int D, int IB>
+// WITH_V false: the keys only (values in another cache type, written by
+// another kernel)
+template <int SCHEME, int D, int IB, bool WITH_V = true>
 __global__ __launch_bounds__(kThreads) void byte_append_kernel(AppendParams p, int64_t pages) {
   constexpr int CB = SCHEME == KVQ_BF16_CACHE ? 2 : 1;   // bytes per code
   constexpr int CH = D * IB / 16;                          // 16-byte chunks per input row
@@ -586,7 +591,7 @@ __global__ __launch_bounds__(kThreads) void byte_append_kernel(AppendParams p, i
     kin[i] = rk >= lo && rk < hi
                  ? *reinterpret_cast<const uint4*>(p.k_new + row0 + rk * row_stride + kc * 16)
                  : make_uint4(0, 0, 0, 0);
-    vin[i] = rv >= lo && rv < hi
+    vin[i] = WITH_V && rv >= lo && rv < hi
                  ? *reinterpret_cast<const uint4*>(p.v_new + row0 + rv * row_stride + vc * 16)
                  : make_uint4(0, 0, 0, 0);
   }
@@ -608,7 +613,7 @@ __global__ __launch_bounds__(kThreads) void byte_append_kernel(AppendParams p, i
   bool exact = false;
   if constexpr (SCHEME != KVQ_BF16_CACHE) {
     ks = p.k_scale[h];
-    vs = p.v_scale[h];
+    vs = WITH_V ? p.v_scale[h] : 1.0f;
     kr = 1.0f / ks;
     vr = 1.0f / vs;
     exact = !(recip_usable(kr) && recip_usable(vr));
@@ -645,6 +650,7 @@ __global__ __launch_bounds__(kThreads) void byte_append_kernel(AppendParams p, i
     }
   }
 
+  if constexpr (!WITH_V) return;
   // V cols: codes of tokens 4vq..4vq+3 of each of the chunk's channels
   float fv[4][EPC];
 #pragma unroll
@@ -750,9 +756,31 @@ hipError_t run_token(const AppendArgs& a, const AppendParams& p, hipStream_t st)
   return hipGetLastError();
 }
 
+// Keys and values in different cache types: FP8 E4M3 key rows (the byte-code
+// kernel, keys only), symmetric value columns and scales (the symmetric
+// kernel, values only); the two write disjoint bytes of the pages.
+template <int D, int IB>
+hipError_t run_fp8k_symv(const AppendArgs& a, const AppendParams& p, hipStream_t st) {
+  const Geometry& g = a.g;
+  const int64_t pages = a.seq_past ? (a.n + kPage - 1) / kPage + 1
+                                   : (a.past + a.n - 1) / kPage - a.past / kPage + 1;
+  constexpr int64_t TPU = 8 * (D * IB / 16);
+  dim3 kgrid(static_cast<unsigned>((pages * TPU + kThreads - 1) / kThreads), g.kv_heads, g.batch);
+  hipLaunchKernelGGL((byte_append_kernel<KVQ_FP8_E4M3, D, IB, false>), kgrid, dim3(kThreads), 0, st, p, pages);
+  dim3 vgrid(static_cast<unsigned>(pages), g.kv_heads, g.batch);
+  switch (g.vbits) {
+    case 2: hipLaunchKernelGGL((token_append_kernel<D, 2, IB, false>), vgrid, dim3(kThreads), 0, st, p); break;
+    case 3: hipLaunchKernelGGL((token_append_kernel<D, 3, IB, false>), vgrid, dim3(kThreads), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((token_append_kernel<D, 4, IB, false>), vgrid, dim3(kThreads), 0, st, p); break;
+    default: hipLaunchKernelGGL((token_append_kernel<D, 8, IB, false>), vgrid, dim3(kThreads), 0, st, p); break;
+  }
+  return hipGetLastError();
+}
+
 template <int D, int IB>
 hipError_t dispatch_bits(const AppendArgs& a, const AppendParams& p, hipStream_t st) {
   const Geometry& g = a.g;
+  if (g.scheme == KVQ_FP8K_SYMV) return run_fp8k_symv<D, IB>(a, p, st);
   if (g.scheme == KVQ_FP8_E4M3) return run_token<KVQ_FP8_E4M3, D, 8, IB>(a, p, st);
   if (g.scheme == KVQ_FP8_E5M2) return run_token<KVQ_FP8_E5M2, D, 8, IB>(a, p, st);
   if (g.scheme == KVQ_BF16_CACHE) return run_token<KVQ_BF16_CACHE, D, 16, IB>(a, p, st);

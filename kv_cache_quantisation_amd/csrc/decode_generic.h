@@ -129,6 +129,10 @@ __device__ __forceinline__ void rope_pair(float& x0, float& x1, int64_t pos, dou
 
 template <int SCHEME, int BITS, int VB, int D, int HG>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
+  // cache types of the key and of the value half (FP8K_SYMV: FP8 E4M3 keys,
+  // symmetric per-token values; the other schemes use one type for both)
+  constexpr int KSCH = SCHEME == KVQ_FP8K_SYMV ? KVQ_FP8_E4M3 : SCHEME;
+  constexpr int VSCH = SCHEME == KVQ_FP8K_SYMV ? KVQ_SYM_TOKEN : SCHEME;
   constexpr int CPL = D >= 64 ? D / 64 : 1;  // channels per lane in the P.V phase
   constexpr int LPC = D / CPL;                // lanes per token subset (64 or 32)
   constexpr int TSUB = 64 / LPC;              // token subsets (1, or 2 when D == 32)
@@ -191,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     __syncthreads();
   }
   {
-    const float ks_h = is_fp8(SCHEME) ? p.k_scale[h] : 1.0f;
+    const float ks_h = is_fp8(KSCH) ? p.k_scale[h] : 1.0f;
     const float mult = p.qscale * ks_h;
     for (int i = tid; i < HG * D / 2; i += kThreads) {
       const int g = i / (D / 2), pr = i % (D / 2);
@@ -284,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         const uint32_t* kw = reinterpret_cast<const uint32_t*>(pg + p.off_kc) +
                              tok * (D * BITS / 32) + hf * NWORD;
         float kst = 1.0f;
-        if constexpr (SCHEME == KVQ_SYM_TOKEN)
+        if constexpr (KSCH == KVQ_SYM_TOKEN)
           kst = reinterpret_cast<const float*>(pg + p.off_ks)[tok];
         if constexpr (BITS == 3) {
           // 3-bit fields straddle words: 8 channels at a time from the row
@@ -292,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
           for (int c0 = hf * HALF; c0 < hf * HALF + HALF; c0 += 8) {
             float kv[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) kv[j] = code3_value<SCHEME>(field_at<3>(krow, c0 + j));
+            for (int j = 0; j < 8; ++j) kv[j] = code3_value<KSCH>(field_at<3>(krow, c0 + j));
             if (rope) {
               if constexpr (SCHEME == KVQ_KIVI) {
 #pragma unroll
@@ -320,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
           const int c0 = hf * HALF + wi * FPW;
           float kv[FPW];
 #pragma unroll
-          for (int j = 0; j < FPW; ++j) kv[j] = code_value<SCHEME, BITS>(w, j);
+          for (int j = 0; j < FPW; ++j) kv[j] = code_value<KSCH, BITS>(w, j);
           if (rope) {
             if constexpr (SCHEME == KVQ_KIVI) {
 #pragma unroll
@@ -384,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
             vdo = reinterpret_cast<const float*>(pg + p.off_vo)[tok] - vz;
             if (hf == 0) voi[tok] = pg[p.off_vi + tok];
           }
-        } else if constexpr (SCHEME == KVQ_SYM_TOKEN) {
+        } else if constexpr (VSCH == KVQ_SYM_TOKEN) {
           vsc = reinterpret_cast<const float*>(pg + p.off_vs)[tok];
         }
       }
@@ -417,7 +421,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
             const uint32_t* col = reinterpret_cast<const uint32_t*>(pg + p.off_vc) + c * COLW;
             for (int j = 0; j < TPS; ++j) {
               const int t = ts * TPS + j;
-              const float cv = code3_value<SCHEME>(field_at<3>(col, t));
+              const float cv = code3_value<VSCH>(field_at<3>(col, t));
 #pragma unroll
               for (int g = 0; g < HG; ++g) o[g][ci] = fmaf(wp[wave][g][t], cv, o[g][ci]);
             }
@@ -433,7 +437,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
             const uint32_t w = vw[wi];
 #pragma unroll
             for (int j = 0; j < FPWV; ++j) {
-              const float cv = code_value<SCHEME, VB>(w, j);
+              const float cv = code_value<VSCH, VB>(w, j);
               const int t = ts * TPS + wi * FPWV + j;
 #pragma unroll
               for (int g = 0; g < HG; ++g) o[g][ci] = fmaf(wp[wave][g][t], cv, o[g][ci]);
@@ -500,7 +504,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   const int unit = b * p.kv_heads + h;   // one arrival counter for every row of b
   int arrived = 0;
   if (p.splits > 1 && tid == 0) arrived = count_arrival(&p.counters[unit]);
-  const float vsc_h = is_fp8(SCHEME) ? p.v_scale[h] : 1.0f;
+  const float vsc_h = is_fp8(VSCH) ? p.v_scale[h] : 1.0f;
   constexpr int PER = (HG * D + kThreads - 1) / kThreads;
   float own_m[PER], own_l[PER], own_o[PER];
 #pragma unroll

@@ -24,16 +24,22 @@ int32_t validate_config(const kvq_config* cfg) {
   if (cfg->struct_size != sizeof(kvq_config)) return KVQ_ERR_INVALID;
   const kvq_config& c = *cfg;
   if (c.scheme != KVQ_KIVI && c.scheme != KVQ_SYM_TOKEN && c.scheme != KVQ_FP8_E4M3 &&
-      c.scheme != KVQ_FP8_E5M2 && c.scheme != KVQ_BF16_CACHE)
+      c.scheme != KVQ_FP8_E5M2 && c.scheme != KVQ_BF16_CACHE && c.scheme != KVQ_FP8K_SYMV)
     return KVQ_ERR_INVALID;
-  if (c.scheme == KVQ_FP8_E4M3 || c.scheme == KVQ_FP8_E5M2) {
+  if (c.scheme == KVQ_FP8K_SYMV) {   // FP8 keys, symmetric values at v_bits
+    if (c.bits != 8) return KVQ_ERR_INVALID;
+    if (c.v_bits != 0 && (c.v_bits < 1 || c.v_bits > 8)) return KVQ_ERR_INVALID;
+    if (c.v_bits != 0 && c.v_bits != 2 && c.v_bits != 3 && c.v_bits != 4 && c.v_bits != 8)
+      return KVQ_ERR_UNSUPPORTED;
+    if (c.v_bits == 3 && c.head_dim < 64) return KVQ_ERR_UNSUPPORTED;
+  } else if (c.scheme == KVQ_FP8_E4M3 || c.scheme == KVQ_FP8_E5M2) {
     if (c.bits != 8) return KVQ_ERR_INVALID;
   } else if (c.scheme == KVQ_BF16_CACHE) {
     if (c.bits != 16) return KVQ_ERR_INVALID;
   } else if (c.bits != 2 && c.bits != 3 && c.bits != 4 && c.bits != 8) {
     return (c.bits >= 1 && c.bits <= 8) ? KVQ_ERR_UNSUPPORTED : KVQ_ERR_INVALID;
   }
-  if (c.v_bits != 0 && c.v_bits != c.bits) {
+  if (c.v_bits != 0 && c.v_bits != c.bits && c.scheme != KVQ_FP8K_SYMV) {
     if (c.scheme != KVQ_KIVI || c.v_bits < 1 || c.v_bits > 8) return KVQ_ERR_INVALID;
     if ((c.v_bits != 2 && c.v_bits != 3 && c.v_bits != 4) || c.v_bits > c.bits)
       return KVQ_ERR_UNSUPPORTED;
@@ -122,6 +128,14 @@ int32_t make_geometry(const kvq_config& c, Geometry* g) {
       x.off_vs = 2 * codes + 4 * kPage;
       x.off_kz = x.off_vz = -1;
       x.page_bytes = 2 * codes + 8 * kPage;
+      x.ring_slots = 0;
+      break;
+    case KVQ_FP8K_SYMV:   // FP8 K rows, symmetric V cols, V scales (padded to 256 bytes)
+      x.off_kc = 0;
+      x.off_vc = codes;
+      x.off_vs = codes + vcodes;
+      x.off_ks = x.off_kz = x.off_vz = -1;
+      x.page_bytes = codes + vcodes + 256;
       x.ring_slots = 0;
       break;
     default:  // FP8, either format (b = 8), and BF16_CACHE (b = 16): K rows, then V cols
@@ -296,7 +310,8 @@ int32_t kvq_quantize_append(const kvq_config* cfg, void* cache, int32_t layer,
     return KVQ_ERR_CAPACITY;
   if (new_tokens == 0) return KVQ_OK;
   if (!k_new || !v_new) return KVQ_ERR_NULL;
-  if (kvq::is_fp8(cfg->scheme) && (!k_scale || !v_scale)) return KVQ_ERR_NULL;
+  if (kvq::has_key_scale(cfg->scheme) && !k_scale) return KVQ_ERR_NULL;
+  if (kvq::is_fp8(cfg->scheme) && !v_scale) return KVQ_ERR_NULL;
   if (!kvq::aligned16(cache) || !kvq::aligned16(k_new) || !kvq::aligned16(v_new))
     return KVQ_ERR_INVALID;
   kvq::AppendArgs a{};
@@ -333,7 +348,8 @@ int32_t append_ragged(const kvq_config* cfg, void* cache, int32_t layer, const i
   if (new_max > cfg->max_tokens) return KVQ_ERR_CAPACITY;
   if (new_max == 0) return KVQ_OK;
   if (!seq_past || !seq_new || !k_new || !v_new) return KVQ_ERR_NULL;
-  if (kvq::is_fp8(cfg->scheme) && (!k_scale || !v_scale)) return KVQ_ERR_NULL;
+  if (kvq::has_key_scale(cfg->scheme) && !k_scale) return KVQ_ERR_NULL;
+  if (kvq::is_fp8(cfg->scheme) && !v_scale) return KVQ_ERR_NULL;
   if (!kvq::aligned16(cache) || !kvq::aligned16(k_new) || !kvq::aligned16(v_new) ||
       (reinterpret_cast<uintptr_t>(seq_past) & 7u) != 0 ||
       (reinterpret_cast<uintptr_t>(seq_new) & 7u) != 0)
@@ -419,7 +435,8 @@ int32_t decode_prepare(const kvq_config* cfg, const void* cache, int32_t layer, 
   const int32_t st = make_geometry(*cfg, &g);
   if (st != KVQ_OK) return st;
   if (!cache || !q || !out || !workspace) return KVQ_ERR_NULL;
-  if (is_fp8(cfg->scheme) && (!k_scale || !v_scale)) return KVQ_ERR_NULL;
+  if (has_key_scale(cfg->scheme) && !k_scale) return KVQ_ERR_NULL;
+  if (is_fp8(cfg->scheme) && !v_scale) return KVQ_ERR_NULL;
   if (layer < 0 || layer >= cfg->layers) return KVQ_ERR_INVALID;
   if (tokens < 1) return KVQ_ERR_INVALID;
   if (tokens > cfg->max_tokens) return KVQ_ERR_CAPACITY;

@@ -16,6 +16,10 @@ constexpr int kPage = 32;  // tokens per page == KIVI key group
 __host__ __device__ constexpr bool is_fp8(int scheme) {
   return scheme == KVQ_FP8_E4M3 || scheme == KVQ_FP8_E5M2;
 }
+// Schemes whose keys take the per-head static key scale (FP8 keys).
+__host__ __device__ constexpr bool has_key_scale(int scheme) {
+  return is_fp8(scheme) || scheme == KVQ_FP8K_SYMV;
+}
 
 // Everything a kernel needs to address one layer of the cache.
 struct Geometry {

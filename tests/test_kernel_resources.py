@@ -36,7 +36,12 @@ def kernels(tmp_path_factory):
     objcopy, bundler, readelf = _tools()
     tmp = tmp_path_factory.mktemp("co")
     fat = tmp / "fatbin"
-    subprocess.run([objcopy, "--dump-section", f".hip_fatbin={fat}", kvq.kvq.LIB_PATH], check=True)
+    # objcopy rewrites its input when given no output file: work on a copy, so
+    # that the library a test process has mapped is never touched
+    lib = tmp / "libkvq.so"
+    shutil.copyfile(kvq.kvq.LIB_PATH, lib)
+    subprocess.run([objcopy, "--dump-section", f".hip_fatbin={fat}", str(lib), str(tmp / "out.so")],
+                   check=True)
     data = fat.read_bytes()
     starts = [m.start() for m in re.finditer(re.escape(BUNDLE), data)]
     assert starts, "no offload bundles in libkvq.so"
