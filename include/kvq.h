@@ -226,11 +226,11 @@ typedef struct kvq_config {
  *
  * Which tokens are quantised (KIVI), for a cache holding T tokens:
  *   q(T) = 32*floor(max(0, T-R)/32) tokens live in pages [0, q(T)/32); the
- *   other n_r = T - q(T) tokens live in the ring. So the newest R tokens are
- *   always in full precision, and whenever R+32 tokens are unquantised the
- *   oldest 32 are encoded as one group. [QKV] "Keys and values are shaped
+ *   other n_r = T - q(T) tokens live in the ring. So a window of at least the
+ *   last R tokens stays unquantised, and whenever R+32 tokens are unquantised
+ *   the oldest 32 are encoded as one group. [QKV] "Keys and values are shaped
  *   differently" (window of recent tokens quantised as a group once it fills)
- *   and going deeper (the newest R tokens kept in full precision); [KIVI] How
+ *   and going deeper (a full-precision window of recent tokens); [KIVI] How
  *   It Works (residual length).
  * Encoding of one KIVI group (fp32 arithmetic, IEEE division, ties-to-even
  * rounding, no fused multiply-add), L = 2^bk - 1 for keys and 2^bv - 1 for

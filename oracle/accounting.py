@@ -46,7 +46,7 @@ def flush_plan(tokens, residual, group=PAGE):
     The newest `residual` tokens always stay in full precision; whenever the
     unquantised tokens reach residual+group, the oldest `group` of them are
     encoded together ("Quantizing the KV cache": the window is quantised as a
-    group once it fills, and the newest R tokens are kept in full precision;
+    group once it fills, and a recent window of R tokens is never rounded;
     KIVI How It Works: the most recent tokens kept unquantised).
     Returns (q, n_r): q tokens in quantised groups, n_r = T - q unquantised."""
     q = group * (max(0, tokens - residual) // group)

@@ -11,7 +11,7 @@ chunked by construction:
   narrower: "Quantizing the KV cache", How the KV cache is quantized, names
   separate key and value cache types) and the newest T - q(T) sit in the
   residual ring unquantised, slot t mod (R + 32) ("Quantizing the KV cache":
-  the newest R tokens stay in full precision, a full window is quantised as a
+  a window of the last R tokens is left unrounded, a full window is quantised as a
   group; KIVI How It Works: recent tokens kept in 16-bit).
 * SYM_TOKEN / FP8 (E4M3FN or E5M2): every token is encoded as it arrives ("Quantising the
   Cache.", Workshop: rounded before it enters the cache).
