@@ -124,16 +124,20 @@ def bf16_page(k32, v32, n_valid):
 
 def fp8_page(k32, v32, k_scale, v_scale, n_valid, fmt="e4m3"):
     """FP8 page (E4M3FN or E5M2) with the KV head's scalar scales; tokens >=
-    n_valid undefined."""
+    n_valid undefined. K rows; the values of a full page (n_valid = 32) in V
+    cols, those of an open page (the cache's last page while it holds fewer
+    than 32 tokens) in rows like the keys, so that a token appended to it
+    writes one contiguous row."""
     d = k32.shape[1]
     kc = codec.fp8_quantize(k32, k_scale, fmt)
     vc = codec.fp8_quantize(v32, v_scale, fmt)
     valid = np.arange(PAGE) < n_valid
     kc = np.where(valid[:, None], kc, 0).astype(np.uint8)
     vc = np.where(valid[:, None], vc, 0).astype(np.uint8)
-    buf = np.concatenate([kc.reshape(-1), vc.T.reshape(-1)])
-    mask = np.concatenate([np.repeat(np.where(valid, 0xFF, 0).astype(np.uint8), d),
-                           np.tile(np.where(valid, 0xFF, 0).astype(np.uint8), d)])
+    tok = np.where(valid, 0xFF, 0).astype(np.uint8)
+    rows = n_valid < PAGE
+    buf = np.concatenate([kc.reshape(-1), vc.reshape(-1) if rows else vc.T.reshape(-1)])
+    mask = np.concatenate([np.repeat(tok, d), np.repeat(tok, d) if rows else np.tile(tok, d)])
     return buf, mask
 
 

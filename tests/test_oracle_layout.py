@@ -74,11 +74,19 @@ def test_sym_and_fp8_partial_page_masks():
     # V cols: first 5 of each channel's 32 four-bit fields defined -> 0xFF,0xFF,0x0F,0...
     vmask = mask[32 * row + 128: 32 * row + 128 + 16]
     assert vmask.tolist() == [0xFF, 0xFF, 0x0F] + [0] * 13
+    # open FP8 page (31 tokens): K rows and V rows (token 30's 32 value bytes
+    # contiguous, token 31's undefined)
     buf, mask = layout.fp8_page(k, v, F32(0.5), F32(2.0), 31)
     assert buf.size == 2048 and mask.sum() == 0xFF * 31 * 32 * 2
     assert mask[32 * 31 + 1] == 0 and mask[32 * 30 + 1] == 0xFF
     assert buf[32 * 30 + 1] == codec.fp8_quantize(k[30, 1], F32(0.5))
+    assert buf[1024 + 30 * 32 + 7] == codec.fp8_quantize(v[30, 7], F32(2.0))
+    assert np.all(mask[1024 + 30 * 32:1024 + 31 * 32] == 0xFF) and np.all(mask[1024 + 31 * 32:] == 0)
+    # full page: V cols (channel 7's 32 tokens contiguous)
+    buf, mask = layout.fp8_page(k, v, F32(0.5), F32(2.0), 32)
+    assert np.all(mask == 0xFF)
     assert buf[1024 + 7 * 32 + 30] == codec.fp8_quantize(v[30, 7], F32(2.0))
+    assert buf[1024 + 30 * 32 + 7] == codec.fp8_quantize(v[7, 30], F32(2.0))
 
 
 def _bf16(rng, *shape):
@@ -294,3 +302,32 @@ def test_fp8k_symv_cache_dequant_matches_bytes():
                 f = np.where(f >= 8, f - 16, f).T[:n]
                 sc = pg[32 * d + 32 * d * vb // 8:32 * d + 32 * d * vb // 8 + 128].view(F32)[:n]
                 assert np.array_equal(vh[b, h, 32 * p:32 * p + n], f * sc[:, None].astype(np.float64))
+
+
+@pytest.mark.parametrize("fmt_scheme,fmt", [(acc.FP8_E4M3, "e4m3"), (acc.FP8_E5M2, "e5m2")])
+def test_fp8_cache_open_page_rows_then_columns(fmt_scheme, fmt):
+    """dequantized() of an FP8 cache equals its byte image decoded by hand
+    after every append of a sequence that opens, extends and closes pages
+    (one token, a chunk ending inside a page, one closing it and opening the
+    next): a full page's values are read as channel columns, the last page's
+    (fewer than 32 tokens) as token rows."""
+    rng = np.random.default_rng(21)
+    B, H, d = 1, 2, 32
+    c = OracleCache(fmt_scheme, 8, 1, B, H, d, 128, in_dtype="f32")
+    ks, vs = np.array([0.02, 0.05], F32), np.array([0.03, 0.01], F32)
+    k = rng.standard_normal((B, 100, H, d)).astype(F32)
+    v = rng.standard_normal((B, 100, H, d)).astype(F32)
+    ps = acc.page_bytes(fmt_scheme, d, 8)
+    for a, z in ((0, 1), (1, 20), (20, 31), (31, 32), (32, 45), (45, 70), (70, 71), (71, 100)):
+        c.append(0, k[:, a:z], v[:, a:z], k_scale=ks, v_scale=vs)
+        kh, vh = c.dequantized(0)
+        for h in range(H):
+            buf, mask = c.slab_image(0, 0, h)
+            for p in range(-(-z // 32)):
+                n = min(32, z - 32 * p)
+                pg = buf[p * ps:(p + 1) * ps]
+                kc = pg[:32 * d].reshape(32, d)[:n]
+                assert np.array_equal(kh[0, h, 32 * p:32 * p + n], codec.fp8_dequantize(kc, ks[h], fmt))
+                vb = pg[32 * d:].reshape(32, d)
+                vc = vb[:n] if n < 32 else vb.T            # open page: rows; full: columns
+                assert np.array_equal(vh[0, h, 32 * p:32 * p + n], codec.fp8_dequantize(vc, vs[h], fmt))
