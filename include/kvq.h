@@ -63,11 +63,12 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 9   /* 3: ragged-batch entry points; 4: several queries per sequence;
+#define KVQ_ABI_VERSION 10  /* 3: ragged-batch entry points; 4: several queries per sequence;
                                5: decode without a caller workspace; 6: sparse outliers;
                                7: paged caches (block tables);
                                8: one-token append fused with decode;
-                               9: keys and values in different cache types */
+                               9: keys and values in different cache types;
+                               10: FP8 values of an open page in token rows */
 
 /* Exported entry points (the library is built with hidden visibility). */
 #if defined(__GNUC__)
@@ -215,6 +216,10 @@ typedef struct kvq_config {
  * FP8_E4M3 / FP8_E5M2 page (64*d bytes), P = ceil(max_tokens/32):
  *   Kc  K rows, one FP8 byte per value         32*d
  *   Vc  V cols, one FP8 byte per value         32*d
+ *   except the cache's open page: while the last page of a sequence holds
+ *   fewer than 32 tokens its Vc region holds V rows (token r's d codes at
+ *   r*d), so that appending a token writes one contiguous row; the append
+ *   that fills the page rewrites the region as V cols.
  * BF16_CACHE page (128*d bytes), P = ceil(max_tokens/32):
  *   Kc  K rows, bfloat16 per value (16-bit fields)   64*d
  *   Vc  V cols, bfloat16 per value                   64*d

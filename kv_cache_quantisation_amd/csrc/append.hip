@@ -554,24 +554,53 @@ __global__ __launch_bounds__(kThreads) void token_append_kernel(AppendParams p) 
 // page) flat, so that neighbouring blocks write neighbouring pages of one
 // slab; grid y, z = KV head, sequence. Tokens outside [past, past + n) of a
 // page are neither read nor written.
+// FP8 values of the cache's open last page (fewer than 32 tokens) are kept in
+// token rows, so that a token appended to it writes one contiguous row; a
+// page is written as columns once it holds 32 tokens. The page that was open
+// before the call and fills in it (the sequence's first page of the call) is
+// the first 8 * CH tasks of block 0: that block copies the page's earlier
+// value rows into LDS before any of its threads writes the page's columns.
+// A block covers whole pages (256 threads, or one page of 8 * CH tasks when
+// that is more).
 // WITH_V false: the keys only (values in another cache type, written by
 // another kernel)
+template <int D, int IB>
+constexpr int byte_append_threads() {
+  return 8 * (D * IB / 16) > kThreads ? 8 * (D * IB / 16) : kThreads;
+}
+
 template <int SCHEME, int D, int IB, bool WITH_V = true>
-__global__ __launch_bounds__(kThreads) void byte_append_kernel(AppendParams p, int64_t pages) {
+__global__ __launch_bounds__((byte_append_threads<D, IB>())) void byte_append_kernel(AppendParams p,
+                                                                                    int64_t pages) {
   constexpr int CB = SCHEME == KVQ_BF16_CACHE ? 2 : 1;   // bytes per code
   constexpr int CH = D * IB / 16;                          // 16-byte chunks per input row
   constexpr int EPC = 16 / IB;                             // elements per chunk
   constexpr int TPU = 8 * CH;                              // tiles per page
-  const int64_t gtask = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  constexpr int NTH = byte_append_threads<D, IB>();
+  static_assert(NTH % TPU == 0, "a block covers whole pages");
+  constexpr bool ROWS = CB == 1 && WITH_V;                 // FP8 values: open pages in rows
+  const int64_t gtask = static_cast<int64_t>(blockIdx.x) * NTH + threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   int64_t past, n;
   seq_counts(p, b, past, n);
   const int64_t end = past + n;
+  const int64_t first = past / kPage;
+  // the open page at the start of the call fills in it: its earlier value
+  // rows become columns
+  const bool closes = ROWS && past % kPage != 0 && end >= (first + 1) * kPage;
+  __shared__ __attribute__((aligned(16))) uint8_t oldv[ROWS ? kPage * D : 16];
+  if (closes && blockIdx.x == 0) {   // block-uniform
+    const uint8_t* pv = p.pm.page(b, h, first) + p.off_vc;
+    const int chunks = static_cast<int>(past % kPage) * D / 16;
+    for (int i = threadIdx.x; i < chunks; i += NTH)
+      *reinterpret_cast<uint4*>(oldv + 16 * i) = *reinterpret_cast<const uint4*>(pv + 16 * i);
+    __syncthreads();   // read before any column of the page is written
+  }
   // pages this sequence touches (at most `pages`, the launch's bound)
-  const int64_t mine = n > 0 ? (end - 1) / kPage - past / kPage + 1 : 0;
+  const int64_t mine = n > 0 ? (end - 1) / kPage - first + 1 : 0;
   if (gtask >= (mine < pages ? mine : pages) * TPU) return;
   const int task = static_cast<int>(gtask % TPU);
-  const int64_t page = past / kPage + gtask / TPU;
+  const int64_t page = first + gtask / TPU;
   const int lo = static_cast<int>((past > page * kPage ? past : page * kPage) - page * kPage);
   const int hi = static_cast<int>((end < page * kPage + kPage ? end : page * kPage + kPage) -
                                   page * kPage);
@@ -659,6 +688,23 @@ __global__ __launch_bounds__(kThreads) void byte_append_kernel(AppendParams p, i
     if constexpr (CB == 1) fp8_quotients(fv[i], vs, vr, exact);
   }
   if constexpr (CB == 1) {
+    if (hi < kPage) {
+      // the page stays open: each token's EPC codes into its value row
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * vq + i;
+        if (r < lo || r >= hi) continue;
+        uint32_t w[EPC / 4];
+#pragma unroll
+        for (int e = 0; e < EPC / 4; ++e)
+          w[e] = fp8x2_encode<E5, true>(fv[i][4 * e + 2], fv[i][4 * e + 3],
+                                        fp8x2_encode<E5, false>(fv[i][4 * e], fv[i][4 * e + 1], 0));
+        uint8_t* dst = pg + p.off_vc + static_cast<int64_t>(r) * D + vc * EPC;
+        if constexpr (EPC == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+        else *reinterpret_cast<uint32_t*>(dst) = w[0];
+      }
+      return;
+    }
     // one dword of 4 token codes per channel; 4x4 transposes across the lane
     // quad that holds tokens 16m..16m+15 (vq = 4m + j, j = lane & 3) leave
     // lane j with channel 4t + j's 16 codes in dw[4t..4t+3], so the quad's
@@ -667,19 +713,32 @@ __global__ __launch_bounds__(kThreads) void byte_append_kernel(AppendParams p, i
 #pragma unroll
     for (int e = 0; e < EPC; ++e)
       dw[e] = fp8x2_encode<E5, true>(fv[2][e], fv[3][e], fp8x2_encode<E5, false>(fv[0][e], fv[1][e], 0));
+    // the page filling in this call: its earlier tokens' codes from their rows
+    const bool closing = closes && page == first;
+    if (closing) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * vq + i;
+        if (r >= lo) continue;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e)
+          dw[e] = (dw[e] & ~(0xFFu << (8 * i))) | (uint32_t(oldv[r * D + vc * EPC + e]) << (8 * i));
+      }
+    }
+    const int lo_c = closing ? 0 : lo;   // first token whose column byte is written
     const int j = vq & 3, m = vq >> 2;
 #pragma unroll
     for (int t = 0; t < EPC / 4; ++t) {
       uint32_t blk[4] = {dw[4 * t], dw[4 * t + 1], dw[4 * t + 2], dw[4 * t + 3]};
       quad_transpose(blk, j);
       uint8_t* dst = pg + p.off_vc + static_cast<int64_t>(vc * EPC + 4 * t + j) * kPage + 16 * m;
-      if (16 * m >= lo && 16 * m + 16 <= hi) {
+      if (16 * m >= lo_c && 16 * m + 16 <= hi) {
         *reinterpret_cast<uint4*>(dst) = make_uint4(blk[0], blk[1], blk[2], blk[3]);
       } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int r = 16 * m + i;
-          if (r >= lo && r < hi) dst[i] = static_cast<uint8_t>(blk[i / 4] >> (8 * (i % 4)));
+          if (r >= lo_c && r < hi) dst[i] = static_cast<uint8_t>(blk[i / 4] >> (8 * (i % 4)));
         }
       }
     }
@@ -750,8 +809,9 @@ hipError_t run_token(const AppendArgs& a, const AppendParams& p, hipStream_t st)
     hipLaunchKernelGGL((token_append_kernel<D, BITS, IB>), grid, dim3(kThreads), 0, st, p);
   } else {
     constexpr int64_t TPU = 8 * (D * IB / 16);
-    dim3 grid(static_cast<unsigned>((pages * TPU + kThreads - 1) / kThreads), g.kv_heads, g.batch);
-    hipLaunchKernelGGL((byte_append_kernel<SCHEME, D, IB>), grid, dim3(kThreads), 0, st, p, pages);
+    constexpr int NTH = byte_append_threads<D, IB>();
+    dim3 grid(static_cast<unsigned>((pages * TPU + NTH - 1) / NTH), g.kv_heads, g.batch);
+    hipLaunchKernelGGL((byte_append_kernel<SCHEME, D, IB>), grid, dim3(NTH), 0, st, p, pages);
   }
   return hipGetLastError();
 }
@@ -765,8 +825,9 @@ hipError_t run_fp8k_symv(const AppendArgs& a, const AppendParams& p, hipStream_t
   const int64_t pages = a.seq_past ? (a.n + kPage - 1) / kPage + 1
                                    : (a.past + a.n - 1) / kPage - a.past / kPage + 1;
   constexpr int64_t TPU = 8 * (D * IB / 16);
-  dim3 kgrid(static_cast<unsigned>((pages * TPU + kThreads - 1) / kThreads), g.kv_heads, g.batch);
-  hipLaunchKernelGGL((byte_append_kernel<KVQ_FP8_E4M3, D, IB, false>), kgrid, dim3(kThreads), 0, st, p, pages);
+  constexpr int NTH = byte_append_threads<D, IB>();
+  dim3 kgrid(static_cast<unsigned>((pages * TPU + NTH - 1) / NTH), g.kv_heads, g.batch);
+  hipLaunchKernelGGL((byte_append_kernel<KVQ_FP8_E4M3, D, IB, false>), kgrid, dim3(NTH), 0, st, p, pages);
   dim3 vgrid(static_cast<unsigned>(pages), g.kv_heads, g.batch);
   switch (g.vbits) {
     case 2: hipLaunchKernelGGL((token_append_kernel<D, 2, IB, false>), vgrid, dim3(kThreads), 0, st, p); break;

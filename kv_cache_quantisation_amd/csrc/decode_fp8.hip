@@ -137,6 +137,13 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
     n_pages = static_cast<int32_t>((Tb + kPage - 1) / kPage);
     last_valid = static_cast<int32_t>(Tb - static_cast<int64_t>(n_pages - 1) * kPage);
   }
+  // the cache's open last page (fewer than 32 tokens) keeps FP8 values in
+  // token rows (-1: every page is full)
+  int open_page = -1;
+  if constexpr (!BF16) {
+    const int64_t fill = seq_len(p.seq_tokens, b, p.T);
+    if (fill % kPage != 0) open_page = static_cast<int>(fill / kPage);
+  }
   const int pg0 = static_cast<int>(static_cast<int64_t>(split) * n_pages / p.splits);
   const int pg1 = static_cast<int>(static_cast<int64_t>(split + 1) * n_pages / p.splits);
   const int n_mine = pg0 + wave < pg1 ? (pg1 - pg0 - wave + kWaves - 1) / kWaves : 0;
@@ -220,7 +227,8 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_lane = -INFINITY, l_lane = 0.f;
 
-  auto process_page = [&](const uint8_t* pg, int n_valid, const uint4* vr) {
+  auto process_page = [&](const uint8_t* pg, int n_valid, const uint4* vr, bool vrows) {
+    (void)vrows;   // bfloat16 caches: value columns on every page
     // scores; tile mt row rho = token 8(rho/4) + 4mt + rho%4
     float s[8];
 #pragma unroll
@@ -322,14 +330,33 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
         m0 = k >= 4 ? 0xFFFFFFFFu : (1u << (8 * k)) - 1u;
         m1 = k >= 8 ? 0xFFFFFFFFu : (k <= 4 ? 0u : (1u << (8 * (k - 4))) - 1u);
       }
+      if (vrows) {   // wave-uniform, one page per row: tokens 8g..8g+7 from their rows
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const uint2 w = *reinterpret_cast<const uint2*>(pg + PG::OFF_VC + (16 * nt + j) * kPage + 8 * g);
-        const uint32_t x0 = w.x & m0, x1 = w.y & m1;
-        const uint4 bw = uint4{fp8x2_bf16<E5, false>(x0), fp8x2_bf16<E5, true>(x0),
-                               fp8x2_bf16<E5, false>(x1), fp8x2_bf16<E5, true>(x1)};
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, __builtin_bit_cast(bf16x8, bw), acc[nt],
-                                                           0, 0, 0);
+        for (int nt = 0; nt < NT; ++nt) {
+          const uint8_t* col = pg + PG::OFF_VC + 8 * g * D + 16 * nt + j;
+          uint32_t x0 = 0u, x1 = 0u;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x0 |= uint32_t(col[i * D]) << (8 * i);
+            x1 |= uint32_t(col[(4 + i) * D]) << (8 * i);
+          }
+          x0 &= m0;
+          x1 &= m1;
+          const uint4 bw = uint4{fp8x2_bf16<E5, false>(x0), fp8x2_bf16<E5, true>(x0),
+                                 fp8x2_bf16<E5, false>(x1), fp8x2_bf16<E5, true>(x1)};
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, __builtin_bit_cast(bf16x8, bw), acc[nt],
+                                                             0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const uint2 w = *reinterpret_cast<const uint2*>(pg + PG::OFF_VC + (16 * nt + j) * kPage + 8 * g);
+          const uint32_t x0 = w.x & m0, x1 = w.y & m1;
+          const uint4 bw = uint4{fp8x2_bf16<E5, false>(x0), fp8x2_bf16<E5, true>(x0),
+                                 fp8x2_bf16<E5, false>(x1), fp8x2_bf16<E5, true>(x1)};
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, __builtin_bit_cast(bf16x8, bw), acc[nt],
+                                                             0, 0, 0);
+        }
       }
     }
   };
@@ -350,7 +377,8 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
     }
     __builtin_amdgcn_wave_barrier();
     const int page = pg0 + wave + kWaves * k;
-    process_page(wbuf + (k % PG::NBUF) * PG::BYTES, page == n_pages - 1 ? last_valid : kPage, cur);
+    process_page(wbuf + (k % PG::NBUF) * PG::BYTES, page == n_pages - 1 ? last_valid : kPage, cur,
+                 page == open_page);
   };
 #pragma unroll 1
   for (int k = 0; k < n_mine; k += 2) {

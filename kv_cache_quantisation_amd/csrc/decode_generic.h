@@ -427,6 +427,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
             }
           }
         } else {
+        // FP8 values of the cache's open last page (fewer than 32 tokens) are
+        // in token rows: the 4 codes of a word are gathered from 4 rows
+        const bool vrows = (SCHEME == KVQ_FP8_E4M3 || SCHEME == KVQ_FP8_E5M2) && fill % kPage != 0 &&
+                           item == fill / kPage;
 #pragma unroll
         for (int ci = 0; ci < CPL; ++ci) {
           const int c = cs * CPL + ci;
@@ -434,7 +438,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
                                ts * SUBW;
 #pragma unroll
           for (int wi = 0; wi < SUBW; ++wi) {
-            const uint32_t w = vw[wi];
+            uint32_t w;
+            if (vrows) {
+              const uint8_t* vr = pg + p.off_vc + static_cast<int64_t>(ts * TPS + wi * FPWV) * D + c;
+              w = uint32_t(vr[0]) | (uint32_t(vr[D]) << 8) | (uint32_t(vr[2 * D]) << 16) |
+                  (uint32_t(vr[3 * D]) << 24);
+            } else {
+              w = vw[wi];
+            }
 #pragma unroll
             for (int j = 0; j < FPWV; ++j) {
               const float cv = code_value<VSCH, VB>(w, j);

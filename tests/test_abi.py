@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert kvq.kvq_abi_version() == 9
+    assert kvq.kvq_abi_version() == 10
     assert kvq.status_string(0) == "ok"
     for st in (-1, -2, -3, -4, -5, -6):
         assert kvq.status_string(st) != "unknown status"
