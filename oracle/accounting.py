@@ -15,7 +15,7 @@
 
 from fractions import Fraction
 
-KIVI, SYM_TOKEN, FP8_E4M3, BF16_CACHE, FP8_E5M2, FP8K_SYMV = 0, 1, 2, 3, 4, 5
+KIVI, SYM_TOKEN, FP8_E4M3, BF16_CACHE, FP8_E5M2, FP8K_SYMV, FP8K_KIVIV = 0, 1, 2, 3, 4, 5, 6
 PAGE = 32
 
 
@@ -83,6 +83,9 @@ def page_bytes(scheme, head_dim, bits, v_bits=None, outliers=0):
         # FP8 K rows + symmetric V codes at v_bits + one V scale per token,
         # the scales padded to 256 bytes (pages stay 256-byte multiples)
         return PAGE * d + PAGE * d * vb // 8 + 256
+    if scheme == FP8K_KIVIV:
+        # FP8 K rows + KIVI V codes at v_bits + V scale and offset per token
+        return PAGE * d + PAGE * d * vb // 8 + 4 * PAGE + 4 * PAGE
     raise ValueError(scheme)
 
 

@@ -21,6 +21,9 @@ chunked by construction:
   cache", How the KV cache is quantized: separate key and value cache
   types): each token's key encoded as FP8 E4M3 with the KV head's static key
   scale and its value symmetric per token at v_bits, as it arrives.
+* FP8K_KIVIV: as FP8K_SYMV with each token's value encoded by KIVI's
+  per-token Q_b at v_bits (KIVI How It Works: values per token), as it
+  arrives (values need no group of later tokens, so no residual ring).
 
 Decode attention (``decode``) dequantises in float64, applies the rotary
 embedding to keys at their positions and to the query at position T-1 when
@@ -35,9 +38,9 @@ import numpy as np
 
 from . import accounting, attention, codec, layout, rope
 
-KIVI, SYM_TOKEN, FP8_E4M3, BF16_CACHE, FP8_E5M2, FP8K_SYMV = (
+KIVI, SYM_TOKEN, FP8_E4M3, BF16_CACHE, FP8_E5M2, FP8K_SYMV, FP8K_KIVIV = (
     accounting.KIVI, accounting.SYM_TOKEN, accounting.FP8_E4M3, accounting.BF16_CACHE,
-    accounting.FP8_E5M2, accounting.FP8K_SYMV)
+    accounting.FP8_E5M2, accounting.FP8K_SYMV, accounting.FP8K_KIVIV)
 PAGE = 32
 
 
@@ -52,7 +55,7 @@ class OracleCache:
 
     def __init__(self, scheme, bits, layers, batch, kv_heads, head_dim, capacity,
                  residual=0, in_dtype="bf16", v_bits=None, outliers=0):
-        if scheme == FP8K_SYMV:
+        if scheme in (FP8K_SYMV, FP8K_KIVIV):
             assert residual == 0 and bits == 8 and v_bits in (2, 3, 4, 8) and not outliers
         elif scheme != KIVI:
             assert residual == 0 and v_bits in (None, bits) and not outliers
@@ -75,7 +78,7 @@ class OracleCache:
         k_new, v_new = np.asarray(k_new), np.asarray(v_new)
         assert k_new.shape == v_new.shape and k_new.shape[0] == self.batch
         assert self.tokens(layer) + k_new.shape[1] <= self.capacity
-        if self.scheme == FP8K_SYMV:   # a static key scale only
+        if self.scheme in (FP8K_SYMV, FP8K_KIVIV):   # a static key scale only
             ks = np.asarray(k_scale, np.float32)
             if self.k_scale[layer] is not None:
                 assert np.array_equal(ks, self.k_scale[layer])
@@ -152,6 +155,8 @@ class OracleCache:
                     pb, pm = layout.bf16_page(k32, v32, n)
                 elif self.scheme == FP8K_SYMV:
                     pb, pm = layout.fp8k_symv_page(k32, v32, self.k_scale[layer][h], self.v_bits, n)
+                elif self.scheme == FP8K_KIVIV:
+                    pb, pm = layout.fp8k_kiviv_page(k32, v32, self.k_scale[layer][h], self.v_bits, n)
                 else:
                     pb, pm = layout.fp8_page(k32, v32, self.k_scale[layer][h],
                                              self.v_scale[layer][h], n, self.fp8_format())
@@ -197,11 +202,15 @@ class OracleCache:
         elif self.scheme == BF16_CACHE:
             kh[:] = codec.bf16_decode(codec.bf16_encode(K))
             vh[:] = codec.bf16_decode(codec.bf16_encode(V))
-        elif self.scheme == FP8K_SYMV:
+        elif self.scheme in (FP8K_SYMV, FP8K_KIVIV):
             ksc = self.k_scale[layer][None, :, None, None]
             kh[:] = codec.fp8_dequantize(codec.fp8_quantize(K, ksc, "e4m3"), ksc, "e4m3")
-            vc, vs = codec.sym_quantize(V, self.v_bits, axis=3)
-            vh[:] = codec.sym_dequantize(vc, vs, axis=3)
+            if self.scheme == FP8K_SYMV:
+                vc, vs = codec.sym_quantize(V, self.v_bits, axis=3)
+                vh[:] = codec.sym_dequantize(vc, vs, axis=3)
+            else:
+                vc, vs, vz = codec.kivi_quantize(V, self.v_bits, axis=3)
+                vh[:] = codec.kivi_dequantize(vc, vs, vz, axis=3)
         elif self.scheme == SYM_TOKEN:
             kc, ks = codec.sym_quantize(K, self.bits, axis=3)
             vc, vs = codec.sym_quantize(V, self.bits, axis=3)

@@ -156,3 +156,25 @@ def fp8k_symv_page(k32, v32, k_scale, v_bits, n_valid):
     pad = np.zeros(128, np.uint8)
     return (np.concatenate([fb[:k_end], sb[v_start:], pad]),
             np.concatenate([fm[:k_end], sm[v_start:], pad]))
+
+
+def fp8k_kiviv_page(k32, v32, k_scale, v_bits, n_valid):
+    """FP8 keys with KIVI values ("Quantizing the KV cache", How the KV cache
+    is quantized: separate key and value cache types; KIVI How It Works:
+    values quantised per token): the key rows of an FP8 E4M3 page with the KV
+    head's scalar key scale, then value columns of unsigned v_bits codes, each
+    token's value vector encoded by Q_b over its d channels as the KIVI
+    page's values are, then the fp32 scale and the fp32 offset (minimum) of
+    each token; tokens >= n_valid undefined."""
+    d = k32.shape[1]
+    fb, fm = fp8_page(k32, v32, k_scale, np.float32(1), n_valid, "e4m3")
+    vc, vs, vz = codec.kivi_quantize(v32, v_bits, axis=1)   # per token over the channels
+    valid = np.arange(PAGE) < n_valid
+    vc = np.where(valid[:, None], vc, 0)
+    vs = np.where(valid, vs, np.float32(0))
+    vz = np.where(valid, vz, np.float32(0))
+    tok = np.repeat(np.where(valid, 0xFF, 0).astype(np.uint8), 4)
+    buf = np.concatenate([fb[:PAGE * d], pack_fields(vc.T, v_bits), _f32_bytes(vs), _f32_bytes(vz)])
+    mask = np.concatenate([fm[:PAGE * d], np.tile(_valid_fields_mask(n_valid, PAGE, v_bits), d),
+                           tok, tok])
+    return buf, mask

@@ -331,3 +331,69 @@ def test_fp8_cache_open_page_rows_then_columns(fmt_scheme, fmt):
                 vb = pg[32 * d:].reshape(32, d)
                 vc = vb[:n] if n < 32 else vb.T            # open page: rows; full: columns
                 assert np.array_equal(vh[0, h, 32 * p:32 * p + n], codec.fp8_dequantize(vc, vs[h], fmt))
+
+
+@pytest.mark.parametrize("vb", [2, 3, 4, 8])
+def test_fp8k_kiviv_page_halves(vb):
+    """FP8 keys with KIVI values: the FP8 page's key rows, then value columns
+    of unsigned vb-bit fields, then each token's fp32 scale and fp32 offset.
+    Decoded here from the bytes by hand: each token's smallest value has code
+    0 and decodes to itself, its largest has code 2^vb - 1, every value lies
+    within half a step of its decoded value, and a partial page's undefined
+    tokens are masked."""
+    rng = np.random.default_rng(31 + vb)
+    d, n = 64, 27
+    k = rng.standard_normal((32, d)).astype(F32) * 3
+    v = rng.standard_normal((32, d)).astype(F32) + F32(0.5)
+    ks = F32(0.0125)
+    buf, mask = layout.fp8k_kiviv_page(k, v, ks, vb, n)
+    vend = 32 * d + 32 * d * vb // 8
+    assert buf.size == mask.size == acc.page_bytes(acc.FP8K_KIVIV, d, 8, vb) == vend + 256
+    assert buf.size % 256 == 0
+    kb = buf[:32 * d].reshape(32, d)
+    assert np.array_equal(kb[:n], codec.fp8_quantize(k[:n], ks, "e4m3"))
+    assert np.all(mask[:n * d] == 0xFF) and np.all(mask[n * d:32 * d] == 0)
+    f = layout.unpack_fields(buf[32 * d:vend], vb, 32 * d).reshape(d, 32).T.astype(np.int64)   # [token, channel]
+    s = buf[vend:vend + 128].view(F32).astype(np.float64)
+    z = buf[vend + 128:vend + 256].view(F32).astype(np.float64)
+    L = (1 << vb) - 1
+    for t in range(n):
+        lo, hi = int(np.argmin(v[t])), int(np.argmax(v[t]))
+        assert f[t, lo] == 0 and z[t] == v[t, lo] and f[t, hi] == L
+        assert np.isclose(s[t], (float(v[t, hi]) - float(v[t, lo])) / L, rtol=1e-6)
+        assert np.all(np.abs(f[t] * s[t] + z[t] - v[t]) <= s[t] / 2 * (1 + 1e-5) + 1e-7)
+    vm = mask[32 * d:vend]
+    assert np.array_equal(vm, np.tile(layout._valid_fields_mask(n, 32, vb), d))
+    sm = mask[vend:]
+    for part in (sm[:128], sm[128:]):
+        assert np.all(part[:4 * n] == 0xFF) and np.all(part[4 * n:] == 0)
+
+
+def test_fp8k_kiviv_cache_dequant_matches_bytes():
+    """dequantized() of a cache with FP8 keys and KIVI values equals the byte
+    image decoded by hand (keys: code value x key scale; values: field x token
+    scale + token offset), across several appends and a partial last page."""
+    rng = np.random.default_rng(13)
+    B, H, d, vb = 2, 2, 32, 4
+    c = OracleCache(acc.FP8K_KIVIV, 8, 1, B, H, d, 96, in_dtype="f32", v_bits=vb)
+    scales = np.array([0.02, 0.05], F32)
+    k = rng.standard_normal((B, 70, H, d)).astype(F32)
+    v = rng.standard_normal((B, 70, H, d)).astype(F32)
+    for a, z in ((0, 1), (1, 33), (33, 70)):
+        c.append(0, k[:, a:z], v[:, a:z], k_scale=scales)
+    kh, vh = c.dequantized(0)
+    ps = acc.page_bytes(acc.FP8K_KIVIV, d, 8, vb)
+    vend = 32 * d + 32 * d * vb // 8
+    for b in range(B):
+        for h in range(H):
+            buf, _ = c.slab_image(0, b, h)
+            for p in range(3):
+                n = min(32, 70 - 32 * p)
+                pg = buf[p * ps:(p + 1) * ps]
+                kc = pg[:32 * d].reshape(32, d)[:n]
+                assert np.array_equal(kh[b, h, 32 * p:32 * p + n],
+                                      codec.fp8_dequantize(kc, scales[h], "e4m3"))
+                f = layout.unpack_fields(pg[32 * d:vend], vb, 32 * d).reshape(d, 32).T[:n]
+                sc = pg[vend:vend + 128].view(F32)[:n].astype(np.float64)
+                zz = pg[vend + 128:vend + 256].view(F32)[:n].astype(np.float64)
+                assert np.array_equal(vh[b, h, 32 * p:32 * p + n], f * sc[:, None] + zz[:, None])
