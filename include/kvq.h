@@ -63,12 +63,13 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 10  /* 3: ragged-batch entry points; 4: several queries per sequence;
+#define KVQ_ABI_VERSION 11  /* 3: ragged-batch entry points; 4: several queries per sequence;
                                5: decode without a caller workspace; 6: sparse outliers;
                                7: paged caches (block tables);
                                8: one-token append fused with decode;
                                9: keys and values in different cache types;
-                               10: FP8 values of an open page in token rows */
+                               10: FP8 values of an open page in token rows;
+                               11: FP8 keys with KIVI values */
 
 /* Exported entry points (the library is built with hidden visibility). */
 #if defined(__GNUC__)
@@ -111,13 +112,19 @@ extern "C" {
  *   KVQ_FP8_E4M3 (static per-(layer, KV head) key scale), values as in
  *   KVQ_SYM_TOKEN at v_bits (one scale per (token, KV head)); every token is
  *   encoded on arrival. bits must be 8; v_bits in {2,3,4,8} (0 means 8; 3
- *   needs head_dim >= 64). */
+ *   needs head_dim >= 64).
+ * KVQ_FP8K_KIVIV: as KVQ_FP8K_SYMV with the values encoded as KIVI encodes
+ *   them, asymmetric per (token, KV head) over the d channels at v_bits
+ *   ([KIVI] How It Works: values per token), on arrival: a value vector
+ *   needs no group of later tokens, so there is no residual ring. Same bits
+ *   and v_bits rules. */
 #define KVQ_KIVI       0
 #define KVQ_SYM_TOKEN  1
 #define KVQ_FP8_E4M3   2
 #define KVQ_BF16_CACHE 3
 #define KVQ_FP8_E5M2   4
 #define KVQ_FP8K_SYMV  5
+#define KVQ_FP8K_KIVIV 6
 
 /* ---- dtypes (K/V input + residual ring, and the query) ------------------ */
 #define KVQ_F32   0
@@ -163,8 +170,8 @@ typedef struct kvq_config {
                             costs keys more than values, [QKV] "How the KV
                             cache is quantized", INT8 / INT4 blocks with
                             separate key and value cache types); 0 = `bits`.
-                            FP8K_SYMV: bits of the symmetric value codes,
-                            2, 3, 4 or 8 (0 = 8). Other schemes: 0 or
+                            FP8K_SYMV / FP8K_KIVIV: bits of the value
+                            codes, 2, 3, 4 or 8 (0 = 8). Other schemes: 0 or
                             equal to `bits`.                               */
   int32_t  outliers;     /* KIVI: 1 = dense-and-sparse pages (each key
                             channel's 32 tokens and each value token keep
@@ -228,6 +235,11 @@ typedef struct kvq_config {
  *   Vc  V cols, bv-bit two's-complement codes          32*d*bv/8
  *   Vs  fp32 scale per token                           128
  *   (then 128 bytes of padding, unspecified)
+ * FP8K_KIVIV page (32*d + 4*d*bv + 256 bytes), P = ceil(max_tokens/32):
+ *   Kc  K rows, one FP8 E4M3 byte per value            32*d
+ *   Vc  V cols, unsigned bv-bit codes                  32*d*bv/8
+ *   Vs  fp32 scale per token                           128
+ *   Vz  fp32 offset (minimum) per token                128
  *
  * Which tokens are quantised (KIVI), for a cache holding T tokens:
  *   q(T) = 32*floor(max(0, T-R)/32) tokens live in pages [0, q(T)/32); the
@@ -244,6 +256,7 @@ typedef struct kvq_config {
  *   mn = min x (+0 replaces -0), mx = max x, s = (mx - mn) / L,
  *   code = s == 0 ? 0 : clamp(rint((x - mn) / s), 0, L),  stored offset = mn;
  *   dequantised value = code*s + mn.  [QKV] going deeper, Q_b and s.
+ *   FP8K_KIVIV values are encoded the same way, per value token on arrival.
  * Dense-and-sparse KIVI group (outliers = 1): the value of largest magnitude
  *   |x| of each vector (lowest index among equal magnitudes) goes to the side
  *   matrix with its index; mn, mx and s above are taken over the other values
@@ -281,8 +294,8 @@ KVQ_API int64_t kvq_cache_bytes(const kvq_config* cfg, int64_t tokens, int32_t k
  *   k_new, v_new device [batch][new_tokens][kv_heads][head_dim], in_dtype
  *   k_scale,
  *   v_scale      FP8 (either format) only: device fp32 [kv_heads], this layer's per-head
- *                scales (must be > 0); FP8K_SYMV: k_scale only (v_scale
- *                ignored); NULL for the other schemes
+ *                scales (must be > 0); FP8K_SYMV / FP8K_KIVIV: k_scale
+ *                only (v_scale ignored); NULL for the other schemes
  * Requires past_tokens + new_tokens <= max_tokens (else KVQ_ERR_CAPACITY).
  * new_tokens == 0 is a no-op. Appending in any chunking (one call of T tokens
  * or T calls of one token) leaves identical bytes in every defined field.
@@ -326,8 +339,8 @@ KVQ_API int32_t kvq_quantize_append_ragged(const kvq_config* cfg, void* cache, i
  * (2i, 2i+1) turned by angle pos * theta^(-2i/head_dim).  [KVQ] Summary.
  *   q          device [batch][q_heads][head_dim], q_dtype
  *   k_scale,
- *   v_scale    FP8 only: as for append (FP8K_SYMV: k_scale only, v_scale
- *              ignored); NULL otherwise
+ *   v_scale    FP8 only: as for append (FP8K_SYMV / FP8K_KIVIV: k_scale
+ *              only, v_scale ignored); NULL otherwise
  *   out        device fp32 [batch][q_heads][head_dim]
  *   workspace  device, >= kvq_cache_bytes(cfg, tokens, KVQ_BYTES_WORKSPACE);
  *              zero-filled before its first use. It begins with one int32

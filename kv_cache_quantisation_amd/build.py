@@ -18,7 +18,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvq.so")
 
 SOURCES = ["kvq_api.cpp", "append.hip", "decode.hip", "decode_kivi.hip", "decode_kivi3.hip",
-           "decode_other.hip", "decode_mfma.hip", "decode_fp8.hip", "scratch.hip"]
+           "decode_other.hip", "decode_mixed.hip", "decode_mfma.hip", "decode_fp8.hip", "scratch.hip"]
 
 # -ffp-contract=off: the encodings must round exactly as written (no FMA
 # contraction); the decode kernels call fmaf explicitly where they want FMA.

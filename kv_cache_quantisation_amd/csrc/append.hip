@@ -413,17 +413,21 @@ __global__ __launch_bounds__(64) void ring_write_kernel(AppendParams p) {
 // grid = (pages touched, kv_heads, batch). Codes narrower than a byte share
 // 32-bit words across tokens, so the page's new rows are staged in LDS first.
 // WITH_K false: the values only (keys in another cache type, written by
-// another kernel)
-template <int D, int BITS, int IB, bool WITH_K = true>
+// another kernel). ASYM (values only): each value token encoded as KIVI
+// encodes its values, unsigned codes over [min, max] with a per-token scale
+// and offset, instead of the symmetric codes.
+template <int D, int BITS, int IB, bool WITH_K = true, bool ASYM = false>
 __global__ __launch_bounds__(kThreads) void token_append_kernel(AppendParams p) {
+  static_assert(!(ASYM && WITH_K), "asymmetric codes for the value half only");
   constexpr int LD = D + 1;
   constexpr int FPW = 32 / BITS;
   constexpr int CHUNKS = D * IB / 16;
   constexpr uint32_t kMask = (1u << BITS) - 1u;  // BITS < 32
   constexpr float kQmax = float((1 << (BITS - 1)) - 1);
+  constexpr float kLevels = float((1 << BITS) - 1);
   __shared__ float ktile[kPage * LD];
   __shared__ float vtile[kPage * LD];
-  __shared__ float k_sc[kPage], v_sc[kPage];
+  __shared__ float k_sc[kPage], v_sc[kPage], v_mn[kPage];
 
   const int tid = threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -466,20 +470,40 @@ __global__ __launch_bounds__(kThreads) void token_append_kernel(AppendParams p) 
   }
   __syncthreads();
 
-  // one scale per (token, head) for K and for V: s = max|x| / Q
+  // one scale per (token, head) for K and for V: s = max|x| / Q (ASYM
+  // values: s = (max - min) / L and the offset min, -0 made +0)
   for (int i = tid; i < 2 * kPage; i += kThreads) {
     const int which = i / kPage, r = i % kPage;
     if (r < lo || r >= hi || (!WITH_K && which == 0)) continue;
     const float* row = (which ? vtile : ktile) + r * LD;
-    float a = fabsf(row[0]);
-    for (int c = 1; c < D; ++c) a = fmaxf(a, fabsf(row[c]));
-    const float s = a / kQmax;
-    (which ? v_sc : k_sc)[r] = s;
-    reinterpret_cast<float*>(pg + (which ? p.off_vs : p.off_ks))[r] = s;
+    if constexpr (ASYM) {
+      float mn = row[0], mx = row[0];
+      for (int c = 1; c < D; ++c) {
+        mn = fminf(mn, row[c]);
+        mx = fmaxf(mx, row[c]);
+      }
+      mn = mn + 0.0f;
+      const float s = (mx - mn) / kLevels;
+      v_sc[r] = s;
+      v_mn[r] = mn;
+      reinterpret_cast<float*>(pg + p.off_vs)[r] = s;
+      reinterpret_cast<float*>(pg + p.off_vz)[r] = mn;
+    } else {
+      float a = fabsf(row[0]);
+      for (int c = 1; c < D; ++c) a = fmaxf(a, fabsf(row[c]));
+      const float s = a / kQmax;
+      (which ? v_sc : k_sc)[r] = s;
+      reinterpret_cast<float*>(pg + (which ? p.off_vs : p.off_ks))[r] = s;
+    }
   }
   __syncthreads();
 
   auto encode = [&](float x, float s) -> uint32_t { return quant_sym(x, s, kQmax, kMask); };
+  // value code of token t, channel c
+  auto encode_v = [&](int t, int c) -> uint32_t {
+    if constexpr (ASYM) return quant_asym(vtile[t * LD + c], v_mn[t], v_sc[t], kLevels);
+    else return encode(vtile[t * LD + c], v_sc[t]);
+  };
 
   // K rows of the new tokens: whole words
   constexpr int ROW_WORDS = D * BITS / 32;
@@ -504,7 +528,7 @@ __global__ __launch_bounds__(kThreads) void token_append_kernel(AppendParams p) 
       uint32_t wd[3] = {0u, 0u, 0u}, m[3] = {0u, 0u, 0u};
 #pragma unroll
       for (int t = 0; t < kPage; ++t)
-        if (t >= lo && t < hi) put_field<3>(wd, m, t, encode(vtile[t * LD + c], v_sc[t]));
+        if (t >= lo && t < hi) put_field<3>(wd, m, t, encode_v(t, c));
 #pragma unroll
       for (int k = 0; k < 3; ++k) vc3[3 * c + k] = (vc3[3 * c + k] & ~m[k]) | wd[k];
     }
@@ -530,7 +554,7 @@ __global__ __launch_bounds__(kThreads) void token_append_kernel(AppendParams p) 
     for (int j = 0; j < FPW; ++j) {
       const int t = w * FPW + j;
       if (t >= lo && t < hi) {
-        word |= encode(vtile[t * LD + c], v_sc[t]) << (j * BITS);
+        word |= encode_v(t, c) << (j * BITS);
         mask |= kMask << (j * BITS);
       }
     }
@@ -817,10 +841,11 @@ hipError_t run_token(const AppendArgs& a, const AppendParams& p, hipStream_t st)
 }
 
 // Keys and values in different cache types: FP8 E4M3 key rows (the byte-code
-// kernel, keys only), symmetric value columns and scales (the symmetric
-// kernel, values only); the two write disjoint bytes of the pages.
-template <int D, int IB>
-hipError_t run_fp8k_symv(const AppendArgs& a, const AppendParams& p, hipStream_t st) {
+// kernel, keys only), symmetric or KIVI (ASYM) value columns and their
+// per-token scales (the per-token kernel, values only); the two write
+// disjoint bytes of the pages.
+template <int D, int IB, bool ASYM>
+hipError_t run_fp8k_mixed(const AppendArgs& a, const AppendParams& p, hipStream_t st) {
   const Geometry& g = a.g;
   const int64_t pages = a.seq_past ? (a.n + kPage - 1) / kPage + 1
                                    : (a.past + a.n - 1) / kPage - a.past / kPage + 1;
@@ -830,10 +855,10 @@ hipError_t run_fp8k_symv(const AppendArgs& a, const AppendParams& p, hipStream_t
   hipLaunchKernelGGL((byte_append_kernel<KVQ_FP8_E4M3, D, IB, false>), kgrid, dim3(NTH), 0, st, p, pages);
   dim3 vgrid(static_cast<unsigned>(pages), g.kv_heads, g.batch);
   switch (g.vbits) {
-    case 2: hipLaunchKernelGGL((token_append_kernel<D, 2, IB, false>), vgrid, dim3(kThreads), 0, st, p); break;
-    case 3: hipLaunchKernelGGL((token_append_kernel<D, 3, IB, false>), vgrid, dim3(kThreads), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((token_append_kernel<D, 4, IB, false>), vgrid, dim3(kThreads), 0, st, p); break;
-    default: hipLaunchKernelGGL((token_append_kernel<D, 8, IB, false>), vgrid, dim3(kThreads), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((token_append_kernel<D, 2, IB, false, ASYM>), vgrid, dim3(kThreads), 0, st, p); break;
+    case 3: hipLaunchKernelGGL((token_append_kernel<D, 3, IB, false, ASYM>), vgrid, dim3(kThreads), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((token_append_kernel<D, 4, IB, false, ASYM>), vgrid, dim3(kThreads), 0, st, p); break;
+    default: hipLaunchKernelGGL((token_append_kernel<D, 8, IB, false, ASYM>), vgrid, dim3(kThreads), 0, st, p); break;
   }
   return hipGetLastError();
 }
@@ -841,7 +866,8 @@ hipError_t run_fp8k_symv(const AppendArgs& a, const AppendParams& p, hipStream_t
 template <int D, int IB>
 hipError_t dispatch_bits(const AppendArgs& a, const AppendParams& p, hipStream_t st) {
   const Geometry& g = a.g;
-  if (g.scheme == KVQ_FP8K_SYMV) return run_fp8k_symv<D, IB>(a, p, st);
+  if (g.scheme == KVQ_FP8K_SYMV) return run_fp8k_mixed<D, IB, false>(a, p, st);
+  if (g.scheme == KVQ_FP8K_KIVIV) return run_fp8k_mixed<D, IB, true>(a, p, st);
   if (g.scheme == KVQ_FP8_E4M3) return run_token<KVQ_FP8_E4M3, D, 8, IB>(a, p, st);
   if (g.scheme == KVQ_FP8_E5M2) return run_token<KVQ_FP8_E5M2, D, 8, IB>(a, p, st);
   if (g.scheme == KVQ_BF16_CACHE) return run_token<KVQ_BF16_CACHE, D, 16, IB>(a, p, st);

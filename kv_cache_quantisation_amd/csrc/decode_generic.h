@@ -129,10 +129,11 @@ __device__ __forceinline__ void rope_pair(float& x0, float& x1, int64_t pos, dou
 
 template <int SCHEME, int BITS, int VB, int D, int HG>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
-  // cache types of the key and of the value half (FP8K_SYMV: FP8 E4M3 keys,
-  // symmetric per-token values; the other schemes use one type for both)
-  constexpr int KSCH = SCHEME == KVQ_FP8K_SYMV ? KVQ_FP8_E4M3 : SCHEME;
-  constexpr int VSCH = SCHEME == KVQ_FP8K_SYMV ? KVQ_SYM_TOKEN : SCHEME;
+  // cache types of the key and of the value half (FP8K_SYMV / FP8K_KIVIV:
+  // FP8 E4M3 keys, symmetric / KIVI per-token values; the other schemes use
+  // one type for both)
+  constexpr int KSCH = is_fp8_keys_mixed(SCHEME) ? KVQ_FP8_E4M3 : SCHEME;
+  constexpr int VSCH = SCHEME == KVQ_FP8K_SYMV ? KVQ_SYM_TOKEN : SCHEME == KVQ_FP8K_KIVIV ? KVQ_KIVI : SCHEME;
   constexpr int CPL = D >= 64 ? D / 64 : 1;  // channels per lane in the P.V phase
   constexpr int LPC = D / CPL;                // lanes per token subset (64 or 32)
   constexpr int TSUB = 64 / LPC;              // token subsets (1, or 2 when D == 32)
@@ -381,10 +382,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
       // ---- online softmax --------------------------------------------------
       float vsc = 1.0f, vz = 0.0f, vdo = 0.0f;
       if (is_page && valid) {
-        if constexpr (SCHEME == KVQ_KIVI) {
+        if constexpr (VSCH == KVQ_KIVI) {
           vsc = reinterpret_cast<const float*>(pg + p.off_vs)[tok];
           vz = reinterpret_cast<const float*>(pg + p.off_vz)[tok];
-          if (p.outliers) {   // moved value: code 0 gave z; its channel gets (outlier - z)
+          if (SCHEME == KVQ_KIVI && p.outliers) {   // moved value: code 0 gave z; its channel gets (outlier - z)
             vdo = reinterpret_cast<const float*>(pg + p.off_vo)[tok] - vz;
             if (hf == 0) voi[tok] = pg[p.off_vi + tok];
           }
@@ -592,6 +593,7 @@ hipError_t by_d(const DecodeParams& p, int d, int hg, int batch, hipStream_t st)
 hipError_t run_kivi(const DecodeParams& p, const Geometry& g, hipStream_t st);
 hipError_t run_kivi3(const DecodeParams& p, const Geometry& g, hipStream_t st);
 hipError_t run_other(const DecodeParams& p, const Geometry& g, hipStream_t st);
+hipError_t run_mixed(const DecodeParams& p, const Geometry& g, hipStream_t st);
 
 }  // namespace gen
 }  // namespace kvq

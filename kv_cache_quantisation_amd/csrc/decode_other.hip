@@ -1,6 +1,6 @@
 // Generic decode kernel instances: symmetric per-token caches (2/3/4/8-bit),
-// FP8 caches (E4M3, E5M2), FP8 keys with symmetric values, and the bfloat16
-// cache, where the matrix-core kernels do not take them.
+// FP8 caches (E4M3, E5M2) and the bfloat16 cache, where the matrix-core
+// kernels do not take them.
 #include "decode_generic.h"
 
 namespace kvq {
@@ -19,13 +19,9 @@ hipError_t run_other(const DecodeParams& p, const Geometry& g, hipStream_t st) {
       return by_d<KVQ_BF16_CACHE, 16>(p, g.d, g.hg, g.batch, st);
     case KVQ_FP8_E5M2:
       return by_d<KVQ_FP8_E5M2, 8>(p, g.d, g.hg, g.batch, st);
-    case KVQ_FP8K_SYMV:   // FP8 keys, symmetric values at v_bits
-      switch (g.vbits) {
-        case 2: return by_d<KVQ_FP8K_SYMV, 8, 2>(p, g.d, g.hg, g.batch, st);
-        case 3: return by_d<KVQ_FP8K_SYMV, 8, 3>(p, g.d, g.hg, g.batch, st);
-        case 4: return by_d<KVQ_FP8K_SYMV, 8, 4>(p, g.d, g.hg, g.batch, st);
-        default: return by_d<KVQ_FP8K_SYMV, 8, 8>(p, g.d, g.hg, g.batch, st);
-      }
+    case KVQ_FP8K_SYMV:
+    case KVQ_FP8K_KIVIV:
+      return run_mixed(p, g, st);
     default:
       return by_d<KVQ_FP8_E4M3, 8>(p, g.d, g.hg, g.batch, st);
   }

@@ -24,9 +24,10 @@ int32_t validate_config(const kvq_config* cfg) {
   if (cfg->struct_size != sizeof(kvq_config)) return KVQ_ERR_INVALID;
   const kvq_config& c = *cfg;
   if (c.scheme != KVQ_KIVI && c.scheme != KVQ_SYM_TOKEN && c.scheme != KVQ_FP8_E4M3 &&
-      c.scheme != KVQ_FP8_E5M2 && c.scheme != KVQ_BF16_CACHE && c.scheme != KVQ_FP8K_SYMV)
+      c.scheme != KVQ_FP8_E5M2 && c.scheme != KVQ_BF16_CACHE && c.scheme != KVQ_FP8K_SYMV &&
+      c.scheme != KVQ_FP8K_KIVIV)
     return KVQ_ERR_INVALID;
-  if (c.scheme == KVQ_FP8K_SYMV) {   // FP8 keys, symmetric values at v_bits
+  if (kvq::is_fp8_keys_mixed(c.scheme)) {   // FP8 keys, symmetric or KIVI values at v_bits
     if (c.bits != 8) return KVQ_ERR_INVALID;
     if (c.v_bits != 0 && (c.v_bits < 1 || c.v_bits > 8)) return KVQ_ERR_INVALID;
     if (c.v_bits != 0 && c.v_bits != 2 && c.v_bits != 3 && c.v_bits != 4 && c.v_bits != 8)
@@ -39,7 +40,7 @@ int32_t validate_config(const kvq_config* cfg) {
   } else if (c.bits != 2 && c.bits != 3 && c.bits != 4 && c.bits != 8) {
     return (c.bits >= 1 && c.bits <= 8) ? KVQ_ERR_UNSUPPORTED : KVQ_ERR_INVALID;
   }
-  if (c.v_bits != 0 && c.v_bits != c.bits && c.scheme != KVQ_FP8K_SYMV) {
+  if (c.v_bits != 0 && c.v_bits != c.bits && !kvq::is_fp8_keys_mixed(c.scheme)) {
     if (c.scheme != KVQ_KIVI || c.v_bits < 1 || c.v_bits > 8) return KVQ_ERR_INVALID;
     if ((c.v_bits != 2 && c.v_bits != 3 && c.v_bits != 4) || c.v_bits > c.bits)
       return KVQ_ERR_UNSUPPORTED;
@@ -136,6 +137,15 @@ int32_t make_geometry(const kvq_config& c, Geometry* g) {
       x.off_vs = codes + vcodes;
       x.off_ks = x.off_kz = x.off_vz = -1;
       x.page_bytes = codes + vcodes + 256;
+      x.ring_slots = 0;
+      break;
+    case KVQ_FP8K_KIVIV:   // FP8 K rows, KIVI V cols, V scale and offset per token
+      x.off_kc = 0;
+      x.off_vc = codes;
+      x.off_vs = codes + vcodes;
+      x.off_vz = codes + vcodes + 4 * kPage;
+      x.off_ks = x.off_kz = -1;
+      x.page_bytes = codes + vcodes + 8 * kPage;
       x.ring_slots = 0;
       break;
     default:  // FP8, either format (b = 8), and BF16_CACHE (b = 16): K rows, then V cols

@@ -18,7 +18,11 @@ __host__ __device__ constexpr bool is_fp8(int scheme) {
 }
 // Schemes whose keys take the per-head static key scale (FP8 keys).
 __host__ __device__ constexpr bool has_key_scale(int scheme) {
-  return is_fp8(scheme) || scheme == KVQ_FP8K_SYMV;
+  return is_fp8(scheme) || scheme == KVQ_FP8K_SYMV || scheme == KVQ_FP8K_KIVIV;
+}
+// FP8 keys with values of another cache type (symmetric or KIVI, per token).
+__host__ __device__ constexpr bool is_fp8_keys_mixed(int scheme) {
+  return scheme == KVQ_FP8K_SYMV || scheme == KVQ_FP8K_KIVIV;
 }
 
 // Everything a kernel needs to address one layer of the cache.

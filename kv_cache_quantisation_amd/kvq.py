@@ -15,11 +15,11 @@ LIB_PATH = os.path.join(PKG, "libkvq.so")
 
 KVQ_OK, KVQ_ERR_NULL, KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED = 0, -1, -2, -3
 KVQ_ERR_CAPACITY, KVQ_ERR_WORKSPACE, KVQ_ERR_DEVICE = -4, -5, -6
-KVQ_KIVI, KVQ_SYM_TOKEN, KVQ_FP8_E4M3, KVQ_BF16_CACHE, KVQ_FP8_E5M2, KVQ_FP8K_SYMV = 0, 1, 2, 3, 4, 5
+KVQ_KIVI, KVQ_SYM_TOKEN, KVQ_FP8_E4M3, KVQ_BF16_CACHE, KVQ_FP8_E5M2, KVQ_FP8K_SYMV, KVQ_FP8K_KIVIV = 0, 1, 2, 3, 4, 5, 6
 KVQ_F32, KVQ_BF16 = 0, 1
 KVQ_BYTES_FORMULA, KVQ_BYTES_CACHE, KVQ_BYTES_WORKSPACE = 0, 1, 2
 
-ABI_VERSION = 10  # KVQ_ABI_VERSION of include/kvq.h that this binding mirrors
+ABI_VERSION = 11  # KVQ_ABI_VERSION of include/kvq.h that this binding mirrors
 
 SYMBOLS = ("kvq_cache_bytes", "kvq_quantize_append", "kvq_quantize_append_ragged",
            "kvq_decode_attention", "kvq_decode_attention_ragged", "kvq_decode_attention_multi",

@@ -23,7 +23,7 @@ from dataclasses import dataclass, replace
 
 import torch
 
-KIVI, SYM_TOKEN, FP8_E4M3, BF16_CACHE, FP8_E5M2, FP8K_SYMV = 0, 1, 2, 3, 4, 5
+KIVI, SYM_TOKEN, FP8_E4M3, BF16_CACHE, FP8_E5M2, FP8K_SYMV, FP8K_KIVIV = 0, 1, 2, 3, 4, 5, 6
 
 
 @dataclass(frozen=True)

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert kvq.kvq_abi_version() == 10
+    assert kvq.kvq_abi_version() == 11
     assert kvq.status_string(0) == "ok"
     for st in (-1, -2, -3, -4, -5, -6):
         assert kvq.status_string(st) != "unknown status"
@@ -396,26 +396,29 @@ def test_append_decode_validation():
 
 @pytest.mark.parametrize("vb,d,dtype", [(2, 128, kvq.KVQ_BF16), (3, 64, kvq.KVQ_F32), (4, 32, kvq.KVQ_BF16),
                                         (8, 256, kvq.KVQ_F32), (0, 64, kvq.KVQ_BF16)])
-def test_fp8k_symv_sizes(vb, d, dtype):
-    """FP8 keys with symmetric values: layout size and KV-bytes equation (keys
+@pytest.mark.parametrize("scheme", ["symv", "kiviv"])
+def test_fp8k_mixed_sizes(vb, d, dtype, scheme):
+    """FP8 keys with symmetric or KIVI values: layout size and KV-bytes equation (keys
     at 8 bits, values at v_bits; v_bits 0 means 8) as the oracle has them;
     every page a multiple of 256 bytes."""
-    c = cfg(scheme=kvq.KVQ_FP8K_SYMV, bits=8, v_bits=vb, head_dim=d, residual=0, in_dtype=dtype,
+    sch = {"symv": (kvq.KVQ_FP8K_SYMV, acc.FP8K_SYMV), "kiviv": (kvq.KVQ_FP8K_KIVIV, acc.FP8K_KIVIV)}[scheme]
+    c = cfg(scheme=sch[0], bits=8, v_bits=vb, head_dim=d, residual=0, in_dtype=dtype,
             q_heads=8)
     v = vb or 8
     item = 2 if dtype == kvq.KVQ_BF16 else 4
-    assert acc.page_bytes(acc.FP8K_SYMV, d, 8, v) % 256 == 0
+    assert acc.page_bytes(sch[1], d, 8, v) % 256 == 0
     for T in (0, 1, 31, 32, 33, 161, 4096):
         assert kvq.kvq_cache_bytes(c, T, kvq.KVQ_BYTES_CACHE) == \
-            acc.layout_cache_bytes(acc.FP8K_SYMV, 2, 3, 8, d, 8, T, 0, item, v), T
+            acc.layout_cache_bytes(sch[1], 2, 3, 8, d, 8, T, 0, item, v), T
         assert kvq.kvq_cache_bytes(c, T, kvq.KVQ_BYTES_FORMULA) == \
             acc.kv_bytes_formula(2, 8, d, T, 8, batch=3, v_bits=v)
 
 
-def test_fp8k_symv_validation():
+@pytest.mark.parametrize("scheme", ["symv", "kiviv"])
+def test_fp8k_mixed_validation(scheme):
     L = kvq.lib()
     def st(**kw):
-        base = dict(scheme=kvq.KVQ_FP8K_SYMV, bits=8, residual=0)
+        base = dict(scheme=kvq.KVQ_FP8K_SYMV if scheme == "symv" else kvq.KVQ_FP8K_KIVIV, bits=8, residual=0)
         base.update(kw)
         c = cfg(**base)
         return L.kvq_cache_bytes(ctypes.byref(c), 64, kvq.KVQ_BYTES_CACHE)
@@ -427,12 +430,14 @@ def test_fp8k_symv_validation():
     assert st(outliers=1) == kvq.KVQ_ERR_INVALID
 
 
-def test_fp8k_symv_needs_the_key_scale_only():
+@pytest.mark.parametrize("scheme", ["symv", "kiviv"])
+def test_fp8k_mixed_needs_the_key_scale_only(scheme):
     """The key scale is required (KVQ_ERR_NULL without it, nothing launched);
     the value scale is not read (validation passes it as NULL and stops at the
     next check, a null cache)."""
     L = kvq.lib()
-    c = cfg(scheme=kvq.KVQ_FP8K_SYMV, bits=8, v_bits=4, residual=0)
+    c = cfg(scheme=kvq.KVQ_FP8K_SYMV if scheme == "symv" else kvq.KVQ_FP8K_KIVIV, bits=8, v_bits=4,
+            residual=0)
     fake = ctypes.c_void_p(16)
     ks = ctypes.cast(ctypes.c_void_p(16), ctypes.POINTER(ctypes.c_float))
     nul = ctypes.POINTER(ctypes.c_float)()

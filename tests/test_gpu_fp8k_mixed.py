@@ -1,9 +1,11 @@
-"""GPU parity of keys and values in different cache types (KVQ_FP8K_SYMV:
-FP8 E4M3 keys with the KV head's static key scale, symmetric per-token
-values at v_bits), through the C ABI: every defined byte of the cache equals
-the oracle's image for several chunkings; decode within max-abs 2e-3 of the
-oracle's fp64 attention over the dequantised cache (GQA 1-8, split counts,
-rotary keys, several queries per sequence, a ragged batch)."""
+"""GPU parity of keys and values in different cache types: FP8 E4M3 keys
+with the KV head's static key scale and per-token values at v_bits, either
+symmetric (KVQ_FP8K_SYMV) or KIVI's asymmetric codes with a per-token scale
+and offset (KVQ_FP8K_KIVIV), through the C ABI: every defined byte of the
+cache equals the oracle's image for several chunkings; decode within max-abs
+2e-3 of the oracle's fp64 attention over the dequantised cache (GQA 1-8,
+split counts, rotary keys, several queries per sequence, ragged and paged
+batches)."""
 
 import pytest
 import torch
@@ -22,8 +24,11 @@ CHUNKINGS = {
 }
 
 
-def mixed(vb, d, dtype=torch.bfloat16, B=2, Hkv=2, hg=2, T=260, rope=0.0):
-    return synth.Workload(f"mx{vb}d{d}", 80 + vb, synth.FP8K_SYMV, 8, B, Hkv * hg, Hkv, d, T,
+SCHEMES = {"symv": synth.FP8K_SYMV, "kiviv": synth.FP8K_KIVIV}
+
+
+def mixed(vb, d, dtype=torch.bfloat16, B=2, Hkv=2, hg=2, T=260, rope=0.0, scheme=synth.FP8K_SYMV):
+    return synth.Workload(f"mx{scheme}v{vb}d{d}", 80 + vb + 10 * scheme, scheme, 8, B, Hkv * hg, Hkv, d, T,
                           in_dtype=dtype, q_dtype=dtype, k_outlier_channels=min(4, d // 16),
                           k_outlier_factor=20.0, v_outlier_frac=0.01, v_outlier_factor=10.0,
                           rope_theta=rope, v_bits=vb)
@@ -41,14 +46,15 @@ def run(w, chunks, capacity):
     return cfg, cache, oc, k, v, ks
 
 
+@pytest.mark.parametrize("scheme", list(SCHEMES))
 @pytest.mark.parametrize("chunking", list(CHUNKINGS))
 @pytest.mark.parametrize("vb,d,dtype", [(2, 128, torch.bfloat16), (3, 64, torch.float32),
                                         (4, 32, torch.bfloat16), (8, 256, torch.float32)])
-def test_append_bytes(vb, d, dtype, chunking):
-    w = mixed(vb, d, dtype)
+def test_append_bytes(vb, d, dtype, chunking, scheme):
+    w = mixed(vb, d, dtype, scheme=SCHEMES[scheme])
     cfg, cache, oc, *_ = run(w, CHUNKINGS[chunking](w.tokens), capacity=288)
     want, mask = oc.cache_image()
-    H.compare_bytes(cache.cpu().numpy(), want, mask, f"fp8k_symv v{vb} d{d} {chunking}")
+    H.compare_bytes(cache.cpu().numpy(), want, mask, f"fp8k_{scheme} v{vb} d{d} {chunking}")
 
 
 DECODE = [
@@ -62,21 +68,23 @@ DECODE = [
 ]
 
 
+@pytest.mark.parametrize("scheme", list(SCHEMES))
 @pytest.mark.parametrize("vb,d,hg,dtype,T,rope,splits", DECODE)
-def test_decode(vb, d, hg, dtype, T, rope, splits):
-    w = mixed(vb, d, dtype, hg=hg, T=T, rope=rope)
+def test_decode(vb, d, hg, dtype, T, rope, splits, scheme):
+    w = mixed(vb, d, dtype, hg=hg, T=T, rope=rope, scheme=SCHEMES[scheme])
     cfg, cache, oc, k, v, ks = run(w, [T], capacity=T + 40)
     cfg.num_splits = splits
     q = synth.query(w, device=DEV)
     out = H.decode(cfg, cache, 0, T, q, ks=ks)
     err = H.max_err(out, oc.decode(0, H.values(q), rope_theta=rope))
-    print(f"[fp8k_symv decode] v{vb} d{d} hg{hg} rope {rope}: max-abs error {err:.2e}", flush=True)
+    print(f"[fp8k_{scheme} decode] v{vb} d{d} hg{hg} rope {rope}: max-abs error {err:.2e}", flush=True)
     assert err <= H.ATOL, err
 
 
-def test_decode_multi_and_ragged():
+@pytest.mark.parametrize("scheme", list(SCHEMES))
+def test_decode_multi_and_ragged(scheme):
     from oracle.cache import RaggedCache
-    w = mixed(4, 128, torch.bfloat16, B=3, hg=4, T=400)
+    w = mixed(4, 128, torch.bfloat16, B=3, hg=4, T=400, scheme=SCHEMES[scheme])
     cfg, cache, oc, k, v, ks = run(w, [w.tokens], capacity=440)
     nq = 5
     qm = torch.stack([synth.query(w, device=DEV, tag=1 + i) for i in range(nq)], dim=1).contiguous()
@@ -90,7 +98,7 @@ def test_decode_multi_and_ragged():
     lens = [400, 150, 33]
     cfg2 = H.config(w, 440)
     cache2 = kvq.alloc_cache(cfg2)
-    rc = RaggedCache(synth.FP8K_SYMV, 8, 1, 3, w.kv_heads, w.head_dim, 440, in_dtype="bf16", v_bits=4)
+    rc = RaggedCache(SCHEMES[scheme], 8, 1, 3, w.kv_heads, w.head_dim, 440, in_dtype="bf16", v_bits=4)
     kn, vn = k.clone(), v.clone()
     for b, n in enumerate(lens):
         kn[b, n:] = float("nan")
@@ -100,7 +108,7 @@ def test_decode_multi_and_ragged():
     seq = torch.tensor(lens, dtype=torch.int64, device=DEV)
     kvq.kvq_quantize_append_ragged(cfg2, cache2, 0, zeros, seq, kn.contiguous(), vn.contiguous(), k_scale=ks)
     want, mask = rc.cache_image()
-    H.compare_bytes(cache2.cpu().numpy(), want, mask, "fp8k_symv ragged")
+    H.compare_bytes(cache2.cpu().numpy(), want, mask, f"fp8k_{scheme} ragged")
     q = synth.query(w, device=DEV)
     out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
     ws2 = kvq.alloc_workspace(cfg2, max(lens), device=DEV)
@@ -108,15 +116,16 @@ def test_decode_multi_and_ragged():
     assert H.max_err(out, rc.decode(0, H.values(q))) <= H.ATOL
 
 
-def test_paged():
+@pytest.mark.parametrize("scheme", list(SCHEMES))
+def test_paged(scheme):
     """A paged cache (block table over a shared pool) with FP8 keys and
-    symmetric values: bytes equal the oracle's paged image, decode equals the
+    per-token values: bytes equal the oracle's paged image, decode equals the
     slab layout's bit for bit and the oracle within 2e-3."""
     import numpy as np
     from oracle.cache import RaggedCache, paged_image
     from test_gpu_ragged import B, CALLS, CAP, ragged_inputs
     T = max(sum(c[b] for c in CALLS) for b in range(B))
-    w = mixed(2, 64, torch.bfloat16, B=B, hg=4, T=T)
+    w = mixed(2, 64, torch.bfloat16, B=B, hg=4, T=T, scheme=SCHEMES[scheme])
     cfg = H.config(w, CAP)
     pages = -(-CAP // 32)
     nb = B * pages + 5
@@ -126,7 +135,7 @@ def test_paged():
     slab = kvq.alloc_cache(cfg)
     k, v = synth.keys_values(w, device=DEV)
     ks = synth.fp8_scales(k, v)[0].to(DEV)
-    oc = RaggedCache(synth.FP8K_SYMV, 8, 1, B, w.kv_heads, w.head_dim, CAP, in_dtype="bf16", v_bits=2)
+    oc = RaggedCache(SCHEMES[scheme], 8, 1, B, w.kv_heads, w.head_dim, CAP, in_dtype="bf16", v_bits=2)
     past = [0] * B
     for counts in CALLS:
         kn, vn = ragged_inputs(w, k, v, past, counts)
@@ -139,7 +148,7 @@ def test_paged():
             past[b] += n
     torch.cuda.synchronize()
     want, mask = paged_image(oc, table_h, nb)
-    H.compare_bytes(paged.cpu().numpy(), want, mask, "fp8k_symv paged")
+    H.compare_bytes(paged.cpu().numpy(), want, mask, f"fp8k_{scheme} paged")
     q = synth.query(w, device=DEV)
     seq = torch.tensor(past, dtype=torch.int64, device=DEV)
     out_p = torch.empty(q.shape, dtype=torch.float32, device=DEV)
