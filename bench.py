@@ -67,11 +67,11 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 # change to those, `traffic` is reported as null until they are taken again.
 ROOFLINE_EXTRA = 64            # roofline context = workload tokens + this
 COUNTERS = {
-    "kivi2": {"context": 4096 + ROOFLINE_EXTRA, "fetch_kib": 30826.3125, "write_kib": 892.0,
+    "kivi2": {"context": 4096 + ROOFLINE_EXTRA, "fetch_kib": 30750.0, "write_kib": 905.5,
               "fetch_scale": 262144 / 131084, "write_scale": 1.0,
-              "sources_sha256": "ad22a81afb0fcc76276f08cc5693a6ab0de21724cc6ac1021697a49b42074993"},
+              "sources_sha256": "0e387ac4bc1887a6f0e30cd347e5652be2a682c9cf683954c185d840a6a7f8cb"},
 }
-DECODE_SOURCES = ["decode_mfma.hip", "kvq_device.h", "kvq_internal.h", "kvq_wave.h"]
+DECODE_SOURCES = ["decode_mfma.hip", "kvq_device.h", "kvq_internal.h", "kvq_merge.h", "kvq_wave.h"]
 
 
 def decode_sources_sha256():
