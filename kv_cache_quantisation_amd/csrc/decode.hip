@@ -1,6 +1,6 @@
 // Decode attention: chooses the kernel of a call -- the matrix-core kernels
-// (decode_mfma.hip: KIVI 2/4-bit pages of 16-bit inputs; decode_fp8.hip: FP8
-// and bfloat16 pages) where they apply, else the generic vector-ALU kernel
+// (decode_mfma.hip: KIVI 2/4-bit pages of 16-bit inputs; decode_fp8.hip: FP8,
+// bfloat16 and 2/4-bit per-token-code pages) where they apply, else the generic vector-ALU kernel
 // (decode_generic.h) -- and fills its launch parameters.
 #include <hip/hip_runtime.h>
 

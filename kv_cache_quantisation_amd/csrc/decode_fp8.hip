@@ -1,4 +1,5 @@
-// Decode attention over an FP8 E4M3 cache on the matrix cores (gfx950).
+// Decode attention over FP8, bfloat16 and per-token-code caches on the matrix
+// cores (gfx950).
 //
 // softmax(sm_scale q.K^T) V over the dequantised cache ("Quantizing the KV
 // cache", going deeper; FP8 cache with a scale per KV head, "How the KV cache
@@ -72,15 +73,28 @@ struct Fp8Params {
   PageMap pm;                     // pages of the layer (slab or paged)
 };
 
-template <bool BF16, int D>
+// Page layout of cache type FMT (key codes of KB bits for SYM_TOKEN, value
+// codes of VB bits for the per-token value types), as include/kvq.h lays it out.
+template <int FMT, int D, int KB, int VB>
 struct PagedGeom {
-  static constexpr int EB = BF16 ? 2 : 1;            // bytes per cached value
-  static constexpr int KROW = D * EB;                // bytes per key token row
-  static constexpr int OFF_VC = 32 * KROW;           // V cols after the K rows
-  static constexpr int BYTES = BF16 ? OFF_VC : 2 * OFF_VC;   // staged in LDS per page
-  static constexpr int DMA = BYTES / 1024;           // 16-byte-per-lane copies
+  static constexpr bool BF16 = FMT == KVQ_BF16_CACHE;
+  static constexpr bool SYMK = FMT == KVQ_SYM_TOKEN;
+  static constexpr int KROW = BF16 ? 2 * D : SYMK ? D * KB / 8 : D;   // bytes per key token row
+  static constexpr int KCODES = 32 * KROW;           // the K rows (chunk-permuted in LDS)
+  static constexpr int OFF_KS = KCODES;              // SYM_TOKEN: fp32 key scale per token
+  static constexpr int OFF_VC = SYMK ? OFF_KS + 128 : KCODES;   // V cols
+  static constexpr int VCODES = BF16 ? 64 * D : (FMT == KVQ_FP8_E4M3 || FMT == KVQ_FP8_E5M2) ? 32 * D
+                                                                                               : 32 * D * VB / 8;
+  static constexpr int OFF_VS = OFF_VC + VCODES;     // per-token value scale (code values)
+  static constexpr int OFF_VZ = OFF_VS + 128;        // per-token value offset (FP8K_KIVIV)
+  // staged in LDS per page: bfloat16 keys only; FP8 keys and values; per-token
+  // codes with their scales (and offsets)
+  static constexpr int BYTES = BF16 ? KCODES : (FMT == KVQ_FP8_E4M3 || FMT == KVQ_FP8_E5M2) ? OFF_VS
+                             : FMT == KVQ_FP8K_KIVIV ? OFF_VZ + 128 : OFF_VS + 128;
+  static constexpr int DMA = (BYTES + 1023) / 1024;  // 16-byte-per-lane copies (the last may be partial)
   static constexpr int NBUF = 2;
   static constexpr int WAVE_LDS = NBUF * BYTES;
+  static_assert(BYTES % 16 == 0, "whole 16-byte chunks");
 };
 
 // Two FP8 bytes (low or high half of w; E4M3, or E5M2 when E5) -> packed
@@ -96,16 +110,33 @@ __device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
   else return bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
-// FMT: KVQ_FP8_E4M3, KVQ_FP8_E5M2 or KVQ_BF16_CACHE. The E5M2 key scale is
-// applied to the scores after the product instead of to q: with the scales
-// that E5M2's range calls for (max |x| / 57344), q * ks would fall among the
-// f16 subnormals.
-template <int FMT, int D, int HG>
+// FMT: KVQ_FP8_E4M3, KVQ_FP8_E5M2 or KVQ_BF16_CACHE; or a cache whose
+// values are codes with a scale per token: KVQ_SYM_TOKEN (keys too: KB-bit
+// codes with a scale per token), KVQ_FP8K_SYMV and KVQ_FP8K_KIVIV (E4M3 keys
+// with the KV head's key scale; VB-bit values, symmetric or with a
+// per-token offset). The E5M2 key scale is applied to the scores after the
+// product instead of to q: with the scales that E5M2's range calls for
+// (max |x| / 57344), q * ks would fall among the f16 subnormals.
+// Per-token codes (2 or 4 bits) convert exactly to f16 / bf16 as unsigned
+// fields; a two's-complement field with its top bit flipped is the code plus
+// 2^(b-1), so for symmetric codes
+//   key:   q . (s_t k_t)  = s_t (q . u_t - 2^(KB-1) sum_c q_c)
+//   value: sum_t p_t s_t v_t = sum_t (p_t s_t) u_t - sum_t p_t s_t 2^(VB-1)
+// (u the flipped field), the value term being the per-token offset
+// z_t = -2^(VB-1) s_t that KIVI values carry explicitly. The unsigned code
+// converts give the channel (token) order {0,2,1,3,4,6,5,7} within each 8,
+// which the query (weight) operand follows.
+template <int FMT, int D, int HG, int KB = 8, int VB = 8>
 __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   static_assert(2 * HG <= 16, "high and remainder columns of the GQA group fit one tile");
   constexpr bool BF16 = FMT == KVQ_BF16_CACHE;
   constexpr bool E5 = FMT == KVQ_FP8_E5M2;
-  using PG = PagedGeom<BF16, D>;
+  constexpr bool SYMK = FMT == KVQ_SYM_TOKEN;                    // key codes, a scale per token
+  constexpr bool CODEV = SYMK || FMT == KVQ_FP8K_SYMV || FMT == KVQ_FP8K_KIVIV;   // value codes
+  constexpr bool ASYMV = FMT == KVQ_FP8K_KIVIV;                  // value offset per token
+  static_assert(!SYMK || KB == 2 || KB == 4, "2- or 4-bit key codes");
+  static_assert(!CODEV || VB == 2 || VB == 4, "2- or 4-bit value codes");
+  using PG = PagedGeom<FMT, D, KB, VB>;
   constexpr int KS = D / 32;             // k-steps of the key product
   constexpr int NT = D / 16;             // channel tiles of the value product
   constexpr int CPG = D / 4;             // key channels per lane group (contiguous bytes)
@@ -140,7 +171,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   // the cache's open last page (fewer than 32 tokens) keeps FP8 values in
   // token rows (-1: every page is full)
   int open_page = -1;
-  if constexpr (!BF16) {
+  if constexpr (FMT == KVQ_FP8_E4M3 || FMT == KVQ_FP8_E5M2) {
     const int64_t fill = seq_len(p.seq_tokens, b, p.T);
     if (fill % kPage != 0) open_page = static_cast<int>(fill / kPage);
   }
@@ -154,8 +185,8 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
 #pragma unroll
     for (int i = 0; i < PG::DMA; ++i) {
       const int off = i * 1024 + lane * 16;   // key rows: chunk permutation (see kswz)
-      const int from = off < PG::OFF_VC ? krow_off<PG::KROW / 16>(off / PG::KROW, off % PG::KROW) : off;
-      dma16(src + from, dst + i * 1024);
+      const int from = off < PG::KCODES ? krow_off<PG::KROW / 16>(off / PG::KROW, off % PG::KROW) : off;
+      if (i + 1 < PG::DMA || off < PG::BYTES) dma16(src + from, dst + i * 1024);
     }
   };
   // bf16 values: lane (j, g) loads tokens 8g..8g+7 of channel 16 nt + j (16 bytes)
@@ -173,7 +204,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
 
   // ---- query group: q * sm_scale * log2(e) * ks_h ----------------------------
   {
-    const float mult = (BF16 || E5) ? p.qscale : p.qscale * p.k_scale[h];
+    const float mult = (BF16 || E5 || SYMK) ? p.qscale : p.qscale * p.k_scale[h];
     const int64_t q0 = (static_cast<int64_t>(row) * p.q_heads + h * HG) * D;
     for (int i = tid; i < HG * D; i += kThreads) {
       const float x = p.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(p.q)[q0 + i])
@@ -203,6 +234,16 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
       esc = __builtin_amdgcn_readfirstlane(ex - 15);
     }
   }
+  // SYM_TOKEN keys: 2^(KB-1) times the sum of head j % HG's scaled query
+  float kbias = 0.f;
+  if constexpr (SYMK) {
+    float sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPG; ++i) sq += qs[j % HG][g * CPG + i];
+    sq += xor16(sq);
+    sq += xor32(sq);
+    kbias = sq * static_cast<float>(1 << (KB - 1));
+  }
   {
     const int hh = j % HG, part = j / HG;
 #pragma unroll
@@ -210,8 +251,11 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
       uint32_t w4[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float a = ldexpf(qs[hh][g * CPG + 8 * ks + 2 * i], -esc);
-        const float c = ldexpf(qs[hh][g * CPG + 8 * ks + 2 * i + 1], -esc);
+        // pair i: channels (2i, 2i+1), or for key codes the converts' order
+        // (0,2), (1,3), (4,6), (5,7)
+        const int c0 = SYMK ? (i & 2) * 2 + (i & 1) : 2 * i, c1 = SYMK ? c0 + 2 : 2 * i + 1;
+        const float a = ldexpf(qs[hh][g * CPG + 8 * ks + c0], -esc);
+        const float c = ldexpf(qs[hh][g * CPG + 8 * ks + c1], -esc);
         uint32_t hi, lo;
         if constexpr (BF16) split_bf16(a, c, hi, lo);
         else split_f16(a, c, hi, lo);
@@ -225,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   floatx4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m_lane = -INFINITY, l_lane = 0.f;
+  float m_lane = -INFINITY, l_lane = 0.f, z_lane = 0.f;
 
   auto process_page = [&](const uint8_t* pg, int n_valid, const uint4* vr, bool vrows) {
     (void)vrows;   // bfloat16 caches: value columns on every page
@@ -241,6 +285,19 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
           const uint4 w = *reinterpret_cast<const uint4*>(
               pg + krow_off<PG::KROW / 16>(row, 2 * (g * CPG + 8 * ks)));
           c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), bq[ks], c, 0, 0, 0);
+        } else if constexpr (SYMK && KB == 4) {   // one word: the 8 channels of this k-step
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(
+                                 pg + krow_off<PG::KROW / 16>(row, (g * CPG + 8 * ks) / 2)) ^ 0x88888888u;
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes4_frag(w), bq[ks], c, 0, 0, 0);
+        } else if constexpr (SYMK) {   // one word: the 16 channels of k-steps ks, ks + 1
+          if (ks % 2 == 0) {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(
+                                   pg + krow_off<PG::KROW / 16>(row, (g * CPG + 8 * ks) / 4)) ^ 0xAAAAAAAAu;
+            half8 a0, a1;
+            codes2_frags(w, a0, a1);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bq[ks], c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bq[ks + 1], c, 0, 0, 0);
+          }
         } else {
           const uint2 w = *reinterpret_cast<const uint2*>(pg + krow_off<D / 16>(row, g * CPG + 8 * ks));
           const half8 a = cat4h(fp8x2_f16<E5, false>(w.x), fp8x2_f16<E5, true>(w.x),
@@ -259,6 +316,13 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) s[i] = ldexpf(s[i], esc);
     }
+    if constexpr (SYMK) {   // s_t (q . u_t - 2^(KB-1) sum q) for tokens 8g..8g+7
+      const float4 k0 = *reinterpret_cast<const float4*>(pg + PG::OFF_KS + 32 * g);
+      const float4 k1 = *reinterpret_cast<const float4*>(pg + PG::OFF_KS + 32 * g + 16);
+      const float kst[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[i] = kst[i] * (s[i] - kbias);
+    }
     if (n_valid < kPage) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) s[i] = 8 * g + i < n_valid ? s[i] : -INFINITY;
@@ -275,6 +339,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
       const float m_new = fmaxf(m_lane, pmax);
       const float alpha = fast_exp2(m_lane - m_new);
       l_lane *= alpha;
+      z_lane *= alpha;
       m_lane = m_new;
       auto alpha_of = [&](int hh) {   // head hh's factor, read from lane hh
         return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), hh));
@@ -298,10 +363,43 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
       s[i] = fast_exp2(s[i] - m_lane);
       l_lane += s[i];
     }
+    // per-token value codes: P' = p s_t (tokens 8g..8g+7), sum of p z_t; an
+    // absent token's scale and offset are taken as 0 (its bytes are undefined)
+    if constexpr (CODEV) {
+      const float4 v0 = *reinterpret_cast<const float4*>(pg + PG::OFF_VS + 32 * g);
+      const float4 v1 = *reinterpret_cast<const float4*>(pg + PG::OFF_VS + 32 * g + 16);
+      float vsv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      float vzv[8];
+      if constexpr (ASYMV) {
+        const float4 z0 = *reinterpret_cast<const float4*>(pg + PG::OFF_VZ + 32 * g);
+        const float4 z1 = *reinterpret_cast<const float4*>(pg + PG::OFF_VZ + 32 * g + 16);
+        vzv[0] = z0.x; vzv[1] = z0.y; vzv[2] = z0.z; vzv[3] = z0.w;
+        vzv[4] = z1.x; vzv[5] = z1.y; vzv[6] = z1.z; vzv[7] = z1.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) vzv[i] = -static_cast<float>(1 << (VB - 1)) * vsv[i];
+      }
+      if (n_valid < kPage) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const bool ok = 8 * g + i < n_valid;
+          vsv[i] = ok ? vsv[i] : 0.f;
+          vzv[i] = ok ? vzv[i] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) z_lane = fmaf(s[i], vzv[i], z_lane);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[i] *= vsv[i];
+    }
     // P rows: j < HG high part of head j, HG <= j < 2HG remainder of head j-HG
+    // (value codes: tokens in the converts' order {0,2,1,3,4,6,5,7})
     uint32_t ph[4], pl[4], pa[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) split_bf16(s[2 * i], s[2 * i + 1], ph[i], pl[i]);
+    for (int i = 0; i < 4; ++i) {
+      const int t0 = CODEV ? (i & 2) * 2 + (i & 1) : 2 * i, t1 = CODEV ? t0 + 2 : 2 * i + 1;
+      split_bf16(s[t0], s[t1], ph[i], pl[i]);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) pa[i] = shr_keep<HG>(ph[i], pl[i]);
     const bf16x8 ap = __builtin_bit_cast(bf16x8, uint4{pa[0], pa[1], pa[2], pa[3]});
@@ -320,6 +418,43 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
         const uint4 bw = uint4{vr[nt].x & mw[0], vr[nt].y & mw[1], vr[nt].z & mw[2], vr[nt].w & mw[3]};
         acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, __builtin_bit_cast(bf16x8, bw), acc[nt],
                                                            0, 0, 0);
+      }
+    } else if constexpr (CODEV) {
+      (void)vr;
+      // value codes of tokens 8g..8g+7 of channel 16 nt + j (the column's
+      // bits [8 VB g, 8 VB (g + 1))); symmetric codes with the top bit flipped
+      constexpr int VROW = 32 * VB / 8;   // bytes per channel column
+      constexpr uint32_t FLIP = ASYMV ? 0u : (VB == 4 ? 0x88888888u : 0xAAAAAAAAu);
+      if constexpr (VB == 4) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(pg + PG::OFF_VC + (16 * nt + j) * VROW + 4 * g) ^ FLIP;
+          const uint32_t y0 = w & 0x0F0F0F0Fu, y1 = (w >> 4) & 0x0F0F0F0Fu;
+          const uint4 bw{bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y0, 512.0f, false)),
+                         bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y1, 512.0f, false)),
+                         bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y0, 512.0f, true)),
+                         bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y1, 512.0f, true))};
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, __builtin_bit_cast(bf16x8, bw), acc[nt], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < NT; nt += 2) {   // two channel tiles per word
+          const uint8_t* col = pg + PG::OFF_VC + (16 * nt + j) * VROW + 2 * g;
+          const uint32_t x = (uint32_t(*reinterpret_cast<const uint16_t*>(col)) |
+                              (uint32_t(*reinterpret_cast<const uint16_t*>(col + 16 * VROW)) << 16)) ^ FLIP;
+          const uint32_t y0 = x & 0x33333333u, y1 = (x >> 2) & 0x33333333u;
+          const uint4 b0{bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y0, 2.0f, 0)),
+                         bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 0)),
+                         bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y0, 2.0f, 1)),
+                         bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 1))};
+          const uint4 b1{bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y0, 2.0f, 2)),
+                         bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 2)),
+                         bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y0, 2.0f, 3)),
+                         bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 3))};
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, __builtin_bit_cast(bf16x8, b0), acc[nt], 0, 0, 0);
+          acc[nt + 1] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, __builtin_bit_cast(bf16x8, b1), acc[nt + 1], 0, 0, 0);
+        }
       }
     } else {
       (void)vr;
@@ -388,15 +523,20 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   wait_lds();
 
   // ---- wave epilogue -----------------------------------------------------------
-  float lsum[HG], mh[HG];
+  float lsum[HG], mh[HG], zsum[HG];
   {
-    float l_ = l_lane;
+    float l_ = l_lane, z_ = z_lane;
     l_ += xor16(l_);
     l_ += xor32(l_);
+    if constexpr (CODEV) {
+      z_ += xor16(z_);
+      z_ += xor32(z_);
+    }
 #pragma unroll
     for (int hh = 0; hh < HG; ++hh) {
       lsum[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_), hh));
       mh[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_lane), hh));
+      zsum[hh] = CODEV ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, z_), hh)) : 0.f;
     }
   }
   __syncthreads();   // every wave is done with its page buffers (the arena)
@@ -425,7 +565,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int hh = 4 * g + r;
-        if (hh < HG) R(wave, hh)[2 + c] = v[r];
+        if (hh < HG) R(wave, hh)[2 + c] = v[r] + zsum[hh];   // + sum of p z (value codes)
       }
     }
   }
@@ -443,7 +583,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   if (p.splits > 1 && tid == 0) arrived = count_arrival(&p.counters[unit]);
 
   // ---- combine the waves: this thread's elements i = tid + e * kThreads ----
-  const float vs_h = BF16 ? 1.0f : p.v_scale[h];
+  const float vs_h = (BF16 || CODEV) ? 1.0f : p.v_scale[h];
   constexpr int PER = (HG * D + kThreads - 1) / kThreads;
   float own_m[PER], own_l[PER], own_o[PER];
 #pragma unroll
@@ -485,33 +625,38 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
                                   row, split, own_m, own_l, own_o, tid);
 }
 
-template <int FMT, int D>
+template <int FMT, int D, int KB, int VB>
 hipError_t by_hg(const Fp8Params& p, int hg, int batch, hipStream_t st) {
   dim3 grid(p.splits, p.kv_heads, batch);
   switch (hg) {
-    case 1: hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 1>), grid, dim3(kThreads), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 2>), grid, dim3(kThreads), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 4>), grid, dim3(kThreads), 0, st, p); break;
-    default: hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 8>), grid, dim3(kThreads), 0, st, p); break;
+    case 1: hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 1, KB, VB>), grid, dim3(kThreads), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 2, KB, VB>), grid, dim3(kThreads), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 4, KB, VB>), grid, dim3(kThreads), 0, st, p); break;
+    default: hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 8, KB, VB>), grid, dim3(kThreads), 0, st, p); break;
   }
   return hipGetLastError();
 }
 
-template <int FMT>
+template <int FMT, int KB = 8, int VB = 8>
 hipError_t by_d(const Fp8Params& p, int d, int hg, int batch, hipStream_t st) {
   switch (d) {
-    case 64: return by_hg<FMT, 64>(p, hg, batch, st);
-    case 128: return by_hg<FMT, 128>(p, hg, batch, st);
-    default: return by_hg<FMT, 256>(p, hg, batch, st);
+    case 64: return by_hg<FMT, 64, KB, VB>(p, hg, batch, st);
+    case 128: return by_hg<FMT, 128, KB, VB>(p, hg, batch, st);
+    default: return by_hg<FMT, 256, KB, VB>(p, hg, batch, st);
   }
 }
 
 }  // namespace
 
-// FP8 (either format) and bf16 caches (head_dim >= 64, no rotary embedding)
-// take the matrix-core paged kernel.
+// FP8 (either format) and bf16 caches, and caches of per-token codes at 2 or
+// 4 bits (symmetric keys and values; FP8 keys with symmetric or KIVI values)
+// take the matrix-core paged kernel (head_dim >= 64, no rotary embedding).
 bool fp8_mfma_path(const Geometry& g) {
-  return (is_fp8(g.scheme) || g.scheme == KVQ_BF16_CACHE) && g.rope == 0.0 && g.d >= 64;
+  if (g.rope != 0.0 || g.d < 64) return false;
+  if (is_fp8(g.scheme) || g.scheme == KVQ_BF16_CACHE) return true;
+  if (g.scheme == KVQ_SYM_TOKEN) return g.bits == 2 || g.bits == 4;
+  if (is_fp8_keys_mixed(g.scheme)) return g.vbits == 2 || g.vbits == 4;
+  return false;
 }
 
 int32_t fp8_mfma_splits(const Geometry& g, int64_t tokens, int32_t requested) {
@@ -559,10 +704,20 @@ hipError_t launch_fp8_mfma(const DecodeArgs& a, hipStream_t st) {
   p.q_heads = g.q_heads;
   p.q_bf16 = a.q_dtype == KVQ_BF16;
   p.qscale = a.sm_scale * kLog2e;
+  const int rows_n = g.batch * nq;
   switch (g.scheme) {
-    case KVQ_BF16_CACHE: return by_d<KVQ_BF16_CACHE>(p, g.d, g.hg, g.batch * nq, st);
-    case KVQ_FP8_E5M2: return by_d<KVQ_FP8_E5M2>(p, g.d, g.hg, g.batch * nq, st);
-    default: return by_d<KVQ_FP8_E4M3>(p, g.d, g.hg, g.batch * nq, st);
+    case KVQ_BF16_CACHE: return by_d<KVQ_BF16_CACHE>(p, g.d, g.hg, rows_n, st);
+    case KVQ_FP8_E5M2: return by_d<KVQ_FP8_E5M2>(p, g.d, g.hg, rows_n, st);
+    case KVQ_SYM_TOKEN:
+      return g.bits == 2 ? by_d<KVQ_SYM_TOKEN, 2, 2>(p, g.d, g.hg, rows_n, st)
+                         : by_d<KVQ_SYM_TOKEN, 4, 4>(p, g.d, g.hg, rows_n, st);
+    case KVQ_FP8K_SYMV:
+      return g.vbits == 2 ? by_d<KVQ_FP8K_SYMV, 8, 2>(p, g.d, g.hg, rows_n, st)
+                          : by_d<KVQ_FP8K_SYMV, 8, 4>(p, g.d, g.hg, rows_n, st);
+    case KVQ_FP8K_KIVIV:
+      return g.vbits == 2 ? by_d<KVQ_FP8K_KIVIV, 8, 2>(p, g.d, g.hg, rows_n, st)
+                          : by_d<KVQ_FP8K_KIVIV, 8, 4>(p, g.d, g.hg, rows_n, st);
+    default: return by_d<KVQ_FP8_E4M3>(p, g.d, g.hg, rows_n, st);
   }
 }
 

@@ -111,29 +111,6 @@ struct PageGeom {
   static constexpr int WAVE_LDS = NBUF * BYTES + RING;
 };
 
-// 16 two-bit codes (one word) -> two 8-channel fragments, channel order
-// {0,2,1,3,4,6,5,7} within each 8.
-__device__ __forceinline__ void codes2_frags(uint32_t w, half8& f0, half8& f1) {
-  const uint32_t y0 = w & 0x33333333u, y1 = (w >> 2) & 0x33333333u;
-  f0 = cat4h(bits32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y0, 2.0f, 0)),
-             bits32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y1, 2.0f, 0)),
-             bits32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y0, 2.0f, 1)),
-             bits32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y1, 2.0f, 1)));
-  f1 = cat4h(bits32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y0, 2.0f, 2)),
-             bits32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y1, 2.0f, 2)),
-             bits32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y0, 2.0f, 3)),
-             bits32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y1, 2.0f, 3)));
-}
-
-// 8 four-bit codes (one word) -> one fragment, channel order {0,2,1,3,4,6,5,7}.
-__device__ __forceinline__ half8 codes4_frag(uint32_t w) {
-  const uint32_t y0 = w & 0x0F0F0F0Fu, y1 = (w >> 4) & 0x0F0F0F0Fu;
-  return cat4h(bits32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(y0, 512.0f, false)),
-               bits32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(y1, 512.0f, false)),
-               bits32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(y0, 512.0f, true)),
-               bits32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(y1, 512.0f, true)));
-}
-
 // Page token held by row r of the 16-row key tile mt. The C layout of the key
 // product gives lane group g rows 4g..4g+3 of each tile, so with this map lane
 // group g ends with the scores of tokens 8g..8g+7: the contiguous run of a

@@ -1,0 +1,84 @@
+"""GPU parity of the matrix-core decode of caches whose codes carry a scale
+per token: symmetric 2/4-bit keys and values (KVQ_SYM_TOKEN) and FP8 E4M3 keys
+with symmetric or KIVI 2/4-bit values (KVQ_FP8K_SYMV, KVQ_FP8K_KIVIV), at
+head_dim 64-256 without rotary keys (`paged_mfma_kernel`): outputs within
+max-abs 2e-3 of the oracle's fp64 attention over the dequantised cache, for
+every GQA width, partial last pages (down to one token), split counts,
+several queries per sequence and a ragged batch."""
+
+import pytest
+import torch
+
+import harness as H
+import kv_cache_quantisation_amd as kvq
+import synth
+from test_gpu_parity import run_append, small
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda", 0)
+
+CASES = [
+    # scheme, bits, v_bits, d, hg, dtype, T, splits
+    (synth.SYM_TOKEN, 2, 0, 128, 4, torch.bfloat16, 700, 0),
+    (synth.SYM_TOKEN, 4, 0, 128, 8, torch.bfloat16, 333, 3),
+    (synth.SYM_TOKEN, 2, 0, 64, 1, torch.float32, 1, 0),
+    (synth.SYM_TOKEN, 4, 0, 64, 2, torch.float32, 97, 1),
+    (synth.SYM_TOKEN, 4, 0, 256, 4, torch.bfloat16, 260, 0),
+    (synth.SYM_TOKEN, 2, 0, 256, 2, torch.bfloat16, 64, 5),
+    (synth.FP8K_SYMV, 8, 2, 128, 4, torch.bfloat16, 515, 0),
+    (synth.FP8K_SYMV, 8, 4, 64, 8, torch.float32, 31, 2),
+    (synth.FP8K_SYMV, 8, 4, 256, 1, torch.bfloat16, 129, 0),
+    (synth.FP8K_KIVIV, 8, 2, 64, 2, torch.bfloat16, 200, 0),
+    (synth.FP8K_KIVIV, 8, 4, 128, 4, torch.bfloat16, 1000, 4),
+    (synth.FP8K_KIVIV, 8, 2, 256, 8, torch.float32, 33, 1),
+]
+
+
+def build(case, B=2):
+    scheme, bits, vb, d, hg, dtype, T, splits = case
+    w = small(scheme, bits, d, dtype, B=B, hg=hg, T=T, v_bits=vb)
+    if scheme == synth.SYM_TOKEN:
+        cfg, cache, oc, k, v, ks, vs = run_append(w, [T], capacity=T + 40)
+    else:
+        from test_gpu_fp8k_mixed import run
+        cfg, cache, oc, k, v, ks = run(w, [T], capacity=T + 40)
+        vs = None
+    cfg.num_splits = splits
+    return w, cfg, cache, oc, ks, vs
+
+
+@pytest.mark.parametrize("case", list(range(len(CASES))))
+def test_decode(case):
+    w, cfg, cache, oc, ks, vs = build(CASES[case])
+    q = synth.query(w, device=DEV)
+    out = H.decode(cfg, cache, 0, w.tokens, q, ks, vs)
+    err = H.max_err(out, oc.decode(0, H.values(q)))
+    assert err <= H.ATOL, (case, err)
+
+
+@pytest.mark.parametrize("case", [0, 4, 7, 10])
+def test_multi_query(case):
+    w, cfg, cache, oc, ks, vs = build(CASES[case], B=3)
+    nq = min(5, w.tokens)
+    q = torch.stack([synth.query(w, device=DEV, tag=1 + i) for i in range(nq)], dim=1).contiguous()
+    out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    ws = torch.zeros(nq * kvq.kvq_cache_bytes(cfg, w.tokens, kvq.KVQ_BYTES_WORKSPACE), dtype=torch.uint8,
+                     device=DEV)
+    kvq.kvq_decode_attention_multi(cfg, cache, 0, w.tokens, q, out, ws, k_scale=ks, v_scale=vs)
+    assert H.max_err(out, oc.decode_multi(0, H.values(q))) <= H.ATOL
+    assert int(ws.count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("case", [1, 6, 11])
+def test_ragged(case):
+    """Sequences attend to their own first T_b tokens of the same cache."""
+    w, cfg, cache, oc, ks, vs = build(CASES[case], B=3)
+    T = w.tokens
+    lens = [T, max(1, T // 2), max(1, T // 3 + 1)]
+    seq = torch.tensor(lens, dtype=torch.int64, device=DEV)
+    q = synth.query(w, device=DEV)
+    out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    ws = kvq.alloc_workspace(cfg, T, device=DEV)
+    kvq.kvq_decode_attention_ragged(cfg, cache, 0, T, seq, q, out, ws, k_scale=ks, v_scale=vs)
+    want = oc.decode(0, H.values(q), seq_tokens=lens)
+    assert H.max_err(out, want) <= H.ATOL
