@@ -56,6 +56,7 @@ class OracleCache:
     def __init__(self, scheme, bits, layers, batch, kv_heads, head_dim, capacity,
                  residual=0, in_dtype="bf16", v_bits=None, outliers=0):
         if scheme in (FP8K_SYMV, FP8K_KIVIV):
+            v_bits = 8 if v_bits is None else v_bits   # the value codes' width when not given
             assert residual == 0 and bits == 8 and v_bits in (2, 3, 4, 8) and not outliers
         elif scheme != KIVI:
             assert residual == 0 and v_bits in (None, bits) and not outliers
