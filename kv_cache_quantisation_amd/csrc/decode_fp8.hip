@@ -117,7 +117,7 @@ __device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
 // per-token offset). The E5M2 key scale is applied to the scores after the
 // product instead of to q: with the scales that E5M2's range calls for
 // (max |x| / 57344), q * ks would fall among the f16 subnormals.
-// Per-token codes (2 or 4 bits) convert exactly to f16 / bf16 as unsigned
+// Per-token codes (2, 4 or 8 bits) convert exactly to f16 / bf16 as unsigned
 // fields; a two's-complement field with its top bit flipped is the code plus
 // 2^(b-1), so for symmetric codes
 //   key:   q . (s_t k_t)  = s_t (q . u_t - 2^(KB-1) sum_c q_c)
@@ -125,7 +125,7 @@ __device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
 // (u the flipped field), the value term being the per-token offset
 // z_t = -2^(VB-1) s_t that KIVI values carry explicitly. The unsigned code
 // converts give the channel (token) order {0,2,1,3,4,6,5,7} within each 8,
-// which the query (weight) operand follows.
+// which the query (weight) operand follows (8-bit codes keep their order).
 template <int FMT, int D, int HG, int KB = 8, int VB = 8>
 __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   static_assert(2 * HG <= 16, "high and remainder columns of the GQA group fit one tile");
@@ -134,8 +134,10 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   constexpr bool SYMK = FMT == KVQ_SYM_TOKEN;                    // key codes, a scale per token
   constexpr bool CODEV = SYMK || FMT == KVQ_FP8K_SYMV || FMT == KVQ_FP8K_KIVIV;   // value codes
   constexpr bool ASYMV = FMT == KVQ_FP8K_KIVIV;                  // value offset per token
-  static_assert(!SYMK || KB == 2 || KB == 4, "2- or 4-bit key codes");
-  static_assert(!CODEV || VB == 2 || VB == 4, "2- or 4-bit value codes");
+  static_assert(!SYMK || KB == 2 || KB == 4 || KB == 8, "2-, 4- or 8-bit key codes");
+  static_assert(!CODEV || VB == 2 || VB == 4 || VB == 8, "2-, 4- or 8-bit value codes");
+  constexpr bool PERMK = SYMK && KB < 8;    // key channels in the order {0,2,1,3,4,6,5,7}
+  constexpr bool PERMV = CODEV && VB < 8;   // value tokens in that order
   using PG = PagedGeom<FMT, D, KB, VB>;
   constexpr int KS = D / 32;             // k-steps of the key product
   constexpr int NT = D / 16;             // channel tiles of the value product
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
       for (int i = 0; i < 4; ++i) {
         // pair i: channels (2i, 2i+1), or for key codes the converts' order
         // (0,2), (1,3), (4,6), (5,7)
-        const int c0 = SYMK ? (i & 2) * 2 + (i & 1) : 2 * i, c1 = SYMK ? c0 + 2 : 2 * i + 1;
+        const int c0 = PERMK ? (i & 2) * 2 + (i & 1) : 2 * i, c1 = PERMK ? c0 + 2 : 2 * i + 1;
         const float a = ldexpf(qs[hh][g * CPG + 8 * ks + c0], -esc);
         const float c = ldexpf(qs[hh][g * CPG + 8 * ks + c1], -esc);
         uint32_t hi, lo;
@@ -285,6 +287,14 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
           const uint4 w = *reinterpret_cast<const uint4*>(
               pg + krow_off<PG::KROW / 16>(row, 2 * (g * CPG + 8 * ks)));
           c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), bq[ks], c, 0, 0, 0);
+        } else if constexpr (SYMK && KB == 8) {   // bytes with the top bit flipped, as f16 integers
+          const uint2 w = *reinterpret_cast<const uint2*>(pg + krow_off<PG::KROW / 16>(row, g * CPG + 8 * ks));
+          const uint32_t x0 = w.x ^ 0x80808080u, x1 = w.y ^ 0x80808080u;
+          const half8 a = cat4h(bits32(__builtin_amdgcn_cvt_pkrtz(float(x0 & 255u), float((x0 >> 8) & 255u))),
+                                bits32(__builtin_amdgcn_cvt_pkrtz(float((x0 >> 16) & 255u), float(x0 >> 24))),
+                                bits32(__builtin_amdgcn_cvt_pkrtz(float(x1 & 255u), float((x1 >> 8) & 255u))),
+                                bits32(__builtin_amdgcn_cvt_pkrtz(float((x1 >> 16) & 255u), float(x1 >> 24))));
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[ks], c, 0, 0, 0);
         } else if constexpr (SYMK && KB == 4) {   // one word: the 8 channels of this k-step
           const uint32_t w = *reinterpret_cast<const uint32_t*>(
                                  pg + krow_off<PG::KROW / 16>(row, (g * CPG + 8 * ks) / 2)) ^ 0x88888888u;
@@ -397,7 +407,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
     uint32_t ph[4], pl[4], pa[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t0 = CODEV ? (i & 2) * 2 + (i & 1) : 2 * i, t1 = CODEV ? t0 + 2 : 2 * i + 1;
+      const int t0 = PERMV ? (i & 2) * 2 + (i & 1) : 2 * i, t1 = PERMV ? t0 + 2 : 2 * i + 1;
       split_bf16(s[t0], s[t1], ph[i], pl[i]);
     }
 #pragma unroll
@@ -424,8 +434,20 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
       // value codes of tokens 8g..8g+7 of channel 16 nt + j (the column's
       // bits [8 VB g, 8 VB (g + 1))); symmetric codes with the top bit flipped
       constexpr int VROW = 32 * VB / 8;   // bytes per channel column
-      constexpr uint32_t FLIP = ASYMV ? 0u : (VB == 4 ? 0x88888888u : 0xAAAAAAAAu);
-      if constexpr (VB == 4) {
+      constexpr uint32_t FLIP = ASYMV ? 0u : (VB == 8 ? 0x80808080u : VB == 4 ? 0x88888888u : 0xAAAAAAAAu);
+      if constexpr (VB == 8) {   // bytes as bf16 integers (exact up to 256), tokens in order
+        auto bf2 = [](uint32_t lo, uint32_t hi) {   // two small integers -> packed bf16 (exact)
+          return (__float_as_uint(float(lo)) >> 16) | (__float_as_uint(float(hi)) & 0xFFFF0000u);
+        };
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const uint2 w = *reinterpret_cast<const uint2*>(pg + PG::OFF_VC + (16 * nt + j) * VROW + 8 * g);
+          const uint32_t x0 = w.x ^ FLIP, x1 = w.y ^ FLIP;
+          const uint4 bw{bf2(x0 & 255u, (x0 >> 8) & 255u), bf2((x0 >> 16) & 255u, x0 >> 24),
+                         bf2(x1 & 255u, (x1 >> 8) & 255u), bf2((x1 >> 16) & 255u, x1 >> 24)};
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, __builtin_bit_cast(bf16x8, bw), acc[nt], 0, 0, 0);
+        }
+      } else if constexpr (VB == 4) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const uint32_t w = *reinterpret_cast<const uint32_t*>(pg + PG::OFF_VC + (16 * nt + j) * VROW + 4 * g) ^ FLIP;
@@ -648,14 +670,14 @@ hipError_t by_d(const Fp8Params& p, int d, int hg, int batch, hipStream_t st) {
 
 }  // namespace
 
-// FP8 (either format) and bf16 caches, and caches of per-token codes at 2 or
-// 4 bits (symmetric keys and values; FP8 keys with symmetric or KIVI values)
+// FP8 (either format) and bf16 caches, and caches of per-token codes at 2, 4
+// or 8 bits (symmetric keys and values; FP8 keys with symmetric or KIVI values)
 // take the matrix-core paged kernel (head_dim >= 64, no rotary embedding).
 bool fp8_mfma_path(const Geometry& g) {
   if (g.rope != 0.0 || g.d < 64) return false;
   if (is_fp8(g.scheme) || g.scheme == KVQ_BF16_CACHE) return true;
-  if (g.scheme == KVQ_SYM_TOKEN) return g.bits == 2 || g.bits == 4;
-  if (is_fp8_keys_mixed(g.scheme)) return g.vbits == 2 || g.vbits == 4;
+  if (g.scheme == KVQ_SYM_TOKEN) return g.bits == 2 || g.bits == 4 || g.bits == 8;
+  if (is_fp8_keys_mixed(g.scheme)) return g.vbits == 2 || g.vbits == 4 || g.vbits == 8;
   return false;
 }
 
@@ -709,14 +731,17 @@ hipError_t launch_fp8_mfma(const DecodeArgs& a, hipStream_t st) {
     case KVQ_BF16_CACHE: return by_d<KVQ_BF16_CACHE>(p, g.d, g.hg, rows_n, st);
     case KVQ_FP8_E5M2: return by_d<KVQ_FP8_E5M2>(p, g.d, g.hg, rows_n, st);
     case KVQ_SYM_TOKEN:
-      return g.bits == 2 ? by_d<KVQ_SYM_TOKEN, 2, 2>(p, g.d, g.hg, rows_n, st)
-                         : by_d<KVQ_SYM_TOKEN, 4, 4>(p, g.d, g.hg, rows_n, st);
+      return g.bits == 2   ? by_d<KVQ_SYM_TOKEN, 2, 2>(p, g.d, g.hg, rows_n, st)
+             : g.bits == 4 ? by_d<KVQ_SYM_TOKEN, 4, 4>(p, g.d, g.hg, rows_n, st)
+                           : by_d<KVQ_SYM_TOKEN, 8, 8>(p, g.d, g.hg, rows_n, st);
     case KVQ_FP8K_SYMV:
-      return g.vbits == 2 ? by_d<KVQ_FP8K_SYMV, 8, 2>(p, g.d, g.hg, rows_n, st)
-                          : by_d<KVQ_FP8K_SYMV, 8, 4>(p, g.d, g.hg, rows_n, st);
+      return g.vbits == 2   ? by_d<KVQ_FP8K_SYMV, 8, 2>(p, g.d, g.hg, rows_n, st)
+             : g.vbits == 4 ? by_d<KVQ_FP8K_SYMV, 8, 4>(p, g.d, g.hg, rows_n, st)
+                            : by_d<KVQ_FP8K_SYMV, 8, 8>(p, g.d, g.hg, rows_n, st);
     case KVQ_FP8K_KIVIV:
-      return g.vbits == 2 ? by_d<KVQ_FP8K_KIVIV, 8, 2>(p, g.d, g.hg, rows_n, st)
-                          : by_d<KVQ_FP8K_KIVIV, 8, 4>(p, g.d, g.hg, rows_n, st);
+      return g.vbits == 2   ? by_d<KVQ_FP8K_KIVIV, 8, 2>(p, g.d, g.hg, rows_n, st)
+             : g.vbits == 4 ? by_d<KVQ_FP8K_KIVIV, 8, 4>(p, g.d, g.hg, rows_n, st)
+                            : by_d<KVQ_FP8K_KIVIV, 8, 8>(p, g.d, g.hg, rows_n, st);
     default: return by_d<KVQ_FP8_E4M3>(p, g.d, g.hg, rows_n, st);
   }
 }

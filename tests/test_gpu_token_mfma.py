@@ -1,6 +1,6 @@
 """GPU parity of the matrix-core decode of caches whose codes carry a scale
-per token: symmetric 2/4-bit keys and values (KVQ_SYM_TOKEN) and FP8 E4M3 keys
-with symmetric or KIVI 2/4-bit values (KVQ_FP8K_SYMV, KVQ_FP8K_KIVIV), at
+per token: symmetric 2/4/8-bit keys and values (KVQ_SYM_TOKEN) and FP8 E4M3
+keys with symmetric or KIVI 2/4/8-bit values (KVQ_FP8K_SYMV, KVQ_FP8K_KIVIV), at
 head_dim 64-256 without rotary keys (`paged_mfma_kernel`): outputs within
 max-abs 2e-3 of the oracle's fp64 attention over the dequantised cache, for
 every GQA width, partial last pages (down to one token), split counts,
@@ -31,6 +31,12 @@ CASES = [
     (synth.FP8K_KIVIV, 8, 2, 64, 2, torch.bfloat16, 200, 0),
     (synth.FP8K_KIVIV, 8, 4, 128, 4, torch.bfloat16, 1000, 4),
     (synth.FP8K_KIVIV, 8, 2, 256, 8, torch.float32, 33, 1),
+    # 8-bit codes (bytes converted as integers, channel/token order kept)
+    (synth.SYM_TOKEN, 8, 0, 128, 4, torch.bfloat16, 300, 0),
+    (synth.SYM_TOKEN, 8, 0, 64, 2, torch.float32, 45, 2),
+    (synth.FP8K_SYMV, 8, 8, 128, 2, torch.bfloat16, 257, 0),
+    (synth.FP8K_SYMV, 8, 0, 64, 4, torch.bfloat16, 7, 1),
+    (synth.FP8K_KIVIV, 8, 8, 256, 4, torch.float32, 100, 3),
 ]
 
 
@@ -56,7 +62,7 @@ def test_decode(case):
     assert err <= H.ATOL, (case, err)
 
 
-@pytest.mark.parametrize("case", [0, 4, 7, 10])
+@pytest.mark.parametrize("case", [0, 4, 7, 10, 12, 14])
 def test_multi_query(case):
     w, cfg, cache, oc, ks, vs = build(CASES[case], B=3)
     nq = min(5, w.tokens)
@@ -69,7 +75,7 @@ def test_multi_query(case):
     assert int(ws.count_nonzero()) == 0
 
 
-@pytest.mark.parametrize("case", [1, 6, 11])
+@pytest.mark.parametrize("case", [1, 6, 11, 13, 16])
 def test_ragged(case):
     """Sequences attend to their own first T_b tokens of the same cache."""
     w, cfg, cache, oc, ks, vs = build(CASES[case], B=3)
