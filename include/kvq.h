@@ -383,7 +383,10 @@ KVQ_API int32_t kvq_append_decode(const kvq_config* cfg, void* cache, int32_t la
  * tokens (its own fill level, as appended by kvq_quantize_append_ragged; for
  * KIVI its quantised pages are [0, q(seq_tokens[b])) and the rest sits in its
  * ring) and attends to all of them, its query at position seq_tokens[b] - 1
- * (for the rotary embedding). Everything else is as kvq_decode_attention.
+ * (for the rotary embedding). seq_tokens[b] must be what the sequence holds:
+ * a smaller count is not a prefix of it (KIVI's page/ring split and the
+ * layout of an FP8 cache's open last page follow the fill level).
+ * Everything else is as kvq_decode_attention.
  * Serving batches hold requests of different lengths: [KIVI] Key points
  * (KIVI pairs with PagedAttention for production serving).
  *   tokens      bound on every seq_tokens[b] (<= max_tokens); the split plan

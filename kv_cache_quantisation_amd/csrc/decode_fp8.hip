@@ -662,6 +662,9 @@ hipError_t by_hg(const Fp8Params& p, int hg, int batch, hipStream_t st) {
 template <int FMT, int KB = 8, int VB = 8>
 hipError_t by_d(const Fp8Params& p, int d, int hg, int batch, hipStream_t st) {
   switch (d) {
+    case 32:
+      if constexpr (!(FMT == KVQ_SYM_TOKEN && KB == 2)) return by_hg<FMT, 32, KB, VB>(p, hg, batch, st);
+      return hipErrorInvalidValue;   // not routed here (fp8_mfma_path)
     case 64: return by_hg<FMT, 64, KB, VB>(p, hg, batch, st);
     case 128: return by_hg<FMT, 128, KB, VB>(p, hg, batch, st);
     default: return by_hg<FMT, 256, KB, VB>(p, hg, batch, st);
@@ -672,9 +675,12 @@ hipError_t by_d(const Fp8Params& p, int d, int hg, int batch, hipStream_t st) {
 
 // FP8 (either format) and bf16 caches, and caches of per-token codes at 2, 4
 // or 8 bits (symmetric keys and values; FP8 keys with symmetric or KIVI values)
-// take the matrix-core paged kernel (head_dim >= 64, no rotary embedding).
+// take the matrix-core paged kernel (head_dim >= 32, no rotary embedding;
+// at head_dim 32 a 2-bit symmetric key row is 8 bytes, less than the 16-byte
+// chunk the page staging permutes, and stays on the generic kernel).
 bool fp8_mfma_path(const Geometry& g) {
-  if (g.rope != 0.0 || g.d < 64) return false;
+  if (g.rope != 0.0 || g.d < 32) return false;
+  if (g.d == 32 && g.scheme == KVQ_SYM_TOKEN && g.bits == 2) return false;
   if (is_fp8(g.scheme) || g.scheme == KVQ_BF16_CACHE) return true;
   if (g.scheme == KVQ_SYM_TOKEN) return g.bits == 2 || g.bits == 4 || g.bits == 8;
   if (is_fp8_keys_mixed(g.scheme)) return g.vbits == 2 || g.vbits == 4 || g.vbits == 8;
