@@ -662,8 +662,11 @@ def decode_kernel_name(w):
             f"kivi_mfma_kernel<2,2,{w.head_dim},{hg},true>"
     if w.scheme == synth.KIVI and w.bits in (2, 4) and w.in_dtype == torch.bfloat16:
         return f"kivi_mfma_kernel<{w.bits},{w.v_bits or w.bits},{w.head_dim},{hg},false>"
-    if w.scheme == synth.FP8_E4M3 and w.head_dim >= 64:
+    if w.scheme == synth.FP8_E4M3 and w.rope_theta == 0:
         return f"paged_mfma_kernel<FP8_E4M3,{w.head_dim},{hg}>"
+    if (w.scheme == synth.SYM_TOKEN and w.rope_theta == 0 and w.bits in (2, 4, 8)
+            and not (w.bits == 2 and w.head_dim == 32)):
+        return f"paged_mfma_kernel<SYM_TOKEN,{w.head_dim},{hg},{w.bits},{w.bits}>"
     return f"decode_split_kernel<scheme {w.scheme},{w.bits},{w.head_dim},{hg}>"
 
 
