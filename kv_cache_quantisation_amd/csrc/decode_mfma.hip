@@ -372,13 +372,16 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   // it: the pages and the ring up to its own token, or, when its token is in
   // a page, the pages up to that one (the rest of that page masked)
   // (with QN = 2 the block's second query sits one token later, at TbL - 1;
-  // both tokens are in the ring then)
+  // when every query's token is in a page the block takes the pages up to
+  // the last one's and masks each column after its own query's token; when
+  // the first query's token is the last quantised one, it sees every page
+  // whole and only ring steps mask it)
   const int64_t Tb = fill - (p.nq - 1 - qi);
   const int64_t TbL = Tb + QN - 1;
   if (p.seq_tokens || p.nq > 1) n_steps = static_cast<int32_t>((TbL - q_tokens + 7) / 8);
-  const bool in_page = Tb <= q_tokens;   // block-uniform: mask this row's last page
+  const bool in_page = TbL <= q_tokens;   // block-uniform: mask the rows' last pages
   if (in_page) {
-    n_pages = static_cast<int32_t>((Tb + kPage - 1) / kPage);
+    n_pages = static_cast<int32_t>((TbL + kPage - 1) / kPage);
     n_steps = 0;
   }
   uint8_t* wbuf = arena + wave * WAVE_LDS;
@@ -668,8 +671,12 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
     }
     }   // rotary / plain keys
 
-    if (in_page && Tb - t0 < kPage) {   // the query's own token is in this page
-      const int nvalid = static_cast<int>(Tb - t0);
+    // a query's own token is in this page (or, with two queries, the first
+    // query's last token is on the page before): each column masks the tokens
+    // after its own query's (wave-uniform check)
+    const bool masked_page = in_page && Tb - t0 < kPage;
+    const int nvalid = static_cast<int>(Tb + (QN == 1 ? 0 : j / (2 * HG)) - t0);
+    if (masked_page) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -677,6 +684,17 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
           if (tile_tok<ROPE>(mt, 4 * g + r) >= nvalid) s[4 * mt + r] = -INFINITY;
     }
     softmax_update(s, std::integral_constant<int, 8>{});
+    if constexpr (QN == 2) {
+      // the first query may have no token in the page, and a wave that has
+      // seen none of its tokens yet has reference max -inf: weight 0
+      if (masked_page) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (tile_tok<ROPE>(mt, 4 * g + r) >= nvalid) s[4 * mt + r] = 0.f;
+      }
+    }
     // per-token value scale and offset of this lane's tokens tile_tok(mt, 4g + r)
     constexpr int VT0 = ROPE ? 16 : 32, VT1 = ROPE ? 64 : 16;
     const float4 vs0 = *reinterpret_cast<const float4*>(pg + PG::OFF_VS + VT0 * g);
@@ -1685,9 +1703,8 @@ hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t st) {
   // split count is planned for that many rows (never more splits than the
   // one-query plan, whose workspace nq copies of hold the partials)
   // two queries per block: GQA 4, keys without rotation, an even number of
-  // queries whose tokens are all in the ring (every page visible to both)
-  const int qn = (nq >= 2 && nq % 2 == 0 && g.hg == 4 && a.rope_theta == 0.0 &&
-                  a.tokens - nq >= kivi_quantised(a.tokens, g.residual)) ? 2 : 1;
+  // queries (their tokens in the ring or in pages)
+  const int qn = (nq >= 2 && nq % 2 == 0 && g.hg == 4 && a.rope_theta == 0.0) ? 2 : 1;
   Geometry rows = g;
   rows.batch = g.batch * nq / qn;
   const MfmaPlan pl = mfma_plan(rows, a.tokens, a.requested_splits);
