@@ -53,6 +53,14 @@ CASES = [
     (synth.KIVI, 2, 128, 4, torch.bfloat16, 0, 64, 0.0, 0, 64),
     (synth.KIVI, 2, 128, 4, torch.bfloat16, 128, 50, 0.0, 0, 50),
     (synth.KIVI, 2, 128, 4, torch.bfloat16, 0, 96, 10000.0, 0, 96),
+    # two queries per block with their tokens in pages; the first query of
+    # the first block sits at a page boundary (token 320), so the page after
+    # holds none of its tokens (many splits: it is a wave's first page)
+    (synth.KIVI, 2, 128, 4, torch.bfloat16, 0, 361, 0.0, 11, 42),
+    (synth.KIVI, 4, 64, 4, torch.bfloat16, 8, 361, 0.0, 9, 42),
+    # a block whose first query's token is the last quantised one (288) and
+    # whose second is the first ring token: every page whole, one ring step
+    (synth.KIVI, 2, 128, 4, torch.bfloat16, 16, 305, 0.0, 0, 22),
     # FP8 and bfloat16 caches without rotary keys: their matrix-core kernel
     (synth.FP8_E5M2, 8, 128, 8, torch.bfloat16, 0, 301, 0.0, 3, 45),     # queries across pages
     (synth.BF16_CACHE, 16, 64, 2, torch.bfloat16, 0, 77, 0.0, 1, 9),     # one split: no merge
