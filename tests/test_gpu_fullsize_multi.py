@@ -18,19 +18,21 @@ import synth
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
-# workload -> (queries per sequence, (sequence, KV head) units checked)
+# case -> (workload, queries per sequence, (sequence, KV head) units checked)
+# (kivi2 with 8 queries: four queries per block, their rows filling the chip)
 CASES = {
-    "kivi2": (4, [(0, 0), (15, 7)]),
-    "int4": (8, [(31, 7)]),
-    "longctx": (4, [(0, 3)]),
-    "fp8": (3, [(63, 2)]),
+    "kivi2": ("kivi2", 4, [(0, 0), (15, 7)]),
+    "kivi2_8q": ("kivi2", 8, [(0, 0), (9, 3), (15, 7)]),
+    "int4": ("int4", 8, [(31, 7)]),
+    "longctx": ("longctx", 4, [(0, 3)]),
+    "fp8": ("fp8", 3, [(63, 2)]),
 }
 
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_fullsize_multi_query(name):
-    w = synth.WORKLOADS[name]
-    nq, units = CASES[name]
+    wname, nq, units = CASES[name]
+    w = synth.WORKLOADS[wname]
     T = w.tokens
     print(f"[fullsize-multi] {name}: B={w.batch} Hkv={w.kv_heads} d={w.head_dim} T={T} n_q={nq}",
           flush=True)

@@ -3,9 +3,9 @@
 tokens [0, T - n_q + i] of the cache, compared with the oracle's decode_multi
 (float64) on the same seeded inputs, for every scheme, with and without
 rotary keys, queries whose tokens sit in KIVI's ring or in its pages (the
-matrix-core kernel when the cache's inputs are 16-bit, the generic kernel for
-fp32 inputs), and FP8 and bfloat16 caches (their matrix-core kernel without
-rotary keys)."""
+matrix-core kernel when the cache's inputs are 16-bit, one, two or four
+queries per block; the generic kernel for fp32 inputs), and FP8 and bfloat16
+caches (their matrix-core kernel without rotary keys)."""
 
 import pytest
 import torch
@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda", 0)
 
 CASES = [
-    # scheme, bits, d, hg, dtype, R, T, rope, splits, n_q
+    # scheme, bits, d, hg, dtype, R, T, rope, splits, n_q[, value bits, batch]
     (synth.KIVI, 2, 128, 4, torch.bfloat16, 128, 700, 0.0, 0, 4),
     (synth.KIVI, 2, 128, 4, torch.bfloat16, 0, 300, 0.0, 0, 40),     # queries over pages
     (synth.KIVI, 4, 64, 2, torch.float32, 16, 257, 10000.0, 3, 17),
@@ -61,6 +61,18 @@ CASES = [
     # a block whose first query's token is the last quantised one (288) and
     # whose second is the first ring token: every page whole, one ring step
     (synth.KIVI, 2, 128, 4, torch.bfloat16, 16, 305, 0.0, 0, 22),
+    # four queries per block (a multiple of four queries, GQA 4, 2-bit
+    # values, and batch x n_q / 4 x KV heads >= 256 rows of blocks; value
+    # bits and batch last): the block's first query's token in the last page
+    # and the other three in the ring (each sees a different part of it)
+    (synth.KIVI, 2, 128, 4, torch.bfloat16, 16, 305, 0.0, 0, 20, 0, 26),
+    # a block whose first query sees exactly ten pages: the page after holds
+    # none of its tokens (weight 0), many splits
+    (synth.KIVI, 2, 128, 4, torch.bfloat16, 0, 363, 0.0, 11, 44, 0, 12),
+    # 4-bit keys with 2-bit values, head_dim 64 and 128, pages and ring
+    (synth.KIVI, 4, 64, 4, torch.bfloat16, 8, 361, 0.0, 9, 44, 2, 12),
+    (synth.KIVI, 4, 128, 4, torch.bfloat16, 64, 500, 0.0, 0, 16, 2, 32),
+    (synth.KIVI, 4, 128, 4, torch.bfloat16, 32, 300, 0.0, 3, 100, 2, 6),
     # FP8 and bfloat16 caches without rotary keys: their matrix-core kernel
     (synth.FP8_E5M2, 8, 128, 8, torch.bfloat16, 0, 301, 0.0, 3, 45),     # queries across pages
     (synth.BF16_CACHE, 16, 64, 2, torch.bfloat16, 0, 77, 0.0, 1, 9),     # one split: no merge
@@ -73,8 +85,10 @@ def queries(w, nq):
 
 @pytest.mark.parametrize("case", list(range(len(CASES))))
 def test_multi_query_decode(case):
-    scheme, bits, d, hg, dtype, R, T, rope, splits, nq = CASES[case]
-    w = small(scheme, bits, d, dtype, R, B=3, hg=hg, T=T, rope=rope)
+    scheme, bits, d, hg, dtype, R, T, rope, splits, nq = CASES[case][:10]
+    vb = CASES[case][10] if len(CASES[case]) > 10 else 0
+    batch = CASES[case][11] if len(CASES[case]) > 11 else 3
+    w = small(scheme, bits, d, dtype, R, B=batch, hg=hg, T=T, rope=rope, v_bits=vb)
     cfg, cache, oc, k, v, ks, vs = run_append(w, [T], capacity=T + 40)
     cfg.num_splits = splits
     q = queries(w, nq)

@@ -91,6 +91,7 @@ BUDGETS = [
     ("kivi_mfma_kernelILi4ELi2ELi128ELi4ELb0ELi1E", 256),   # 4-bit keys, 2-bit values (88 KB LDS)
     ("kivi_mfma_kernelILi4ELi4ELi128ELi4ELb0ELi1E", 168),   # KIVI 4-bit
     ("kivi_mfma_kernelILi2ELi2ELi128ELi4ELb0ELi2E", 256),   # 2-bit, two queries per block (one per CU)
+    ("kivi_mfma_kernelILi2ELi2ELi128ELi4ELb0ELi4E", 256),   # 2-bit, four queries per block (one per CU)
     ("rope4_kernelILi128ELi4E", 168),                       # rotary keys, GQA 4
 ]
 
