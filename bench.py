@@ -67,9 +67,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 # change to those, `traffic` is reported as null until they are taken again.
 ROOFLINE_EXTRA = 64            # roofline context = workload tokens + this
 COUNTERS = {
-    "kivi2": {"context": 4096 + ROOFLINE_EXTRA, "fetch_kib": 30753.84, "write_kib": 907.5,
+    "kivi2": {"context": 4096 + ROOFLINE_EXTRA, "fetch_kib": 30741.75, "write_kib": 905.0,
               "fetch_scale": 262144 / 131084, "write_scale": 1.0,
-              "sources_sha256": "2cc3b224786b24a963a5d26972c7b870d37edf13a04a5cd5b35ff212db314425"},
+              "sources_sha256": "9234f4ab9ce0ba0f1ef47a32b27acde8647c0cae29aa84c1d7434204772a4cc6"},
 }
 DECODE_SOURCES = ["decode_mfma.hip", "kvq_device.h", "kvq_internal.h", "kvq_merge.h", "kvq_wave.h"]
 
