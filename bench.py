@@ -67,9 +67,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 # change to those, `traffic` is reported as null until they are taken again.
 ROOFLINE_EXTRA = 64            # roofline context = workload tokens + this
 COUNTERS = {
-    "kivi2": {"context": 4096 + ROOFLINE_EXTRA, "fetch_kib": 30741.75, "write_kib": 905.0,
+    "kivi2": {"context": 4096 + ROOFLINE_EXTRA, "fetch_kib": 30751.63, "write_kib": 905.5,
               "fetch_scale": 262144 / 131084, "write_scale": 1.0,
-              "sources_sha256": "9234f4ab9ce0ba0f1ef47a32b27acde8647c0cae29aa84c1d7434204772a4cc6"},
+              "sources_sha256": "20ebe99275bac870ee013212ae8894c824bedcbe47966af43bd13761035d59fd"},
 }
 DECODE_SOURCES = ["decode_mfma.hip", "kvq_device.h", "kvq_internal.h", "kvq_merge.h", "kvq_wave.h"]
 
@@ -365,8 +365,8 @@ def gpu_bench(args, w):
 
     # several causal queries per sequence (4 and 8: e.g. speculated tokens
     # being verified) over the same caches; their tokens are in the ring, so
-    # they run on the matrix-core kernel (two queries per block for 4, four
-    # per block for 8, whose rows then fill the chip without splits)
+    # they run on the matrix-core kernel of four queries per block, whose
+    # keys are dequantised once per page for the four
     multi = []
     for nq in (4, 8):
         qm = [torch.stack([synth.query(w, layer=l, device=dev, tag=1 + i) for i in range(nq)], dim=1)
@@ -389,8 +389,7 @@ def gpu_bench(args, w):
         multi.append({"n_queries": nq, "median_launch_us": round(multi_us, 3), "bytes_per_launch": multi_b,
                       "gbs": round(multi_b / (multi_us * 1e-6) / 1e9, 1),
                       "x_one_query": round(multi_us / burst_us[len(burst_us) // 2], 2),
-                      "kernel": f"kivi_mfma_kernel<2,2,128,4,false,{2 if nq == 4 else 4}> "
-                                f"(rows b * n_q / {2 if nq == 4 else 4} + i, merge fused)"})
+                      "kernel": "kivi_deq_kernel<2,2,128> (rows b * n_q / 4 + i, merge fused)"})
         del qm, om, wsm
 
     # ragged batch: 32 more layer caches whose sequences hold lens[b] tokens

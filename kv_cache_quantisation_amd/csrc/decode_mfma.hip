@@ -136,17 +136,15 @@ __device__ __forceinline__ float load_q(const uint8_t* base, int64_t idx, int bf
 // high parts of its heads, then their remainders), writes the output rows
 // (one split) or the block's partials, and in the last block of a (sequence,
 // KV head) to finish merges every partial. QN: queries of the block, rows
-// b * nq + qi + qq of q, out and the partials; with four queries acc holds two
-// sets of NT tiles, one per pair of queries.
-template <int D, int HG, int NW = kWaves, int QN = 1>
+// b * nq + qi + qq of q, out and the partials. DIRECT: acc rows 4g + r are
+// the pairs 4g + r themselves (kivi_deq_kernel).
+template <int D, int HG, int NW = kWaves, int QN = 1, bool DIRECT = false>
 __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* acc, const float* mh,
                                             const float* lsum, const float* zsum, uint8_t* arena,
                                             int& last_block, int b, int qi, int h, int split) {
   constexpr int NT = D / 16;
   constexpr int NTH = NW * 64;             // threads of the block
   constexpr int GC = HG * QN;              // (query, head) pairs
-  constexpr int CS = QN == 4 ? 2 : 1;      // column sets of the products
-  constexpr int QS = QN / CS;              // queries per column set
   static_assert(QN == 1 || HG == 4, "several queries per block: GQA 4");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -157,22 +155,30 @@ __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* 
   __syncthreads();   // every wave is done with its page buffers (the arena)
   float* red = reinterpret_cast<float*>(arena);   // [wave][GC][D + 2]: m, l, o
   auto R = [&](int w, int vh) { return red + (w * GC + vh) * (D + 2); };
-  // acc rows 4g+r: row < HG is head row (hi), HG <= row < 2HG is head row-HG
-  // (lo); with two queries rows 2HG.. repeat that for the second query (of
-  // the set: set cs holds queries QS cs ..)
+  if constexpr (DIRECT) {   // acc rows 4g+r: pair 4g+r
 #pragma unroll
-  for (int cs = 0; cs < CS; ++cs)
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int vh = 4 * g + r;
+        float zz = 0.f;   // sum_t p z_t of pair vh goes to every channel
+#pragma unroll
+        for (int k = 0; k < GC; ++k) zz = vh == k ? zsum[k] : zz;
+        if (vh < GC) R(wave, vh)[2 + 16 * nt + j] = acc[nt][r] + zz;
+      }
+  } else
+  // acc rows 4g+r: row < HG is head row (hi), HG <= row < 2HG is head row-HG
+  // (lo); with two queries rows 2HG.. repeat that for the second query
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const floatx4 a = acc[cs * NT + nt];
     float v[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float x = a[r];
+      float x = acc[nt][r];
       if constexpr (HG == 1) {
-        x = r == 0 ? a[0] + a[1] : 0.f;
+        x = r == 0 ? acc[nt][0] + acc[nt][1] : 0.f;
       } else if constexpr (HG == 2) {
-        x = r < 2 ? a[r] + a[r + 2] : 0.f;
+        x = r < 2 ? acc[nt][r] + acc[nt][r + 2] : 0.f;
       } else if constexpr (HG == 4) {
         x += xor16(x);          // rows 0-3 (g=0) + rows 4-7 (g=1); with QN = 2, 8-11 + 12-15
       } else {
@@ -181,10 +187,10 @@ __device__ __forceinline__ void finish_unit(const MfmaParams& p, const floatx4* 
       v[r] = x;
     }
     const int c = 16 * nt + j;
-    if ((4 * g) % (2 * HG) < HG && 4 * g < 2 * HG * QS) {   // lane groups holding the high rows
+    if ((4 * g) % (2 * HG) < HG && 4 * g < 2 * GC) {   // lane groups holding the high rows
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int vh = cs * HG * QS + (4 * g / (2 * HG)) * HG + (4 * g) % (2 * HG) + r;
+        const int vh = (4 * g / (2 * HG)) * HG + (4 * g) % (2 * HG) + r;
         float zz = 0.f;   // sum_t p z_t of pair vh goes to every channel
 #pragma unroll
         for (int k = 0; k < GC; ++k) zz = vh == k ? zsum[k] : zz;
@@ -295,13 +301,6 @@ constexpr int kivi_waves(int kb, int vb, int d, int hg, bool rope) {
   return ((kb == 2 || kb == 4) && vb == 2 && d <= 128 && hg <= 4 && !rope) ? 8 : 4;
 }
 
-// Four queries per block (GQA 4, keys without rotation) for eight-wave
-// blocks: the doubled fragments of q' (two column sets) still fit the LDS of
-// one block per CU (2-bit keys, d 128: 127 KB; 4-bit keys: 143 KB).
-constexpr bool kivi_qn4(int kb, int vb, int d) {
-  return kivi_waves(kb, vb, d, 4, false) == 8;
-}
-
 // KB, VB: bits of the key and of the value codes. QN: queries of a sequence
 // per block (2: two consecutive queries share every page; their high and
 // remainder columns fill the 16 columns of the key product and the 16 rows
@@ -311,12 +310,8 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
                              QN > 1 ? 1 : kivi_waves(KB, VB, D, HG, ROPE) == 8 ? 2 : kivi_blocks_per_cu(KB, D, ROPE)) void kivi_mfma_kernel(MfmaParams p) {
   static_assert((KB == 2 || KB == 4) && (VB == 2 || VB == 4) && VB <= KB, "2- or 4-bit codes");
   static_assert(!ROPE || (KB == 2 && D <= 128), "rotary decode: 2-bit pages, head_dim <= 128");
-  static_assert(QN == 1 || ((QN == 2 || QN == 4) && HG == 4 && !ROPE),
-                "several queries per block: GQA 4, keys without rotation");
-  // column sets of the key and value products: two queries (at GQA 4) each
-  constexpr int CS = QN == 4 ? 2 : 1;
-  constexpr int QS = QN / CS;            // queries per column set
-  static_assert(2 * HG * QS <= 16, "hi and lo columns of a set's GQA group(s) fit one tile");
+  static_assert(2 * HG * QN <= 16, "hi and lo columns of the GQA group(s) fit one tile");
+  static_assert(QN == 1 || (QN == 2 && HG == 4 && !ROPE), "two queries per block: GQA 4, keys without rotation");
   using PG = PageGeom<KB, VB, D>;
   constexpr int NW = kivi_waves(KB, VB, D, HG, ROPE);   // waves per block
   constexpr int NTH = 64 * NW;
@@ -331,7 +326,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   constexpr int COMBOS = GC * 4 * KS;    // (pair, lane group, k-step) fold units
   constexpr int REPS = (COMBOS + 63) / 64;
   constexpr int PER_HEAD = 4 * KS;       // fold units (lanes) per head
-  // bf16 B-operand sets for the residual keys (one per query when QN > 1)
+  // bf16 B-operand sets for the residual keys (one per query when QN = 2)
   constexpr int QB = QN == 1 ? (3 * HG + 15) / 16 : QN;
   // the residual-key B operand is built once per wave and kept in registers
   // when it is small (QB * KS words of 16 bytes), else rebuilt for every step
@@ -370,9 +365,9 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   // sequence b and its (first) query qi of the block
   const int rows_b = p.nq / QN;
   const int b = blockIdx.z / rows_b, qi = (blockIdx.z - b * rows_b) * QN;
-  // lane column j of a set's key product: the set's query j / (2HG), high
-  // part when j % (2HG) < HG (then holding the scores of the set's pair
-  // col_vh after the key product); with one query only columns j < HG are live
+  // lane column j of the key product: query j / (2HG), high part when
+  // j % (2HG) < HG (then holding the scores of pair col_vh after the key
+  // product); with one query only columns j < HG are live
   const bool col_hi = (j % (2 * HG)) < HG;
   const bool col_live = QN == 1 ? j < HG : col_hi;
   const int col_vh = (j / (2 * HG)) * HG + j % HG;
@@ -412,27 +407,15 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   // Lane (j, g), j < HG, tracks head j: running max m, and the sums of p and
   // p*z over its tokens (reduced over g at the end). acc rows 4g+r hold head
   // (4g+r) % HG: hi rows, then lo rows.
-  // (one state per column set: with four queries per block, set cs holds
-  // queries 2cs and 2cs + 1 in the same lanes and rows)
-  floatx4 acc[CS][NT];
+  floatx4 acc[NT];
 #pragma unroll
-  for (int cs = 0; cs < CS; ++cs)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[cs][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m_lane[CS], l_lane[CS], z_lane[CS];
-#pragma unroll
-  for (int cs = 0; cs < CS; ++cs) {
-    m_lane[cs] = -INFINITY;
-    l_lane[cs] = 0.f;
-    z_lane[cs] = 0.f;
-  }
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_lane = -INFINITY, l_lane = 0.f, z_lane = 0.f;
 
-  // Folds NS scores per lane of column set cs into its softmax state
-  // (rescaling the running sums and accumulators if a head's max grows);
-  // turns s into weights 2^(s-m).
-  auto softmax_update = [&](float* s, auto ns_tag, auto cs_tag) {
+  // Folds NS scores per lane into the softmax state (rescaling the running
+  // sums and accumulators if a head's max grows); turns s into weights 2^(s-m).
+  auto softmax_update = [&](float* s, auto ns_tag) {
     constexpr int NS = decltype(ns_tag)::value;
-    constexpr int cs = decltype(cs_tag)::value;
     float pmax = s[0];
 #pragma unroll
     for (int i = 1; i < NS; ++i) pmax = fmaxf(pmax, s[i]);
@@ -442,18 +425,18 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
     // spread over its four lane groups; whether any of them exceeds the slack
     // is decided by each lane's own maximum, so the maximum over the lane
     // groups is only formed on the rare rescaling pages.
-    const bool grows = col_live && (pmax > m_lane[cs] + kMaxSlack);
+    const bool grows = col_live && (pmax > m_lane + kMaxSlack);
     if (__builtin_amdgcn_ballot_w64(grows) != 0) {   // wave-uniform
       pmax = fmaxf(pmax, xor16(pmax));
       pmax = fmaxf(pmax, xor32(pmax));
-      const float m_new = fmaxf(m_lane[cs], pmax);
+      const float m_new = fmaxf(m_lane, pmax);
       // a column whose max stays keeps its sums (also one that has seen no
       // token yet, -inf: with two queries per block the other query's
       // columns may move while this one stays there)
-      const float alpha = m_new == m_lane[cs] ? 1.0f : fast_exp2(m_lane[cs] - m_new);
-      l_lane[cs] *= alpha;
-      z_lane[cs] *= alpha;
-      m_lane[cs] = m_new;
+      const float alpha = m_new == m_lane ? 1.0f : fast_exp2(m_lane - m_new);
+      l_lane *= alpha;
+      z_lane *= alpha;
+      m_lane = m_new;
       auto alpha_of = [&](int hh) {   // head hh's factor, read from lane hh
         return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), hh));
       };
@@ -467,21 +450,19 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
           const float a_odd = alpha_of(4 + r);
           a = (g & 1) ? a_odd : a;
         }
-        // two queries per set: rows 4g + r of lane groups 2, 3 belong to the
-        // set's second query, whose head r is column 2HG + r
-        if constexpr (QS == 2) {
+        // QN = 2: rows 4g + r of lane groups 2, 3 belong to the second query,
+        // whose head r is column 2HG + r
+        if constexpr (QN == 2) {
           const float a_q1 = alpha_of(2 * HG + r);
           a = g >= 2 ? a_q1 : a;
         }
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[cs][nt][r] *= a;
+        for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= a;
       }
     }
 #pragma unroll
-    for (int i = 0; i < NS; ++i) s[i] = fast_exp2(s[i] - m_lane[cs]);
+    for (int i = 0; i < NS; ++i) s[i] = fast_exp2(s[i] - m_lane);
   };
-  using Cs0 = std::integral_constant<int, 0>;
-  using Cs1 = std::integral_constant<int, CS - 1>;   // the second set (CS = 2)
 
   // ---- work of this wave --------------------------------------------------------
   // Block `split` takes a contiguous range of pages; its waves take every
@@ -551,7 +532,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   };
 
   auto process_page = [&](const uint8_t* pg, int64_t t0) {
-    float s[CS][8];   // scores of this lane's tokens, per column set
+    float s[8];
     if constexpr (ROPE) {
       // scores of tile row j = qpage . R(omega tau) (code * s + z), tau = 16 mt + j,
       // on v_mfma_f32_16x16x4f32 (lane group g holds channels (D/4) g ..)
@@ -583,7 +564,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
 #pragma unroll
         for (int ks = 0; ks < D / 4; ++ks) c = __builtin_amdgcn_mfma_f32_16x16x4f32(y[ks], bqv[ks], c, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s[0][4 * mt + r] = c[r];
+        for (int r = 0; r < 4; ++r) s[4 * mt + r] = c[r];
       }
     } else {
     // q' = q * s per channel, split hi/lo into B fragments; bias q . z
@@ -594,10 +575,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
       const int cidx = lane + 64 * r;
       const int fh = cidx / PER_HEAD, fg = (cidx / KS) % 4, fk = cidx % KS;
       const int c0 = fg * CPG + 8 * fk;
-      // B columns of pair fh: set fh / (HG QS) (16 columns each), then the
-      // pair's query in the set and its head
-      const int fs = fh / (HG * QS), fhs = fh % (HG * QS);
-      const int chi = 16 * fs + (fhs / HG) * 2 * HG + fhs % HG, clo = chi + HG;
+      const int chi = (fh / HG) * 2 * HG + fh % HG, clo = chi + HG;   // B columns of pair fh
       const float4 s0 = *reinterpret_cast<const float4*>(pg + PG::OFF_KS + 4 * c0);
       const float4 s1 = *reinterpret_cast<const float4*>(pg + PG::OFF_KS + 4 * c0 + 16);
       const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
@@ -646,12 +624,9 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
 #pragma unroll
       for (int r = 0; r < REPS; ++r) fold(r, esc, false);
     }
-    // bias of head j for this lane: the fold units of pair vh are lanes
-    // [PER_HEAD*vh, PER_HEAD*(vh+1)) counted across reps of 64 (set cs: pair
-    // HG QS cs + col_vh)
-    float bias_j[CS];
-#pragma unroll
-    for (int cs = 0; cs < CS; ++cs) bias_j[cs] = 0.f;
+    // bias of head j for this lane: the fold units of head hh are lanes
+    // [PER_HEAD*hh, PER_HEAD*(hh+1)) counted across reps of 64
+    float bias_j = 0.f;
 #pragma unroll
     for (int r = 0; r < REPS; ++r) {
       float v = bias_part[r];
@@ -661,30 +636,22 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
         v = row_sum16(v);
         if constexpr (PER_HEAD == 32) v += xor16(v);
       }
-#pragma unroll
-      for (int cs = 0; cs < CS; ++cs) {
-        const int src = PER_HEAD * (col_live ? HG * QS * cs + col_vh : 0) - 64 * r;
-        const float got = __shfl(v, src & 63, 64);
-        if (src >= 0 && src < 64) bias_j[cs] = got;
-      }
+      const int src = PER_HEAD * (col_live ? col_vh : 0) - 64 * r;
+      const float got = __shfl(v, src & 63, 64);
+      if (src >= 0 && src < 64) bias_j = got;
     }
-#pragma unroll
-    for (int cs = 0; cs < CS; ++cs) {
-      if (!col_live) bias_j[cs] = 0.f;   // lo columns carry no offset
-      if (big) bias_j[cs] = ldexpf(bias_j[cs], -esc);   // scaled with the product, undone below
-    }
+    if (!col_live) bias_j = 0.f;   // lo columns carry no offset
+    if (big) bias_j = ldexpf(bias_j, -esc);   // scaled with the product, undone below
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     // (with one query, columns >= 2*HG only produce score columns that are
     // never read)
-    half8 bq[CS][KS];
-#pragma unroll
-    for (int cs = 0; cs < CS; ++cs)
+    half8 bq[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int col = 16 * cs + j % (2 * HG * QS);
+      const int col = j % (2 * GC);
       const uint4 f = *reinterpret_cast<const uint4*>(frag[col * FSTRIDE + ((4 * ks + g) ^ (col & 7))]);
-      bq[cs][ks] = cat4h(f.x, f.y, f.z, f.w);
+      bq[ks] = cat4h(f.x, f.y, f.z, f.w);
     }
 
     // scores S^T = codes x q'^T
@@ -694,70 +661,51 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
 #pragma unroll
       for (int w = 0; w < KW; ++w)
         kp[w] = *reinterpret_cast<const uint32_t*>(pg + krow_off<CPR_K>(tile_tok<ROPE>(mt, j), g * (KW * 4) + 4 * w));
-      floatx4 c[CS];
-#pragma unroll
-      for (int cs = 0; cs < CS; ++cs)   // hi column carries q . z
-        c[cs] = floatx4{bias_j[cs], bias_j[cs], bias_j[cs], bias_j[cs]};
+      floatx4 c = {bias_j, bias_j, bias_j, bias_j};   // hi column carries q . z
       if constexpr (KB == 2) {
 #pragma unroll
         for (int w = 0; w < KW; ++w) {
           half8 a0, a1;
           codes2_frags(kp[w], a0, a1);
-#pragma unroll
-          for (int cs = 0; cs < CS; ++cs) {
-            c[cs] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bq[cs][2 * w], c[cs], 0, 0, 0);
-            c[cs] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bq[cs][2 * w + 1], c[cs], 0, 0, 0);
-          }
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bq[2 * w], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bq[2 * w + 1], c, 0, 0, 0);
         }
       } else {
 #pragma unroll
-        for (int w = 0; w < KW; ++w) {
-          const half8 a = codes4_frag(kp[w]);
-#pragma unroll
-          for (int cs = 0; cs < CS; ++cs)
-            c[cs] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[cs][w], c[cs], 0, 0, 0);
-        }
+        for (int w = 0; w < KW; ++w)
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes4_frag(kp[w]), bq[w], c, 0, 0, 0);
       }
 #pragma unroll
-      for (int cs = 0; cs < CS; ++cs)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s[cs][4 * mt + r] = c[cs][r] + row_shl<HG>(c[cs][r]);
+      for (int r = 0; r < 4; ++r) s[4 * mt + r] = c[r] + row_shl<HG>(c[r]);
     }
     if (big) {
 #pragma unroll
-      for (int cs = 0; cs < CS; ++cs)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) s[cs][i] = ldexpf(s[cs][i], esc);
+      for (int i = 0; i < 8; ++i) s[i] = ldexpf(s[i], esc);
     }
     }   // rotary / plain keys
 
-    // a query's own token is in this page (or, with several queries, the
-    // first query's last token is on the page before): each column masks the
-    // tokens after its own query's (wave-uniform check). With four queries the
-    // block may hold its first query's token in the last page and the others'
-    // in the ring, so any page that the first query does not see whole is
-    // masked.
-    const bool masked_page = (QN == 4 || in_page) && Tb - t0 < kPage;
-    const auto mask_page = [&](float* sc, int cs, float fill_v) {
-      const int nvalid = static_cast<int>(Tb + QS * cs + (QS == 1 ? 0 : j / (2 * HG)) - t0);
+    // a query's own token is in this page (or, with two queries, the first
+    // query's last token is on the page before): each column masks the tokens
+    // after its own query's (wave-uniform check)
+    const bool masked_page = in_page && Tb - t0 < kPage;
+    const int nvalid = static_cast<int>(Tb + (QN == 1 ? 0 : j / (2 * HG)) - t0);
+    if (masked_page) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (tile_tok<ROPE>(mt, 4 * g + r) >= nvalid) sc[4 * mt + r] = fill_v;
-    };
-    if (masked_page) {
-#pragma unroll
-      for (int cs = 0; cs < CS; ++cs) mask_page(s[cs], cs, -INFINITY);
+          if (tile_tok<ROPE>(mt, 4 * g + r) >= nvalid) s[4 * mt + r] = -INFINITY;
     }
-    softmax_update(s[0], std::integral_constant<int, 8>{}, Cs0{});
-    if constexpr (CS == 2) softmax_update(s[CS - 1], std::integral_constant<int, 8>{}, Cs1{});
-    if constexpr (QN > 1) {
+    softmax_update(s, std::integral_constant<int, 8>{});
+    if constexpr (QN == 2) {
       // the first query may have no token in the page, and a wave that has
       // seen none of its tokens yet has reference max -inf: weight 0
       if (masked_page) {
 #pragma unroll
-        for (int cs = 0; cs < CS; ++cs) mask_page(s[cs], cs, 0.f);
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (tile_tok<ROPE>(mt, 4 * g + r) >= nvalid) s[4 * mt + r] = 0.f;
       }
     }
     // per-token value scale and offset of this lane's tokens tile_tok(mt, 4g + r)
@@ -768,34 +716,29 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
     const float4 vz1 = *reinterpret_cast<const float4*>(pg + PG::OFF_VZ + VT1 + VT0 * g);
     const float vsv[8] = {vs0.x, vs0.y, vs0.z, vs0.w, vs1.x, vs1.y, vs1.z, vs1.w};
     const float vzv[8] = {vz0.x, vz0.y, vz0.z, vz0.w, vz1.x, vz1.y, vz1.z, vz1.w};
-    bf16x8 ap[CS];
+    float pv[8];
 #pragma unroll
-    for (int cs = 0; cs < CS; ++cs) {
-      float pv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        l_lane[cs] += s[cs][i];
-        z_lane[cs] = fmaf(s[cs][i], vzv[i], z_lane[cs]);
-        pv[i] = s[cs][i] * vsv[i];
-      }
-      // P' into A fragments: the lane's tokens in the order {0,2,1,3,4,6,5,7}
-      uint32_t ph[4], pl[4];
-      split_bf16(pv[0], pv[2], ph[0], pl[0]);
-      split_bf16(pv[1], pv[3], ph[1], pl[1]);
-      split_bf16(pv[4], pv[6], ph[2], pl[2]);
-      split_bf16(pv[5], pv[7], ph[3], pl[3]);
-      // rows j < HG: hi of head j; rows j >= HG: lo of lane j-HG (rows >= 2HG
-      // only reach accumulator rows that are never read)
-      // (two queries per set: the second query's high rows 2HG.. keep their
-      // own values)
-      uint32_t pa[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pa[i] = shr_keep<HG>(ph[i], pl[i]);
-        if constexpr (QS == 2) pa[i] = col_hi ? ph[i] : pa[i];
-      }
-      ap[cs] = __builtin_bit_cast(bf16x8, uint4{pa[0], pa[1], pa[2], pa[3]});
+    for (int i = 0; i < 8; ++i) {
+      l_lane += s[i];
+      z_lane = fmaf(s[i], vzv[i], z_lane);
+      pv[i] = s[i] * vsv[i];
     }
+    // P' into A fragments: the lane's tokens in the order {0,2,1,3,4,6,5,7}
+    uint32_t ph[4], pl[4];
+    split_bf16(pv[0], pv[2], ph[0], pl[0]);
+    split_bf16(pv[1], pv[3], ph[1], pl[1]);
+    split_bf16(pv[4], pv[6], ph[2], pl[2]);
+    split_bf16(pv[5], pv[7], ph[3], pl[3]);
+    // rows j < HG: hi of head j; rows j >= HG: lo of lane j-HG (rows >= 2HG
+    // only reach accumulator rows that are never read)
+    // (QN = 2: the second query's high rows 2HG.. keep their own values)
+    uint32_t pa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pa[i] = shr_keep<HG>(ph[i], pl[i]);
+      if constexpr (QN == 2) pa[i] = col_hi ? ph[i] : pa[i];
+    }
+    const bf16x8 ap = __builtin_bit_cast(bf16x8, uint4{pa[0], pa[1], pa[2], pa[3]});
 
     // P' x value codes; channel of N-tile nt in column j is 16 nt + j (adjacent
     // lanes read adjacent value columns: no LDS bank conflicts). Lane group g
@@ -812,7 +755,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
                        bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 0)),
                        bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y0, 2.0f, 1)),
                        bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 1))};
-        acc[0][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap[0], __builtin_bit_cast(bf16x8, bw), acc[0][nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, __builtin_bit_cast(bf16x8, bw), acc[nt], 0, 0, 0);
       }
     } else if constexpr (VB == 2) {
 #pragma unroll
@@ -831,13 +774,9 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
                        bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 2)),
                        bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y0, 2.0f, 3)),
                        bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 3))};
-#pragma unroll
-        for (int cs = 0; cs < CS; ++cs) {
-          acc[cs][nt] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap[cs], __builtin_bit_cast(bf16x8, b0), acc[cs][nt], 0, 0, 0);
-          acc[cs][nt + 1] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap[cs], __builtin_bit_cast(bf16x8, b1), acc[cs][nt + 1], 0, 0, 0);
-        }
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, __builtin_bit_cast(bf16x8, b0), acc[nt], 0, 0, 0);
+        acc[nt + 1] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, __builtin_bit_cast(bf16x8, b1), acc[nt + 1], 0, 0, 0);
       }
     } else {
 #pragma unroll
@@ -848,10 +787,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
                        bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y1, 512.0f, false)),
                        bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y0, 512.0f, true)),
                        bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y1, 512.0f, true))};
-#pragma unroll
-        for (int cs = 0; cs < CS; ++cs)
-          acc[cs][nt] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap[cs], __builtin_bit_cast(bf16x8, bw), acc[cs][nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, __builtin_bit_cast(bf16x8, bw), acc[nt], 0, 0, 0);
       }
     }
   };
@@ -902,7 +838,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   uint4 qstep[QPRE ? QB : 1][QPRE ? KS : 1];
   // B operand of the residual key product: q^T in three bf16 parts, columns
   // [0,HG) hi, [HG,2HG) mid, [2HG,3HG) lo, the rest zero (from the scaled q in qs)
-  // (several queries: set qb is query qb's, the same 3HG columns)
+  // (QN = 2: set qb is query qb's, the same 3HG columns)
   auto qstep_operand = [&](int qb, int ks) -> uint4 {
     const int col = QN == 1 ? 16 * qb + j : j;
     const int part = col / HG, hh = (QN == 1 ? 0 : qb * HG) + col % HG;
@@ -922,14 +858,10 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
   // tile rows (tokens) 8..15 of a step are masked; key rows repeat rows 0..7
   auto process_step = [&](int hs) {
     const int64_t t0 = q_tokens + static_cast<int64_t>(hs) * RSTEP;
-    // tokens of the step this lane's column of set cs sees (its query's own count)
-    int nv[CS];
-#pragma unroll
-    for (int cs = 0; cs < CS; ++cs) {
-      const int64_t Tj = Tb + QS * cs + (QS == 1 ? 0 : j / (2 * HG));
-      nv[cs] = static_cast<int>(Tj - t0 < RSTEP ? Tj - t0 : RSTEP);
-    }
-    float sc[CS][4];
+    // tokens of the step this lane's column sees (its query's own count)
+    const int64_t Tj = Tb + (QN == 1 ? 0 : j / (2 * HG));
+    const int nv = static_cast<int>(Tj - t0 < RSTEP ? Tj - t0 : RSTEP);
+    float sc[4];
     if constexpr (ROPE) {
       // key rows rotated by their position in the step, fp32 product as for pages
       rotate_q(t0);
@@ -946,7 +878,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
 #pragma unroll
       for (int ks = 0; ks < D / 4; ++ks) c = __builtin_amdgcn_mfma_f32_16x16x4f32(y[ks], bqv[ks], c, 0, 0, 0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sc[0][r] = (4 * g + r < nv[0]) ? c[r] : -INFINITY;
+      for (int r = 0; r < 4; ++r) sc[r] = (4 * g + r < nv) ? c[r] : -INFINITY;
     } else {
     floatx4 cres[QB];
 #pragma unroll
@@ -963,50 +895,42 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
       }
     }
 #pragma unroll
-    for (int cs = 0; cs < CS; ++cs)
-#pragma unroll
     for (int r = 0; r < 4; ++r) {
       float v;
-      if constexpr (QS == 2) {   // query q's sums in lanes < HG of set q; set 1 moves to columns 2HG..
-        const floatx4 x0 = cres[2 * cs], x1 = cres[2 * cs + 1];   // the set's two queries
-        const float v0 = x0[r] + row_shl<HG>(x0[r]) + row_shl<2 * HG>(x0[r]);
-        const float v1 = x1[r] + row_shl<HG>(x1[r]) + row_shl<2 * HG>(x1[r]);
+      if constexpr (QN == 2) {   // query q's sums in lanes < HG of set q; set 1 moves to columns 2HG..
+        const float v0 = cres[0][r] + row_shl<HG>(cres[0][r]) + row_shl<2 * HG>(cres[0][r]);
+        const float v1 = cres[1][r] + row_shl<HG>(cres[1][r]) + row_shl<2 * HG>(cres[1][r]);
         v = __uint_as_float(shr_keep<2 * HG>(__float_as_uint(v0), __float_as_uint(v1)));
       } else if constexpr (3 * HG <= 16) {
         v = cres[0][r] + row_shl<HG>(cres[0][r]) + row_shl<2 * HG>(cres[0][r]);
       } else {   // HG = 8: hi and mid in set 0, lo in set 1
         v = cres[0][r] + row_shl<HG>(cres[0][r]) + cres[QB - 1][r];
       }
-      sc[cs][r] = (4 * g + r < nv[cs]) ? v : -INFINITY;
+      sc[r] = (4 * g + r < nv) ? v : -INFINITY;
     }
     }   // rotary / plain keys
-    softmax_update(sc[0], std::integral_constant<int, 4>{}, Cs0{});
-    if constexpr (CS == 2) softmax_update(sc[CS - 1], std::integral_constant<int, 4>{}, Cs1{});
-    bf16x8 ap[CS];
+    softmax_update(sc, std::integral_constant<int, 4>{});
+    if constexpr (QN == 2) {
+      // the block's steps reach its second query's token, so a step may hold
+      // none of the first query's tokens; in a wave that has seen no token of
+      // it yet (reference max still -inf) 2^(-inf - -inf) is not 0: absent
+      // tokens get weight 0 explicitly
 #pragma unroll
-    for (int cs = 0; cs < CS; ++cs) {
-      if constexpr (QN > 1) {
-        // the block's steps reach its last query's token, so a step may hold
-        // none of an earlier query's tokens; in a wave that has seen no token
-        // of it yet (reference max still -inf) 2^(-inf - -inf) is not 0:
-        // absent tokens get weight 0 explicitly
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sc[cs][r] = 4 * g + r < nv[cs] ? sc[cs][r] : 0.f;
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) l_lane[cs] += sc[cs][r];   // absent tokens contribute 0
-      // P in bf16 hi/lo rows; k index 8g+i holds token 4g+i for i < 4, zero after
-      uint32_t ph[2], pl[2];
-      split_bf16(sc[cs][0], sc[cs][1], ph[0], pl[0]);
-      split_bf16(sc[cs][2], sc[cs][3], ph[1], pl[1]);
-      uint32_t pa[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        pa[i] = shr_keep<HG>(ph[i], pl[i]);
-        if constexpr (QS == 2) pa[i] = col_hi ? ph[i] : pa[i];
-      }
-      ap[cs] = __builtin_bit_cast(bf16x8, uint4{pa[0], pa[1], 0u, 0u});
+      for (int r = 0; r < 4; ++r) sc[r] = 4 * g + r < nv ? sc[r] : 0.f;
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) l_lane += sc[r];   // absent tokens contribute 0
+    // P in bf16 hi/lo rows; k index 8g+i holds token 4g+i for i < 4, zero after
+    uint32_t ph[2], pl[2];
+    split_bf16(sc[0], sc[1], ph[0], pl[0]);
+    split_bf16(sc[2], sc[3], ph[1], pl[1]);
+    uint32_t pa[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      pa[i] = shr_keep<HG>(ph[i], pl[i]);
+      if constexpr (QN == 2) pa[i] = col_hi ? ph[i] : pa[i];
+    }
+    const bf16x8 ap = __builtin_bit_cast(bf16x8, uint4{pa[0], pa[1], 0u, 0u});
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int c = 16 * nt + j;
@@ -1015,9 +939,7 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
       const uint32_t v0 = vr[(t4 + 0) * D], v1 = vr[(t4 + 1) * D];
       const uint32_t v2 = vr[(t4 + 2) * D], v3 = vr[(t4 + 3) * D];
       const bf16x8 bv = __builtin_bit_cast(bf16x8, uint4{v0 | (v1 << 16), v2 | (v3 << 16), 0u, 0u});
-#pragma unroll
-      for (int cs = 0; cs < CS; ++cs)
-        acc[cs][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap[cs], bv, acc[cs][nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, bv, acc[nt], 0, 0, 0);
     }
   };
 
@@ -1157,25 +1079,506 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
 
   __builtin_amdgcn_s_setprio(3);   // the epilogue and merge end the block's critical path
   // ---- wave epilogue -----------------------------------------------------------
-  // per (query, head) pair vh: set vh / (HG QS), in it column
-  // (query in the set) 2HG + vh % HG
+  // per (query, head) pair vh: its column (vh / HG) 2HG + vh % HG
   float lsum[GC], zsum[GC], mh[GC];
-#pragma unroll
-  for (int cs = 0; cs < CS; ++cs) {
-    float l_ = l_lane[cs], z_ = z_lane[cs];
+  {
+    float l_ = l_lane, z_ = z_lane;
     l_ += xor16(l_);
     l_ += xor32(l_);
     z_ += xor16(z_);
     z_ += xor32(z_);
 #pragma unroll
-    for (int k = 0; k < HG * QS; ++k) {
-      const int vh = HG * QS * cs + k, col = (k / HG) * 2 * HG + k % HG;
+    for (int vh = 0; vh < GC; ++vh) {
+      const int col = (vh / HG) * 2 * HG + vh % HG;
       lsum[vh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_), col));
       zsum[vh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, z_), col));
-      mh[vh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_lane[cs]), col));
+      mh[vh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_lane), col));
     }
   }
-  finish_unit<D, HG, NW, QN>(p, &acc[0][0], mh, lsum, zsum, arena, last_block, b, qi, h, split);
+  finish_unit<D, HG, NW, QN>(p, acc, mh, lsum, zsum, arena, last_block, b, qi, h, split);
+}
+
+// ---- four queries per block over dequantised keys (GQA 4) -----------------------
+// Four consecutive queries of a sequence per block: their 16 (query, head)
+// pairs are the 16 columns of the key product and the 16 rows of the value
+// product. Each page's keys are dequantised in registers (code * s + z per
+// channel, in fp32) straight into the f16 high and remainder parts of the A
+// operand, and the query's parts (high and remainder of q', built once) are
+// the B operand: three products per k-step, Kh Qh + Kl Qh + Kh Ql. The page
+// work that grows with the queries is then the softmax and the weights only;
+// kivi_mfma_kernel instead folds the page's key scales into every query's
+// columns, work that grows with each query. f16 range: q' and the page's
+// keys are scaled by powers of two below 2^15 (exact; the page's bound is
+// max(|z|, |z + (2^KB - 1) s|) over its channels), undone on the scores.
+// Residual tokens: the bf16 key rows against q' in three bf16 parts, as in
+// kivi_mfma_kernel. Uniform batches only (one fill level).
+template <int KB, int VB, int D>
+__global__ __launch_bounds__(512, 1) void kivi_deq_kernel(MfmaParams p) {
+  static_assert((KB == 2 || KB == 4) && VB == 2 && D <= 128, "2- or 4-bit keys, 2-bit values, d <= 128");
+  constexpr int HG = 4, QN = 4, GC = HG * QN;   // 16 (query, head) pairs
+  constexpr int NW = 8, NTH = 64 * NW;
+  using PG = PageGeom<KB, VB, D>;
+  constexpr int KS = D / 32;             // k-steps of the key product
+  constexpr int NT = D / 16;             // channel tiles of the value product
+  constexpr int CPG = D / 4;             // key channels per lane group
+  constexpr int KROW = D * KB / 8;       // bytes per key token row
+  constexpr int CPR_K = KROW / 16;
+  constexpr int FPW = 32 / KB;           // codes per 32-bit word
+  constexpr int KW = CPG / FPW;          // key-code words per lane per 16-token tile
+  constexpr int VROW = 32 * VB / 8;
+  constexpr float kLevels = float((1 << KB) - 1);
+  // per-wave LDS: two page buffers; a residual step's 8 key + 8 value rows
+  // borrow page buffer 1 (and what follows) before the first page and after
+  // the last
+  constexpr int WAVE_LDS = 2 * PG::BYTES > PG::BYTES + PG::RING ? 2 * PG::BYTES : PG::BYTES + PG::RING;
+  constexpr int RED = NW * GC * (D + 2) * 4;
+  constexpr int ARENA = NW * WAVE_LDS > RED ? NW * WAVE_LDS : RED;
+  __shared__ __attribute__((aligned(16))) float qs[GC][D];
+  __shared__ __attribute__((aligned(16))) uint8_t arena[ARENA];
+  __shared__ int last_block;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 15, g = lane >> 4;
+  const int split = blockIdx.x, h = blockIdx.y;
+  const int rows_b = p.nq / QN;
+  const int b = blockIdx.z / rows_b, qi = (blockIdx.z - b * rows_b) * QN;
+  const uint8_t* ringp = p.pm.ring(b, h);
+  // column j: query j / HG of the block (at position Tb - 1 + j / HG), head j % HG
+  const int64_t q_tokens = p.q_tokens;
+  const int64_t Tb = p.T - (p.nq - 1 - qi);   // tokens the block's first query sees
+  const int64_t TbL = Tb + QN - 1;            // ... and its last
+  int32_t n_pages = p.n_pages;
+  int32_t n_steps = static_cast<int32_t>((TbL - q_tokens + 7) / 8);
+  const bool in_page = TbL <= q_tokens;
+  if (in_page) {
+    n_pages = static_cast<int32_t>((TbL + kPage - 1) / kPage);
+    n_steps = 0;
+  }
+  const int64_t Tj = Tb + j / HG;             // tokens column j's query sees
+  uint8_t* wbuf = arena + wave * WAVE_LDS;
+
+  floatx4 acc[NT];   // rows 4g + r: pair 4g + r
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_lane = -INFINITY, l_lane = 0.f, z_lane = 0.f;   // column j (summed over g at the end)
+
+  auto softmax_update = [&](float* s, auto ns_tag) {
+    constexpr int NS = decltype(ns_tag)::value;
+    float pmax = s[0];
+#pragma unroll
+    for (int i = 1; i < NS; ++i) pmax = fmaxf(pmax, s[i]);
+    const bool grows = pmax > m_lane + kMaxSlack;
+    if (__builtin_amdgcn_ballot_w64(grows) != 0) {   // wave-uniform
+      pmax = fmaxf(pmax, xor16(pmax));
+      pmax = fmaxf(pmax, xor32(pmax));
+      const float m_new = fmaxf(m_lane, pmax);
+      const float alpha = m_new == m_lane ? 1.0f : fast_exp2(m_lane - m_new);
+      l_lane *= alpha;
+      z_lane *= alpha;
+      m_lane = m_new;
+      // accumulator row 4g + r is pair 4g + r: its factor from lane 4g + r
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float a = __shfl(alpha, 4 * g + r, 64);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= a;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i) s[i] = fast_exp2(s[i] - m_lane);
+  };
+
+  // ---- this wave's pages: block `split` takes a contiguous range, its waves
+  // every NW-th page of it ---------------------------------------------------
+  const int waves_total = p.splits * NW;
+  const int pg0 = static_cast<int>(static_cast<int64_t>(split) * n_pages / p.splits);
+  const int pg1 = static_cast<int>(static_cast<int64_t>(split + 1) * n_pages / p.splits);
+  const int n_mine = pg0 + wave < pg1 ? (pg1 - pg0 - wave + NW - 1) / NW : 0;
+
+  auto issue_page = [&](int k) {   // page k of this wave -> buffer k % 2
+    const uint8_t* src = p.pm.page(b, h, pg0 + wave + NW * k);
+    const uint32_t dst = lds_addr(wbuf + (k % 2) * PG::BYTES);
+#pragma unroll
+    for (int i = 0; i < PG::DMA; ++i) {
+      const int off = i * 1024 + lane * 16;
+      int from = off;
+      if (off < PG::CODES) from = krow_off<CPR_K>(off / KROW, off % KROW);
+      if (i + 1 < PG::DMA || off < PG::BYTES) dma16(src + from, dst + i * 1024);
+    }
+  };
+
+  // B operand of the key product (q' of pair j, scaled by 2^-eq), for k-step
+  // ks and lane group g: channels g CPG + 8 ks + {0,2,1,3,4,6,5,7}, the order
+  // in which the key fragments below are built
+  half8 bqh[KS], bql[KS];
+  int eq = 0;
+
+  // one word of key codes -> its FPW codes as f32, field order
+  auto codes_f32 = [&](uint32_t wd, float* x) {
+    if constexpr (KB == 2) {
+      const uint32_t y0 = wd & 0x33333333u, y1 = (wd >> 2) & 0x33333333u;
+      // byte SEL of y0 holds fields 4 SEL, 4 SEL + 2; of y1 fields 4 SEL + 1, 4 SEL + 3
+      const float2 a0 = codes2_f32<0>(y0), a1 = codes2_f32<0>(y1);
+      const float2 a2 = codes2_f32<1>(y0), a3 = codes2_f32<1>(y1);
+      const float2 a4 = codes2_f32<2>(y0), a5 = codes2_f32<2>(y1);
+      const float2 a6 = codes2_f32<3>(y0), a7 = codes2_f32<3>(y1);
+      x[0] = a0.x; x[2] = a0.y; x[1] = a1.x; x[3] = a1.y;
+      x[4] = a2.x; x[6] = a2.y; x[5] = a3.x; x[7] = a3.y;
+      x[8] = a4.x; x[10] = a4.y; x[9] = a5.x; x[11] = a5.y;
+      x[12] = a6.x; x[14] = a6.y; x[13] = a7.x; x[15] = a7.y;
+    } else {
+      // nibbles -> bytes: byte k of y0 holds field 2k, of y1 field 2k + 1
+      const uint32_t y0 = wd & 0x0F0F0F0Fu, y1 = (wd >> 4) & 0x0F0F0F0Fu;
+      const auto a0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(y0, 512.0f, false);
+      const auto a1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(y1, 512.0f, false);
+      const auto a2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(y0, 512.0f, true);
+      const auto a3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(y1, 512.0f, true);
+      x[0] = a0[0]; x[2] = a0[1]; x[1] = a1[0]; x[3] = a1[1];
+      x[4] = a2[0]; x[6] = a2[1]; x[5] = a3[0]; x[7] = a3[1];
+    }
+  };
+
+  auto process_page = [&](const uint8_t* pg, int64_t t0) {
+    // f16 range of the page's keys: |code s + z| <= max(|z|, |z + levels s|)
+    float kb = 0.f;
+#pragma unroll
+    for (int c = lane; c < D; c += 64) {
+      const float sc = reinterpret_cast<const float*>(pg + PG::OFF_KS)[c];
+      const float zc = reinterpret_cast<const float*>(pg + PG::OFF_KZ)[c];
+      kb = fmaxf(kb, fmaxf(fabsf(zc), fabsf(fmaf(kLevels, sc, zc))));
+    }
+    int ek = 0;
+    if (__builtin_amdgcn_ballot_w64(kb >= 32768.f) != 0) {   // rare: keys beyond 2^15
+      int ex;
+      frexpf(wave_max(kb), &ex);
+      ek = __builtin_amdgcn_readfirstlane(ex - 15);
+    }
+    uint32_t kp[2][KW];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int w = 0; w < KW; ++w)
+        kp[mt][w] = *reinterpret_cast<const uint32_t*>(pg + krow_off<CPR_K>(tile_tok<false>(mt, j), g * (KW * 4) + 4 * w));
+    floatx4 c[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int w = 0; w < KW; ++w) {
+      // scale and offset of this word's FPW channels g CPG + FPW w + i
+      const int cw = g * CPG + FPW * w;
+      float sv[FPW], zv[FPW];
+#pragma unroll
+      for (int i = 0; i < FPW / 4; ++i) {
+        const float4 s4 = *reinterpret_cast<const float4*>(pg + PG::OFF_KS + 4 * (cw + 4 * i));
+        const float4 z4 = *reinterpret_cast<const float4*>(pg + PG::OFF_KZ + 4 * (cw + 4 * i));
+        sv[4 * i] = s4.x; sv[4 * i + 1] = s4.y; sv[4 * i + 2] = s4.z; sv[4 * i + 3] = s4.w;
+        zv[4 * i] = z4.x; zv[4 * i + 1] = z4.y; zv[4 * i + 2] = z4.z; zv[4 * i + 3] = z4.w;
+      }
+      if (ek) {
+#pragma unroll
+        for (int i = 0; i < FPW; ++i) {
+          sv[i] = ldexpf(sv[i], -ek);
+          zv[i] = ldexpf(zv[i], -ek);
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        float x[FPW];
+        codes_f32(kp[mt][w], x);
+#pragma unroll
+        for (int i = 0; i < FPW; ++i) x[i] = fmaf(x[i], sv[i], zv[i]);
+        // k-steps of this word: 8 channels each, fragment order {0,2,1,3,4,6,5,7}
+#pragma unroll
+        for (int k8 = 0; k8 < FPW / 8; ++k8) {
+          const float* y = x + 8 * k8;
+          uint32_t hi[4], lo[4];
+          split_f16(y[0], y[2], hi[0], lo[0]);
+          split_f16(y[1], y[3], hi[1], lo[1]);
+          split_f16(y[4], y[6], hi[2], lo[2]);
+          split_f16(y[5], y[7], hi[3], lo[3]);
+          const half8 ah = cat4h(hi[0], hi[1], hi[2], hi[3]), al = cat4h(lo[0], lo[1], lo[2], lo[3]);
+          const int ks = w * (FPW / 8) + k8;
+          c[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bqh[ks], c[mt], 0, 0, 0);
+          c[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bqh[ks], c[mt], 0, 0, 0);
+          c[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bql[ks], c[mt], 0, 0, 0);
+        }
+      }
+    }
+    float s[8];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[4 * mt + r] = c[mt][r];
+    const int es = ek + eq;
+    if (es) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[i] = ldexpf(s[i], es);
+    }
+    // causal mask: a page that the first query does not see whole (its last
+    // page, or one past it when a later query's token opens it)
+    const bool masked_page = Tb - t0 < kPage;
+    const int nvalid = static_cast<int>(Tj - t0);
+    if (masked_page) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (tile_tok<false>(mt, 4 * g + r) >= nvalid) s[4 * mt + r] = -INFINITY;
+    }
+    softmax_update(s, std::integral_constant<int, 8>{});
+    if (masked_page) {   // a column with no token yet has max -inf: weight 0
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (tile_tok<false>(mt, 4 * g + r) >= nvalid) s[4 * mt + r] = 0.f;
+    }
+    // per-token value scale and offset of this lane's tokens tile_tok(mt, 4g + r)
+    const float4 vs0 = *reinterpret_cast<const float4*>(pg + PG::OFF_VS + 32 * g);
+    const float4 vs1 = *reinterpret_cast<const float4*>(pg + PG::OFF_VS + 16 + 32 * g);
+    const float4 vz0 = *reinterpret_cast<const float4*>(pg + PG::OFF_VZ + 32 * g);
+    const float4 vz1 = *reinterpret_cast<const float4*>(pg + PG::OFF_VZ + 16 + 32 * g);
+    const float vsv[8] = {vs0.x, vs0.y, vs0.z, vs0.w, vs1.x, vs1.y, vs1.z, vs1.w};
+    const float vzv[8] = {vz0.x, vz0.y, vz0.z, vz0.w, vz1.x, vz1.y, vz1.z, vz1.w};
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      l_lane += s[i];
+      z_lane = fmaf(s[i], vzv[i], z_lane);
+      pv[i] = s[i] * vsv[i];
+    }
+    // P' rows (pair j) in bf16 high and remainder parts, tokens in the order
+    // {0,2,1,3,4,6,5,7}: two A operands on the same value codes
+    uint32_t ph[4], pl[4];
+    split_bf16(pv[0], pv[2], ph[0], pl[0]);
+    split_bf16(pv[1], pv[3], ph[1], pl[1]);
+    split_bf16(pv[4], pv[6], ph[2], pl[2]);
+    split_bf16(pv[5], pv[7], ph[3], pl[3]);
+    const bf16x8 aph = __builtin_bit_cast(bf16x8, uint4{ph[0], ph[1], ph[2], ph[3]});
+    const bf16x8 apl = __builtin_bit_cast(bf16x8, uint4{pl[0], pl[1], pl[2], pl[3]});
+#pragma unroll
+    for (int nt = 0; nt < NT; nt += 2) {   // two channel tiles per code word
+      const uint8_t* col = pg + PG::OFF_VC + (16 * nt + j) * VROW + 2 * g;
+      u16x2 xv;
+      xv.x = *reinterpret_cast<const uint16_t*>(col);
+      xv.y = *reinterpret_cast<const uint16_t*>(col + 16 * VROW);
+      const uint32_t x = __builtin_bit_cast(uint32_t, xv);
+      const uint32_t y0 = x & 0x33333333u, y1 = (x >> 2) & 0x33333333u;
+      const bf16x8 b0 = __builtin_bit_cast(bf16x8, uint4{bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y0, 2.0f, 0)),
+                                                         bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 0)),
+                                                         bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y0, 2.0f, 1)),
+                                                         bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 1))});
+      const bf16x8 b1 = __builtin_bit_cast(bf16x8, uint4{bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y0, 2.0f, 2)),
+                                                         bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 2)),
+                                                         bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y0, 2.0f, 3)),
+                                                         bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 3))});
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aph, b0, acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(apl, b0, acc[nt], 0, 0, 0);
+      acc[nt + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aph, b1, acc[nt + 1], 0, 0, 0);
+      acc[nt + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(apl, b1, acc[nt + 1], 0, 0, 0);
+    }
+  };
+
+  // ---- residual (unquantised) tokens, 8 per step -----------------------------
+  uint8_t* wring = wbuf + PG::BYTES;
+  constexpr int LPR = 2 * D / 16;           // lanes per bf16 row
+  constexpr int RPI = 64 / LPR;             // rows per 16-byte-per-lane copy
+  constexpr int RSTEP = 8;
+  auto issue_step = [&](int hs) -> int {    // returns the copies issued
+    const int64_t t0 = q_tokens + static_cast<int64_t>(hs) * RSTEP;
+    const int nv = static_cast<int>(TbL - t0 < RSTEP ? TbL - t0 : RSTEP);
+    const int row_in = lane / LPR, col_b = (lane % LPR) * 16;
+    const int slots = static_cast<int>(p.ring_slots);
+    const int slot0 = static_cast<int>(t0 % p.ring_slots);
+    int issued = 0;
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+#pragma unroll
+      for (int i = 0; i < (RSTEP + RPI - 1) / RPI; ++i) {
+        if (i * RPI >= nv) continue;          // wave-uniform
+        const int r = i * RPI + row_in;
+        const int slot = slot0 + r < slots ? slot0 + r : slot0 + r - slots;
+        const uint8_t* src = ringp + (kv * p.ring_slots + slot) * (2 * D) + col_b;
+        if (r < nv && r < RSTEP) dma16(src, lds_addr(wring + kv * RSTEP * 2 * D + i * 1024));
+        ++issued;
+      }
+    }
+    // value rows of absent tokens must be finite (they meet weight 0): zero them
+    for (int i = lane; i < (RSTEP - nv) * 2 * D / 16; i += 64)
+      *reinterpret_cast<uint4*>(wring + RSTEP * 2 * D + nv * 2 * D + i * 16) = uint4{0u, 0u, 0u, 0u};
+    return issued;
+  };
+  // B operands of the residual key product: q' of pair j (unscaled) in three
+  // bf16 parts (high, middle, remainder), channels 32 ks + 8 g + 0..7
+  auto qpart = [&](int part, int ks) -> bf16x8 {
+    uint32_t w4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float2 qq = *reinterpret_cast<const float2*>(&qs[j][32 * ks + 8 * g + 2 * i]);
+      const float h0 = bf16_trunc(qq.x), h1 = bf16_trunc(qq.y);
+      const float m0 = bf16_trunc(qq.x - h0), m1 = bf16_trunc(qq.y - h1);
+      const float x0 = part == 0 ? h0 : (part == 1 ? m0 : qq.x - h0 - m0);
+      const float x1 = part == 0 ? h1 : (part == 1 ? m1 : qq.y - h1 - m1);
+      w4[i] = pack_bf16(x0, x1);
+    }
+    return __builtin_bit_cast(bf16x8, uint4{w4[0], w4[1], w4[2], w4[3]});
+  };
+  // tile rows 8..15 of a step repeat rows 0..7 and are masked
+  auto process_step = [&](int hs) {
+    const int64_t t0 = q_tokens + static_cast<int64_t>(hs) * RSTEP;
+    const int nv = static_cast<int>(Tj - t0 < RSTEP ? Tj - t0 : RSTEP);
+    floatx4 cr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(wring + (j & 7) * 2 * D + (32 * ks + 8 * g) * 2);
+#pragma unroll
+      for (int part = 0; part < 3; ++part)
+        cr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qpart(part, ks), cr, 0, 0, 0);
+    }
+    float sc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[r] = (4 * g + r < nv) ? cr[r] : -INFINITY;
+    softmax_update(sc, std::integral_constant<int, 4>{});
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[r] = 4 * g + r < nv ? sc[r] : 0.f;   // absent tokens: weight 0
+#pragma unroll
+    for (int r = 0; r < 4; ++r) l_lane += sc[r];
+    uint32_t ph[2], pl[2];
+    split_bf16(sc[0], sc[1], ph[0], pl[0]);
+    split_bf16(sc[2], sc[3], ph[1], pl[1]);
+    const bf16x8 aph = __builtin_bit_cast(bf16x8, uint4{ph[0], ph[1], 0u, 0u});
+    const bf16x8 apl = __builtin_bit_cast(bf16x8, uint4{pl[0], pl[1], 0u, 0u});
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int c = 16 * nt + j;
+      const uint16_t* vr = reinterpret_cast<const uint16_t*>(wring + RSTEP * 2 * D) + c;
+      const int t4 = (4 * g) & 7;             // tokens >= 8 carry weight 0
+      const uint32_t v0 = vr[(t4 + 0) * D], v1 = vr[(t4 + 1) * D];
+      const uint32_t v2 = vr[(t4 + 2) * D], v3 = vr[(t4 + 3) * D];
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, uint4{v0 | (v1 << 16), v2 | (v3 << 16), 0u, 0u});
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aph, bv, acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(apl, bv, acc[nt], 0, 0, 0);
+    }
+  };
+
+  // ---- first requests: q (wave 0), this wave's first residual step, its first page
+  const int my_wave = (NW - 1 - wave) * p.splits + split;
+  const int q_bytes = HG * D * (p.q_bf16 ? 2 : 4);   // one query's heads of this KV head
+  int after_q = 0;
+  if (wave == 0) {
+#pragma unroll
+    for (int qq = 0; qq < QN; ++qq) {
+      const uint8_t* qsrc = p.q + (static_cast<int64_t>(b * p.nq + qi + qq) * p.q_heads + h * HG) * D * (p.q_bf16 ? 2 : 4);
+      for (int off = 0; off < q_bytes; off += 1024)
+        if (off + lane * 16 < q_bytes) dma16(qsrc + off + lane * 16, lds_addr(&qs[0][0]) + qq * q_bytes + off);
+    }
+  }
+  const bool has_step = my_wave < n_steps;
+  if (has_step) after_q += issue_step(my_wave);
+  if (n_mine > 0) {
+    issue_page(0);
+    after_q += PG::DMA;
+  }
+  if (wave == 0) wait_vm_upto(after_q);   // q has landed
+  __syncthreads();
+  {
+    // raw query (bf16 or f32) -> f32 * sm_scale * log2(e), in place
+    constexpr int PER = (GC * D + NTH - 1) / NTH;
+    float qv[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = tid + k * NTH;
+      qv[k] = 0.f;
+      if (i < GC * D)
+        qv[k] = p.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(&qs[0][0])[i]) : (&qs[0][0])[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = tid + k * NTH;
+      if (i < GC * D) (&qs[0][0])[i] = qv[k] * p.qscale;
+    }
+    __syncthreads();
+  }
+  {
+    // the key product's B operand: q' of pair j, channels g CPG + 8 ks +
+    // {0,2,1,3,4,6,5,7}, scaled below 2^15 (the wave sees every pair and channel)
+    float qa = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qa = fmaxf(qa, fabsf(qs[j][g * CPG + 8 * ks + i]));
+    if (__builtin_amdgcn_ballot_w64(qa >= 32768.f) != 0) {
+      int ex;
+      frexpf(wave_max(qa), &ex);
+      eq = __builtin_amdgcn_readfirstlane(ex - 15);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      float y[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = ldexpf(qs[j][g * CPG + 8 * ks + i], -eq);
+      uint32_t hi[4], lo[4];
+      split_f16(y[0], y[2], hi[0], lo[0]);
+      split_f16(y[1], y[3], hi[1], lo[1]);
+      split_f16(y[4], y[6], hi[2], lo[2]);
+      split_f16(y[5], y[7], hi[3], lo[3]);
+      bqh[ks] = cat4h(hi[0], hi[1], hi[2], hi[3]);
+      bql[ks] = cat4h(lo[0], lo[1], lo[2], lo[3]);
+    }
+  }
+  if (has_step) {
+    if (n_mine > 0) wait_vm<PG::DMA>();   // the first page may stay in flight
+    else wait_vm<0>();
+    wait_lds();
+    __builtin_amdgcn_wave_barrier();
+    process_step(my_wave);
+    wait_lds();
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- pages: DMA pipeline, one page ahead (page 0 already requested) --------
+#pragma unroll 1
+  for (int k = 0; k < n_mine; ++k) {
+    wait_lds();   // the buffer about to be refilled has been read
+    __builtin_amdgcn_wave_barrier();
+    const bool next = k + 1 < n_mine;
+    if (next) issue_page(k + 1);
+    if (next) wait_vm<PG::DMA>();
+    else wait_vm<0>();
+    __builtin_amdgcn_wave_barrier();
+    process_page(wbuf + (k % 2) * PG::BYTES, static_cast<int64_t>(pg0 + wave + NW * k) * kPage);
+  }
+
+  // ---- any further residual steps of this wave ---------------------------------
+#pragma unroll 1
+  for (int hs = my_wave + waves_total; hs < n_steps; hs += waves_total) {
+    wait_lds();
+    __builtin_amdgcn_wave_barrier();
+    issue_step(hs);
+    wait_vm<0>();
+    wait_lds();
+    __builtin_amdgcn_wave_barrier();
+    process_step(hs);
+  }
+  wait_lds();
+
+  // ---- wave epilogue: column j's sums over the lane groups ----------------------
+  float lsum[GC], zsum[GC], mh[GC];
+  {
+    float l_ = l_lane, z_ = z_lane;
+    l_ += xor16(l_);
+    l_ += xor32(l_);
+    z_ += xor16(z_);
+    z_ += xor32(z_);
+#pragma unroll
+    for (int vh = 0; vh < GC; ++vh) {
+      lsum[vh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_), vh));
+      zsum[vh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, z_), vh));
+      mh[vh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_lane), vh));
+    }
+  }
+  finish_unit<D, HG, NW, QN, true>(p, acc, mh, lsum, zsum, arena, last_block, b, qi, h, split);
 }
 
 // ---- rotary keys, GQA group of 4: dense scores on v_mfma_f32_4x4x1_16b_f32 ----
@@ -1697,8 +2100,8 @@ __global__ __launch_bounds__(NW * 64, 3) void rope4_kernel(MfmaParams p) {
 }
 
 
-// rows: grid rows (batch * queries / qn); qn: queries per block (2 or 4: GQA
-// 4, keys without rotation; 4 only where kivi_qn4 allows)
+// rows: grid rows (batch * queries / qn); qn: queries per block (2: GQA 4,
+// keys without rotation; 4: kivi_deq_kernel, 2-bit values, d <= 128)
 template <int KB, int VB, int D, bool ROPE>
 hipError_t by_hg(const MfmaParams& p, int hg, int rows, int qn, hipStream_t st) {
   dim3 grid(p.splits, p.kv_heads, rows);
@@ -1706,9 +2109,9 @@ hipError_t by_hg(const MfmaParams& p, int hg, int rows, int qn, hipStream_t st) 
     case 1: hipLaunchKernelGGL((kivi_mfma_kernel<KB, VB, D, 1, ROPE>), grid, dim3(64 * kivi_waves(KB, VB, D, 1, ROPE)), 0, st, p); break;
     case 2: hipLaunchKernelGGL((kivi_mfma_kernel<KB, VB, D, 2, ROPE>), grid, dim3(64 * kivi_waves(KB, VB, D, 2, ROPE)), 0, st, p); break;
     case 4:
-      if constexpr (!ROPE && kivi_qn4(KB, VB, D)) {
-        if (qn == 4) {
-          hipLaunchKernelGGL((kivi_mfma_kernel<KB, VB, D, 4, ROPE, 4>), grid, dim3(64 * kivi_waves(KB, VB, D, 4, ROPE)), 0, st, p);
+      if constexpr (!ROPE && VB == 2 && D <= 128) {
+        if (qn == 4) {   // four queries per block over dequantised keys
+          hipLaunchKernelGGL((kivi_deq_kernel<KB, VB, D>), grid, dim3(512), 0, st, p);
           break;
         }
       }
@@ -1803,15 +2206,12 @@ hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t st) {
   // one-query plan, whose workspace nq copies of hold the partials)
   // two queries per block: GQA 4, keys without rotation, an even number of
   // queries (their tokens in the ring or in pages)
-  // four per block (two column sets) where its LDS fits (a multiple of four
-  // queries, eight-wave blocks: 2-bit values, head_dim <= 128) and its rows
-  // alone fill a round of the 256 CUs: a four-query block costs about 1.6
-  // two-query blocks per page, so it only pays where it needs no more splits
-  // (at the kivi2 shape, 8 queries: 56.4 vs 69.5 us, 16: 110 vs 137; 4
-  // queries, which would need two splits and their merge: 39.9 vs 37.4)
+  // four per block over dequantised keys (kivi_deq_kernel): a multiple of
+  // four queries of a uniform batch, 2-bit values, head_dim <= 128 (at the
+  // kivi2 shape 4 queries 33.9 us against 35.5 with two per block, 8: 44.0
+  // against 69.0, 16: 84.5 against 136.1)
   const bool pairs = nq >= 2 && nq % 2 == 0 && g.hg == 4 && a.rope_theta == 0.0;
-  const bool fours = pairs && nq % 4 == 0 && kivi_qn4(g.bits, g.vbits, g.d) &&
-                     static_cast<int64_t>(g.batch) * (nq / 4) * g.kv_heads >= 256;
+  const bool fours = pairs && nq % 4 == 0 && g.vbits == 2 && g.d <= 128 && !a.seq_tokens;
   const int qn = fours ? 4 : pairs ? 2 : 1;
   Geometry rows = g;
   rows.batch = g.batch * nq / qn;

@@ -61,10 +61,10 @@ CASES = [
     # a block whose first query's token is the last quantised one (288) and
     # whose second is the first ring token: every page whole, one ring step
     (synth.KIVI, 2, 128, 4, torch.bfloat16, 16, 305, 0.0, 0, 22),
-    # four queries per block (a multiple of four queries, GQA 4, 2-bit
-    # values, and batch x n_q / 4 x KV heads >= 256 rows of blocks; value
-    # bits and batch last): the block's first query's token in the last page
-    # and the other three in the ring (each sees a different part of it)
+    # four queries per block over dequantised keys (a multiple of four
+    # queries, GQA 4, 2-bit values; value bits and batch last): the block's
+    # first query's token in the last page and the other three in the ring
+    # (each sees a different part of it)
     (synth.KIVI, 2, 128, 4, torch.bfloat16, 16, 305, 0.0, 0, 20, 0, 26),
     # a block whose first query sees exactly ten pages: the page after holds
     # none of its tokens (weight 0), many splits

@@ -73,7 +73,7 @@ def _family(kernels, stem):
     return {n: v for n, v in kernels.items() if stem in n}
 
 
-@pytest.mark.parametrize("stem", ["kivi_mfma_kernel", "rope4_kernel", "paged_mfma_kernel"])
+@pytest.mark.parametrize("stem", ["kivi_mfma_kernel", "kivi_deq_kernel", "rope4_kernel", "paged_mfma_kernel"])
 def test_matrix_core_decodes_use_no_scratch(kernels, stem):
     fam = _family(kernels, stem)
     assert fam, stem
@@ -91,7 +91,7 @@ BUDGETS = [
     ("kivi_mfma_kernelILi4ELi2ELi128ELi4ELb0ELi1E", 256),   # 4-bit keys, 2-bit values (88 KB LDS)
     ("kivi_mfma_kernelILi4ELi4ELi128ELi4ELb0ELi1E", 168),   # KIVI 4-bit
     ("kivi_mfma_kernelILi2ELi2ELi128ELi4ELb0ELi2E", 256),   # 2-bit, two queries per block (one per CU)
-    ("kivi_mfma_kernelILi2ELi2ELi128ELi4ELb0ELi4E", 256),   # 2-bit, four queries per block (one per CU)
+    ("kivi_deq_kernelILi2ELi2ELi128E", 256),                # 2-bit, four queries per block, dequantised keys
     ("rope4_kernelILi128ELi4E", 168),                       # rotary keys, GQA 4
 ]
 
