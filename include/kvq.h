@@ -50,6 +50,15 @@
  *     bound). No operand saturates: a page whose folded query
  *     q * s * sm_scale * log2(e) exceeds the f16 maximum (65504) is rescaled
  *     by a power of two inside the kernel and the scaling undone on its scores.
+ *     Several queries decoded four per block (kvq_decode_attention_multi with
+ *     a multiple of four queries of a KIVI cache at GQA 4 with 2-bit values,
+ *     head_dim <= 128) take each page's keys dequantised into f16 high and
+ *     remainder parts, and q' = q * sm_scale * log2(e) likewise, each scaled
+ *     below 2^15 by a power of two: a score then carries, besides the bound
+ *     above, up to 2^-24 * (|q'|_1 * max(1, K/2^14) + sum_c K_c * max(1,
+ *     Q/2^14)) log2 units from f16 subnormals, K the page's largest |key|
+ *     and Q = max_c |q'_c| (negligible unless some channel's keys or queries
+ *     are tiny beside another's that reach 2^14).
  *   - Calls on distinct streams are independent; concurrent calls that touch
  *     the same cache slab or workspace race (the caller's responsibility).
  */

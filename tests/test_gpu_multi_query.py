@@ -7,6 +7,7 @@ matrix-core kernel when the cache's inputs are 16-bit, one, two or four
 queries per block; the generic kernel for fp32 inputs), and FP8 and bfloat16
 caches (their matrix-core kernel without rotary keys)."""
 
+import numpy as np
 import pytest
 import torch
 
@@ -113,3 +114,53 @@ def test_single_query_is_the_plain_decode():
     kvq.kvq_decode_attention_multi(cfg, cache, 0, T, q.unsqueeze(1).contiguous(), out, ws)
     assert torch.equal(out[:, 0], want)
 
+
+
+
+@pytest.mark.parametrize("which", ["keys", "queries"])
+def test_four_query_blocks_f16_range(which):
+    """Four queries per block take the keys dequantised into f16 high and
+    remainder parts and q' = q * sm_scale * log2(e) likewise; a page whose
+    keys reach 2^15, or queries that do, are scaled by powers of two on the
+    device and the scaling undone on the scores. Tokens X and Y of the first
+    page are built so that X wins the softmax by more than 1e4 log2 units
+    with the true operands, while Y would win had the large operand
+    saturated at the f16 maximum (high and remainder parts both at 65504):
+    "keys": X's channel 0 is 3e5 against q_0 = 1 (true score 3.8e4, 1.7e4
+    saturated) and Y's channel 1 is 2e4 against q_1 = 9.8 (2.5e4);
+    "queries": q_5 = 2e6 against X's channel 5 of 10 (q'_5 = 2.5e5, 1.3e5
+    saturated) and q_6 = 3.9e5 against Y's channel 6 of 40. Every output row
+    is then X's dequantised value row; plain 2e-3 against the oracle, queries
+    in the ring."""
+    w = small(synth.KIVI, 2, 128, torch.bfloat16, 16, B=2, Hkv=1, hg=4, T=100)
+    T, X, Y = w.tokens, 3, 17
+    k, v = synth.keys_values(w, device=DEV)
+    q = queries(w, 4).float()
+    k = k.float()
+    if which == "keys":
+        k[:, X, :, 0] = 3.0e5
+        k[:, Y, :, 1] = 2.0e4
+        q[:, :, :, 0] = 1.0
+        q[:, :, :, 1] = 9.8
+    else:
+        k[:, :, :, 5:7] *= 0.1
+        k[:, X, :, 5] = 10.0
+        k[:, Y, :, 6] = 40.0
+        q[:, :, :, 5] = 2.0e6
+        q[:, :, :, 6] = 3.92e5
+    k = k.to(torch.bfloat16).contiguous()
+    q = q.to(torch.bfloat16).contiguous()
+    cfg = H.config(w, T + 40)
+    cache = kvq.alloc_cache(cfg)
+    oc = H.oracle_cache(w, T + 40)
+    H.append_chunks(cfg, cache, k, v, [T], oc=oc)
+    out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    ws = torch.zeros(4 * kvq.kvq_cache_bytes(cfg, T, kvq.KVQ_BYTES_WORKSPACE), dtype=torch.uint8, device=DEV)
+    kvq.kvq_decode_attention_multi(cfg, cache, 0, T, q, out, ws)
+    want = oc.decode_multi(0, H.values(q))
+    # the construction: every row is X's value row
+    vx = want[:, :1, :1]
+    assert np.allclose(want, np.broadcast_to(vx, want.shape), atol=1e-6)
+    err = H.max_err(out, want)
+    print(f"[four-query range] {which}: max-abs error {err:.2e}", flush=True)
+    assert err <= H.ATOL, err
