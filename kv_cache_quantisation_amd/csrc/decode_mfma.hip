@@ -1581,6 +1581,357 @@ __global__ __launch_bounds__(512, 1) void kivi_deq_kernel(MfmaParams p) {
   finish_unit<D, HG, NW, QN, true>(p, acc, mh, lsum, zsum, arena, last_block, b, qi, h, split);
 }
 
+// ---- long chunks of queries: one pass over the pages for 32 queries ----------
+// 32 consecutive queries of a sequence per block (GQA 4, head_dim 128, 2- or
+// 4-bit keys, 2-bit values), wave w taking queries 4w..4w+3 (its 16 (query,
+// head) pairs are the columns of its key product, as in kivi_deq_kernel).
+// The block walks the tokens in chunks of 32: the quantised pages up to the
+// last query's, then the residual ring up to its token. Each chunk is copied
+// to LDS once, and the block dequantises it once: wave w builds the f16
+// high/remainder key fragment (token tile w / 4, k-step w % 4) and the bf16
+// value fragment of channel tile w for every wave to read. Every wave then
+// takes the whole chunk against its own queries. Per chunk: copy (issued
+// during the previous chunk's products), barrier, dequantisation, barrier,
+// products. One split: the grid's rows are (sequence, 32 queries), enough to
+// fill the chip when batch * KV heads * n_q / 32 >= 256, and each wave writes
+// its own rows' outputs.
+template <int KB>
+__device__ __forceinline__ void key_codes8(uint32_t wd, int half, float* x) {
+  // the 8 codes of k-step `half` of a word (2-bit: fields 8 half ..; 4-bit:
+  // the word), field order
+  if constexpr (KB == 2) {
+    const uint32_t y0 = wd & 0x33333333u, y1 = (wd >> 2) & 0x33333333u;
+    float2 a0, a1, a2, a3;
+    if (half == 0) {
+      a0 = codes2_f32<0>(y0); a1 = codes2_f32<0>(y1); a2 = codes2_f32<1>(y0); a3 = codes2_f32<1>(y1);
+    } else {
+      a0 = codes2_f32<2>(y0); a1 = codes2_f32<2>(y1); a2 = codes2_f32<3>(y0); a3 = codes2_f32<3>(y1);
+    }
+    x[0] = a0.x; x[2] = a0.y; x[1] = a1.x; x[3] = a1.y;
+    x[4] = a2.x; x[6] = a2.y; x[5] = a3.x; x[7] = a3.y;
+  } else {
+    const uint32_t y0 = wd & 0x0F0F0F0Fu, y1 = (wd >> 4) & 0x0F0F0F0Fu;
+    const auto a0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(y0, 512.0f, false);
+    const auto a1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(y1, 512.0f, false);
+    const auto a2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(y0, 512.0f, true);
+    const auto a3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(y1, 512.0f, true);
+    x[0] = a0[0]; x[2] = a0[1]; x[1] = a1[0]; x[3] = a1[1];
+    x[4] = a2[0]; x[6] = a2[1]; x[5] = a3[0]; x[7] = a3[1];
+  }
+}
+
+template <int KB>
+__global__ __launch_bounds__(512, 1) void kivi_chunk_kernel(MfmaParams p) {
+  constexpr int D = 128, VB = 2, HG = 4;
+  constexpr int NW = 8, NTH = 512, QB = 4 * NW;   // 32 queries per block
+  using PG = PageGeom<KB, VB, D>;
+  constexpr int KS = D / 32, NT = D / 16, CPG = D / 4;
+  constexpr int KROW = D * KB / 8, CPR_K = KROW / 16;
+  constexpr int FPW = 32 / KB, KW = CPG / FPW;
+  constexpr int VROW = 32 * VB / 8;
+  constexpr int ROWB = 2 * D;                      // bytes of a bf16 residual row
+  constexpr int STAGE = 2 * kPage * ROWB;          // a ring chunk: 32 key + 32 value rows
+  static_assert(PG::BYTES <= STAGE && NW == 2 * KS && NW == NT, "one fragment of each kind per wave");
+  constexpr float kLevels = float((1 << KB) - 1);
+  __shared__ __attribute__((aligned(16))) uint8_t stage[2][STAGE];
+  __shared__ __attribute__((aligned(16))) uint4 kfrag[2 * KS][2][64];   // [tile * KS + ks][hi, lo][lane]
+  __shared__ __attribute__((aligned(16))) uint4 vfrag[NT][64];          // [channel tile][lane]
+  __shared__ __attribute__((aligned(16))) float vsc[kPage], vzc[kPage];
+  __shared__ int chunk_e;                                               // the chunk's key scaling
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 15, g = lane >> 4;
+  const int h = blockIdx.y;
+  const int groups = p.nq / QB;
+  const int b = blockIdx.z / groups, qi = (blockIdx.z - b * groups) * QB;
+  const uint8_t* ringp = p.pm.ring(b, h);
+  const int64_t q_tokens = p.q_tokens;
+  const int64_t Tb = p.T - (p.nq - 1 - qi);        // tokens the block's first query sees
+  const int64_t TbL = Tb + QB - 1;                 // ... and its last
+  const int64_t Tj = Tb + 4 * wave + j / HG;       // ... and column j of this wave
+  const int n_pages = static_cast<int>(TbL <= q_tokens ? (TbL + kPage - 1) / kPage : q_tokens / kPage);
+  const int n_ring = TbL <= q_tokens ? 0 : static_cast<int>((TbL - q_tokens + kPage - 1) / kPage);
+  const int n_chunks = n_pages + n_ring;
+
+  // stale ring rows (past the last query's token) must be finite: zero both stages
+  for (int i = tid; i < 2 * STAGE / 16; i += NTH) reinterpret_cast<uint4*>(&stage[0][0])[i] = uint4{0u, 0u, 0u, 0u};
+  __syncthreads();   // zeroed before any copy lands
+
+  // ---- the key product's B operand for this wave's 16 pairs (q' scaled by 2^-eq)
+  half8 bqh[KS], bql[KS];
+  int eq = 0;
+  {
+    const int64_t row = static_cast<int64_t>(b) * p.nq + qi + 4 * wave + j / HG;
+    const int64_t base = (row * p.q_heads + h * HG + j % HG) * D;
+    float y[KS][8];
+    float qa = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c0 = g * CPG + 8 * ks;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        y[ks][i] = load_q(p.q, base + c0 + i, p.q_bf16) * p.qscale;
+        qa = fmaxf(qa, fabsf(y[ks][i]));
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(qa >= 32768.f) != 0) {
+      int ex;
+      frexpf(wave_max(qa), &ex);
+      eq = __builtin_amdgcn_readfirstlane(ex - 15);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      float z[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) z[i] = ldexpf(y[ks][i], -eq);
+      uint32_t hi[4], lo[4];
+      split_f16(z[0], z[2], hi[0], lo[0]);
+      split_f16(z[1], z[3], hi[1], lo[1]);
+      split_f16(z[4], z[6], hi[2], lo[2]);
+      split_f16(z[5], z[7], hi[3], lo[3]);
+      bqh[ks] = cat4h(hi[0], hi[1], hi[2], hi[3]);
+      bql[ks] = cat4h(lo[0], lo[1], lo[2], lo[3]);
+    }
+  }
+
+  floatx4 acc[NT];   // rows 4g + r: pair 4g + r of this wave
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_lane = -INFINITY, l_lane = 0.f, z_lane = 0.f;
+
+  // chunk c: page c (c < n_pages), else ring tokens from q_tokens + 32 (c - n_pages)
+  auto issue_chunk = [&](int c) {
+    uint8_t* dst = stage[c & 1];
+    if (c < n_pages) {
+      const uint8_t* src = p.pm.page(b, h, c);
+      const int off = wave * 1024 + lane * 16;
+      int from = off;
+      if (off < PG::CODES) from = krow_off<CPR_K>(off / KROW, off % KROW);
+      if (wave * 1024 < PG::BYTES && off < PG::BYTES) dma16(src + from, lds_addr(dst + wave * 1024));
+    } else {
+      const int64_t t0 = q_tokens + static_cast<int64_t>(c - n_pages) * kPage;
+      const int r = wave * 4 + lane / 16, cb = (lane % 16) * 16;   // row r of the chunk, 16 bytes
+      const bool valid = t0 + r < TbL;
+      const int64_t slot = (t0 + r) % p.ring_slots;
+#pragma unroll
+      for (int kv = 0; kv < 2; ++kv) {
+        uint8_t* d = dst + kv * kPage * ROWB;
+        if (valid) dma16(ringp + (kv * p.ring_slots + slot) * ROWB + cb, lds_addr(d + wave * 1024));
+        else *reinterpret_cast<uint4*>(d + r * ROWB + cb) = uint4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+
+  // wave w's fragments of chunk c (token tile w / KS, k-step w % KS; channel tile w)
+  auto dequant_chunk = [&](int c) {
+    const uint8_t* st = stage[c & 1];
+    const int mt = wave / KS, ks = wave % KS;
+    const int tok = tile_tok<false>(mt, j);
+    const int c0 = g * CPG + 8 * ks;
+    float x[8];
+    int e = 0;
+    if (c < n_pages) {
+      // page bound max(|z|, |z + levels s|) over the channels (every wave the same)
+      float kb = 0.f;
+#pragma unroll
+      for (int cc = lane; cc < D; cc += 64) {
+        const float sc = reinterpret_cast<const float*>(st + PG::OFF_KS)[cc];
+        const float zc = reinterpret_cast<const float*>(st + PG::OFF_KZ)[cc];
+        kb = fmaxf(kb, fmaxf(fabsf(zc), fabsf(fmaf(kLevels, sc, zc))));
+      }
+      if (__builtin_amdgcn_ballot_w64(kb >= 32768.f) != 0) {
+        int ex;
+        frexpf(wave_max(kb), &ex);
+        e = __builtin_amdgcn_readfirstlane(ex - 15);
+      }
+      const int word = (8 * ks) / FPW;
+      const uint32_t wd = *reinterpret_cast<const uint32_t*>(st + krow_off<CPR_K>(tok, g * (KW * 4) + 4 * word));
+      key_codes8<KB>(wd, ((8 * ks) % FPW) / 8, x);
+      const float4 s0 = *reinterpret_cast<const float4*>(st + PG::OFF_KS + 4 * c0);
+      const float4 s1 = *reinterpret_cast<const float4*>(st + PG::OFF_KS + 4 * c0 + 16);
+      const float4 z0 = *reinterpret_cast<const float4*>(st + PG::OFF_KZ + 4 * c0);
+      const float4 z1 = *reinterpret_cast<const float4*>(st + PG::OFF_KZ + 4 * c0 + 16);
+      float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+      if (e) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          sv[i] = ldexpf(sv[i], -e);
+          zv[i] = ldexpf(zv[i], -e);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = fmaf(x[i], sv[i], zv[i]);
+      // values: channel tile `wave`, tokens 8g .. 8g + 7
+      const uint32_t xv = *reinterpret_cast<const uint16_t*>(st + PG::OFF_VC + (16 * wave + j) * VROW + 2 * g);
+      const uint32_t y0 = xv & 0x3333u, y1 = (xv >> 2) & 0x3333u;
+      vfrag[wave][lane] = uint4{bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y0, 2.0f, 0)),
+                                bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 0)),
+                                bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y0, 2.0f, 1)),
+                                bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(y1, 2.0f, 1))};
+      if (wave == 0 && lane < kPage) {
+        vsc[lane] = reinterpret_cast<const float*>(st + PG::OFF_VS)[lane];
+        vzc[lane] = reinterpret_cast<const float*>(st + PG::OFF_VZ)[lane];
+      }
+    } else {
+      // ring rows: bound max |k| over the chunk (every wave the same)
+      float kb = 0.f;
+#pragma unroll
+      for (int i = 0; i < kPage * ROWB / (64 * 16); ++i) {
+        float f[8];
+        unpack_bf16x8(reinterpret_cast<const uint4*>(st)[i * 64 + lane], f);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) kb = fmaxf(kb, fabsf(f[k]));
+      }
+      if (__builtin_amdgcn_ballot_w64(kb >= 32768.f) != 0) {
+        int ex;
+        frexpf(wave_max(kb), &ex);
+        e = __builtin_amdgcn_readfirstlane(ex - 15);
+      }
+      unpack_bf16x8(*reinterpret_cast<const uint4*>(st + tok * ROWB + 2 * c0), x);
+      if (e) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = ldexpf(x[i], -e);
+      }
+      // values: channel 16 wave + j of tokens 8g + {0,2,1,3,4,6,5,7}
+      const uint16_t* vr = reinterpret_cast<const uint16_t*>(st + kPage * ROWB) + 16 * wave + j;
+      uint32_t v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = vr[(8 * g + i) * D];
+      vfrag[wave][lane] = uint4{v[0] | (v[2] << 16), v[1] | (v[3] << 16), v[4] | (v[6] << 16), v[5] | (v[7] << 16)};
+      if (wave == 0 && lane < kPage) {
+        vsc[lane] = 1.f;
+        vzc[lane] = 0.f;
+      }
+    }
+    if (wave == 0 && lane == 0) chunk_e = e;
+    uint32_t hi[4], lo[4];
+    split_f16(x[0], x[2], hi[0], lo[0]);
+    split_f16(x[1], x[3], hi[1], lo[1]);
+    split_f16(x[4], x[6], hi[2], lo[2]);
+    split_f16(x[5], x[7], hi[3], lo[3]);
+    kfrag[wave][0][lane] = uint4{hi[0], hi[1], hi[2], hi[3]};
+    kfrag[wave][1][lane] = uint4{lo[0], lo[1], lo[2], lo[3]};
+  };
+
+  auto compute_chunk = [&](int c) {
+    const int64_t t0 = c < n_pages ? static_cast<int64_t>(c) * kPage
+                                   : q_tokens + static_cast<int64_t>(c - n_pages) * kPage;
+    floatx4 sc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 fh = kfrag[mt * KS + ks][0][lane], fl = kfrag[mt * KS + ks][1][lane];
+        const half8 ah = cat4h(fh.x, fh.y, fh.z, fh.w), al = cat4h(fl.x, fl.y, fl.z, fl.w);
+        sc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bqh[ks], sc[mt], 0, 0, 0);
+        sc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bqh[ks], sc[mt], 0, 0, 0);
+        sc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bql[ks], sc[mt], 0, 0, 0);
+      }
+    float s[8];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[4 * mt + r] = sc[mt][r];
+    const int es = chunk_e + eq;
+    if (es) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[i] = ldexpf(s[i], es);
+    }
+    // tokens past each column's query (and stale ring rows) are masked
+    const bool masked = Tb - t0 < kPage;
+    const int nvalid = static_cast<int>(Tj - t0);
+    if (masked) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (tile_tok<false>(mt, 4 * g + r) >= nvalid) s[4 * mt + r] = -INFINITY;
+    }
+    float pmax = s[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) pmax = fmaxf(pmax, s[i]);
+    if (__builtin_amdgcn_ballot_w64(pmax > m_lane + kMaxSlack) != 0) {
+      pmax = fmaxf(pmax, xor16(pmax));
+      pmax = fmaxf(pmax, xor32(pmax));
+      const float m_new = fmaxf(m_lane, pmax);
+      const float alpha = m_new == m_lane ? 1.0f : fast_exp2(m_lane - m_new);
+      l_lane *= alpha;
+      z_lane *= alpha;
+      m_lane = m_new;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float a = __shfl(alpha, 4 * g + r, 64);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= a;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[i] = fast_exp2(s[i] - m_lane);
+    if (masked) {   // a column with no token yet has max -inf: weight 0
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (tile_tok<false>(mt, 4 * g + r) >= nvalid) s[4 * mt + r] = 0.f;
+    }
+    const float4 vs0 = *reinterpret_cast<const float4*>(&vsc[8 * g]);
+    const float4 vs1 = *reinterpret_cast<const float4*>(&vsc[8 * g + 4]);
+    const float4 vz0 = *reinterpret_cast<const float4*>(&vzc[8 * g]);
+    const float4 vz1 = *reinterpret_cast<const float4*>(&vzc[8 * g + 4]);
+    const float vsv[8] = {vs0.x, vs0.y, vs0.z, vs0.w, vs1.x, vs1.y, vs1.z, vs1.w};
+    const float vzv[8] = {vz0.x, vz0.y, vz0.z, vz0.w, vz1.x, vz1.y, vz1.z, vz1.w};
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      l_lane += s[i];
+      z_lane = fmaf(s[i], vzv[i], z_lane);
+      pv[i] = s[i] * vsv[i];
+    }
+    uint32_t ph[4], pl[4];
+    split_bf16(pv[0], pv[2], ph[0], pl[0]);
+    split_bf16(pv[1], pv[3], ph[1], pl[1]);
+    split_bf16(pv[4], pv[6], ph[2], pl[2]);
+    split_bf16(pv[5], pv[7], ph[3], pl[3]);
+    const bf16x8 aph = __builtin_bit_cast(bf16x8, uint4{ph[0], ph[1], ph[2], ph[3]});
+    const bf16x8 apl = __builtin_bit_cast(bf16x8, uint4{pl[0], pl[1], pl[2], pl[3]});
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, vfrag[nt][lane]);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aph, bv, acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(apl, bv, acc[nt], 0, 0, 0);
+    }
+  };
+
+  if (n_chunks > 0) issue_chunk(0);
+#pragma unroll 1
+  for (int c = 0; c < n_chunks; ++c) {
+    wait_vm<0>();      // this wave's copies of chunk c have landed
+    __syncthreads();   // chunk c is in its stage; every wave is done with chunk c - 1's fragments
+    dequant_chunk(c);
+    __syncthreads();   // the fragments of chunk c are complete
+    if (c + 1 < n_chunks) issue_chunk(c + 1);
+    compute_chunk(c);
+  }
+
+  // ---- outputs of this wave's 16 pairs: (acc + sum p z) / sum p -----------------
+  float l_ = l_lane, z_ = z_lane;
+  l_ += xor16(l_);
+  l_ += xor32(l_);
+  z_ += xor16(z_);
+  z_ += xor32(z_);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int vh = 4 * g + r;   // this lane's accumulator rows
+    const float lv = __shfl(l_, vh, 64), zv = __shfl(z_, vh, 64);
+    const int64_t row = static_cast<int64_t>(b) * p.nq + qi + 4 * wave + vh / HG;
+    float* o = p.out + (row * p.q_heads + h * HG + vh % HG) * D;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) o[16 * nt + j] = (acc[nt][r] + zv) / lv;
+  }
+}
+
 // ---- rotary keys, GQA group of 4: dense scores on v_mfma_f32_4x4x1_16b_f32 ----
 // Same result as kivi_mfma_kernel<2, D, 4, true> with the key product laid out
 // so that no MFMA column is wasted. Lane l takes token l % 32 of a page (or of
@@ -2247,6 +2598,16 @@ hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t st) {
     p.new_tok = a.tokens - 1;
   }
   const int grid_rows = g.batch * nq / qn;
+  // long chunks (a multiple of 32 queries whose rows of 32 fill the chip):
+  // one block per (sequence, KV head, 32 queries), one split
+  if (fours && g.d == 128 && nq % 32 == 0 &&
+      static_cast<int64_t>(g.batch) * (nq / 32) * g.kv_heads >= 256) {
+    p.splits = 1;
+    const dim3 grid(1, g.kv_heads, g.batch * (nq / 32));
+    if (g.bits == 2) hipLaunchKernelGGL((kivi_chunk_kernel<2>), grid, dim3(512), 0, st, p);
+    else hipLaunchKernelGGL((kivi_chunk_kernel<4>), grid, dim3(512), 0, st, p);
+    return hipGetLastError();
+  }
   if (a.rope_theta > 0.0) return by_d_rope(p, g.d, g.hg, grid_rows, st);
   if (g.bits == 2) return by_d<2, 2>(p, g.d, g.hg, grid_rows, qn, st);
   return g.vbits == 2 ? by_d<4, 2>(p, g.d, g.hg, grid_rows, qn, st)

@@ -23,6 +23,7 @@ DEV = "cuda"
 CASES = {
     "kivi2": ("kivi2", 4, [(0, 0), (15, 7)]),
     "kivi2_8q": ("kivi2", 8, [(0, 0), (9, 3), (15, 7)]),
+    "kivi2_64q": ("kivi2", 64, [(0, 0), (15, 7)]),
     "int4": ("int4", 8, [(31, 7)]),
     "longctx": ("longctx", 4, [(0, 3)]),
     "fp8": ("fp8", 3, [(63, 2)]),

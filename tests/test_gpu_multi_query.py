@@ -74,6 +74,14 @@ CASES = [
     (synth.KIVI, 4, 64, 4, torch.bfloat16, 8, 361, 0.0, 9, 44, 2, 12),
     (synth.KIVI, 4, 128, 4, torch.bfloat16, 64, 500, 0.0, 0, 16, 2, 32),
     (synth.KIVI, 4, 128, 4, torch.bfloat16, 32, 300, 0.0, 3, 100, 2, 6),
+    # long chunks (a multiple of 32 queries, batch x n_q / 32 x KV heads >=
+    # 256): each chunk of 32 tokens copied and dequantised once per block of
+    # 32 queries; early query groups end inside the pages, later ones reach
+    # into the ring (a last ring chunk with rows past the last query), none
+    # without a ring
+    (synth.KIVI, 2, 128, 4, torch.bfloat16, 32, 300, 0.0, 0, 128, 0, 32),
+    (synth.KIVI, 4, 128, 4, torch.bfloat16, 64, 400, 0.0, 0, 64, 2, 64),
+    (synth.KIVI, 2, 128, 4, torch.bfloat16, 0, 256, 0.0, 0, 128, 0, 32),
     # FP8 and bfloat16 caches without rotary keys: their matrix-core kernel
     (synth.FP8_E5M2, 8, 128, 8, torch.bfloat16, 0, 301, 0.0, 3, 45),     # queries across pages
     (synth.BF16_CACHE, 16, 64, 2, torch.bfloat16, 0, 77, 0.0, 1, 9),     # one split: no merge

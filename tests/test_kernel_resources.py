@@ -73,7 +73,8 @@ def _family(kernels, stem):
     return {n: v for n, v in kernels.items() if stem in n}
 
 
-@pytest.mark.parametrize("stem", ["kivi_mfma_kernel", "kivi_deq_kernel", "rope4_kernel", "paged_mfma_kernel"])
+@pytest.mark.parametrize("stem", ["kivi_mfma_kernel", "kivi_deq_kernel", "kivi_chunk_kernel", "rope4_kernel",
+                                  "paged_mfma_kernel"])
 def test_matrix_core_decodes_use_no_scratch(kernels, stem):
     fam = _family(kernels, stem)
     assert fam, stem
