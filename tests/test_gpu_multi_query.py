@@ -125,8 +125,9 @@ def test_single_query_is_the_plain_decode():
 
 
 
-@pytest.mark.parametrize("which", ["keys", "queries"])
-def test_four_query_blocks_f16_range(which):
+@pytest.mark.parametrize("nq", [4, 32])
+@pytest.mark.parametrize("which", ["keys", "ring_keys", "queries"])
+def test_four_query_blocks_f16_range(which, nq):
     """Four queries per block take the keys dequantised into f16 high and
     remainder parts and q' = q * sm_scale * log2(e) likewise; a page whose
     keys reach 2^15, or queries that do, are scaled by powers of two on the
@@ -137,15 +138,19 @@ def test_four_query_blocks_f16_range(which):
     "keys": X's channel 0 is 3e5 against q_0 = 1 (true score 3.8e4, 1.7e4
     saturated) and Y's channel 1 is 2e4 against q_1 = 9.8 (2.5e4);
     "queries": q_5 = 2e6 against X's channel 5 of 10 (q'_5 = 2.5e5, 1.3e5
-    saturated) and q_6 = 3.9e5 against Y's channel 6 of 40. Every output row
-    is then X's dequantised value row; plain 2e-3 against the oracle, queries
-    in the ring."""
-    w = small(synth.KIVI, 2, 128, torch.bfloat16, 16, B=2, Hkv=1, hg=4, T=100)
-    T, X, Y = w.tokens, 3, 17
+    saturated) and q_6 = 3.9e5 against Y's channel 6 of 40; "ring_keys": as
+    "keys" with X and Y residual tokens (keys rescaled per 32-token chunk of
+    the ring by the long-chunk kernel). Every output row is then X's value
+    row; plain 2e-3 against the oracle. n_q = 4: four queries per block;
+    n_q = 32 over 256 sequences: the long-chunk kernel (32 per block)."""
+    B = 2 if nq == 4 else 256
+    w = small(synth.KIVI, 2, 128, torch.bfloat16, 16, B=B, Hkv=1, hg=4, T=100)
+    T = w.tokens
+    X, Y = (66, 67) if which == "ring_keys" else (3, 17)   # ring from token 64; queries from 68
     k, v = synth.keys_values(w, device=DEV)
-    q = queries(w, 4).float()
+    q = queries(w, nq).float()
     k = k.float()
-    if which == "keys":
+    if which in ("keys", "ring_keys"):
         k[:, X, :, 0] = 3.0e5
         k[:, Y, :, 1] = 2.0e4
         q[:, :, :, 0] = 1.0
@@ -163,12 +168,12 @@ def test_four_query_blocks_f16_range(which):
     oc = H.oracle_cache(w, T + 40)
     H.append_chunks(cfg, cache, k, v, [T], oc=oc)
     out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
-    ws = torch.zeros(4 * kvq.kvq_cache_bytes(cfg, T, kvq.KVQ_BYTES_WORKSPACE), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(nq * kvq.kvq_cache_bytes(cfg, T, kvq.KVQ_BYTES_WORKSPACE), dtype=torch.uint8, device=DEV)
     kvq.kvq_decode_attention_multi(cfg, cache, 0, T, q, out, ws)
     want = oc.decode_multi(0, H.values(q))
     # the construction: every row is X's value row
     vx = want[:, :1, :1]
     assert np.allclose(want, np.broadcast_to(vx, want.shape), atol=1e-6)
     err = H.max_err(out, want)
-    print(f"[four-query range] {which}: max-abs error {err:.2e}", flush=True)
+    print(f"[four-query range] {which} n_q {nq}: max-abs error {err:.2e}", flush=True)
     assert err <= H.ATOL, err
