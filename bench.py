@@ -363,12 +363,14 @@ def gpu_bench(args, w):
     graph = graph_replay(cfg, cache, ws, qs, outs, news, L, T_end, n_rep)
     cache_bytes = int(cache.numel())
 
-    # several causal queries per sequence (4 and 8: e.g. speculated tokens
-    # being verified) over the same caches; their tokens are in the ring, so
-    # they run on the matrix-core kernel of four queries per block, whose
-    # keys are dequantised once per page for the four
+    # several causal queries per sequence over the same caches: 4 and 8
+    # (e.g. speculated tokens being verified; their tokens in the ring) on the
+    # kernel of four queries per block, whose keys are dequantised once per
+    # page for the four, and a chunk of 64 (chunked prefill; tokens reaching
+    # into the pages) on the kernel of 32 queries per block, which copies and
+    # dequantises each 32-token chunk once for the 32
     multi = []
-    for nq in (4, 8):
+    for nq in (4, 8, 64):
         qm = [torch.stack([synth.query(w, layer=l, device=dev, tag=1 + i) for i in range(nq)], dim=1)
               .contiguous() for l in range(L)]
         om = [torch.empty(x.shape, dtype=torch.float32, device=dev) for x in qm]
@@ -389,7 +391,8 @@ def gpu_bench(args, w):
         multi.append({"n_queries": nq, "median_launch_us": round(multi_us, 3), "bytes_per_launch": multi_b,
                       "gbs": round(multi_b / (multi_us * 1e-6) / 1e9, 1),
                       "x_one_query": round(multi_us / burst_us[len(burst_us) // 2], 2),
-                      "kernel": "kivi_deq_kernel<2,2,128> (rows b * n_q / 4 + i, merge fused)"})
+                      "kernel": ("kivi_chunk_kernel<2> (rows b * n_q / 32 + i, one split)" if nq % 32 == 0
+                                 else "kivi_deq_kernel<2,2,128> (rows b * n_q / 4 + i, merge fused)")})
         del qm, om, wsm
 
     # ragged batch: 32 more layer caches whose sequences hold lens[b] tokens
