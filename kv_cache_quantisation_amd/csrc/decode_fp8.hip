@@ -126,9 +126,16 @@ __device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
 // z_t = -2^(VB-1) s_t that KIVI values carry explicitly. The unsigned code
 // converts give the channel (token) order {0,2,1,3,4,6,5,7} within each 8,
 // which the query (weight) operand follows (8-bit codes keep their order).
-template <int FMT, int D, int HG, int KB = 8, int VB = 8>
+// QN = 2 (FP8 pages, GQA 4): two consecutive queries of a sequence per block,
+// the second one's high and remainder columns and weight rows in the halves
+// of the products that one query at GQA 4 leaves idle; the pages up to the
+// second query's token, each column masking after its own query's.
+template <int FMT, int D, int HG, int KB = 8, int VB = 8, int QN = 1>
 __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
-  static_assert(2 * HG <= 16, "high and remainder columns of the GQA group fit one tile");
+  static_assert(2 * HG * QN <= 16, "high and remainder columns of the GQA group(s) fit one tile");
+  static_assert(QN == 1 || (QN == 2 && HG == 4 && (FMT == KVQ_FP8_E4M3 || FMT == KVQ_FP8_E5M2)),
+                "two queries per block: FP8 pages, GQA 4");
+  constexpr int GC = HG * QN;             // (query, head) pairs of the block
   constexpr bool BF16 = FMT == KVQ_BF16_CACHE;
   constexpr bool E5 = FMT == KVQ_FP8_E5M2;
   constexpr bool SYMK = FMT == KVQ_SYM_TOKEN;                    // key codes, a scale per token
@@ -142,10 +149,10 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   constexpr int KS = D / 32;             // k-steps of the key product
   constexpr int NT = D / 16;             // channel tiles of the value product
   constexpr int CPG = D / 4;             // key channels per lane group (contiguous bytes)
-  constexpr int RED = kWaves * HG * (D + 2) * 4;
+  constexpr int RED = kWaves * GC * (D + 2) * 4;
   constexpr int ARENA = kWaves * PG::WAVE_LDS > RED ? kWaves * PG::WAVE_LDS : RED;
 
-  __shared__ __attribute__((aligned(16))) float qs[HG][D];
+  __shared__ __attribute__((aligned(16))) float qs[GC][D];
   __shared__ __attribute__((aligned(16))) uint8_t arena[ARENA];
   __shared__ int last_block;
 
@@ -154,8 +161,12 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform in the wave
   const int j = lane & 15, g = lane >> 4;
   const int split = blockIdx.x, h = blockIdx.y;
-  const int row = blockIdx.z;                      // query row b * nq + qi
-  const int b = row / p.nq, qi = row - b * p.nq;   // sequence, its query
+  const int rows_b = p.nq / QN;                    // grid rows per sequence
+  const int b = blockIdx.z / rows_b, qi = (blockIdx.z - b * rows_b) * QN;   // sequence, its (first) query
+  const int row = b * p.nq + qi;                   // query row b * nq + qi (of q, out, partials)
+  // lane column j: query j / (2HG) of the block, high part when j % (2HG) < HG
+  const bool col_hi = (j % (2 * HG)) < HG;
+  const bool col_live = QN == 1 ? j < HG : col_hi;
   const int unit = b * p.kv_heads + h;             // one arrival counter for every row of b
   uint8_t* wbuf = arena + wave * PG::WAVE_LDS;
   const float ks_h = E5 ? p.k_scale[h] : 1.0f;   // applied to the scores (E5M2)
@@ -164,9 +175,11 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   // pages this sequence holds (a ragged batch: its own fill level), cut at
   // the query's own token when there are several (query qi of nq sits at
   // position fill - nq + qi)
+  // (QN = 2: the pages up to the second query's token; the first query's
+  // columns see one token less of the last page, possibly none)
   int32_t n_pages = p.n_pages, last_valid = p.last_valid;
   if (p.seq_tokens || p.nq > 1) {
-    const int64_t Tb = seq_len(p.seq_tokens, b, p.T) - (p.nq - 1 - qi);
+    const int64_t Tb = seq_len(p.seq_tokens, b, p.T) - (p.nq - 1 - qi) + (QN - 1);
     n_pages = static_cast<int32_t>((Tb + kPage - 1) / kPage);
     last_valid = static_cast<int32_t>(Tb - static_cast<int64_t>(n_pages - 1) * kPage);
   }
@@ -207,10 +220,11 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   // ---- query group: q * sm_scale * log2(e) * ks_h ----------------------------
   {
     const float mult = (BF16 || E5 || SYMK) ? p.qscale : p.qscale * p.k_scale[h];
-    const int64_t q0 = (static_cast<int64_t>(row) * p.q_heads + h * HG) * D;
-    for (int i = tid; i < HG * D; i += kThreads) {
-      const float x = p.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(p.q)[q0 + i])
-                               : reinterpret_cast<const float*>(p.q)[q0 + i];
+    for (int i = tid; i < GC * D; i += kThreads) {
+      const int qq = i / (HG * D);   // the block's query qq: row + qq
+      const int64_t q0 = (static_cast<int64_t>(row + qq) * p.q_heads + h * HG) * D + (i - qq * HG * D);
+      const float x = p.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(p.q)[q0])
+                               : reinterpret_cast<const float*>(p.q)[q0];
       (&qs[0][0])[i] = x * mult;
     }
   }
@@ -225,10 +239,10 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   // q' 2^-esc into the product and multiplies its scores by 2^esc (exact)
   int esc = 0;
   if constexpr (!BF16) {
-    const int hh = j % HG;
+    const int hh = (j / (2 * HG)) * HG + j % HG;   // pair of column j (QN = 1: head j % HG)
     float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < D / 4; ++i) amax = fmaxf(amax, fabsf(qs[hh][g * CPG + i]));
+    for (int i = 0; i < D / 4; ++i) amax = fmaxf(amax, fabsf(qs[QN == 1 ? j % HG : hh][g * CPG + i]));
     if (__builtin_amdgcn_ballot_w64(amax > 65504.f) != 0) {
       amax = wave_max(amax);
       int ex;
@@ -247,7 +261,8 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
     kbias = sq * static_cast<float>(1 << (KB - 1));
   }
   {
-    const int hh = j % HG, part = j / HG;
+    const int hh = QN == 1 ? j % HG : (j / (2 * HG)) * HG + j % HG;
+    const int part = QN == 1 ? j / HG : (j % (2 * HG)) / HG;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       uint32_t w4[4];
@@ -273,7 +288,9 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_lane = -INFINITY, l_lane = 0.f, z_lane = 0.f;
 
-  auto process_page = [&](const uint8_t* pg, int n_valid, const uint4* vr, bool vrows) {
+  // n_valid: tokens of the page the block's (last) query sees; n_valid0: the
+  // first query's (QN = 2), for its columns
+  auto process_page = [&](const uint8_t* pg, int n_valid, int n_valid0, const uint4* vr, bool vrows) {
     (void)vrows;   // bfloat16 caches: value columns on every page
     // scores; tile mt row rho = token 8(rho/4) + 4mt + rho%4
     float s[8];
@@ -333,9 +350,10 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) s[i] = kst[i] * (s[i] - kbias);
     }
-    if (n_valid < kPage) {
+    const int nv_col = (QN == 2 && j < 2 * HG) ? n_valid0 : n_valid;   // this column's query
+    if (nv_col < kPage) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s[i] = 8 * g + i < n_valid ? s[i] : -INFINITY;
+      for (int i = 0; i < 8; ++i) s[i] = 8 * g + i < nv_col ? s[i] : -INFINITY;
     }
     // online softmax: running max per head (lanes j < HG), weights 2^(s - m)
     // (whether a head's max grows is decided by each lane's own maximum; the
@@ -343,11 +361,13 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
     float pmax = s[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) pmax = fmaxf(pmax, s[i]);
-    if (__builtin_amdgcn_ballot_w64((j < HG) && (pmax > m_lane)) != 0) {
+    if (__builtin_amdgcn_ballot_w64(col_live && (pmax > m_lane)) != 0) {
       pmax = fmaxf(pmax, xor16(pmax));
       pmax = fmaxf(pmax, xor32(pmax));
       const float m_new = fmaxf(m_lane, pmax);
-      const float alpha = fast_exp2(m_lane - m_new);
+      // (QN = 2: a column whose max stays -inf while the other query's move
+      // keeps its sums; 2^(-inf - -inf) would be NaN)
+      const float alpha = (QN == 2 && m_new == m_lane) ? 1.0f : fast_exp2(m_lane - m_new);
       l_lane *= alpha;
       z_lane *= alpha;
       m_lane = m_new;
@@ -364,15 +384,28 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
           const float a_odd = alpha_of(4 + r);
           a = (g & 1) ? a_odd : a;
         }
+        // QN = 2: rows 4g + r of lane groups 2, 3 belong to the second query,
+        // whose head r is column 2HG + r
+        if constexpr (QN == 2) {
+          const float a_q1 = alpha_of(2 * HG + r);
+          a = g >= 2 ? a_q1 : a;
+        }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= a;
       }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      s[i] = fast_exp2(s[i] - m_lane);
-      l_lane += s[i];
+    for (int i = 0; i < 8; ++i) s[i] = fast_exp2(s[i] - m_lane);
+    if constexpr (QN == 2) {
+      // a column that has seen no token yet (max -inf) gets weight 0 for its
+      // absent tokens (2^(-inf - -inf) is not 0)
+      if (nv_col < kPage) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s[i] = 8 * g + i < nv_col ? s[i] : 0.f;
+      }
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) l_lane += s[i];
     // per-token value codes: P' = p s_t (tokens 8g..8g+7), sum of p z_t; an
     // absent token's scale and offset are taken as 0 (its bytes are undefined)
     if constexpr (CODEV) {
@@ -411,7 +444,10 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
       split_bf16(s[t0], s[t1], ph[i], pl[i]);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pa[i] = shr_keep<HG>(ph[i], pl[i]);
+    for (int i = 0; i < 4; ++i) {
+      pa[i] = shr_keep<HG>(ph[i], pl[i]);
+      if constexpr (QN == 2) pa[i] = col_hi ? ph[i] : pa[i];   // the second query's high rows keep theirs
+    }
     const bf16x8 ap = __builtin_bit_cast(bf16x8, uint4{pa[0], pa[1], pa[2], pa[3]});
     if constexpr (BF16) {
       // values of tokens 8g..8g+7 of channel 16 nt + j (registers); absent
@@ -534,8 +570,9 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
     }
     __builtin_amdgcn_wave_barrier();
     const int page = pg0 + wave + kWaves * k;
-    process_page(wbuf + (k % PG::NBUF) * PG::BYTES, page == n_pages - 1 ? last_valid : kPage, cur,
-                 page == open_page);
+    const bool last = page == n_pages - 1;
+    process_page(wbuf + (k % PG::NBUF) * PG::BYTES, last ? last_valid : kPage,
+                 last ? last_valid - (QN - 1) : kPage, cur, page == open_page);
   };
 #pragma unroll 1
   for (int k = 0; k < n_mine; k += 2) {
@@ -545,7 +582,8 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   wait_lds();
 
   // ---- wave epilogue -----------------------------------------------------------
-  float lsum[HG], mh[HG], zsum[HG];
+  // per (query, head) pair vh: its column (vh / HG) 2HG + vh % HG
+  float lsum[GC], mh[GC], zsum[GC];
   {
     float l_ = l_lane, z_ = z_lane;
     l_ += xor16(l_);
@@ -555,16 +593,18 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
       z_ += xor32(z_);
     }
 #pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-      lsum[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_), hh));
-      mh[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_lane), hh));
-      zsum[hh] = CODEV ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, z_), hh)) : 0.f;
+    for (int vh = 0; vh < GC; ++vh) {
+      const int col = (vh / HG) * 2 * HG + vh % HG;
+      lsum[vh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_), col));
+      mh[vh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_lane), col));
+      zsum[vh] = CODEV ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, z_), col)) : 0.f;
     }
   }
   __syncthreads();   // every wave is done with its page buffers (the arena)
-  float* red = reinterpret_cast<float*>(arena);   // [wave][HG][D + 2]: m, l, o
-  auto R = [&](int w, int hh) { return red + (w * HG + hh) * (D + 2); };
-  // acc rows 4g+r: row < HG is head row (high), HG <= row < 2HG head row-HG (remainder)
+  float* red = reinterpret_cast<float*>(arena);   // [wave][GC][D + 2]: m, l, o
+  auto R = [&](int w, int vh) { return red + (w * GC + vh) * (D + 2); };
+  // acc rows 4g+r: row < HG is head row (high), HG <= row < 2HG head row-HG
+  // (remainder); with two queries rows 2HG.. repeat that for the second
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     float v[4];
@@ -583,19 +623,23 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
       v[r] = x;
     }
     const int c = 16 * nt + j;
-    if (4 * g < HG) {
+    if ((4 * g) % (2 * HG) < HG && 4 * g < 2 * GC) {   // lane groups holding the high rows
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int hh = 4 * g + r;
-        if (hh < HG) R(wave, hh)[2 + c] = v[r] + zsum[hh];   // + sum of p z (value codes)
+        const int hh = (4 * g) % (2 * HG) + r;
+        const int vh = (4 * g / (2 * HG)) * HG + hh;
+        float zz = 0.f;   // sum of p z (value codes) of pair vh
+#pragma unroll
+        for (int k = 0; k < GC; ++k) zz = vh == k ? zsum[k] : zz;
+        if (hh < HG) R(wave, vh)[2 + c] = v[r] + zz;
       }
     }
   }
   if (lane == 0) {
 #pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-      R(wave, hh)[0] = mh[hh];
-      R(wave, hh)[1] = lsum[hh];
+    for (int vh = 0; vh < GC; ++vh) {
+      R(wave, vh)[0] = mh[vh];
+      R(wave, vh)[1] = lsum[vh];
     }
   }
   __syncthreads();
@@ -606,7 +650,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
 
   // ---- combine the waves: this thread's elements i = tid + e * kThreads ----
   const float vs_h = (BF16 || CODEV) ? 1.0f : p.v_scale[h];
-  constexpr int PER = (HG * D + kThreads - 1) / kThreads;
+  constexpr int PER = (GC * D + kThreads - 1) / kThreads;
   float own_m[PER], own_l[PER], own_o[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
@@ -614,20 +658,21 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
     own_m[e] = -INFINITY;
     own_l[e] = 0.f;
     own_o[e] = 0.f;
-    if (i < HG * D) {
-      const int hh = i / D, c = i % D;
+    if (i < GC * D) {
+      const int vh = i / D, c = i % D;   // pair vh: query vh / HG of the block, head vh % HG
       float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, R(w, hh)[0]);
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, R(w, vh)[0]);
       float so = 0.f, sl = 0.f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float ew = exp2_rel(R(w, hh)[0], M);   // idle wave (or block): 0
-        so = fmaf(ew, R(w, hh)[2 + c], so);
-        sl = fmaf(ew, R(w, hh)[1], sl);
+        const float ew = exp2_rel(R(w, vh)[0], M);   // idle wave (or block): 0
+        so = fmaf(ew, R(w, vh)[2 + c], so);
+        sl = fmaf(ew, R(w, vh)[1], sl);
       }
       so *= vs_h;
-      if (p.splits == 1) p.out[(static_cast<int64_t>(row) * p.q_heads + h * HG + hh) * D + c] = so / sl;
+      if (p.splits == 1)
+        p.out[(static_cast<int64_t>(row + vh / HG) * p.q_heads + h * HG + vh % HG) * D + c] = so / sl;
       own_m[e] = M;
       own_l[e] = sl;
       own_o[e] = so;
@@ -635,39 +680,71 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   }
   if (p.splits == 1) return;
 
-  // ---- the last of the nq * splits blocks of (b, h) to arrive merges --------
-  if (tid == 0) last_block = arrived == p.nq * p.splits - 1;
+  // ---- the last of the (nq / QN) * splits blocks of (b, h) to arrive merges --
+  if (tid == 0) last_block = arrived == (p.nq / QN) * p.splits - 1;
   __syncthreads();
-  float* part_rh = p.partials + (static_cast<int64_t>(row) * p.q_heads + h * HG) * p.splits * (D + 2);
-  if (!last_block) {
-    store_partial<D, HG, kThreads>(part_rh, p.splits, split, own_m, own_l, own_o, tid);
-    return;
+  if constexpr (QN == 1) {
+    float* part_rh = p.partials + (static_cast<int64_t>(row) * p.q_heads + h * HG) * p.splits * (D + 2);
+    if (!last_block) {
+      store_partial<D, HG, kThreads>(part_rh, p.splits, split, own_m, own_l, own_o, tid);
+      return;
+    }
+    merge_partials<D, HG, kThreads>(p.partials, p.out, &p.counters[unit], p.q_heads, p.splits, p.nq, b, h,
+                                    row, split, own_m, own_l, own_o, tid);
+  } else {
+    // every block stores the partials of its rows; the last one merges them
+    // all from memory (row -1: none from registers)
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int i = tid + e * kThreads;
+      if (i < GC * D) {
+        const int vh = i / D, c = i % D;
+        float* part = p.partials +
+                      ((static_cast<int64_t>(row + vh / HG) * p.q_heads + h * HG + vh % HG) * p.splits + split) *
+                          (D + 2);
+        put_partial(part + 2 + c, own_o[e]);
+        if (c == 0) {
+          put_partial(part, own_m[e]);
+          put_partial(part + 1, own_l[e]);
+        }
+      }
+    }
+    if (!last_block) return;
+    merge_partials<D, HG, kThreads>(p.partials, p.out, &p.counters[unit], p.q_heads, p.splits, p.nq, b, h, -1,
+                                    split, own_m, own_l, own_o, tid);
   }
-  merge_partials<D, HG, kThreads>(p.partials, p.out, &p.counters[unit], p.q_heads, p.splits, p.nq, b, h,
-                                  row, split, own_m, own_l, own_o, tid);
 }
 
+// batch: grid rows (sequences x queries / qn); qn 2: two queries per block (FP8, GQA 4)
 template <int FMT, int D, int KB, int VB>
-hipError_t by_hg(const Fp8Params& p, int hg, int batch, hipStream_t st) {
+hipError_t by_hg(const Fp8Params& p, int hg, int batch, hipStream_t st, int qn = 1) {
   dim3 grid(p.splits, p.kv_heads, batch);
   switch (hg) {
     case 1: hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 1, KB, VB>), grid, dim3(kThreads), 0, st, p); break;
     case 2: hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 2, KB, VB>), grid, dim3(kThreads), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 4, KB, VB>), grid, dim3(kThreads), 0, st, p); break;
+    case 4:
+      if constexpr (FMT == KVQ_FP8_E4M3 || FMT == KVQ_FP8_E5M2) {
+        if (qn == 2) {
+          hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 4, KB, VB, 2>), grid, dim3(kThreads), 0, st, p);
+          break;
+        }
+      }
+      hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 4, KB, VB>), grid, dim3(kThreads), 0, st, p);
+      break;
     default: hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 8, KB, VB>), grid, dim3(kThreads), 0, st, p); break;
   }
   return hipGetLastError();
 }
 
 template <int FMT, int KB = 8, int VB = 8>
-hipError_t by_d(const Fp8Params& p, int d, int hg, int batch, hipStream_t st) {
+hipError_t by_d(const Fp8Params& p, int d, int hg, int batch, hipStream_t st, int qn = 1) {
   switch (d) {
     case 32:
-      if constexpr (!(FMT == KVQ_SYM_TOKEN && KB == 2)) return by_hg<FMT, 32, KB, VB>(p, hg, batch, st);
+      if constexpr (!(FMT == KVQ_SYM_TOKEN && KB == 2)) return by_hg<FMT, 32, KB, VB>(p, hg, batch, st, qn);
       return hipErrorInvalidValue;   // not routed here (fp8_mfma_path)
-    case 64: return by_hg<FMT, 64, KB, VB>(p, hg, batch, st);
-    case 128: return by_hg<FMT, 128, KB, VB>(p, hg, batch, st);
-    default: return by_hg<FMT, 256, KB, VB>(p, hg, batch, st);
+    case 64: return by_hg<FMT, 64, KB, VB>(p, hg, batch, st, qn);
+    case 128: return by_hg<FMT, 128, KB, VB>(p, hg, batch, st, qn);
+    default: return by_hg<FMT, 256, KB, VB>(p, hg, batch, st, qn);
   }
 }
 
@@ -709,8 +786,10 @@ hipError_t launch_fp8_mfma(const DecodeArgs& a, hipStream_t st) {
   // several queries per sequence: batch * nq rows, and the split count
   // planned for that many (never more than the one-query plan, whose
   // workspace nq copies of hold the partials)
+  // two queries per block: FP8 pages at GQA 4, an even number of queries
+  const int qn = (is_fp8(g.scheme) && g.hg == 4 && nq >= 2 && nq % 2 == 0) ? 2 : 1;
   Geometry rows = g;
-  rows.batch = g.batch * nq;
+  rows.batch = g.batch * nq / qn;
   Fp8Params p{};
   p.pm = a.pm;
   p.layer_base = a.layer_base;
@@ -732,10 +811,10 @@ hipError_t launch_fp8_mfma(const DecodeArgs& a, hipStream_t st) {
   p.q_heads = g.q_heads;
   p.q_bf16 = a.q_dtype == KVQ_BF16;
   p.qscale = a.sm_scale * kLog2e;
-  const int rows_n = g.batch * nq;
+  const int rows_n = g.batch * nq / qn;
   switch (g.scheme) {
     case KVQ_BF16_CACHE: return by_d<KVQ_BF16_CACHE>(p, g.d, g.hg, rows_n, st);
-    case KVQ_FP8_E5M2: return by_d<KVQ_FP8_E5M2>(p, g.d, g.hg, rows_n, st);
+    case KVQ_FP8_E5M2: return by_d<KVQ_FP8_E5M2>(p, g.d, g.hg, rows_n, st, qn);
     case KVQ_SYM_TOKEN:
       return g.bits == 2   ? by_d<KVQ_SYM_TOKEN, 2, 2>(p, g.d, g.hg, rows_n, st)
              : g.bits == 4 ? by_d<KVQ_SYM_TOKEN, 4, 4>(p, g.d, g.hg, rows_n, st)
@@ -748,7 +827,7 @@ hipError_t launch_fp8_mfma(const DecodeArgs& a, hipStream_t st) {
       return g.vbits == 2   ? by_d<KVQ_FP8K_KIVIV, 8, 2>(p, g.d, g.hg, rows_n, st)
              : g.vbits == 4 ? by_d<KVQ_FP8K_KIVIV, 8, 4>(p, g.d, g.hg, rows_n, st)
                             : by_d<KVQ_FP8K_KIVIV, 8, 8>(p, g.d, g.hg, rows_n, st);
-    default: return by_d<KVQ_FP8_E4M3>(p, g.d, g.hg, rows_n, st);
+    default: return by_d<KVQ_FP8_E4M3>(p, g.d, g.hg, rows_n, st, qn);
   }
 }
 

@@ -4,8 +4,9 @@ split plan): query i of n_q, at position T - n_q + i, attends to tokens
 [0, T - n_q + i] of the cache. Sampled (sequence, KV head) units are checked
 against the oracle's fp64 attention over that unit's dequantised keys and
 values (the KIVI page/ring split of the whole cache), cut at each query's own
-token. KIVI caches run on the matrix-core kernel (their queries' tokens are
-in the ring), FP8 on the generic kernel."""
+token. KIVI caches run on their matrix-core kernels (four or 32 queries per
+block for 8 and 64 queries), FP8 on its matrix-core kernel (two queries per
+block for an even n_q)."""
 
 import numpy as np
 import pytest
@@ -27,6 +28,7 @@ CASES = {
     "int4": ("int4", 8, [(31, 7)]),
     "longctx": ("longctx", 4, [(0, 3)]),
     "fp8": ("fp8", 3, [(63, 2)]),
+    "fp8_4q": ("fp8", 4, [(0, 0), (63, 2)]),
 }
 
 

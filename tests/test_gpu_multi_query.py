@@ -84,6 +84,13 @@ CASES = [
     (synth.KIVI, 2, 128, 4, torch.bfloat16, 0, 256, 0.0, 0, 128, 0, 32),
     # FP8 and bfloat16 caches without rotary keys: their matrix-core kernel
     (synth.FP8_E5M2, 8, 128, 8, torch.bfloat16, 0, 301, 0.0, 3, 45),     # queries across pages
+    # FP8 at GQA 4 with an even n_q: two queries per block (the second one's
+    # columns and rows in the halves one query leaves idle); the open last
+    # page in token rows; a first query at a page boundary whose partner's
+    # token opens the next page (the first sees none of it); head_dim 64
+    (synth.FP8_E4M3, 8, 128, 4, torch.bfloat16, 0, 333, 0.0, 0, 4),
+    (synth.FP8_E5M2, 8, 128, 4, torch.bfloat16, 0, 321, 0.0, 3, 2),
+    (synth.FP8_E4M3, 8, 64, 4, torch.bfloat16, 0, 200, 0.0, 5, 16),
     (synth.BF16_CACHE, 16, 64, 2, torch.bfloat16, 0, 77, 0.0, 1, 9),     # one split: no merge
 ]
 
