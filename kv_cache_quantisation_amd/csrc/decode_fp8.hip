@@ -126,15 +126,16 @@ __device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
 // z_t = -2^(VB-1) s_t that KIVI values carry explicitly. The unsigned code
 // converts give the channel (token) order {0,2,1,3,4,6,5,7} within each 8,
 // which the query (weight) operand follows (8-bit codes keep their order).
-// QN = 2 (FP8 pages, GQA 4): two consecutive queries of a sequence per block,
+// QN = 2 (FP8 or bfloat16 pages, GQA 4): two consecutive queries of a sequence per block,
 // the second one's high and remainder columns and weight rows in the halves
 // of the products that one query at GQA 4 leaves idle; the pages up to the
 // second query's token, each column masking after its own query's.
 template <int FMT, int D, int HG, int KB = 8, int VB = 8, int QN = 1>
 __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   static_assert(2 * HG * QN <= 16, "high and remainder columns of the GQA group(s) fit one tile");
-  static_assert(QN == 1 || (QN == 2 && HG == 4 && (FMT == KVQ_FP8_E4M3 || FMT == KVQ_FP8_E5M2)),
-                "two queries per block: FP8 pages, GQA 4");
+  static_assert(QN == 1 || (QN == 2 && HG == 4 && (FMT == KVQ_FP8_E4M3 || FMT == KVQ_FP8_E5M2 ||
+                                                   FMT == KVQ_BF16_CACHE)),
+                "two queries per block: FP8 or bfloat16 pages, GQA 4");
   constexpr int GC = HG * QN;             // (query, head) pairs of the block
   constexpr bool BF16 = FMT == KVQ_BF16_CACHE;
   constexpr bool E5 = FMT == KVQ_FP8_E5M2;
@@ -715,7 +716,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   }
 }
 
-// batch: grid rows (sequences x queries / qn); qn 2: two queries per block (FP8, GQA 4)
+// batch: grid rows (sequences x queries / qn); qn 2: two queries per block (FP8 or bf16, GQA 4)
 template <int FMT, int D, int KB, int VB>
 hipError_t by_hg(const Fp8Params& p, int hg, int batch, hipStream_t st, int qn = 1) {
   dim3 grid(p.splits, p.kv_heads, batch);
@@ -723,7 +724,7 @@ hipError_t by_hg(const Fp8Params& p, int hg, int batch, hipStream_t st, int qn =
     case 1: hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 1, KB, VB>), grid, dim3(kThreads), 0, st, p); break;
     case 2: hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 2, KB, VB>), grid, dim3(kThreads), 0, st, p); break;
     case 4:
-      if constexpr (FMT == KVQ_FP8_E4M3 || FMT == KVQ_FP8_E5M2) {
+      if constexpr (FMT == KVQ_FP8_E4M3 || FMT == KVQ_FP8_E5M2 || FMT == KVQ_BF16_CACHE) {
         if (qn == 2) {
           hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 4, KB, VB, 2>), grid, dim3(kThreads), 0, st, p);
           break;
@@ -786,8 +787,8 @@ hipError_t launch_fp8_mfma(const DecodeArgs& a, hipStream_t st) {
   // several queries per sequence: batch * nq rows, and the split count
   // planned for that many (never more than the one-query plan, whose
   // workspace nq copies of hold the partials)
-  // two queries per block: FP8 pages at GQA 4, an even number of queries
-  const int qn = (is_fp8(g.scheme) && g.hg == 4 && nq >= 2 && nq % 2 == 0) ? 2 : 1;
+  // two queries per block: FP8 or bfloat16 pages at GQA 4, an even number of queries
+  const int qn = ((is_fp8(g.scheme) || g.scheme == KVQ_BF16_CACHE) && g.hg == 4 && nq >= 2 && nq % 2 == 0) ? 2 : 1;
   Geometry rows = g;
   rows.batch = g.batch * nq / qn;
   Fp8Params p{};
@@ -813,7 +814,7 @@ hipError_t launch_fp8_mfma(const DecodeArgs& a, hipStream_t st) {
   p.qscale = a.sm_scale * kLog2e;
   const int rows_n = g.batch * nq / qn;
   switch (g.scheme) {
-    case KVQ_BF16_CACHE: return by_d<KVQ_BF16_CACHE>(p, g.d, g.hg, rows_n, st);
+    case KVQ_BF16_CACHE: return by_d<KVQ_BF16_CACHE>(p, g.d, g.hg, rows_n, st, qn);
     case KVQ_FP8_E5M2: return by_d<KVQ_FP8_E5M2>(p, g.d, g.hg, rows_n, st, qn);
     case KVQ_SYM_TOKEN:
       return g.bits == 2   ? by_d<KVQ_SYM_TOKEN, 2, 2>(p, g.d, g.hg, rows_n, st)

@@ -91,6 +91,8 @@ CASES = [
     (synth.FP8_E4M3, 8, 128, 4, torch.bfloat16, 0, 333, 0.0, 0, 4),
     (synth.FP8_E5M2, 8, 128, 4, torch.bfloat16, 0, 321, 0.0, 3, 2),
     (synth.FP8_E4M3, 8, 64, 4, torch.bfloat16, 0, 200, 0.0, 5, 16),
+    (synth.BF16_CACHE, 16, 128, 4, torch.bfloat16, 0, 150, 0.0, 2, 6),   # bfloat16 pages, two per block
+    (synth.BF16_CACHE, 16, 64, 4, torch.bfloat16, 0, 129, 0.0, 0, 2),    # the second query opens a page
     (synth.BF16_CACHE, 16, 64, 2, torch.bfloat16, 0, 77, 0.0, 1, 9),     # one split: no merge
 ]
 
