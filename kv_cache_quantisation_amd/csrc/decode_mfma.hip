@@ -1114,7 +1114,8 @@ __global__ __launch_bounds__(64 * kivi_waves(KB, VB, D, HG, ROPE),
 // kivi_mfma_kernel. Uniform batches only (one fill level).
 template <int KB, int VB, int D>
 __global__ __launch_bounds__(512, 1) void kivi_deq_kernel(MfmaParams p) {
-  static_assert((KB == 2 || KB == 4) && VB == 2 && D <= 128, "2- or 4-bit keys, 2-bit values, d <= 128");
+  static_assert((KB == 2 || KB == 4) && (VB == 2 || VB == 4) && VB <= KB && D <= 128,
+                "2- or 4-bit keys, 2- or 4-bit values, d <= 128");
   constexpr int HG = 4, QN = 4, GC = HG * QN;   // 16 (query, head) pairs
   constexpr int NW = 8, NTH = 64 * NW;
   using PG = PageGeom<KB, VB, D>;
@@ -1356,6 +1357,19 @@ __global__ __launch_bounds__(512, 1) void kivi_deq_kernel(MfmaParams p) {
     split_bf16(pv[5], pv[7], ph[3], pl[3]);
     const bf16x8 aph = __builtin_bit_cast(bf16x8, uint4{ph[0], ph[1], ph[2], ph[3]});
     const bf16x8 apl = __builtin_bit_cast(bf16x8, uint4{pl[0], pl[1], pl[2], pl[3]});
+    if constexpr (VB == 4) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {   // a word per channel tile: tokens 8g..8g+7
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(pg + PG::OFF_VC + (16 * nt + j) * VROW + 4 * g);
+        const uint32_t y0 = w & 0x0F0F0F0Fu, y1 = (w >> 4) & 0x0F0F0F0Fu;
+        const bf16x8 bw = __builtin_bit_cast(bf16x8, uint4{bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y0, 512.0f, false)),
+                                                           bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y1, 512.0f, false)),
+                                                           bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y0, 512.0f, true)),
+                                                           bits32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y1, 512.0f, true))});
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aph, bw, acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(apl, bw, acc[nt], 0, 0, 0);
+      }
+    } else {
 #pragma unroll
     for (int nt = 0; nt < NT; nt += 2) {   // two channel tiles per code word
       const uint8_t* col = pg + PG::OFF_VC + (16 * nt + j) * VROW + 2 * g;
@@ -1376,6 +1390,7 @@ __global__ __launch_bounds__(512, 1) void kivi_deq_kernel(MfmaParams p) {
       acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(apl, b0, acc[nt], 0, 0, 0);
       acc[nt + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aph, b1, acc[nt + 1], 0, 0, 0);
       acc[nt + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(apl, b1, acc[nt + 1], 0, 0, 0);
+    }
     }
   };
 
@@ -2460,7 +2475,7 @@ hipError_t by_hg(const MfmaParams& p, int hg, int rows, int qn, hipStream_t st) 
     case 1: hipLaunchKernelGGL((kivi_mfma_kernel<KB, VB, D, 1, ROPE>), grid, dim3(64 * kivi_waves(KB, VB, D, 1, ROPE)), 0, st, p); break;
     case 2: hipLaunchKernelGGL((kivi_mfma_kernel<KB, VB, D, 2, ROPE>), grid, dim3(64 * kivi_waves(KB, VB, D, 2, ROPE)), 0, st, p); break;
     case 4:
-      if constexpr (!ROPE && VB == 2 && D <= 128) {
+      if constexpr (!ROPE && D <= 128) {
         if (qn == 4) {   // four queries per block over dequantised keys
           hipLaunchKernelGGL((kivi_deq_kernel<KB, VB, D>), grid, dim3(512), 0, st, p);
           break;
@@ -2562,7 +2577,7 @@ hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t st) {
   // kivi2 shape 4 queries 33.9 us against 35.5 with two per block, 8: 44.0
   // against 69.0, 16: 84.5 against 136.1)
   const bool pairs = nq >= 2 && nq % 2 == 0 && g.hg == 4 && a.rope_theta == 0.0;
-  const bool fours = pairs && nq % 4 == 0 && g.vbits == 2 && g.d <= 128 && !a.seq_tokens;
+  const bool fours = pairs && nq % 4 == 0 && g.d <= 128 && !a.seq_tokens;
   const int qn = fours ? 4 : pairs ? 2 : 1;
   Geometry rows = g;
   rows.batch = g.batch * nq / qn;
@@ -2600,7 +2615,7 @@ hipError_t launch_kivi_mfma(const DecodeArgs& a, hipStream_t st) {
   const int grid_rows = g.batch * nq / qn;
   // long chunks (a multiple of 32 queries whose rows of 32 fill the chip):
   // one block per (sequence, KV head, 32 queries), one split
-  if (fours && g.d == 128 && nq % 32 == 0 &&
+  if (fours && g.vbits == 2 && g.d == 128 && nq % 32 == 0 &&
       static_cast<int64_t>(g.batch) * (nq / 32) * g.kv_heads >= 256) {
     p.splits = 1;
     const dim3 grid(1, g.kv_heads, g.batch * (nq / 32));

@@ -74,6 +74,7 @@ CASES = [
     (synth.KIVI, 4, 64, 4, torch.bfloat16, 8, 361, 0.0, 9, 44, 2, 12),
     (synth.KIVI, 4, 128, 4, torch.bfloat16, 64, 500, 0.0, 0, 16, 2, 32),
     (synth.KIVI, 4, 128, 4, torch.bfloat16, 32, 300, 0.0, 3, 100, 2, 6),
+    (synth.KIVI, 4, 64, 4, torch.bfloat16, 16, 300, 0.0, 4, 8),           # 4-bit values too
     # long chunks (a multiple of 32 queries, batch x n_q / 32 x KV heads >=
     # 256): each chunk of 32 tokens copied and dequantised once per block of
     # 32 queries; early query groups end inside the pages, later ones reach
