@@ -51,8 +51,9 @@
  *     q * s * sm_scale * log2(e) exceeds the f16 maximum (65504) is rescaled
  *     by a power of two inside the kernel and the scaling undone on its scores.
  *     Several queries decoded four per block (kvq_decode_attention_multi with
- *     a multiple of four queries of a KIVI cache at GQA 4 with 2-bit values,
- *     head_dim <= 128) take each page's keys dequantised into f16 high and
+ *     a multiple of four queries of a KIVI cache of 16-bit inputs at GQA 4
+ *     without rotary keys, head_dim <= 128) take each page's keys
+ *     dequantised into f16 high and
  *     remainder parts, and q' = q * sm_scale * log2(e) likewise, each scaled
  *     below 2^15 by a power of two: a score then carries, besides the bound
  *     above, up to 2^-24 * (|q'|_1 * max(1, K/2^14) + sum_c K_c * max(1,
