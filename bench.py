@@ -67,9 +67,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 # change to those, `traffic` is reported as null until they are taken again.
 ROOFLINE_EXTRA = 64            # roofline context = workload tokens + this
 COUNTERS = {
-    "kivi2": {"context": 4096 + ROOFLINE_EXTRA, "fetch_kib": 30750.69, "write_kib": 907.25,
+    "kivi2": {"context": 4096 + ROOFLINE_EXTRA, "fetch_kib": 30747.38, "write_kib": 904.25,
               "fetch_scale": 262144 / 131084, "write_scale": 1.0,
-              "sources_sha256": "f40594d61721cb5110ae35137326038674ae3ca8400d7ad91fcd051b12aa9470"},
+              "sources_sha256": "eca54787c857f4fd22490c3a1cb4c558b15b44c089421ce8c3ed9af0173859b6"},
 }
 DECODE_SOURCES = ["decode_mfma.hip", "kvq_device.h", "kvq_internal.h", "kvq_merge.h", "kvq_wave.h"]
 
