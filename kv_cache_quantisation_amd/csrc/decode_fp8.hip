@@ -126,16 +126,14 @@ __device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
 // z_t = -2^(VB-1) s_t that KIVI values carry explicitly. The unsigned code
 // converts give the channel (token) order {0,2,1,3,4,6,5,7} within each 8,
 // which the query (weight) operand follows (8-bit codes keep their order).
-// QN = 2 (FP8 or bfloat16 pages, GQA 4): two consecutive queries of a sequence per block,
+// QN = 2 (GQA 4): two consecutive queries of a sequence per block,
 // the second one's high and remainder columns and weight rows in the halves
 // of the products that one query at GQA 4 leaves idle; the pages up to the
 // second query's token, each column masking after its own query's.
 template <int FMT, int D, int HG, int KB = 8, int VB = 8, int QN = 1>
 __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   static_assert(2 * HG * QN <= 16, "high and remainder columns of the GQA group(s) fit one tile");
-  static_assert(QN == 1 || (QN == 2 && HG == 4 && (FMT == KVQ_FP8_E4M3 || FMT == KVQ_FP8_E5M2 ||
-                                                   FMT == KVQ_BF16_CACHE)),
-                "two queries per block: FP8 or bfloat16 pages, GQA 4");
+  static_assert(QN == 1 || (QN == 2 && HG == 4), "two queries per block: GQA 4");
   constexpr int GC = HG * QN;             // (query, head) pairs of the block
   constexpr bool BF16 = FMT == KVQ_BF16_CACHE;
   constexpr bool E5 = FMT == KVQ_FP8_E5M2;
@@ -256,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   if constexpr (SYMK) {
     float sq = 0.f;
 #pragma unroll
-    for (int i = 0; i < CPG; ++i) sq += qs[j % HG][g * CPG + i];
+    for (int i = 0; i < CPG; ++i) sq += qs[QN == 1 ? j % HG : (j / (2 * HG)) * HG + j % HG][g * CPG + i];
     sq += xor16(sq);
     sq += xor32(sq);
     kbias = sq * static_cast<float>(1 << (KB - 1));
@@ -716,7 +714,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_mfma_kernel(Fp8Params p) {
   }
 }
 
-// batch: grid rows (sequences x queries / qn); qn 2: two queries per block (FP8 or bf16, GQA 4)
+// batch: grid rows (sequences x queries / qn); qn 2: two queries per block (GQA 4)
 template <int FMT, int D, int KB, int VB>
 hipError_t by_hg(const Fp8Params& p, int hg, int batch, hipStream_t st, int qn = 1) {
   dim3 grid(p.splits, p.kv_heads, batch);
@@ -724,11 +722,9 @@ hipError_t by_hg(const Fp8Params& p, int hg, int batch, hipStream_t st, int qn =
     case 1: hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 1, KB, VB>), grid, dim3(kThreads), 0, st, p); break;
     case 2: hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 2, KB, VB>), grid, dim3(kThreads), 0, st, p); break;
     case 4:
-      if constexpr (FMT == KVQ_FP8_E4M3 || FMT == KVQ_FP8_E5M2 || FMT == KVQ_BF16_CACHE) {
-        if (qn == 2) {
-          hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 4, KB, VB, 2>), grid, dim3(kThreads), 0, st, p);
-          break;
-        }
+      if (qn == 2) {
+        hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 4, KB, VB, 2>), grid, dim3(kThreads), 0, st, p);
+        break;
       }
       hipLaunchKernelGGL((paged_mfma_kernel<FMT, D, 4, KB, VB>), grid, dim3(kThreads), 0, st, p);
       break;
@@ -787,8 +783,8 @@ hipError_t launch_fp8_mfma(const DecodeArgs& a, hipStream_t st) {
   // several queries per sequence: batch * nq rows, and the split count
   // planned for that many (never more than the one-query plan, whose
   // workspace nq copies of hold the partials)
-  // two queries per block: FP8 or bfloat16 pages at GQA 4, an even number of queries
-  const int qn = ((is_fp8(g.scheme) || g.scheme == KVQ_BF16_CACHE) && g.hg == 4 && nq >= 2 && nq % 2 == 0) ? 2 : 1;
+  // two queries per block: GQA 4, an even number of queries
+  const int qn = (g.hg == 4 && nq >= 2 && nq % 2 == 0) ? 2 : 1;
   Geometry rows = g;
   rows.batch = g.batch * nq / qn;
   Fp8Params p{};
@@ -817,17 +813,17 @@ hipError_t launch_fp8_mfma(const DecodeArgs& a, hipStream_t st) {
     case KVQ_BF16_CACHE: return by_d<KVQ_BF16_CACHE>(p, g.d, g.hg, rows_n, st, qn);
     case KVQ_FP8_E5M2: return by_d<KVQ_FP8_E5M2>(p, g.d, g.hg, rows_n, st, qn);
     case KVQ_SYM_TOKEN:
-      return g.bits == 2   ? by_d<KVQ_SYM_TOKEN, 2, 2>(p, g.d, g.hg, rows_n, st)
-             : g.bits == 4 ? by_d<KVQ_SYM_TOKEN, 4, 4>(p, g.d, g.hg, rows_n, st)
-                           : by_d<KVQ_SYM_TOKEN, 8, 8>(p, g.d, g.hg, rows_n, st);
+      return g.bits == 2   ? by_d<KVQ_SYM_TOKEN, 2, 2>(p, g.d, g.hg, rows_n, st, qn)
+             : g.bits == 4 ? by_d<KVQ_SYM_TOKEN, 4, 4>(p, g.d, g.hg, rows_n, st, qn)
+                           : by_d<KVQ_SYM_TOKEN, 8, 8>(p, g.d, g.hg, rows_n, st, qn);
     case KVQ_FP8K_SYMV:
-      return g.vbits == 2   ? by_d<KVQ_FP8K_SYMV, 8, 2>(p, g.d, g.hg, rows_n, st)
-             : g.vbits == 4 ? by_d<KVQ_FP8K_SYMV, 8, 4>(p, g.d, g.hg, rows_n, st)
-                            : by_d<KVQ_FP8K_SYMV, 8, 8>(p, g.d, g.hg, rows_n, st);
+      return g.vbits == 2   ? by_d<KVQ_FP8K_SYMV, 8, 2>(p, g.d, g.hg, rows_n, st, qn)
+             : g.vbits == 4 ? by_d<KVQ_FP8K_SYMV, 8, 4>(p, g.d, g.hg, rows_n, st, qn)
+                            : by_d<KVQ_FP8K_SYMV, 8, 8>(p, g.d, g.hg, rows_n, st, qn);
     case KVQ_FP8K_KIVIV:
-      return g.vbits == 2   ? by_d<KVQ_FP8K_KIVIV, 8, 2>(p, g.d, g.hg, rows_n, st)
-             : g.vbits == 4 ? by_d<KVQ_FP8K_KIVIV, 8, 4>(p, g.d, g.hg, rows_n, st)
-                            : by_d<KVQ_FP8K_KIVIV, 8, 8>(p, g.d, g.hg, rows_n, st);
+      return g.vbits == 2   ? by_d<KVQ_FP8K_KIVIV, 8, 2>(p, g.d, g.hg, rows_n, st, qn)
+             : g.vbits == 4 ? by_d<KVQ_FP8K_KIVIV, 8, 4>(p, g.d, g.hg, rows_n, st, qn)
+                            : by_d<KVQ_FP8K_KIVIV, 8, 8>(p, g.d, g.hg, rows_n, st, qn);
     default: return by_d<KVQ_FP8_E4M3>(p, g.d, g.hg, rows_n, st, qn);
   }
 }

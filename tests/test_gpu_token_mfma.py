@@ -71,10 +71,12 @@ def test_decode(case):
     assert err <= H.ATOL, (case, err)
 
 
-@pytest.mark.parametrize("case", [0, 4, 7, 10, 12, 14, 17, 19, 21])
-def test_multi_query(case):
+@pytest.mark.parametrize("nq", [5, 6])
+@pytest.mark.parametrize("case", [0, 4, 6, 7, 10, 12, 14, 15, 17, 18, 19, 21])
+def test_multi_query(case, nq):
+    """Several queries; an even n_q at GQA 4 runs two queries per block."""
     w, cfg, cache, oc, ks, vs = build(CASES[case], B=3)
-    nq = min(5, w.tokens)
+    nq = min(nq, w.tokens)
     q = torch.stack([synth.query(w, device=DEV, tag=1 + i) for i in range(nq)], dim=1).contiguous()
     out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
     ws = torch.zeros(nq * kvq.kvq_cache_bytes(cfg, w.tokens, kvq.KVQ_BYTES_WORKSPACE), dtype=torch.uint8,
