@@ -449,18 +449,27 @@ def gpu_bench(args, w):
 
 
 def graph_replay(cfg, cache, ws, qs, outs, news, L, T, n_rep):
-    """The decode burst and one whole step (append + decode, every layer) at a
-    fixed context T, captured once in a HIP graph and replayed, so no host
-    launch cost is counted. Replays repeat identical work (the append writes
-    the same ring slot), and their decode outputs are checked bit for bit
+    """The decode burst at a fixed context T and one whole step (append +
+    decode, every layer) captured once each in a HIP graph and replayed, so
+    no host launch cost is counted. The step appends token T - 2 and decodes
+    over T - 1 tokens, a position where no page is encoded (as on the eager
+    steps). Replays repeat identical work (the append writes the same ring
+    slot with the same row), and their outputs are checked bit for bit
     against eager launches before and after the timed replays."""
     stream = torch.cuda.current_stream()
+    # the cache's tokens T - 2 and T - 1: the rows the step and the prefix re-append
     for layer in range(L):
+        kvq.kvq_quantize_append(cfg, cache, layer, T - 2, 1, news[layer][0][1], news[layer][1][1],
+                                stream=stream)
         kvq.kvq_quantize_append(cfg, cache, layer, T - 1, 1, news[layer][0][0], news[layer][1][0],
                                 stream=stream)
+    outs_step = [torch.empty_like(o) for o in outs]
+    for layer in range(L):
         kvq.kvq_decode_attention(cfg, cache, layer, T, qs[layer], outs[layer], ws, stream=stream)
+        kvq.kvq_decode_attention(cfg, cache, layer, T - 1, qs[layer], outs_step[layer], ws, stream=stream)
     torch.cuda.synchronize()
-    eager = [o.clone() for o in outs]
+    eager = {"decode_burst": [o.clone() for o in outs], "step": [o.clone() for o in outs_step]}
+    target = {"decode_burst": outs, "step": outs_step}
 
     def burst():
         for layer in range(L):
@@ -468,33 +477,34 @@ def graph_replay(cfg, cache, ws, qs, outs, news, L, T, n_rep):
 
     def step():
         for layer in range(L):
-            kvq.kvq_append_decode(cfg, cache, layer, T - 1, news[layer][0][0], news[layer][1][0],
-                                  qs[layer], outs[layer], ws)
+            kvq.kvq_append_decode(cfg, cache, layer, T - 2, news[layer][0][1], news[layer][1][1],
+                                  qs[layer], outs_step[layer], ws)
 
     res, ok = {}, True
     for name, fn in (("decode_burst", burst), ("step", step)):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             fn()
-        for o in outs:
+        for o in target[name]:
             o.zero_()
         g.replay()
         torch.cuda.synchronize()
-        ok &= all(torch.equal(o, e) for o, e in zip(outs, eager))
+        ok &= all(torch.equal(o, e) for o, e in zip(target[name], eager[name]))
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         for _ in range(n_rep):
             g.replay()
         b.record(stream)
         torch.cuda.synchronize()
-        ok &= all(torch.equal(o, e) for o, e in zip(outs, eager))
+        ok &= all(torch.equal(o, e) for o, e in zip(target[name], eager[name]))
         res[name] = a.elapsed_time(b) * 1e3 / n_rep
         del g
     burst()   # eager again after the replays
     torch.cuda.synchronize()
-    ok &= all(torch.equal(o, e) for o, e in zip(outs, eager))
+    ok &= all(torch.equal(o, e) for o, e in zip(outs, eager["decode_burst"]))
     return {"decode_us_per_launch": round(res["decode_burst"] / L, 3),
-            "ms_per_step": round(res["step"] / 1e3, 4), "context": T, "outputs_match_eager": ok}
+            "ms_per_step": round(res["step"] / 1e3, 4), "context": T, "step_context": T - 1,
+            "outputs_match_eager": ok}
 
 
 def copy_ceiling(gib=1, reps=10):
