@@ -653,7 +653,15 @@ def config_row(name, dec_reps=20, pre_reps=3):
     ws = kvq.alloc_workspace(cfg, T + 1, device=dev)
     dec = each(lambda: kvq.kvq_decode_attention(cfg, cache, 0, T + 1, q, out, ws, k_scale=ks,
                                                 v_scale=vs, stream=stream), dec_reps)
-    del cache, ws
+    # four causal queries per sequence over the same cache (the last four
+    # tokens' positions; e.g. speculated tokens being verified)
+    qm = torch.stack([synth.query(w, device=dev, tag=1 + i) for i in range(4)], dim=1).contiguous()
+    om = torch.empty(qm.shape, dtype=torch.float32, device=dev)
+    wsm = torch.zeros(4 * kvq.kvq_cache_bytes(cfg, T + 1, kvq.KVQ_BYTES_WORKSPACE), dtype=torch.uint8,
+                      device=dev)
+    dec4 = each(lambda: kvq.kvq_decode_attention_multi(cfg, cache, 0, T + 1, qm, om, wsm, k_scale=ks,
+                                                       v_scale=vs, stream=stream), max(3, dec_reps // 4))
+    del cache, ws, wsm
     torch.cuda.empty_cache()
     med = lambda xs: xs[len(xs) // 2]   # noqa: E731
     dec_b, pre_b = any_decode_bytes(w, T + 1), any_append_bytes(w, 0, T)
@@ -667,6 +675,8 @@ def config_row(name, dec_reps=20, pre_reps=3):
         "prefill_tokens_per_s": round(w.batch * T / (med(pre) * 1e-6)),
         "prefill_frac_of_hbm_peak": round(pre_b / med(pre) / 1e3 / HBM_PEAK_GBS, 4),
         "append1_us_median": round(med(app), 2),
+        "decode_4_queries_us_median": round(med(dec4), 2),
+        "decode_4_queries_x_one_query": round(med(dec4) / med(dec), 2),
     }
 
 
